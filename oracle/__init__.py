@@ -1,0 +1,1 @@
+"""Oracle package -- test infrastructure only (see oracle.py)."""

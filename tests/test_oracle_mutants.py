@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in a copy of the oracle's C source (on the CPU),
+build each copy, and check that at least one pin rejects it.  This shows the
+pins are strong enough to catch a dropped term, a wrong sign or index, a
+transposed operand, a flipped kernel or a missing bounds check."""
+import os
+import tempfile
+
+import pytest
+
+from oracle import oracle as O
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(O.__file__), "oracle.c")
+
+# (name, text to replace, replacement, which occurrence (0-based))
+MUTANTS = [
+    ("flat-index wrap: no column bounds check",
+     "if (yy >= 0 && yy < H && xx >= 0 && xx < W) v = map[yy * W + xx];",
+     "{ int32_t q = yy * W + xx; if (q >= 0 && q < H * W) v = map[q]; }", 0),
+    ("tap order transposed (dx-major)",
+     "int32_t yy = y + (j / 3 - 1), xx = x + (j % 3 - 1);",
+     "int32_t yy = y + (j % 3 - 1), xx = x + (j / 3 - 1);", 0),
+    ("map not reset between frames",
+     "for (int64_t c = 0; c < cells; ++c) map[c] = -1;",
+     "if (t == 0) for (int64_t c = 0; c < cells; ++c) map[c] = -1;", 0),
+    ("duplicate coordinate not detected",
+     "if (map[p] != -1) { status = ORC_DUPLICATE; break; }", "", 0),
+    ("forward drops the centre tap",
+     "int32_t m = N[k * 9 + j];\n            if (m < 0) continue;\n            const double *x",
+     "int32_t m = N[k * 9 + j];\n            if (m < 0 || j == 4) continue;\n            const double *x", 0),
+    ("forward flips the kernel (true convolution)",
+     "const double *w = Wt + (int64_t)j * Ci * Co;",
+     "const double *w = Wt + (int64_t)(8 - j) * Ci * Co;", 0),
+    ("forward reads the own row instead of the neighbour",
+     "const double *x = X + (int64_t)m * Ci;", "const double *x = X + k * Ci;", 0),
+    ("forward drops the bias",
+     "if (b)\n            for (int32_t o = 0; o < Co; ++o) acc[o] += b[o];", "", 0),
+    ("dX gather without the mirrored tap",
+     "int32_t m = N[k * 9 + (8 - j)];", "int32_t m = N[k * 9 + j];", 0),
+    ("dX scatter with the wrong sign",
+     "dX[(int64_t)m * Ci + i] += s;", "dX[(int64_t)m * Ci + i] -= s;", 0),
+    ("dW with operands swapped between gathered and own row",
+     "double xv = X[(int64_t)m * Ci + i];\n            const double *g = dY + k * Co;",
+     "double xv = X[k * Ci + i];\n            const double *g = dY + (int64_t)m * Co;", 0),
+    ("db drops the last token",
+     "for (int64_t k = 0; k < n; ++k)\n        for (int32_t o = 0; o < Co; ++o) db[o]",
+     "for (int64_t k = 0; k + 1 < n; ++k)\n        for (int32_t o = 0; o < Co; ++o) db[o]", 0),
+]
+
+
+def _mutate(src, old, new, occ):
+    pos = -1
+    for _ in range(occ + 1):
+        pos = src.index(old, pos + 1)
+    return src[:pos] + new + src[pos + len(old):]
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_rejected(name, old, new, occ, tmp_path):
+    src = open(SRC).read()
+    assert old in src, f"mutation anchor not found: {name}"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(_mutate(src, old, new, occ))
+    lib = O.compile_source(str(mpath), str(tmp_path / "libmutant.so"))
+    orc = O.Oracle(lib)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin rejects the mutant '{name}'"
