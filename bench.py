@@ -1,0 +1,418 @@
+#!/usr/bin/env python3
+"""SparseConv2D fwd+bwd throughput on one MI355X.
+
+Default workload (one "step" = one pass of the whole hot path over one
+batch): T = 384 frames of a 16 x 16 patch grid, three nested pruning stages
+(per-frame keep ratios U[.5,.7], U[.3,.5], U[.15,.3]), two adapter layers per
+stage, C_in = C_out = 256, bf16 storage with fp32 accumulation:
+  per stage: neighbour-table build (sv_build_index), reused by its 2 layers;
+  forward through 6 layers with a row gather at each stage change;
+  backward through 6 layers: dW + db (split-K), dX, row scatter at stage
+  changes.
+Inputs are resident in HBM before the timed region starts; the timed region
+is K steps between two device synchronisations.
+
+Output: one JSON line (metric, value in effective TFLOP/s over kept tokens,
+ms_per_step, a per-kernel breakdown, the roofline of the dominant kernel
+measured with HIP events on its launch stream, and the CPU oracle timed on
+a bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SparseConv2D fwd+bwd effective TFLOP/s & HBM GB/s vs roofline, 1×MI355X"
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3      # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4"])
+    p.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-frames", type=int, default=384,
+                   help="frames of the workload the CPU oracle is timed on")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="also run one plain device copy of this size (HBM counter calibration)")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+class StagedRun:
+    """Config c5: nested stages, 2 layers per stage, fwd + bwd through all."""
+
+    def __init__(self, kernel="auto"):
+        import torch
+        from sparse_convolution_pruned_amd import ops, workloads as wl
+
+        self.ops, self.torch, self.kernel = ops, torch, kernel
+        S = wl.make_staged("c5")
+        self.S = S
+        bf = torch.bfloat16
+        dev = lambda a, d=None: (torch.from_numpy(a).to(d) if d is not None else torch.from_numpy(a)).cuda()
+        C = S.X0.shape[1]
+        self.C = C
+        self.L = len(S.weights)
+        self.lps = S.layers_per_stage
+        self.stage_of = [l // self.lps for l in range(self.L)]
+        self.coords = [dev(s["coords"]) for s in S.stages]
+        self.offs = [dev(s["frame_offsets"]) for s in S.stages]
+        self.sels = [None] + [dev(s["sel"]) for s in S.stages[1:]]
+        self.ns = [int(s["coords"].shape[0]) for s in S.stages]
+        self.N = [torch.empty((n, 9), dtype=torch.int32, device="cuda") for n in self.ns]
+        self.flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.W = [dev(w, bf) for w in S.weights]
+        self.b = [dev(b, bf) for b in S.biases]
+        self.x0 = dev(S.X0, bf)
+        self.dy_last = dev(S.dY_last, bf)
+        # activations: xs[l] = input of layer l; ys[l] = output
+        self.xs, self.ys = [], []
+        for l in range(self.L):
+            s = self.stage_of[l]
+            if l == 0:
+                self.xs.append(self.x0)
+            elif self.stage_of[l - 1] != s:
+                self.xs.append(torch.empty((self.ns[s], C), dtype=bf, device="cuda"))
+            else:
+                self.xs.append(self.ys[l - 1])
+            self.ys.append(torch.empty((self.ns[s], C), dtype=bf, device="cuda"))
+        # gradients: gy[l] = dL/dY_l ; gx[l] = dL/dX_l
+        self.gx = [torch.empty((self.ns[self.stage_of[l]], C), dtype=bf, device="cuda") for l in range(self.L)]
+        self.gscat = {l: torch.empty((self.ns[self.stage_of[l] - 1], C), dtype=bf, device="cuda")
+                      for l in range(1, self.L) if self.stage_of[l - 1] != self.stage_of[l]}
+        self.dW = [torch.empty((9, C, C), dtype=torch.float32, device="cuda") for _ in range(self.L)]
+        self.db = [torch.empty((C,), dtype=torch.float32, device="cuda") for _ in range(self.L)]
+        wsb = max(ops.sv_workspace_bytes(ops.SV_OP_DW, n, C, C, bf) for n in self.ns)
+        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+
+    def flops(self):
+        """Effective FLOPs per step: 2 * n * 9 * C_in * C_out per pass, all
+        9 taps counted, over kept tokens; 3 passes per layer."""
+        C = self.C
+        return sum(3 * 2 * self.ns[self.stage_of[l]] * 9 * C * C for l in range(self.L))
+
+    def step(self, ev=None):
+        ops, kern = self.ops, self.kernel
+        rec = ev.record if ev is not None else (lambda *a, **k: None)
+        S = self.S
+        for s in range(len(self.ns)):
+            t = rec("index", None)
+            ops.sv_build_index(self.coords[s], self.offs[s], S.T, S.H, S.W, self.N[s], None, self.flag)
+            rec("index", t, units=self.ns[s])
+        for l in range(self.L):
+            s = self.stage_of[l]
+            if l > 0 and self.stage_of[l - 1] != s:
+                t = rec("gather", None)
+                ops.sv_stage_gather(self.ys[l - 1], self.sels[s], self.xs[l])
+                rec("gather", t, units=self.ns[s])
+            t = rec("fwd", None)
+            ops.sv_sparseconv2d_fwd(self.xs[l], self.N[s], self.W[l], self.b[l], self.ys[l], kern)
+            rec("fwd", t, units=self.ns[s])
+        g = self.dy_last
+        for l in reversed(range(self.L)):
+            s = self.stage_of[l]
+            t = rec("dw", None)
+            ops.sv_sparseconv2d_bwd_dw(self.xs[l], self.N[s], g, self.dW[l], self.db[l], False, self.ws)
+            rec("dw", t, units=self.ns[s])
+            t = rec("dx", None)
+            ops.sv_sparseconv2d_bwd_dx(g, self.N[s], self.W[l], self.gx[l], kern)
+            rec("dx", t, units=self.ns[s])
+            g = self.gx[l]
+            if l > 0 and self.stage_of[l - 1] != s:
+                t = rec("scatter", None)
+                ops.sv_stage_scatter(g, self.sels[s], self.gscat[l])
+                rec("scatter", t, units=self.ns[s])
+                g = self.gscat[l]
+
+    def cpu_sample(self, frames):
+        """The oracle on the first `frames` frames of the same workload:
+        index build per stage, fwd through 6 layers, then dW, db, dX back
+        through them (float64 loops), the same chain as a GPU step."""
+        import numpy as np
+        from oracle import oracle as O
+        from sparse_convolution_pruned_amd import workloads as wl
+
+        Ssub = wl.make_staged("c5", scale_T=frames)
+        ns = [int(st["coords"].shape[0]) for st in Ssub.stages]
+        stage_of = self.stage_of
+        t0 = time.perf_counter()
+        Ns = []
+        for st in Ssub.stages:
+            _, N, _ = O.build_index(st["coords"], st["frame_offsets"], Ssub.T, Ssub.H, Ssub.W)
+            Ns.append(N)
+        xs = []
+        x = Ssub.X0.astype(np.float64)
+        for l in range(self.L):
+            s = stage_of[l]
+            if l > 0 and stage_of[l - 1] != s:
+                x = x[Ssub.stages[s]["sel"]]
+            xs.append(x)
+            x = O.fwd(x, Ns[s], Ssub.weights[l], Ssub.biases[l])
+        g = Ssub.dY_last.astype(np.float64)
+        for l in reversed(range(self.L)):
+            s = stage_of[l]
+            O.bwd_dw(xs[l], Ns[s], g)
+            O.bwd_db(g)
+            g = O.bwd_dx(g, Ns[s], Ssub.weights[l])
+            if l > 0 and stage_of[l - 1] != s:
+                gp = np.zeros((ns[s - 1], g.shape[1]))
+                gp[Ssub.stages[s]["sel"]] = g
+                g = gp
+        dt = time.perf_counter() - t0
+        fl = sum(3 * 2 * ns[stage_of[l]] * 9 * self.C * self.C for l in range(self.L))
+        return fl, dt, O.threads()
+
+
+class Events:
+    """HIP events around each entry-point call, on the stream the kernels
+    are launched on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.items = []
+
+    def record(self, kind, start, units=0):
+        t = self.torch
+        e = t.cuda.Event(enable_timing=True)
+        e.record(t.cuda.current_stream())
+        if start is None:
+            return e
+        self.items.append((kind, start, e, units))
+        return None
+
+    def summary(self):
+        out = {}
+        for kind, s, e, units in self.items:
+            d = out.setdefault(kind, {"ms": 0.0, "launches": 0, "units": 0})
+            d["ms"] += s.elapsed_time(e)
+            d["launches"] += 1
+            d["units"] += units
+        return out
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel_file, kernel_name):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, only
+    when they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_name)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != source_sha([kernel_file, "sparse_convolution_pruned_amd/csrc/internal.h"]):
+        return None
+    return rec
+
+
+def layer_workload(args):
+    """Single-layer workloads (c2, c3a, c3b, c4), for the design notes'
+    per-configuration table; prints one JSON line of its own."""
+    import torch
+    from sparse_convolution_pruned_amd import ops, workloads as wl
+
+    L = wl.make_layer(args.workload)
+    cfg = wl.CONFIGS[args.workload]
+    bf = torch.bfloat16
+    dev = lambda a, d=None: (torch.from_numpy(a).to(d) if d is not None else torch.from_numpy(a)).cuda()
+    coords, offs = dev(L.coords), dev(L.frame_offsets)
+    X, Wt, b, dY = dev(L.X, bf), dev(L.Wt, bf), dev(L.b, bf), dev(L.dY, bf)
+    n, C = L.n, L.X.shape[1]
+    N = torch.empty((n, 9), dtype=torch.int32, device="cuda")
+    Y = torch.empty((n, C), dtype=bf, device="cuda")
+    dX = torch.empty((n, C), dtype=bf, device="cuda")
+    dW = torch.empty((9, C, C), dtype=torch.float32, device="cuda")
+    db = torch.empty((C,), dtype=torch.float32, device="cuda")
+    passes = cfg["passes"]
+    chunked = "chunk_frames" in cfg
+    if chunked:
+        desc = ops.make_chunked_desc(L.T, L.H, L.W, coords, offs, torch.from_numpy(L.frame_offsets.copy()),
+                                     C, C, bf, cfg["chunk_frames"], X=X, Wt=Wt, bias=b, Y=Y, dY=dY,
+                                     dX=dX, dW=dW, db=db, kernel=args.kernel)
+        pm = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
+        ws = torch.empty(max(256, ops.sv_chunked_workspace_bytes(desc, pm)), dtype=torch.uint8, device="cuda")
+
+        def step():
+            ops.sv_sparseconv2d_chunked(desc, pm, ws)
+    else:
+        ws = torch.empty(max(256, ops.sv_workspace_bytes(ops.SV_OP_DW, n, C, C, bf)), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            ops.sv_build_index(coords, offs, L.T, L.H, L.W, N)
+            ops.sv_sparseconv2d_fwd(X, N, Wt, b, Y, args.kernel)
+            if "dx" in passes:
+                ops.sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, args.kernel)
+            if "dw" in passes:
+                ops.sv_sparseconv2d_bwd_dw(X, N, dY, dW, db, False, ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.reset_peak_memory_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    fl = len(passes) * 2 * n * 9 * C * C
+    print(json.dumps({"workload": args.workload, "name": cfg["name"], "kernel": args.kernel, "n": n,
+                      "ms_per_step": round(sec * 1e3, 4), "tflops": round(fl / sec / 1e12, 3),
+                      "frac_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "peak_mem_mb": round(torch.cuda.max_memory_allocated() / 2 ** 20, 1),
+                      "workspace_mb": round(ws.numel() / 2 ** 20, 2)}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding by frames is described in the design notes, not built)"}))
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload != "c5":
+        return layer_workload(args)
+
+    run = StagedRun(args.kernel)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+    assert int(run.flag.item()) == 0, "index build reported a coordinate error"
+    torch.cuda.reset_peak_memory_stats()
+
+    # timed region: K steps, no instrumentation
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    fl = run.flops()
+    tflops = fl / (wall / args.steps) / 1e12
+
+    # instrumented timed region: the same K steps with HIP events per call
+    ev = Events(torch)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        run.step(ev)
+    torch.cuda.synchronize()
+    ms_instr = (time.perf_counter() - t1) * 1e3 / args.steps
+    kinds = ev.summary()
+    C = run.C
+    per_unit = {  # algorithmic FLOPs and compulsory HBM bytes per token (bf16)
+        "fwd": (2 * 9 * C * C, 2 * (C + C) + 36),
+        "dx": (2 * 9 * C * C, 2 * (C + C) + 36),
+        "dw": (2 * 9 * C * C, 2 * (C + C) + 36),
+        "index": (0, 40),
+        "gather": (0, 4 * C + 4),
+        "scatter": (0, 4 * C + 4),
+    }
+    breakdown = {}
+    for k, d in kinds.items():
+        f_unit, b_unit = per_unit[k]
+        sec = d["ms"] / 1e3
+        breakdown[k] = {
+            "ms_per_step": round(d["ms"] / args.steps, 4),
+            "launches_per_step": d["launches"] // args.steps,
+            "avg_launch_us": round(d["ms"] * 1e3 / d["launches"], 2),
+            "tflops": round(f_unit * d["units"] / sec / 1e12, 2) if f_unit else None,
+            "gbps_compulsory": round(b_unit * d["units"] / sec / 1e9, 1),
+        }
+    conv = {k: kinds[k]["ms"] for k in ("fwd", "dx", "dw") if k in kinds}
+    dom = max(conv, key=conv.get)
+    d = kinds[dom]
+    # per launch: FLOPs of the tokens it processed / its duration; averaged
+    # over launches weighted by duration (sum of FLOPs / sum of durations)
+    achieved = per_unit[dom][0] * d["units"] / (d["ms"] / 1e3) / 1e12
+    kernel_names = {"fwd": ("k_conv_mfma<false>", "sparse_convolution_pruned_amd/csrc/conv_mfma.hip"),
+                    "dx": ("k_conv_mfma<true>", "sparse_convolution_pruned_amd/csrc/conv_mfma.hip"),
+                    "dw": ("k_dw_mfma", "sparse_convolution_pruned_amd/csrc/dw.hip")}
+    kname, kfile = kernel_names[dom]
+    tr = traffic_record(kfile, kname)
+    roofline = {
+        "bound": "mfma",
+        "kernel": kname,
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": None if tr is None else tr.get("bytes_per_launch"),
+        "avg_launch_us": round(d["ms"] * 1e3 / d["launches"], 2),
+        "flops_per_launch": round(per_unit[dom][0] * d["units"] / d["launches"]),
+    }
+    step_bytes = sum(per_unit[k][1] * kinds[k]["units"] for k in kinds) / args.steps
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "T=384 frames, 16x16 grid, 3 nested pruning stages (keep U[.5,.7]/U[.3,.5]/"
+                        "U[.15,.3]), 2 layers per stage, C_in=C_out=256, fwd+bwd through 6 layers",
+            "tokens_per_stage": run.ns,
+            "kernel": args.kernel,
+            "flops_per_step": fl,
+        },
+        "hbm_gbps_compulsory": round(step_bytes / (wall / args.steps) / 1e9, 1),
+        "peak_mem_mb": round(torch.cuda.max_memory_allocated() / 2 ** 20, 1),
+        "ms_per_step_instrumented": round(ms_instr, 4),
+        "kernels": breakdown,
+        "roofline": roofline,
+    }
+    if args.calibrate_copy_mib:
+        nb = args.calibrate_copy_mib * 2 ** 20
+        a = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = nb
+    if not args.no_cpu_baseline:
+        cfl, cdt, threads = run.cpu_sample(args.cpu_frames)
+        out["cpu_baseline"] = {
+            "value": round(cfl / cdt / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {args.cpu_frames} of 384 frames of the same workload: index build per "
+                      f"stage, fwd through 6 layers, dW+db+dX back through them, float64 loops "
+                      f"({cdt:.1f} s)",
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * svconv -- native SparseConv2D on pruned token sequences, HIP for gfx950.
+ *
+ * C ABI.  Plain pointers and sizes only; every pointer argument named "device"
+ * is device memory owned by the caller; the library never allocates, never
+ * frees, never synchronises the stream and keeps no state other than a cached
+ * device property.  All work is enqueued asynchronously on the caller's
+ * hipStream_t (NULL = the default stream).  No C++ exception crosses this
+ * boundary.  Status codes report argument errors synchronously, before any
+ * work is enqueued; data errors found on the device (coordinates) are OR-ed
+ * into a caller-provided device flag.
+ *
+ * The method ("SV-TAD: Native Sparse Convolutions for Efficient Temporal
+ * Action Detection", paper notes page):
+ *   - Key Design 1 (Static Neighbor Index Table): a per-frame lookup map M of
+ *     H x W cells set to -1, then M[y_k, x_k] = k for every kept token; the
+ *     neighbour table N [n x 9] reads M at the nine 3x3 offsets, -1 where the
+ *     neighbour was pruned or falls outside the grid.
+ *   - Key Design 2 (Native Sparse 2D Convolution Kernels): y_k =
+ *     sum_j W_j x[N[k, j]], an entry of -1 acting as zero padding, computed
+ *     directly on the packed token sequence; chunked execution keeps memory
+ *     independent of video length.
+ *
+ * Conventions used throughout:
+ *   tap j = 3*(dy+1) + (dx+1), dy, dx in {-1,0,1}; centre tap j = 4.
+ *   Cross-correlation: tap j of token k reads the token at (y+dy, x+dx).
+ *   Flat coordinate p = y * W + x.  Tokens are packed frame-major; frame t
+ *   owns tokens frame_offsets[t] .. frame_offsets[t+1]-1.
+ *   Row-major contiguous layouts:
+ *     X [n][C_in], Y [n][C_out], N [n][9] int32 (global packed indices),
+ *     Wt [9][C_in][C_out]  (Wt[j][i][o] = torch weight[o][i][j/3][j%3]),
+ *     bias [C_out] (same dtype as X), dW [9][C_in][C_out] fp32, db [C_out] fp32.
+ *   bf16 = IEEE binary32 truncated to its upper 16 bits; outputs rounded to
+ *   nearest even.  Accumulation is always fp32.
+ */
+#ifndef SVCONV_H
+#define SVCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = 1,     /* null pointer, negative size, bad combination   */
+    SV_ERR_UNSUPPORTED = 2,     /* dtype / shape not supported by the kernel asked */
+    SV_ERR_WORKSPACE = 3,       /* workspace missing or smaller than required      */
+    SV_ERR_HIP = 4,             /* a HIP launch or query failed                   */
+    SV_ERR_COORD_RANGE = 5,     /* (device flag bit 1) coordinate outside H x W    */
+    SV_ERR_DUPLICATE_COORD = 6  /* (device flag bit 2) two tokens on one cell      */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Kernel choice for the convolution passes.  AUTO picks the bf16 MFMA kernel
+ * when dtype is bf16, C_in % 32 == 0 and C_out % 16 == 0 (dX: the same with
+ * C_in and C_out swapped), and the VALU kernel otherwise. */
+typedef enum sv_kernel { SV_KERNEL_AUTO = 0, SV_KERNEL_VALU = 1, SV_KERNEL_MFMA = 2 } sv_kernel;
+
+/* Bits of the device error flag written by sv_build_index. */
+#define SV_FLAG_COORD_RANGE   1  /* a coordinate p < 0 or p >= H*W                        */
+#define SV_FLAG_DUPLICATE     2  /* two tokens of one frame on one cell                   */
+#define SV_FLAG_BAD_OFFSETS   4  /* frame_offsets not non-decreasing within [0, n]        */
+
+/* Passes of sv_sparseconv2d_chunked. */
+#define SV_PASS_FWD 1u
+#define SV_PASS_DX  2u
+#define SV_PASS_DW  4u
+
+/* Operations for sv_workspace_bytes. */
+typedef enum sv_op { SV_OP_FWD = 0, SV_OP_DX = 1, SV_OP_DW = 2 } sv_op;
+
+/* ------------------------------------------------------------------------ */
+/* Key Design 1, both steps, on the GPU: per frame the map M lives in LDS
+ * (one workgroup per frame), is filled with -1, receives M[p_k] = k by atomic
+ * exchange (a second token on one cell raises SV_FLAG_DUPLICATE), and the
+ * nine lookups write N with bounds checked on y and x separately.
+ *
+ *   coords        device int32 [n]   flat coordinate of each kept token
+ *   frame_offsets device int32 [T+1] exclusive prefix sums of tokens per frame
+ *   T, H, W       frames and grid; H*W <= 16384 (LDS map), T >= 0
+ *   n             number of tokens = length of coords = rows of N_out
+ *   N_out         device int32 [n][9], written
+ *   M_out         nullable; device int32 [T][H][W], written with token
+ *                 indices (-1 for pruned cells)
+ *   err_flag      nullable; device int32, SV_FLAG_* bits OR-ed in (never
+ *                 cleared by the library).  Tokens with a bad coordinate get
+ *                 an all -1 row; with duplicates N is unspecified.
+ * Returns SV_ERR_INVALID_ARG for null required pointers or bad sizes,
+ * SV_ERR_UNSUPPORTED for H*W > 16384. */
+sv_status sv_build_index(const int32_t *coords, const int32_t *frame_offsets,
+                         int32_t T, int32_t H, int32_t W, int64_t n,
+                         int32_t *N_out, int32_t *M_out, int32_t *err_flag,
+                         hipStream_t stream);
+
+/* Key Design 2, forward: Y[k][o] = sum_j sum_i X[N[k,j]][i] Wt[j][i][o]
+ * + bias[o]; entries of N that are -1 (or outside [0, n)) contribute zero.
+ *   X [n][C_in], N [n][9], Wt [9][C_in][C_out], bias [C_out] nullable,
+ *   Y [n][C_out] written; all device, all in `dtype` except N.
+ * SV_ERR_UNSUPPORTED if `kernel` is MFMA and the shape/dtype does not fit it. */
+sv_status sv_sparseconv2d_fwd(const void *X, const int32_t *N, const void *Wt,
+                              const void *bias, void *Y, int64_t n,
+                              int32_t C_in, int32_t C_out, sv_dtype dtype,
+                              sv_kernel kernel, hipStream_t stream);
+
+/* Input gradient (the adjoint of the forward sum, written as gathers thanks
+ * to the mirrored offsets: token m is tap j of k exactly when k is tap 8-j
+ * of m):  dX[k][i] = sum_j sum_o dY[N[k,8-j]][o] Wt[j][i][o].
+ *   dY [n][C_out], N [n][9], Wt [9][C_in][C_out], dX [n][C_in] written. */
+sv_status sv_sparseconv2d_bwd_dx(const void *dY, const int32_t *N, const void *Wt,
+                                 void *dX, int64_t n, int32_t C_in, int32_t C_out,
+                                 sv_dtype dtype, sv_kernel kernel, hipStream_t stream);
+
+/* Weight (and bias) gradient, a split-K reduction over tokens:
+ *   dW[j][i][o] (+)= sum_k X[N[k,j]][i] dY[k][o],   db[o] (+)= sum_k dY[k][o].
+ * Token slices write fp32 partials to the workspace, then a fixed-order
+ * reduction adds them (deterministic: the same inputs give the same bits).
+ *   X [n][C_in], N [n][9], dY [n][C_out] in `dtype`;
+ *   dW [9][C_in][C_out] fp32 device, written (accumulate == 0) or added to;
+ *   db [C_out] fp32 device, nullable, same accumulate rule;
+ *   workspace: device, at least sv_workspace_bytes(SV_OP_DW, ...) bytes,
+ *   16-byte aligned; its contents are scratch. */
+sv_status sv_sparseconv2d_bwd_dw(const void *X, const int32_t *N, const void *dY,
+                                 float *dW, float *db, int64_t n, int32_t C_in,
+                                 int32_t C_out, sv_dtype dtype, int32_t accumulate,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Workspace bytes an operation needs for these sizes (0 for FWD and DX).
+ * Depends only on its arguments, never on the device. */
+size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype);
+
+/* Chunked execution over whole frames (Key Design 2's chunking): the frames
+ * are processed chunk_frames at a time; for each chunk the index table is
+ * built with chunk-local indices into the workspace, then the requested
+ * passes run on the chunk's token range.  Spatial neighbourhoods never cross
+ * frames, so chunks need no halo and the results equal the unchunked ones
+ * (N shifted by the chunk base; Y and dX identical; dW/db summed over chunks
+ * in chunk order).  Workspace is sized by the largest chunk, not by T. */
+typedef struct sv_chunked_desc {
+    int32_t T, H, W;
+    int32_t C_in, C_out;
+    sv_dtype dtype;
+    sv_kernel kernel;
+    int32_t chunk_frames;               /* >= 1                                  */
+    const int32_t *coords;              /* device [n]                            */
+    const int32_t *frame_offsets;       /* device [T+1]                          */
+    const int32_t *frame_offsets_host;  /* host [T+1], the same values           */
+    const void *X;                      /* device [n][C_in]   (FWD, DW)          */
+    const void *Wt;                     /* device [9][C_in][C_out] (FWD, DX)     */
+    const void *bias;                   /* device [C_out], nullable              */
+    void *Y;                            /* device [n][C_out]  (FWD)              */
+    const void *dY;                     /* device [n][C_out]  (DX, DW)           */
+    void *dX;                           /* device [n][C_in]   (DX)               */
+    float *dW;                          /* device [9][C_in][C_out] fp32 (DW), overwritten */
+    float *db;                          /* device [C_out] fp32, nullable (DW), overwritten */
+    int32_t *err_flag;                  /* device int32, nullable                */
+} sv_chunked_desc;
+
+sv_status sv_sparseconv2d_chunked(const sv_chunked_desc *desc, uint32_t passes,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* Workspace bytes sv_sparseconv2d_chunked needs for this descriptor (reads
+ * only the host fields: T, H, W, C_in, C_out, dtype, chunk_frames,
+ * frame_offsets_host).  Returns 0 and nothing else on bad descriptors. */
+size_t sv_chunked_workspace_bytes(const sv_chunked_desc *desc, uint32_t passes);
+
+/* Stage transition between pruning stages (the map is rebuilt at each
+ * selection point and reused by the adapter layers in between, Key Design 1):
+ * the next stage's packed input keeps a subset of the current rows.
+ *   sv_stage_gather:  dst[r] = src[rows[r]]            for r < n_rows
+ *   sv_stage_scatter: dst[m] = 0 for every m < n_dst, then dst[rows[r]] = src[r]
+ * (the backward of the gather).  Rows are C elements of `dtype`; rows[] is
+ * device int32 [n_rows]; for the scatter rows[] must be distinct; an index
+ * outside [0, n_src) / [0, n_dst) skips that row. */
+sv_status sv_stage_gather(const void *src, int64_t n_src, const int32_t *rows,
+                          int64_t n_rows, void *dst, int32_t C, sv_dtype dtype,
+                          hipStream_t stream);
+sv_status sv_stage_scatter(const void *src, const int32_t *rows, int64_t n_rows,
+                           void *dst, int64_t n_dst, int32_t C, sv_dtype dtype,
+                           hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *sv_status_string(sv_status status);
+
+/* Library version, e.g. "svconv 0.1.0 gfx950". */
+const char *sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVCONV_H */

@@ -1,0 +1,251 @@
+// C ABI of libsvconv: argument validation, kernel dispatch, chunk driver.
+// Nothing here allocates or synchronises; every launch goes to the caller's
+// stream.  Declarations and contracts: include/svconv.h.
+#include <limits>
+
+#include "internal.h"
+
+using namespace svc;
+
+namespace {
+
+constexpr int kMaxCells = 16384;
+constexpr int64_t kMaxRows = std::numeric_limits<int32_t>::max() / 9;
+
+bool valid_dtype(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
+bool valid_kernel(sv_kernel k) { return k == SV_KERNEL_AUTO || k == SV_KERNEL_VALU || k == SV_KERNEL_MFMA; }
+sv_status hip_status(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
+size_t align_up(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// Which conv kernel runs a pass; SV_ERR_UNSUPPORTED when MFMA is forced and
+// does not fit.
+sv_status choose(sv_kernel req, sv_dtype dt, bool dx, int Ci, int Co, bool* use_mfma) {
+    const bool fits = dt == SV_BF16 && conv_mfma_supported(dx, Ci, Co);
+    if (req == SV_KERNEL_MFMA && !fits) return SV_ERR_UNSUPPORTED;
+    *use_mfma = (req == SV_KERNEL_MFMA) || (req == SV_KERNEL_AUTO && fits);
+    return SV_OK;
+}
+
+sv_status conv_args_ok(int64_t n, int32_t Ci, int32_t Co, sv_dtype dt, sv_kernel k) {
+    if (n < 0 || n > kMaxRows || Ci <= 0 || Co <= 0) return SV_ERR_INVALID_ARG;
+    if (!valid_dtype(dt) || !valid_kernel(k)) return SV_ERR_INVALID_ARG;
+    return SV_OK;
+}
+
+sv_status run_fwd(const void* X, const int32_t* N, const void* Wt, const void* bias, void* Y,
+                  int64_t n, int32_t Ci, int32_t Co, sv_dtype dt, sv_kernel kernel, hipStream_t s) {
+    bool mfma = false;
+    sv_status st = choose(kernel, dt, false, Ci, Co, &mfma);
+    if (st != SV_OK) return st;
+    if (n == 0) return SV_OK;
+    if (mfma)
+        return hip_status(launch_conv_mfma(false, static_cast<const uint16_t*>(X), N,
+                                           static_cast<const uint16_t*>(Wt),
+                                           static_cast<const uint16_t*>(bias),
+                                           static_cast<uint16_t*>(Y), n, Ci, Co, s));
+    return hip_status(launch_conv_valu(dt == SV_BF16, false, X, N, Wt, bias, Y, n, Ci, Co, s));
+}
+
+sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int64_t n, int32_t Ci,
+                 int32_t Co, sv_dtype dt, sv_kernel kernel, hipStream_t s) {
+    bool mfma = false;
+    sv_status st = choose(kernel, dt, true, Ci, Co, &mfma);
+    if (st != SV_OK) return st;
+    if (n == 0) return SV_OK;
+    if (mfma)
+        return hip_status(launch_conv_mfma(true, static_cast<const uint16_t*>(dY), N,
+                                           static_cast<const uint16_t*>(Wt), nullptr,
+                                           static_cast<uint16_t*>(dX), n, Ci, Co, s));
+    return hip_status(launch_conv_valu(dt == SV_BF16, true, dY, N, Wt, nullptr, dX, n, Ci, Co, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status sv_build_index(const int32_t* coords, const int32_t* frame_offsets, int32_t T, int32_t H,
+                         int32_t W, int64_t n, int32_t* N_out, int32_t* M_out, int32_t* err_flag,
+                         hipStream_t stream) {
+    if (T < 0 || H <= 0 || W <= 0 || n < 0 || n > kMaxRows) return SV_ERR_INVALID_ARG;
+    if (!frame_offsets || (n > 0 && (!coords || !N_out))) return SV_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(H) * W > kMaxCells) return SV_ERR_UNSUPPORTED;
+    if (T == 0) return SV_OK;
+    return hip_status(launch_build_index(coords, frame_offsets, 0, T, H, W, n, 0, N_out, M_out,
+                                         err_flag, stream));
+}
+
+sv_status sv_sparseconv2d_fwd(const void* X, const int32_t* N, const void* Wt, const void* bias,
+                              void* Y, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                              sv_kernel kernel, hipStream_t stream) {
+    sv_status st = conv_args_ok(n, C_in, C_out, dtype, kernel);
+    if (st != SV_OK) return st;
+    if (!Wt || (n > 0 && (!X || !N || !Y))) return SV_ERR_INVALID_ARG;
+    return run_fwd(X, N, Wt, bias, Y, n, C_in, C_out, dtype, kernel, stream);
+}
+
+sv_status sv_sparseconv2d_bwd_dx(const void* dY, const int32_t* N, const void* Wt, void* dX,
+                                 int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                 sv_kernel kernel, hipStream_t stream) {
+    sv_status st = conv_args_ok(n, C_in, C_out, dtype, kernel);
+    if (st != SV_OK) return st;
+    if (!Wt || (n > 0 && (!dY || !N || !dX))) return SV_ERR_INVALID_ARG;
+    return run_dx(dY, N, Wt, dX, n, C_in, C_out, dtype, kernel, stream);
+}
+
+size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype) {
+    if (op != SV_OP_DW) return 0;
+    if (n < 0 || C_in <= 0 || C_out <= 0 || !valid_dtype(dtype)) return 0;
+    return dw_workspace_bytes(plan_dw(n, C_in, C_out, dtype == SV_BF16));
+}
+
+sv_status sv_sparseconv2d_bwd_dw(const void* X, const int32_t* N, const void* dY, float* dW, float* db,
+                                 int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                 int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    sv_status st = conv_args_ok(n, C_in, C_out, dtype, SV_KERNEL_AUTO);
+    if (st != SV_OK) return st;
+    if (!dW || (n > 0 && (!X || !N || !dY))) return SV_ERR_INVALID_ARG;
+    const DwPlan plan = plan_dw(n, C_in, C_out, dtype == SV_BF16);
+    const size_t need = dw_workspace_bytes(plan);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SV_ERR_WORKSPACE;
+    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_dw(plan, dtype == SV_BF16, X, N, dY, dW, db, n, C_in, C_out,
+                                accumulate ? 1 : 0, workspace, stream));
+}
+
+// ------------------------------------------------------------ chunk driver
+namespace {
+
+struct ChunkLayout {
+    int64_t max_tokens = 0;   // largest chunk, in tokens
+    size_t n_bytes = 0;       // chunk-local N table
+    size_t dw_bytes = 0;      // dW/db partials of the largest plan
+    size_t total = 0;
+};
+
+bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
+    if (!d || !d->frame_offsets_host || d->T < 0 || d->H <= 0 || d->W <= 0 ||
+        d->chunk_frames <= 0 || d->C_in <= 0 || d->C_out <= 0 || !valid_dtype(d->dtype))
+        return false;
+    const int32_t* ho = d->frame_offsets_host;
+    if (ho[0] != 0) return false;
+    for (int t = 0; t < d->T; ++t)
+        if (ho[t + 1] < ho[t]) return false;
+    L->max_tokens = 0;
+    // With the dW pass even an empty video needs the (zero-token) plan's db partials.
+    L->dw_bytes = (passes & SV_PASS_DW)
+                      ? dw_workspace_bytes(plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16))
+                      : 0;
+    for (int f0 = 0; f0 < d->T; f0 += d->chunk_frames) {
+        const int f1 = std::min(d->T, f0 + d->chunk_frames);
+        const int64_t toks = static_cast<int64_t>(ho[f1]) - ho[f0];
+        L->max_tokens = std::max(L->max_tokens, toks);
+        if (passes & SV_PASS_DW)
+            L->dw_bytes = std::max(L->dw_bytes, dw_workspace_bytes(plan_dw(toks, d->C_in, d->C_out,
+                                                                          d->dtype == SV_BF16)));
+    }
+    L->n_bytes = align_up(static_cast<size_t>(L->max_tokens) * 9 * sizeof(int32_t));
+    L->total = L->n_bytes + L->dw_bytes;
+    return true;
+}
+
+}  // namespace
+
+size_t sv_chunked_workspace_bytes(const sv_chunked_desc* desc, uint32_t passes) {
+    ChunkLayout L;
+    if (!chunk_layout(desc, passes, &L)) return 0;
+    return L.total;
+}
+
+sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    ChunkLayout L;
+    if (!chunk_layout(d, passes, &L)) return SV_ERR_INVALID_ARG;
+    if (passes & ~(SV_PASS_FWD | SV_PASS_DX | SV_PASS_DW)) return SV_ERR_INVALID_ARG;
+    if (!valid_kernel(d->kernel)) return SV_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(d->H) * d->W > kMaxCells) return SV_ERR_UNSUPPORTED;
+    const int64_t n = d->frame_offsets_host[d->T];
+    if (n > kMaxRows) return SV_ERR_INVALID_ARG;
+    if (!d->frame_offsets || (n > 0 && !d->coords)) return SV_ERR_INVALID_ARG;
+    if ((passes & SV_PASS_FWD) && (!d->X || !d->Wt || !d->Y)) return SV_ERR_INVALID_ARG;
+    if ((passes & SV_PASS_DX) && (!d->dY || !d->Wt || !d->dX)) return SV_ERR_INVALID_ARG;
+    if ((passes & SV_PASS_DW) && (!d->X || !d->dY || !d->dW)) return SV_ERR_INVALID_ARG;
+    bool m;
+    if ((passes & SV_PASS_FWD) && choose(d->kernel, d->dtype, false, d->C_in, d->C_out, &m) != SV_OK)
+        return SV_ERR_UNSUPPORTED;
+    if ((passes & SV_PASS_DX) && choose(d->kernel, d->dtype, true, d->C_in, d->C_out, &m) != SV_OK)
+        return SV_ERR_UNSUPPORTED;
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return SV_ERR_WORKSPACE;
+    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256) return SV_ERR_INVALID_ARG;
+
+    const size_t es = d->dtype == SV_BF16 ? 2 : 4;
+    int32_t* Nc = static_cast<int32_t*>(workspace);
+    void* dws = static_cast<char*>(workspace) + L.n_bytes;
+    const int32_t* ho = d->frame_offsets_host;
+    bool first = true;
+    for (int f0 = 0; f0 < d->T; f0 += d->chunk_frames) {
+        const int f1 = std::min(d->T, f0 + d->chunk_frames);
+        const int64_t t0 = ho[f0], nc = static_cast<int64_t>(ho[f1]) - t0;
+        sv_status st = hip_status(launch_build_index(d->coords, d->frame_offsets, f0, f1 - f0, d->H, d->W,
+                                                     nc, t0, Nc, nullptr, d->err_flag, stream));
+        if (st != SV_OK) return st;
+        const char* X = d->X ? static_cast<const char*>(d->X) + t0 * d->C_in * es : nullptr;
+        const char* dY = d->dY ? static_cast<const char*>(d->dY) + t0 * d->C_out * es : nullptr;
+        if (passes & SV_PASS_FWD) {
+            st = run_fwd(X, Nc, d->Wt, d->bias, static_cast<char*>(d->Y) + t0 * d->C_out * es, nc,
+                         d->C_in, d->C_out, d->dtype, d->kernel, stream);
+            if (st != SV_OK) return st;
+        }
+        if (passes & SV_PASS_DX) {
+            st = run_dx(dY, Nc, d->Wt, static_cast<char*>(d->dX) + t0 * d->C_in * es, nc, d->C_in,
+                        d->C_out, d->dtype, d->kernel, stream);
+            if (st != SV_OK) return st;
+        }
+        if (passes & SV_PASS_DW) {
+            const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16);
+            st = hip_status(launch_dw(plan, d->dtype == SV_BF16, X, Nc, dY, d->dW, d->db, nc, d->C_in,
+                                      d->C_out, first ? 0 : 1, dws, stream));
+            if (st != SV_OK) return st;
+        }
+        first = false;
+    }
+    if (first && (passes & SV_PASS_DW)) {
+        // No frames at all: the gradients of an empty sum are zero.
+        const DwPlan plan = plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16);
+        return hip_status(launch_dw(plan, d->dtype == SV_BF16, d->X, Nc, d->dY, d->dW, d->db, 0, d->C_in,
+                                    d->C_out, 0, dws, stream));
+    }
+    return SV_OK;
+}
+
+sv_status sv_stage_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n_rows, void* dst,
+                          int32_t C, sv_dtype dtype, hipStream_t stream) {
+    if (n_src < 0 || n_rows < 0 || C <= 0 || !valid_dtype(dtype)) return SV_ERR_INVALID_ARG;
+    if (n_rows > 0 && (!src || !rows || !dst)) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_stage_gather(src, n_src, rows, n_rows, dst, C, dtype == SV_BF16 ? 2 : 4, stream));
+}
+
+sv_status sv_stage_scatter(const void* src, const int32_t* rows, int64_t n_rows, void* dst, int64_t n_dst,
+                           int32_t C, sv_dtype dtype, hipStream_t stream) {
+    if (n_dst < 0 || n_rows < 0 || C <= 0 || !valid_dtype(dtype)) return SV_ERR_INVALID_ARG;
+    if (n_dst > 0 && !dst) return SV_ERR_INVALID_ARG;
+    if (n_rows > 0 && (!src || !rows)) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_stage_scatter(src, rows, n_rows, dst, n_dst, C, dtype == SV_BF16 ? 2 : 4, stream));
+}
+
+const char* sv_status_string(sv_status s) {
+    switch (s) {
+        case SV_OK: return "SV_OK";
+        case SV_ERR_INVALID_ARG: return "SV_ERR_INVALID_ARG: invalid argument";
+        case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED: shape or dtype not supported by the kernel";
+        case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: workspace missing or too small";
+        case SV_ERR_HIP: return "SV_ERR_HIP: a HIP call failed";
+        case SV_ERR_COORD_RANGE: return "SV_ERR_COORD_RANGE: coordinate outside the grid";
+        case SV_ERR_DUPLICATE_COORD: return "SV_ERR_DUPLICATE_COORD: two tokens on one grid cell";
+    }
+    return "unknown sv_status";
+}
+
+const char* sv_version(void) { return "svconv 0.1.0 gfx950"; }
+
+}  // extern "C"

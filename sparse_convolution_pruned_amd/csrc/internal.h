@@ -1,0 +1,102 @@
+// Internal declarations shared by the HIP translation units of libsvconv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "svconv.h"
+
+namespace svc {
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p) { return *p; }
+    static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_to_f32(*p); }
+    static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// A row of N is valid when 0 <= m < n; anything else reads as zero padding.
+__device__ __forceinline__ int clamp_index(int m, int n) {
+    return (static_cast<unsigned>(m) < static_cast<unsigned>(n)) ? m : -1;
+}
+
+// 8x8 transpose of 16-bit elements held as 8 rows of 4 dwords (element 2d in
+// the low half of dword d, element 2d+1 in the high half).  out[c] is column c
+// of the input, in the same packing.
+__device__ __forceinline__ void transpose8x8_b16(const uint4 in[8], uint4 out[8]) {
+    uint32_t r[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        r[i][0] = in[i].x; r[i][1] = in[i].y; r[i][2] = in[i].z; r[i][3] = in[i].w;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            uint32_t a = r[2 * p][c >> 1], b = r[2 * p + 1][c >> 1];
+            o[p] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        }
+        out[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+
+hipError_t launch_build_index(const int32_t* coords, const int32_t* offs, int frame_begin,
+                              int frames, int H, int W, int64_t n, int64_t tok_base,
+                              int32_t* N, int32_t* M, int32_t* err, hipStream_t stream);
+
+// VALU path (fp32 or bf16, any channel count).  `dx` selects the input
+// gradient: A = dY [n][Co], output [n][Ci], weights read transposed with the
+// tap mirrored; otherwise A = X [n][Ci], output [n][Co].
+hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
+                            const void* Wt, const void* bias, void* out, int64_t n,
+                            int Ci, int Co, hipStream_t stream);
+
+// MFMA path (bf16, K % 32 == 0 and Nout % 16 == 0 where K/Nout are the
+// contracted/produced channel counts of the pass).
+hipError_t launch_conv_mfma(bool dx, const uint16_t* A, const int32_t* N, const uint16_t* Wt,
+                            const uint16_t* bias, uint16_t* out, int64_t n, int Ci, int Co,
+                            hipStream_t stream);
+bool conv_mfma_supported(bool dx, int Ci, int Co);
+
+// dW: split-K plan, partial kernels, reduction.
+struct DwPlan {
+    bool mfma;
+    int slices;            // token slices (split-K factor)
+    int64_t slice_tokens;  // tokens per slice (multiple of the kernel's token step)
+    size_t partial_floats; // floats of dW partials in the workspace (0 when slices == 1)
+    size_t db_floats;      // floats of db partials
+};
+DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16);
+size_t dw_workspace_bytes(const DwPlan& p);
+hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t* N,
+                     const void* dY, float* dW, float* db, int64_t n, int Ci, int Co,
+                     int accumulate, void* ws, hipStream_t stream);
+
+hipError_t launch_stage_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n_rows,
+                               void* dst, int C, int elem_bytes, hipStream_t stream);
+hipError_t launch_stage_scatter(const void* src, const int32_t* rows, int64_t n_rows, void* dst,
+                                int64_t n_dst, int C, int elem_bytes, hipStream_t stream);
+
+}  // namespace svc

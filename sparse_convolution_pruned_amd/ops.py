@@ -1,0 +1,316 @@
+"""ctypes binding over libsvconv (include/svconv.h).
+
+Argument marshalling only: every function here takes torch tensors that
+already live on the GPU, checks dtype/shape/contiguity, passes raw device
+pointers plus the current HIP stream to the C entry point of the same name,
+and raises ``SvError`` on a non-OK status.  All arithmetic runs in the HIP
+kernels.  If the library is missing or cannot be loaded the first call
+raises -- there is no fallback.
+
+Layouts (row-major, contiguous), as in the C header:
+  coords int32 [n], frame_offsets int32 [T+1], N int32 [n, 9],
+  X [n, C_in], Y [n, C_out], Wt [9, C_in, C_out], bias [C_out],
+  dW fp32 [9, C_in, C_out], db fp32 [C_out].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvconv.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, 1, 2, 3, 4
+SV_ERR_COORD_RANGE, SV_ERR_DUPLICATE_COORD = 5, 6
+SV_F32, SV_BF16 = 0, 1
+SV_KERNEL_AUTO, SV_KERNEL_VALU, SV_KERNEL_MFMA = 0, 1, 2
+SV_FLAG_COORD_RANGE, SV_FLAG_DUPLICATE, SV_FLAG_BAD_OFFSETS = 1, 2, 4
+SV_PASS_FWD, SV_PASS_DX, SV_PASS_DW = 1, 2, 4
+SV_OP_FWD, SV_OP_DX, SV_OP_DW = 0, 1, 2
+
+KERNELS = {"auto": SV_KERNEL_AUTO, "valu": SV_KERNEL_VALU, "mfma": SV_KERNEL_MFMA}
+
+# Exported symbols, in header order.
+SYMBOLS = (
+    "sv_build_index", "sv_sparseconv2d_fwd", "sv_sparseconv2d_bwd_dx",
+    "sv_sparseconv2d_bwd_dw", "sv_workspace_bytes", "sv_sparseconv2d_chunked",
+    "sv_chunked_workspace_bytes", "sv_stage_gather", "sv_stage_scatter",
+    "sv_status_string", "sv_version",
+)
+
+
+class SvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class ChunkedDesc(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("C_in", ctypes.c_int32), ("C_out", ctypes.c_int32),
+        ("dtype", ctypes.c_int), ("kernel", ctypes.c_int),
+        ("chunk_frames", ctypes.c_int32),
+        ("coords", ctypes.c_void_p), ("frame_offsets", ctypes.c_void_p),
+        ("frame_offsets_host", ctypes.c_void_p),
+        ("X", ctypes.c_void_p), ("Wt", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p), ("dY", ctypes.c_void_p), ("dX", ctypes.c_void_p),
+        ("dW", ctypes.c_void_p), ("db", ctypes.c_void_p), ("err_flag", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Open libsvconv.so and declare its signatures.  torch is imported
+    first so that the library binds to the HIP runtime torch already
+    loaded (same soname)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libsvconv.so not built ({path}); run "
+                           "`python -m sparse_convolution_pruned_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    E = ctypes.c_int
+    sig = {
+        "sv_build_index": ([P, P, i32, i32, i32, i64, P, P, P, P], E),
+        "sv_sparseconv2d_fwd": ([P, P, P, P, P, i64, i32, i32, E, E, P], E),
+        "sv_sparseconv2d_bwd_dx": ([P, P, P, P, i64, i32, i32, E, E, P], E),
+        "sv_sparseconv2d_bwd_dw": ([P, P, P, P, P, i64, i32, i32, E, i32, P, sz, P], E),
+        "sv_workspace_bytes": ([E, i64, i32, i32, E], sz),
+        "sv_sparseconv2d_chunked": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32, P, sz, P], E),
+        "sv_chunked_workspace_bytes": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32], sz),
+        "sv_stage_gather": ([P, i64, P, i64, P, i32, E, P], E),
+        "sv_stage_scatter": ([P, P, i64, P, i64, i32, E, P], E),
+        "sv_status_string": ([E], ctypes.c_char_p),
+        "sv_version": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().sv_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return load().sv_version().decode()
+
+
+# ------------------------------------------------------------------ helpers
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(st: int, where: str):
+    if st != SV_OK:
+        raise SvError(st, where)
+
+
+def _kernel(kernel) -> int:
+    return KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+
+
+# ------------------------------------------------------------- entry points
+def sv_build_index(coords, frame_offsets, T, H, W, N_out, M_out=None, err_flag=None, stream=None):
+    assert coords.dtype == torch.int32 and frame_offsets.dtype == torch.int32
+    assert N_out.dtype == torch.int32 and N_out.shape == (coords.shape[0], 9)
+    assert frame_offsets.shape == (T + 1,)
+    if M_out is not None:
+        assert M_out.dtype == torch.int32 and M_out.numel() == T * H * W
+    if err_flag is not None:
+        assert err_flag.dtype == torch.int32 and err_flag.numel() >= 1
+    st = load().sv_build_index(_ptr(coords), _ptr(frame_offsets), int(T), int(H), int(W),
+                               int(coords.shape[0]), _ptr(N_out), _ptr(M_out), _ptr(err_flag),
+                               _stream(stream))
+    _check(st, "sv_build_index")
+
+
+def sv_sparseconv2d_fwd(X, N, Wt, bias, Y, kernel="auto", stream=None):
+    n, Ci = X.shape
+    Co = Wt.shape[2]
+    assert Wt.shape == (9, Ci, Co) and Y.shape == (n, Co) and N.shape == (n, 9)
+    assert X.dtype == Wt.dtype == Y.dtype and N.dtype == torch.int32
+    if bias is not None:
+        assert bias.dtype == X.dtype and bias.shape == (Co,)
+    st = load().sv_sparseconv2d_fwd(_ptr(X), _ptr(N), _ptr(Wt), _ptr(bias), _ptr(Y), n, Ci, Co,
+                                    _dt(X), _kernel(kernel), _stream(stream))
+    _check(st, "sv_sparseconv2d_fwd")
+
+
+def sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, kernel="auto", stream=None):
+    n, Co = dY.shape
+    Ci = Wt.shape[1]
+    assert Wt.shape == (9, Ci, Co) and dX.shape == (n, Ci) and N.shape == (n, 9)
+    assert dY.dtype == Wt.dtype == dX.dtype and N.dtype == torch.int32
+    st = load().sv_sparseconv2d_bwd_dx(_ptr(dY), _ptr(N), _ptr(Wt), _ptr(dX), n, Ci, Co,
+                                       _dt(dY), _kernel(kernel), _stream(stream))
+    _check(st, "sv_sparseconv2d_bwd_dx")
+
+
+def sv_workspace_bytes(op, n, C_in, C_out, dtype) -> int:
+    dt = SV_BF16 if dtype in (torch.bfloat16, SV_BF16, "bf16") else SV_F32
+    return int(load().sv_workspace_bytes(int(op), int(n), int(C_in), int(C_out), dt))
+
+
+def sv_sparseconv2d_bwd_dw(X, N, dY, dW, db=None, accumulate=False, workspace=None, stream=None):
+    n, Ci = X.shape
+    Co = dY.shape[1]
+    assert dY.shape[0] == n and N.shape == (n, 9) and dW.shape == (9, Ci, Co)
+    assert dW.dtype == torch.float32 and X.dtype == dY.dtype
+    if db is not None:
+        assert db.dtype == torch.float32 and db.shape == (Co,)
+    need = sv_workspace_bytes(SV_OP_DW, n, Ci, Co, X.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_sparseconv2d_bwd_dw(_ptr(X), _ptr(N), _ptr(dY), _ptr(dW), _ptr(db), n, Ci, Co,
+                                       _dt(X), 1 if accumulate else 0, _ptr(workspace), wsb,
+                                       _stream(stream))
+    _check(st, "sv_sparseconv2d_bwd_dw")
+
+
+def make_chunked_desc(T, H, W, coords, frame_offsets, frame_offsets_host, C_in, C_out, dtype,
+                      chunk_frames, X=None, Wt=None, bias=None, Y=None, dY=None, dX=None,
+                      dW=None, db=None, err_flag=None, kernel="auto"):
+    """Build the descriptor; `frame_offsets_host` must be a CPU int32 tensor
+    (kept referenced by the returned object)."""
+    assert frame_offsets_host.device.type == "cpu" and frame_offsets_host.dtype == torch.int32
+    fh = frame_offsets_host.contiguous()
+    d = ChunkedDesc()
+    d.T, d.H, d.W, d.C_in, d.C_out = int(T), int(H), int(W), int(C_in), int(C_out)
+    d.dtype = SV_BF16 if dtype == torch.bfloat16 else SV_F32
+    d.kernel = _kernel(kernel)
+    d.chunk_frames = int(chunk_frames)
+    d.coords, d.frame_offsets = _ptr(coords), _ptr(frame_offsets)
+    d.frame_offsets_host = fh.data_ptr()
+    d.X, d.Wt, d.bias, d.Y = _ptr(X), _ptr(Wt), _ptr(bias), _ptr(Y)
+    d.dY, d.dX, d.dW, d.db, d.err_flag = _ptr(dY), _ptr(dX), _ptr(dW), _ptr(db), _ptr(err_flag)
+    d._keep = (fh, coords, frame_offsets, X, Wt, bias, Y, dY, dX, dW, db, err_flag)
+    return d
+
+
+def sv_chunked_workspace_bytes(desc: ChunkedDesc, passes: int) -> int:
+    return int(load().sv_chunked_workspace_bytes(ctypes.byref(desc), ctypes.c_uint32(passes)))
+
+
+def sv_sparseconv2d_chunked(desc: ChunkedDesc, passes: int, workspace=None, stream=None):
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_sparseconv2d_chunked(ctypes.byref(desc), ctypes.c_uint32(passes),
+                                        _ptr(workspace), wsb, _stream(stream))
+    _check(st, "sv_sparseconv2d_chunked")
+
+
+def sv_stage_gather(src, rows, dst, stream=None):
+    C = src.shape[1]
+    assert rows.dtype == torch.int32 and dst.shape == (rows.shape[0], C) and dst.dtype == src.dtype
+    st = load().sv_stage_gather(_ptr(src), src.shape[0], _ptr(rows), rows.shape[0], _ptr(dst), C,
+                                _dt(src), _stream(stream))
+    _check(st, "sv_stage_gather")
+
+
+def sv_stage_scatter(src, rows, dst, stream=None):
+    C = src.shape[1]
+    assert rows.dtype == torch.int32 and dst.shape[1] == C and dst.dtype == src.dtype
+    st = load().sv_stage_scatter(_ptr(src), _ptr(rows), rows.shape[0], _ptr(dst), dst.shape[0], C,
+                                 _dt(src), _stream(stream))
+    _check(st, "sv_stage_scatter")
+
+
+# ---------------------------------------------------------- conveniences
+def build_index(coords, frame_offsets, T, H, W, with_map=False, check=True, stream=None):
+    """Allocate and fill N (and M); with `check`, synchronise and raise on a
+    coordinate error reported by the device flag."""
+    n = coords.shape[0]
+    N = torch.empty((n, 9), dtype=torch.int32, device=coords.device)
+    M = torch.empty((T, H, W), dtype=torch.int32, device=coords.device) if with_map else None
+    flag = torch.zeros(1, dtype=torch.int32, device=coords.device)
+    sv_build_index(coords, frame_offsets, T, H, W, N, M, flag, stream)
+    if check:
+        f = int(flag.item())
+        if f & SV_FLAG_BAD_OFFSETS:
+            raise SvError(SV_ERR_INVALID_ARG, "sv_build_index (frame offsets)")
+        if f & SV_FLAG_COORD_RANGE:
+            raise SvError(SV_ERR_COORD_RANGE, "sv_build_index")
+        if f & SV_FLAG_DUPLICATE:
+            raise SvError(SV_ERR_DUPLICATE_COORD, "sv_build_index")
+    return (N, M) if with_map else N
+
+
+def sparseconv2d_fwd(X, N, Wt, bias=None, kernel="auto"):
+    Y = torch.empty((X.shape[0], Wt.shape[2]), dtype=X.dtype, device=X.device)
+    sv_sparseconv2d_fwd(X, N, Wt, bias, Y, kernel)
+    return Y
+
+
+def sparseconv2d_bwd_dx(dY, N, Wt, kernel="auto"):
+    dX = torch.empty((dY.shape[0], Wt.shape[1]), dtype=dY.dtype, device=dY.device)
+    sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, kernel)
+    return dX
+
+
+def sparseconv2d_bwd_dw(X, N, dY, with_db=True, workspace=None):
+    Ci, Co = X.shape[1], dY.shape[1]
+    dW = torch.empty((9, Ci, Co), dtype=torch.float32, device=X.device)
+    db = torch.empty((Co,), dtype=torch.float32, device=X.device) if with_db else None
+    sv_sparseconv2d_bwd_dw(X, N, dY, dW, db, False, workspace)
+    return dW, db
+
+
+class SparseConv2dFunction(torch.autograd.Function):
+    """autograd wrapper: forward via sv_sparseconv2d_fwd, backward via
+    sv_sparseconv2d_bwd_dx and sv_sparseconv2d_bwd_dw (gradients of Wt and
+    bias returned in the parameters' dtype)."""
+
+    @staticmethod
+    def forward(ctx, X, N, Wt, bias=None, kernel="auto"):
+        ctx.save_for_backward(X, N, Wt)
+        ctx.kernel = kernel
+        ctx.has_bias = bias is not None
+        return sparseconv2d_fwd(X.contiguous(), N, Wt.contiguous(),
+                                None if bias is None else bias.contiguous(), kernel)
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, N, Wt = ctx.saved_tensors
+        dY = dY.contiguous()
+        dX = sparseconv2d_bwd_dx(dY, N, Wt, ctx.kernel) if ctx.needs_input_grad[0] else None
+        dW = db = None
+        if ctx.needs_input_grad[2] or (ctx.has_bias and ctx.needs_input_grad[3]):
+            dW, db = sparseconv2d_bwd_dw(X, N, dY, with_db=ctx.has_bias)
+            dW = dW.to(Wt.dtype)
+            db = None if db is None else db.to(Wt.dtype)
+        return dX, None, dW, db, None
+
+
+def sparseconv2d(X, N, Wt, bias=None, kernel="auto"):
+    return SparseConv2dFunction.apply(X, N, Wt, bias, kernel)

@@ -1,0 +1,133 @@
+"""The C-ABI library on the CPU: it loads, exports every function
+include/svconv.h declares, and its host-only logic (argument validation,
+workspace sizing, status strings) behaves as documented.  No call here
+reaches the GPU: every call returns before any HIP work is enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_convolution_pruned_amd import ops, workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svconv.h")
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_convolution_pruned_amd import build
+    if not os.path.exists(ops.LIB_PATH):
+        build.build()
+    return ops.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in svconv.h but not exported"
+    assert sorted(ops.SYMBOLS) == names, "binding symbol list differs from the header"
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = ops.status_string(code)
+        assert s.startswith("SV_"), s
+    assert "unknown" in ops.status_string(99)
+    assert ops.version().startswith("svconv") and "gfx950" in ops.version()
+
+
+def test_validation_without_device(lib):
+    F32, BF16 = ops.SV_F32, ops.SV_BF16
+    # negative n, zero channels, bad dtype, bad kernel enum
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, -1, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 0, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 4, 4, 7, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 4, 4, F32, 9, None) == ops.SV_ERR_INVALID_ARG
+    # null required pointers
+    assert lib.sv_sparseconv2d_fwd(None, FAKE, FAKE, None, FAKE, 8, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_bwd_dx(FAKE, None, FAKE, FAKE, 8, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    # MFMA forced where it does not fit: fp32, or channels not multiples of 32/16
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 64, F32, 2, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 48, 64, BF16, 2, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, 8, 64, 40, BF16, 2, None) == ops.SV_ERR_UNSUPPORTED
+    # grid larger than the LDS map
+    assert lib.sv_build_index(FAKE, FAKE, 1, 129, 128, 1, FAKE, None, None, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_build_index(FAKE, None, 1, 4, 4, 1, FAKE, None, None, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_build_index(FAKE, FAKE, -1, 4, 4, 1, FAKE, None, None, None) == ops.SV_ERR_INVALID_ARG
+    # dW workspace missing / too small
+    need = lib.sv_workspace_bytes(ops.SV_OP_DW, 22656, 256, 256, BF16)
+    assert need > 0
+    assert lib.sv_sparseconv2d_bwd_dw(FAKE, FAKE, FAKE, FAKE, None, 22656, 256, 256, BF16, 0,
+                                      None, 0, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_sparseconv2d_bwd_dw(FAKE, FAKE, FAKE, FAKE, None, 22656, 256, 256, BF16, 0,
+                                      FAKE, need - 1, None) == ops.SV_ERR_WORKSPACE
+    # stage copies
+    assert lib.sv_stage_gather(FAKE, 10, FAKE, 5, FAKE, 0, BF16, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_stage_scatter(FAKE, FAKE, -1, FAKE, 10, 4, BF16, None) == ops.SV_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(lib):
+    assert lib.sv_workspace_bytes(ops.SV_OP_FWD, 1000, 64, 64, ops.SV_BF16) == 0
+    assert lib.sv_workspace_bytes(ops.SV_OP_DX, 1000, 64, 64, ops.SV_BF16) == 0
+    assert lib.sv_workspace_bytes(ops.SV_OP_DW, -1, 64, 64, ops.SV_BF16) == 0
+    # bounded: never more than 64 slices of partials plus db partials
+    for n, C in [(0, 64), (100, 64), (22656, 256), (22656, 512), (181248, 128), (10 ** 7, 256)]:
+        b = lib.sv_workspace_bytes(ops.SV_OP_DW, n, C, C, ops.SV_BF16)
+        assert b <= 64 * 9 * C * C * 4 + 64 * C * 4 + 512
+
+
+def _desc(T, offs_h, C=128, chunk=256):
+    d = ops.ChunkedDesc()
+    d.T, d.H, d.W, d.C_in, d.C_out = T, 14, 14, C, C
+    d.dtype, d.kernel, d.chunk_frames = ops.SV_BF16, ops.SV_KERNEL_AUTO, chunk
+    d.frame_offsets_host = offs_h.ctypes.data
+    return d
+
+
+def test_chunked_workspace_flat_in_T(lib):
+    """The chunk driver's workspace depends on the largest chunk, not on the
+    video length: 256 frames and 3072 frames need the same bytes."""
+    passes = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
+    sizes = []
+    for T in (256, 768, 3072):
+        offs = (np.arange(T + 1, dtype=np.int32) * 59).astype(np.int32)
+        d = _desc(T, offs)
+        sizes.append(lib.sv_chunked_workspace_bytes(ctypes.byref(d), passes))
+    assert sizes[0] > 0 and sizes[0] == sizes[1] == sizes[2]
+    # bad descriptors: decreasing offsets, zero chunk size
+    offs = np.array([0, 5, 3], dtype=np.int32)
+    assert lib.sv_chunked_workspace_bytes(ctypes.byref(_desc(2, offs)), passes) == 0
+    offs = np.array([0, 5, 9], dtype=np.int32)
+    assert lib.sv_chunked_workspace_bytes(ctypes.byref(_desc(2, offs, chunk=0)), passes) == 0
+    assert lib.sv_sparseconv2d_chunked(ctypes.byref(_desc(2, offs, chunk=0)), passes, None, 0, None) \
+        == ops.SV_ERR_INVALID_ARG
+
+
+def test_workloads_shapes():
+    """The synthetic workloads have the sizes the configurations state."""
+    assert wl.make_layer("c1").n == 98
+    L = wl.make_layer("c2", scale_T=8)
+    assert np.all(np.diff(L.frame_offsets) == 78)
+    L = wl.make_layer("c3a", scale_T=8)
+    assert np.all(np.diff(L.frame_offsets) == 59)
+    x = L.X.view(np.uint32)
+    assert np.all((x & 0xFFFF) == 0), "bf16 inputs must be bf16-representable"
+    S = wl.make_staged("c5", scale_T=16)
+    c = [np.diff(s["frame_offsets"]) for s in S.stages]
+    assert np.all(c[0] >= 128) and np.all(c[0] <= 180)
+    assert np.all(c[1] <= c[0]) and np.all(c[2] <= c[1])
+    # nesting: stage s+1 coordinates are a subset of stage s, per frame
+    for s in (1, 2):
+        prev, cur = S.stages[s - 1], S.stages[s]
+        assert np.array_equal(prev["coords"][cur["sel"]], cur["coords"])

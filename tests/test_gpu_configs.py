@@ -1,0 +1,183 @@
+"""The five workloads at full size, in the launch configuration the
+benchmark times, against the oracle.
+
+c1 and c2 are compared element by element on every output; c3a/c3b/c4/c5
+on sampled output rows (first/last rows, tile boundaries and random rows;
+for dW a set of (tap, input channel) rows, each a sum over all tokens), which
+the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_convolution_pruned_amd import ops, workloads as wl
+from tests.gpu_util import assert_close, dev, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_layer(L, kernel="auto", passes=("fwd", "dx", "dw")):
+    dt = torch.bfloat16 if L.dtype == "bf16" else torch.float32
+    coords, offs = dev(L.coords), dev(L.frame_offsets)
+    N = ops.build_index(coords, offs, L.T, L.H, L.W)
+    X, Wt, b, dY = dev(L.X, dt), dev(L.Wt, dt), dev(L.b, dt), dev(L.dY, dt)
+    out = {"N": N}
+    if "fwd" in passes:
+        out["Y"] = ops.sparseconv2d_fwd(X, N, Wt, b, kernel)
+    if "dx" in passes:
+        out["dX"] = ops.sparseconv2d_bwd_dx(dY, N, Wt, kernel)
+    if "dw" in passes:
+        out["dW"], out["db"] = ops.sparseconv2d_bwd_dw(X, N, dY)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}
+
+
+def dw_rows(Ci, seed=0, count=48):
+    rng = np.random.default_rng(seed)
+    fixed = [0, Ci - 1, 4 * Ci, 4 * Ci + Ci - 1, 9 * Ci - 1, 8 * Ci]
+    return np.unique(np.array(fixed + list(rng.choice(9 * Ci, size=count, replace=False)))).astype(np.int64)
+
+
+def test_c1_full():
+    L = wl.make_layer("c1")
+    st, Nr, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    g = gpu_layer(L)
+    assert np.array_equal(g["N"], Nr)
+    assert_close(g["Y"], O.fwd(L.X, Nr, L.Wt, L.b), "f32", "c1 Y")
+    assert_close(g["dX"], O.bwd_dx(L.dY, Nr, L.Wt), "f32", "c1 dX")
+    assert_close(g["dW"], O.bwd_dw(L.X, Nr, L.dY), "f32", "c1 dW")
+    assert_close(g["db"], O.bwd_db(L.dY), "f32", "c1 db")
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+def test_c2_full(kernel):
+    L = wl.make_layer("c2")
+    st, Nr, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    g = gpu_layer(L, kernel, passes=("fwd",))
+    assert np.array_equal(g["N"], Nr)
+    assert_close(g["Y"], O.fwd(L.X, Nr, L.Wt, L.b), "bf16", f"c2 Y ({kernel})")
+
+
+@pytest.mark.parametrize("key", ["c3a", "c3b"])
+def test_c3_sampled(key):
+    L = wl.make_layer(key)
+    print(f"config {key} n={L.n}", flush=True)
+    st, Nr, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    g = gpu_layer(L)
+    assert np.array_equal(g["N"], Nr)
+    rows = sample_rows(L.n, 384, seed=1)
+    assert_close(g["Y"][rows], O.fwd_rows(L.X, Nr, L.Wt, L.b, rows), "bf16", f"{key} Y")
+    assert_close(g["dX"][rows], O.bwd_dx_rows(L.dY, Nr, L.Wt, rows), "bf16", f"{key} dX")
+    Ci = L.X.shape[1]
+    ji = dw_rows(Ci, seed=2)
+    assert_close(g["dW"].reshape(9 * Ci, -1)[ji], O.bwd_dw_rows(L.X, Nr, L.dY, ji), "bf16", f"{key} dW")
+    assert_close(g["db"], O.bwd_db(L.dY), "bf16", f"{key} db")
+
+
+def test_c4_chunked():
+    """Chunks of 256 frames through sv_sparseconv2d_chunked: equal to the
+    unchunked kernels (Y, dX bit for bit; dW within tolerance) and to the
+    oracle on sampled rows; the workspace does not grow with T."""
+    L = wl.make_layer("c4")
+    dt = torch.bfloat16
+    coords, offs = dev(L.coords), dev(L.frame_offsets)
+    X, Wt, b, dY = dev(L.X, dt), dev(L.Wt, dt), dev(L.b, dt), dev(L.dY, dt)
+    n, C = L.n, L.X.shape[1]
+    Y = torch.empty((n, C), dtype=dt, device="cuda")
+    dX = torch.empty((n, C), dtype=dt, device="cuda")
+    dW = torch.empty((9, C, C), dtype=torch.float32, device="cuda")
+    db = torch.empty((C,), dtype=torch.float32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    offs_h = torch.from_numpy(L.frame_offsets.copy())
+    d = ops.make_chunked_desc(L.T, L.H, L.W, coords, offs, offs_h, C, C, dt, 256, X=X, Wt=Wt,
+                              bias=b, Y=Y, dY=dY, dX=dX, dW=dW, db=db, err_flag=flag)
+    passes = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
+    wsb = ops.sv_chunked_workspace_bytes(d, passes)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ops.sv_sparseconv2d_chunked(d, passes, ws)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    # workspace is sized by one chunk: the same for the first 256 frames alone
+    Ls = wl.make_layer("c4", scale_T=256)
+    d1 = ops.make_chunked_desc(256, L.H, L.W, coords, offs, torch.from_numpy(Ls.frame_offsets.copy()),
+                               C, C, dt, 256)
+    assert wsb <= ops.sv_chunked_workspace_bytes(d1, passes) * 1.25 + (1 << 20)
+
+    g = gpu_layer(L)   # unchunked
+    assert np.array_equal(host(Y), g["Y"])
+    assert np.array_equal(host(dX), g["dX"])
+    assert_close(host(dW), g["dW"], "bf16", "c4 chunked vs unchunked dW")
+    st, Nr, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    assert np.array_equal(g["N"], Nr)
+    rows = sample_rows(n, 384, seed=3)
+    assert_close(host(Y)[rows], O.fwd_rows(L.X, Nr, L.Wt, L.b, rows), "bf16", "c4 Y")
+    assert_close(host(dX)[rows], O.bwd_dx_rows(L.dY, Nr, L.Wt, rows), "bf16", "c4 dX")
+    ji = dw_rows(C, seed=4, count=24)
+    assert_close(host(dW).reshape(9 * C, -1)[ji], O.bwd_dw_rows(L.X, Nr, L.dY, ji), "bf16", "c4 dW")
+    assert_close(host(db), O.bwd_db(L.dY), "bf16", "c4 db")
+
+
+def test_c5_staged():
+    """Three nested stages, two layers each, forward then backward through
+    all six layers.  Each layer is graded with teacher forcing: the oracle
+    takes the GPU's own bf16 input of that layer.  Index tables bit-exact;
+    stage gathers and scatters bit-exact."""
+    S = wl.make_staged("c5")
+    dt = torch.bfloat16
+    C = S.X0.shape[1]
+    Ns, Nh = [], []
+    for stg in S.stages:
+        Ns.append(ops.build_index(dev(stg["coords"]), dev(stg["frame_offsets"]), S.T, S.H, S.W))
+        st, Nr, _ = O.build_index(stg["coords"], stg["frame_offsets"], S.T, S.H, S.W)
+        assert np.array_equal(host(Ns[-1]), Nr)
+        Nh.append(Nr)
+    Ws = [dev(w, dt) for w in S.weights]
+    bs = [dev(b, dt) for b in S.biases]
+    sels = [None] + [dev(stg["sel"]) for stg in S.stages[1:]]
+    L = len(S.weights)
+    stage_of = [l // S.layers_per_stage for l in range(L)]
+    # forward
+    xs = []
+    x = dev(S.X0, dt)
+    for l in range(L):
+        s = stage_of[l]
+        if l > 0 and stage_of[l - 1] != s:
+            xn = torch.empty((sels[s].shape[0], C), dtype=dt, device="cuda")
+            ops.sv_stage_gather(x, sels[s], xn)
+            assert np.array_equal(host(xn), host(x)[S.stages[s]["sel"]])
+            x = xn
+        xs.append(x)
+        x = ops.sparseconv2d_fwd(x, Ns[s], Ws[l], bs[l])
+    # backward
+    g = dev(S.dY_last, dt)
+    gys = [None] * L
+    dWs = [None] * L
+    for l in reversed(range(L)):
+        s = stage_of[l]
+        gys[l] = g
+        dWs[l], _ = ops.sparseconv2d_bwd_dw(xs[l], Ns[s], g, with_db=False)
+        g = ops.sparseconv2d_bwd_dx(g, Ns[s], Ws[l])
+        if l > 0 and stage_of[l - 1] != s:
+            prev_n = S.stages[s - 1]["coords"].shape[0]
+            gp = torch.empty((prev_n, C), dtype=dt, device="cuda")
+            ops.sv_stage_scatter(g, sels[s], gp)
+            exp = np.zeros((prev_n, C), np.float32)
+            exp[S.stages[s]["sel"]] = host(g)
+            assert np.array_equal(host(gp), exp)
+            g = gp
+    torch.cuda.synchronize()
+    # teacher-forced per-layer checks on sampled rows
+    for l in range(L):
+        s = stage_of[l]
+        xin, gin = host(xs[l]), host(gys[l])
+        y = host(xs[l + 1]) if l + 1 < L and stage_of[l + 1] == s else None
+        rows = sample_rows(xin.shape[0], 128, seed=10 + l)
+        yl = host(ops.sparseconv2d_fwd(xs[l], Ns[s], Ws[l], bs[l]))
+        assert_close(yl[rows], O.fwd_rows(xin, Nh[s], S.weights[l], S.biases[l], rows), "bf16", f"layer {l} Y")
+        if y is not None:
+            assert np.array_equal(y, yl)
+        dxl = host(ops.sparseconv2d_bwd_dx(gys[l], Ns[s], Ws[l]))
+        assert_close(dxl[rows], O.bwd_dx_rows(gin, Nh[s], S.weights[l], rows), "bf16", f"layer {l} dX")
+        ji = dw_rows(C, seed=20 + l, count=12)
+        assert_close(host(dWs[l]).reshape(9 * C, -1)[ji], O.bwd_dw_rows(xin, Nh[s], gin, ji), "bf16",
+                     f"layer {l} dW")

@@ -1,0 +1,158 @@
+"""SparseConv2D kernels (fwd, dX, dW, db) against the oracle on small and
+ragged cases: fp32 and bf16, VALU and MFMA kernels, the LDS-window and the
+gather staging modes of the MFMA kernel, empty inputs, determinism."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_convolution_pruned_amd import ops, workloads as wl
+from tests.gpu_util import assert_close, dev, host, tdtype
+
+pytestmark = pytest.mark.gpu
+
+
+def run_all(L, N, kernel, with_bias=True):
+    dt = tdtype(L.dtype)
+    X, Wt, dY = dev(L.X, dt), dev(L.Wt, dt), dev(L.dY, dt)
+    b = dev(L.b, dt) if with_bias else None
+    Nd = dev(N)
+    Y = ops.sparseconv2d_fwd(X, Nd, Wt, b, kernel)
+    dX = ops.sparseconv2d_bwd_dx(dY, Nd, Wt, kernel)
+    dW, db = ops.sparseconv2d_bwd_dw(X, Nd, dY)
+    torch.cuda.synchronize()
+    return host(Y), host(dX), host(dW), host(db)
+
+
+def check_against_oracle(L, N, kernel, with_bias=True, what=""):
+    Y, dX, dW, db = run_all(L, N, kernel, with_bias)
+    b = L.b if with_bias else None
+    assert_close(Y, O.fwd(L.X, N, L.Wt, b), L.dtype, f"{what} Y")
+    assert_close(dX, O.bwd_dx(L.dY, N, L.Wt), L.dtype, f"{what} dX")
+    assert_close(dW, O.bwd_dw(L.X, N, L.dY), L.dtype, f"{what} dW")
+    assert_close(db, O.bwd_db(L.dY), L.dtype, f"{what} db")
+
+
+# (seed, T, H, W, keep, Ci, Co, shuffle)
+F32_CASES = [
+    (1, 1, 14, 14, 0.5, 64, 64, False),
+    (2, 3, 6, 7, 0.4, 1, 1, True),
+    (3, 2, 9, 5, 0.8, 3, 17, False),
+    (4, 4, 14, 14, [0, 1, 196, 60], 65, 33, True),
+    (5, 2, 16, 16, 0.3, 17, 130, False),
+    (6, 1, 1, 1, 1.0, 8, 8, False),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: f"seed{c[0]}")
+def test_f32_valu(case):
+    seed, T, H, W, keep, Ci, Co, sh = case
+    L = wl.make_random_case(seed, T, H, W, keep, Ci, Co, "f32", shuffle=sh)
+    print(f"case {case} n={L.n}", flush=True)
+    st, N, _ = O.build_index(L.coords, L.frame_offsets, T, H, W)
+    check_against_oracle(L, N, "valu", what=f"f32 {case}")
+
+
+BF16_CASES = [
+    # MFMA-compatible channel counts (C_in % 32, C_out % 16 and the reverse for dX)
+    (11, 3, 14, 14, 0.4, 128, 128, False),
+    (12, 5, 14, 14, 0.3, 64, 96, False),
+    (13, 2, 16, 16, 0.6, 96, 64, True),       # shuffled packing: wide windows -> gather mode
+    (14, 9, 14, 14, [0, 1, 2, 196, 0, 77, 5, 196, 33], 256, 128, False),
+    (15, 1, 40, 40, 0.9, 32, 32, True),       # 1440 shuffled tokens in one frame
+    (16, 2, 14, 14, 0.3, 160, 64, False),     # K tail of 32 channels after full 64-chunks
+]
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: f"seed{c[0]}")
+def test_bf16(case, kernel):
+    seed, T, H, W, keep, Ci, Co, sh = case
+    L = wl.make_random_case(seed, T, H, W, keep, Ci, Co, "bf16", shuffle=sh)
+    print(f"case {case} kernel={kernel} n={L.n}", flush=True)
+    st, N, _ = O.build_index(L.coords, L.frame_offsets, T, H, W)
+    check_against_oracle(L, N, kernel, what=f"bf16 {kernel} {case}")
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_arbitrary_table_gather_mode(kernel):
+    """Any N with entries in [-1, n) is a valid table for the kernels; random
+    far-apart rows force the MFMA kernel out of its window mode."""
+    rng = np.random.default_rng(7)
+    n, Ci, Co = 1000, 64, 64
+    L = wl.make_random_case(17, 1, 40, 40, [n], Ci, Co, "bf16")
+    N = rng.integers(-1, n, size=(n, 9)).astype(np.int32)
+    N[rng.random((n, 9)) < 0.2] = -1
+    check_against_oracle(L, N, kernel, what=f"random-N {kernel}")
+
+
+def test_out_of_range_entries_read_as_padding():
+    """Entries >= n or < -1 contribute nothing (never read out of bounds)."""
+    L = wl.make_random_case(18, 1, 14, 14, 0.5, 64, 64, "bf16")
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, 1, 14, 14)
+    Nbad = N.copy()
+    Nbad[::3, 0] = L.n + 5
+    Nbad[1::3, 8] = -7
+    Nclean = Nbad.copy()
+    Nclean[(Nclean >= L.n) | (Nclean < -1)] = -1
+    for kernel in ("valu", "mfma"):
+        Y, dX, dW, db = run_all(L, Nbad, kernel)
+        assert_close(Y, O.fwd(L.X, Nclean, L.Wt, L.b), "bf16", "Y")
+        assert_close(dX, O.bwd_dx(L.dY, Nclean, L.Wt), "bf16", "dX")
+        assert_close(dW, O.bwd_dw(L.X, Nclean, L.dY), "bf16", "dW")
+
+
+def test_mfma_and_valu_agree():
+    L = wl.make_random_case(19, 4, 14, 14, 0.4, 128, 128, "bf16")
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    a = run_all(L, N, "mfma")
+    b = run_all(L, N, "valu")
+    for x, y, nm in zip(a, b, ("Y", "dX")):
+        assert_close(x, y, "bf16", f"mfma vs valu {nm}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_empty_input(dt):
+    L = wl.make_random_case(20, 2, 5, 5, 0.0, 64, 64, dt)
+    assert L.n == 0
+    N = np.zeros((0, 9), np.int32)
+    Y, dX, dW, db = run_all(L, N, "auto")
+    assert Y.shape == (0, 64) and dX.shape == (0, 64)
+    assert np.all(dW == 0) and np.all(db == 0)
+
+
+def test_dw_accumulate():
+    L = wl.make_random_case(21, 3, 14, 14, 0.5, 128, 128, "bf16")
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    X, dY, Nd = dev(L.X, torch.bfloat16), dev(L.dY, torch.bfloat16), dev(N)
+    dW = torch.ones((9, 128, 128), dtype=torch.float32, device="cuda")
+    db = torch.ones(128, dtype=torch.float32, device="cuda")
+    ops.sv_sparseconv2d_bwd_dw(X, Nd, dY, dW, db, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close(host(dW), O.bwd_dw(L.X, N, L.dY) + 1.0, "bf16", "dW accumulate")
+    assert_close(host(db), O.bwd_db(L.dY) + 1.0, "bf16", "db accumulate")
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_deterministic(kernel):
+    L = wl.make_random_case(22, 6, 14, 14, 0.5, 128, 128, "bf16")
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    a = run_all(L, N, kernel)
+    b = run_all(L, N, kernel)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_autograd_function():
+    L = wl.make_random_case(23, 2, 14, 14, 0.5, 64, 64, "bf16")
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    X = dev(L.X, torch.bfloat16).requires_grad_(True)
+    Wt = dev(L.Wt, torch.float32).to(torch.bfloat16).requires_grad_(True)
+    b = dev(L.b, torch.bfloat16).requires_grad_(True)
+    Y = ops.sparseconv2d(X, dev(N), Wt, b)
+    Y.backward(dev(L.dY, torch.bfloat16))
+    torch.cuda.synchronize()
+    assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), "bf16", "Y")
+    assert_close(host(X.grad), O.bwd_dx(L.dY, N, L.Wt), "bf16", "dX")
+    assert_close(host(Wt.grad), O.bwd_dw(L.X, N, L.dY), "bf16", "dW")
+    assert_close(host(b.grad), O.bwd_db(L.dY), "bf16", "db")
