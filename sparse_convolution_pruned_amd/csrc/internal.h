@@ -59,6 +59,19 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 in[8], uint4 out[8]
     }
 }
 
+// Workgroups of a 1-D grid go to the 8 XCDs of the chip round-robin by
+// linear id, and each XCD has its own L2.  This maps the linear id to a
+// logical tile id so that every XCD receives one contiguous range of logical
+// tiles, in order: tiles that share inputs (neighbouring token ranges, the
+// output-channel tiles of one token range) then run on the same XCD at about
+// the same time and meet their shared rows in its L2.  Bijective on [0, count).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int linear, int count) {
+    const int xcd = linear % kXcds, local = linear / kXcds;
+    const int base = count / kXcds, extra = count % kXcds;
+    return xcd * base + min(xcd, extra) + local;
+}
+
 // ---------------------------------------------------------------- launchers
 // Every launcher enqueues on `stream` and returns hipGetLastError().
 
