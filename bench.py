@@ -98,6 +98,8 @@ class StagedRun:
         self.db = [torch.empty((C,), dtype=torch.float32, device="cuda") for _ in range(self.L)]
         wsb = max(ops.sv_workspace_bytes(ops.SV_OP_DW, n, C, C, bf) for n in self.ns)
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+        self.fws = torch.empty(max(256, ops.sv_workspace_bytes(ops.SV_OP_FWD, 0, C, C, bf)),
+                               dtype=torch.uint8, device="cuda")
 
     def flops(self):
         """Effective FLOPs per step: 2 * n * 9 * C_in * C_out per pass, all
@@ -120,7 +122,8 @@ class StagedRun:
                 ops.sv_stage_gather(self.ys[l - 1], self.sels[s], self.xs[l])
                 rec("gather", t, units=self.ns[s])
             t = rec("fwd", None)
-            ops.sv_sparseconv2d_fwd(self.xs[l], self.N[s], self.W[l], self.b[l], self.ys[l], kern)
+            ops.sv_sparseconv2d_fwd(self.xs[l], self.N[s], self.W[l], self.b[l], self.ys[l], kern,
+                                    workspace=self.fws)
             rec("fwd", t, units=self.ns[s])
         g = self.dy_last
         for l in reversed(range(self.L)):
@@ -259,10 +262,12 @@ def layer_workload(args):
     else:
         ws = torch.empty(max(256, ops.sv_workspace_bytes(ops.SV_OP_DW, n, C, C, bf)), dtype=torch.uint8,
                          device="cuda")
+        fws = torch.empty(max(256, ops.sv_workspace_bytes(ops.SV_OP_FWD, n, C, C, bf)), dtype=torch.uint8,
+                          device="cuda")
 
         def step():
             ops.sv_build_index(coords, offs, L.T, L.H, L.W, N)
-            ops.sv_sparseconv2d_fwd(X, N, Wt, b, Y, args.kernel)
+            ops.sv_sparseconv2d_fwd(X, N, Wt, b, Y, args.kernel, workspace=fws)
             if "dx" in passes:
                 ops.sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, args.kernel)
             if "dw" in passes:

@@ -101,11 +101,17 @@ sv_status sv_build_index(const int32_t *coords, const int32_t *frame_offsets,
  * + bias[o]; entries of N that are -1 (or outside [0, n)) contribute zero.
  *   X [n][C_in], N [n][9], Wt [9][C_in][C_out], bias [C_out] nullable,
  *   Y [n][C_out] written; all device, all in `dtype` except N.
- * SV_ERR_UNSUPPORTED if `kernel` is MFMA and the shape/dtype does not fit it. */
+ *   workspace: device, 16-byte aligned, at least
+ *   sv_workspace_bytes(SV_OP_FWD, ...) bytes (0 unless the bf16 matrix-core
+ *   kernel can run; it receives the weights repacked per tap as
+ *   [tap][C_out][C_in]); contents are scratch.
+ * SV_ERR_UNSUPPORTED if `kernel` is MFMA and the shape/dtype does not fit it;
+ * SV_ERR_WORKSPACE if the MFMA kernel runs and the workspace is short. */
 sv_status sv_sparseconv2d_fwd(const void *X, const int32_t *N, const void *Wt,
                               const void *bias, void *Y, int64_t n,
                               int32_t C_in, int32_t C_out, sv_dtype dtype,
-                              sv_kernel kernel, hipStream_t stream);
+                              sv_kernel kernel, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /* Input gradient (the adjoint of the forward sum, written as gathers thanks
  * to the mirrored offsets: token m is tap j of k exactly when k is tap 8-j
@@ -130,8 +136,9 @@ sv_status sv_sparseconv2d_bwd_dw(const void *X, const int32_t *N, const void *dY
                                  void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
-/* Workspace bytes an operation needs for these sizes (0 for FWD and DX).
- * Depends only on its arguments, never on the device. */
+/* Workspace bytes an operation needs for these sizes (FWD: the repacked
+ * weights of the bf16 matrix-core kernel, else 0; DX: 0; DW: token-slice
+ * partials).  Depends only on its arguments, never on the device. */
 size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype);
 
 /* Chunked execution over whole frames (Key Design 2's chunking): the frames

@@ -32,17 +32,17 @@ sv_status conv_args_ok(int64_t n, int32_t Ci, int32_t Co, sv_dtype dt, sv_kernel
     return SV_OK;
 }
 
-sv_status run_fwd(const void* X, const int32_t* N, const void* Wt, const void* bias, void* Y,
-                  int64_t n, int32_t Ci, int32_t Co, sv_dtype dt, sv_kernel kernel, hipStream_t s) {
-    bool mfma = false;
-    sv_status st = choose(kernel, dt, false, Ci, Co, &mfma);
-    if (st != SV_OK) return st;
+// Forward with the repacked weights already in `V` (MFMA path) or straight
+// from Wt (VALU path).
+sv_status run_fwd_prepared(bool mfma, const void* X, const int32_t* N, const void* Wt, const void* V,
+                           const void* bias, void* Y, int64_t n, int32_t Ci, int32_t Co, sv_dtype dt,
+                           hipStream_t s) {
     if (n == 0) return SV_OK;
     if (mfma)
-        return hip_status(launch_conv_mfma(false, static_cast<const uint16_t*>(X), N,
-                                           static_cast<const uint16_t*>(Wt),
-                                           static_cast<const uint16_t*>(bias),
-                                           static_cast<uint16_t*>(Y), n, Ci, Co, s));
+        return hip_status(launch_conv_mfma_packed(static_cast<const uint16_t*>(X), N,
+                                                  static_cast<const uint16_t*>(V),
+                                                  static_cast<const uint16_t*>(bias),
+                                                  static_cast<uint16_t*>(Y), n, Ci, Co, s));
     return hip_status(launch_conv_valu(dt == SV_BF16, false, X, N, Wt, bias, Y, n, Ci, Co, s));
 }
 
@@ -53,10 +53,15 @@ sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int
     if (st != SV_OK) return st;
     if (n == 0) return SV_OK;
     if (mfma)
-        return hip_status(launch_conv_mfma(true, static_cast<const uint16_t*>(dY), N,
-                                           static_cast<const uint16_t*>(Wt), nullptr,
-                                           static_cast<uint16_t*>(dX), n, Ci, Co, s));
+        return hip_status(launch_conv_mfma_packed(static_cast<const uint16_t*>(dY), N,
+                                                  static_cast<const uint16_t*>(Wt), nullptr,
+                                                  static_cast<uint16_t*>(dX), n, Co, Ci, s));
     return hip_status(launch_conv_valu(dt == SV_BF16, true, dY, N, Wt, nullptr, dX, n, Ci, Co, s));
+}
+
+// Bytes of repacked weights the forward needs when the MFMA kernel may run.
+size_t fwd_ws_bytes(int32_t Ci, int32_t Co, sv_dtype dt) {
+    return (dt == SV_BF16 && conv_mfma_supported(false, Ci, Co)) ? conv_mfma_fwd_workspace(Ci, Co) : 0;
 }
 
 }  // namespace
@@ -76,11 +81,23 @@ sv_status sv_build_index(const int32_t* coords, const int32_t* frame_offsets, in
 
 sv_status sv_sparseconv2d_fwd(const void* X, const int32_t* N, const void* Wt, const void* bias,
                               void* Y, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
-                              sv_kernel kernel, hipStream_t stream) {
+                              sv_kernel kernel, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
     sv_status st = conv_args_ok(n, C_in, C_out, dtype, kernel);
     if (st != SV_OK) return st;
     if (!Wt || (n > 0 && (!X || !N || !Y))) return SV_ERR_INVALID_ARG;
-    return run_fwd(X, N, Wt, bias, Y, n, C_in, C_out, dtype, kernel, stream);
+    bool mfma = false;
+    if ((st = choose(kernel, dtype, false, C_in, C_out, &mfma)) != SV_OK) return st;
+    if (mfma) {
+        const size_t need = conv_mfma_fwd_workspace(C_in, C_out);
+        if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return SV_ERR_INVALID_ARG;
+        if (n == 0) return SV_OK;
+        st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(workspace),
+                                          C_in, C_out, stream));
+        if (st != SV_OK) return st;
+    }
+    return run_fwd_prepared(mfma, X, N, Wt, workspace, bias, Y, n, C_in, C_out, dtype, stream);
 }
 
 sv_status sv_sparseconv2d_bwd_dx(const void* dY, const int32_t* N, const void* Wt, void* dX,
@@ -93,8 +110,9 @@ sv_status sv_sparseconv2d_bwd_dx(const void* dY, const int32_t* N, const void* W
 }
 
 size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype) {
-    if (op != SV_OP_DW) return 0;
     if (n < 0 || C_in <= 0 || C_out <= 0 || !valid_dtype(dtype)) return 0;
+    if (op == SV_OP_FWD) return fwd_ws_bytes(C_in, C_out, dtype);
+    if (op != SV_OP_DW) return 0;
     return dw_workspace_bytes(plan_dw(n, C_in, C_out, dtype == SV_BF16));
 }
 
@@ -119,6 +137,7 @@ namespace {
 struct ChunkLayout {
     int64_t max_tokens = 0;   // largest chunk, in tokens
     size_t n_bytes = 0;       // chunk-local N table
+    size_t w_bytes = 0;       // forward weights repacked for the MFMA kernel
     size_t dw_bytes = 0;      // dW/db partials of the largest plan
     size_t total = 0;
 };
@@ -145,7 +164,8 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
                                                                           d->dtype == SV_BF16)));
     }
     L->n_bytes = align_up(static_cast<size_t>(L->max_tokens) * 9 * sizeof(int32_t));
-    L->total = L->n_bytes + L->dw_bytes;
+    L->w_bytes = (passes & SV_PASS_FWD) ? fwd_ws_bytes(d->C_in, d->C_out, d->dtype) : 0;
+    L->total = L->n_bytes + L->w_bytes + L->dw_bytes;
     return true;
 }
 
@@ -180,7 +200,18 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
 
     const size_t es = d->dtype == SV_BF16 ? 2 : 4;
     int32_t* Nc = static_cast<int32_t*>(workspace);
-    void* dws = static_cast<char*>(workspace) + L.n_bytes;
+    void* Vw = static_cast<char*>(workspace) + L.n_bytes;
+    void* dws = static_cast<char*>(workspace) + L.n_bytes + L.w_bytes;
+    bool fwd_mfma = false;
+    if (passes & SV_PASS_FWD) {
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, &fwd_mfma);
+        if (fwd_mfma && d->T > 0) {
+            // the weights are repacked once for every chunk
+            sv_status st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(d->Wt),
+                                                        static_cast<uint16_t*>(Vw), d->C_in, d->C_out, stream));
+            if (st != SV_OK) return st;
+        }
+    }
     const int32_t* ho = d->frame_offsets_host;
     bool first = true;
     for (int f0 = 0; f0 < d->T; f0 += d->chunk_frames) {
@@ -192,8 +223,9 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
         const char* X = d->X ? static_cast<const char*>(d->X) + t0 * d->C_in * es : nullptr;
         const char* dY = d->dY ? static_cast<const char*>(d->dY) + t0 * d->C_out * es : nullptr;
         if (passes & SV_PASS_FWD) {
-            st = run_fwd(X, Nc, d->Wt, d->bias, static_cast<char*>(d->Y) + t0 * d->C_out * es, nc,
-                         d->C_in, d->C_out, d->dtype, d->kernel, stream);
+            st = run_fwd_prepared(fwd_mfma, X, Nc, d->Wt, Vw, d->bias,
+                                  static_cast<char*>(d->Y) + t0 * d->C_out * es, nc, d->C_in, d->C_out,
+                                  d->dtype, stream);
             if (st != SV_OK) return st;
         }
         if (passes & SV_PASS_DX) {

@@ -2,11 +2,25 @@
 // fp32 accumulation) for the forward pass and the input gradient.
 // ("SV-TAD: Native Sparse Convolutions for Efficient Temporal Action
 // Detection", Key Design 2: y_k = sum_j W_j x[N[k, j]] as an implicit GEMM
-// with M = tokens, K = 9 * C_in, N = C_out; -1 entries are zero padding.)
+// with M = tokens, K = 9 * C, N = output channels; -1 entries are zero
+// padding.)
+//
+// One kernel serves both passes.  It computes
+//     out[k][c] = sum_j sum_i A[N[k, j]][i] * B[8 - j][c][i]  (+ bias[c])
+// with B stored [tap][output channel][contracted channel]:
+//   input gradient: A = dY, B = Wt itself ([9][C_in][C_out]: tap 8-j of the
+//     weights meets the row gathered through tap j, the mirror of the 3x3
+//     offsets);
+//   forward: A = X, B = V with V[8-j][o][i] = Wt[j][i][o], written by a small
+//     repacking kernel into the caller's workspace.
+// Every MFMA fragment is then one 16-byte LDS read and every staging copy a
+// plain 16-byte copy.
 //
 // Workgroup: 256 threads = 4 waves (2 x 2); output tile 128 tokens x 128
 // channels; each wave 64 x 64 = 2 x 2 blocks of 32 x 32.  Two workgroups fit
-// on a compute unit (72 KiB of LDS each).
+// on a compute unit (70 KiB of LDS each).  The 1-D grid is remapped so that
+// each XCD runs a contiguous range of tiles (neighbouring token ranges and
+// the channel tiles of one range share rows in that XCD's L2).
 //
 // Neighbour window.  Tokens are packed frame-major and, inside a frame, in
 // ascending flat order, so every neighbour of token k lies within W+1 packed
@@ -23,18 +37,10 @@
 // start of round r the weight tile of round r + 1 goes from registers into
 // the free LDS buffer and the loads of round r + 2 are issued, all ahead of
 // round r's MFMAs; the next chunk's window rows load into registers half-way
-// through the current chunk.  One barrier per round.  The output tile leaves
-// through LDS so that global stores are whole 16-byte row pieces.
-//
-// Weights.  Both passes keep the weight tile in LDS as [output column][k]
-// so that every MFMA fragment is one 16-byte LDS read.  Input gradient:
-// B(k = o, col = i) = Wt[8-j][i][o] is already contiguous along k and is
-// copied.  Forward: B(k = i, col = o) = Wt[j][i][o] is contiguous along the
-// column, so half of the threads load 8 x 8 blocks and transpose them in
-// registers on the way to LDS.
-//
-// Each round's 4 k-steps are fully unrolled with all fragment reads issued
-// before the 16 MFMAs, so LDS latency overlaps the matrix work.
+// through the current chunk.  One barrier per round; each round's 4 k-steps
+// are unrolled with all fragment reads issued before the 16 MFMAs.  The
+// output tile leaves through LDS so that global stores are whole 16-byte row
+// pieces.
 #include "internal.h"
 #include "mfma.h"
 
@@ -48,12 +54,12 @@ constexpr int CM_ZROW = CM_WIN;         // an all-zero row: target of -1 entries
 constexpr int CM_LDA = CM_KC + 8;       // 144 B pitch: conflict-free 16-byte row reads
 constexpr int CM_LDB = CM_KC + 8;       // 144 B pitch
 constexpr int CM_SB = CM_BN * CM_LDB;
-constexpr int CM_WREGS = (CM_WIN * (CM_KC / 8) + 255) / 256;   // window chunks per thread (6)
+constexpr int CM_WREGS = (CM_WIN * (CM_KC / 8) + 255) / 256;   // window pieces per thread (6)
 
-// One round: KS k-steps of 16, all fragments read first, then 4 KS MFMAs.
-template <int KS>
+// One round: 4 k-steps of 16, all fragments read first, then 16 MFMAs.
 __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const uint16_t* __restrict__ sb,
                                           const int arow[2], floatx16_t acc[2][2]) {
+    constexpr int KS = CM_KC / 16;
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
     const int l32 = lane & 31, lhi = lane >> 5;
     bf16x8_t a[KS][2], b[KS][2];
@@ -73,16 +79,13 @@ __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const
             for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[ks][mb], b[ks][nb], acc[mb][nb]);
 }
 
-template <bool DX>
+// A [n][K], B [9][NO][K], bias [NO] (nullable), out [n][NO]; K % 32 == 0,
+// NO % 16 == 0.
 __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict__ A,
                                                       const int32_t* __restrict__ Nt,
-                                                      const uint16_t* __restrict__ Wt,
+                                                      const uint16_t* __restrict__ B,
                                                       const uint16_t* __restrict__ bias,
-                                                      uint16_t* __restrict__ out, int n, int Ci,
-                                                      int Co) {
-    const int K = DX ? Co : Ci;    // contracted channels per tap
-    const int NO = DX ? Ci : Co;   // produced channels
-
+                                                      uint16_t* __restrict__ out, int n, int K, int NO) {
     __shared__ __align__(16) uint16_t sA[(CM_WIN + 1) * CM_LDA];
     __shared__ __align__(16) uint16_t sB[2][CM_SB];
     __shared__ int sN[CM_BM * 9];
@@ -109,14 +112,33 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
 
     // ---- the tile's slice of N, its row range, and the LDS row of every entry
     {
-        int lo = 0x7fffffff, hi = -1;
-        for (int e = tid; e < CM_BM * 9; e += 256) {
-            const int64_t k = k0 + e / 9;
-            const int m = (k < n) ? clamp_index(Nt[k * 9 + e % 9], n) : -1;
-            sN[e] = m;
-            if (m >= 0) { lo = min(lo, m); hi = max(hi, m); }
+        // The tile's N rows are contiguous: 1152 consecutive ints, all loads
+        // issued before any is used.
+        constexpr int NE = (CM_BM * 9 + 255) / 256;
+        const int64_t base = k0 * 9;
+        const int64_t lim = static_cast<int64_t>(n) * 9;
+        int m[NE];
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = tid + 256 * u;
+            m[u] = (e < CM_BM * 9 && base + e < lim) ? Nt[base + e] : -1;
         }
-        if (hi >= 0) { atomicMin(&sLo, lo); atomicMax(&sHi, hi); }
+        int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = tid + 256 * u;
+            const int v = clamp_index(m[u], n);
+            if (e < CM_BM * 9) sN[e] = v;
+            if (v >= 0) { lo = min(lo, v); hi = max(hi, v); }
+        }
+        // Reduce within the wave first (same-address LDS atomics from every
+        // thread serialise), then one atomic pair per wave.
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            lo = min(lo, __shfl_xor(lo, d, 64));
+            hi = max(hi, __shfl_xor(hi, d, 64));
+        }
+        if (lane == 0 && hi >= 0) { atomicMin(&sLo, lo); atomicMax(&sHi, hi); }
     }
     __syncthreads();
     const int wlo = sLo;
@@ -127,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         sRow[e] = static_cast<short>(m < 0 ? CM_ZROW : (window ? m - wlo : e / 9));
     }
 
-    // ---- staging helpers
+    // ---- staging helpers (16-byte pieces; channels past K load as zeros)
     auto kc_of = [&](int c) { return min(CM_KC, K - c * CM_KC); };
     auto load_window = [&](int c, uint4* regs) {
         const int c0 = c * CM_KC, kc = kc_of(c);
@@ -149,59 +171,28 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
             if (r < span) *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) = regs[u];
         }
     };
-    // Weight tile of round rr (chunk rr / 9, tap rr % 9) into registers.
-    // Forward: threads 0..127 each load one 8 x 8 block (8 rows k of 8
-    // columns).  Input gradient: every thread loads 4 16-byte pieces.
-    // Block (kb, nb) lands at LDS rows nb*8 + e, column kb*8; with the
-    // 144-byte pitch its bank group is (kb + e) mod 8, so the 8 lanes that
-    // share a write cycle take 8 different kb: no bank conflicts.
+    // Weight tile of round rr (chunk rr / 9, tap rr % 9): B[8-j][n0 + nn][c0 + ...].
     auto load_B = [&](int rr, uint4* regs) {
         const int c = rr / 9, j = rr - c * 9;
-        const int jt = DX ? 8 - j : j;
         const int c0 = c * CM_KC, kc = kc_of(c);
-        const uint16_t* __restrict__ Wj = Wt + static_cast<int64_t>(jt) * Ci * Co;
-        if (!DX) {
-            if (tid < (CM_KC / 8) * (CM_BN / 8)) {
-                const int kb = tid & 7, nb = tid >> 3;   // 8 neighbouring lanes: 8 k groups
-                const bool ok = n0 + nb * 8 < NO;
+        const uint16_t* __restrict__ Bj = B + static_cast<int64_t>(8 - j) * NO * K;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int kk = kb * 8 + r;
-                    regs[r] = (ok && kk < kc)
-                                  ? *reinterpret_cast<const uint4*>(Wj + static_cast<int64_t>(c0 + kk) * Co + n0 + nb * 8)
-                                  : make_uint4(0, 0, 0, 0);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int q = tid + 256 * u;
-                const int nn = q >> 3, ch = q & 7;         // Wt[8-j][n0 + nn][c0 + 8 ch ...]
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (n0 + nn < NO && ch * 8 < kc)
-                    v = *reinterpret_cast<const uint4*>(Wj + static_cast<int64_t>(n0 + nn) * Co + c0 + ch * 8);
-                regs[u] = v;
-            }
+        for (int u = 0; u < 4; ++u) {
+            const int q = tid + 256 * u;
+            const int nn = q >> 3, ch = q & 7;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (n0 + nn < NO && ch * 8 < kc)
+                v = *reinterpret_cast<const uint4*>(Bj + static_cast<int64_t>(n0 + nn) * K + c0 + ch * 8);
+            regs[u] = v;
         }
     };
     auto store_B = [&](int buf, const uint4* regs) {
         uint16_t* sb = sB[buf];
-        if (!DX) {
-            if (tid < (CM_KC / 8) * (CM_BN / 8)) {
-                const int kb = tid & 7, nb = tid >> 3;   // 8 neighbouring lanes: 8 k groups
-                uint4 cols[8];
-                transpose8x8_b16(regs, cols);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *reinterpret_cast<uint4*>(&sb[(nb * 8 + e) * CM_LDB + kb * 8]) = cols[e];
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int q = tid + 256 * u;
-                const int nn = q >> 3, ch = q & 7;
-                *reinterpret_cast<uint4*>(&sb[nn * CM_LDB + ch * 8]) = regs[u];
-            }
+        for (int u = 0; u < 4; ++u) {
+            const int q = tid + 256 * u;
+            const int nn = q >> 3, ch = q & 7;
+            *reinterpret_cast<uint4*>(&sb[nn * CM_LDB + ch * 8]) = regs[u];
         }
     };
     // Gather mode: the 128 rows of tap j, chunk c, straight into sA.
@@ -226,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
-    uint4 breg[8], wreg[CM_WREGS];
+    uint4 breg[4], wreg[CM_WREGS];
     if (window) {
         load_window(0, wreg);
         store_window(wreg);
@@ -251,14 +242,13 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
             if (r + 2 < R) load_B(r + 2, breg);
         }
         if (window && j == 4 && c + 1 < nchunks) load_window(c + 1, wreg);
-        const uint16_t* __restrict__ sb = sB[r & 1];
         int arow[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) arow[mb] = sRow[(wm * 64 + mb * 32 + l32) * 9 + j];
         // Always the full 4 k-steps: a 32-channel tail chunk is zero-filled
         // past its end in both operands, and one code path keeps the
         // accumulators in fixed registers.
-        mma_round<CM_KC / 16>(sA, sb, arow, acc);
+        mma_round(sA, sB[r & 1], arow, acc);
         if (r + 1 < R) {
             if (window && (r + 1) % 9 == 0) {
                 __syncthreads();           // every wave is done with this chunk's window
@@ -277,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const int cl = wn * 64 + nb * 32 + l32;
-        const float bv = (!DX && bias && n0 + cl < NO) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
+        const float bv = (bias && n0 + cl < NO) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -298,23 +288,50 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     }
 }
 
+// V[8-j][o][i] = Wt[j][i][o]: nine C_in x C_out transposes through LDS,
+// 32 x 32 tiles (rows padded by one element), 4 elements per thread.
+__global__ __launch_bounds__(256) void k_repack_fwd(const uint16_t* __restrict__ Wt, uint16_t* __restrict__ V,
+                                                    int Ci, int Co) {
+    __shared__ uint16_t t[32][33];
+    const int j = blockIdx.z;
+    const int i0 = blockIdx.y * 32, o0 = blockIdx.x * 32;
+    const uint16_t* src = Wt + static_cast<int64_t>(j) * Ci * Co;
+    uint16_t* dst = V + static_cast<int64_t>(8 - j) * Co * Ci;
+    const int c = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = r0 + 8 * u;                  // r: input channel, c: output channel
+        t[r][c] = (i0 + r < Ci && o0 + c < Co) ? src[static_cast<int64_t>(i0 + r) * Co + o0 + c] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = r0 + 8 * u;                  // r: output channel, c: input channel
+        if (o0 + r < Co && i0 + c < Ci) dst[static_cast<int64_t>(o0 + r) * Ci + i0 + c] = t[c][r];
+    }
+}
+
 bool conv_mfma_supported(bool dx, int Ci, int Co) {
     const int K = dx ? Co : Ci, NO = dx ? Ci : Co;
     return K > 0 && NO > 0 && K % 32 == 0 && NO % 16 == 0;
 }
 
-hipError_t launch_conv_mfma(bool dx, const uint16_t* A, const int32_t* N, const uint16_t* Wt,
-                            const uint16_t* bias, uint16_t* out, int64_t n, int Ci, int Co,
-                            hipStream_t stream) {
+size_t conv_mfma_fwd_workspace(int Ci, int Co) {
+    return (static_cast<size_t>(9) * Ci * Co * sizeof(uint16_t) + 255) & ~static_cast<size_t>(255);
+}
+
+hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, hipStream_t stream) {
+    dim3 grid((Co + 31) / 32, (Ci + 31) / 32, 9);
+    hipLaunchKernelGGL(k_repack_fwd, grid, dim3(256), 0, stream, Wt, V, Ci, Co);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const uint16_t* B,
+                                   const uint16_t* bias, uint16_t* out, int64_t n, int K, int NO,
+                                   hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    const int NO = dx ? Ci : Co;
     dim3 grid(static_cast<unsigned>(((n + CM_BM - 1) / CM_BM) * ((NO + CM_BN - 1) / CM_BN)));
-    if (dx)
-        hipLaunchKernelGGL(k_conv_mfma<true>, grid, dim3(256), 0, stream, A, N, Wt, bias, out,
-                           static_cast<int>(n), Ci, Co);
-    else
-        hipLaunchKernelGGL(k_conv_mfma<false>, grid, dim3(256), 0, stream, A, N, Wt, bias, out,
-                           static_cast<int>(n), Ci, Co);
+    hipLaunchKernelGGL(k_conv_mfma, grid, dim3(256), 0, stream, A, N, B, bias, out, static_cast<int>(n), K, NO);
     return hipGetLastError();
 }
 

@@ -253,7 +253,7 @@ DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16) {
         const double dwb = 9.0 * Ci * Co * 4;
         double best = 1e30;
         slices = 1;
-        for (int64_t s = 1; s <= 128; ++s) {
+        for (int64_t s = 1; s <= 64; ++s) {
             if (s > 1 && ceil_div(n, s) < 4 * DW_TK) break;
             const double rounds = static_cast<double>(ceil_div(tiles * s, 256));
             const double t = rounds * flops / static_cast<double>(tiles * s) / 4e12 +

@@ -86,11 +86,17 @@ hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
                             const void* Wt, const void* bias, void* out, int64_t n,
                             int Ci, int Co, hipStream_t stream);
 
-// MFMA path (bf16, K % 32 == 0 and Nout % 16 == 0 where K/Nout are the
-// contracted/produced channel counts of the pass).
-hipError_t launch_conv_mfma(bool dx, const uint16_t* A, const int32_t* N, const uint16_t* Wt,
-                            const uint16_t* bias, uint16_t* out, int64_t n, int Ci, int Co,
-                            hipStream_t stream);
+// MFMA path (bf16).  One gather-GEMM serves both passes:
+//   out[k][c] = sum_j sum_i A[N[k,j]][i] * B[8-j][c][i] (+ bias[c]),
+// A [n][K], B [9][NO][K] (K % 32 == 0, NO % 16 == 0).  The input gradient
+// calls it with A = dY and B = Wt; the forward with A = X and B = V, the
+// weights repacked by launch_repack_fwd (V[8-j][o][i] = Wt[j][i][o]) into
+// conv_mfma_fwd_workspace(Ci, Co) bytes.
+hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const uint16_t* B,
+                                   const uint16_t* bias, uint16_t* out, int64_t n, int K, int NO,
+                                   hipStream_t stream);
+hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, hipStream_t stream);
+size_t conv_mfma_fwd_workspace(int Ci, int Co);
 bool conv_mfma_supported(bool dx, int Ci, int Co);
 
 // dW: split-K plan, partial kernels, reduction.

@@ -80,7 +80,7 @@ def load(path: str = LIB_PATH):
     E = ctypes.c_int
     sig = {
         "sv_build_index": ([P, P, i32, i32, i32, i64, P, P, P, P], E),
-        "sv_sparseconv2d_fwd": ([P, P, P, P, P, i64, i32, i32, E, E, P], E),
+        "sv_sparseconv2d_fwd": ([P, P, P, P, P, i64, i32, i32, E, E, P, sz, P], E),
         "sv_sparseconv2d_bwd_dx": ([P, P, P, P, i64, i32, i32, E, E, P], E),
         "sv_sparseconv2d_bwd_dw": ([P, P, P, P, P, i64, i32, i32, E, i32, P, sz, P], E),
         "sv_workspace_bytes": ([E, i64, i32, i32, E], sz),
@@ -155,15 +155,19 @@ def sv_build_index(coords, frame_offsets, T, H, W, N_out, M_out=None, err_flag=N
     _check(st, "sv_build_index")
 
 
-def sv_sparseconv2d_fwd(X, N, Wt, bias, Y, kernel="auto", stream=None):
+def sv_sparseconv2d_fwd(X, N, Wt, bias, Y, kernel="auto", workspace=None, stream=None):
     n, Ci = X.shape
     Co = Wt.shape[2]
     assert Wt.shape == (9, Ci, Co) and Y.shape == (n, Co) and N.shape == (n, 9)
     assert X.dtype == Wt.dtype == Y.dtype and N.dtype == torch.int32
     if bias is not None:
         assert bias.dtype == X.dtype and bias.shape == (Co,)
+    need = sv_workspace_bytes(SV_OP_FWD, n, Ci, Co, X.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().sv_sparseconv2d_fwd(_ptr(X), _ptr(N), _ptr(Wt), _ptr(bias), _ptr(Y), n, Ci, Co,
-                                    _dt(X), _kernel(kernel), _stream(stream))
+                                    _dt(X), _kernel(kernel), _ptr(workspace), wsb, _stream(stream))
     _check(st, "sv_sparseconv2d_fwd")
 
 

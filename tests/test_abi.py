@@ -50,17 +50,21 @@ def test_status_strings(lib):
 def test_validation_without_device(lib):
     F32, BF16 = ops.SV_F32, ops.SV_BF16
     # negative n, zero channels, bad dtype, bad kernel enum
-    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, -1, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
-    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 0, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
-    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 4, 4, 7, 0, None) == ops.SV_ERR_INVALID_ARG
-    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 4, 4, F32, 9, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, -1, 4, 4, F32, 0, None, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 0, 4, F32, 0, None, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 4, 4, 7, 0, None, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 4, 4, F32, 9, None, 0, None) == ops.SV_ERR_INVALID_ARG
     # null required pointers
-    assert lib.sv_sparseconv2d_fwd(None, FAKE, FAKE, None, FAKE, 8, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_fwd(None, FAKE, FAKE, None, FAKE, 8, 4, 4, F32, 0, None, 0, None) == ops.SV_ERR_INVALID_ARG
     assert lib.sv_sparseconv2d_bwd_dx(FAKE, None, FAKE, FAKE, 8, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
     # MFMA forced where it does not fit: fp32, or channels not multiples of 32/16
-    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 64, F32, 2, None) == ops.SV_ERR_UNSUPPORTED
-    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 48, 64, BF16, 2, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 64, F32, 2, None, 0, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 48, 64, BF16, 2, None, 0, None) == ops.SV_ERR_UNSUPPORTED
     assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, 8, 64, 40, BF16, 2, None) == ops.SV_ERR_UNSUPPORTED
+    # forward on the matrix cores without its weight workspace
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 64, BF16, 0, None, 0, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_workspace_bytes(ops.SV_OP_FWD, 8, 64, 64, BF16) >= 9 * 64 * 64 * 2
+    assert lib.sv_workspace_bytes(ops.SV_OP_FWD, 8, 64, 64, F32) == 0
     # grid larger than the LDS map
     assert lib.sv_build_index(FAKE, FAKE, 1, 129, 128, 1, FAKE, None, None, None) == ops.SV_ERR_UNSUPPORTED
     assert lib.sv_build_index(FAKE, None, 1, 4, 4, 1, FAKE, None, None, None) == ops.SV_ERR_INVALID_ARG
@@ -78,7 +82,6 @@ def test_validation_without_device(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.sv_workspace_bytes(ops.SV_OP_FWD, 1000, 64, 64, ops.SV_BF16) == 0
     assert lib.sv_workspace_bytes(ops.SV_OP_DX, 1000, 64, 64, ops.SV_BF16) == 0
     assert lib.sv_workspace_bytes(ops.SV_OP_DW, -1, 64, 64, ops.SV_BF16) == 0
     # bounded: never more than 64 slices of partials plus db partials
