@@ -92,8 +92,10 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     __shared__ short sRow[CM_BM * 9];
     __shared__ int sLo, sHi;
 
+    // The wave index is uniform; through the scalar unit it keeps every
+    // per-wave quantity scalar.
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, lhi = lane >> 5;
     // 1-D grid: logical tile = (token tile, output-channel tile), the
@@ -121,7 +123,9 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
             const int e = tid + 256 * u;
-            m[u] = (e < CM_BM * 9 && base + e < lim) ? Nt[base + e] : -1;
+            const bool ok = e < CM_BM * 9 && base + e < lim;
+            const int v = Nt[min(base + min(e, CM_BM * 9 - 1), lim - 1)];   // clamped: branch-free
+            m[u] = ok ? v : -1;
         }
         int lo = 0x7fffffff, hi = -1;
 #pragma unroll
@@ -149,7 +153,11 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         sRow[e] = static_cast<short>(m < 0 ? CM_ZROW : (window ? m - wlo : e / 9));
     }
 
-    // ---- staging helpers (16-byte pieces; channels past K load as zeros)
+    // ---- staging helpers (16-byte pieces; channels past K load as zeros).
+    // Loads are unconditional, from addresses clamped into the valid range;
+    // pieces outside the tile are zeroed when stored to LDS, a round or more
+    // later.  Testing right after the load would make the wave wait for it
+    // (and for every load queued before it) at the point of issue.
     auto kc_of = [&](int c) { return min(CM_KC, K - c * CM_KC); };
     auto load_window = [&](int c, uint4* regs) {
         const int c0 = c * CM_KC, kc = kc_of(c);
@@ -157,18 +165,18 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         for (int u = 0; u < CM_WREGS; ++u) {
             const int q = tid + 256 * u;
             const int r = q >> 3, ch = q & 7;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (r < span && ch * 8 < kc)
-                v = *reinterpret_cast<const uint4*>(A + static_cast<int64_t>(wlo + r) * K + c0 + ch * 8);
-            regs[u] = v;
+            regs[u] = *reinterpret_cast<const uint4*>(
+                A + static_cast<int64_t>(wlo + min(r, span - 1)) * K + c0 + min(ch * 8, kc - 8));
         }
     };
-    auto store_window = [&](const uint4* regs) {
+    auto store_window = [&](int c, const uint4* regs) {
+        const int kc = kc_of(c);
 #pragma unroll
         for (int u = 0; u < CM_WREGS; ++u) {
             const int q = tid + 256 * u;
-            const int r = q >> 3, ch = q & 7;
-            if (r < span) *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) = regs[u];
+            const int r = q >> 3, ch = q & 7;     // r < CM_WIN: rows past span hold zeros
+            *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) =
+                (r < span && ch * 8 < kc) ? regs[u] : make_uint4(0, 0, 0, 0);
         }
     };
     // Weight tile of round rr (chunk rr / 9, tap rr % 9): B[8-j][n0 + nn][c0 + ...].
@@ -180,19 +188,19 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         for (int u = 0; u < 4; ++u) {
             const int q = tid + 256 * u;
             const int nn = q >> 3, ch = q & 7;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (n0 + nn < NO && ch * 8 < kc)
-                v = *reinterpret_cast<const uint4*>(Bj + static_cast<int64_t>(n0 + nn) * K + c0 + ch * 8);
-            regs[u] = v;
+            regs[u] = *reinterpret_cast<const uint4*>(
+                Bj + static_cast<int64_t>(min(n0 + nn, NO - 1)) * K + c0 + min(ch * 8, kc - 8));
         }
     };
-    auto store_B = [&](int buf, const uint4* regs) {
+    auto store_B = [&](int buf, int rr, const uint4* regs) {
         uint16_t* sb = sB[buf];
+        const int kc = kc_of(rr / 9);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int q = tid + 256 * u;
             const int nn = q >> 3, ch = q & 7;
-            *reinterpret_cast<uint4*>(&sb[nn * CM_LDB + ch * 8]) = regs[u];
+            *reinterpret_cast<uint4*>(&sb[nn * CM_LDB + ch * 8]) =
+                (n0 + nn < NO && ch * 8 < kc) ? regs[u] : make_uint4(0, 0, 0, 0);
         }
     };
     // Gather mode: the 128 rows of tap j, chunk c, straight into sA.
@@ -204,10 +212,10 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
             const int q = tid + 256 * u;
             const int r = q >> 3, ch = q & 7;
             const int m = sN[r * 9 + j];
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (m >= 0 && ch * 8 < kc)
-                v = *reinterpret_cast<const uint4*>(A + static_cast<int64_t>(m) * K + c0 + ch * 8);
-            *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) = v;
+            const uint4 v = *reinterpret_cast<const uint4*>(
+                A + static_cast<int64_t>(max(m, 0)) * K + c0 + min(ch * 8, kc - 8));
+            *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) =
+                (m >= 0 && ch * 8 < kc) ? v : make_uint4(0, 0, 0, 0);
         }
     };
 
@@ -218,12 +226,12 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
     uint4 breg[4], wreg[CM_WREGS];
-    if (window) {
+    if (window && span > 0) {
         load_window(0, wreg);
-        store_window(wreg);
+        store_window(0, wreg);
     }
     load_B(0, breg);
-    store_B(0, breg);
+    store_B(0, 0, breg);
     if (R > 1) load_B(1, breg);
     __syncthreads();
 
@@ -238,10 +246,10 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         // one after: issued ahead of this round's MFMAs so that their
         // latency hides behind the matrix work.
         if (r + 1 < R) {
-            store_B((r + 1) & 1, breg);
+            store_B((r + 1) & 1, r + 1, breg);
             if (r + 2 < R) load_B(r + 2, breg);
         }
-        if (window && j == 4 && c + 1 < nchunks) load_window(c + 1, wreg);
+        if (window && span > 0 && j == 4 && c + 1 < nchunks) load_window(c + 1, wreg);
         int arow[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) arow[mb] = sRow[(wm * 64 + mb * 32 + l32) * 9 + j];
@@ -250,9 +258,9 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         // accumulators in fixed registers.
         mma_round(sA, sB[r & 1], arow, acc);
         if (r + 1 < R) {
-            if (window && (r + 1) % 9 == 0) {
+            if (window && span > 0 && (r + 1) % 9 == 0) {
                 __syncthreads();           // every wave is done with this chunk's window
-                store_window(wreg);
+                store_window(c + 1, wreg);
             }
             __syncthreads();
         }

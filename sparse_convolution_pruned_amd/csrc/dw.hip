@@ -67,7 +67,10 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     const int steps = kend > kbeg ? static_cast<int>((kend - kbeg + DW_TK - 1) / DW_TK) : 0;
     const bool do_db = dbout != nullptr && kr == 1 && i0 == 0;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform across a wave; reading it through the scalar
+    // unit lets every per-wave condition below compile to a scalar branch.
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, lhi = lane >> 5;
     const int wi = wave & 3, wo = wave >> 2;
 
@@ -76,27 +79,38 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     // lands at LDS rows cg*8 + e, column tg*8: bank group (tg + e) mod 8 with
     // the 144-byte pitch, so the 8 lanes that share a write cycle (8 token
     // groups) never collide.
-    const int tile = tid >> 7, tg = tid & 7, cg = (tid >> 3) & 15;
+    const int tile = wave >> 1, tg = tid & 7, cg = (tid >> 3) & 15;
     const bool is_x = tile < 3;
     uint4 rr[8];
     int ni[8];
+    // Loads of pruned neighbours are masked off (no memory request at all):
+    // the gathered X rows are the kernel's main traffic.
+    const int64_t klast = kend - 1;
+    const int ncol = 3 * kr + (is_x ? tile : 0);
+    // The N entries are loaded unconditionally (clamped address) and only
+    // tested when the rows they point to are requested, one step later: a
+    // test right after the load would make the wave wait for it, and for the
+    // row loads queued before it.
     auto load_n = [&](int s) {
+        const int64_t kb = kbeg + static_cast<int64_t>(s) * DW_TK + tg * 8;
+        if (is_x)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int64_t k = kbeg + static_cast<int64_t>(s) * DW_TK + tg * 8 + t;
-            ni[t] = (is_x && k < kend) ? clamp_index(Nt[k * 9 + 3 * kr + tile], n) : -1;
-        }
+            for (int t = 0; t < 8; ++t) ni[t] = Nt[min(kb + t, klast) * 9 + ncol];
     };
     auto load_rows = [&](int s) {
+        const int64_t kb = kbeg + static_cast<int64_t>(s) * DW_TK + tg * 8;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
+            uint4 v = make_uint4(0, 0, 0, 0);
             if (is_x) {
-                rr[t] = ni[t] >= 0 ? *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(ni[t]) * Ci + i0 + cg * 8)
-                                   : make_uint4(0, 0, 0, 0);
+                const int j = clamp_index(ni[t], n);
+                if (j >= 0 && kb + t <= klast)
+                    v = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(j) * Ci + i0 + cg * 8);
             } else {
-                const int64_t k = kbeg + static_cast<int64_t>(s) * DW_TK + tg * 8 + t;
-                rr[t] = k < kend ? *reinterpret_cast<const uint4*>(dY + k * Co + o0 + cg * 8) : make_uint4(0, 0, 0, 0);
+                const int64_t k = kb + t;
+                if (k <= klast) v = *reinterpret_cast<const uint4*>(dY + k * Co + o0 + cg * 8);
             }
+            rr[t] = v;
         }
     };
     auto store_rows = [&](int buf) {
@@ -147,7 +161,7 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) acc[t][nb] = mfma32(a[t], b[nb], acc[t][nb]);
         }
-        if (do_db && tid < DW_BO) {
+        if (do_db && wave < DW_BO / 64) {
             // row tid of the dY tile: output channel o0 + tid over the 64 tokens
 #pragma unroll
             for (int q = 0; q < DW_TK / 8; ++q) {
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
                     *d = (direct && accumulate) ? *d + v : v;
                 }
     }
-    if (do_db && tid < DW_BO) {
+    if (do_db && wave < DW_BO / 64) {
         float* d = dbout + (direct ? 0 : static_cast<int64_t>(slice) * Co) + o0 + tid;
         *d = (direct && accumulate) ? *d + dbacc : dbacc;
     }
