@@ -34,21 +34,33 @@ hipError_t launch_dw_valu(bool bf16, const void* X, const int32_t* N, const void
 // 16-byte rows (the X rows through N[k][3r + tap]), transposed in registers
 // and written to LDS channel-major, [tile][channel][token], where every MFMA
 // fragment is one 16-byte read.  At the start of step s the tiles of step
-// s + 1 go into the free LDS buffer and the loads of step s + 2 (N entries of
-// step s + 3) are issued, ahead of step s's MFMAs; each step ends with a
-// single barrier.
+// s + 1 go into the free LDS buffer and the row loads of step s + 2 are
+// issued, ahead of step s's MFMAs; each step ends with a single barrier.
+//
+// The N entries a step needs (64 tokens x 3 taps) are fetched once per
+// workgroup by one wave, lane = token, two steps ahead, and passed through a
+// small double-buffered LDS table: per-thread loads would request each entry
+// 16 times and touch 8 cache lines per instruction for 32 useful bytes.
+//
+// All global reads are raw buffer loads with 32-bit offsets: rows of pruned
+// neighbours and tokens past the slice get an out-of-range offset and read
+// as zeros without a memory request or a branch.  The host sends inputs
+// larger than the buffer range (2 GiB) to the VALU kernel.
 constexpr int DW_BI = 128, DW_BO = 128, DW_TK = 64, DW_THREADS = 512;
 constexpr int DW_LD = DW_TK + 8;                 // 144-byte rows
 constexpr int DW_TILE = 128 * DW_LD;             // one [128 channels][64 tokens] tile
 constexpr int DW_BUF = 4 * DW_TILE;              // 3 X tiles + 1 dY tile
+constexpr int DW_NTAB = 2 * 3 * DW_TK;           // N table: [2 buffers][3 taps][64 tokens]
+constexpr size_t DW_LDS = 2 * DW_BUF * sizeof(uint16_t) + DW_NTAB * sizeof(int);
 
 __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restrict__ X,
                                                         const int32_t* __restrict__ Nt,
                                                         const uint16_t* __restrict__ dY,
                                                         float* __restrict__ out, float* __restrict__ dbout,
-                                                        int n, int Ci, int Co, int64_t slice_tokens,
+                                                        int n, int Ci, int Co, int slice_tokens,
                                                         int direct, int accumulate) {
-    extern __shared__ __align__(16) uint16_t dwsm[];   // 2 buffers of DW_BUF
+    extern __shared__ __align__(16) uint16_t dwsm[];   // 2 buffers of DW_BUF, then the N table
+    int* const ntab = reinterpret_cast<int*>(dwsm + 2 * DW_BUF);
 
     // 1-D grid of tiles x slices: logical id = slice * tiles + tile, so the
     // tiles of one token slice (which gather the same X and dY rows) sit
@@ -62,9 +74,9 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     bid /= 3;
     const int i0 = (bid % tilesI) * DW_BI;
     const int o0 = (bid / tilesI) * DW_BO;
-    const int64_t kbeg = static_cast<int64_t>(slice) * slice_tokens;
-    const int64_t kend = min(static_cast<int64_t>(n), kbeg + slice_tokens);
-    const int steps = kend > kbeg ? static_cast<int>((kend - kbeg + DW_TK - 1) / DW_TK) : 0;
+    const int kbeg = slice * slice_tokens;
+    const int cnt = max(0, min(n - kbeg, slice_tokens));     // tokens of this slice
+    const int steps = (cnt + DW_TK - 1) / DW_TK;
     const bool do_db = dbout != nullptr && kr == 1 && i0 == 0;
 
     // The wave index is uniform across a wave; reading it through the scalar
@@ -74,43 +86,64 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     const int l32 = lane & 31, lhi = lane >> 5;
     const int wi = wave & 3, wo = wave >> 2;
 
-    // This thread's 8 x 8 block: tile = tid >> 7 (taps 0..2 of the row, then
+    // This thread's 8 x 8 block: tile = wave >> 1 (taps 0..2 of the row, then
     // dY), token group tid & 7, channel group (tid >> 3) & 15.  The block
     // lands at LDS rows cg*8 + e, column tg*8: bank group (tg + e) mod 8 with
     // the 144-byte pitch, so the 8 lanes that share a write cycle (8 token
     // groups) never collide.
     const int tile = wave >> 1, tg = tid & 7, cg = (tid >> 3) & 15;
     const bool is_x = tile < 3;
+    const rsrc_t rX = make_rsrc(X, static_cast<uint32_t>(n) * Ci * 2);
+    const rsrc_t rN = make_rsrc(Nt + static_cast<int64_t>(kbeg) * 9, static_cast<uint32_t>(cnt) * 36);
+    const rsrc_t rY = make_rsrc(dY + static_cast<int64_t>(kbeg) * Co, static_cast<uint32_t>(cnt) * Co * 2);
+    const uint32_t nOff = static_cast<uint32_t>(tg * 8) * 36 + (3 * kr + (is_x ? tile : 0)) * 4;
+    const uint32_t yOff = static_cast<uint32_t>(tg * 8) * Co * 2 + (o0 + cg * 8) * 2;
+    const uint32_t xCol = (i0 + cg * 8) * 2, rowX = Ci * 2, rowY = Co * 2;
     uint4 rr[8];
     int ni[8];
-    // Loads of pruned neighbours are masked off (no memory request at all):
-    // the gathered X rows are the kernel's main traffic.
-    const int64_t klast = kend - 1;
-    const int ncol = 3 * kr + (is_x ? tile : 0);
-    // The N entries are loaded unconditionally (clamped address) and only
-    // tested when the rows they point to are requested, one step later: a
-    // test right after the load would make the wave wait for it, and for the
-    // row loads queued before it.
+    // N entries are used as they are loaded and tested only when the rows
+    // they point to are requested: a test right after a load would make the
+    // wave wait for it (and for the row loads queued before it) on the spot.
+    //   load_n: this thread's 8 entries straight from N (first two steps);
+    //   fetch_n / put_n: the loader wave's 3 entries (lane = token) into the
+    //     table buffer of the step's parity;
+    //   get_n: this thread's 8 entries from the table.
+    const bool loader = wave == 6;
+    int nreg[3];
     auto load_n = [&](int s) {
-        const int64_t kb = kbeg + static_cast<int64_t>(s) * DW_TK + tg * 8;
-        if (is_x)
+        if (is_x) {
+            const uint32_t base = nOff + static_cast<uint32_t>(s * DW_TK) * 36;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) ni[t] = Nt[min(kb + t, klast) * 9 + ncol];
+            for (int t = 0; t < 8; ++t) ni[t] = load4(rN, base + t * 36);
+        }
+    };
+    auto fetch_n = [&](int s) {
+        const uint32_t base = static_cast<uint32_t>(s * DW_TK + lane) * 36 + 3 * kr * 4;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) nreg[t] = load4(rN, base + t * 4);
+    };
+    auto put_n = [&](int s) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t) ntab[((s & 1) * 3 + t) * DW_TK + lane] = nreg[t];
+    };
+    auto get_n = [&](int s) {
+        const int* p = &ntab[((s & 1) * 3 + tile) * DW_TK + tg * 8];
+        const int4 a = *reinterpret_cast<const int4*>(p), b = *reinterpret_cast<const int4*>(p + 4);
+        ni[0] = a.x; ni[1] = a.y; ni[2] = a.z; ni[3] = a.w;
+        ni[4] = b.x; ni[5] = b.y; ni[6] = b.z; ni[7] = b.w;
     };
     auto load_rows = [&](int s) {
-        const int64_t kb = kbeg + static_cast<int64_t>(s) * DW_TK + tg * 8;
+        if (is_x) {
+            const int lim = cnt - s * DW_TK - tg * 8;     // tokens t < lim lie in the slice
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (is_x) {
-                const int j = clamp_index(ni[t], n);
-                if (j >= 0 && kb + t <= klast)
-                    v = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(j) * Ci + i0 + cg * 8);
-            } else {
-                const int64_t k = kb + t;
-                if (k <= klast) v = *reinterpret_cast<const uint4*>(dY + k * Co + o0 + cg * 8);
+            for (int t = 0; t < 8; ++t) {
+                const bool ok = static_cast<unsigned>(ni[t]) < static_cast<unsigned>(n) && t < lim;
+                rr[t] = load16(rX, ok ? __umul24(static_cast<unsigned>(ni[t]), rowX) + xCol : kOob);
             }
-            rr[t] = v;
+        } else {
+            const uint32_t base = yOff + static_cast<uint32_t>(s * DW_TK) * rowY;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) rr[t] = load16(rY, base + t * rowY);   // past the slice: zeros
         }
     };
     auto store_rows = [&](int buf) {
@@ -126,26 +159,45 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     for (int t = 0; t < 3; ++t)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[t][b] = zero16();
+    // db: thread = (output channel o0 + (tid & 127), 16-token quarter tid >> 7)
+    // of each step's dY tile, summed with bf16 dot products against ones.
     float dbacc = 0.f;
+    typedef __attribute__((__vector_size__(2 * sizeof(short)))) short short2_t;
+    const short2_t ones = __builtin_bit_cast(short2_t, 0x3f803f80u);
 
     if (steps > 0) {
         load_n(0);
         load_rows(0);
         store_rows(0);
         if (steps > 1) { load_n(1); load_rows(1); }
-        if (steps > 2) load_n(2);
+        if (loader && steps > 2) {
+            fetch_n(2);
+            put_n(2);
+            if (steps > 3) fetch_n(3);
+        }
     }
     __syncthreads();
 
-    for (int s = 0; s < steps; ++s) {
-        // Next step's tiles into the free buffer (last read in step s - 1),
-        // loads for the step after, N entries for the one after that: all
-        // issued ahead of this step's MFMAs.
-        if (s + 1 < steps) {
-            store_rows((s + 1) & 1);
-            if (s + 2 < steps) load_rows(s + 2);
-            if (s + 3 < steps) load_n(s + 3);
+    // One step.  With `all` every look-ahead exists (s + 4 < steps): the
+    // main loop runs that form without any branch around loads and stores,
+    // so the compiler's wait counts stay exact; the last steps take the
+    // guarded form.
+    auto step = [&](int s, bool all) {
+        const bool n1 = all || s + 1 < steps, n2 = all || s + 2 < steps;
+        const bool n3 = all || s + 3 < steps, n4 = all || s + 4 < steps;
+        // Step s + 2's N entries from the table (written in step s - 1), the
+        // next step's tiles into the free buffer (last read in step s - 1),
+        // the loader wave's table entries for step s + 3 (into the buffer
+        // step s + 1 read in step s - 1) and the row loads of step s + 2:
+        // all ahead of this step's MFMAs.  The loader's entries go out
+        // before the row loads, so that neither waits behind the other.
+        if (is_x && n2) get_n(s + 2);
+        if (n1) store_rows((s + 1) & 1);
+        if (loader && n3) {
+            put_n(s + 3);
+            if (n4) fetch_n(s + 4);
         }
+        if (n2) load_rows(s + 2);
         const uint16_t* __restrict__ sb = dwsm + (s & 1) * DW_BUF;
         const uint16_t* __restrict__ sd = sb + 3 * DW_TILE;
 #pragma unroll
@@ -161,21 +213,20 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) acc[t][nb] = mfma32(a[t], b[nb], acc[t][nb]);
         }
-        if (do_db && wave < DW_BO / 64) {
-            // row tid of the dY tile: output channel o0 + tid over the 64 tokens
+        if (do_db) {
+            const uint16_t* p = &sd[(tid & 127) * DW_LD + (tid >> 7) * 16];
+            const uint4 v0 = *reinterpret_cast<const uint4*>(p);
+            const uint4 v1 = *reinterpret_cast<const uint4*>(p + 8);
+            const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-            for (int q = 0; q < DW_TK / 8; ++q) {
-                const uint4 v = *reinterpret_cast<const uint4*>(&sd[tid * DW_LD + q * 8]);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    dbacc += bf16_to_f32(static_cast<uint16_t>(w[h] & 0xffffu));
-                    dbacc += bf16_to_f32(static_cast<uint16_t>(w[h] >> 16));
-                }
-            }
+            for (int h = 0; h < 8; ++h)
+                dbacc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short2_t, w[h]), ones, dbacc, false);
         }
-        if (s + 1 < steps) __syncthreads();
-    }
+        if (n1) __syncthreads();
+    };
+    int s = 0;
+    for (; s + 4 < steps; ++s) step(s, true);
+    for (; s < steps; ++s) step(s, false);
 
     // D block (32 input channels x 32 output channels): lane holds output
     // channel l32 and input channels 8g + 4*lhi + q.
@@ -196,9 +247,17 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
                     *d = (direct && accumulate) ? *d + v : v;
                 }
     }
-    if (do_db && wave < DW_BO / 64) {
-        float* d = dbout + (direct ? 0 : static_cast<int64_t>(slice) * Co) + o0 + tid;
-        *d = (direct && accumulate) ? *d + dbacc : dbacc;
+    if (do_db) {
+        // the four quarters of each channel, added in a fixed order
+        float* red = reinterpret_cast<float*>(dwsm);
+        __syncthreads();
+        red[tid] = dbacc;
+        __syncthreads();
+        if (tid < DW_BO) {
+            const float v = ((red[tid] + red[tid + 128]) + red[tid + 256]) + red[tid + 384];
+            float* d = dbout + (direct ? 0 : static_cast<int64_t>(slice) * Co) + o0 + tid;
+            *d = (direct && accumulate) ? *d + v : v;
+        }
     }
 }
 
@@ -253,7 +312,9 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16) {
     DwPlan p{};
-    p.mfma = bf16 && Ci % DW_BI == 0 && Co % DW_BO == 0;
+    // The MFMA kernel addresses X, dY and N through 32-bit buffer offsets.
+    p.mfma = bf16 && Ci % DW_BI == 0 && Co % DW_BO == 0 && n * Ci * 2 <= kMaxRange &&
+             n * Co * 2 <= kMaxRange && n * 36 <= kMaxRange;
     int64_t slices;
     const int64_t step = p.mfma ? DW_TK : 16;
     if (p.mfma) {
@@ -304,16 +365,16 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
     const bool direct = plan.slices == 1;
     hipError_t err;
     if (plan.mfma) {
-        // 144 KiB of dynamic LDS: above the default limit, so raise it once.
+        // 145.5 KiB of dynamic LDS: above the default limit, so raise it once.
         static const hipError_t attr = hipFuncSetAttribute(
             reinterpret_cast<const void*>(k_dw_mfma), hipFuncAttributeMaxDynamicSharedMemorySize,
-            static_cast<int>(2 * DW_BUF * sizeof(uint16_t)));
+            static_cast<int>(DW_LDS));
         if (attr != hipSuccess) return attr;
         dim3 grid(3 * (Ci / DW_BI) * (Co / DW_BO) * plan.slices);
-        hipLaunchKernelGGL(k_dw_mfma, grid, dim3(DW_THREADS), 2 * DW_BUF * sizeof(uint16_t), stream, static_cast<const uint16_t*>(X), N,
+        hipLaunchKernelGGL(k_dw_mfma, grid, dim3(DW_THREADS), DW_LDS, stream, static_cast<const uint16_t*>(X), N,
                            static_cast<const uint16_t*>(dY), direct ? dW : part,
                            db ? (direct ? db : dbpart) : nullptr, static_cast<int>(n), Ci, Co,
-                           plan.slice_tokens, direct ? 1 : 0, accumulate);
+                           static_cast<int>(plan.slice_tokens), direct ? 1 : 0, accumulate);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     } else {
         err = launch_dw_valu(bf16, X, N, dY, direct ? dW : part, n, Ci, Co, plan.slices, plan.slice_tokens,

@@ -40,7 +40,9 @@ __device__ __forceinline__ int clamp_index(int m, int n) {
 
 // 8x8 transpose of 16-bit elements held as 8 rows of 4 dwords (element 2d in
 // the low half of dword d, element 2d+1 in the high half).  out[c] is column c
-// of the input, in the same packing.
+// of the input, in the same packing.  Each output dword takes one half of a
+// dword from each of two neighbouring rows: one byte permute (v_perm_b32,
+// bytes 0-3 from the second operand, 4-7 from the first).
 __device__ __forceinline__ void transpose8x8_b16(const uint4 in[8], uint4 out[8]) {
     uint32_t r[8][4];
 #pragma unroll
@@ -49,14 +51,35 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 in[8], uint4 out[8]
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
+        // even c: low halves  (a & 0xffff) | (b << 16)
+        // odd c:  high halves (a >> 16) | (b & 0xffff0000)
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
         uint32_t o[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint32_t a = r[2 * p][c >> 1], b = r[2 * p + 1][c >> 1];
-            o[p] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-        }
+        for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(r[2 * p + 1][c >> 1], r[2 * p][c >> 1], sel);
         out[c] = make_uint4(o[0], o[1], o[2], o[3]);
     }
+}
+
+// Raw buffer loads: a 128-bit resource (base, byte range) in scalar
+// registers, 32-bit per-lane byte offsets, and the hardware range check: a
+// load at an offset at or past the range returns zeros and makes no memory
+// request.  kOob is such an offset for every range used here (all ranges are
+// at most 2^31 bytes; callers check that on the host).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;
+constexpr uint32_t kMaxRange = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // dword 3 = 0x00020000: untyped 32-bit data format, the CDNA default
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ int load4(rsrc_t r, uint32_t off) {
+    return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 // Workgroups of a 1-D grid go to the 8 XCDs of the chip round-robin by

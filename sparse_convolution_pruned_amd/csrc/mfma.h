@@ -34,14 +34,4 @@ __device__ __forceinline__ bf16x8_t frag_row(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
 
-// 8 bf16 down a column of a row-major LDS tile: p[0], p[pitch], ... p[7*pitch].
-// Used where the contraction index runs along rows (the MFMA needs 8
-// consecutive k per lane); 32 lanes read one 64-byte row segment per step.
-__device__ __forceinline__ bf16x8_t frag_col(const uint16_t* p, int pitch) {
-    short8_t v;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = static_cast<short>(p[t * pitch]);
-    return __builtin_bit_cast(bf16x8_t, v);
-}
-
 }  // namespace svc
