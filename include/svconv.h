@@ -58,7 +58,10 @@ typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 /* Kernel choice for the convolution passes.  AUTO picks the bf16 MFMA kernel
  * when dtype is bf16, C_in % 32 == 0 and C_out % 16 == 0 (dX: the same with
- * C_in and C_out swapped), and the VALU kernel otherwise. */
+ * C_in and C_out swapped) and the gathered input (n x contracted channels
+ * bf16) spans at most 2 GiB, and the VALU kernel otherwise.  The weight and
+ * bias gradients use the MFMA kernel under the same size bound with both
+ * channel counts multiples of 128. */
 typedef enum sv_kernel { SV_KERNEL_AUTO = 0, SV_KERNEL_VALU = 1, SV_KERNEL_MFMA = 2 } sv_kernel;
 
 /* Bits of the device error flag written by sv_build_index. */

@@ -19,8 +19,8 @@ size_t align_up(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 // Which conv kernel runs a pass; SV_ERR_UNSUPPORTED when MFMA is forced and
 // does not fit.
-sv_status choose(sv_kernel req, sv_dtype dt, bool dx, int Ci, int Co, bool* use_mfma) {
-    const bool fits = dt == SV_BF16 && conv_mfma_supported(dx, Ci, Co);
+sv_status choose(sv_kernel req, sv_dtype dt, bool dx, int Ci, int Co, int64_t n, bool* use_mfma) {
+    const bool fits = dt == SV_BF16 && conv_mfma_supported(dx, Ci, Co, n);
     if (req == SV_KERNEL_MFMA && !fits) return SV_ERR_UNSUPPORTED;
     *use_mfma = (req == SV_KERNEL_MFMA) || (req == SV_KERNEL_AUTO && fits);
     return SV_OK;
@@ -49,7 +49,7 @@ sv_status run_fwd_prepared(bool mfma, const void* X, const int32_t* N, const voi
 sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int64_t n, int32_t Ci,
                  int32_t Co, sv_dtype dt, sv_kernel kernel, hipStream_t s) {
     bool mfma = false;
-    sv_status st = choose(kernel, dt, true, Ci, Co, &mfma);
+    sv_status st = choose(kernel, dt, true, Ci, Co, n, &mfma);
     if (st != SV_OK) return st;
     if (n == 0) return SV_OK;
     if (mfma)
@@ -60,8 +60,8 @@ sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int
 }
 
 // Bytes of repacked weights the forward needs when the MFMA kernel may run.
-size_t fwd_ws_bytes(int32_t Ci, int32_t Co, sv_dtype dt) {
-    return (dt == SV_BF16 && conv_mfma_supported(false, Ci, Co)) ? conv_mfma_fwd_workspace(Ci, Co) : 0;
+size_t fwd_ws_bytes(int32_t Ci, int32_t Co, sv_dtype dt, int64_t n) {
+    return (dt == SV_BF16 && conv_mfma_supported(false, Ci, Co, n)) ? conv_mfma_fwd_workspace(Ci, Co) : 0;
 }
 
 }  // namespace
@@ -87,7 +87,7 @@ sv_status sv_sparseconv2d_fwd(const void* X, const int32_t* N, const void* Wt, c
     if (st != SV_OK) return st;
     if (!Wt || (n > 0 && (!X || !N || !Y))) return SV_ERR_INVALID_ARG;
     bool mfma = false;
-    if ((st = choose(kernel, dtype, false, C_in, C_out, &mfma)) != SV_OK) return st;
+    if ((st = choose(kernel, dtype, false, C_in, C_out, n, &mfma)) != SV_OK) return st;
     if (mfma) {
         const size_t need = conv_mfma_fwd_workspace(C_in, C_out);
         if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
@@ -111,7 +111,7 @@ sv_status sv_sparseconv2d_bwd_dx(const void* dY, const int32_t* N, const void* W
 
 size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype) {
     if (n < 0 || C_in <= 0 || C_out <= 0 || !valid_dtype(dtype)) return 0;
-    if (op == SV_OP_FWD) return fwd_ws_bytes(C_in, C_out, dtype);
+    if (op == SV_OP_FWD) return fwd_ws_bytes(C_in, C_out, dtype, n);
     if (op != SV_OP_DW) return 0;
     return dw_workspace_bytes(plan_dw(n, C_in, C_out, dtype == SV_BF16));
 }
@@ -164,7 +164,7 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
                                                                           d->dtype == SV_BF16)));
     }
     L->n_bytes = align_up(static_cast<size_t>(L->max_tokens) * 9 * sizeof(int32_t));
-    L->w_bytes = (passes & SV_PASS_FWD) ? fwd_ws_bytes(d->C_in, d->C_out, d->dtype) : 0;
+    L->w_bytes = (passes & SV_PASS_FWD) ? fwd_ws_bytes(d->C_in, d->C_out, d->dtype, L->max_tokens) : 0;
     L->total = L->n_bytes + L->w_bytes + L->dw_bytes;
     return true;
 }
@@ -191,9 +191,13 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     if ((passes & SV_PASS_DX) && (!d->dY || !d->Wt || !d->dX)) return SV_ERR_INVALID_ARG;
     if ((passes & SV_PASS_DW) && (!d->X || !d->dY || !d->dW)) return SV_ERR_INVALID_ARG;
     bool m;
-    if ((passes & SV_PASS_FWD) && choose(d->kernel, d->dtype, false, d->C_in, d->C_out, &m) != SV_OK)
+    // Every chunk holds at most L.max_tokens tokens: a kernel that fits the
+    // largest chunk fits them all.
+    if ((passes & SV_PASS_FWD) &&
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.max_tokens, &m) != SV_OK)
         return SV_ERR_UNSUPPORTED;
-    if ((passes & SV_PASS_DX) && choose(d->kernel, d->dtype, true, d->C_in, d->C_out, &m) != SV_OK)
+    if ((passes & SV_PASS_DX) &&
+        choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.max_tokens, &m) != SV_OK)
         return SV_ERR_UNSUPPORTED;
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return SV_ERR_WORKSPACE;
     if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256) return SV_ERR_INVALID_ARG;
@@ -204,7 +208,7 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     void* dws = static_cast<char*>(workspace) + L.n_bytes + L.w_bytes;
     bool fwd_mfma = false;
     if (passes & SV_PASS_FWD) {
-        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, &fwd_mfma);
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.max_tokens, &fwd_mfma);
         if (fwd_mfma && d->T > 0) {
             // the weights are repacked once for every chunk
             sv_status st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(d->Wt),

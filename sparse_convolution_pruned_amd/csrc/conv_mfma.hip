@@ -153,11 +153,13 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         sRow[e] = static_cast<short>(m < 0 ? CM_ZROW : (window ? m - wlo : e / 9));
     }
 
-    // ---- staging helpers (16-byte pieces; channels past K load as zeros).
-    // Loads are unconditional, from addresses clamped into the valid range;
-    // pieces outside the tile are zeroed when stored to LDS, a round or more
-    // later.  Testing right after the load would make the wave wait for it
-    // (and for every load queued before it) at the point of issue.
+    // ---- staging helpers: raw buffer loads, 16-byte pieces.  Pieces outside
+    // the tile (rows past the window, output channels past NO, channels past
+    // K in a 32-channel tail chunk, -1 entries in gather mode) get an
+    // out-of-range offset and read as zeros, so every store below is plain
+    // and no load sits behind a branch.
+    const rsrc_t rA = make_rsrc(A, static_cast<uint32_t>(n) * K * 2);
+    const rsrc_t rB = make_rsrc(B, 9u * NO * K * 2);
     auto kc_of = [&](int c) { return min(CM_KC, K - c * CM_KC); };
     auto load_window = [&](int c, uint4* regs) {
         const int c0 = c * CM_KC, kc = kc_of(c);
@@ -165,42 +167,44 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         for (int u = 0; u < CM_WREGS; ++u) {
             const int q = tid + 256 * u;
             const int r = q >> 3, ch = q & 7;
-            regs[u] = *reinterpret_cast<const uint4*>(
-                A + static_cast<int64_t>(wlo + min(r, span - 1)) * K + c0 + min(ch * 8, kc - 8));
+            const bool ok = r < span && ch * 8 < kc;
+            regs[u] = load16(rA, ok ? (static_cast<uint32_t>(wlo + r) * K + c0 + ch * 8) * 2 : kOob);
         }
     };
-    auto store_window = [&](int c, const uint4* regs) {
-        const int kc = kc_of(c);
+    auto store_window = [&](const uint4* regs) {
 #pragma unroll
         for (int u = 0; u < CM_WREGS; ++u) {
             const int q = tid + 256 * u;
             const int r = q >> 3, ch = q & 7;     // r < CM_WIN: rows past span hold zeros
-            *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) =
-                (r < span && ch * 8 < kc) ? regs[u] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) = regs[u];
         }
     };
     // Weight tile of round rr (chunk rr / 9, tap rr % 9): B[8-j][n0 + nn][c0 + ...].
+    // The per-thread part of the offset is fixed; a round adds a uniform part.
+    uint32_t bOff[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int q = tid + 256 * u;
+        const int nn = q >> 3, ch = q & 7;
+        bOff[u] = n0 + nn < NO ? (static_cast<uint32_t>(n0 + nn) * K + ch * 8) * 2 : kOob;
+    }
     auto load_B = [&](int rr, uint4* regs) {
         const int c = rr / 9, j = rr - c * 9;
         const int c0 = c * CM_KC, kc = kc_of(c);
-        const uint16_t* __restrict__ Bj = B + static_cast<int64_t>(8 - j) * NO * K;
+        const uint32_t roff = (static_cast<uint32_t>(8 - j) * NO * K + c0) * 2;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int q = tid + 256 * u;
-            const int nn = q >> 3, ch = q & 7;
-            regs[u] = *reinterpret_cast<const uint4*>(
-                Bj + static_cast<int64_t>(min(n0 + nn, NO - 1)) * K + c0 + min(ch * 8, kc - 8));
+            const int ch = (tid + 256 * u) & 7;
+            regs[u] = load16(rB, ch * 8 < kc ? bOff[u] + roff : kOob);
         }
     };
-    auto store_B = [&](int buf, int rr, const uint4* regs) {
+    auto store_B = [&](int buf, const uint4* regs) {
         uint16_t* sb = sB[buf];
-        const int kc = kc_of(rr / 9);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int q = tid + 256 * u;
             const int nn = q >> 3, ch = q & 7;
-            *reinterpret_cast<uint4*>(&sb[nn * CM_LDB + ch * 8]) =
-                (n0 + nn < NO && ch * 8 < kc) ? regs[u] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(&sb[nn * CM_LDB + ch * 8]) = regs[u];
         }
     };
     // Gather mode: the 128 rows of tap j, chunk c, straight into sA.
@@ -212,10 +216,9 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
             const int q = tid + 256 * u;
             const int r = q >> 3, ch = q & 7;
             const int m = sN[r * 9 + j];
-            const uint4 v = *reinterpret_cast<const uint4*>(
-                A + static_cast<int64_t>(max(m, 0)) * K + c0 + min(ch * 8, kc - 8));
+            const bool ok = m >= 0 && ch * 8 < kc;
             *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) =
-                (m >= 0 && ch * 8 < kc) ? v : make_uint4(0, 0, 0, 0);
+                load16(rA, ok ? (static_cast<uint32_t>(m) * K + c0 + ch * 8) * 2 : kOob);
         }
     };
 
@@ -228,11 +231,11 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     uint4 breg[4], wreg[CM_WREGS];
     if (window && span > 0) {
         load_window(0, wreg);
-        store_window(0, wreg);
+        store_window(wreg);
     }
     load_B(0, breg);
-    store_B(0, 0, breg);
-    if (R > 1) load_B(1, breg);
+    store_B(0, breg);
+    load_B(min(1, R - 1), breg);
     __syncthreads();
 
     for (int r = 0; r < R; ++r) {
@@ -244,12 +247,16 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         // Stage the next round's weights into the other buffer (last read in
         // round r - 1, before the previous barrier) and start loading the
         // one after: issued ahead of this round's MFMAs so that their
-        // latency hides behind the matrix work.
-        if (r + 1 < R) {
-            store_B((r + 1) & 1, r + 1, breg);
-            if (r + 2 < R) load_B(r + 2, breg);
-        }
+        // latency hides behind the matrix work.  Mid-chunk, the next chunk's
+        // window rows go out first, so that they never queue behind (and
+        // wait for) the weight loads of this round.  The weight staging runs
+        // unconditionally (the last two rounds re-stage the final tile into
+        // the idle buffer): a branch around it would leave the compiler
+        // unsure whether the registers are still being loaded, and it would
+        // wait for every load in flight before reusing them.
+        store_B((r + 1) & 1, breg);
         if (window && span > 0 && j == 4 && c + 1 < nchunks) load_window(c + 1, wreg);
+        load_B(min(r + 2, R - 1), breg);
         int arow[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) arow[mb] = sRow[(wm * 64 + mb * 32 + l32) * 9 + j];
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         if (r + 1 < R) {
             if (window && span > 0 && (r + 1) % 9 == 0) {
                 __syncthreads();           // every wave is done with this chunk's window
-                store_window(c + 1, wreg);
+                store_window(wreg);
             }
             __syncthreads();
         }
@@ -319,9 +326,10 @@ __global__ __launch_bounds__(256) void k_repack_fwd(const uint16_t* __restrict__
     }
 }
 
-bool conv_mfma_supported(bool dx, int Ci, int Co) {
+bool conv_mfma_supported(bool dx, int Ci, int Co, int64_t n) {
     const int K = dx ? Co : Ci, NO = dx ? Ci : Co;
-    return K > 0 && NO > 0 && K % 32 == 0 && NO % 16 == 0;
+    return K > 0 && NO > 0 && K % 32 == 0 && NO % 16 == 0 && n * K * 2 <= kMaxRange &&
+           9ll * NO * K * 2 <= kMaxRange;
 }
 
 size_t conv_mfma_fwd_workspace(int Ci, int Co) {

@@ -120,7 +120,9 @@ hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const ui
                                    hipStream_t stream);
 hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, hipStream_t stream);
 size_t conv_mfma_fwd_workspace(int Ci, int Co);
-bool conv_mfma_supported(bool dx, int Ci, int Co);
+// bf16, contracted channels a multiple of 32, output channels of 16, and
+// the n rows of A within the 2 GiB range of a buffer load.
+bool conv_mfma_supported(bool dx, int Ci, int Co, int64_t n);
 
 // dW: split-K plan, partial kernels, reduction.
 struct DwPlan {
