@@ -280,8 +280,12 @@ __global__ __launch_bounds__(256) void k_db_partial(const T* __restrict__ dY, fl
 }
 
 // out[e] (+)= sum_{s < slices} part[s][e], s ascending (4 floats per thread).
+// The db partials ride along: block 0 also reduces them (Co floats, one per
+// thread, same order), which saves a launch.
 __global__ __launch_bounds__(256) void k_reduce_slices4(const float4* __restrict__ part, float4* __restrict__ out,
-                                                        int64_t count4, int slices, int accumulate) {
+                                                        int64_t count4, int slices, int accumulate,
+                                                        const float* __restrict__ dbpart, float* __restrict__ db,
+                                                        int Co) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < count4; e += stride) {
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -295,6 +299,21 @@ __global__ __launch_bounds__(256) void k_reduce_slices4(const float4* __restrict
         }
         out[e] = v;
     }
+    if (db && blockIdx.x == 0)
+        for (int o = threadIdx.x; o < Co; o += blockDim.x) {
+            // loads issued 8 at a time, added in slice order
+            float v = 0.f;
+            int s = 0;
+            for (; s + 8 <= slices; s += 8) {
+                float p[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) p[u] = dbpart[static_cast<int64_t>(s + u) * Co + o];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v += p[u];
+            }
+            for (; s < slices; ++s) v += dbpart[static_cast<int64_t>(s) * Co + o];
+            db[o] = accumulate ? db[o] + v : v;
+        }
 }
 
 // out[e] (+)= sum_{s < slices} part[s][e], s ascending.
@@ -393,13 +412,16 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
     }
+    // db partials of the MFMA kernel go through the dW reduction launch.
+    bool db_done = db && plan.mfma && direct;
     if (!direct) {
         const int64_t count = 9ll * Ci * Co;
         if (count % 4 == 0) {
             const int blocks = static_cast<int>(std::min<int64_t>(ceil_div(count / 4, 256), 8192));
             hipLaunchKernelGGL(k_reduce_slices4, dim3(blocks), dim3(256), 0, stream,
                                reinterpret_cast<const float4*>(part), reinterpret_cast<float4*>(dW), count / 4,
-                               plan.slices, accumulate);
+                               plan.slices, accumulate, db ? dbpart : nullptr, db, Co);
+            db_done = db != nullptr;
         } else {
             const int blocks = static_cast<int>(std::min<int64_t>(ceil_div(count, 256), 8192));
             hipLaunchKernelGGL(k_reduce_slices, dim3(blocks), dim3(256), 0, stream, part, dW, count,
@@ -407,7 +429,7 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
         }
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    if (db && !(plan.mfma && direct)) {
+    if (db && !db_done) {
         const int blocks = static_cast<int>(ceil_div(Co, 256));
         hipLaunchKernelGGL(k_reduce_slices, dim3(blocks), dim3(256), 0, stream, dbpart, db,
                            static_cast<int64_t>(Co), plan.slices, accumulate);
