@@ -52,7 +52,7 @@ constexpr int CM_KC = 64;               // channels per round
 constexpr int CM_WIN = 192;             // window rows held in LDS
 constexpr int CM_ZROW = CM_WIN;         // an all-zero row: target of -1 entries
 constexpr int CM_LDA = CM_KC + 8;       // 144 B pitch: conflict-free 16-byte row reads
-constexpr int CM_LDB = CM_KC + 8;       // 144 B pitch
+constexpr int CM_LDB = CM_KC;           // weight tile rows: 128 B, XOR-swizzled 16-byte chunks
 constexpr int CM_SB = CM_BN * CM_LDB;
 constexpr int CM_WREGS = (CM_WIN * (CM_KC / 8) + 255) / 256;   // window pieces per thread (6)
 
@@ -69,7 +69,8 @@ __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) a[ks][mb] = frag_row(&sA[arow[mb] * CM_LDA + kof]);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) b[ks][nb] = frag_row(&sb[(wn * 64 + nb * 32 + l32) * CM_LDB + kof]);
+        for (int nb = 0; nb < 2; ++nb)
+            b[ks][nb] = frag_row(&sb[(wn * 64 + nb * 32 + l32) * CM_LDB + (((2 * ks + lhi) ^ (l32 & 7)) << 3)]);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ out, int n, int K, int NO) {
     __shared__ __align__(16) uint16_t sA[(CM_WIN + 1) * CM_LDA];
-    __shared__ __align__(16) uint16_t sB[2][CM_SB];
+    __shared__ __align__(16) uint16_t sB[2][CM_SB];   // weight tiles, written by direct loads
     __shared__ int sN[CM_BM * 9];
     __shared__ short sRow[CM_BM * 9];
     __shared__ int sLo, sHi;
@@ -179,33 +180,36 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
             *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) = regs[u];
         }
     };
-    // Weight tile of round rr (chunk rr / 9, tap rr % 9): B[8-j][n0 + nn][c0 + ...].
-    // The per-thread part of the offset is fixed; a round adds a uniform part.
+    // Weight tile of round rr (chunk rr / 9, tap rr % 9): B[8-j][n0 + nn][c0 + ...],
+    // loaded straight into LDS (buffer_load ... lds: lane L of an
+    // instruction writes the 16 bytes at the instruction's LDS base + 16 L),
+    // so it needs no registers and no LDS store instructions.  Row nn's
+    // 16-byte chunk ch sits at position ch ^ (nn & 7) of its 128-byte row;
+    // the fragment reads of 8 consecutive rows then hit 8 distinct bank
+    // groups.  Each wave issues 4 of the tile's 16 instructions; the lane
+    // chooses the chunk that belongs in its slot.  The per-lane part of the
+    // offset is fixed; a round adds a uniform part.
     uint32_t bOff[4];
+    int bChunk;
+    {
+        const int pos = lane & 7, rsub = lane >> 3;
+        bChunk = pos ^ rsub;                      // rows of an instruction are 8 apart in their low bits
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int q = tid + 256 * u;
-        const int nn = q >> 3, ch = q & 7;
-        bOff[u] = n0 + nn < NO ? (static_cast<uint32_t>(n0 + nn) * K + ch * 8) * 2 : kOob;
+        for (int u = 0; u < 4; ++u) {
+            const int nn = (wave * 4 + u) * 8 + rsub;
+            bOff[u] = n0 + nn < NO ? (static_cast<uint32_t>(n0 + nn) * K + bChunk * 8) * 2 : kOob;
+        }
     }
-    auto load_B = [&](int rr, uint4* regs) {
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    auto issue_B = [&](int rr, int buf) {
         const int c = rr / 9, j = rr - c * 9;
         const int c0 = c * CM_KC, kc = kc_of(c);
         const uint32_t roff = (static_cast<uint32_t>(8 - j) * NO * K + c0) * 2;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int ch = (tid + 256 * u) & 7;
-            regs[u] = load16(rB, ch * 8 < kc ? bOff[u] + roff : kOob);
-        }
-    };
-    auto store_B = [&](int buf, const uint4* regs) {
         uint16_t* sb = sB[buf];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q = tid + 256 * u;
-            const int nn = q >> 3, ch = q & 7;
-            *reinterpret_cast<uint4*>(&sb[nn * CM_LDB + ch * 8]) = regs[u];
-        }
+        for (int u = 0; u < 4; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t*)(sb + (wave * 4 + u) * 512), 16,
+                                                     bChunk * 8 < kc ? bOff[u] + roff : kOob, 0, 0, 0);
     };
     // Gather mode: the 128 rows of tap j, chunk c, straight into sA.
     auto stage_gather = [&](int rr) {
@@ -228,15 +232,13 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
-    uint4 breg[4], wreg[CM_WREGS];
+    uint4 wreg[CM_WREGS];
     if (window && span > 0) {
         load_window(0, wreg);
         store_window(wreg);
     }
-    load_B(0, breg);
-    store_B(0, breg);
-    load_B(min(1, R - 1), breg);
-    __syncthreads();
+    issue_B(0, 0);
+    __syncthreads();                      // also waits for the direct loads
 
     for (int r = 0; r < R; ++r) {
         const int c = r / 9, j = r - c * 9;
@@ -244,19 +246,12 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
             stage_gather(r);
             __syncthreads();
         }
-        // Stage the next round's weights into the other buffer (last read in
-        // round r - 1, before the previous barrier) and start loading the
-        // one after: issued ahead of this round's MFMAs so that their
-        // latency hides behind the matrix work.  Mid-chunk, the next chunk's
-        // window rows go out first, so that they never queue behind (and
-        // wait for) the weight loads of this round.  The weight staging runs
-        // unconditionally (the last two rounds re-stage the final tile into
-        // the idle buffer): a branch around it would leave the compiler
-        // unsure whether the registers are still being loaded, and it would
-        // wait for every load in flight before reusing them.
-        store_B((r + 1) & 1, breg);
+        // The next round's weights go into the other buffer (last read in
+        // round r - 1, before the previous barrier), issued ahead of this
+        // round's MFMAs; the barrier at the end of the round waits for them.
+        // Mid-chunk, the next chunk's window rows go out first.
         if (window && span > 0 && j == 4 && c + 1 < nchunks) load_window(c + 1, wreg);
-        load_B(min(r + 2, R - 1), breg);
+        if (r + 1 < R) issue_B(r + 1, (r + 1) & 1);
         int arow[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) arow[mb] = sRow[(wm * 64 + mb * 32 + l32) * 9 + j];
@@ -274,10 +269,13 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     }
 
     // ---- epilogue: bias, round to bf16, stage the 128 x 128 tile in LDS
-    // (over the weight buffers), then write whole 16-byte row pieces.
+    // (rows 0-63 over the window, rows 64-127 over the weight buffers), then
+    // write whole 16-byte row pieces.
     constexpr int OLD = CM_BN + 8;      // 272-byte pitch: rows 4 apart in opposite bank halves
-    static_assert(CM_BM * OLD <= 2 * CM_SB, "output tile must fit the weight buffers");
-    uint16_t* sOut = &sB[0][0];
+    static_assert(64 * OLD <= (CM_WIN + 1) * CM_LDA && 64 * OLD <= 2 * CM_SB,
+                  "output tile halves must fit the window and the weight buffers");
+    uint16_t* const sOutLo = sA;
+    uint16_t* const sOutHi = &sB[0][0];
     __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -289,7 +287,8 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
             for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    sOut[(wm * 64 + mb * 32 + g * 8 + lhi * 4 + q) * OLD + cl] = f32_to_bf16(acc[mb][nb][g * 4 + q] + bv);
+                    (wm ? sOutHi : sOutLo)[(mb * 32 + g * 8 + lhi * 4 + q) * OLD + cl] =
+                        f32_to_bf16(acc[mb][nb][g * 4 + q] + bv);
     }
     __syncthreads();
 #pragma unroll
@@ -299,7 +298,8 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         const int64_t row = k0 + rl;
         const int col = n0 + ch * 8;
         if (row < n && col < NO)
-            *reinterpret_cast<uint4*>(out + row * NO + col) = *reinterpret_cast<const uint4*>(&sOut[rl * OLD + ch * 8]);
+            *reinterpret_cast<uint4*>(out + row * NO + col) =
+                *reinterpret_cast<const uint4*>(&(rl < 64 ? sOutLo : sOutHi)[(rl & 63) * OLD + ch * 8]);
     }
 }
 
