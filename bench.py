@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4"])
     p.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--dw-stream", choices=["side", "same"], default="side",
+                   help="run each layer's weight gradient on a second stream, concurrent with its "
+                        "input gradient (side), or in order on one stream (same)")
     p.add_argument("--cpu-frames", type=int, default=384,
                    help="frames of the workload the CPU oracle is timed on")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -55,7 +58,7 @@ def parse():
 class StagedRun:
     """Config c5: nested stages, 2 layers per stage, fwd + bwd through all."""
 
-    def __init__(self, kernel="auto"):
+    def __init__(self, kernel="auto", dw_stream="side"):
         import torch
         from sparse_convolution_pruned_amd import ops, workloads as wl
 
@@ -100,6 +103,11 @@ class StagedRun:
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
         self.fws = torch.empty(max(256, ops.sv_workspace_bytes(ops.SV_OP_FWD, 0, C, C, bf)),
                                dtype=torch.uint8, device="cuda")
+        # dW and dX of a layer both read dY and nothing else either writes, so
+        # dW can run on a second stream (default priority) while dX runs on
+        # the caller's; the streams join at the end of the step.
+        self.side = torch.cuda.Stream() if dw_stream == "side" else None
+        self.ready = [torch.cuda.Event() for _ in range(self.L)]
 
     def flops(self):
         """Effective FLOPs per step: 2 * n * 9 * C_in * C_out per pass, all
@@ -107,8 +115,13 @@ class StagedRun:
         C = self.C
         return sum(3 * 2 * self.ns[self.stage_of[l]] * 9 * C * C for l in range(self.L))
 
-    def step(self, ev=None):
+    def step(self, ev=None, overlap=True):
+        """One pass of the whole hot path.  With `overlap` each layer's dW
+        runs on the side stream concurrently with its dX; without it (the
+        instrumented repeat) every call runs alone, in order, on the current
+        stream, so that its HIP events bracket that call's kernels only."""
         ops, kern = self.ops, self.kernel
+        side = self.side if overlap else None
         rec = ev.record if ev is not None else (lambda *a, **k: None)
         S = self.S
         for s in range(len(self.ns)):
@@ -126,11 +139,21 @@ class StagedRun:
                                     workspace=self.fws)
             rec("fwd", t, units=self.ns[s])
         g = self.dy_last
+        main = self.torch.cuda.current_stream()
         for l in reversed(range(self.L)):
             s = self.stage_of[l]
-            t = rec("dw", None)
-            ops.sv_sparseconv2d_bwd_dw(self.xs[l], self.N[s], g, self.dW[l], self.db[l], False, self.ws)
-            rec("dw", t, units=self.ns[s])
+            if side is not None:
+                # dY of this layer is ready on the main stream at this point
+                self.ready[l].record(main)
+                with self.torch.cuda.stream(side):
+                    side.wait_event(self.ready[l])
+                    t = rec("dw", None)
+                    ops.sv_sparseconv2d_bwd_dw(self.xs[l], self.N[s], g, self.dW[l], self.db[l], False, self.ws)
+                    rec("dw", t, units=self.ns[s])
+            else:
+                t = rec("dw", None)
+                ops.sv_sparseconv2d_bwd_dw(self.xs[l], self.N[s], g, self.dW[l], self.db[l], False, self.ws)
+                rec("dw", t, units=self.ns[s])
             t = rec("dx", None)
             ops.sv_sparseconv2d_bwd_dx(g, self.N[s], self.W[l], self.gx[l], kern)
             rec("dx", t, units=self.ns[s])
@@ -140,6 +163,8 @@ class StagedRun:
                 ops.sv_stage_scatter(g, self.sels[s], self.gscat[l])
                 rec("scatter", t, units=self.ns[s])
                 g = self.gscat[l]
+        if side is not None:
+            main.wait_stream(side)          # the next step overwrites the activations dW reads
 
     def cpu_sample(self, frames, min_seconds=10.0):
         """The oracle on the first `frames` frames of the same workload:
@@ -314,7 +339,7 @@ def main():
     if args.workload != "c5":
         return layer_workload(args)
 
-    run = StagedRun(args.kernel)
+    run = StagedRun(args.kernel, args.dw_stream)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run.step()
@@ -333,12 +358,14 @@ def main():
     fl = run.flops()
     tflops = fl / (wall / args.steps) / 1e12
 
-    # instrumented timed region: the same K steps with HIP events per call
+    # instrumented timed region: the same K steps with HIP events per call,
+    # every call alone on the current stream (no dW/dX overlap), so that the
+    # per-kernel durations are the kernels' own
     ev = Events(torch)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(args.steps):
-        run.step(ev)
+        run.step(ev, overlap=False)
     torch.cuda.synchronize()
     ms_instr = (time.perf_counter() - t1) * 1e3 / args.steps
     kinds = ev.summary()
@@ -406,6 +433,7 @@ def main():
                         "U[.15,.3]), 2 layers per stage, C_in=C_out=256, fwd+bwd through 6 layers",
             "tokens_per_stage": run.ns,
             "kernel": args.kernel,
+            "dw_stream": args.dw_stream,
             "flops_per_step": fl,
         },
         "hbm_gbps_compulsory": round(step_bytes / (wall / args.steps) / 1e9, 1),
