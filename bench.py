@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "SparseConv2D fwd+bwd effective TFLOP/s & HBM GB/s vs roofline, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
+PCIE_GBPS_PER_DIRECTION = 64.0   # PCIe 5.0 x16 host link, one direction
 PEAK_F32_TFLOPS = 157.3      # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 
@@ -41,7 +42,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4"])
+    p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4", "c4-host"])
     p.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--dw-stream", choices=["side", "same"], default="side",
@@ -327,6 +328,73 @@ def layer_workload(args):
                       "workspace_mb": round(ws.numel() / 2 ** 20, 2)}), flush=True)
 
 
+def host_stream_workload(args):
+    """Config 4 through the host-streamed chunk driver: X, dY, Y, dX and the
+    coordinates stay in pinned host memory and stream through two device
+    staging sets; the device holds the weights, dW/db and the workspace.
+    Reports the PCIe-inclusive rate and the device memory at the full length
+    and at 256 frames (flat in T)."""
+    import torch
+    from sparse_convolution_pruned_amd import ops, workloads as wl
+
+    cfg = wl.CONFIGS["c4"]
+    bf = torch.bfloat16
+    pm = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
+
+    def setup(L):
+        n, C = L.n, L.X.shape[1]
+        pin = lambda a, d=None: (torch.from_numpy(a).to(d) if d is not None else torch.from_numpy(a)).pin_memory()
+        h = dict(coords=pin(L.coords), offs=pin(L.frame_offsets), X=pin(L.X, bf), dY=pin(L.dY, bf),
+                 Y=torch.empty((n, C), dtype=bf).pin_memory(), dX=torch.empty((n, C), dtype=bf).pin_memory())
+        Wt = torch.from_numpy(L.Wt).to(bf).cuda()
+        b = torch.from_numpy(L.b).to(bf).cuda()
+        dW = torch.empty((9, C, C), dtype=torch.float32, device="cuda")
+        db = torch.empty((C,), dtype=torch.float32, device="cuda")
+        d = ops.make_chunked_host_desc(L.T, L.H, L.W, h["coords"], h["offs"], C, C, bf, cfg["chunk_frames"],
+                                       X_host=h["X"], Wt=Wt, bias=b, Y_host=h["Y"], dY_host=h["dY"],
+                                       dX_host=h["dX"], dW=dW, db=db, kernel=args.kernel)
+        ws = torch.empty(max(256, ops.sv_chunked_host_workspace_bytes(d, pm)), dtype=torch.uint8, device="cuda")
+        return d, ws, (h, Wt, b, dW, db)
+
+    s_h2d, s_d2h = torch.cuda.Stream(), torch.cuda.Stream()
+    peaks = {}
+    for frames in (256, None):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        L = wl.make_layer("c4", scale_T=frames)
+        d, ws, keep = setup(L)
+        reps = args.warmup if frames is not None else 0
+        for _ in range(max(reps, 1)):
+            ops.sv_sparseconv2d_chunked_host(d, pm, ws, s_h2d, s_d2h)
+        torch.cuda.synchronize()
+        peaks[L.T] = (torch.cuda.max_memory_allocated() - base) / 2 ** 20
+        if frames is None:
+            for _ in range(args.warmup):
+                ops.sv_sparseconv2d_chunked_host(d, pm, ws, s_h2d, s_d2h)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                ops.sv_sparseconv2d_chunked_host(d, pm, ws, s_h2d, s_d2h)
+            torch.cuda.synchronize()
+            sec = (time.perf_counter() - t0) / args.steps
+            n, C = L.n, L.X.shape[1]
+            h2d = 4 * n + 4 * (L.T + 1) + 2 * (2 * n * C)     # coords, offsets, X, dY
+            d2h = 2 * (2 * n * C)                             # Y, dX
+            fl = 3 * 2 * n * 9 * C * C
+            out = {"workload": "c4-host", "name": cfg["name"] + ", activations in pinned host memory",
+                   "kernel": args.kernel, "n": n, "ms_per_step": round(sec * 1e3, 4),
+                   "tflops_pcie_inclusive": round(fl / sec / 1e12, 3),
+                   "h2d_gbps": round(h2d / sec / 1e9, 2), "d2h_gbps": round(d2h / sec / 1e9, 2),
+                   "roofline": {"bound": "pcie", "achieved": round(max(h2d, d2h) / sec / 1e9, 2),
+                                "peak": PCIE_GBPS_PER_DIRECTION, "unit": "GB/s per direction",
+                                "frac": round(max(h2d, d2h) / sec / 1e9 / PCIE_GBPS_PER_DIRECTION, 4)},
+                   "workspace_mb": round(ws.numel() / 2 ** 20, 2)}
+    out["device_mem_mb_by_T"] = {str(k): round(v, 1) for k, v in sorted(peaks.items())}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -336,6 +404,8 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == "c4-host":
+        return host_stream_workload(args)
     if args.workload != "c5":
         return layer_workload(args)
 

@@ -180,6 +180,62 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc *desc, uint32_t passes,
  * frame_offsets_host).  Returns 0 and nothing else on bad descriptors. */
 size_t sv_chunked_workspace_bytes(const sv_chunked_desc *desc, uint32_t passes);
 
+/* Host-streamed chunked execution: the chunk driver above with the
+ * per-token tensors left in host memory ("SV-TAD: Native Sparse
+ * Convolutions for Efficient Temporal Action Detection", Key Design 2:
+ * chunking decouples memory from the length of the video; here the device
+ * holds only the weights, the gradients and a workspace sized by one chunk,
+ * so total device memory does not grow with T).
+ *
+ * Each chunk's coordinates, frame offsets, X and dY are copied (by a copy
+ * kernel that reads the page-locked host memory over the bus, so that every
+ * cross-stream wait stays on the GPU) into one of three device staging sets
+ * on `h2d`, computed on `compute` (index build,
+ * then the requested passes, exactly as sv_sparseconv2d_chunked), and its Y
+ * and dX copied back on `d2h`.  Events order the three streams: uploads run
+ * up to two chunks ahead of the compute, and a chunk's results go back while
+ * the next chunks compute.  Results are identical to sv_sparseconv2d_chunked
+ * (same kernels, same chunk order; dW/db accumulate on the device in chunk
+ * order).
+ *
+ * All host arrays must be page-locked (hipHostMalloc, or a pinned torch
+ * tensor; anything else is SV_ERR_INVALID_ARG) and must stay valid, and Y / dX unread, until `compute`
+ * completes: the call returns as soon as the work is enqueued, and it makes
+ * `compute` wait for the last copies, so synchronising `compute` suffices.
+ * The three streams must be distinct.  Uploads start only after the work
+ * already enqueued on `compute`, so back-to-back calls on one workspace are
+ * ordered.  The call creates (and releases) ten HIP events; it allocates no
+ * memory.  On a HIP error part of the work may
+ * already be enqueued. */
+typedef struct sv_chunked_host_desc {
+    int32_t T, H, W;
+    int32_t C_in, C_out;
+    sv_dtype dtype;
+    sv_kernel kernel;
+    int32_t chunk_frames;               /* >= 1                                  */
+    const int32_t *coords_host;         /* pinned host [n]                       */
+    const int32_t *frame_offsets_host;  /* pinned host [T+1]                     */
+    const void *X_host;                 /* pinned host [n][C_in]  (FWD, DW)      */
+    const void *Wt;                     /* device [9][C_in][C_out] (FWD, DX)     */
+    const void *bias;                   /* device [C_out], nullable              */
+    void *Y_host;                       /* pinned host [n][C_out] (FWD)          */
+    const void *dY_host;                /* pinned host [n][C_out] (DX, DW)       */
+    void *dX_host;                      /* pinned host [n][C_in]  (DX)           */
+    float *dW;                          /* device [9][C_in][C_out] fp32 (DW), overwritten */
+    float *db;                          /* device [C_out] fp32, nullable (DW), overwritten */
+    int32_t *err_flag;                  /* device int32, nullable                */
+} sv_chunked_host_desc;
+
+sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc *desc, uint32_t passes,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t compute, hipStream_t h2d, hipStream_t d2h);
+
+/* Workspace bytes sv_sparseconv2d_chunked_host needs: the device driver's
+ * workspace plus three staging sets of the largest chunk's coordinates,
+ * offsets and per-token tensors.  Independent of T.  Returns 0 on bad
+ * descriptors. */
+size_t sv_chunked_host_workspace_bytes(const sv_chunked_host_desc *desc, uint32_t passes);
+
 /* Stage transition between pruning stages (the map is rebuilt at each
  * selection point and reused by the adapter layers in between, Key Design 1):
  * the next stage's packed input keeps a subset of the current rows.

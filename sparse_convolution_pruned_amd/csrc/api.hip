@@ -254,6 +254,242 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     return SV_OK;
 }
 
+// ------------------------------------------------- host-streamed chunk driver
+}  // extern "C"
+
+namespace {
+
+constexpr int kSets = 3;              // staging sets of the host-streamed driver
+
+struct HostLayout {
+    ChunkLayout dev;                  // N table, repacked weights, dW partials
+    int max_frames = 0;
+    size_t coords_b = 0, offs_b = 0, x_b = 0, dy_b = 0, y_b = 0, dx_b = 0;
+    size_t set_bytes = 0;             // one staging set
+    size_t total = 0;
+};
+
+bool host_layout(const sv_chunked_host_desc* d, uint32_t passes, HostLayout* L) {
+    if (!d) return false;
+    // The device driver's layout reads only host fields; build it from a
+    // descriptor carrying the same ones.
+    sv_chunked_desc dd{};
+    dd.T = d->T; dd.H = d->H; dd.W = d->W; dd.C_in = d->C_in; dd.C_out = d->C_out;
+    dd.dtype = d->dtype; dd.kernel = d->kernel; dd.chunk_frames = d->chunk_frames;
+    dd.frame_offsets_host = d->frame_offsets_host;
+    if (!chunk_layout(&dd, passes, &L->dev)) return false;
+    const size_t es = d->dtype == SV_BF16 ? 2 : 4;
+    const size_t tok = static_cast<size_t>(L->dev.max_tokens);
+    L->max_frames = std::min(d->chunk_frames, std::max(d->T, 0));
+    L->coords_b = align_up(tok * sizeof(int32_t));
+    L->offs_b = align_up((static_cast<size_t>(L->max_frames) + 1) * sizeof(int32_t));
+    L->x_b = (passes & (SV_PASS_FWD | SV_PASS_DW)) ? align_up(tok * d->C_in * es) : 0;
+    L->dy_b = (passes & (SV_PASS_DX | SV_PASS_DW)) ? align_up(tok * d->C_out * es) : 0;
+    L->y_b = (passes & SV_PASS_FWD) ? align_up(tok * d->C_out * es) : 0;
+    L->dx_b = (passes & SV_PASS_DX) ? align_up(tok * d->C_in * es) : 0;
+    L->set_bytes = L->coords_b + L->offs_b + L->x_b + L->dy_b + L->y_b + L->dx_b;
+    L->total = L->dev.total + kSets * L->set_bytes;
+    return true;
+}
+
+struct Staging {
+    int32_t* coords;
+    int32_t* offs;
+    char *X, *dY, *Y, *dX;
+};
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_chunked_host_workspace_bytes(const sv_chunked_host_desc* desc, uint32_t passes) {
+    HostLayout L;
+    if (passes & ~(SV_PASS_FWD | SV_PASS_DX | SV_PASS_DW)) return 0;
+    if (!host_layout(desc, passes, &L)) return 0;
+    return L.total;
+}
+
+sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t passes, void* workspace,
+                                       size_t workspace_bytes, hipStream_t compute, hipStream_t h2d,
+                                       hipStream_t d2h) {
+    HostLayout L;
+    if (passes & ~(SV_PASS_FWD | SV_PASS_DX | SV_PASS_DW)) return SV_ERR_INVALID_ARG;
+    if (!host_layout(d, passes, &L)) return SV_ERR_INVALID_ARG;
+    if (!valid_kernel(d->kernel)) return SV_ERR_INVALID_ARG;
+    if (compute == h2d || compute == d2h || h2d == d2h) return SV_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(d->H) * d->W > kMaxCells) return SV_ERR_UNSUPPORTED;
+    const int32_t* ho = d->frame_offsets_host;
+    const int64_t n = ho[d->T];
+    if (n > kMaxRows) return SV_ERR_INVALID_ARG;
+    if (n > 0 && !d->coords_host) return SV_ERR_INVALID_ARG;
+    if ((passes & SV_PASS_FWD) && (!d->X_host || !d->Wt || !d->Y_host)) return SV_ERR_INVALID_ARG;
+    if ((passes & SV_PASS_DX) && (!d->dY_host || !d->Wt || !d->dX_host)) return SV_ERR_INVALID_ARG;
+    if ((passes & SV_PASS_DW) && (!d->X_host || !d->dY_host || !d->dW)) return SV_ERR_INVALID_ARG;
+    bool m;
+    if ((passes & SV_PASS_FWD) &&
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.dev.max_tokens, &m) != SV_OK)
+        return SV_ERR_UNSUPPORTED;
+    if ((passes & SV_PASS_DX) &&
+        choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.dev.max_tokens, &m) != SV_OK)
+        return SV_ERR_UNSUPPORTED;
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return SV_ERR_WORKSPACE;
+    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256) return SV_ERR_INVALID_ARG;
+
+    // Device-visible addresses of the page-locked host arrays; an array
+    // that is not page-locked is an argument error.
+    auto dev_view = [](const void* h, const void** out) {
+        *out = nullptr;
+        if (!h) return true;
+        void* p = nullptr;
+        if (hipHostGetDevicePointer(&p, const_cast<void*>(h), 0) != hipSuccess) return false;
+        *out = p;
+        return true;
+    };
+    const void *coords_dv, *offs_dv, *X_dv, *dY_dv, *Y_dv, *dX_dv;
+    if (!dev_view(d->coords_host, &coords_dv) || !dev_view(d->frame_offsets_host, &offs_dv) ||
+        !dev_view((passes & (SV_PASS_FWD | SV_PASS_DW)) ? d->X_host : nullptr, &X_dv) ||
+        !dev_view((passes & (SV_PASS_DX | SV_PASS_DW)) ? d->dY_host : nullptr, &dY_dv) ||
+        !dev_view((passes & SV_PASS_FWD) ? d->Y_host : nullptr, &Y_dv) ||
+        !dev_view((passes & SV_PASS_DX) ? d->dX_host : nullptr, &dX_dv)) {
+        (void)hipGetLastError();          // clear the query's error state
+        return SV_ERR_INVALID_ARG;
+    }
+
+    // Workspace: N table | repacked weights | dW partials | staging sets.
+    const size_t es = d->dtype == SV_BF16 ? 2 : 4;
+    char* base = static_cast<char*>(workspace);
+    int32_t* Nc = reinterpret_cast<int32_t*>(base);
+    void* Vw = base + L.dev.n_bytes;
+    void* dws = base + L.dev.n_bytes + L.dev.w_bytes;
+    Staging st[kSets];
+    for (int b = 0; b < kSets; ++b) {
+        char* p = base + L.dev.total + b * L.set_bytes;
+        st[b].coords = reinterpret_cast<int32_t*>(p);
+        p += L.coords_b;
+        st[b].offs = reinterpret_cast<int32_t*>(p);
+        p += L.offs_b;
+        st[b].X = p;  p += L.x_b;
+        st[b].dY = p; p += L.dy_b;
+        st[b].Y = p;  p += L.y_b;
+        st[b].dX = p;
+    }
+
+    bool fwd_mfma = false;
+    if (passes & SV_PASS_FWD) {
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.dev.max_tokens, &fwd_mfma);
+        if (fwd_mfma && d->T > 0) {
+            sv_status st0 = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(d->Wt),
+                                                         static_cast<uint16_t*>(Vw), d->C_in, d->C_out, compute));
+            if (st0 != SV_OK) return st0;
+        }
+    }
+    const int nchunks = d->T > 0 ? (d->T + d->chunk_frames - 1) / d->chunk_frames : 0;
+    if (nchunks == 0) {
+        if (!(passes & SV_PASS_DW)) return SV_OK;
+        // No frames at all: the gradients of an empty sum are zero.
+        const DwPlan plan = plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16);
+        return hip_status(launch_dw(plan, d->dtype == SV_BF16, nullptr, Nc, nullptr, d->dW, d->db, 0, d->C_in,
+                                    d->C_out, 0, dws, compute));
+    }
+
+    // Chunk c uses staging set c % kSets.  ev_in[b]: the chunk's inputs are
+    // in set b; ev_done[b]: its compute finished; ev_out[b]: its results left
+    // set b (set b is free again).  ev_start: everything enqueued on
+    // `compute` before this call (a previous call on the same workspace ends
+    // there, after its last copies), which the first uploads wait for.
+    hipEvent_t ev[3 * kSets + 1] = {};
+    for (int i = 0; i < 3 * kSets + 1; ++i)
+        if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
+            for (int k = 0; k < i; ++k) (void)hipEventDestroy(ev[k]);
+            return SV_ERR_HIP;
+        }
+    hipEvent_t* ev_in = ev;
+    hipEvent_t* ev_done = ev + kSets;
+    hipEvent_t* ev_out = ev + 2 * kSets;
+    hipEvent_t ev_start = ev[3 * kSets];
+    auto chunk_bounds = [&](int ci, int* f0, int* f1, int64_t* t0, int64_t* nc) {
+        *f0 = ci * d->chunk_frames;
+        *f1 = std::min(d->T, *f0 + d->chunk_frames);
+        *t0 = ho[*f0];
+        *nc = static_cast<int64_t>(ho[*f1]) - *t0;
+    };
+    auto upload = [&](int ci) -> hipError_t {
+        const int b = ci % kSets;
+        int f0, f1;
+        int64_t t0, nc;
+        chunk_bounds(ci, &f0, &f1, &t0, &nc);
+        hipError_t e = hipSuccess;
+        if (ci >= kSets && (e = hipStreamWaitEvent(h2d, ev_out[b], 0)) != hipSuccess) return e;
+        if ((e = launch_copy_bytes(static_cast<const int32_t*>(coords_dv) + t0, st[b].coords,
+                                   nc * static_cast<int64_t>(sizeof(int32_t)), h2d)))
+            return e;
+        if ((e = launch_copy_bytes(static_cast<const int32_t*>(offs_dv) + f0, st[b].offs,
+                                   (f1 - f0 + 1) * static_cast<int64_t>(sizeof(int32_t)), h2d)))
+            return e;
+        if (L.x_b && (e = launch_copy_bytes(static_cast<const char*>(X_dv) + t0 * d->C_in * es, st[b].X,
+                                            nc * d->C_in * static_cast<int64_t>(es), h2d)))
+            return e;
+        if (L.dy_b && (e = launch_copy_bytes(static_cast<const char*>(dY_dv) + t0 * d->C_out * es, st[b].dY,
+                                             nc * d->C_out * static_cast<int64_t>(es), h2d)))
+            return e;
+        return hipEventRecord(ev_in[b], h2d);
+    };
+    auto run = [&]() -> sv_status {
+        if (hipEventRecord(ev_start, compute) != hipSuccess || hipStreamWaitEvent(h2d, ev_start, 0) != hipSuccess)
+            return SV_ERR_HIP;
+        // Uploads run up to kSets - 1 chunks ahead of the compute.
+        for (int ci = 0; ci < std::min(nchunks, kSets - 1); ++ci)
+            if (upload(ci) != hipSuccess) return SV_ERR_HIP;
+        for (int ci = 0; ci < nchunks; ++ci) {
+            const int b = ci % kSets;
+            int f0, f1;
+            int64_t t0, nc;
+            chunk_bounds(ci, &f0, &f1, &t0, &nc);
+            if (ci + kSets - 1 < nchunks && upload(ci + kSets - 1) != hipSuccess) return SV_ERR_HIP;
+            if (hipStreamWaitEvent(compute, ev_in[b], 0) != hipSuccess) return SV_ERR_HIP;
+            // The staged slices hold global frame offsets and the chunk's own
+            // coordinates; the index kernel reads offs[f0 + f] and coords[k]
+            // for global k, so it gets both bases shifted back.
+            const int32_t* coords_g = st[b].coords - t0;
+            const int32_t* offs_g = st[b].offs - f0;
+            sv_status s2 = hip_status(launch_build_index(coords_g, offs_g, f0, f1 - f0, d->H, d->W, nc, t0, Nc,
+                                                         nullptr, d->err_flag, compute));
+            if (s2 != SV_OK) return s2;
+            if (passes & SV_PASS_FWD) {
+                s2 = run_fwd_prepared(fwd_mfma, st[b].X, Nc, d->Wt, Vw, d->bias, st[b].Y, nc, d->C_in, d->C_out,
+                                      d->dtype, compute);
+                if (s2 != SV_OK) return s2;
+            }
+            if (passes & SV_PASS_DX) {
+                s2 = run_dx(st[b].dY, Nc, d->Wt, st[b].dX, nc, d->C_in, d->C_out, d->dtype, d->kernel, compute);
+                if (s2 != SV_OK) return s2;
+            }
+            if (passes & SV_PASS_DW) {
+                const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16);
+                s2 = hip_status(launch_dw(plan, d->dtype == SV_BF16, st[b].X, Nc, st[b].dY, d->dW, d->db, nc,
+                                          d->C_in, d->C_out, ci == 0 ? 0 : 1, dws, compute));
+                if (s2 != SV_OK) return s2;
+            }
+            if (hipEventRecord(ev_done[b], compute) != hipSuccess) return SV_ERR_HIP;
+            if (hipStreamWaitEvent(d2h, ev_done[b], 0) != hipSuccess) return SV_ERR_HIP;
+            if ((passes & SV_PASS_FWD) &&
+                launch_copy_bytes(st[b].Y, const_cast<char*>(static_cast<const char*>(Y_dv)) + t0 * d->C_out * es,
+                                  nc * d->C_out * static_cast<int64_t>(es), d2h) != hipSuccess)
+                return SV_ERR_HIP;
+            if ((passes & SV_PASS_DX) &&
+                launch_copy_bytes(st[b].dX, const_cast<char*>(static_cast<const char*>(dX_dv)) + t0 * d->C_in * es,
+                                  nc * d->C_in * static_cast<int64_t>(es), d2h) != hipSuccess)
+                return SV_ERR_HIP;
+            if (hipEventRecord(ev_out[b], d2h) != hipSuccess) return SV_ERR_HIP;
+        }
+        // Synchronising `compute` then covers every copy of the call.
+        return hip_status(hipStreamWaitEvent(compute, ev_out[(nchunks - 1) % kSets], 0));
+    };
+    const sv_status result = run();
+    for (int i = 0; i < 3 * kSets + 1; ++i) (void)hipEventDestroy(ev[i]);
+    return result;
+}
+
 sv_status sv_stage_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n_rows, void* dst,
                           int32_t C, sv_dtype dtype, hipStream_t stream) {
     if (n_src < 0 || n_rows < 0 || C <= 0 || !valid_dtype(dtype)) return SV_ERR_INVALID_ARG;

@@ -138,6 +138,9 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
                      const void* dY, float* dW, float* db, int64_t n, int Ci, int Co,
                      int accumulate, void* ws, hipStream_t stream);
 
+// Copies `bytes` bytes with a kernel (either side may be page-locked host
+// memory the device can address).
+hipError_t launch_copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_stage_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n_rows,
                                void* dst, int C, int elem_bytes, hipStream_t stream);
 hipError_t launch_stage_scatter(const void* src, const int32_t* rows, int64_t n_rows, void* dst,

@@ -37,8 +37,8 @@ KERNELS = {"auto": SV_KERNEL_AUTO, "valu": SV_KERNEL_VALU, "mfma": SV_KERNEL_MFM
 SYMBOLS = (
     "sv_build_index", "sv_sparseconv2d_fwd", "sv_sparseconv2d_bwd_dx",
     "sv_sparseconv2d_bwd_dw", "sv_workspace_bytes", "sv_sparseconv2d_chunked",
-    "sv_chunked_workspace_bytes", "sv_stage_gather", "sv_stage_scatter",
-    "sv_status_string", "sv_version",
+    "sv_chunked_workspace_bytes", "sv_sparseconv2d_chunked_host", "sv_chunked_host_workspace_bytes",
+    "sv_stage_gather", "sv_stage_scatter", "sv_status_string", "sv_version",
 )
 
 
@@ -58,6 +58,19 @@ class ChunkedDesc(ctypes.Structure):
         ("frame_offsets_host", ctypes.c_void_p),
         ("X", ctypes.c_void_p), ("Wt", ctypes.c_void_p), ("bias", ctypes.c_void_p),
         ("Y", ctypes.c_void_p), ("dY", ctypes.c_void_p), ("dX", ctypes.c_void_p),
+        ("dW", ctypes.c_void_p), ("db", ctypes.c_void_p), ("err_flag", ctypes.c_void_p),
+    ]
+
+
+class ChunkedHostDesc(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("C_in", ctypes.c_int32), ("C_out", ctypes.c_int32),
+        ("dtype", ctypes.c_int), ("kernel", ctypes.c_int),
+        ("chunk_frames", ctypes.c_int32),
+        ("coords_host", ctypes.c_void_p), ("frame_offsets_host", ctypes.c_void_p),
+        ("X_host", ctypes.c_void_p), ("Wt", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("Y_host", ctypes.c_void_p), ("dY_host", ctypes.c_void_p), ("dX_host", ctypes.c_void_p),
         ("dW", ctypes.c_void_p), ("db", ctypes.c_void_p), ("err_flag", ctypes.c_void_p),
     ]
 
@@ -86,6 +99,8 @@ def load(path: str = LIB_PATH):
         "sv_workspace_bytes": ([E, i64, i32, i32, E], sz),
         "sv_sparseconv2d_chunked": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32, P, sz, P], E),
         "sv_chunked_workspace_bytes": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32], sz),
+        "sv_sparseconv2d_chunked_host": ([ctypes.POINTER(ChunkedHostDesc), ctypes.c_uint32, P, sz, P, P, P], E),
+        "sv_chunked_host_workspace_bytes": ([ctypes.POINTER(ChunkedHostDesc), ctypes.c_uint32], sz),
         "sv_stage_gather": ([P, i64, P, i64, P, i32, E, P], E),
         "sv_stage_scatter": ([P, P, i64, P, i64, i32, E, P], E),
         "sv_status_string": ([E], ctypes.c_char_p),
@@ -232,6 +247,51 @@ def sv_sparseconv2d_chunked(desc: ChunkedDesc, passes: int, workspace=None, stre
     st = load().sv_sparseconv2d_chunked(ctypes.byref(desc), ctypes.c_uint32(passes),
                                         _ptr(workspace), wsb, _stream(stream))
     _check(st, "sv_sparseconv2d_chunked")
+
+
+def _host_ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("host tensor must be in page-locked (pinned) CPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def make_chunked_host_desc(T, H, W, coords_host, frame_offsets_host, C_in, C_out, dtype, chunk_frames,
+                           X_host=None, Wt=None, bias=None, Y_host=None, dY_host=None, dX_host=None,
+                           dW=None, db=None, err_flag=None, kernel="auto"):
+    """Descriptor of the host-streamed chunk driver: coords, frame offsets
+    and the per-token tensors are pinned CPU tensors; Wt, bias, dW, db and
+    err_flag live on the GPU (kept referenced by the returned object)."""
+    assert frame_offsets_host.dtype == torch.int32 and coords_host.dtype == torch.int32
+    d = ChunkedHostDesc()
+    d.T, d.H, d.W, d.C_in, d.C_out = int(T), int(H), int(W), int(C_in), int(C_out)
+    d.dtype = SV_BF16 if dtype == torch.bfloat16 else SV_F32
+    d.kernel = _kernel(kernel)
+    d.chunk_frames = int(chunk_frames)
+    d.coords_host, d.frame_offsets_host = _host_ptr(coords_host), _host_ptr(frame_offsets_host)
+    d.X_host, d.Y_host, d.dY_host, d.dX_host = _host_ptr(X_host), _host_ptr(Y_host), _host_ptr(dY_host), \
+        _host_ptr(dX_host)
+    d.Wt, d.bias, d.dW, d.db, d.err_flag = _ptr(Wt), _ptr(bias), _ptr(dW), _ptr(db), _ptr(err_flag)
+    d._keep = (coords_host, frame_offsets_host, X_host, Wt, bias, Y_host, dY_host, dX_host, dW, db, err_flag)
+    return d
+
+
+def sv_chunked_host_workspace_bytes(desc: ChunkedHostDesc, passes: int) -> int:
+    return int(load().sv_chunked_host_workspace_bytes(ctypes.byref(desc), ctypes.c_uint32(passes)))
+
+
+def sv_sparseconv2d_chunked_host(desc: ChunkedHostDesc, passes: int, workspace, h2d_stream, d2h_stream,
+                                 stream=None):
+    """Enqueue the host-streamed driver: compute on `stream` (default: the
+    current stream), copies on the two given streams.  Synchronising the
+    compute stream covers the whole call."""
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_sparseconv2d_chunked_host(ctypes.byref(desc), ctypes.c_uint32(passes), _ptr(workspace), wsb,
+                                             _stream(stream), _stream(h2d_stream), _stream(d2h_stream))
+    _check(st, "sv_sparseconv2d_chunked_host")
 
 
 def sv_stage_gather(src, rows, dst, stream=None):

@@ -134,3 +134,32 @@ def test_workloads_shapes():
     for s in (1, 2):
         prev, cur = S.stages[s - 1], S.stages[s]
         assert np.array_equal(prev["coords"][cur["sel"]], cur["coords"])
+
+
+def test_chunked_host_validation_and_workspace(lib):
+    """Host-streamed driver: workspace flat in T and at least the device
+    driver's; distinct streams required; short workspace rejected (all
+    before any HIP work)."""
+    passes = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
+    sizes = []
+    for T in (256, 768, 3072):
+        offs = (np.arange(T + 1, dtype=np.int32) * 59).astype(np.int32)
+        d = ops.ChunkedHostDesc()
+        d.T, d.H, d.W, d.C_in, d.C_out = T, 14, 14, 128, 128
+        d.dtype, d.kernel, d.chunk_frames = ops.SV_BF16, ops.SV_KERNEL_AUTO, 256
+        d.frame_offsets_host = offs.ctypes.data
+        sizes.append(lib.sv_chunked_host_workspace_bytes(ctypes.byref(d), passes))
+        assert sizes[-1] > lib.sv_chunked_workspace_bytes(ctypes.byref(_desc(T, offs)), passes)
+    assert sizes[0] > 0 and sizes[0] == sizes[1] == sizes[2]
+    # same stream twice; then a missing workspace
+    d.coords_host = d.X_host = d.Y_host = d.dY_host = d.dX_host = 4096
+    d.Wt = d.dW = 4096
+    assert lib.sv_sparseconv2d_chunked_host(ctypes.byref(d), passes, None, 0, FAKE, FAKE, ctypes.c_void_p(8192)) \
+        == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_chunked_host(ctypes.byref(d), passes, None, 0, FAKE, ctypes.c_void_p(8192),
+                                            ctypes.c_void_p(12288)) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_sparseconv2d_chunked_host(ctypes.byref(d), 8, None, 0, FAKE, ctypes.c_void_p(8192),
+                                            ctypes.c_void_p(12288)) == ops.SV_ERR_INVALID_ARG
+    d.dX_host = None
+    assert lib.sv_sparseconv2d_chunked_host(ctypes.byref(d), passes, None, 0, FAKE, ctypes.c_void_p(8192),
+                                            ctypes.c_void_p(12288)) == ops.SV_ERR_INVALID_ARG
