@@ -70,7 +70,7 @@ __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const
         for (int mb = 0; mb < 2; ++mb) a[ks][mb] = frag_row(&sA[arow[mb] * CM_LDA + kof]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-            b[ks][nb] = frag_row(&sb[(wn * 64 + nb * 32 + l32) * CM_LDB + (((2 * ks + lhi) ^ (l32 & 7)) << 3)]);
+            b[ks][nb] = frag_row(&sb[(wn * 64 + nb * 32 + l32) * CM_LDB + (((2 * ks + lhi) ^ ((l32 >> 1) & 7)) << 3)]);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -184,20 +184,22 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     // loaded straight into LDS (buffer_load ... lds: lane L of an
     // instruction writes the 16 bytes at the instruction's LDS base + 16 L),
     // so it needs no registers and no LDS store instructions.  Row nn's
-    // 16-byte chunk ch sits at position ch ^ (nn & 7) of its 128-byte row;
-    // the fragment reads of 8 consecutive rows then hit 8 distinct bank
-    // groups.  Each wave issues 4 of the tile's 16 instructions; the lane
-    // chooses the chunk that belongs in its slot.  The per-lane part of the
-    // offset is fixed; a round adds a uniform part.
+    // 16-byte chunk ch sits at position ch ^ ((nn >> 1) & 7) of its 128-byte
+    // row.  LDS serves a 16-byte read 16 lanes at a time over 64 banks (256
+    // bytes); the fragment reads of 16 consecutive rows then cover all 64
+    // banks once (row parity picks the 128-byte half, the swizzle the 16-byte
+    // slot within it).  Each wave issues 4 of the tile's 16 instructions;
+    // the lane chooses the chunk that belongs in its slot.  The per-lane part
+    // of the offset is fixed; a round adds a uniform part.
     uint32_t bOff[4];
-    int bChunk;
+    int bChunk[4];
     {
         const int pos = lane & 7, rsub = lane >> 3;
-        bChunk = pos ^ rsub;                      // rows of an instruction are 8 apart in their low bits
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int nn = (wave * 4 + u) * 8 + rsub;
-            bOff[u] = n0 + nn < NO ? (static_cast<uint32_t>(n0 + nn) * K + bChunk * 8) * 2 : kOob;
+            bChunk[u] = pos ^ ((nn >> 1) & 7);
+            bOff[u] = n0 + nn < NO ? (static_cast<uint32_t>(n0 + nn) * K + bChunk[u] * 8) * 2 : kOob;
         }
     }
     typedef __attribute__((address_space(3))) void lds_void_t;
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t*)(sb + (wave * 4 + u) * 512), 16,
-                                                     bChunk * 8 < kc ? bOff[u] + roff : kOob, 0, 0, 0);
+                                                     bChunk[u] * 8 < kc ? bOff[u] + roff : kOob, 0, 0, 0);
     };
     // Gather mode: the 128 rows of tap j, chunk c, straight into sA.
     auto stage_gather = [&](int rr) {
