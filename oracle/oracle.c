@@ -19,6 +19,16 @@
  *   orc_bwd_dw        forward map, obtained by differentiating the forward sum
  *   orc_bwd_db        (scatter form, dW, db) and by the mirror property of the
  *                     3x3 offsets (gather form of dX).
+ *   orc_xattn_fwd     Key Design 3 ("Asymmetric Cross-Attention"): auxiliary
+ *   orc_xattn_bwd     tokens are the queries, the down-projected sparse
+ *                     visual tokens are both keys and values, and only the
+ *                     auxiliary tokens are updated.  The page prints
+ *                     X'_aux = CrossAttn(X'_vis) and nothing more; the
+ *                     reading here is single-head scaled dot-product
+ *                     attention with no further projections, the scores
+ *                     scaled by 1/sqrt(d) unless another scale is given.
+ *                     The backward is the chain rule through scores, row
+ *                     softmax and the weighted sum.
  *
  * Readings of points the page leaves open:
  *   - tap order j = 3*(dy+1) + (dx+1), dy, dx in {-1, 0, 1}; the centre tap
@@ -42,6 +52,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <math.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -262,4 +273,95 @@ void orc_bwd_db(const double *dY, double *db, int64_t n, int32_t Co)
     for (int32_t o = 0; o < Co; ++o) db[o] = 0.0;
     for (int64_t k = 0; k < n; ++k)
         for (int32_t o = 0; o < Co; ++o) db[o] += dY[k * Co + o];
+}
+
+/* ------------------------------------------------------------------------
+ * Asymmetric cross-attention (Key Design 3).  Q [m][d] auxiliary queries,
+ * X [n][d] sparse visual tokens used as keys and as values:
+ *   S[q][j] = scale * sum_c Q[q][c] X[j][c]
+ *   P[q][j] = exp(S[q][j] - lse[q]),  lse[q] = log sum_j exp(S[q][j])
+ *   O[q][c] = sum_j P[q][j] X[j][c]
+ * The largest score is subtracted before exponentiating (the same value in
+ * exact arithmetic).  With n == 0 there is nothing to attend to: O = 0 and
+ * lse = -infinity.  Keys are visited in ascending order. */
+void orc_xattn_fwd(const double *Q, const double *X, double *O, double *lse,
+                   int64_t m, int64_t n, int32_t d, double scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < m; ++q) {
+        const double *qv = Q + q * d;
+        double *o = O + q * d;
+        for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+        if (n == 0) { lse[q] = -1.0 / 0.0; continue; }
+        double *srow = (double *)malloc((size_t)n * sizeof(double));
+        double mx = -1.0 / 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int32_t c = 0; c < d; ++c) s += qv[c] * X[j * d + c];
+            srow[j] = scale * s;
+            if (srow[j] > mx) mx = srow[j];
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j < n; ++j) sum += exp(srow[j] - mx);
+        for (int64_t j = 0; j < n; ++j) {
+            double pj = exp(srow[j] - mx) / sum;
+            for (int32_t c = 0; c < d; ++c) o[c] += pj * X[j * d + c];
+        }
+        lse[q] = mx + log(sum);
+        free(srow);
+    }
+}
+
+/* Backward of orc_xattn_fwd for an upstream gradient dO [m][d]:
+ *   dP[q][j] = sum_c dO[q][c] X[j][c]
+ *   D[q]     = sum_j P[q][j] dP[q][j]         (= sum_c dO[q][c] O[q][c])
+ *   dS[q][j] = P[q][j] (dP[q][j] - D[q])       (row softmax)
+ *   dQ[q][c] = scale * sum_j dS[q][j] X[j][c]
+ *   dX[j][c] = scale * sum_q dS[q][j] Q[q][c]  (X as keys)
+ *            +         sum_q P[q][j] dO[q][c]  (X as values)
+ * P is recomputed from Q and X here, not taken from the forward. */
+void orc_xattn_bwd(const double *Q, const double *X, const double *dO,
+                   double *dQ, double *dX, int64_t m, int64_t n, int32_t d,
+                   double scale)
+{
+    double *P = (double *)malloc((size_t)(m * n + 1) * sizeof(double));
+    double *dS = (double *)malloc((size_t)(m * n + 1) * sizeof(double));
+    for (int64_t q = 0; q < m; ++q) {
+        const double *qv = Q + q * d, *g = dO + q * d;
+        double mx = -1.0 / 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int32_t c = 0; c < d; ++c) s += qv[c] * X[j * d + c];
+            P[q * n + j] = scale * s;
+            if (P[q * n + j] > mx) mx = P[q * n + j];
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j < n; ++j) sum += exp(P[q * n + j] - mx);
+        for (int64_t j = 0; j < n; ++j) P[q * n + j] = exp(P[q * n + j] - mx) / sum;
+        double D = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            double dp = 0.0;
+            for (int32_t c = 0; c < d; ++c) dp += g[c] * X[j * d + c];
+            dS[q * n + j] = dp;              /* dP for now */
+            D += P[q * n + j] * dp;
+        }
+        for (int64_t j = 0; j < n; ++j) dS[q * n + j] = P[q * n + j] * (dS[q * n + j] - D);
+        for (int32_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < n; ++j) acc += dS[q * n + j] * X[j * d + c];
+            dQ[q * d + c] = scale * acc;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j)
+        for (int32_t c = 0; c < d; ++c) {
+            double key = 0.0, val = 0.0;
+            for (int64_t q = 0; q < m; ++q) {
+                key += dS[q * n + j] * Q[q * d + c];
+                val += P[q * n + j] * dO[q * d + c];
+            }
+            dX[j * d + c] = scale * key + val;
+        }
+    free(P);
+    free(dS);
 }

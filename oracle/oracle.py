@@ -30,10 +30,10 @@ STATUS_DUPLICATE = 6
 
 
 def compile_source(src: str, out: str) -> str:
-    """gcc -O3 -fopenmp: one C file to one shared library."""
+    """gcc -O3 -fopenmp: one C file to one shared library (with libm)."""
     tmp = out + ".tmp"
     subprocess.check_call(["gcc", "-O3", "-std=c99", "-fopenmp", "-fPIC", "-shared",
-                           src, "-o", tmp])
+                           src, "-o", tmp, "-lm"])
     os.replace(tmp, out)
     return out
 
@@ -65,8 +65,11 @@ class Oracle:
         lib.orc_bwd_dw.argtypes = [P, P, P, P, i64, i32, i32]
         lib.orc_bwd_dw_rows.argtypes = [P, P, P, P, i64, P, i64, i32, i32]
         lib.orc_bwd_db.argtypes = [P, P, i64, i32]
+        lib.orc_xattn_fwd.argtypes = [P, P, P, P, i64, i64, i32, ctypes.c_double]
+        lib.orc_xattn_bwd.argtypes = [P, P, P, P, P, i64, i64, i32, ctypes.c_double]
         for f in ("orc_fwd", "orc_fwd_rows", "orc_bwd_dx", "orc_bwd_dx_rows",
-                  "orc_bwd_dx_scatter", "orc_bwd_dw", "orc_bwd_dw_rows", "orc_bwd_db"):
+                  "orc_bwd_dx_scatter", "orc_bwd_dw", "orc_bwd_dw_rows", "orc_bwd_db",
+                  "orc_xattn_fwd", "orc_xattn_bwd"):
             getattr(lib, f).restype = None
         self.lib = lib
         self.path = path
@@ -152,6 +155,31 @@ class Oracle:
         self.lib.orc_bwd_db(_p(dY), _p(db), n, Co)
         return db
 
+    def xattn_fwd(self, Q, X, scale=None):
+        """Cross-attention of the queries Q [m,d] over X [n,d] (keys = values).
+        Returns (O [m,d], lse [m]).  scale defaults to 1/sqrt(d)."""
+        Q, X = _f64(Q), _f64(X)
+        m, d = Q.shape
+        n = X.shape[0]
+        sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+        O = np.empty((m, d), dtype=np.float64)
+        lse = np.empty((m,), dtype=np.float64)
+        self.lib.orc_xattn_fwd(_p(Q), _p(X.reshape(n, d) if n else np.zeros((1, d))), _p(O), _p(lse),
+                               m, n, d, sc)
+        return O, lse
+
+    def xattn_bwd(self, Q, X, dO, scale=None):
+        """Gradients (dQ [m,d], dX [n,d]) of <O, dO> for O = xattn_fwd(Q, X)."""
+        Q, X, dO = _f64(Q), _f64(X), _f64(dO)
+        m, d = Q.shape
+        n = X.shape[0]
+        sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+        dQ = np.empty((m, d), dtype=np.float64)
+        dX = np.empty((max(n, 1), d), dtype=np.float64)
+        Xp = X.reshape(n, d) if n else np.zeros((1, d))
+        self.lib.orc_xattn_bwd(_p(Q), _p(Xp), _p(dO), _p(dQ), _p(dX), m, n, d, sc)
+        return dQ, dX[:n]
+
 
 def _f64(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
@@ -220,3 +248,11 @@ def bwd_dw_rows(X, N, dY, rows):
 
 def bwd_db(dY):
     return default().bwd_db(dY)
+
+
+def xattn_fwd(Q, X, scale=None):
+    return default().xattn_fwd(Q, X, scale)
+
+
+def xattn_bwd(Q, X, dO, scale=None):
+    return default().xattn_bwd(Q, X, dO, scale)

@@ -310,6 +310,120 @@ def pin_row_subsets(orc):
     assert np.array_equal(orc.bwd_dw_rows(L.X, N, L.dY, ji), full[ji])
 
 
+# ------------------------------------------------- asymmetric cross-attention
+# "SV-TAD ...", Key Design 3: auxiliary tokens query the down-projected
+# sparse visual tokens, which serve as keys and values.  Read as single-head
+# scaled dot-product attention, O = softmax(scale * Q X^T) X.
+
+
+def _xattn_case(seed, m, n, d, spread=1.0):
+    rng = np.random.default_rng(seed)
+    return (spread * rng.standard_normal((m, d)), rng.standard_normal((n, d)),
+            rng.standard_normal((m, d)))
+
+
+def pin_xattn_single_key(orc):
+    """One key: every query puts weight 1 on it, so O = x0, lse = the score,
+    dQ = 0 (the softmax of one score is constant) and dX = sum_q dO[q]."""
+    Q, X, dO = _xattn_case(41, 3, 1, 8)
+    sc = 0.3
+    O, lse = orc.xattn_fwd(Q, X, sc)
+    close(O, np.repeat(X, 3, axis=0), 1e-15, "O")
+    close(lse, sc * (Q @ X[0]), 1e-14, "lse")
+    dQ, dX = orc.xattn_bwd(Q, X, dO, sc)
+    close(dQ, np.zeros_like(Q), 1e-15, "dQ")
+    close(dX, dO.sum(axis=0, keepdims=True), 1e-14, "dX")
+
+
+def pin_xattn_two_keys(orc):
+    """Two keys: the weight of x1 is the logistic function of the score gap,
+    O = x0 + sigma(scale q.(x1 - x0)) (x1 - x0)."""
+    Q, X, _ = _xattn_case(42, 4, 2, 6)
+    sc = 0.7
+    O, lse = orc.xattn_fwd(Q, X, sc)
+    p1 = 1.0 / (1.0 + np.exp(-sc * (Q @ (X[1] - X[0]))))
+    close(O, X[0][None, :] + p1[:, None] * (X[1] - X[0])[None, :], 1e-14, "O")
+    close(lse, np.logaddexp(sc * (Q @ X[0]), sc * (Q @ X[1])), 1e-14, "lse")
+
+
+def pin_xattn_zero_queries(orc):
+    """Q = 0: uniform weights, so O = mean of X and lse = log n; then
+    dQ = scale * Cov(X) dO (population covariance) and dX[j] = sum_q dO[q] / n."""
+    _, X, dO = _xattn_case(43, 2, 37, 5)
+    Q = np.zeros((2, 5))
+    sc = 0.45
+    O, lse = orc.xattn_fwd(Q, X, sc)
+    close(O, np.repeat(X.mean(axis=0, keepdims=True), 2, axis=0), 1e-14, "O")
+    close(lse, np.full(2, np.log(37.0)), 1e-14, "lse")
+    dQ, dX = orc.xattn_bwd(Q, X, dO, sc)
+    cov = np.cov(X.T, bias=True)
+    close(dQ, sc * dO @ cov, 1e-13, "dQ")
+    close(dX, np.repeat(dO.sum(axis=0, keepdims=True) / 37.0, 37, axis=0), 1e-14, "dX")
+
+
+def pin_xattn_torch(orc):
+    """torch float64: softmax of the scaled scores times X, and autograd of
+    <O, dO> for dQ and dX (X enters as keys and as values)."""
+    for seed, m, n, d in ((44, 1, 50, 16), (45, 5, 13, 7), (46, 16, 200, 32)):
+        Q, X, dO = _xattn_case(seed, m, n, d)
+        sc = 1.0 / np.sqrt(d)
+        Qt = torch.tensor(Q, requires_grad=True)
+        Xt = torch.tensor(X, requires_grad=True)
+        Ot = torch.softmax(sc * Qt @ Xt.T, dim=1) @ Xt
+        (Ot * torch.tensor(dO)).sum().backward()
+        O, lse = orc.xattn_fwd(Q, X)
+        close(O, Ot.detach().numpy(), 1e-13, f"O {seed}")
+        close(lse, torch.logsumexp(sc * torch.tensor(Q) @ torch.tensor(X).T, dim=1).numpy(), 1e-13, "lse")
+        dQ, dX = orc.xattn_bwd(Q, X, dO)
+        close(dQ, Qt.grad.numpy(), 1e-12, f"dQ {seed}")
+        close(dX, Xt.grad.numpy(), 1e-12, f"dX {seed}")
+
+
+def pin_xattn_finite_differences(orc):
+    """Central differences of <O(Q, X), dO> along random directions."""
+    Q, X, dO = _xattn_case(47, 3, 9, 4)
+    rng = np.random.default_rng(5)
+    VQ, VX = rng.standard_normal(Q.shape), rng.standard_normal(X.shape)
+
+    def loss(Q_, X_):
+        return float(np.sum(orc.xattn_fwd(Q_, X_)[0] * dO))
+
+    eps = 1e-5
+    gQ = (loss(Q + eps * VQ, X) - loss(Q - eps * VQ, X)) / (2 * eps)
+    gX = (loss(Q, X + eps * VX) - loss(Q, X - eps * VX)) / (2 * eps)
+    dQ, dX = orc.xattn_bwd(Q, X, dO)
+    assert abs(gQ - np.sum(dQ * VQ)) < 1e-8 * max(1, abs(gQ))
+    assert abs(gX - np.sum(dX * VX)) < 1e-8 * max(1, abs(gX))
+
+
+def pin_xattn_permutation_and_extremes(orc):
+    """Reordering the keys leaves O and dQ alone and reorders dX; scores in
+    the thousands (the shift by the largest score is what keeps exp finite)
+    put all the weight on the best key; no keys give O = 0, lse = -inf and
+    dQ = 0."""
+    Q, X, dO = _xattn_case(48, 3, 20, 8)
+    perm = np.random.default_rng(6).permutation(20)
+    O1, l1 = orc.xattn_fwd(Q, X)
+    O2, l2 = orc.xattn_fwd(Q, X[perm])
+    close(O2, O1, 1e-13, "O permuted")
+    close(l2, l1, 1e-13, "lse permuted")
+    dQ1, dX1 = orc.xattn_bwd(Q, X, dO)
+    dQ2, dX2 = orc.xattn_bwd(Q, X[perm], dO)
+    close(dQ2, dQ1, 1e-12, "dQ permuted")
+    close(dX2, dX1[perm], 1e-12, "dX permuted")
+    base = np.sort(Q @ X.T / np.sqrt(8), axis=1)
+    big = (60.0 / float(np.min(base[:, -1] - base[:, -2]))) * Q   # score gap >= 60, scores ~ 1e3
+    O, lse = orc.xattn_fwd(big, X)
+    best = np.argmax(big @ X.T, axis=1)
+    assert np.max(np.abs(big @ X.T)) > 700, "scores must overflow exp without the shift"
+    close(O, X[best], 1e-12, "O at large scores")
+    assert np.all(np.isfinite(lse))
+    O, lse = orc.xattn_fwd(Q, np.zeros((0, 8)))
+    assert np.array_equal(O, np.zeros((3, 8))) and np.all(np.isneginf(lse))
+    dQ, dX = orc.xattn_bwd(Q, np.zeros((0, 8)), dO)
+    assert np.array_equal(dQ, np.zeros((3, 8))) and dX.shape == (0, 8)
+
+
 ALL_PINS = [
     pin_golden_hand_3x4,
     pin_golden_frames_2x2,
@@ -322,4 +436,10 @@ ALL_PINS = [
     pin_special_cases,
     pin_finite_differences,
     pin_row_subsets,
+    pin_xattn_single_key,
+    pin_xattn_two_keys,
+    pin_xattn_zero_queries,
+    pin_xattn_torch,
+    pin_xattn_finite_differences,
+    pin_xattn_permutation_and_extremes,
 ]

@@ -45,6 +45,24 @@ MUTANTS = [
     ("db drops the last token",
      "for (int64_t k = 0; k < n; ++k)\n        for (int32_t o = 0; o < Co; ++o) db[o]",
      "for (int64_t k = 0; k + 1 < n; ++k)\n        for (int32_t o = 0; o < Co; ++o) db[o]", 0),
+    ("cross-attention scores not scaled",
+     "srow[j] = scale * s;", "srow[j] = s;", 0),
+    ("cross-attention softmax without the max shift",
+     "for (int64_t j = 0; j < n; ++j) sum += exp(srow[j] - mx);\n        for (int64_t j = 0; j < n; ++j) {\n            double pj = exp(srow[j] - mx) / sum;",
+     "for (int64_t j = 0; j < n; ++j) sum += exp(srow[j]);\n        for (int64_t j = 0; j < n; ++j) {\n            double pj = exp(srow[j]) / sum;", 0),
+    ("cross-attention lse without the shift added back",
+     "lse[q] = mx + log(sum);", "lse[q] = log(sum);", 0),
+    ("cross-attention dX drops the value term",
+     "dX[j * d + c] = scale * key + val;", "dX[j * d + c] = scale * key;", 0),
+    ("cross-attention dX drops the key term",
+     "dX[j * d + c] = scale * key + val;", "dX[j * d + c] = val;", 0),
+    ("cross-attention softmax backward without the row correction",
+     "dS[q * n + j] = P[q * n + j] * (dS[q * n + j] - D);", "dS[q * n + j] = P[q * n + j] * dS[q * n + j];", 0),
+    ("cross-attention dQ not scaled",
+     "dQ[q * d + c] = scale * acc;", "dQ[q * d + c] = acc;", 0),
+    ("cross-attention dQ contracts with the queries instead of the keys",
+     "for (int64_t j = 0; j < n; ++j) acc += dS[q * n + j] * X[j * d + c];",
+     "for (int64_t j = 0; j < n; ++j) acc += dS[q * n + j] * Q[q * d + c];", 0),
 ]
 
 
