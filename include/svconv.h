@@ -236,6 +236,40 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc *desc, uint32_
  * descriptors. */
 size_t sv_chunked_host_workspace_bytes(const sv_chunked_host_desc *desc, uint32_t passes);
 
+/* Asymmetric cross-attention (Key Design 3): auxiliary tokens Q [m][d]
+ * (such as the CLS token) query the down-projected sparse visual tokens
+ * X [n][d], which serve as keys and as values; only the auxiliary tokens are
+ * updated.  Read as single-head scaled dot-product attention with no further
+ * projections:
+ *   S[q][j] = scale * <Q[q], X[j]>,   O[q] = sum_j softmax_j(S[q])[j] X[j],
+ *   lse[q]  = log sum_j exp(S[q][j])  (-inf when n == 0, where O = 0).
+ * scale == 0 selects 1/sqrt(d).  d is 64, 128 or 256 (else
+ * SV_ERR_UNSUPPORTED); m <= 65535.  Q, X, O, dO, dX: device, `dtype`,
+ * row-major, 16-byte aligned; lse and dQ: device fp32.  To attend within one
+ * frame chunk only, pass that chunk's rows of X.
+ *
+ * Forward: O [m][d] and lse [m] written.  Split over key blocks; the
+ * partials go to the workspace (sv_xattn_workspace_bytes(0, m, n, d) bytes,
+ * 16-byte aligned) and are merged in block order: deterministic.
+ *
+ * Backward for an upstream gradient dO [m][d], given the forward's O and
+ * lse: dQ [m][d] (fp32) and dX [n][d] written, with
+ *   dS[q][j] = P[q][j] (<dO[q], X[j]> - <dO[q], O[q]>),
+ *   dQ[q]    = scale sum_j dS[q][j] X[j],
+ *   dX[j]    = scale sum_q dS[q][j] Q[q] + sum_q P[q][j] dO[q]
+ * (X enters as keys and as values).  Workspace sv_xattn_workspace_bytes(1,
+ * m, n, d) bytes.  With m == 0, dX is zeroed. */
+sv_status sv_xattn_fwd(const void *Q, const void *X, int64_t m, int64_t n, int32_t d,
+                       float scale, sv_dtype dtype, void *O, float *lse,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+sv_status sv_xattn_bwd(const void *Q, const void *X, const void *O, const void *dO,
+                       const float *lse, int64_t m, int64_t n, int32_t d, float scale,
+                       sv_dtype dtype, float *dQ, void *dX,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* Workspace bytes of sv_xattn_fwd (backward == 0) or sv_xattn_bwd
+ * (backward != 0); 0 for unsupported sizes.  Depends only on the arguments. */
+size_t sv_xattn_workspace_bytes(int32_t backward, int64_t m, int64_t n, int32_t d);
+
 /* Stage transition between pruning stages (the map is rebuilt at each
  * selection point and reused by the adapter layers in between, Key Design 1):
  * the next stage's packed input keeps a subset of the current rows.

@@ -5,6 +5,8 @@
 
 #include "internal.h"
 
+#include <cmath>
+
 using namespace svc;
 
 namespace {
@@ -488,6 +490,61 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
     const sv_status result = run();
     for (int i = 0; i < 3 * kSets + 1; ++i) (void)hipEventDestroy(ev[i]);
     return result;
+}
+
+// ------------------------------------------------------ cross-attention
+namespace {
+
+bool a16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+sv_status xattn_args_ok(int64_t m, int64_t n, int32_t d, sv_dtype dtype) {
+    if (m < 0 || n < 0 || m > 65535 || !valid_dtype(dtype)) return SV_ERR_INVALID_ARG;
+    if (!xattn_supported(d)) return SV_ERR_UNSUPPORTED;
+    return SV_OK;
+}
+
+float xattn_scale(float scale, int32_t d) { return scale == 0.f ? 1.f / sqrtf(static_cast<float>(d)) : scale; }
+
+}  // namespace
+
+size_t sv_xattn_workspace_bytes(int32_t backward, int64_t m, int64_t n, int32_t d) {
+    if (m < 0 || n < 0 || !xattn_supported(d)) return 0;
+    const XattnPlan p = plan_xattn(m, n, d);
+    return backward ? p.bwd_bytes : p.fwd_bytes;
+}
+
+sv_status sv_xattn_fwd(const void* Q, const void* X, int64_t m, int64_t n, int32_t d, float scale, sv_dtype dtype,
+                       void* O, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    sv_status st = xattn_args_ok(m, n, d, dtype);
+    if (st != SV_OK) return st;
+    if (m == 0) return SV_OK;
+    if (!Q || !O || !lse || (n > 0 && !X) || !std::isfinite(scale)) return SV_ERR_INVALID_ARG;
+    if (!a16(Q) || !a16(O) || (n > 0 && !a16(X))) return SV_ERR_INVALID_ARG;
+    const XattnPlan p = plan_xattn(m, n, d);
+    if (!workspace || workspace_bytes < p.fwd_bytes) return SV_ERR_WORKSPACE;
+    if (!a16(workspace)) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_xattn_fwd(p, dtype == SV_BF16, Q, X, static_cast<int>(m), n, d, xattn_scale(scale, d), O,
+                                       lse, workspace, stream));
+}
+
+sv_status sv_xattn_bwd(const void* Q, const void* X, const void* O, const void* dO, const float* lse, int64_t m,
+                       int64_t n, int32_t d, float scale, sv_dtype dtype, float* dQ, void* dX, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    sv_status st = xattn_args_ok(m, n, d, dtype);
+    if (st != SV_OK) return st;
+    if (m == 0) {
+        // no queries: nothing flows back into the keys
+        if (n == 0) return SV_OK;
+        if (!dX) return SV_ERR_INVALID_ARG;
+        return hip_status(launch_stage_scatter(nullptr, nullptr, 0, dX, n, d, dtype == SV_BF16 ? 2 : 4, stream));
+    }
+    if (!Q || !O || !dO || !lse || !dQ || (n > 0 && (!X || !dX)) || !std::isfinite(scale)) return SV_ERR_INVALID_ARG;
+    if (!a16(Q) || !a16(O) || !a16(dO) || !a16(dQ) || (n > 0 && (!a16(X) || !a16(dX)))) return SV_ERR_INVALID_ARG;
+    const XattnPlan p = plan_xattn(m, n, d);
+    if (p.bwd_bytes > 0 && (!workspace || workspace_bytes < p.bwd_bytes)) return SV_ERR_WORKSPACE;
+    if (workspace && !a16(workspace)) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_xattn_bwd(p, dtype == SV_BF16, Q, X, O, dO, lse, static_cast<int>(m), n, d,
+                                       xattn_scale(scale, d), dQ, dX, workspace, stream));
 }
 
 sv_status sv_stage_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n_rows, void* dst,

@@ -138,6 +138,22 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
                      const void* dY, float* dW, float* db, int64_t n, int Ci, int Co,
                      int accumulate, void* ws, hipStream_t stream);
 
+// Asymmetric cross-attention: key blocks of kpb keys, partials in the
+// workspace (fwd_bytes / bwd_bytes), head width d in {64, 128, 256}.
+struct XattnPlan {
+    int64_t kpb;       // keys per block (a multiple of 16)
+    int64_t blocks;    // key blocks
+    size_t fwd_bytes;  // workspace of the forward
+    size_t bwd_bytes;  // workspace of the backward
+};
+XattnPlan plan_xattn(int64_t m, int64_t n, int d);
+bool xattn_supported(int d);
+hipError_t launch_xattn_fwd(const XattnPlan& p, bool bf16, const void* Q, const void* X, int m, int64_t n, int d,
+                            float scale, void* O, float* lse, void* ws, hipStream_t stream);
+hipError_t launch_xattn_bwd(const XattnPlan& p, bool bf16, const void* Q, const void* X, const void* O,
+                            const void* dO, const float* lse, int m, int64_t n, int d, float scale, float* dQ,
+                            void* dX, void* ws, hipStream_t stream);
+
 // Copies `bytes` bytes with a kernel (either side may be page-locked host
 // memory the device can address).
 hipError_t launch_copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t stream);

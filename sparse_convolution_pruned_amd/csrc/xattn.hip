@@ -1,0 +1,403 @@
+// Asymmetric cross-attention ("SV-TAD: Native Sparse Convolutions for
+// Efficient Temporal Action Detection", Key Design 3): a few auxiliary
+// tokens Q [m][d] query the down-projected sparse visual tokens X [n][d],
+// which are both keys and values, and only the auxiliary tokens are updated:
+//   S[q][j] = scale <Q[q], X[j]>,  P = row softmax of S,  O = P X.
+// Single head, no further projections (the page prints no more than that).
+//
+// The work is a read of X (n d elements) against a handful of queries, so it
+// is bound by HBM bandwidth, and it is split over key blocks like a split-K
+// reduction:
+//   forward:  each workgroup folds its key block into a running maximum,
+//             sum and weighted row sum per query (the online softmax) and
+//             writes them as a partial; a second kernel merges the partials
+//             in block order into O and lse = log sum_j exp S[q][j].
+//   backward: with lse from the forward, P and
+//               dS[q][j] = P[q][j] (<dO[q], X[j]> - <dO[q], O[q]>)
+//             are recomputed per key; each key's row of
+//               dX[j] = scale sum_q dS[q][j] Q[q] + sum_q P[q][j] dO[q]
+//             is written directly, and dQ[q] = scale sum_j dS[q][j] X[j] goes
+//             through block partials merged in block order.
+// Everything is summed in a fixed order, so results are bitwise
+// reproducible.
+//
+// Lanes: 16 lanes share a key row, each holding d / 16 consecutive elements
+// (one or two 16-byte loads), so a row is one contiguous 2d- or 4d-byte read;
+// a workgroup of 256 threads has 16 such groups.  Dot products finish with
+// four butterfly exchanges inside the 16-lane group.  Queries go through in
+// chunks of XA_MQ held in registers.
+#include "internal.h"
+
+namespace svc {
+
+constexpr int XA_THREADS = 256;
+constexpr int XA_GROUPS = XA_THREADS / 16;
+constexpr int XA_MQ = 4;                 // queries per pass
+
+template <typename T, int EPL>
+__device__ __forceinline__ void load_part(const T* __restrict__ p, float (&v)[EPL]) {
+    if constexpr (sizeof(T) == 2) {
+        static_assert(EPL % 4 == 0, "bf16 pieces of 8 bytes at least");
+        if constexpr (EPL % 8 == 0) {
+#pragma unroll
+            for (int u = 0; u < EPL / 8; ++u) {
+                const uint4 w = reinterpret_cast<const uint4*>(p)[u];
+                const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    v[8 * u + 2 * h] = __uint_as_float(a[h] << 16);
+                    v[8 * u + 2 * h + 1] = __uint_as_float(a[h] & 0xffff0000u);
+                }
+            }
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(p);
+            v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+            v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < EPL / 4; ++u) {
+            const float4 w = reinterpret_cast<const float4*>(p)[u];
+            v[4 * u] = w.x; v[4 * u + 1] = w.y; v[4 * u + 2] = w.z; v[4 * u + 3] = w.w;
+        }
+    }
+}
+
+template <typename T, int EPL>
+__device__ __forceinline__ void store_part(T* __restrict__ p, const float (&v)[EPL]) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+            const uint32_t lo = f32_to_bf16(v[e]) | (static_cast<uint32_t>(f32_to_bf16(v[e + 1])) << 16);
+            const uint32_t hi = f32_to_bf16(v[e + 2]) | (static_cast<uint32_t>(f32_to_bf16(v[e + 3])) << 16);
+            *reinterpret_cast<uint2*>(p + e) = make_uint2(lo, hi);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) *reinterpret_cast<float4*>(p + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+    }
+}
+
+// Sum over the 16 lanes of a group; every lane receives the total.
+__device__ __forceinline__ float group_sum(float s) {
+#pragma unroll
+    for (int k = 8; k >= 1; k >>= 1) s += __shfl_xor(s, k, 16);
+    return s;
+}
+
+// ---------------------------------------------------------------- forward
+// Partials per (key block b, query q): pM[b][q] (largest score), pL[b][q]
+// (sum of exp(S - pM)) and pA[b][q][:] (sum of exp(S - pM) X[j]).  A block
+// without keys writes pM = -inf, pL = 0, pA = 0.
+template <typename T, int EPL>
+__global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_part(const T* __restrict__ Q, const T* __restrict__ X,
+                                                               int m, int64_t n, float scale, int64_t kpb,
+                                                               float* __restrict__ pM, float* __restrict__ pL,
+                                                               float* __restrict__ pA) {
+    constexpr int D = 16 * EPL;
+    constexpr int WAVES = XA_THREADS / 64;
+    __shared__ float sM[WAVES][XA_MQ], sL[WAVES][XA_MQ];
+    __shared__ float sA[WAVES][XA_MQ][D];
+    const int tid = threadIdx.x, lane = tid & 15, grp = tid >> 4, wave = tid >> 6;
+    const int64_t b = blockIdx.x;
+    const int q0 = blockIdx.y * XA_MQ, mq = min(XA_MQ, m - q0);
+
+    float qv[XA_MQ][EPL], acc[XA_MQ][EPL], M[XA_MQ], L[XA_MQ];
+#pragma unroll
+    for (int qi = 0; qi < XA_MQ; ++qi) {
+        if (qi < mq) load_part<T, EPL>(Q + static_cast<int64_t>(q0 + qi) * D + lane * EPL, qv[qi]);
+        else
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qv[qi][e] = 0.f;
+        M[qi] = -INFINITY;
+        L[qi] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[qi][e] = 0.f;
+    }
+    const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
+    for (int64_t j = kbeg + grp; j < kend; j += XA_GROUPS) {
+        float x[EPL];
+        load_part<T, EPL>(X + j * D + lane * EPL, x);
+#pragma unroll
+        for (int qi = 0; qi < XA_MQ; ++qi) {
+            if (qi >= mq) break;
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s = fmaf(x[e], qv[qi][e], s);
+            s = scale * group_sum(s);
+            const float mn = fmaxf(M[qi], s);
+            const float corr = __expf(M[qi] - mn);        // 0 on the first key (M = -inf)
+            const float p = __expf(s - mn);
+            L[qi] = fmaf(L[qi], corr, p);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[qi][e] = fmaf(acc[qi][e], corr, p * x[e]);
+            M[qi] = mn;
+        }
+    }
+    // Merge the four groups of a wave (pairs 16 lanes apart, then 32: the
+    // same dims of another group; both partners compute the same sums), then
+    // the four waves in wave order.
+#pragma unroll
+    for (int qi = 0; qi < XA_MQ; ++qi)
+#pragma unroll
+        for (int k = 16; k <= 32; k <<= 1) {
+            const float om = __shfl_xor(M[qi], k, 64), ol = __shfl_xor(L[qi], k, 64);
+            const float mx = fmaxf(M[qi], om);
+            const float w0 = M[qi] == -INFINITY ? 0.f : __expf(M[qi] - mx);
+            const float w1 = om == -INFINITY ? 0.f : __expf(om - mx);
+            L[qi] = L[qi] * w0 + ol * w1;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[qi][e] = acc[qi][e] * w0 + __shfl_xor(acc[qi][e], k, 64) * w1;
+            M[qi] = mx;
+        }
+    if ((tid & 63) < 16)
+#pragma unroll
+        for (int qi = 0; qi < XA_MQ; ++qi) {
+            if (lane == 0) { sM[wave][qi] = M[qi]; sL[wave][qi] = L[qi]; }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sA[wave][qi][lane * EPL + e] = acc[qi][e];
+        }
+    __syncthreads();
+    for (int t = tid; t < mq * D; t += XA_THREADS) {
+        const int qi = t / D, c = t - qi * D;
+        float mx = -INFINITY;
+        for (int g = 0; g < WAVES; ++g) mx = fmaxf(mx, sM[g][qi]);
+        float l = 0.f, a = 0.f;
+        if (mx != -INFINITY)
+            for (int g = 0; g < WAVES; ++g) {
+                const float w = sM[g][qi] == -INFINITY ? 0.f : __expf(sM[g][qi] - mx);
+                l = fmaf(sL[g][qi], w, l);
+                a = fmaf(sA[g][qi][c], w, a);
+            }
+        const int64_t o = b * m + q0 + qi;
+        pA[o * D + c] = a;
+        if (c == 0) { pM[o] = mx; pL[o] = l; }
+    }
+}
+
+// O[q] = sum_b pA[b][q] w_b / sum_b pL[b][q] w_b with w_b = exp(pM[b][q] - max_b pM[b][q]),
+// lse[q] = max + log(sum); blocks in ascending order.  One workgroup per query.
+template <typename T>
+__global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_merge(const float* __restrict__ pM, const float* __restrict__ pL,
+                                                                const float* __restrict__ pA, int64_t blocks, int m,
+                                                                int d, T* __restrict__ O, float* __restrict__ lse) {
+    const int q = blockIdx.x;
+    float mx = -INFINITY;
+    for (int64_t b = 0; b < blocks; ++b) mx = fmaxf(mx, pM[b * m + q]);
+    float l = 0.f;
+    if (mx != -INFINITY)
+        for (int64_t b = 0; b < blocks; ++b) l = fmaf(pL[b * m + q], __expf(pM[b * m + q] - mx), l);
+    for (int c = threadIdx.x; c < d; c += XA_THREADS) {
+        float a = 0.f;
+        if (mx != -INFINITY)
+            for (int64_t b = 0; b < blocks; ++b) a = fmaf(pA[(b * m + q) * d + c], __expf(pM[b * m + q] - mx), a);
+        Elem<T>::store(O + static_cast<int64_t>(q) * d + c, l > 0.f ? a / l : 0.f);
+    }
+    if (threadIdx.x == 0) lse[q] = (mx == -INFINITY || !(l > 0.f)) ? -INFINITY : mx + __logf(l);
+}
+
+// --------------------------------------------------------------- backward
+// One pass covers queries q0 .. q0 + MQ - 1 (MQ = 2 at d = 256, which keeps
+// the kernel near 160 VGPRs; 4 otherwise).  dX rows are written
+// (accumulate = 0) or added to (later passes); dQ partials go to
+// pQ[b][q][:] for the queries of the pass.
+template <typename T, int EPL, int MQ>
+__global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_part(const T* __restrict__ Q, const T* __restrict__ X,
+                                                               const T* __restrict__ O, const T* __restrict__ dO,
+                                                               const float* __restrict__ lse, int m, int q0,
+                                                               int64_t n, float scale, int64_t kpb, int accumulate,
+                                                               T* __restrict__ dX, float* __restrict__ pQ) {
+    constexpr int D = 16 * EPL;
+    constexpr int WAVES = XA_THREADS / 64;
+    __shared__ float sDq[MQ];
+    __shared__ float sQ[WAVES][MQ][D];
+    const int tid = threadIdx.x, lane = tid & 15, grp = tid >> 4, wave = tid >> 6;
+    const int64_t b = blockIdx.x;
+    const int mq = min(MQ, m - q0);
+
+    float qv[MQ][EPL], gv[MQ][EPL], dq[MQ][EPL], lq[MQ];
+#pragma unroll
+    for (int qi = 0; qi < MQ; ++qi) {
+        if (qi < mq) {
+            load_part<T, EPL>(Q + static_cast<int64_t>(q0 + qi) * D + lane * EPL, qv[qi]);
+            load_part<T, EPL>(dO + static_cast<int64_t>(q0 + qi) * D + lane * EPL, gv[qi]);
+            lq[qi] = lse[q0 + qi];
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) { qv[qi][e] = 0.f; gv[qi][e] = 0.f; }
+            lq[qi] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dq[qi][e] = 0.f;
+    }
+    // D[q] = <dO[q], O[q]> by the first group (16 lanes, fixed order).
+    if (grp == 0)
+#pragma unroll
+        for (int qi = 0; qi < MQ; ++qi) {
+            float o[EPL];
+            float s = 0.f;
+            if (qi < mq) {
+                load_part<T, EPL>(O + static_cast<int64_t>(q0 + qi) * D + lane * EPL, o);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s = fmaf(gv[qi][e], o[e], s);
+            }
+            s = group_sum(s);
+            if (lane == 0) sDq[qi] = s;
+        }
+    __syncthreads();
+    float Dq[MQ];
+#pragma unroll
+    for (int qi = 0; qi < MQ; ++qi) Dq[qi] = sDq[qi];
+
+    const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
+    for (int64_t j = kbeg + grp; j < kend; j += XA_GROUPS) {
+        float x[EPL], dx[EPL];
+        load_part<T, EPL>(X + j * D + lane * EPL, x);
+        if (accumulate) load_part<T, EPL>(dX + j * D + lane * EPL, dx);
+        else
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) dx[e] = 0.f;
+#pragma unroll
+        for (int qi = 0; qi < MQ; ++qi) {
+            if (qi >= mq) break;
+            float s = 0.f, g = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                s = fmaf(x[e], qv[qi][e], s);
+                g = fmaf(x[e], gv[qi][e], g);
+            }
+            s = group_sum(s);
+            g = group_sum(g);
+            const float p = __expf(scale * s - lq[qi]);
+            const float ds = p * (g - Dq[qi]);
+            const float ks = scale * ds;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                dx[e] = fmaf(ks, qv[qi][e], fmaf(p, gv[qi][e], dx[e]));
+                dq[qi][e] = fmaf(ks, x[e], dq[qi][e]);
+            }
+        }
+        store_part<T, EPL>(dX + j * D + lane * EPL, dx);
+    }
+    // dQ partial of the block: the groups of a wave added pairwise (16 lanes
+    // apart, then 32), then the waves in wave order.
+#pragma unroll
+    for (int qi = 0; qi < MQ; ++qi)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            dq[qi][e] += __shfl_xor(dq[qi][e], 16, 64);
+            dq[qi][e] += __shfl_xor(dq[qi][e], 32, 64);
+        }
+    if ((tid & 63) < 16)
+#pragma unroll
+        for (int qi = 0; qi < MQ; ++qi)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sQ[wave][qi][lane * EPL + e] = dq[qi][e];
+    __syncthreads();
+    for (int t = tid; t < mq * D; t += XA_THREADS) {
+        const int qi = t / D, c = t - qi * D;
+        float a = 0.f;
+        for (int g = 0; g < WAVES; ++g) a += sQ[g][qi][c];
+        pQ[(b * m + q0 + qi) * D + c] = a;
+    }
+}
+
+// dQ[q][c] = sum_b pQ[b][q][c], b ascending.
+__global__ __launch_bounds__(XA_THREADS) void k_xattn_dq_merge(const float* __restrict__ pQ, int64_t blocks, int m,
+                                                               int d, float* __restrict__ dQ) {
+    const int64_t total = static_cast<int64_t>(m) * d;
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * XA_THREADS + threadIdx.x; t < total;
+         t += static_cast<int64_t>(gridDim.x) * XA_THREADS) {
+        float a = 0.f;
+        for (int64_t b = 0; b < blocks; ++b) a += pQ[b * total + t];
+        dQ[t] = a;
+    }
+}
+
+// ------------------------------------------------------------------- host
+// Keys per block: about 512 blocks over n, a multiple of the 16 groups.
+XattnPlan plan_xattn(int64_t m, int64_t n, int d) {
+    XattnPlan p{};
+    p.kpb = std::max<int64_t>(XA_GROUPS, ((n + 511) / 512 + XA_GROUPS - 1) / XA_GROUPS * XA_GROUPS);
+    p.blocks = n > 0 ? (n + p.kpb - 1) / p.kpb : 0;
+    auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+    const size_t mb = static_cast<size_t>(m) * p.blocks;
+    p.fwd_bytes = up(mb * 4) * 2 + up(mb * d * 4);
+    p.bwd_bytes = up(mb * d * 4);
+    return p;
+}
+
+bool xattn_supported(int d) { return d == 64 || d == 128 || d == 256; }
+
+template <typename T, int EPL>
+static hipError_t fwd_as(const XattnPlan& p, const T* Q, const T* X, int m, int64_t n, float scale, T* O,
+                         float* lse, void* ws, hipStream_t stream) {
+    auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+    const size_t mb = static_cast<size_t>(m) * p.blocks;
+    float* pM = static_cast<float*>(ws);
+    float* pL = reinterpret_cast<float*>(static_cast<char*>(ws) + up(mb * 4));
+    float* pA = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * up(mb * 4));
+    if (p.blocks > 0) {
+        dim3 grid(static_cast<unsigned>(p.blocks), static_cast<unsigned>((m + XA_MQ - 1) / XA_MQ));
+        hipLaunchKernelGGL((k_xattn_fwd_part<T, EPL>), grid, dim3(XA_THREADS), 0, stream, Q, X, m, n, scale, p.kpb,
+                           pM, pL, pA);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_xattn_fwd_merge<T>, dim3(m), dim3(XA_THREADS), 0, stream, pM, pL, pA, p.blocks, m, 16 * EPL,
+                       O, lse);
+    return hipGetLastError();
+}
+
+template <typename T, int EPL>
+static hipError_t bwd_as(const XattnPlan& p, const T* Q, const T* X, const T* O, const T* dO, const float* lse,
+                         int m, int64_t n, float scale, float* dQ, T* dX, void* ws, hipStream_t stream) {
+    constexpr int MQ = EPL >= 16 ? 2 : 4;
+    float* pQ = static_cast<float*>(ws);
+    if (p.blocks > 0)
+        for (int q0 = 0; q0 < m; q0 += MQ) {
+            hipLaunchKernelGGL((k_xattn_bwd_part<T, EPL, MQ>), dim3(static_cast<unsigned>(p.blocks)), dim3(XA_THREADS), 0,
+                               stream, Q, X, O, dO, lse, m, q0, n, scale, p.kpb, q0 > 0 ? 1 : 0, dX, pQ);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    const int64_t total = static_cast<int64_t>(m) * 16 * EPL;
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((total + XA_THREADS - 1) / XA_THREADS, 1024));
+    hipLaunchKernelGGL(k_xattn_dq_merge, dim3(grid), dim3(XA_THREADS), 0, stream, pQ, p.blocks, m, 16 * EPL, dQ);
+    return hipGetLastError();
+}
+
+hipError_t launch_xattn_fwd(const XattnPlan& p, bool bf16, const void* Q, const void* X, int m, int64_t n, int d,
+                            float scale, void* O, float* lse, void* ws, hipStream_t stream) {
+#define XA_FWD(T, EPL)                                                                                         \
+    return fwd_as<T, EPL>(p, static_cast<const T*>(Q), static_cast<const T*>(X), m, n, scale, static_cast<T*>(O), \
+                          lse, ws, stream)
+    if (bf16) {
+        if (d == 64) XA_FWD(uint16_t, 4);
+        if (d == 128) XA_FWD(uint16_t, 8);
+        XA_FWD(uint16_t, 16);
+    }
+    if (d == 64) XA_FWD(float, 4);
+    if (d == 128) XA_FWD(float, 8);
+    XA_FWD(float, 16);
+#undef XA_FWD
+}
+
+hipError_t launch_xattn_bwd(const XattnPlan& p, bool bf16, const void* Q, const void* X, const void* O,
+                            const void* dO, const float* lse, int m, int64_t n, int d, float scale, float* dQ,
+                            void* dX, void* ws, hipStream_t stream) {
+#define XA_BWD(T, EPL)                                                                                          \
+    return bwd_as<T, EPL>(p, static_cast<const T*>(Q), static_cast<const T*>(X), static_cast<const T*>(O),      \
+                          static_cast<const T*>(dO), lse, m, n, scale, dQ, static_cast<T*>(dX), ws, stream)
+    if (bf16) {
+        if (d == 64) XA_BWD(uint16_t, 4);
+        if (d == 128) XA_BWD(uint16_t, 8);
+        XA_BWD(uint16_t, 16);
+    }
+    if (d == 64) XA_BWD(float, 4);
+    if (d == 128) XA_BWD(float, 8);
+    XA_BWD(float, 16);
+#undef XA_BWD
+}
+
+}  // namespace svc

@@ -39,6 +39,7 @@ SYMBOLS = (
     "sv_sparseconv2d_bwd_dw", "sv_workspace_bytes", "sv_sparseconv2d_chunked",
     "sv_chunked_workspace_bytes", "sv_sparseconv2d_chunked_host", "sv_chunked_host_workspace_bytes",
     "sv_stage_gather", "sv_stage_scatter", "sv_status_string", "sv_version",
+    "sv_xattn_fwd", "sv_xattn_bwd", "sv_xattn_workspace_bytes",
 )
 
 
@@ -103,6 +104,9 @@ def load(path: str = LIB_PATH):
         "sv_chunked_host_workspace_bytes": ([ctypes.POINTER(ChunkedHostDesc), ctypes.c_uint32], sz),
         "sv_stage_gather": ([P, i64, P, i64, P, i32, E, P], E),
         "sv_stage_scatter": ([P, P, i64, P, i64, i32, E, P], E),
+        "sv_xattn_fwd": ([P, P, i64, i64, i32, ctypes.c_float, E, P, P, P, sz, P], E),
+        "sv_xattn_bwd": ([P, P, P, P, P, i64, i64, i32, ctypes.c_float, E, P, P, P, sz, P], E),
+        "sv_xattn_workspace_bytes": ([i32, i64, i64, i32], sz),
         "sv_status_string": ([E], ctypes.c_char_p),
         "sv_version": ([], ctypes.c_char_p),
     }
@@ -311,6 +315,56 @@ def sv_stage_scatter(src, rows, dst, stream=None):
 
 
 # ---------------------------------------------------------- conveniences
+def sv_xattn_workspace_bytes(backward, m, n, d) -> int:
+    return int(load().sv_xattn_workspace_bytes(1 if backward else 0, int(m), int(n), int(d)))
+
+
+def sv_xattn_fwd(Q, X, O, lse, workspace, scale=0.0, stream=None):
+    m, d = Q.shape
+    n = X.shape[0]
+    assert X.shape[1] == d and O.shape == (m, d) and lse.shape == (m,) and lse.dtype == torch.float32
+    assert Q.dtype == X.dtype == O.dtype
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_xattn_fwd(_ptr(Q), _ptr(X), m, n, d, float(scale), _dt(Q), _ptr(O), _ptr(lse),
+                             _ptr(workspace), wsb, _stream(stream))
+    _check(st, "sv_xattn_fwd")
+
+
+def sv_xattn_bwd(Q, X, O, dO, lse, dQ, dX, workspace, scale=0.0, stream=None):
+    m, d = Q.shape
+    n = X.shape[0]
+    assert X.shape[1] == d and O.shape == (m, d) and dO.shape == (m, d) and lse.shape == (m,)
+    assert dQ.shape == (m, d) and dQ.dtype == torch.float32 and dX.shape == (n, d)
+    assert Q.dtype == X.dtype == O.dtype == dO.dtype == dX.dtype
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_xattn_bwd(_ptr(Q), _ptr(X), _ptr(O), _ptr(dO), _ptr(lse), m, n, d, float(scale), _dt(Q),
+                             _ptr(dQ), _ptr(dX), _ptr(workspace), wsb, _stream(stream))
+    _check(st, "sv_xattn_bwd")
+
+
+def xattn_fwd(Q, X, scale=0.0):
+    """Cross-attention of the auxiliary tokens Q [m,d] over the visual tokens
+    X [n,d] (keys = values).  Returns (O [m,d] in Q's dtype, lse [m] fp32)."""
+    m, d = Q.shape
+    O = torch.empty_like(Q)
+    lse = torch.empty((m,), dtype=torch.float32, device=Q.device)
+    ws = torch.empty(max(256, sv_xattn_workspace_bytes(False, m, X.shape[0], d)), dtype=torch.uint8,
+                     device=Q.device)
+    sv_xattn_fwd(Q, X, O, lse, ws, scale)
+    return O, lse
+
+
+def xattn_bwd(Q, X, O, dO, lse, scale=0.0):
+    """Returns (dQ [m,d] fp32, dX [n,d] in X's dtype)."""
+    m, d = Q.shape
+    dQ = torch.empty((m, d), dtype=torch.float32, device=Q.device)
+    dX = torch.empty_like(X)
+    ws = torch.empty(max(256, sv_xattn_workspace_bytes(True, m, X.shape[0], d)), dtype=torch.uint8,
+                     device=Q.device)
+    sv_xattn_bwd(Q, X, O, dO, lse, dQ, dX, ws, scale)
+    return dQ, dX
+
+
 def build_index(coords, frame_offsets, T, H, W, with_map=False, check=True, stream=None):
     """Allocate and fill N (and M); with `check`, synchronise and raise on a
     coordinate error reported by the device flag."""

@@ -163,3 +163,38 @@ def test_chunked_host_validation_and_workspace(lib):
     d.dX_host = None
     assert lib.sv_sparseconv2d_chunked_host(ctypes.byref(d), passes, None, 0, FAKE, ctypes.c_void_p(8192),
                                             ctypes.c_void_p(12288)) == ops.SV_ERR_INVALID_ARG
+
+
+def test_xattn_validation_and_workspace(lib):
+    F32, BF16 = ops.SV_F32, ops.SV_BF16
+    ws = lib.sv_xattn_workspace_bytes
+    # unsupported head width, negative sizes, too many queries, bad dtype
+    assert lib.sv_xattn_fwd(FAKE, FAKE, 1, 8, 96, 0.0, BF16, FAKE, FAKE, FAKE, 1 << 20, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_xattn_fwd(FAKE, FAKE, -1, 8, 64, 0.0, BF16, FAKE, FAKE, FAKE, 1 << 20, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_xattn_fwd(FAKE, FAKE, 70000, 8, 64, 0.0, BF16, FAKE, FAKE, FAKE, 1 << 20, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_xattn_fwd(FAKE, FAKE, 1, 8, 64, 0.0, 5, FAKE, FAKE, FAKE, 1 << 20, None) == ops.SV_ERR_INVALID_ARG
+    # null pointers, misaligned rows, a non-finite scale
+    assert lib.sv_xattn_fwd(None, FAKE, 1, 8, 64, 0.0, F32, FAKE, FAKE, FAKE, 1 << 20, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_xattn_fwd(FAKE, ctypes.c_void_p(4100), 1, 8, 64, 0.0, F32, FAKE, FAKE, FAKE, 1 << 20,
+                            None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_xattn_fwd(FAKE, FAKE, 1, 8, 64, float("inf"), F32, FAKE, FAKE, FAKE, 1 << 20,
+                            None) == ops.SV_ERR_INVALID_ARG
+    # short workspace
+    need = ws(0, 3, 50000, 256)
+    assert need > 0
+    assert lib.sv_xattn_fwd(FAKE, FAKE, 3, 50000, 256, 0.0, BF16, FAKE, FAKE, FAKE, need - 1,
+                            None) == ops.SV_ERR_WORKSPACE
+    needb = ws(1, 3, 50000, 256)
+    assert lib.sv_xattn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 50000, 256, 0.0, BF16, FAKE, FAKE, FAKE, needb - 1,
+                            None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_xattn_bwd(FAKE, FAKE, FAKE, None, FAKE, 3, 50000, 256, 0.0, BF16, FAKE, FAKE, FAKE, needb,
+                            None) == ops.SV_ERR_INVALID_ARG
+    # nothing to do: no queries and no keys
+    assert lib.sv_xattn_fwd(None, None, 0, 0, 64, 0.0, BF16, None, None, None, 0, None) == ops.SV_OK
+    assert lib.sv_xattn_bwd(None, None, None, None, None, 0, 0, 64, 0.0, BF16, None, None, None, 0,
+                            None) == ops.SV_OK
+    # workspace: block partials only, bounded by ~512 blocks whatever n
+    assert ws(0, 1, 10, 100) == 0
+    for m, n, d in [(1, 1, 64), (1, 58822, 256), (4, 181248, 128), (16, 10 ** 7, 256)]:
+        assert ws(0, m, n, d) <= 520 * m * (d + 2) * 4 + 1024
+        assert ws(1, m, n, d) <= 520 * m * d * 4 + 256
