@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4", "c4-host"])
+    p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4", "c4-host", "xattn"])
     p.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--dw-stream", choices=["side", "same"], default="side",
@@ -395,6 +395,59 @@ def host_stream_workload(args):
     print(json.dumps(out), flush=True)
 
 
+def xattn_workload(args):
+    """Asymmetric cross-attention of auxiliary queries (CLS: m = 1; and
+    m = 4) over the c5 stage-0 visual tokens (n = 58,822, d = 256, bf16),
+    forward and backward.  Memory-bound: the algorithmic bytes are the
+    token rows read (forward) and read plus written as dX (backward)."""
+    import numpy as np
+    import torch
+    from sparse_convolution_pruned_amd import ops, workloads as wl
+
+    S = wl.make_staged("c5")
+    X = torch.from_numpy(S.X0).to(torch.bfloat16).cuda()
+    n, d = X.shape
+    rng = np.random.default_rng(5)
+    res = []
+    for m in (1, 4):
+        Q = torch.from_numpy(rng.standard_normal((m, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+        dO = torch.from_numpy(rng.standard_normal((m, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+        O = torch.empty_like(Q)
+        lse = torch.empty((m,), dtype=torch.float32, device="cuda")
+        dQ = torch.empty((m, d), dtype=torch.float32, device="cuda")
+        dX = torch.empty_like(X)
+        wf = torch.empty(max(256, ops.sv_xattn_workspace_bytes(False, m, n, d)), dtype=torch.uint8, device="cuda")
+        wb = torch.empty(max(256, ops.sv_xattn_workspace_bytes(True, m, n, d)), dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            ops.sv_xattn_fwd(Q, X, O, lse, wf)
+            ops.sv_xattn_bwd(Q, X, O, dO, lse, dQ, dX, wb)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        tf = tb = 0.0
+        for _ in range(args.steps):
+            ev[0].record()
+            ops.sv_xattn_fwd(Q, X, O, lse, wf)
+            ev[1].record()
+            ops.sv_xattn_bwd(Q, X, O, dO, lse, dQ, dX, wb)
+            ev[2].record()
+            torch.cuda.synchronize()
+            tf += ev[0].elapsed_time(ev[1]) * 1e-3
+            tb += ev[1].elapsed_time(ev[2]) * 1e-3
+        tf /= args.steps
+        tb /= args.steps
+        bf_ = 2 * n * d
+        bb_ = 2 * 2 * n * d
+        res.append({"m": m, "fwd_us": round(tf * 1e6, 2), "bwd_us": round(tb * 1e6, 2),
+                    "fwd_gbps": round(bf_ / tf / 1e9, 1), "bwd_gbps": round(bb_ / tb / 1e9, 1),
+                    "fwd_frac_hbm": round(bf_ / tf / 1e9 / 8000.0, 4),
+                    "bwd_frac_hbm": round(bb_ / tb / 1e9 / 8000.0, 4)})
+    print(json.dumps({"workload": "xattn", "name": "auxiliary queries over the c5 stage-0 tokens, keys = values",
+                      "n": n, "d": d, "dtype": "bf16", "results": res,
+                      "note": "times are whole calls (partial + merge launches) between HIP events on the "
+                              "calling stream; bytes are the token rows read (fwd) and read + written (bwd)"}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -406,6 +459,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload == "c4-host":
         return host_stream_workload(args)
+    if args.workload == "xattn":
+        return xattn_workload(args)
     if args.workload != "c5":
         return layer_workload(args)
 

@@ -25,7 +25,8 @@
 // (one or two 16-byte loads), so a row is one contiguous 2d- or 4d-byte read;
 // a workgroup of 256 threads has 16 such groups.  Dot products finish with
 // four butterfly exchanges inside the 16-lane group.  Queries go through in
-// chunks of XA_MQ held in registers.
+// chunks held in registers (one query, the CLS case, has its own
+// instantiation).
 #include "internal.h"
 
 namespace svc {
@@ -89,22 +90,22 @@ __device__ __forceinline__ float group_sum(float s) {
 // Partials per (key block b, query q): pM[b][q] (largest score), pL[b][q]
 // (sum of exp(S - pM)) and pA[b][q][:] (sum of exp(S - pM) X[j]).  A block
 // without keys writes pM = -inf, pL = 0, pA = 0.
-template <typename T, int EPL>
+template <typename T, int EPL, int MQ>
 __global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_part(const T* __restrict__ Q, const T* __restrict__ X,
                                                                int m, int64_t n, float scale, int64_t kpb,
                                                                float* __restrict__ pM, float* __restrict__ pL,
                                                                float* __restrict__ pA) {
     constexpr int D = 16 * EPL;
     constexpr int WAVES = XA_THREADS / 64;
-    __shared__ float sM[WAVES][XA_MQ], sL[WAVES][XA_MQ];
-    __shared__ float sA[WAVES][XA_MQ][D];
+    __shared__ float sM[WAVES][MQ], sL[WAVES][MQ];
+    __shared__ float sA[WAVES][MQ][D];
     const int tid = threadIdx.x, lane = tid & 15, grp = tid >> 4, wave = tid >> 6;
     const int64_t b = blockIdx.x;
-    const int q0 = blockIdx.y * XA_MQ, mq = min(XA_MQ, m - q0);
+    const int q0 = blockIdx.y * MQ, mq = min(MQ, m - q0);
 
-    float qv[XA_MQ][EPL], acc[XA_MQ][EPL], M[XA_MQ], L[XA_MQ];
+    float qv[MQ][EPL], acc[MQ][EPL], M[MQ], L[MQ];
 #pragma unroll
-    for (int qi = 0; qi < XA_MQ; ++qi) {
+    for (int qi = 0; qi < MQ; ++qi) {
         if (qi < mq) load_part<T, EPL>(Q + static_cast<int64_t>(q0 + qi) * D + lane * EPL, qv[qi]);
         else
 #pragma unroll
@@ -114,12 +115,14 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_part(const T* __restri
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[qi][e] = 0.f;
     }
+    // Each group walks its keys two at a time with the next two rows already
+    // requested (request indices are clamped into the block, so no load sits
+    // behind a branch).
     const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
-    for (int64_t j = kbeg + grp; j < kend; j += XA_GROUPS) {
-        float x[EPL];
-        load_part<T, EPL>(X + j * D + lane * EPL, x);
+    auto row = [&](int64_t j) { return X + min(j, kend - 1) * D + lane * EPL; };
+    auto fold = [&](const float* x) {
 #pragma unroll
-        for (int qi = 0; qi < XA_MQ; ++qi) {
+        for (int qi = 0; qi < MQ; ++qi) {
             if (qi >= mq) break;
             float s = 0.f;
 #pragma unroll
@@ -133,12 +136,24 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_part(const T* __restri
             for (int e = 0; e < EPL; ++e) acc[qi][e] = fmaf(acc[qi][e], corr, p * x[e]);
             M[qi] = mn;
         }
+    };
+    float x0[EPL], x1[EPL];
+    load_part<T, EPL>(row(kbeg + grp), x0);
+    load_part<T, EPL>(row(kbeg + grp + XA_GROUPS), x1);
+    for (int64_t j = kbeg + grp; j < kend; j += 2 * XA_GROUPS) {
+        float n0[EPL], n1[EPL];
+        load_part<T, EPL>(row(j + 2 * XA_GROUPS), n0);
+        load_part<T, EPL>(row(j + 3 * XA_GROUPS), n1);
+        fold(x0);
+        if (j + XA_GROUPS < kend) fold(x1);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) { x0[e] = n0[e]; x1[e] = n1[e]; }
     }
     // Merge the four groups of a wave (pairs 16 lanes apart, then 32: the
     // same dims of another group; both partners compute the same sums), then
     // the four waves in wave order.
 #pragma unroll
-    for (int qi = 0; qi < XA_MQ; ++qi)
+    for (int qi = 0; qi < MQ; ++qi)
 #pragma unroll
         for (int k = 16; k <= 32; k <<= 1) {
             const float om = __shfl_xor(M[qi], k, 64), ol = __shfl_xor(L[qi], k, 64);
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_part(const T* __restri
         }
     if ((tid & 63) < 16)
 #pragma unroll
-        for (int qi = 0; qi < XA_MQ; ++qi) {
+        for (int qi = 0; qi < MQ; ++qi) {
             if (lane == 0) { sM[wave][qi] = M[qi]; sL[wave][qi] = L[qi]; }
 #pragma unroll
             for (int e = 0; e < EPL; ++e) sA[wave][qi][lane * EPL + e] = acc[qi][e];
@@ -175,25 +190,74 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_part(const T* __restri
     }
 }
 
-// O[q] = sum_b pA[b][q] w_b / sum_b pL[b][q] w_b with w_b = exp(pM[b][q] - max_b pM[b][q]),
-// lse[q] = max + log(sum); blocks in ascending order.  One workgroup per query.
+// Merge of the block partials.  Workgroup = (query q, 16 columns); thread
+// (column tid % 16, slice tid / 16) sums the blocks b = slice (mod 16) in
+// ascending order, eight requests in flight, and the 16 slice sums are added
+// in slice order.  The forward weights w_b = exp(pM[b][q] - max_b pM[b][q])
+// are computed once per workgroup into LDS.  XA_MAX_BLOCKS bounds B (the
+// plan stays below it).
+constexpr int XA_MAX_BLOCKS = 2048;
+constexpr int XA_MCOLS = 16;
+
+__device__ __forceinline__ float slice_sum(const float* __restrict__ part, const float* __restrict__ w, int64_t blocks,
+                                           int64_t stride, int slice) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int64_t b = slice;
+    for (; b + 7 * 16 < blocks; b += 8 * 16) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(b + 16 * u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] = fmaf(v[u], w ? w[b + 16 * u] : 1.f, a[u]);
+    }
+    for (int u = 0; b < blocks; b += 16, ++u) a[u & 7] = fmaf(part[b * stride], w ? w[b] : 1.f, a[u & 7]);
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
+__device__ __forceinline__ float slices_total(float v, float (*red)[XA_MCOLS]) {
+    const int c = threadIdx.x % XA_MCOLS, slice = threadIdx.x / XA_MCOLS;
+    red[slice][c] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int k = 0; k < XA_THREADS / XA_MCOLS; ++k) t += red[k][c];
+    return t;
+}
+
 template <typename T>
 __global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_merge(const float* __restrict__ pM, const float* __restrict__ pL,
                                                                 const float* __restrict__ pA, int64_t blocks, int m,
                                                                 int d, T* __restrict__ O, float* __restrict__ lse) {
-    const int q = blockIdx.x;
+    __shared__ float sW[XA_MAX_BLOCKS];
+    __shared__ float sRed[XA_THREADS / XA_MCOLS][XA_MCOLS];
+    __shared__ float sMax[XA_THREADS / 64], sSum[XA_THREADS / 64];
+    const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float mx = -INFINITY;
-    for (int64_t b = 0; b < blocks; ++b) mx = fmaxf(mx, pM[b * m + q]);
+    for (int64_t b = tid; b < blocks; b += XA_THREADS) mx = fmaxf(mx, pM[b * m + q]);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k, 64));
+    if (lane == 0) sMax[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
+    // weights, and the weighted count l = sum_b pL[b][q] w_b (thread sums in
+    // block order, then a fixed tree)
     float l = 0.f;
-    if (mx != -INFINITY)
-        for (int64_t b = 0; b < blocks; ++b) l = fmaf(pL[b * m + q], __expf(pM[b * m + q] - mx), l);
-    for (int c = threadIdx.x; c < d; c += XA_THREADS) {
-        float a = 0.f;
-        if (mx != -INFINITY)
-            for (int64_t b = 0; b < blocks; ++b) a = fmaf(pA[(b * m + q) * d + c], __expf(pM[b * m + q] - mx), a);
-        Elem<T>::store(O + static_cast<int64_t>(q) * d + c, l > 0.f ? a / l : 0.f);
+    for (int64_t b = tid; b < blocks; b += XA_THREADS) {
+        const float pm = pM[b * m + q];
+        const float wb = (mx == -INFINITY || pm == -INFINITY) ? 0.f : __expf(pm - mx);
+        sW[b] = wb;
+        l = fmaf(pL[b * m + q], wb, l);
     }
-    if (threadIdx.x == 0) lse[q] = (mx == -INFINITY || !(l > 0.f)) ? -INFINITY : mx + __logf(l);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) l += __shfl_xor(l, k, 64);
+    if (lane == 0) sSum[wave] = l;
+    __syncthreads();
+    l = (sSum[0] + sSum[1]) + (sSum[2] + sSum[3]);
+    const int c = blockIdx.y * XA_MCOLS + tid % XA_MCOLS;
+    const float v = c < d ? slice_sum(pA + static_cast<int64_t>(q) * d + c, sW, blocks,
+                                      static_cast<int64_t>(m) * d, tid / XA_MCOLS) : 0.f;
+    const float a = slices_total(v, sRed);
+    if (tid < XA_MCOLS && c < d) Elem<T>::store(O + static_cast<int64_t>(q) * d + c, l > 0.f ? a / l : 0.f);
+    if (blockIdx.y == 0 && tid == 0) lse[q] = (mx == -INFINITY || !(l > 0.f)) ? -INFINITY : mx + __logf(l);
 }
 
 // --------------------------------------------------------------- backward
@@ -250,9 +314,9 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_part(const T* __restri
     for (int qi = 0; qi < MQ; ++qi) Dq[qi] = sDq[qi];
 
     const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
-    for (int64_t j = kbeg + grp; j < kend; j += XA_GROUPS) {
-        float x[EPL], dx[EPL];
-        load_part<T, EPL>(X + j * D + lane * EPL, x);
+    auto row = [&](int64_t j) { return X + min(j, kend - 1) * D + lane * EPL; };
+    auto key = [&](int64_t j, const float* x) {
+        float dx[EPL];
         if (accumulate) load_part<T, EPL>(dX + j * D + lane * EPL, dx);
         else
 #pragma unroll
@@ -278,6 +342,18 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_part(const T* __restri
             }
         }
         store_part<T, EPL>(dX + j * D + lane * EPL, dx);
+    };
+    float x0[EPL], x1[EPL];
+    load_part<T, EPL>(row(kbeg + grp), x0);
+    load_part<T, EPL>(row(kbeg + grp + XA_GROUPS), x1);
+    for (int64_t j = kbeg + grp; j < kend; j += 2 * XA_GROUPS) {
+        float n0[EPL], n1[EPL];
+        load_part<T, EPL>(row(j + 2 * XA_GROUPS), n0);
+        load_part<T, EPL>(row(j + 3 * XA_GROUPS), n1);
+        key(j, x0);
+        if (j + XA_GROUPS < kend) key(j + XA_GROUPS, x1);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) { x0[e] = n0[e]; x1[e] = n1[e]; }
     }
     // dQ partial of the block: the groups of a wave added pairwise (16 lanes
     // apart, then 32), then the waves in wave order.
@@ -302,20 +378,21 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_part(const T* __restri
     }
 }
 
-// dQ[q][c] = sum_b pQ[b][q][c], b ascending.
+// dQ[q][c] = sum_b pQ[b][q][c]; same layout as the forward merge.
 __global__ __launch_bounds__(XA_THREADS) void k_xattn_dq_merge(const float* __restrict__ pQ, int64_t blocks, int m,
                                                                int d, float* __restrict__ dQ) {
-    const int64_t total = static_cast<int64_t>(m) * d;
-    for (int64_t t = static_cast<int64_t>(blockIdx.x) * XA_THREADS + threadIdx.x; t < total;
-         t += static_cast<int64_t>(gridDim.x) * XA_THREADS) {
-        float a = 0.f;
-        for (int64_t b = 0; b < blocks; ++b) a += pQ[b * total + t];
-        dQ[t] = a;
-    }
+    __shared__ float sRed[XA_THREADS / XA_MCOLS][XA_MCOLS];
+    const int q = blockIdx.x, tid = threadIdx.x;
+    const int c = blockIdx.y * XA_MCOLS + tid % XA_MCOLS;
+    const float v = c < d ? slice_sum(pQ + static_cast<int64_t>(q) * d + c, nullptr, blocks,
+                                      static_cast<int64_t>(m) * d, tid / XA_MCOLS) : 0.f;
+    const float a = slices_total(v, sRed);
+    if (tid < XA_MCOLS && c < d) dQ[static_cast<int64_t>(q) * d + c] = a;
 }
 
 // ------------------------------------------------------------------- host
-// Keys per block: about 512 blocks over n, a multiple of the 16 groups.
+// Keys per block: about 512 blocks over n (never more than XA_MAX_BLOCKS),
+// a multiple of the 16 groups.
 XattnPlan plan_xattn(int64_t m, int64_t n, int d) {
     XattnPlan p{};
     p.kpb = std::max<int64_t>(XA_GROUPS, ((n + 511) / 512 + XA_GROUPS - 1) / XA_GROUPS * XA_GROUPS);
@@ -338,14 +415,20 @@ static hipError_t fwd_as(const XattnPlan& p, const T* Q, const T* X, int m, int6
     float* pL = reinterpret_cast<float*>(static_cast<char*>(ws) + up(mb * 4));
     float* pA = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * up(mb * 4));
     if (p.blocks > 0) {
-        dim3 grid(static_cast<unsigned>(p.blocks), static_cast<unsigned>((m + XA_MQ - 1) / XA_MQ));
-        hipLaunchKernelGGL((k_xattn_fwd_part<T, EPL>), grid, dim3(XA_THREADS), 0, stream, Q, X, m, n, scale, p.kpb,
-                           pM, pL, pA);
+        // one query (the CLS token) gets an instantiation with a quarter of
+        // the registers, hence twice the waves per SIMD
+        if (m == 1)
+            hipLaunchKernelGGL((k_xattn_fwd_part<T, EPL, 1>), dim3(static_cast<unsigned>(p.blocks)), dim3(XA_THREADS),
+                               0, stream, Q, X, m, n, scale, p.kpb, pM, pL, pA);
+        else
+            hipLaunchKernelGGL((k_xattn_fwd_part<T, EPL, XA_MQ>),
+                               dim3(static_cast<unsigned>(p.blocks), static_cast<unsigned>((m + XA_MQ - 1) / XA_MQ)),
+                               dim3(XA_THREADS), 0, stream, Q, X, m, n, scale, p.kpb, pM, pL, pA);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_xattn_fwd_merge<T>, dim3(m), dim3(XA_THREADS), 0, stream, pM, pL, pA, p.blocks, m, 16 * EPL,
-                       O, lse);
+    hipLaunchKernelGGL(k_xattn_fwd_merge<T>, dim3(m, 16 * EPL / XA_MCOLS), dim3(XA_THREADS), 0, stream, pM, pL, pA,
+                       p.blocks, m, 16 * EPL, O, lse);
     return hipGetLastError();
 }
 
@@ -354,16 +437,21 @@ static hipError_t bwd_as(const XattnPlan& p, const T* Q, const T* X, const T* O,
                          int m, int64_t n, float scale, float* dQ, T* dX, void* ws, hipStream_t stream) {
     constexpr int MQ = EPL >= 16 ? 2 : 4;
     float* pQ = static_cast<float*>(ws);
-    if (p.blocks > 0)
+    if (p.blocks > 0 && m == 1) {
+        hipLaunchKernelGGL((k_xattn_bwd_part<T, EPL, 1>), dim3(static_cast<unsigned>(p.blocks)), dim3(XA_THREADS), 0,
+                           stream, Q, X, O, dO, lse, m, 0, n, scale, p.kpb, 0, dX, pQ);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else if (p.blocks > 0) {
         for (int q0 = 0; q0 < m; q0 += MQ) {
             hipLaunchKernelGGL((k_xattn_bwd_part<T, EPL, MQ>), dim3(static_cast<unsigned>(p.blocks)), dim3(XA_THREADS), 0,
                                stream, Q, X, O, dO, lse, m, q0, n, scale, p.kpb, q0 > 0 ? 1 : 0, dX, pQ);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-    const int64_t total = static_cast<int64_t>(m) * 16 * EPL;
-    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((total + XA_THREADS - 1) / XA_THREADS, 1024));
-    hipLaunchKernelGGL(k_xattn_dq_merge, dim3(grid), dim3(XA_THREADS), 0, stream, pQ, p.blocks, m, 16 * EPL, dQ);
+    }
+    hipLaunchKernelGGL(k_xattn_dq_merge, dim3(m, 16 * EPL / XA_MCOLS), dim3(XA_THREADS), 0, stream, pQ, p.blocks, m,
+                       16 * EPL, dQ);
     return hipGetLastError();
 }
 
