@@ -254,11 +254,16 @@ size_t sv_chunked_host_workspace_bytes(const sv_chunked_host_desc *desc, uint32_
  *
  * Backward for an upstream gradient dO [m][d], given the forward's O and
  * lse: dQ [m][d] (fp32) and dX [n][d] written, with
- *   dS[q][j] = P[q][j] (<dO[q], X[j]> - <dO[q], O[q]>),
+ *   D[q]     = sum_j P[q][j] <dO[q], X[j]>   (summed over the keys)
+ *   dS[q][j] = P[q][j] (<dO[q], X[j]> - D[q]),
  *   dQ[q]    = scale sum_j dS[q][j] X[j],
  *   dX[j]    = scale sum_q dS[q][j] Q[q] + sum_q P[q][j] dO[q]
- * (X enters as keys and as values).  Workspace sv_xattn_workspace_bytes(1,
- * m, n, d) bytes.  With m == 0, dX is zeroed. */
+ * (X enters as keys and as values).  O only shifts the keys inside these
+ * sums (dS sums to zero over the keys, so the result is the same for any
+ * shift in exact arithmetic); shifting by the softmax-weighted mean keeps
+ * fp32 accurate when the tokens share a large component.  Two passes over
+ * X.  Workspace sv_xattn_workspace_bytes(1, m, n, d) bytes.  With m == 0,
+ * dX is zeroed. */
 sv_status sv_xattn_fwd(const void *Q, const void *X, int64_t m, int64_t n, int32_t d,
                        float scale, sv_dtype dtype, void *O, float *lse,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);

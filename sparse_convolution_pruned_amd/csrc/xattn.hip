@@ -12,12 +12,14 @@
 //             sum and weighted row sum per query (the online softmax) and
 //             writes them as a partial; a second kernel merges the partials
 //             in block order into O and lse = log sum_j exp S[q][j].
-//   backward: with lse from the forward, P and
-//               dS[q][j] = P[q][j] (<dO[q], X[j]> - <dO[q], O[q]>)
-//             are recomputed per key; each key's row of
-//               dX[j] = scale sum_q dS[q][j] Q[q] + sum_q P[q][j] dO[q]
-//             is written directly, and dQ[q] = scale sum_j dS[q][j] X[j] goes
-//             through block partials merged in block order.
+//   backward: with lse from the forward, P is recomputed per key; a first
+//             pass sums D[q] = sum_j P[q][j] <dO[q], X[j]> per key block (keys
+//             shifted by O[q], see the backward section), a second writes each
+//             key's row of
+//               dX[j] = scale sum_q dS[q][j] Q[q] + sum_q P[q][j] dO[q],
+//               dS[q][j] = P[q][j] (<dO[q], X[j]> - D[q]),
+//             and block partials of dQ[q] = scale sum_j dS[q][j] X[j], merged
+//             in block order.
 // Everything is summed in a fixed order, so results are bitwise
 // reproducible.
 //
@@ -261,57 +263,136 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_merge(const float* __r
 }
 
 // --------------------------------------------------------------- backward
-// One pass covers queries q0 .. q0 + MQ - 1 (MQ = 2 at d = 256, which keeps
-// the kernel near 160 VGPRs; 4 otherwise).  dX rows are written
-// (accumulate = 0) or added to (later passes); dQ partials go to
-// pQ[b][q][:] for the queries of the pass.
+// Conditioning.  dS[q][j] = P (dP[q][j] - D[q]) sums to zero over j, so dQ
+// and dS do not change when every key row is shifted by the same vector c
+// (the scores shift by a constant per query, which the softmax ignores).
+// When the tokens share a large component, the unshifted sums
+// sum_j dS X[j] and the dot products dP cancel to a small remainder and
+// fp32 loses it; with c = O[q] (the forward output, the softmax-weighted
+// mean of the keys) the shifted rows X[j] - O[q] are small and the sums are
+// well conditioned.  O only serves as this shift: any vector gives the same
+// result in exact arithmetic.
+//   dP~[q][j] = <dO[q], X[j] - O[q]>,  D~[q] = sum_j P dP~  (pass 1, block
+//   sums pS[b][q] added in block order by pass 2),  dS = P (dP~ - D~),
+//   dQ[q] = scale sum_j dS (X[j] - O[q]).
+//
+// Pass 1, queries q0 .. q0 + MQ - 1.
 template <typename T, int EPL, int MQ>
-__global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_part(const T* __restrict__ Q, const T* __restrict__ X,
+__global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_dsum(const T* __restrict__ Q, const T* __restrict__ X,
                                                                const T* __restrict__ O, const T* __restrict__ dO,
-                                                               const float* __restrict__ lse, int m, int q0,
-                                                               int64_t n, float scale, int64_t kpb, int accumulate,
-                                                               T* __restrict__ dX, float* __restrict__ pQ) {
+                                                               const float* __restrict__ lse, int m, int q0, int64_t n,
+                                                               float scale, int64_t kpb, float* __restrict__ pS) {
     constexpr int D = 16 * EPL;
     constexpr int WAVES = XA_THREADS / 64;
-    __shared__ float sDq[MQ];
-    __shared__ float sQ[WAVES][MQ][D];
+    __shared__ float sS[WAVES][MQ];
     const int tid = threadIdx.x, lane = tid & 15, grp = tid >> 4, wave = tid >> 6;
     const int64_t b = blockIdx.x;
     const int mq = min(MQ, m - q0);
-
-    float qv[MQ][EPL], gv[MQ][EPL], dq[MQ][EPL], lq[MQ];
+    float qv[MQ][EPL], gv[MQ][EPL], cv[MQ][EPL], lq[MQ], ss[MQ];
 #pragma unroll
     for (int qi = 0; qi < MQ; ++qi) {
         if (qi < mq) {
             load_part<T, EPL>(Q + static_cast<int64_t>(q0 + qi) * D + lane * EPL, qv[qi]);
             load_part<T, EPL>(dO + static_cast<int64_t>(q0 + qi) * D + lane * EPL, gv[qi]);
+            load_part<T, EPL>(O + static_cast<int64_t>(q0 + qi) * D + lane * EPL, cv[qi]);
             lq[qi] = lse[q0 + qi];
         } else {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) { qv[qi][e] = 0.f; gv[qi][e] = 0.f; }
+            for (int e = 0; e < EPL; ++e) { qv[qi][e] = 0.f; gv[qi][e] = 0.f; cv[qi][e] = 0.f; }
+            lq[qi] = 0.f;
+        }
+        ss[qi] = 0.f;
+    }
+    const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
+    auto row = [&](int64_t j) { return X + min(j, kend - 1) * D + lane * EPL; };
+    auto fold = [&](const float* x) {
+#pragma unroll
+        for (int qi = 0; qi < MQ; ++qi) {
+            if (qi >= mq) break;
+            float s = 0.f, g = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                s = fmaf(x[e], qv[qi][e], s);
+                g = fmaf(x[e] - cv[qi][e], gv[qi][e], g);
+            }
+            s = group_sum(s);
+            g = group_sum(g);
+            ss[qi] = fmaf(__expf(scale * s - lq[qi]), g, ss[qi]);
+        }
+    };
+    float x0[EPL], x1[EPL];
+    load_part<T, EPL>(row(kbeg + grp), x0);
+    load_part<T, EPL>(row(kbeg + grp + XA_GROUPS), x1);
+    for (int64_t j = kbeg + grp; j < kend; j += 2 * XA_GROUPS) {
+        float n0[EPL], n1[EPL];
+        load_part<T, EPL>(row(j + 2 * XA_GROUPS), n0);
+        load_part<T, EPL>(row(j + 3 * XA_GROUPS), n1);
+        fold(x0);
+        if (j + XA_GROUPS < kend) fold(x1);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) { x0[e] = n0[e]; x1[e] = n1[e]; }
+    }
+#pragma unroll
+    for (int qi = 0; qi < MQ; ++qi) {
+        ss[qi] += __shfl_xor(ss[qi], 16, 64);
+        ss[qi] += __shfl_xor(ss[qi], 32, 64);
+    }
+    if ((tid & 63) == 0)
+#pragma unroll
+        for (int qi = 0; qi < MQ; ++qi) sS[wave][qi] = ss[qi];
+    __syncthreads();
+    if (tid < mq) pS[b * m + q0 + tid] = ((sS[0][tid] + sS[1][tid]) + sS[2][tid]) + sS[3][tid];
+}
+
+// Pass 2, the same queries: D[q] from the block sums (in block order, then a
+// fixed tree), dS = P (dP - D) per key; dX rows are written (accumulate = 0)
+// or added to (later query chunks); dQ block partials go to pQ[b][q][:].
+template <typename T, int EPL, int MQ>
+__global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_part(const T* __restrict__ Q, const T* __restrict__ X,
+                                                               const T* __restrict__ O, const T* __restrict__ dO,
+                                                               const float* __restrict__ lse,
+                                                               const float* __restrict__ pS, int64_t blocks, int m,
+                                                               int q0, int64_t n, float scale, int64_t kpb,
+                                                               int accumulate, T* __restrict__ dX,
+                                                               float* __restrict__ pQ) {
+    constexpr int D = 16 * EPL;
+    constexpr int WAVES = XA_THREADS / 64;
+    __shared__ float sD[WAVES][MQ];
+    __shared__ float sQ[WAVES][MQ][D];
+    const int tid = threadIdx.x, lane = tid & 15, grp = tid >> 4, wave = tid >> 6;
+    const int64_t b = blockIdx.x;
+    const int mq = min(MQ, m - q0);
+
+    float Dq[MQ];
+#pragma unroll
+    for (int qi = 0; qi < MQ; ++qi) {
+        float v = 0.f;
+        if (qi < mq)
+            for (int64_t bb = tid; bb < blocks; bb += XA_THREADS) v += pS[bb * m + q0 + qi];
+#pragma unroll
+        for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k, 64);
+        if ((tid & 63) == 0) sD[wave][qi] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qi = 0; qi < MQ; ++qi) Dq[qi] = (sD[0][qi] + sD[1][qi]) + (sD[2][qi] + sD[3][qi]);
+
+    float qv[MQ][EPL], gv[MQ][EPL], cv[MQ][EPL], dq[MQ][EPL], lq[MQ];
+#pragma unroll
+    for (int qi = 0; qi < MQ; ++qi) {
+        if (qi < mq) {
+            load_part<T, EPL>(Q + static_cast<int64_t>(q0 + qi) * D + lane * EPL, qv[qi]);
+            load_part<T, EPL>(dO + static_cast<int64_t>(q0 + qi) * D + lane * EPL, gv[qi]);
+            load_part<T, EPL>(O + static_cast<int64_t>(q0 + qi) * D + lane * EPL, cv[qi]);
+            lq[qi] = lse[q0 + qi];
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) { qv[qi][e] = 0.f; gv[qi][e] = 0.f; cv[qi][e] = 0.f; }
             lq[qi] = 0.f;
         }
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dq[qi][e] = 0.f;
     }
-    // D[q] = <dO[q], O[q]> by the first group (16 lanes, fixed order).
-    if (grp == 0)
-#pragma unroll
-        for (int qi = 0; qi < MQ; ++qi) {
-            float o[EPL];
-            float s = 0.f;
-            if (qi < mq) {
-                load_part<T, EPL>(O + static_cast<int64_t>(q0 + qi) * D + lane * EPL, o);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) s = fmaf(gv[qi][e], o[e], s);
-            }
-            s = group_sum(s);
-            if (lane == 0) sDq[qi] = s;
-        }
-    __syncthreads();
-    float Dq[MQ];
-#pragma unroll
-    for (int qi = 0; qi < MQ; ++qi) Dq[qi] = sDq[qi];
 
     const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
     auto row = [&](int64_t j) { return X + min(j, kend - 1) * D + lane * EPL; };
@@ -324,21 +405,21 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_part(const T* __restri
 #pragma unroll
         for (int qi = 0; qi < MQ; ++qi) {
             if (qi >= mq) break;
-            float s = 0.f, g = 0.f;
+            float s = 0.f, g = 0.f, xc[EPL];
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
+                xc[e] = x[e] - cv[qi][e];
                 s = fmaf(x[e], qv[qi][e], s);
-                g = fmaf(x[e], gv[qi][e], g);
+                g = fmaf(xc[e], gv[qi][e], g);
             }
             s = group_sum(s);
             g = group_sum(g);
             const float p = __expf(scale * s - lq[qi]);
-            const float ds = p * (g - Dq[qi]);
-            const float ks = scale * ds;
+            const float ks = scale * p * (g - Dq[qi]);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 dx[e] = fmaf(ks, qv[qi][e], fmaf(p, gv[qi][e], dx[e]));
-                dq[qi][e] = fmaf(ks, x[e], dq[qi][e]);
+                dq[qi][e] = fmaf(ks, xc[e], dq[qi][e]);
             }
         }
         store_part<T, EPL>(dX + j * D + lane * EPL, dx);
@@ -384,10 +465,10 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_dq_merge(const float* __re
     __shared__ float sRed[XA_THREADS / XA_MCOLS][XA_MCOLS];
     const int q = blockIdx.x, tid = threadIdx.x;
     const int c = blockIdx.y * XA_MCOLS + tid % XA_MCOLS;
-    const float v = c < d ? slice_sum(pQ + static_cast<int64_t>(q) * d + c, nullptr, blocks,
-                                      static_cast<int64_t>(m) * d, tid / XA_MCOLS) : 0.f;
+    const int64_t off = static_cast<int64_t>(q) * d + c;
+    const float v = c < d ? slice_sum(pQ + off, nullptr, blocks, static_cast<int64_t>(m) * d, tid / XA_MCOLS) : 0.f;
     const float a = slices_total(v, sRed);
-    if (tid < XA_MCOLS && c < d) dQ[static_cast<int64_t>(q) * d + c] = a;
+    if (tid < XA_MCOLS && c < d) dQ[off] = a;
 }
 
 // ------------------------------------------------------------------- host
@@ -400,7 +481,7 @@ XattnPlan plan_xattn(int64_t m, int64_t n, int d) {
     auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
     const size_t mb = static_cast<size_t>(m) * p.blocks;
     p.fwd_bytes = up(mb * 4) * 2 + up(mb * d * 4);
-    p.bwd_bytes = up(mb * d * 4);
+    p.bwd_bytes = up(mb * d * 4) + up(mb * 4);
     return p;
 }
 
@@ -433,21 +514,31 @@ static hipError_t fwd_as(const XattnPlan& p, const T* Q, const T* X, int m, int6
 }
 
 template <typename T, int EPL>
-static hipError_t bwd_as(const XattnPlan& p, const T* Q, const T* X, const T* O, const T* dO, const float* lse,
-                         int m, int64_t n, float scale, float* dQ, T* dX, void* ws, hipStream_t stream) {
+static hipError_t bwd_as(const XattnPlan& p, const T* Q, const T* X, const T* O, const T* dO, const float* lse, int m,
+                         int64_t n, float scale, float* dQ, T* dX, void* ws, hipStream_t stream) {
     constexpr int MQ = EPL >= 16 ? 2 : 4;
+    auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+    const size_t mb = static_cast<size_t>(m) * p.blocks;
     float* pQ = static_cast<float*>(ws);
+    float* pS = reinterpret_cast<float*>(static_cast<char*>(ws) + up(mb * 16 * EPL * 4));
+    const dim3 grid(static_cast<unsigned>(p.blocks));
+    hipError_t e = hipSuccess;
     if (p.blocks > 0 && m == 1) {
-        hipLaunchKernelGGL((k_xattn_bwd_part<T, EPL, 1>), dim3(static_cast<unsigned>(p.blocks)), dim3(XA_THREADS), 0,
-                           stream, Q, X, O, dO, lse, m, 0, n, scale, p.kpb, 0, dX, pQ);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_xattn_bwd_dsum<T, EPL, 1>), grid, dim3(XA_THREADS), 0, stream, Q, X, O, dO, lse, m, 0,
+                           n, scale, p.kpb, pS);
+        hipLaunchKernelGGL((k_xattn_bwd_part<T, EPL, 1>), grid, dim3(XA_THREADS), 0, stream, Q, X, O, dO, lse, pS,
+                           p.blocks, m, 0, n, scale, p.kpb, 0, dX, pQ);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (p.blocks > 0) {
         for (int q0 = 0; q0 < m; q0 += MQ) {
-            hipLaunchKernelGGL((k_xattn_bwd_part<T, EPL, MQ>), dim3(static_cast<unsigned>(p.blocks)), dim3(XA_THREADS), 0,
-                               stream, Q, X, O, dO, lse, m, q0, n, scale, p.kpb, q0 > 0 ? 1 : 0, dX, pQ);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((k_xattn_bwd_dsum<T, EPL, MQ>), grid, dim3(XA_THREADS), 0, stream, Q, X, O, dO, lse, m,
+                               q0, n, scale, p.kpb, pS);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        for (int q0 = 0; q0 < m; q0 += MQ) {
+            hipLaunchKernelGGL((k_xattn_bwd_part<T, EPL, MQ>), grid, dim3(XA_THREADS), 0, stream, Q, X, O, dO, lse,
+                               pS, p.blocks, m, q0, n, scale, p.kpb, q0 > 0 ? 1 : 0, dX, pQ);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
     hipLaunchKernelGGL(k_xattn_dq_merge, dim3(m, 16 * EPL / XA_MCOLS), dim3(XA_THREADS), 0, stream, pQ, p.blocks, m,
@@ -474,8 +565,8 @@ hipError_t launch_xattn_fwd(const XattnPlan& p, bool bf16, const void* Q, const 
 hipError_t launch_xattn_bwd(const XattnPlan& p, bool bf16, const void* Q, const void* X, const void* O,
                             const void* dO, const float* lse, int m, int64_t n, int d, float scale, float* dQ,
                             void* dX, void* ws, hipStream_t stream) {
-#define XA_BWD(T, EPL)                                                                                          \
-    return bwd_as<T, EPL>(p, static_cast<const T*>(Q), static_cast<const T*>(X), static_cast<const T*>(O),      \
+#define XA_BWD(T, EPL)                                                                                         \
+    return bwd_as<T, EPL>(p, static_cast<const T*>(Q), static_cast<const T*>(X), static_cast<const T*>(O),     \
                           static_cast<const T*>(dO), lse, m, n, scale, dQ, static_cast<T*>(dX), ws, stream)
     if (bf16) {
         if (d == 64) XA_BWD(uint16_t, 4);

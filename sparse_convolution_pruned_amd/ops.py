@@ -355,7 +355,7 @@ def xattn_fwd(Q, X, scale=0.0):
 
 
 def xattn_bwd(Q, X, O, dO, lse, scale=0.0):
-    """Returns (dQ [m,d] fp32, dX [n,d] in X's dtype)."""
+    """Returns (dQ [m,d] fp32, dX [n,d] in X's dtype), given the forward's O and lse."""
     m, d = Q.shape
     dQ = torch.empty((m, d), dtype=torch.float32, device=Q.device)
     dX = torch.empty_like(X)

@@ -197,4 +197,4 @@ def test_xattn_validation_and_workspace(lib):
     assert ws(0, 1, 10, 100) == 0
     for m, n, d in [(1, 1, 64), (1, 58822, 256), (4, 181248, 128), (16, 10 ** 7, 256)]:
         assert ws(0, m, n, d) <= 520 * m * (d + 2) * 4 + 1024
-        assert ws(1, m, n, d) <= 520 * m * d * 4 + 256
+        assert ws(1, m, n, d) <= 520 * m * (d + 1) * 4 + 512
