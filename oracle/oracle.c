@@ -10,7 +10,9 @@
  * Convolutions for Efficient Temporal Action Detection", paper notes page):
  *
  *   orc_build_index   Key Design 1 ("Static Neighbor Index Table"), the two
- *                     steps and the piecewise equation for N[k, j].
+ *                     steps and the piecewise equation for N[k, j], for a
+ *                     K x K neighbourhood (the Background's "K x K spatial
+ *                     neighbors"; the page's tables and kernels use K = 3).
  *   orc_fwd           Key Design 2 ("Native Sparse 2D Convolution Kernels"),
  *                     the equation y_k = sum_j W_j x[N[k, j]] with N = -1 read
  *                     as zero padding, plus a per-channel bias.
@@ -31,18 +33,19 @@
  *                     softmax and the weighted sum.
  *
  * Readings of points the page leaves open:
- *   - tap order j = 3*(dy+1) + (dx+1), dy, dx in {-1, 0, 1}; the centre tap
- *     is j = 4 and is part of the 9-column table;
+ *   - K odd; tap order j = K*(dy+r) + (dx+r) with r = K/2 and dy, dx in
+ *     [-r, r] (for K = 3: j = 3*(dy+1) + (dx+1)); the centre tap j = K*K/2
+ *     is part of the K*K-column table; the mirror of tap j is K*K-1-j;
  *   - one map M per frame (the convolution is spatial, within a frame), the
  *     table holds global indices into the packed sequence;
  *   - cross-correlation convention: tap j of token k reads the token at
  *     (y_k + dy_j, x_k + dx_j) and applies W[j] to it;
  *   - row form: W[j] is C_in x C_out and y_k = sum_j x[N[k,j]] W[j] + b;
- *   - stride 1, zero padding 1, no dilation;
+ *   - stride 1, zero padding r, no dilation;
  *   - out-of-range or duplicate coordinates are errors, never "last writer".
  *
- * Layouts (row-major, contiguous): X [n][Ci], Y [n][Co], N [n][9],
- * W [9][Ci][Co], b [Co], dW [9][Ci][Co], db [Co].  Flat coordinate
+ * Layouts (row-major, contiguous): X [n][Ci], Y [n][Co], N [n][K*K],
+ * W [K*K][Ci][Co], b [Co], dW [K*K][Ci][Co], db [Co].  Flat coordinate
  * p = y * W + x; frame t holds tokens frame_offsets[t] .. frame_offsets[t+1]-1.
  *
  * Every function sums each output in a fixed order (tap ascending, then
@@ -73,10 +76,11 @@ int orc_threads(int want)
 /* Key Design 1, step 1 then step 2, frame by frame.
  * M (nullable) receives [T][H][W] global token indices, -1 where no token. */
 int orc_build_index(const int32_t *coords, const int32_t *frame_offsets,
-                    int32_t T, int32_t H, int32_t W, int64_t n,
+                    int32_t T, int32_t H, int32_t W, int64_t n, int32_t K,
                     int32_t *N, int32_t *M)
 {
-    if (T < 0 || H <= 0 || W <= 0 || n < 0) return ORC_BAD_ARGS;
+    if (T < 0 || H <= 0 || W <= 0 || n < 0 || K < 1 || K % 2 == 0) return ORC_BAD_ARGS;
+    const int taps = K * K, r = K / 2;
     if (frame_offsets[0] != 0 || frame_offsets[T] != n) return ORC_BAD_ARGS;
     int64_t cells = (int64_t)H * W;
     int32_t *map = (int32_t *)malloc(sizeof(int32_t) * (size_t)cells);
@@ -95,15 +99,15 @@ int orc_build_index(const int32_t *coords, const int32_t *frame_offsets,
             map[p] = (int32_t)k;
         }
         if (status != ORC_OK) break;
-        /* step 2: for each kept token, read the map at the 9 offsets; a
+        /* step 2: for each kept token, read the map at the K*K offsets; a
          * cell outside the H x W grid reads as -1. */
         for (int64_t k = beg; k < end; ++k) {
             int32_t y = coords[k] / W, x = coords[k] % W;
-            for (int j = 0; j < 9; ++j) {
-                int32_t yy = y + (j / 3 - 1), xx = x + (j % 3 - 1);
+            for (int j = 0; j < taps; ++j) {
+                int32_t yy = y + (j / K - r), xx = x + (j % K - r);
                 int32_t v = -1;
                 if (yy >= 0 && yy < H && xx >= 0 && xx < W) v = map[yy * W + xx];
-                N[k * 9 + j] = v;
+                N[k * taps + j] = v;
             }
         }
         if (M) memcpy(M + (int64_t)t * cells, map, sizeof(int32_t) * (size_t)cells);
@@ -115,14 +119,14 @@ int orc_build_index(const int32_t *coords, const int32_t *frame_offsets,
 /* Key Design 2: Y[k][o] = sum_j sum_i X[N[k,j]][i] * W[j][i][o] + b[o];
  * a tap whose entry is -1 contributes nothing (zero padding). */
 void orc_fwd(const double *X, const int32_t *N, const double *Wt,
-             const double *b, double *Y, int64_t n, int32_t Ci, int32_t Co)
+             const double *b, double *Y, int64_t n, int32_t Ci, int32_t Co, int32_t taps)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t k = 0; k < n; ++k) {
         double *acc = Y + k * Co;
         for (int32_t o = 0; o < Co; ++o) acc[o] = 0.0;
-        for (int j = 0; j < 9; ++j) {
-            int32_t m = N[k * 9 + j];
+        for (int j = 0; j < taps; ++j) {
+            int32_t m = N[k * taps + j];
             if (m < 0) continue;
             const double *x = X + (int64_t)m * Ci;
             const double *w = Wt + (int64_t)j * Ci * Co;
@@ -141,15 +145,15 @@ void orc_fwd(const double *X, const int32_t *N, const double *Wt,
  * full size): Yr[r] = Y[rows[r]]. */
 void orc_fwd_rows(const double *X, const int32_t *N, const double *Wt,
                   const double *b, const int64_t *rows, int64_t nrows,
-                  double *Yr, int32_t Ci, int32_t Co)
+                  double *Yr, int32_t Ci, int32_t Co, int32_t taps)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t k = rows[r];
         double *acc = Yr + r * Co;
         for (int32_t o = 0; o < Co; ++o) acc[o] = 0.0;
-        for (int j = 0; j < 9; ++j) {
-            int32_t m = N[k * 9 + j];
+        for (int j = 0; j < taps; ++j) {
+            int32_t m = N[k * taps + j];
             if (m < 0) continue;
             const double *x = X + (int64_t)m * Ci;
             const double *w = Wt + (int64_t)j * Ci * Co;
@@ -164,17 +168,17 @@ void orc_fwd_rows(const double *X, const int32_t *N, const double *Wt,
     }
 }
 
-/* Gather form of the input gradient.  The 3x3 offsets mirror: token m sits
- * at offset j of token k exactly when k sits at offset 8-j of m.  So the
- * contributions that token k received in the forward map through tap j
- * come back to it through tap 8-j:
- *   dX[k][i] = sum_j sum_o dY[N[k,8-j]][o] * W[j][i][o]. */
+/* Gather form of the input gradient.  The K x K offsets mirror: token m
+ * sits at offset j of token k exactly when k sits at offset taps-1-j of m
+ * (the offset negated).  So the contributions that token k received in the
+ * forward map through tap j come back to it through tap taps-1-j:
+ *   dX[k][i] = sum_j sum_o dY[N[k,taps-1-j]][o] * W[j][i][o]. */
 static void dx_gather_one(const double *dY, const int32_t *N, const double *Wt,
-                          int64_t k, double *out, int32_t Ci, int32_t Co)
+                          int64_t k, double *out, int32_t Ci, int32_t Co, int32_t taps)
 {
     for (int32_t i = 0; i < Ci; ++i) out[i] = 0.0;
-    for (int j = 0; j < 9; ++j) {
-        int32_t m = N[k * 9 + (8 - j)];
+    for (int j = 0; j < taps; ++j) {
+        int32_t m = N[k * taps + (taps - 1 - j)];
         if (m < 0) continue;
         const double *g = dY + (int64_t)m * Co;
         const double *w = Wt + (int64_t)j * Ci * Co;
@@ -188,33 +192,33 @@ static void dx_gather_one(const double *dY, const int32_t *N, const double *Wt,
 }
 
 void orc_bwd_dx(const double *dY, const int32_t *N, const double *Wt,
-                double *dX, int64_t n, int32_t Ci, int32_t Co)
+                double *dX, int64_t n, int32_t Ci, int32_t Co, int32_t taps)
 {
 #pragma omp parallel for schedule(static)
-    for (int64_t k = 0; k < n; ++k) dx_gather_one(dY, N, Wt, k, dX + k * Ci, Ci, Co);
+    for (int64_t k = 0; k < n; ++k) dx_gather_one(dY, N, Wt, k, dX + k * Ci, Ci, Co, taps);
 }
 
 void orc_bwd_dx_rows(const double *dY, const int32_t *N, const double *Wt,
                      const int64_t *rows, int64_t nrows, double *dXr,
-                     int32_t Ci, int32_t Co)
+                     int32_t Ci, int32_t Co, int32_t taps)
 {
 #pragma omp parallel for schedule(static)
-    for (int64_t r = 0; r < nrows; ++r) dx_gather_one(dY, N, Wt, rows[r], dXr + r * Ci, Ci, Co);
+    for (int64_t r = 0; r < nrows; ++r) dx_gather_one(dY, N, Wt, rows[r], dXr + r * Ci, Ci, Co, taps);
 }
 
 /* Scatter form: the literal adjoint of the forward sum.  Every forward term
  * Y[k] += X[m] W[j] (m = N[k,j]) sends dY[k] W[j]^T back to row m.
  * Parallel over input channels so that no two threads write one element. */
 void orc_bwd_dx_scatter(const double *dY, const int32_t *N, const double *Wt,
-                        double *dX, int64_t n, int32_t Ci, int32_t Co)
+                        double *dX, int64_t n, int32_t Ci, int32_t Co, int32_t taps)
 {
 #pragma omp parallel for schedule(static)
     for (int32_t i = 0; i < Ci; ++i) {
         for (int64_t m = 0; m < n; ++m) dX[m * Ci + i] = 0.0;
         for (int64_t k = 0; k < n; ++k) {
             const double *g = dY + k * Co;
-            for (int j = 0; j < 9; ++j) {
-                int32_t m = N[k * 9 + j];
+            for (int j = 0; j < taps; ++j) {
+                int32_t m = N[k * taps + j];
                 if (m < 0) continue;
                 const double *wr = Wt + ((int64_t)j * Ci + i) * Co;
                 double s = 0.0;
@@ -227,16 +231,16 @@ void orc_bwd_dx_scatter(const double *dY, const int32_t *N, const double *Wt,
 
 /* dW[j][i][o] = sum_k [N[k,j] >= 0] X[N[k,j]][i] * dY[k][o], k ascending. */
 void orc_bwd_dw(const double *X, const int32_t *N, const double *dY,
-                double *dW, int64_t n, int32_t Ci, int32_t Co)
+                double *dW, int64_t n, int32_t Ci, int32_t Co, int32_t taps)
 {
 #pragma omp parallel for schedule(static)
-    for (int64_t ji = 0; ji < (int64_t)9 * Ci; ++ji) {
+    for (int64_t ji = 0; ji < (int64_t)taps * Ci; ++ji) {
         int j = (int)(ji / Ci);
         int32_t i = (int32_t)(ji % Ci);
         double *acc = dW + ji * Co;
         for (int32_t o = 0; o < Co; ++o) acc[o] = 0.0;
         for (int64_t k = 0; k < n; ++k) {
-            int32_t m = N[k * 9 + j];
+            int32_t m = N[k * taps + j];
             if (m < 0) continue;
             double xv = X[(int64_t)m * Ci + i];
             const double *g = dY + k * Co;
@@ -249,7 +253,7 @@ void orc_bwd_dw(const double *X, const int32_t *N, const double *dY,
  * dW[j][i][o] with ji = rows[r] = j * Ci + i. */
 void orc_bwd_dw_rows(const double *X, const int32_t *N, const double *dY,
                      const int64_t *rows, int64_t nrows, double *out,
-                     int64_t n, int32_t Ci, int32_t Co)
+                     int64_t n, int32_t Ci, int32_t Co, int32_t taps)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < nrows; ++r) {
@@ -258,7 +262,7 @@ void orc_bwd_dw_rows(const double *X, const int32_t *N, const double *dY,
         double *acc = out + r * Co;
         for (int32_t o = 0; o < Co; ++o) acc[o] = 0.0;
         for (int64_t k = 0; k < n; ++k) {
-            int32_t m = N[k * 9 + j];
+            int32_t m = N[k * taps + j];
             if (m < 0) continue;
             double xv = X[(int64_t)m * Ci + i];
             const double *g = dY + k * Co;

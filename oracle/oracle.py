@@ -55,15 +55,15 @@ class Oracle:
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.orc_threads.argtypes = [ctypes.c_int]
         lib.orc_threads.restype = ctypes.c_int
-        lib.orc_build_index.argtypes = [P, P, i32, i32, i32, i64, P, P]
+        lib.orc_build_index.argtypes = [P, P, i32, i32, i32, i64, i32, P, P]
         lib.orc_build_index.restype = ctypes.c_int
-        lib.orc_fwd.argtypes = [P, P, P, P, P, i64, i32, i32]
-        lib.orc_fwd_rows.argtypes = [P, P, P, P, P, i64, P, i32, i32]
-        lib.orc_bwd_dx.argtypes = [P, P, P, P, i64, i32, i32]
-        lib.orc_bwd_dx_rows.argtypes = [P, P, P, P, i64, P, i32, i32]
-        lib.orc_bwd_dx_scatter.argtypes = [P, P, P, P, i64, i32, i32]
-        lib.orc_bwd_dw.argtypes = [P, P, P, P, i64, i32, i32]
-        lib.orc_bwd_dw_rows.argtypes = [P, P, P, P, i64, P, i64, i32, i32]
+        lib.orc_fwd.argtypes = [P, P, P, P, P, i64, i32, i32, i32]
+        lib.orc_fwd_rows.argtypes = [P, P, P, P, P, i64, P, i32, i32, i32]
+        lib.orc_bwd_dx.argtypes = [P, P, P, P, i64, i32, i32, i32]
+        lib.orc_bwd_dx_rows.argtypes = [P, P, P, P, i64, P, i32, i32, i32]
+        lib.orc_bwd_dx_scatter.argtypes = [P, P, P, P, i64, i32, i32, i32]
+        lib.orc_bwd_dw.argtypes = [P, P, P, P, i64, i32, i32, i32]
+        lib.orc_bwd_dw_rows.argtypes = [P, P, P, P, i64, P, i64, i32, i32, i32]
         lib.orc_bwd_db.argtypes = [P, P, i64, i32]
         lib.orc_xattn_fwd.argtypes = [P, P, P, P, i64, i64, i32, ctypes.c_double]
         lib.orc_xattn_bwd.argtypes = [P, P, P, P, P, i64, i64, i32, ctypes.c_double]
@@ -78,14 +78,14 @@ class Oracle:
         """Set (want > 0) and return the OpenMP thread count the oracle uses."""
         return int(self.lib.orc_threads(int(want)))
 
-    def build_index(self, coords, frame_offsets, T, H, W, want_map=False):
-        """Returns (status, N [n,9] int32, M [T,H,W] int32 or None)."""
+    def build_index(self, coords, frame_offsets, T, H, W, want_map=False, K=3):
+        """Returns (status, N [n,K*K] int32, M [T,H,W] int32 or None)."""
         coords = _i32(coords)
         offs = _i32(frame_offsets)
         n = coords.shape[0]
-        N = np.full((n, 9), -7, dtype=np.int32)
+        N = np.full((n, K * K), -7, dtype=np.int32)
         M = np.full((T, H, W), -7, dtype=np.int32) if want_map else None
-        st = self.lib.orc_build_index(_p(coords), _p(offs), int(T), int(H), int(W), int(n),
+        st = self.lib.orc_build_index(_p(coords), _p(offs), int(T), int(H), int(W), int(n), int(K),
                                       _p(N), _p(M))
         return int(st), N, M
 
@@ -95,7 +95,7 @@ class Oracle:
         Co = Wt.shape[2]
         bb = None if b is None else _f64(b)
         Y = np.empty((n, Co), dtype=np.float64)
-        self.lib.orc_fwd(_p(X), _p(N), _p(Wt), _p(bb), _p(Y), n, Ci, Co)
+        self.lib.orc_fwd(_p(X), _p(N), _p(Wt), _p(bb), _p(Y), n, Ci, Co, _taps(N, Wt))
         return Y
 
     def fwd_rows(self, X, N, Wt, b, rows):
@@ -104,7 +104,7 @@ class Oracle:
         bb = None if b is None else _f64(b)
         out = np.empty((rows.shape[0], Co), dtype=np.float64)
         self.lib.orc_fwd_rows(_p(X), _p(N), _p(Wt), _p(bb), _p(rows), rows.shape[0], _p(out),
-                              Ci, Co)
+                              Ci, Co, _taps(N, Wt))
         return out
 
     def bwd_dx(self, dY, N, Wt):
@@ -112,14 +112,15 @@ class Oracle:
         n = dY.shape[0]
         Ci, Co = Wt.shape[1], Wt.shape[2]
         dX = np.empty((n, Ci), dtype=np.float64)
-        self.lib.orc_bwd_dx(_p(dY), _p(N), _p(Wt), _p(dX), n, Ci, Co)
+        self.lib.orc_bwd_dx(_p(dY), _p(N), _p(Wt), _p(dX), n, Ci, Co, _taps(N, Wt))
         return dX
 
     def bwd_dx_rows(self, dY, N, Wt, rows):
         dY, N, Wt, rows = _f64(dY), _i32(N), _f64(Wt), _i64(rows)
         Ci, Co = Wt.shape[1], Wt.shape[2]
         out = np.empty((rows.shape[0], Ci), dtype=np.float64)
-        self.lib.orc_bwd_dx_rows(_p(dY), _p(N), _p(Wt), _p(rows), rows.shape[0], _p(out), Ci, Co)
+        self.lib.orc_bwd_dx_rows(_p(dY), _p(N), _p(Wt), _p(rows), rows.shape[0], _p(out), Ci, Co,
+                                 _taps(N, Wt))
         return out
 
     def bwd_dx_scatter(self, dY, N, Wt):
@@ -127,15 +128,16 @@ class Oracle:
         n = dY.shape[0]
         Ci, Co = Wt.shape[1], Wt.shape[2]
         dX = np.empty((n, Ci), dtype=np.float64)
-        self.lib.orc_bwd_dx_scatter(_p(dY), _p(N), _p(Wt), _p(dX), n, Ci, Co)
+        self.lib.orc_bwd_dx_scatter(_p(dY), _p(N), _p(Wt), _p(dX), n, Ci, Co, _taps(N, Wt))
         return dX
 
     def bwd_dw(self, X, N, dY):
         X, N, dY = _f64(X), _i32(N), _f64(dY)
         n, Ci = X.shape
         Co = dY.shape[1]
-        dW = np.empty((9, Ci, Co), dtype=np.float64)
-        self.lib.orc_bwd_dw(_p(X), _p(N), _p(dY), _p(dW), n, Ci, Co)
+        taps = N.shape[1]
+        dW = np.empty((taps, Ci, Co), dtype=np.float64)
+        self.lib.orc_bwd_dw(_p(X), _p(N), _p(dY), _p(dW), n, Ci, Co, taps)
         return dW
 
     def bwd_dw_rows(self, X, N, dY, rows):
@@ -145,7 +147,7 @@ class Oracle:
         Co = dY.shape[1]
         out = np.empty((rows.shape[0], Co), dtype=np.float64)
         self.lib.orc_bwd_dw_rows(_p(X), _p(N), _p(dY), _p(rows), rows.shape[0], _p(out), n, Ci,
-                                 Co)
+                                 Co, N.shape[1])
         return out
 
     def bwd_db(self, dY):
@@ -181,6 +183,13 @@ class Oracle:
         return dQ, dX[:n]
 
 
+def _taps(N, Wt):
+    """Number of taps of a call: the columns of N, which must match the
+    weights' first dimension."""
+    assert N.ndim == 2 and Wt.shape[0] == N.shape[1], (N.shape, Wt.shape)
+    return int(N.shape[1])
+
+
 def _f64(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
@@ -214,8 +223,8 @@ def threads(want: int = 0) -> int:
     return default().threads(want)
 
 
-def build_index(coords, frame_offsets, T, H, W, want_map=False):
-    return default().build_index(coords, frame_offsets, T, H, W, want_map)
+def build_index(coords, frame_offsets, T, H, W, want_map=False, K=3):
+    return default().build_index(coords, frame_offsets, T, H, W, want_map, K)
 
 
 def fwd(X, N, Wt, b=None):

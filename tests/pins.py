@@ -31,19 +31,20 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 # ----------------------------------------------------------------- references
-def brute_index(coords, offs, T, H, W):
+def brute_index(coords, offs, T, H, W, K=3):
     """N by direct search: the token of the same frame whose (y, x) equals
-    (y_k + dy, x_k + dx); -1 if there is none.  Tap j = 3*(dy+1) + (dx+1)."""
-    n = len(coords)
-    N = np.full((n, 9), -1, dtype=np.int64)
+    (y_k + dy, x_k + dx); -1 if there is none.  Tap j = K*(dy+r) + (dx+r)
+    with r = K // 2 (K = 3: j = 3*(dy+1) + (dx+1))."""
+    n, r = len(coords), K // 2
+    N = np.full((n, K * K), -1, dtype=np.int64)
     for t in range(T):
         beg, end = int(offs[t]), int(offs[t + 1])
         yx = [divmod(int(coords[m]), W) for m in range(beg, end)]
         for k in range(beg, end):
             y, x = yx[k - beg]
-            for dy in (-1, 0, 1):
-                for dx in (-1, 0, 1):
-                    j = 3 * (dy + 1) + (dx + 1)
+            for dy in range(-r, r + 1):
+                for dx in range(-r, r + 1):
+                    j = K * (dy + r) + (dx + r)
                     for m in range(beg, end):
                         if yx[m - beg] == (y + dy, x + dx):
                             N[k, j] = m
@@ -51,11 +52,12 @@ def brute_index(coords, offs, T, H, W):
 
 
 def torch_weight(Wt):
-    """[9, Ci, Co] taps -> torch conv2d weight [Co, Ci, 3, 3] with
-    weight[o, i, dy+1, dx+1] = Wt[3*(dy+1) + (dx+1)][i][o]."""
+    """[K*K, Ci, Co] taps -> torch conv2d weight [Co, Ci, K, K] with
+    weight[o, i, dy+r, dx+r] = Wt[K*(dy+r) + (dx+r)][i][o]."""
     Wt = torch.as_tensor(np.asarray(Wt, dtype=np.float64))
+    K = int(round(Wt.shape[0] ** 0.5))
     Ci, Co = Wt.shape[1], Wt.shape[2]
-    return Wt.reshape(3, 3, Ci, Co).permute(3, 2, 0, 1).contiguous()
+    return Wt.reshape(K, K, Ci, Co).permute(3, 2, 0, 1).contiguous()
 
 
 def frame_of(offs):
@@ -64,8 +66,9 @@ def frame_of(offs):
 
 def dense_recon(X, coords, offs, T, H, W, Wt, b, dY=None):
     """Scatter the kept tokens into a zero T x C x H x W grid, run a
-    zero-padded 3x3 conv2d (cross-correlation), gather the kept positions,
-    add b.  With dY, also returns autograd's dX, dW [9,Ci,Co], db."""
+    zero-padded K x K conv2d (cross-correlation, K*K = taps of Wt), gather
+    the kept positions, add b.  With dY, also returns autograd's dX,
+    dW [K*K,Ci,Co], db."""
     X = torch.tensor(np.asarray(X, dtype=np.float64), requires_grad=dY is not None)
     w = torch_weight(Wt).requires_grad_(dY is not None)
     bb = torch.tensor(np.asarray(b, dtype=np.float64), requires_grad=dY is not None)
@@ -74,12 +77,12 @@ def dense_recon(X, coords, offs, T, H, W, Wt, b, dY=None):
     p = torch.as_tensor(np.asarray(coords, dtype=np.int64))
     grid = torch.zeros(T, H * W, Ci, dtype=torch.float64)
     grid = grid.index_put((f, p), X)
-    out = F.conv2d(grid.reshape(T, H, W, Ci).permute(0, 3, 1, 2), w, padding=1)
+    out = F.conv2d(grid.reshape(T, H, W, Ci).permute(0, 3, 1, 2), w, padding=w.shape[2] // 2)
     Y = out.permute(0, 2, 3, 1).reshape(T, H * W, Co)[f, p] + bb
     if dY is None:
         return Y.detach().numpy()
     (Y * torch.as_tensor(np.asarray(dY, dtype=np.float64))).sum().backward()
-    dW = w.grad.permute(2, 3, 1, 0).reshape(9, Ci, Co)
+    dW = w.grad.permute(2, 3, 1, 0).reshape(-1, Ci, Co)
     return Y.detach().numpy(), X.grad.numpy(), dW.numpy(), bb.grad.numpy()
 
 
@@ -424,6 +427,49 @@ def pin_xattn_permutation_and_extremes(orc):
     assert np.array_equal(dQ, np.zeros((3, 8))) and dX.shape == (0, 8)
 
 
+# ------------------------------------------------------------ K x K kernels
+# The Background states the idea for K x K neighbourhoods; the page's tables
+# and kernels are 3 x 3.  The same definitions with K = 1, 5, 7.
+
+
+def pin_kxk_index_and_dense(orc):
+    """For K = 1, 5, 7: N by brute force; keep ratio 1 against an ordinary
+    zero-padded K x K conv2d; pruned cases against the dense reconstruction
+    (forward) and torch autograd through it (dX in both forms, dW, db)."""
+    for K in (1, 5, 7):
+        r = K // 2
+        for c in (CASES[1], CASES[3], CASES[5]):
+            L = case_layer(c)
+            st, N, _ = orc.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K=K)
+            assert st == 0 and N.shape == (L.n, K * K)
+            assert np.array_equal(N, brute_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K)), (K, c)
+            rng = np.random.default_rng(100 + K)
+            Wt = rng.standard_normal((K * K, L.X.shape[1], L.dY.shape[1]))
+            Y, dX, dW, db = dense_recon(L.X, L.coords, L.frame_offsets, L.T, L.H, L.W, Wt, L.b, dY=L.dY)
+            close(orc.fwd(L.X, N, Wt, L.b), Y, 1e-12, f"K={K} fwd {c}")
+            close(orc.bwd_dx(L.dY, N, Wt), dX, 1e-12, f"K={K} dX gather {c}")
+            close(orc.bwd_dx_scatter(L.dY, N, Wt), dX, 1e-12, f"K={K} dX scatter {c}")
+            close(orc.bwd_dw(L.X, N, L.dY), dW, 1e-12, f"K={K} dW {c}")
+        T, H, W, Ci, Co = 2, 6, 7, 3, 2
+        coords = np.tile(np.arange(H * W, dtype=np.int32), T)
+        offs = np.arange(T + 1, dtype=np.int32) * H * W
+        st, N, _ = orc.build_index(coords, offs, T, H, W, K=K)
+        for k in range(T * H * W):
+            y, x = divmod(k % (H * W), W)
+            for j in range(K * K):
+                dy, dx = j // K - r, j % K - r
+                inside = 0 <= y + dy < H and 0 <= x + dx < W
+                assert N[k, j] == (k + dy * W + dx if inside else -1), (K, k, j)
+        rng = np.random.default_rng(7 + K)
+        X, Wt, b = rng.standard_normal((T * H * W, Ci)), rng.standard_normal((K * K, Ci, Co)), rng.standard_normal(Co)
+        img = torch.tensor(X).reshape(T, H, W, Ci).permute(0, 3, 1, 2)
+        ref = F.conv2d(img, torch_weight(Wt), bias=torch.tensor(b), padding=r)
+        close(orc.fwd(X, N, Wt, b), ref.permute(0, 2, 3, 1).reshape(T * H * W, Co).numpy(), 1e-12,
+              f"K={K} keep=1 vs conv2d")
+    st, _, _ = orc.build_index(np.zeros(1, np.int32), np.array([0, 1], np.int32), 1, 1, 1, K=4)
+    assert st != 0, "even K must be rejected"
+
+
 ALL_PINS = [
     pin_golden_hand_3x4,
     pin_golden_frames_2x2,
@@ -436,6 +482,7 @@ ALL_PINS = [
     pin_special_cases,
     pin_finite_differences,
     pin_row_subsets,
+    pin_kxk_index_and_dense,
     pin_xattn_single_key,
     pin_xattn_two_keys,
     pin_xattn_zero_queries,

@@ -18,30 +18,32 @@ MUTANTS = [
      "if (yy >= 0 && yy < H && xx >= 0 && xx < W) v = map[yy * W + xx];",
      "{ int32_t q = yy * W + xx; if (q >= 0 && q < H * W) v = map[q]; }", 0),
     ("tap order transposed (dx-major)",
-     "int32_t yy = y + (j / 3 - 1), xx = x + (j % 3 - 1);",
-     "int32_t yy = y + (j % 3 - 1), xx = x + (j / 3 - 1);", 0),
+     "int32_t yy = y + (j / K - r), xx = x + (j % K - r);",
+     "int32_t yy = y + (j % K - r), xx = x + (j / K - r);", 0),
     ("map not reset between frames",
      "for (int64_t c = 0; c < cells; ++c) map[c] = -1;",
      "if (t == 0) for (int64_t c = 0; c < cells; ++c) map[c] = -1;", 0),
     ("duplicate coordinate not detected",
      "if (map[p] != -1) { status = ORC_DUPLICATE; break; }", "", 0),
     ("forward drops the centre tap",
-     "int32_t m = N[k * 9 + j];\n            if (m < 0) continue;\n            const double *x",
-     "int32_t m = N[k * 9 + j];\n            if (m < 0 || j == 4) continue;\n            const double *x", 0),
+     "int32_t m = N[k * taps + j];\n            if (m < 0) continue;\n            const double *x",
+     "int32_t m = N[k * taps + j];\n            if (m < 0 || j == taps / 2) continue;\n            const double *x", 0),
     ("forward flips the kernel (true convolution)",
      "const double *w = Wt + (int64_t)j * Ci * Co;",
-     "const double *w = Wt + (int64_t)(8 - j) * Ci * Co;", 0),
+     "const double *w = Wt + (int64_t)(taps - 1 - j) * Ci * Co;", 0),
     ("forward reads the own row instead of the neighbour",
      "const double *x = X + (int64_t)m * Ci;", "const double *x = X + k * Ci;", 0),
     ("forward drops the bias",
      "if (b)\n            for (int32_t o = 0; o < Co; ++o) acc[o] += b[o];", "", 0),
     ("dX gather without the mirrored tap",
-     "int32_t m = N[k * 9 + (8 - j)];", "int32_t m = N[k * 9 + j];", 0),
+     "int32_t m = N[k * taps + (taps - 1 - j)];", "int32_t m = N[k * taps + j];", 0),
     ("dX scatter with the wrong sign",
      "dX[(int64_t)m * Ci + i] += s;", "dX[(int64_t)m * Ci + i] -= s;", 0),
     ("dW with operands swapped between gathered and own row",
      "double xv = X[(int64_t)m * Ci + i];\n            const double *g = dY + k * Co;",
      "double xv = X[k * Ci + i];\n            const double *g = dY + (int64_t)m * Co;", 0),
+    ("K x K offsets not centred (radius taken as K - 1 over 2 rounded up)",
+     "const int taps = K * K, r = K / 2;", "const int taps = K * K, r = (K + 1) / 2;", 0),
     ("db drops the last token",
      "for (int64_t k = 0; k < n; ++k)\n        for (int32_t o = 0; o < Co; ++o) db[o]",
      "for (int64_t k = 0; k + 1 < n; ++k)\n        for (int32_t o = 0; o < Co; ++o) db[o]", 0),
