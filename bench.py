@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4", "c4-host", "xattn"])
     p.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
+    p.add_argument("--ksize", type=int, default=3, choices=[1, 3, 5, 7],
+                   help="single-layer workloads: K of a K x K neighbourhood (weights of the same "
+                        "distribution, std 1/sqrt(K*K*C))")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--dw-stream", choices=["side", "same"], default="side",
                    help="run each layer's weight gradient on a second stream, concurrent with its "
@@ -52,7 +55,10 @@ def parse():
                    help="frames of the workload the CPU oracle is timed on")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one plain device copy of this size (HBM counter calibration)")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.ksize != 3 and a.workload not in ("c2", "c3a", "c3b", "c4"):
+        p.error("--ksize applies to the single-layer workloads c2, c3a, c3b and c4")
+    return a
 
 
 # ---------------------------------------------------------------- workloads
@@ -272,6 +278,7 @@ def traffic_record(kernel_name, kernel_files):
 def layer_workload(args):
     """Single-layer workloads (c2, c3a, c3b, c4), for the design notes'
     per-configuration table; prints one JSON line of its own."""
+    import numpy as np
     import torch
     from sparse_convolution_pruned_amd import ops, workloads as wl
 
@@ -280,37 +287,53 @@ def layer_workload(args):
     bf = torch.bfloat16
     dev = lambda a, d=None: (torch.from_numpy(a).to(d) if d is not None else torch.from_numpy(a)).cuda()
     coords, offs = dev(L.coords), dev(L.frame_offsets)
-    X, Wt, b, dY = dev(L.X, bf), dev(L.Wt, bf), dev(L.b, bf), dev(L.dY, bf)
+    K = args.ksize
+    taps = K * K
     n, C = L.n, L.X.shape[1]
-    N = torch.empty((n, 9), dtype=torch.int32, device="cuda")
+    Wk = L.Wt
+    if K != 3:
+        rng = np.random.default_rng(900 + K)
+        Wk = wl.round_bf16(rng.standard_normal((taps, C, C)).astype(np.float32) / np.sqrt(taps * C))
+    X, Wt, b, dY = dev(L.X, bf), dev(Wk, bf), dev(L.b, bf), dev(L.dY, bf)
+    N = torch.empty((n, taps), dtype=torch.int32, device="cuda")
     Y = torch.empty((n, C), dtype=bf, device="cuda")
     dX = torch.empty((n, C), dtype=bf, device="cuda")
-    dW = torch.empty((9, C, C), dtype=torch.float32, device="cuda")
+    dW = torch.empty((taps, C, C), dtype=torch.float32, device="cuda")
     db = torch.empty((C,), dtype=torch.float32, device="cuda")
     passes = cfg["passes"]
     chunked = "chunk_frames" in cfg
     if chunked:
         desc = ops.make_chunked_desc(L.T, L.H, L.W, coords, offs, torch.from_numpy(L.frame_offsets.copy()),
                                      C, C, bf, cfg["chunk_frames"], X=X, Wt=Wt, bias=b, Y=Y, dY=dY,
-                                     dX=dX, dW=dW, db=db, kernel=args.kernel)
+                                     dX=dX, dW=dW, db=db, kernel=args.kernel, ksize=K)
         pm = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
         ws = torch.empty(max(256, ops.sv_chunked_workspace_bytes(desc, pm)), dtype=torch.uint8, device="cuda")
 
         def step():
             ops.sv_sparseconv2d_chunked(desc, pm, ws)
     else:
-        ws = torch.empty(max(256, ops.sv_workspace_bytes(ops.SV_OP_DW, n, C, C, bf)), dtype=torch.uint8,
+        ws = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_DW, n, K, C, C, bf)), dtype=torch.uint8,
                          device="cuda")
-        fws = torch.empty(max(256, ops.sv_workspace_bytes(ops.SV_OP_FWD, n, C, C, bf)), dtype=torch.uint8,
+        fws = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_FWD, n, K, C, C, bf)), dtype=torch.uint8,
                           device="cuda")
+        if K == 3:
+            run = {"index": lambda: ops.sv_build_index(coords, offs, L.T, L.H, L.W, N),
+                   "fwd": lambda: ops.sv_sparseconv2d_fwd(X, N, Wt, b, Y, args.kernel, workspace=fws),
+                   "dx": lambda: ops.sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, args.kernel),
+                   "dw": lambda: ops.sv_sparseconv2d_bwd_dw(X, N, dY, dW, db, False, ws)}
+        else:
+            run = {"index": lambda: ops.sv_build_index_k(coords, offs, L.T, L.H, L.W, K, N),
+                   "fwd": lambda: ops.sv_sparseconv2d_fwd_k(X, N, Wt, b, Y, args.kernel, workspace=fws),
+                   "dx": lambda: ops.sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, args.kernel),
+                   "dw": lambda: ops.sv_sparseconv2d_bwd_dw_k(X, N, dY, dW, db, False, ws)}
 
         def step():
-            ops.sv_build_index(coords, offs, L.T, L.H, L.W, N)
-            ops.sv_sparseconv2d_fwd(X, N, Wt, b, Y, args.kernel, workspace=fws)
+            run["index"]()
+            run["fwd"]()
             if "dx" in passes:
-                ops.sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, args.kernel)
+                run["dx"]()
             if "dw" in passes:
-                ops.sv_sparseconv2d_bwd_dw(X, N, dY, dW, db, False, ws)
+                run["dw"]()
     for _ in range(args.warmup):
         step()
     torch.cuda.reset_peak_memory_stats()
@@ -320,9 +343,20 @@ def layer_workload(args):
         step()
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / args.steps
-    fl = len(passes) * 2 * n * 9 * C * C
-    print(json.dumps({"workload": args.workload, "name": cfg["name"], "kernel": args.kernel, "n": n,
-                      "ms_per_step": round(sec * 1e3, 4), "tflops": round(fl / sec / 1e12, 3),
+    # each pass alone (device time of `steps` back-to-back calls)
+    pass_ms = {}
+    if not chunked:
+        for name in ["index", "fwd"] + [p for p in ("dx", "dw") if p in passes]:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                run[name]()
+            e1.record()
+            torch.cuda.synchronize()
+            pass_ms[name] = round(e0.elapsed_time(e1) / args.steps, 4)
+    fl = len(passes) * 2 * n * taps * C * C
+    print(json.dumps({"workload": args.workload, "name": cfg["name"], "kernel": args.kernel, "ksize": K, "n": n,
+                      "ms_per_step": round(sec * 1e3, 4), "pass_ms": pass_ms, "tflops": round(fl / sec / 1e12, 3),
                       "frac_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "peak_mem_mb": round(torch.cuda.max_memory_allocated() / 2 ** 20, 1),
                       "workspace_mb": round(ws.numel() / 2 ** 20, 2)}), flush=True)

@@ -144,6 +144,42 @@ sv_status sv_sparseconv2d_bwd_dw(const void *X, const int32_t *N, const void *dY
  * partials).  Depends only on its arguments, never on the device. */
 size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype);
 
+/* K x K neighbourhoods.  The five calls above for any odd K in {1, 3, 5, 7}
+ * (they are these with K = 3).  With taps = K*K and r = K/2:
+ *   tap j = K*(dy + r) + (dx + r), dy, dx in [-r, r]; centre tap taps/2;
+ *   tap taps-1-j is the mirror (-dy, -dx) of tap j, so the input gradient
+ *   reads Wt[taps-1-j] where the 3 x 3 case reads Wt[8-j];
+ *   N [n][taps], Wt and dW [taps][C_in][C_out]
+ *   (Wt[j][i][o] = torch weight[o][i][j/K][j%K]).
+ * The page ("SV-TAD: Native Sparse Convolutions for Efficient Temporal
+ * Action Detection", Key Design 2) builds the 3 x 3 convolution of its
+ * adapter; K = 1 is the pointwise projection around it (N[k][0] = k) and
+ * 5 and 7 widen the receptive field with the same index table and
+ * kernels.  Both kernel families serve every K listed; the MFMA conditions
+ * of sv_kernel are unchanged.  n * taps must stay below 2^31.
+ * Returns SV_ERR_INVALID_ARG for an even or non-positive K and
+ * SV_ERR_UNSUPPORTED for an odd K above 7 (sv_workspace_bytes_k: 0), then
+ * behaves exactly as the 3 x 3 call of the same name. */
+sv_status sv_build_index_k(const int32_t *coords, const int32_t *frame_offsets,
+                           int32_t T, int32_t H, int32_t W, int32_t K, int64_t n,
+                           int32_t *N_out, int32_t *M_out, int32_t *err_flag,
+                           hipStream_t stream);
+sv_status sv_sparseconv2d_fwd_k(const void *X, const int32_t *N, const void *Wt,
+                                const void *bias, void *Y, int64_t n, int32_t K,
+                                int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                sv_kernel kernel, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+sv_status sv_sparseconv2d_bwd_dx_k(const void *dY, const int32_t *N, const void *Wt,
+                                   void *dX, int64_t n, int32_t K, int32_t C_in, int32_t C_out,
+                                   sv_dtype dtype, sv_kernel kernel, hipStream_t stream);
+sv_status sv_sparseconv2d_bwd_dw_k(const void *X, const int32_t *N, const void *dY,
+                                   float *dW, float *db, int64_t n, int32_t K, int32_t C_in,
+                                   int32_t C_out, sv_dtype dtype, int32_t accumulate,
+                                   void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_t C_out,
+                            sv_dtype dtype);
+
 /* Chunked execution over whole frames (Key Design 2's chunking): the frames
  * are processed chunk_frames at a time; for each chunk the index table is
  * built with chunk-local indices into the workspace, then the requested
@@ -169,6 +205,8 @@ typedef struct sv_chunked_desc {
     float *dW;                          /* device [9][C_in][C_out] fp32 (DW), overwritten */
     float *db;                          /* device [C_out] fp32, nullable (DW), overwritten */
     int32_t *err_flag;                  /* device int32, nullable                */
+    int32_t ksize;                      /* K of a K x K neighbourhood (the _k calls);
+                                           0 selects 3.  N, Wt, dW then hold K*K taps */
 } sv_chunked_desc;
 
 sv_status sv_sparseconv2d_chunked(const sv_chunked_desc *desc, uint32_t passes,
@@ -177,7 +215,9 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc *desc, uint32_t passes,
 
 /* Workspace bytes sv_sparseconv2d_chunked needs for this descriptor (reads
  * only the host fields: T, H, W, C_in, C_out, dtype, chunk_frames,
- * frame_offsets_host).  Returns 0 and nothing else on bad descriptors. */
+ * frame_offsets_host, ksize).  Returns 0 and nothing else on bad
+ * descriptors.  sv_sparseconv2d_chunked returns SV_ERR_UNSUPPORTED for an
+ * odd ksize above 7 and SV_ERR_INVALID_ARG for other bad ones. */
 size_t sv_chunked_workspace_bytes(const sv_chunked_desc *desc, uint32_t passes);
 
 /* Host-streamed chunked execution: the chunk driver above with the
@@ -224,6 +264,7 @@ typedef struct sv_chunked_host_desc {
     float *dW;                          /* device [9][C_in][C_out] fp32 (DW), overwritten */
     float *db;                          /* device [C_out] fp32, nullable (DW), overwritten */
     int32_t *err_flag;                  /* device int32, nullable                */
+    int32_t ksize;                      /* as in sv_chunked_desc: 0 selects 3    */
 } sv_chunked_host_desc;
 
 sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc *desc, uint32_t passes,

@@ -12,7 +12,20 @@ using namespace svc;
 namespace {
 
 constexpr int kMaxCells = 16384;
-constexpr int64_t kMaxRows = std::numeric_limits<int32_t>::max() / 9;
+constexpr int kMaxK = 7;
+
+// Rows of N: n * taps int32 entries must stay addressable with 32-bit
+// element indices.
+int64_t max_rows(int taps) { return std::numeric_limits<int32_t>::max() / taps; }
+
+// taps = K * K for a supported odd K; SV_ERR_INVALID_ARG for an even or
+// non-positive K, SV_ERR_UNSUPPORTED for odd K > kMaxK.
+sv_status taps_of(int32_t K, int* taps) {
+    if (K < 1 || K % 2 == 0) return SV_ERR_INVALID_ARG;
+    if (K > kMaxK) return SV_ERR_UNSUPPORTED;
+    *taps = K * K;
+    return SV_OK;
+}
 
 bool valid_dtype(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
 bool valid_kernel(sv_kernel k) { return k == SV_KERNEL_AUTO || k == SV_KERNEL_VALU || k == SV_KERNEL_MFMA; }
@@ -21,15 +34,15 @@ size_t align_up(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 // Which conv kernel runs a pass; SV_ERR_UNSUPPORTED when MFMA is forced and
 // does not fit.
-sv_status choose(sv_kernel req, sv_dtype dt, bool dx, int Ci, int Co, int64_t n, bool* use_mfma) {
-    const bool fits = dt == SV_BF16 && conv_mfma_supported(dx, Ci, Co, n);
+sv_status choose(sv_kernel req, sv_dtype dt, bool dx, int Ci, int Co, int64_t n, int taps, bool* use_mfma) {
+    const bool fits = dt == SV_BF16 && conv_mfma_supported(dx, Ci, Co, n, taps);
     if (req == SV_KERNEL_MFMA && !fits) return SV_ERR_UNSUPPORTED;
     *use_mfma = (req == SV_KERNEL_MFMA) || (req == SV_KERNEL_AUTO && fits);
     return SV_OK;
 }
 
-sv_status conv_args_ok(int64_t n, int32_t Ci, int32_t Co, sv_dtype dt, sv_kernel k) {
-    if (n < 0 || n > kMaxRows || Ci <= 0 || Co <= 0) return SV_ERR_INVALID_ARG;
+sv_status conv_args_ok(int64_t n, int taps, int32_t Ci, int32_t Co, sv_dtype dt, sv_kernel k) {
+    if (n < 0 || n > max_rows(taps) || Ci <= 0 || Co <= 0) return SV_ERR_INVALID_ARG;
     if (!valid_dtype(dt) || !valid_kernel(k)) return SV_ERR_INVALID_ARG;
     return SV_OK;
 }
@@ -37,95 +50,130 @@ sv_status conv_args_ok(int64_t n, int32_t Ci, int32_t Co, sv_dtype dt, sv_kernel
 // Forward with the repacked weights already in `V` (MFMA path) or straight
 // from Wt (VALU path).
 sv_status run_fwd_prepared(bool mfma, const void* X, const int32_t* N, const void* Wt, const void* V,
-                           const void* bias, void* Y, int64_t n, int32_t Ci, int32_t Co, sv_dtype dt,
-                           hipStream_t s) {
+                           const void* bias, void* Y, int64_t n, int32_t Ci, int32_t Co, int taps,
+                           sv_dtype dt, hipStream_t s) {
     if (n == 0) return SV_OK;
     if (mfma)
         return hip_status(launch_conv_mfma_packed(static_cast<const uint16_t*>(X), N,
                                                   static_cast<const uint16_t*>(V),
                                                   static_cast<const uint16_t*>(bias),
-                                                  static_cast<uint16_t*>(Y), n, Ci, Co, s));
-    return hip_status(launch_conv_valu(dt == SV_BF16, false, X, N, Wt, bias, Y, n, Ci, Co, s));
+                                                  static_cast<uint16_t*>(Y), n, Ci, Co, taps, s));
+    return hip_status(launch_conv_valu(dt == SV_BF16, false, X, N, Wt, bias, Y, n, Ci, Co, taps, s));
 }
 
 sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int64_t n, int32_t Ci,
-                 int32_t Co, sv_dtype dt, sv_kernel kernel, hipStream_t s) {
+                 int32_t Co, int taps, sv_dtype dt, sv_kernel kernel, hipStream_t s) {
     bool mfma = false;
-    sv_status st = choose(kernel, dt, true, Ci, Co, n, &mfma);
+    sv_status st = choose(kernel, dt, true, Ci, Co, n, taps, &mfma);
     if (st != SV_OK) return st;
     if (n == 0) return SV_OK;
     if (mfma)
         return hip_status(launch_conv_mfma_packed(static_cast<const uint16_t*>(dY), N,
                                                   static_cast<const uint16_t*>(Wt), nullptr,
-                                                  static_cast<uint16_t*>(dX), n, Co, Ci, s));
-    return hip_status(launch_conv_valu(dt == SV_BF16, true, dY, N, Wt, nullptr, dX, n, Ci, Co, s));
+                                                  static_cast<uint16_t*>(dX), n, Co, Ci, taps, s));
+    return hip_status(launch_conv_valu(dt == SV_BF16, true, dY, N, Wt, nullptr, dX, n, Ci, Co, taps, s));
 }
 
 // Bytes of repacked weights the forward needs when the MFMA kernel may run.
-size_t fwd_ws_bytes(int32_t Ci, int32_t Co, sv_dtype dt, int64_t n) {
-    return (dt == SV_BF16 && conv_mfma_supported(false, Ci, Co, n)) ? conv_mfma_fwd_workspace(Ci, Co) : 0;
+size_t fwd_ws_bytes(int32_t Ci, int32_t Co, sv_dtype dt, int64_t n, int taps) {
+    return (dt == SV_BF16 && conv_mfma_supported(false, Ci, Co, n, taps)) ? conv_mfma_fwd_workspace(Ci, Co, taps)
+                                                                           : 0;
 }
 
 }  // namespace
 
 extern "C" {
 
-sv_status sv_build_index(const int32_t* coords, const int32_t* frame_offsets, int32_t T, int32_t H,
-                         int32_t W, int64_t n, int32_t* N_out, int32_t* M_out, int32_t* err_flag,
-                         hipStream_t stream) {
-    if (T < 0 || H <= 0 || W <= 0 || n < 0 || n > kMaxRows) return SV_ERR_INVALID_ARG;
+sv_status sv_build_index_k(const int32_t* coords, const int32_t* frame_offsets, int32_t T, int32_t H,
+                           int32_t W, int32_t K, int64_t n, int32_t* N_out, int32_t* M_out, int32_t* err_flag,
+                           hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
+    if (st != SV_OK) return st;
+    if (T < 0 || H <= 0 || W <= 0 || n < 0 || n > max_rows(taps)) return SV_ERR_INVALID_ARG;
     if (!frame_offsets || (n > 0 && (!coords || !N_out))) return SV_ERR_INVALID_ARG;
     if (static_cast<int64_t>(H) * W > kMaxCells) return SV_ERR_UNSUPPORTED;
     if (T == 0) return SV_OK;
-    return hip_status(launch_build_index(coords, frame_offsets, 0, T, H, W, n, 0, N_out, M_out,
+    return hip_status(launch_build_index(coords, frame_offsets, 0, T, H, W, K, n, 0, N_out, M_out,
                                          err_flag, stream));
+}
+
+sv_status sv_build_index(const int32_t* coords, const int32_t* frame_offsets, int32_t T, int32_t H,
+                         int32_t W, int64_t n, int32_t* N_out, int32_t* M_out, int32_t* err_flag,
+                         hipStream_t stream) {
+    return sv_build_index_k(coords, frame_offsets, T, H, W, 3, n, N_out, M_out, err_flag, stream);
+}
+
+sv_status sv_sparseconv2d_fwd_k(const void* X, const int32_t* N, const void* Wt, const void* bias, void* Y,
+                                int64_t n, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                sv_kernel kernel, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
+    if (st != SV_OK) return st;
+    if ((st = conv_args_ok(n, taps, C_in, C_out, dtype, kernel)) != SV_OK) return st;
+    if (!Wt || (n > 0 && (!X || !N || !Y))) return SV_ERR_INVALID_ARG;
+    bool mfma = false;
+    if ((st = choose(kernel, dtype, false, C_in, C_out, n, taps, &mfma)) != SV_OK) return st;
+    if (mfma) {
+        const size_t need = conv_mfma_fwd_workspace(C_in, C_out, taps);
+        if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return SV_ERR_INVALID_ARG;
+        if (n == 0) return SV_OK;
+        st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(workspace),
+                                          C_in, C_out, taps, stream));
+        if (st != SV_OK) return st;
+    }
+    return run_fwd_prepared(mfma, X, N, Wt, workspace, bias, Y, n, C_in, C_out, taps, dtype, stream);
 }
 
 sv_status sv_sparseconv2d_fwd(const void* X, const int32_t* N, const void* Wt, const void* bias,
                               void* Y, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
                               sv_kernel kernel, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-    sv_status st = conv_args_ok(n, C_in, C_out, dtype, kernel);
+    return sv_sparseconv2d_fwd_k(X, N, Wt, bias, Y, n, 3, C_in, C_out, dtype, kernel, workspace,
+                                 workspace_bytes, stream);
+}
+
+sv_status sv_sparseconv2d_bwd_dx_k(const void* dY, const int32_t* N, const void* Wt, void* dX, int64_t n,
+                                   int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype, sv_kernel kernel,
+                                   hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
     if (st != SV_OK) return st;
-    if (!Wt || (n > 0 && (!X || !N || !Y))) return SV_ERR_INVALID_ARG;
-    bool mfma = false;
-    if ((st = choose(kernel, dtype, false, C_in, C_out, n, &mfma)) != SV_OK) return st;
-    if (mfma) {
-        const size_t need = conv_mfma_fwd_workspace(C_in, C_out);
-        if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
-        if (reinterpret_cast<uintptr_t>(workspace) % 16) return SV_ERR_INVALID_ARG;
-        if (n == 0) return SV_OK;
-        st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(workspace),
-                                          C_in, C_out, stream));
-        if (st != SV_OK) return st;
-    }
-    return run_fwd_prepared(mfma, X, N, Wt, workspace, bias, Y, n, C_in, C_out, dtype, stream);
+    if ((st = conv_args_ok(n, taps, C_in, C_out, dtype, kernel)) != SV_OK) return st;
+    if (!Wt || (n > 0 && (!dY || !N || !dX))) return SV_ERR_INVALID_ARG;
+    return run_dx(dY, N, Wt, dX, n, C_in, C_out, taps, dtype, kernel, stream);
 }
 
 sv_status sv_sparseconv2d_bwd_dx(const void* dY, const int32_t* N, const void* Wt, void* dX,
                                  int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
                                  sv_kernel kernel, hipStream_t stream) {
-    sv_status st = conv_args_ok(n, C_in, C_out, dtype, kernel);
-    if (st != SV_OK) return st;
-    if (!Wt || (n > 0 && (!dY || !N || !dX))) return SV_ERR_INVALID_ARG;
-    return run_dx(dY, N, Wt, dX, n, C_in, C_out, dtype, kernel, stream);
+    return sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, n, 3, C_in, C_out, dtype, kernel, stream);
+}
+
+size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype) {
+    int taps = 0;
+    if (taps_of(K, &taps) != SV_OK) return 0;
+    if (n < 0 || C_in <= 0 || C_out <= 0 || !valid_dtype(dtype)) return 0;
+    if (op == SV_OP_FWD) return fwd_ws_bytes(C_in, C_out, dtype, n, taps);
+    if (op != SV_OP_DW) return 0;
+    return dw_workspace_bytes(plan_dw(n, C_in, C_out, dtype == SV_BF16, taps));
 }
 
 size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype) {
-    if (n < 0 || C_in <= 0 || C_out <= 0 || !valid_dtype(dtype)) return 0;
-    if (op == SV_OP_FWD) return fwd_ws_bytes(C_in, C_out, dtype, n);
-    if (op != SV_OP_DW) return 0;
-    return dw_workspace_bytes(plan_dw(n, C_in, C_out, dtype == SV_BF16));
+    return sv_workspace_bytes_k(op, n, 3, C_in, C_out, dtype);
 }
 
-sv_status sv_sparseconv2d_bwd_dw(const void* X, const int32_t* N, const void* dY, float* dW, float* db,
-                                 int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
-                                 int32_t accumulate, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream) {
-    sv_status st = conv_args_ok(n, C_in, C_out, dtype, SV_KERNEL_AUTO);
+sv_status sv_sparseconv2d_bwd_dw_k(const void* X, const int32_t* N, const void* dY, float* dW, float* db,
+                                   int64_t n, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                   int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
     if (st != SV_OK) return st;
+    if ((st = conv_args_ok(n, taps, C_in, C_out, dtype, SV_KERNEL_AUTO)) != SV_OK) return st;
     if (!dW || (n > 0 && (!X || !N || !dY))) return SV_ERR_INVALID_ARG;
-    const DwPlan plan = plan_dw(n, C_in, C_out, dtype == SV_BF16);
+    const DwPlan plan = plan_dw(n, C_in, C_out, dtype == SV_BF16, taps);
     const size_t need = dw_workspace_bytes(plan);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SV_ERR_WORKSPACE;
     if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16) return SV_ERR_INVALID_ARG;
@@ -133,10 +181,19 @@ sv_status sv_sparseconv2d_bwd_dw(const void* X, const int32_t* N, const void* dY
                                 accumulate ? 1 : 0, workspace, stream));
 }
 
+sv_status sv_sparseconv2d_bwd_dw(const void* X, const int32_t* N, const void* dY, float* dW, float* db,
+                                 int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                 int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    return sv_sparseconv2d_bwd_dw_k(X, N, dY, dW, db, n, 3, C_in, C_out, dtype, accumulate, workspace,
+                                    workspace_bytes, stream);
+}
+
 // ------------------------------------------------------------ chunk driver
 namespace {
 
 struct ChunkLayout {
+    int K = 3, taps = 9;      // neighbourhood of the descriptor (ksize 0 reads as 3)
     int64_t max_tokens = 0;   // largest chunk, in tokens
     size_t n_bytes = 0;       // chunk-local N table
     size_t w_bytes = 0;       // forward weights repacked for the MFMA kernel
@@ -144,10 +201,14 @@ struct ChunkLayout {
     size_t total = 0;
 };
 
+int ksize_of(int32_t ksize) { return ksize == 0 ? 3 : ksize; }
+
 bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
     if (!d || !d->frame_offsets_host || d->T < 0 || d->H <= 0 || d->W <= 0 ||
         d->chunk_frames <= 0 || d->C_in <= 0 || d->C_out <= 0 || !valid_dtype(d->dtype))
         return false;
+    L->K = ksize_of(d->ksize);
+    if (taps_of(L->K, &L->taps) != SV_OK) return false;
     const int32_t* ho = d->frame_offsets_host;
     if (ho[0] != 0) return false;
     for (int t = 0; t < d->T; ++t)
@@ -155,7 +216,7 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
     L->max_tokens = 0;
     // With the dW pass even an empty video needs the (zero-token) plan's db partials.
     L->dw_bytes = (passes & SV_PASS_DW)
-                      ? dw_workspace_bytes(plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16))
+                      ? dw_workspace_bytes(plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16, L->taps))
                       : 0;
     for (int f0 = 0; f0 < d->T; f0 += d->chunk_frames) {
         const int f1 = std::min(d->T, f0 + d->chunk_frames);
@@ -163,10 +224,10 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
         L->max_tokens = std::max(L->max_tokens, toks);
         if (passes & SV_PASS_DW)
             L->dw_bytes = std::max(L->dw_bytes, dw_workspace_bytes(plan_dw(toks, d->C_in, d->C_out,
-                                                                          d->dtype == SV_BF16)));
+                                                                          d->dtype == SV_BF16, L->taps)));
     }
-    L->n_bytes = align_up(static_cast<size_t>(L->max_tokens) * 9 * sizeof(int32_t));
-    L->w_bytes = (passes & SV_PASS_FWD) ? fwd_ws_bytes(d->C_in, d->C_out, d->dtype, L->max_tokens) : 0;
+    L->n_bytes = align_up(static_cast<size_t>(L->max_tokens) * L->taps * sizeof(int32_t));
+    L->w_bytes = (passes & SV_PASS_FWD) ? fwd_ws_bytes(d->C_in, d->C_out, d->dtype, L->max_tokens, L->taps) : 0;
     L->total = L->n_bytes + L->w_bytes + L->dw_bytes;
     return true;
 }
@@ -181,13 +242,15 @@ size_t sv_chunked_workspace_bytes(const sv_chunked_desc* desc, uint32_t passes) 
 
 sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
+    int taps0 = 0;
+    if (d && taps_of(ksize_of(d->ksize), &taps0) == SV_ERR_UNSUPPORTED) return SV_ERR_UNSUPPORTED;
     ChunkLayout L;
     if (!chunk_layout(d, passes, &L)) return SV_ERR_INVALID_ARG;
     if (passes & ~(SV_PASS_FWD | SV_PASS_DX | SV_PASS_DW)) return SV_ERR_INVALID_ARG;
     if (!valid_kernel(d->kernel)) return SV_ERR_INVALID_ARG;
     if (static_cast<int64_t>(d->H) * d->W > kMaxCells) return SV_ERR_UNSUPPORTED;
     const int64_t n = d->frame_offsets_host[d->T];
-    if (n > kMaxRows) return SV_ERR_INVALID_ARG;
+    if (n > max_rows(L.taps)) return SV_ERR_INVALID_ARG;
     if (!d->frame_offsets || (n > 0 && !d->coords)) return SV_ERR_INVALID_ARG;
     if ((passes & SV_PASS_FWD) && (!d->X || !d->Wt || !d->Y)) return SV_ERR_INVALID_ARG;
     if ((passes & SV_PASS_DX) && (!d->dY || !d->Wt || !d->dX)) return SV_ERR_INVALID_ARG;
@@ -196,10 +259,10 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     // Every chunk holds at most L.max_tokens tokens: a kernel that fits the
     // largest chunk fits them all.
     if ((passes & SV_PASS_FWD) &&
-        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.max_tokens, &m) != SV_OK)
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.max_tokens, L.taps, &m) != SV_OK)
         return SV_ERR_UNSUPPORTED;
     if ((passes & SV_PASS_DX) &&
-        choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.max_tokens, &m) != SV_OK)
+        choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.max_tokens, L.taps, &m) != SV_OK)
         return SV_ERR_UNSUPPORTED;
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return SV_ERR_WORKSPACE;
     if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256) return SV_ERR_INVALID_ARG;
@@ -210,11 +273,12 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     void* dws = static_cast<char*>(workspace) + L.n_bytes + L.w_bytes;
     bool fwd_mfma = false;
     if (passes & SV_PASS_FWD) {
-        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.max_tokens, &fwd_mfma);
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.max_tokens, L.taps, &fwd_mfma);
         if (fwd_mfma && d->T > 0) {
             // the weights are repacked once for every chunk
             sv_status st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(d->Wt),
-                                                        static_cast<uint16_t*>(Vw), d->C_in, d->C_out, stream));
+                                                        static_cast<uint16_t*>(Vw), d->C_in, d->C_out, L.taps,
+                                                        stream));
             if (st != SV_OK) return st;
         }
     }
@@ -223,7 +287,7 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     for (int f0 = 0; f0 < d->T; f0 += d->chunk_frames) {
         const int f1 = std::min(d->T, f0 + d->chunk_frames);
         const int64_t t0 = ho[f0], nc = static_cast<int64_t>(ho[f1]) - t0;
-        sv_status st = hip_status(launch_build_index(d->coords, d->frame_offsets, f0, f1 - f0, d->H, d->W,
+        sv_status st = hip_status(launch_build_index(d->coords, d->frame_offsets, f0, f1 - f0, d->H, d->W, L.K,
                                                      nc, t0, Nc, nullptr, d->err_flag, stream));
         if (st != SV_OK) return st;
         const char* X = d->X ? static_cast<const char*>(d->X) + t0 * d->C_in * es : nullptr;
@@ -231,16 +295,16 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
         if (passes & SV_PASS_FWD) {
             st = run_fwd_prepared(fwd_mfma, X, Nc, d->Wt, Vw, d->bias,
                                   static_cast<char*>(d->Y) + t0 * d->C_out * es, nc, d->C_in, d->C_out,
-                                  d->dtype, stream);
+                                  L.taps, d->dtype, stream);
             if (st != SV_OK) return st;
         }
         if (passes & SV_PASS_DX) {
             st = run_dx(dY, Nc, d->Wt, static_cast<char*>(d->dX) + t0 * d->C_in * es, nc, d->C_in,
-                        d->C_out, d->dtype, d->kernel, stream);
+                        d->C_out, L.taps, d->dtype, d->kernel, stream);
             if (st != SV_OK) return st;
         }
         if (passes & SV_PASS_DW) {
-            const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16);
+            const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16, L.taps);
             st = hip_status(launch_dw(plan, d->dtype == SV_BF16, X, Nc, dY, d->dW, d->db, nc, d->C_in,
                                       d->C_out, first ? 0 : 1, dws, stream));
             if (st != SV_OK) return st;
@@ -249,7 +313,7 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     }
     if (first && (passes & SV_PASS_DW)) {
         // No frames at all: the gradients of an empty sum are zero.
-        const DwPlan plan = plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16);
+        const DwPlan plan = plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16, L.taps);
         return hip_status(launch_dw(plan, d->dtype == SV_BF16, d->X, Nc, d->dY, d->dW, d->db, 0, d->C_in,
                                     d->C_out, 0, dws, stream));
     }
@@ -277,7 +341,7 @@ bool host_layout(const sv_chunked_host_desc* d, uint32_t passes, HostLayout* L) 
     // descriptor carrying the same ones.
     sv_chunked_desc dd{};
     dd.T = d->T; dd.H = d->H; dd.W = d->W; dd.C_in = d->C_in; dd.C_out = d->C_out;
-    dd.dtype = d->dtype; dd.kernel = d->kernel; dd.chunk_frames = d->chunk_frames;
+    dd.dtype = d->dtype; dd.kernel = d->kernel; dd.chunk_frames = d->chunk_frames; dd.ksize = d->ksize;
     dd.frame_offsets_host = d->frame_offsets_host;
     if (!chunk_layout(&dd, passes, &L->dev)) return false;
     const size_t es = d->dtype == SV_BF16 ? 2 : 4;
@@ -314,6 +378,8 @@ size_t sv_chunked_host_workspace_bytes(const sv_chunked_host_desc* desc, uint32_
 sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t passes, void* workspace,
                                        size_t workspace_bytes, hipStream_t compute, hipStream_t h2d,
                                        hipStream_t d2h) {
+    int taps0 = 0;
+    if (d && taps_of(ksize_of(d->ksize), &taps0) == SV_ERR_UNSUPPORTED) return SV_ERR_UNSUPPORTED;
     HostLayout L;
     if (passes & ~(SV_PASS_FWD | SV_PASS_DX | SV_PASS_DW)) return SV_ERR_INVALID_ARG;
     if (!host_layout(d, passes, &L)) return SV_ERR_INVALID_ARG;
@@ -322,17 +388,18 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
     if (static_cast<int64_t>(d->H) * d->W > kMaxCells) return SV_ERR_UNSUPPORTED;
     const int32_t* ho = d->frame_offsets_host;
     const int64_t n = ho[d->T];
-    if (n > kMaxRows) return SV_ERR_INVALID_ARG;
+    const int taps = L.dev.taps;
+    if (n > max_rows(taps)) return SV_ERR_INVALID_ARG;
     if (n > 0 && !d->coords_host) return SV_ERR_INVALID_ARG;
     if ((passes & SV_PASS_FWD) && (!d->X_host || !d->Wt || !d->Y_host)) return SV_ERR_INVALID_ARG;
     if ((passes & SV_PASS_DX) && (!d->dY_host || !d->Wt || !d->dX_host)) return SV_ERR_INVALID_ARG;
     if ((passes & SV_PASS_DW) && (!d->X_host || !d->dY_host || !d->dW)) return SV_ERR_INVALID_ARG;
     bool m;
     if ((passes & SV_PASS_FWD) &&
-        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.dev.max_tokens, &m) != SV_OK)
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.dev.max_tokens, taps, &m) != SV_OK)
         return SV_ERR_UNSUPPORTED;
     if ((passes & SV_PASS_DX) &&
-        choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.dev.max_tokens, &m) != SV_OK)
+        choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.dev.max_tokens, taps, &m) != SV_OK)
         return SV_ERR_UNSUPPORTED;
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return SV_ERR_WORKSPACE;
     if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256) return SV_ERR_INVALID_ARG;
@@ -378,10 +445,11 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
 
     bool fwd_mfma = false;
     if (passes & SV_PASS_FWD) {
-        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.dev.max_tokens, &fwd_mfma);
+        choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.dev.max_tokens, taps, &fwd_mfma);
         if (fwd_mfma && d->T > 0) {
             sv_status st0 = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(d->Wt),
-                                                         static_cast<uint16_t*>(Vw), d->C_in, d->C_out, compute));
+                                                         static_cast<uint16_t*>(Vw), d->C_in, d->C_out, taps,
+                                                         compute));
             if (st0 != SV_OK) return st0;
         }
     }
@@ -389,7 +457,7 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
     if (nchunks == 0) {
         if (!(passes & SV_PASS_DW)) return SV_OK;
         // No frames at all: the gradients of an empty sum are zero.
-        const DwPlan plan = plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16);
+        const DwPlan plan = plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16, taps);
         return hip_status(launch_dw(plan, d->dtype == SV_BF16, nullptr, Nc, nullptr, d->dW, d->db, 0, d->C_in,
                                     d->C_out, 0, dws, compute));
     }
@@ -454,20 +522,21 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
             // for global k, so it gets both bases shifted back.
             const int32_t* coords_g = st[b].coords - t0;
             const int32_t* offs_g = st[b].offs - f0;
-            sv_status s2 = hip_status(launch_build_index(coords_g, offs_g, f0, f1 - f0, d->H, d->W, nc, t0, Nc,
-                                                         nullptr, d->err_flag, compute));
+            sv_status s2 = hip_status(launch_build_index(coords_g, offs_g, f0, f1 - f0, d->H, d->W, L.dev.K, nc,
+                                                         t0, Nc, nullptr, d->err_flag, compute));
             if (s2 != SV_OK) return s2;
             if (passes & SV_PASS_FWD) {
                 s2 = run_fwd_prepared(fwd_mfma, st[b].X, Nc, d->Wt, Vw, d->bias, st[b].Y, nc, d->C_in, d->C_out,
-                                      d->dtype, compute);
+                                      taps, d->dtype, compute);
                 if (s2 != SV_OK) return s2;
             }
             if (passes & SV_PASS_DX) {
-                s2 = run_dx(st[b].dY, Nc, d->Wt, st[b].dX, nc, d->C_in, d->C_out, d->dtype, d->kernel, compute);
+                s2 = run_dx(st[b].dY, Nc, d->Wt, st[b].dX, nc, d->C_in, d->C_out, taps, d->dtype, d->kernel,
+                            compute);
                 if (s2 != SV_OK) return s2;
             }
             if (passes & SV_PASS_DW) {
-                const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16);
+                const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16, taps);
                 s2 = hip_status(launch_dw(plan, d->dtype == SV_BF16, st[b].X, Nc, st[b].dY, d->dW, d->db, nc,
                                           d->C_in, d->C_out, ci == 0 ? 0 : 1, dws, compute));
                 if (s2 != SV_OK) return s2;

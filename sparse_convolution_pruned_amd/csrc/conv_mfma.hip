@@ -5,32 +5,35 @@
 // with M = tokens, K = 9 * C, N = output channels; -1 entries are zero
 // padding.)
 //
-// One kernel serves both passes.  It computes
-//     out[k][c] = sum_j sum_i A[N[k, j]][i] * B[8 - j][c][i]  (+ bias[c])
+// One kernel serves both passes and every K x K neighbourhood it is built
+// for (TAPS = K * K = 1, 9, 25 or 49; P = TAPS - 1).  It computes
+//     out[k][c] = sum_j sum_i A[N[k, j]][i] * B[P - j][c][i]  (+ bias[c])
 // with B stored [tap][output channel][contracted channel]:
-//   input gradient: A = dY, B = Wt itself ([9][C_in][C_out]: tap 8-j of the
-//     weights meets the row gathered through tap j, the mirror of the 3x3
-//     offsets);
-//   forward: A = X, B = V with V[8-j][o][i] = Wt[j][i][o], written by a small
+//   input gradient: A = dY, B = Wt itself ([TAPS][C_in][C_out]: tap P-j of
+//     the weights meets the row gathered through tap j, the mirror of the
+//     K x K offsets);
+//   forward: A = X, B = V with V[P-j][o][i] = Wt[j][i][o], written by a small
 //     repacking kernel into the caller's workspace.
 // Every MFMA fragment is then one 16-byte LDS read and every staging copy a
 // plain 16-byte copy.
 //
 // Workgroup: 256 threads = 4 waves (2 x 2); output tile 128 tokens x 128
 // channels; each wave 64 x 64 = 2 x 2 blocks of 32 x 32.  Two workgroups fit
-// on a compute unit (70 KiB of LDS each).  The 1-D grid is remapped so that
+// on a compute unit at 3 x 3 (67 KiB of LDS each) and 5 x 5 (78 KiB); one at
+// 7 x 7 (96 KiB).  The 1-D grid is remapped so that
 // each XCD runs a contiguous range of tiles (neighbouring token ranges and
 // the channel tiles of one range share rows in that XCD's L2).
 //
 // Neighbour window.  Tokens are packed frame-major and, inside a frame, in
-// ascending flat order, so every neighbour of token k lies within W+1 packed
-// positions of k and a tile's gathered rows sit in one short range [lo, hi].
+// ascending flat order, so every neighbour of token k lies within
+// (K/2)(W+1) packed positions of k and a tile's gathered rows sit in one
+// short range [lo, hi].
 // The kernel reads the tile's N slice, finds lo/hi, and when the range holds
 // at most 192 rows it stages exactly those rows (64 channels at a time, 16-byte
-// coalesced loads) in LDS once for all nine taps; A fragments are then read
+// coalesced loads) in LDS once for all taps; A fragments are then read
 // from LDS by row index (N - lo; -1 maps to an all-zero row).  Tiles whose rows
-// are spread wider (another packing order, grids wider than 31) fall back to
-// staging the 128 gathered rows tap by tap.  Both modes feed the same MFMA
+// are spread wider (another packing order, grids wider than 31 at 3 x 3)
+// fall back to staging the 128 gathered rows tap by tap.  Both modes feed the same MFMA
 // sequence, so the result does not depend on the mode.
 //
 // Pipeline.  The K loop runs over rounds (64-channel chunk, tap).  At the
@@ -80,17 +83,18 @@ __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const
             for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[ks][mb], b[ks][nb], acc[mb][nb]);
 }
 
-// A [n][K], B [9][NO][K], bias [NO] (nullable), out [n][NO]; K % 32 == 0,
+// A [n][K], B [TAPS][NO][K], bias [NO] (nullable), out [n][NO]; K % 32 == 0,
 // NO % 16 == 0.
-__global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict__ A,
+template <int TAPS>
+__global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uint16_t* __restrict__ A,
                                                       const int32_t* __restrict__ Nt,
                                                       const uint16_t* __restrict__ B,
                                                       const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ out, int n, int K, int NO) {
     __shared__ __align__(16) uint16_t sA[(CM_WIN + 1) * CM_LDA];
     __shared__ __align__(16) uint16_t sB[2][CM_SB];   // weight tiles, written by direct loads
-    __shared__ int sN[CM_BM * 9];
-    __shared__ short sRow[CM_BM * 9];
+    __shared__ int sN[CM_BM * TAPS];
+    __shared__ short sRow[CM_BM * TAPS];
     __shared__ int sLo, sHi;
 
     // The wave index is uniform; through the scalar unit it keeps every
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     const int64_t k0 = static_cast<int64_t>(logical / tilesN) * CM_BM;
     const int n0 = (logical % tilesN) * CM_BN;
     const int nchunks = (K + CM_KC - 1) / CM_KC;
-    const int R = nchunks * 9;
+    const int R = nchunks * TAPS;
 
     if (tid == 0) { sLo = 0x7fffffff; sHi = -1; }
     if (tid < CM_KC / 8)
@@ -115,17 +119,17 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
 
     // ---- the tile's slice of N, its row range, and the LDS row of every entry
     {
-        // The tile's N rows are contiguous: 1152 consecutive ints, all loads
-        // issued before any is used.
-        constexpr int NE = (CM_BM * 9 + 255) / 256;
-        const int64_t base = k0 * 9;
-        const int64_t lim = static_cast<int64_t>(n) * 9;
+        // The tile's N rows are contiguous: 128 * TAPS consecutive ints, all
+        // loads issued before any is used.
+        constexpr int NE = (CM_BM * TAPS + 255) / 256;
+        const int64_t base = k0 * TAPS;
+        const int64_t lim = static_cast<int64_t>(n) * TAPS;
         int m[NE];
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
             const int e = tid + 256 * u;
-            const bool ok = e < CM_BM * 9 && base + e < lim;
-            const int v = Nt[min(base + min(e, CM_BM * 9 - 1), lim - 1)];   // clamped: branch-free
+            const bool ok = e < CM_BM * TAPS && base + e < lim;
+            const int v = Nt[min(base + min(e, CM_BM * TAPS - 1), lim - 1)];   // clamped: branch-free
             m[u] = ok ? v : -1;
         }
         int lo = 0x7fffffff, hi = -1;
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         for (int u = 0; u < NE; ++u) {
             const int e = tid + 256 * u;
             const int v = clamp_index(m[u], n);
-            if (e < CM_BM * 9) sN[e] = v;
+            if (e < CM_BM * TAPS) sN[e] = v;
             if (v >= 0) { lo = min(lo, v); hi = max(hi, v); }
         }
         // Reduce within the wave first (same-address LDS atomics from every
@@ -149,9 +153,9 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     const int wlo = sLo;
     const int span = (sHi >= 0) ? sHi - wlo + 1 : 0;
     const bool window = span <= CM_WIN;
-    for (int e = tid; e < CM_BM * 9; e += 256) {
+    for (int e = tid; e < CM_BM * TAPS; e += 256) {
         const int m = sN[e];
-        sRow[e] = static_cast<short>(m < 0 ? CM_ZROW : (window ? m - wlo : e / 9));
+        sRow[e] = static_cast<short>(m < 0 ? CM_ZROW : (window ? m - wlo : e / TAPS));
     }
 
     // ---- staging helpers: raw buffer loads, 16-byte pieces.  Pieces outside
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     // out-of-range offset and read as zeros, so every store below is plain
     // and no load sits behind a branch.
     const rsrc_t rA = make_rsrc(A, static_cast<uint32_t>(n) * K * 2);
-    const rsrc_t rB = make_rsrc(B, 9u * NO * K * 2);
+    const rsrc_t rB = make_rsrc(B, static_cast<uint32_t>(TAPS) * NO * K * 2);
     auto kc_of = [&](int c) { return min(CM_KC, K - c * CM_KC); };
     auto load_window = [&](int c, uint4* regs) {
         const int c0 = c * CM_KC, kc = kc_of(c);
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
             *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) = regs[u];
         }
     };
-    // Weight tile of round rr (chunk rr / 9, tap rr % 9): B[8-j][n0 + nn][c0 + ...],
+    // Weight tile of round rr (chunk rr / TAPS, tap rr % TAPS): B[P-j][n0 + nn][c0 + ...],
     // loaded straight into LDS (buffer_load ... lds: lane L of an
     // instruction writes the 16 bytes at the instruction's LDS base + 16 L),
     // so it needs no registers and no LDS store instructions.  Row nn's
@@ -204,9 +208,9 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     }
     typedef __attribute__((address_space(3))) void lds_void_t;
     auto issue_B = [&](int rr, int buf) {
-        const int c = rr / 9, j = rr - c * 9;
+        const int c = rr / TAPS, j = rr - c * TAPS;
         const int c0 = c * CM_KC, kc = kc_of(c);
-        const uint32_t roff = (static_cast<uint32_t>(8 - j) * NO * K + c0) * 2;
+        const uint32_t roff = (static_cast<uint32_t>(TAPS - 1 - j) * NO * K + c0) * 2;
         uint16_t* sb = sB[buf];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -215,13 +219,13 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     };
     // Gather mode: the 128 rows of tap j, chunk c, straight into sA.
     auto stage_gather = [&](int rr) {
-        const int c = rr / 9, j = rr - c * 9;
+        const int c = rr / TAPS, j = rr - c * TAPS;
         const int c0 = c * CM_KC, kc = kc_of(c);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int q = tid + 256 * u;
             const int r = q >> 3, ch = q & 7;
-            const int m = sN[r * 9 + j];
+            const int m = sN[r * TAPS + j];
             const bool ok = m >= 0 && ch * 8 < kc;
             *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) =
                 load16(rA, ok ? (static_cast<uint32_t>(m) * K + c0 + ch * 8) * 2 : kOob);
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     __syncthreads();                      // also waits for the direct loads
 
     for (int r = 0; r < R; ++r) {
-        const int c = r / 9, j = r - c * 9;
+        const int c = r / TAPS, j = r - c * TAPS;
         if (!window) {
             stage_gather(r);
             __syncthreads();
@@ -252,17 +256,17 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
         // round r - 1, before the previous barrier), issued ahead of this
         // round's MFMAs; the barrier at the end of the round waits for them.
         // Mid-chunk, the next chunk's window rows go out first.
-        if (window && span > 0 && j == 4 && c + 1 < nchunks) load_window(c + 1, wreg);
+        if (window && span > 0 && j == TAPS / 2 && c + 1 < nchunks) load_window(c + 1, wreg);
         if (r + 1 < R) issue_B(r + 1, (r + 1) & 1);
         int arow[2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) arow[mb] = sRow[(wm * 64 + mb * 32 + l32) * 9 + j];
+        for (int mb = 0; mb < 2; ++mb) arow[mb] = sRow[(wm * 64 + mb * 32 + l32) * TAPS + j];
         // Always the full 4 k-steps: a 32-channel tail chunk is zero-filled
         // past its end in both operands, and one code path keeps the
         // accumulators in fixed registers.
         mma_round(sA, sB[r & 1], arow, acc);
         if (r + 1 < R) {
-            if (window && span > 0 && (r + 1) % 9 == 0) {
+            if (window && span > 0 && (r + 1) % TAPS == 0) {
                 __syncthreads();           // every wave is done with this chunk's window
                 store_window(wreg);
             }
@@ -305,15 +309,15 @@ __global__ __launch_bounds__(256, 2) void k_conv_mfma(const uint16_t* __restrict
     }
 }
 
-// V[8-j][o][i] = Wt[j][i][o]: nine C_in x C_out transposes through LDS,
-// 32 x 32 tiles (rows padded by one element), 4 elements per thread.
+// V[P-j][o][i] = Wt[j][i][o]: one C_in x C_out transpose per tap through
+// LDS, 32 x 32 tiles (rows padded by one element), 4 elements per thread.
 __global__ __launch_bounds__(256) void k_repack_fwd(const uint16_t* __restrict__ Wt, uint16_t* __restrict__ V,
                                                     int Ci, int Co) {
     __shared__ uint16_t t[32][33];
     const int j = blockIdx.z;
     const int i0 = blockIdx.y * 32, o0 = blockIdx.x * 32;
     const uint16_t* src = Wt + static_cast<int64_t>(j) * Ci * Co;
-    uint16_t* dst = V + static_cast<int64_t>(8 - j) * Co * Ci;
+    uint16_t* dst = V + static_cast<int64_t>(gridDim.z - 1 - j) * Co * Ci;
     const int c = threadIdx.x & 31, r0 = threadIdx.x >> 5;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -328,28 +332,36 @@ __global__ __launch_bounds__(256) void k_repack_fwd(const uint16_t* __restrict__
     }
 }
 
-bool conv_mfma_supported(bool dx, int Ci, int Co, int64_t n) {
+bool conv_mfma_supported(bool dx, int Ci, int Co, int64_t n, int taps) {
     const int K = dx ? Co : Ci, NO = dx ? Ci : Co;
-    return K > 0 && NO > 0 && K % 32 == 0 && NO % 16 == 0 && n * K * 2 <= kMaxRange &&
-           9ll * NO * K * 2 <= kMaxRange;
+    const bool built = taps == 1 || taps == 9 || taps == 25 || taps == 49;
+    return built && K > 0 && NO > 0 && K % 32 == 0 && NO % 16 == 0 && n * K * 2 <= kMaxRange &&
+           static_cast<int64_t>(taps) * NO * K * 2 <= kMaxRange;
 }
 
-size_t conv_mfma_fwd_workspace(int Ci, int Co) {
-    return (static_cast<size_t>(9) * Ci * Co * sizeof(uint16_t) + 255) & ~static_cast<size_t>(255);
+size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps) {
+    return (static_cast<size_t>(taps) * Ci * Co * sizeof(uint16_t) + 255) & ~static_cast<size_t>(255);
 }
 
-hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, hipStream_t stream) {
-    dim3 grid((Co + 31) / 32, (Ci + 31) / 32, 9);
+hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream) {
+    dim3 grid((Co + 31) / 32, (Ci + 31) / 32, taps);
     hipLaunchKernelGGL(k_repack_fwd, grid, dim3(256), 0, stream, Wt, V, Ci, Co);
     return hipGetLastError();
 }
 
 hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const uint16_t* B,
-                                   const uint16_t* bias, uint16_t* out, int64_t n, int K, int NO,
+                                   const uint16_t* bias, uint16_t* out, int64_t n, int K, int NO, int taps,
                                    hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>(((n + CM_BM - 1) / CM_BM) * ((NO + CM_BN - 1) / CM_BN)));
-    hipLaunchKernelGGL(k_conv_mfma, grid, dim3(256), 0, stream, A, N, B, bias, out, static_cast<int>(n), K, NO);
+    const int nn = static_cast<int>(n);
+    switch (taps) {
+        case 1: hipLaunchKernelGGL(k_conv_mfma<1>, grid, dim3(256), 0, stream, A, N, B, bias, out, nn, K, NO); break;
+        case 9: hipLaunchKernelGGL(k_conv_mfma<9>, grid, dim3(256), 0, stream, A, N, B, bias, out, nn, K, NO); break;
+        case 25: hipLaunchKernelGGL(k_conv_mfma<25>, grid, dim3(256), 0, stream, A, N, B, bias, out, nn, K, NO); break;
+        case 49: hipLaunchKernelGGL(k_conv_mfma<49>, grid, dim3(256), 0, stream, A, N, B, bias, out, nn, K, NO); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Weight and bias gradients as a split-K reduction over tokens.
-//   dW[j][i][o] = sum_k X[N[k,j]][i] dY[k][o]      (a GEMM with M = 9 C_in,
+//   dW[j][i][o] = sum_k X[N[k,j]][i] dY[k][o]      (a GEMM with M = taps C_in,
 //   db[o]       = sum_k dY[k][o]                     N = C_out, K = tokens)
+// for a K x K neighbourhood with taps = K * K (9 in the page's 3 x 3 case).
 // ("SV-TAD: Native Sparse Convolutions for Efficient Temporal Action
 // Detection", Key Design 2 names dedicated backward kernels; the formula is
 // the adjoint of the forward sum.)
@@ -18,26 +19,30 @@
 namespace svc {
 
 hipError_t launch_dw_valu(bool bf16, const void* X, const int32_t* N, const void* dY, float* out,
-                          int64_t n, int Ci, int Co, int slices, int64_t slice_tokens, int direct,
-                          int accumulate, hipStream_t stream);
+                          int64_t n, int Ci, int Co, int taps, int slices, int64_t slice_tokens,
+                          int direct, int accumulate, hipStream_t stream);
 
-// MFMA kernel: workgroup = (kernel row r: taps 3r, 3r+1, 3r+2; 128 input
-// channels; 128 output channels; token slice), 8 waves.  Wave w owns input
-// channels 32 (w & 3) .. +31 for the three taps and output channels
-// 64 (w >> 2) .. +63: 3 x 2 blocks of 32 x 32 (96 accumulators), so each dY
-// fragment feeds three taps.
+// MFMA kernel.  A unit is one (tap, 128-input-channel tile) pair; units are
+// numbered tap-fastest (u = tile * taps + tap) and cut into groups of three,
+// the last group padded with empty units.  At 3 x 3 a group is one kernel
+// row (taps 3r, 3r+1, 3r+2) of one input tile; at 1 x 1 it is three input
+// tiles.  Workgroup = (group; 128 output channels; token slice), 8 waves.
+// Wave w owns input channels 32 (w & 3) .. +31 of the three units and output
+// channels 64 (w >> 2) .. +63: 3 x 2 blocks of 32 x 32 (96 accumulators), so
+// each dY fragment feeds three units.  An empty unit stages zeros and stores
+// nothing.
 //
 // The contraction runs over tokens while both operands are stored with
 // channels contiguous.  Each step of 64 tokens is staged transposed: the
-// workgroup's 512 8 x 8 blocks (3 taps x 8 token groups x 16 channel groups
+// workgroup's 512 8 x 8 blocks (3 units x 8 token groups x 16 channel groups
 // of gathered X rows, 8 x 16 of dY rows; one per thread) are loaded as
-// 16-byte rows (the X rows through N[k][3r + tap]), transposed in registers
+// 16-byte rows (the X rows through N[k][unit's tap]), transposed in registers
 // and written to LDS channel-major, [tile][channel][token], where every MFMA
 // fragment is one 16-byte read.  At the start of step s the tiles of step
 // s + 1 go into the free LDS buffer and the row loads of step s + 2 are
 // issued, ahead of step s's MFMAs; each step ends with a single barrier.
 //
-// The N entries a step needs (64 tokens x 3 taps) are fetched once per
+// The N entries a step needs (64 tokens x 3 units) are fetched once per
 // workgroup by one wave, lane = token, two steps ahead, and passed through a
 // small double-buffered LDS table: per-thread loads would request each entry
 // 16 times and touch 8 cache lines per instruction for 32 useful bytes.
@@ -50,14 +55,14 @@ constexpr int DW_BI = 128, DW_BO = 128, DW_TK = 64, DW_THREADS = 512;
 constexpr int DW_LD = DW_TK + 8;                 // 144-byte rows
 constexpr int DW_TILE = 128 * DW_LD;             // one [128 channels][64 tokens] tile
 constexpr int DW_BUF = 4 * DW_TILE;              // 3 X tiles + 1 dY tile
-constexpr int DW_NTAB = 2 * 3 * DW_TK;           // N table: [2 buffers][3 taps][64 tokens]
+constexpr int DW_NTAB = 2 * 3 * DW_TK;           // N table: [2 buffers][3 units][64 tokens]
 constexpr size_t DW_LDS = 2 * DW_BUF * sizeof(uint16_t) + DW_NTAB * sizeof(int);
 
 __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restrict__ X,
                                                         const int32_t* __restrict__ Nt,
                                                         const uint16_t* __restrict__ dY,
                                                         float* __restrict__ out, float* __restrict__ dbout,
-                                                        int n, int Ci, int Co, int slice_tokens,
+                                                        int n, int Ci, int Co, int taps, int slice_tokens,
                                                         int direct, int accumulate) {
     extern __shared__ __align__(16) uint16_t dwsm[];   // 2 buffers of DW_BUF, then the N table
     int* const ntab = reinterpret_cast<int*>(dwsm + 2 * DW_BUF);
@@ -65,19 +70,20 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     // 1-D grid of tiles x slices: logical id = slice * tiles + tile, so the
     // tiles of one token slice (which gather the same X and dY rows) sit
     // together on one XCD and share its L2.
-    const int tilesI = Ci / DW_BI;
-    const int tiles = 3 * tilesI * (Co / DW_BO);
+    const int units = taps * (Ci / DW_BI);
+    const int groups = (units + 2) / 3;
+    const int tiles = groups * (Co / DW_BO);
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int slice = logical / tiles;
-    int bid = logical % tiles;
-    const int kr = bid % 3;
-    bid /= 3;
-    const int i0 = (bid % tilesI) * DW_BI;
-    const int o0 = (bid / tilesI) * DW_BO;
+    const int bid = logical % tiles;
+    const int grp = bid % groups;
+    const int o0 = (bid / groups) * DW_BO;
     const int kbeg = slice * slice_tokens;
     const int cnt = max(0, min(n - kbeg, slice_tokens));     // tokens of this slice
     const int steps = (cnt + DW_TK - 1) / DW_TK;
-    const bool do_db = dbout != nullptr && kr == 1 && i0 == 0;
+    // one group per output tile also sums db (group 1 at 3 x 3: kernel row 1
+    // of the first input tile)
+    const bool do_db = dbout != nullptr && grp == min(1, groups - 1);
 
     // The wave index is uniform across a wave; reading it through the scalar
     // unit lets every per-wave condition below compile to a scalar branch.
@@ -86,19 +92,24 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     const int l32 = lane & 31, lhi = lane >> 5;
     const int wi = wave & 3, wo = wave >> 2;
 
-    // This thread's 8 x 8 block: tile = wave >> 1 (taps 0..2 of the row, then
-    // dY), token group tid & 7, channel group (tid >> 3) & 15.  The block
+    // This thread's 8 x 8 block: tile = wave >> 1 (units 0..2 of the group,
+    // then dY), token group tid & 7, channel group (tid >> 3) & 15.  The block
     // lands at LDS rows cg*8 + e, column tg*8: bank group (tg + e) mod 8 with
     // the 144-byte pitch, so the 8 lanes that share a write cycle (8 token
     // groups) never collide.
     const int tile = wave >> 1, tg = tid & 7, cg = (tid >> 3) & 15;
     const bool is_x = tile < 3;
+    // this wave's unit (X tiles only): its tap and input-channel tile
+    const int unit = 3 * grp + (is_x ? tile : 0);
+    const bool xlive = is_x && unit < units;
+    const int utap = unit % taps, ui0 = (unit / taps) * DW_BI;
+    const uint32_t nrow = static_cast<uint32_t>(taps) * 4;   // bytes per N row
     const rsrc_t rX = make_rsrc(X, static_cast<uint32_t>(n) * Ci * 2);
-    const rsrc_t rN = make_rsrc(Nt + static_cast<int64_t>(kbeg) * 9, static_cast<uint32_t>(cnt) * 36);
+    const rsrc_t rN = make_rsrc(Nt + static_cast<int64_t>(kbeg) * taps, static_cast<uint32_t>(cnt) * nrow);
     const rsrc_t rY = make_rsrc(dY + static_cast<int64_t>(kbeg) * Co, static_cast<uint32_t>(cnt) * Co * 2);
-    const uint32_t nOff = static_cast<uint32_t>(tg * 8) * 36 + (3 * kr + (is_x ? tile : 0)) * 4;
+    const uint32_t nOff = static_cast<uint32_t>(tg * 8) * nrow + utap * 4;
     const uint32_t yOff = static_cast<uint32_t>(tg * 8) * Co * 2 + (o0 + cg * 8) * 2;
-    const uint32_t xCol = (i0 + cg * 8) * 2, rowX = Ci * 2, rowY = Co * 2;
+    const uint32_t xCol = (ui0 + cg * 8) * 2, rowX = Ci * 2, rowY = Co * 2;
     uint4 rr[8];
     int ni[8];
     // N entries are used as they are loaded and tested only when the rows
@@ -110,17 +121,21 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     //   get_n: this thread's 8 entries from the table.
     const bool loader = wave == 6;
     int nreg[3];
+    // the loader's column of N for each unit of the group (-1: empty unit)
+    int ltap[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) ltap[t] = 3 * grp + t < units ? (3 * grp + t) % taps : -1;
     auto load_n = [&](int s) {
         if (is_x) {
-            const uint32_t base = nOff + static_cast<uint32_t>(s * DW_TK) * 36;
+            const uint32_t base = nOff + static_cast<uint32_t>(s * DW_TK) * nrow;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) ni[t] = load4(rN, base + t * 36);
+            for (int t = 0; t < 8; ++t) ni[t] = load4(rN, base + t * nrow);
         }
     };
     auto fetch_n = [&](int s) {
-        const uint32_t base = static_cast<uint32_t>(s * DW_TK + lane) * 36 + 3 * kr * 4;
+        const uint32_t base = static_cast<uint32_t>(s * DW_TK + lane) * nrow;
 #pragma unroll
-        for (int t = 0; t < 3; ++t) nreg[t] = load4(rN, base + t * 4);
+        for (int t = 0; t < 3; ++t) nreg[t] = ltap[t] >= 0 ? load4(rN, base + ltap[t] * 4) : -1;
     };
     auto put_n = [&](int s) {
 #pragma unroll
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
             const int lim = cnt - s * DW_TK - tg * 8;     // tokens t < lim lie in the slice
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const bool ok = static_cast<unsigned>(ni[t]) < static_cast<unsigned>(n) && t < lim;
+                const bool ok = xlive && static_cast<unsigned>(ni[t]) < static_cast<unsigned>(n) && t < lim;
                 rr[t] = load16(rX, ok ? __umul24(static_cast<unsigned>(ni[t]), rowX) + xCol : kOob);
             }
         } else {
@@ -230,10 +245,13 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
 
     // D block (32 input channels x 32 output channels): lane holds output
     // channel l32 and input channels 8g + 4*lhi + q.
-    float* dst = out + (direct ? 0 : static_cast<int64_t>(slice) * 9 * Ci * Co);
+    float* dst = out + (direct ? 0 : static_cast<int64_t>(slice) * taps * Ci * Co);
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-        float* dj = dst + static_cast<int64_t>(3 * kr + t) * Ci * Co;
+        const int u = 3 * grp + t;
+        if (u >= units) continue;
+        const int i0 = (u / taps) * DW_BI;
+        float* dj = dst + static_cast<int64_t>(u % taps) * Ci * Co;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -329,11 +347,12 @@ __global__ __launch_bounds__(256) void k_reduce_slices(const float* __restrict__
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16) {
+DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16, int taps) {
     DwPlan p{};
+    p.taps = taps;
     // The MFMA kernel addresses X, dY and N through 32-bit buffer offsets.
     p.mfma = bf16 && Ci % DW_BI == 0 && Co % DW_BO == 0 && n * Ci * 2 <= kMaxRange &&
-             n * Co * 2 <= kMaxRange && n * 36 <= kMaxRange;
+             n * Co * 2 <= kMaxRange && n * taps * 4 <= kMaxRange;
     int64_t slices;
     const int64_t step = p.mfma ? DW_TK : 16;
     if (p.mfma) {
@@ -342,9 +361,9 @@ DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16) {
         // rounds, plus the fp32 partials written and read back (~5 TB/s) and
         // a fixed cost for the extra reduction launch.  Depends on the
         // arguments only, so workspace sizing and the call agree.
-        const int64_t tiles = 3ll * (Ci / DW_BI) * (Co / DW_BO);
-        const double flops = 2.0 * static_cast<double>(n) * 9 * Ci * Co;
-        const double dwb = 9.0 * Ci * Co * 4;
+        const int64_t tiles = ceil_div(static_cast<int64_t>(taps) * (Ci / DW_BI), 3) * (Co / DW_BO);
+        const double flops = 2.0 * static_cast<double>(n) * (3 * tiles / (Co / DW_BO)) * DW_BI * Co;
+        const double dwb = static_cast<double>(taps) * Ci * Co * 4;
         double best = 1e30;
         slices = 1;
         for (int64_t s = 1; s <= 64; ++s) {
@@ -355,7 +374,7 @@ DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16) {
             if (t < best) { best = t; slices = s; }
         }
     } else {
-        const int64_t tiles = 9ll * ceil_div(Ci, 64) * ceil_div(Co, 64);
+        const int64_t tiles = static_cast<int64_t>(taps) * ceil_div(Ci, 64) * ceil_div(Co, 64);
         slices = ceil_div(512, tiles);
         slices = std::min<int64_t>(slices, std::max<int64_t>(1, n / 512));
         slices = std::max<int64_t>(1, std::min<int64_t>(slices, 64));
@@ -365,7 +384,7 @@ DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16) {
     slices = std::max<int64_t>(1, ceil_div(n, st));
     p.slices = static_cast<int>(slices);
     p.slice_tokens = st;
-    p.partial_floats = slices > 1 ? static_cast<size_t>(slices) * 9 * Ci * Co : 0;
+    p.partial_floats = slices > 1 ? static_cast<size_t>(slices) * taps * Ci * Co : 0;
     p.db_floats = static_cast<size_t>(slices) * Co;
     return p;
 }
@@ -389,15 +408,16 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
             reinterpret_cast<const void*>(k_dw_mfma), hipFuncAttributeMaxDynamicSharedMemorySize,
             static_cast<int>(DW_LDS));
         if (attr != hipSuccess) return attr;
-        dim3 grid(3 * (Ci / DW_BI) * (Co / DW_BO) * plan.slices);
+        const int groups = (plan.taps * (Ci / DW_BI) + 2) / 3;
+        dim3 grid(groups * (Co / DW_BO) * plan.slices);
         hipLaunchKernelGGL(k_dw_mfma, grid, dim3(DW_THREADS), DW_LDS, stream, static_cast<const uint16_t*>(X), N,
                            static_cast<const uint16_t*>(dY), direct ? dW : part,
-                           db ? (direct ? db : dbpart) : nullptr, static_cast<int>(n), Ci, Co,
+                           db ? (direct ? db : dbpart) : nullptr, static_cast<int>(n), Ci, Co, plan.taps,
                            static_cast<int>(plan.slice_tokens), direct ? 1 : 0, accumulate);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     } else {
-        err = launch_dw_valu(bf16, X, N, dY, direct ? dW : part, n, Ci, Co, plan.slices, plan.slice_tokens,
-                             direct ? 1 : 0, accumulate, stream);
+        err = launch_dw_valu(bf16, X, N, dY, direct ? dW : part, n, Ci, Co, plan.taps, plan.slices,
+                             plan.slice_tokens, direct ? 1 : 0, accumulate, stream);
         if (err != hipSuccess) return err;
         if (db) {
             dim3 grid(static_cast<unsigned>(ceil_div(Co, 64)), plan.slices);
@@ -415,7 +435,7 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
     // db partials of the MFMA kernel go through the dW reduction launch.
     bool db_done = db && plan.mfma && direct;
     if (!direct) {
-        const int64_t count = 9ll * Ci * Co;
+        const int64_t count = static_cast<int64_t>(plan.taps) * Ci * Co;
         if (count % 4 == 0) {
             const int blocks = static_cast<int>(std::min<int64_t>(ceil_div(count / 4, 256), 8192));
             hipLaunchKernelGGL(k_reduce_slices4, dim3(blocks), dim3(256), 0, stream,

@@ -6,7 +6,9 @@
 // 64 KiB): fill with -1, scatter M[p_k] = k with an atomic exchange (a
 // previous value other than -1 means two tokens on one cell), then each
 // thread produces consecutive elements of the frame's contiguous N block, so
-// the 36-byte rows are written fully coalesced.
+// the rows (K*K int32 each) are written fully coalesced.  The neighbourhood
+// is K x K (K odd), tap j = K (dy + K/2) + (dx + K/2) for offsets dy, dx in
+// [-K/2, K/2]: the 3 x 3 case is the one the page builds.
 #include "internal.h"
 
 namespace svc {
@@ -15,7 +17,7 @@ constexpr int kIndexThreads = 256;
 
 __global__ __launch_bounds__(kIndexThreads) void k_build_index(
     const int32_t* __restrict__ coords, const int32_t* __restrict__ offs, int frame_begin,
-    int H, int W, int64_t n_rows, int64_t tok_base, int32_t* __restrict__ N,
+    int H, int W, int K, int64_t n_rows, int64_t tok_base, int32_t* __restrict__ N,
     int32_t* __restrict__ M, int32_t* __restrict__ err) {
     extern __shared__ int32_t smap[];
     const int cells = H * W;
@@ -46,17 +48,19 @@ __global__ __launch_bounds__(kIndexThreads) void k_build_index(
 
     // Step 2: N[k][j] = M[y + dy_j][x + dx_j], bounds checked per axis.
     if (ok) {
-        const int total = static_cast<int>(end - beg) * 9;
-        int32_t* __restrict__ Nf = N + (beg - tok_base) * 9;
+        const int taps = K * K, rad = K / 2;
+        const int total = static_cast<int>(end - beg) * taps;   // <= 16384 * 49
+        int32_t* __restrict__ Nf = N + (beg - tok_base) * taps;
         const int32_t* __restrict__ cf = coords + beg;
         for (int e = threadIdx.x; e < total; e += kIndexThreads) {
-            const int r = e / 9;
-            const int j = e - r * 9;
+            const int r = e / taps;
+            const int j = e - r * taps;
             const int p = cf[r];
             int v = -1;
             if (static_cast<unsigned>(p) < static_cast<unsigned>(cells)) {
                 const int y = p / W, x = p - y * W;
-                const int yy = y + j / 3 - 1, xx = x + j % 3 - 1;
+                const int dy = j / K;
+                const int yy = y + dy - rad, xx = x + (j - dy * K) - rad;
                 if (yy >= 0 && yy < H && xx >= 0 && xx < W) v = smap[yy * W + xx];
             }
             Nf[e] = v;
@@ -70,12 +74,12 @@ __global__ __launch_bounds__(kIndexThreads) void k_build_index(
 }
 
 hipError_t launch_build_index(const int32_t* coords, const int32_t* offs, int frame_begin,
-                              int frames, int H, int W, int64_t n_rows, int64_t tok_base,
+                              int frames, int H, int W, int K, int64_t n_rows, int64_t tok_base,
                               int32_t* N, int32_t* M, int32_t* err, hipStream_t stream) {
     if (frames <= 0) return hipSuccess;
     const size_t lds = sizeof(int32_t) * static_cast<size_t>(H) * W;
     hipLaunchKernelGGL(k_build_index, dim3(frames), dim3(kIndexThreads), lds, stream, coords,
-                       offs, frame_begin, H, W, n_rows, tok_base, N, M, err);
+                       offs, frame_begin, H, W, K, n_rows, tok_base, N, M, err);
     return hipGetLastError();
 }
 

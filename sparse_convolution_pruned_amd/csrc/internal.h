@@ -98,41 +98,48 @@ __device__ __forceinline__ int xcd_remap(int linear, int count) {
 // ---------------------------------------------------------------- launchers
 // Every launcher enqueues on `stream` and returns hipGetLastError().
 
+// K: side of the K x K neighbourhood (odd); N rows hold K * K entries.
 hipError_t launch_build_index(const int32_t* coords, const int32_t* offs, int frame_begin,
-                              int frames, int H, int W, int64_t n, int64_t tok_base,
+                              int frames, int H, int W, int K, int64_t n, int64_t tok_base,
                               int32_t* N, int32_t* M, int32_t* err, hipStream_t stream);
 
+// In the conv launchers `taps` = K * K: the columns of N and the leading
+// dimension of the weights; tap taps-1-j is the mirror of tap j.
+//
 // VALU path (fp32 or bf16, any channel count).  `dx` selects the input
 // gradient: A = dY [n][Co], output [n][Ci], weights read transposed with the
 // tap mirrored; otherwise A = X [n][Ci], output [n][Co].
 hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
                             const void* Wt, const void* bias, void* out, int64_t n,
-                            int Ci, int Co, hipStream_t stream);
+                            int Ci, int Co, int taps, hipStream_t stream);
 
-// MFMA path (bf16).  One gather-GEMM serves both passes:
-//   out[k][c] = sum_j sum_i A[N[k,j]][i] * B[8-j][c][i] (+ bias[c]),
-// A [n][K], B [9][NO][K] (K % 32 == 0, NO % 16 == 0).  The input gradient
+// MFMA path (bf16, taps in {1, 9, 25, 49}).  One gather-GEMM serves both
+// passes:
+//   out[k][c] = sum_j sum_i A[N[k,j]][i] * B[taps-1-j][c][i] (+ bias[c]),
+// A [n][K], B [taps][NO][K] (K % 32 == 0, NO % 16 == 0).  The input gradient
 // calls it with A = dY and B = Wt; the forward with A = X and B = V, the
-// weights repacked by launch_repack_fwd (V[8-j][o][i] = Wt[j][i][o]) into
-// conv_mfma_fwd_workspace(Ci, Co) bytes.
+// weights repacked by launch_repack_fwd (V[taps-1-j][o][i] = Wt[j][i][o])
+// into conv_mfma_fwd_workspace(Ci, Co, taps) bytes.
 hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const uint16_t* B,
                                    const uint16_t* bias, uint16_t* out, int64_t n, int K, int NO,
-                                   hipStream_t stream);
-hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, hipStream_t stream);
-size_t conv_mfma_fwd_workspace(int Ci, int Co);
-// bf16, contracted channels a multiple of 32, output channels of 16, and
-// the n rows of A within the 2 GiB range of a buffer load.
-bool conv_mfma_supported(bool dx, int Ci, int Co, int64_t n);
+                                   int taps, hipStream_t stream);
+hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream);
+size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps);
+// bf16, a tap count the kernel is built for, contracted channels a multiple
+// of 32, output channels of 16, and the n rows of A within the 2 GiB range
+// of a buffer load.
+bool conv_mfma_supported(bool dx, int Ci, int Co, int64_t n, int taps);
 
 // dW: split-K plan, partial kernels, reduction.
 struct DwPlan {
+    int taps;              // K * K
     bool mfma;
     int slices;            // token slices (split-K factor)
     int64_t slice_tokens;  // tokens per slice (multiple of the kernel's token step)
     size_t partial_floats; // floats of dW partials in the workspace (0 when slices == 1)
     size_t db_floats;      // floats of db partials
 };
-DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16);
+DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16, int taps);
 size_t dw_workspace_bytes(const DwPlan& p);
 hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t* N,
                      const void* dY, float* dW, float* db, int64_t n, int Ci, int Co,

@@ -11,6 +11,9 @@ Layouts (row-major, contiguous), as in the C header:
   coords int32 [n], frame_offsets int32 [T+1], N int32 [n, 9],
   X [n, C_in], Y [n, C_out], Wt [9, C_in, C_out], bias [C_out],
   dW fp32 [9, C_in, C_out], db fp32 [C_out].
+The ``_k`` entry points take a K x K neighbourhood (K odd, 1..7): N has
+K*K columns and Wt, dW K*K taps.  The conveniences at the end infer K from
+the shapes.
 """
 from __future__ import annotations
 
@@ -36,7 +39,9 @@ KERNELS = {"auto": SV_KERNEL_AUTO, "valu": SV_KERNEL_VALU, "mfma": SV_KERNEL_MFM
 # Exported symbols, in header order.
 SYMBOLS = (
     "sv_build_index", "sv_sparseconv2d_fwd", "sv_sparseconv2d_bwd_dx",
-    "sv_sparseconv2d_bwd_dw", "sv_workspace_bytes", "sv_sparseconv2d_chunked",
+    "sv_sparseconv2d_bwd_dw", "sv_workspace_bytes",
+    "sv_build_index_k", "sv_sparseconv2d_fwd_k", "sv_sparseconv2d_bwd_dx_k",
+    "sv_sparseconv2d_bwd_dw_k", "sv_workspace_bytes_k", "sv_sparseconv2d_chunked",
     "sv_chunked_workspace_bytes", "sv_sparseconv2d_chunked_host", "sv_chunked_host_workspace_bytes",
     "sv_stage_gather", "sv_stage_scatter", "sv_status_string", "sv_version",
     "sv_xattn_fwd", "sv_xattn_bwd", "sv_xattn_workspace_bytes",
@@ -60,6 +65,7 @@ class ChunkedDesc(ctypes.Structure):
         ("X", ctypes.c_void_p), ("Wt", ctypes.c_void_p), ("bias", ctypes.c_void_p),
         ("Y", ctypes.c_void_p), ("dY", ctypes.c_void_p), ("dX", ctypes.c_void_p),
         ("dW", ctypes.c_void_p), ("db", ctypes.c_void_p), ("err_flag", ctypes.c_void_p),
+        ("ksize", ctypes.c_int32),
     ]
 
 
@@ -73,6 +79,7 @@ class ChunkedHostDesc(ctypes.Structure):
         ("X_host", ctypes.c_void_p), ("Wt", ctypes.c_void_p), ("bias", ctypes.c_void_p),
         ("Y_host", ctypes.c_void_p), ("dY_host", ctypes.c_void_p), ("dX_host", ctypes.c_void_p),
         ("dW", ctypes.c_void_p), ("db", ctypes.c_void_p), ("err_flag", ctypes.c_void_p),
+        ("ksize", ctypes.c_int32),
     ]
 
 
@@ -98,6 +105,11 @@ def load(path: str = LIB_PATH):
         "sv_sparseconv2d_bwd_dx": ([P, P, P, P, i64, i32, i32, E, E, P], E),
         "sv_sparseconv2d_bwd_dw": ([P, P, P, P, P, i64, i32, i32, E, i32, P, sz, P], E),
         "sv_workspace_bytes": ([E, i64, i32, i32, E], sz),
+        "sv_build_index_k": ([P, P, i32, i32, i32, i32, i64, P, P, P, P], E),
+        "sv_sparseconv2d_fwd_k": ([P, P, P, P, P, i64, i32, i32, i32, E, E, P, sz, P], E),
+        "sv_sparseconv2d_bwd_dx_k": ([P, P, P, P, i64, i32, i32, i32, E, E, P], E),
+        "sv_sparseconv2d_bwd_dw_k": ([P, P, P, P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
+        "sv_workspace_bytes_k": ([E, i64, i32, i32, i32, E], sz),
         "sv_sparseconv2d_chunked": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32, P, sz, P], E),
         "sv_chunked_workspace_bytes": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32], sz),
         "sv_sparseconv2d_chunked_host": ([ctypes.POINTER(ChunkedHostDesc), ctypes.c_uint32, P, sz, P, P, P], E),
@@ -222,11 +234,86 @@ def sv_sparseconv2d_bwd_dw(X, N, dY, dW, db=None, accumulate=False, workspace=No
     _check(st, "sv_sparseconv2d_bwd_dw")
 
 
+def ksize_of_taps(taps: int) -> int:
+    """K of a K x K neighbourhood from its tap count (K * K, K odd)."""
+    K = int(round(taps ** 0.5))
+    if K * K != taps or K % 2 == 0:
+        raise ValueError(f"{taps} taps is not an odd K x K neighbourhood")
+    return K
+
+
+def sv_build_index_k(coords, frame_offsets, T, H, W, K, N_out, M_out=None, err_flag=None, stream=None):
+    assert coords.dtype == torch.int32 and frame_offsets.dtype == torch.int32
+    assert N_out.dtype == torch.int32 and N_out.shape == (coords.shape[0], K * K)
+    assert frame_offsets.shape == (T + 1,)
+    if M_out is not None:
+        assert M_out.dtype == torch.int32 and M_out.numel() == T * H * W
+    if err_flag is not None:
+        assert err_flag.dtype == torch.int32 and err_flag.numel() >= 1
+    st = load().sv_build_index_k(_ptr(coords), _ptr(frame_offsets), int(T), int(H), int(W), int(K),
+                                 int(coords.shape[0]), _ptr(N_out), _ptr(M_out), _ptr(err_flag),
+                                 _stream(stream))
+    _check(st, "sv_build_index_k")
+
+
+def sv_workspace_bytes_k(op, n, K, C_in, C_out, dtype) -> int:
+    dt = SV_BF16 if dtype in (torch.bfloat16, SV_BF16, "bf16") else SV_F32
+    return int(load().sv_workspace_bytes_k(int(op), int(n), int(K), int(C_in), int(C_out), dt))
+
+
+def sv_sparseconv2d_fwd_k(X, N, Wt, bias, Y, kernel="auto", workspace=None, stream=None):
+    n, Ci = X.shape
+    taps, Co = Wt.shape[0], Wt.shape[2]
+    K = ksize_of_taps(taps)
+    assert Wt.shape == (taps, Ci, Co) and Y.shape == (n, Co) and N.shape == (n, taps)
+    assert X.dtype == Wt.dtype == Y.dtype and N.dtype == torch.int32
+    if bias is not None:
+        assert bias.dtype == X.dtype and bias.shape == (Co,)
+    need = sv_workspace_bytes_k(SV_OP_FWD, n, K, Ci, Co, X.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_sparseconv2d_fwd_k(_ptr(X), _ptr(N), _ptr(Wt), _ptr(bias), _ptr(Y), n, K, Ci, Co,
+                                      _dt(X), _kernel(kernel), _ptr(workspace), wsb, _stream(stream))
+    _check(st, "sv_sparseconv2d_fwd_k")
+
+
+def sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, kernel="auto", stream=None):
+    n, Co = dY.shape
+    taps, Ci = Wt.shape[0], Wt.shape[1]
+    K = ksize_of_taps(taps)
+    assert Wt.shape == (taps, Ci, Co) and dX.shape == (n, Ci) and N.shape == (n, taps)
+    assert dY.dtype == Wt.dtype == dX.dtype and N.dtype == torch.int32
+    st = load().sv_sparseconv2d_bwd_dx_k(_ptr(dY), _ptr(N), _ptr(Wt), _ptr(dX), n, K, Ci, Co,
+                                         _dt(dY), _kernel(kernel), _stream(stream))
+    _check(st, "sv_sparseconv2d_bwd_dx_k")
+
+
+def sv_sparseconv2d_bwd_dw_k(X, N, dY, dW, db=None, accumulate=False, workspace=None, stream=None):
+    n, Ci = X.shape
+    Co = dY.shape[1]
+    taps = dW.shape[0]
+    K = ksize_of_taps(taps)
+    assert dY.shape[0] == n and N.shape == (n, taps) and dW.shape == (taps, Ci, Co)
+    assert dW.dtype == torch.float32 and X.dtype == dY.dtype
+    if db is not None:
+        assert db.dtype == torch.float32 and db.shape == (Co,)
+    need = sv_workspace_bytes_k(SV_OP_DW, n, K, Ci, Co, X.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_sparseconv2d_bwd_dw_k(_ptr(X), _ptr(N), _ptr(dY), _ptr(dW), _ptr(db), n, K, Ci, Co,
+                                         _dt(X), 1 if accumulate else 0, _ptr(workspace), wsb,
+                                         _stream(stream))
+    _check(st, "sv_sparseconv2d_bwd_dw_k")
+
+
 def make_chunked_desc(T, H, W, coords, frame_offsets, frame_offsets_host, C_in, C_out, dtype,
                       chunk_frames, X=None, Wt=None, bias=None, Y=None, dY=None, dX=None,
-                      dW=None, db=None, err_flag=None, kernel="auto"):
+                      dW=None, db=None, err_flag=None, kernel="auto", ksize=3):
     """Build the descriptor; `frame_offsets_host` must be a CPU int32 tensor
-    (kept referenced by the returned object)."""
+    (kept referenced by the returned object).  `ksize`: K of the K x K
+    neighbourhood."""
     assert frame_offsets_host.device.type == "cpu" and frame_offsets_host.dtype == torch.int32
     fh = frame_offsets_host.contiguous()
     d = ChunkedDesc()
@@ -238,6 +325,7 @@ def make_chunked_desc(T, H, W, coords, frame_offsets, frame_offsets_host, C_in, 
     d.frame_offsets_host = fh.data_ptr()
     d.X, d.Wt, d.bias, d.Y = _ptr(X), _ptr(Wt), _ptr(bias), _ptr(Y)
     d.dY, d.dX, d.dW, d.db, d.err_flag = _ptr(dY), _ptr(dX), _ptr(dW), _ptr(db), _ptr(err_flag)
+    d.ksize = int(ksize)
     d._keep = (fh, coords, frame_offsets, X, Wt, bias, Y, dY, dX, dW, db, err_flag)
     return d
 
@@ -265,7 +353,7 @@ def _host_ptr(t: Optional[torch.Tensor]):
 
 def make_chunked_host_desc(T, H, W, coords_host, frame_offsets_host, C_in, C_out, dtype, chunk_frames,
                            X_host=None, Wt=None, bias=None, Y_host=None, dY_host=None, dX_host=None,
-                           dW=None, db=None, err_flag=None, kernel="auto"):
+                           dW=None, db=None, err_flag=None, kernel="auto", ksize=3):
     """Descriptor of the host-streamed chunk driver: coords, frame offsets
     and the per-token tensors are pinned CPU tensors; Wt, bias, dW, db and
     err_flag live on the GPU (kept referenced by the returned object)."""
@@ -279,6 +367,7 @@ def make_chunked_host_desc(T, H, W, coords_host, frame_offsets_host, C_in, C_out
     d.X_host, d.Y_host, d.dY_host, d.dX_host = _host_ptr(X_host), _host_ptr(Y_host), _host_ptr(dY_host), \
         _host_ptr(dX_host)
     d.Wt, d.bias, d.dW, d.db, d.err_flag = _ptr(Wt), _ptr(bias), _ptr(dW), _ptr(db), _ptr(err_flag)
+    d.ksize = int(ksize)
     d._keep = (coords_host, frame_offsets_host, X_host, Wt, bias, Y_host, dY_host, dX_host, dW, db, err_flag)
     return d
 
@@ -365,14 +454,17 @@ def xattn_bwd(Q, X, O, dO, lse, scale=0.0):
     return dQ, dX
 
 
-def build_index(coords, frame_offsets, T, H, W, with_map=False, check=True, stream=None):
-    """Allocate and fill N (and M); with `check`, synchronise and raise on a
-    coordinate error reported by the device flag."""
+def build_index(coords, frame_offsets, T, H, W, with_map=False, check=True, stream=None, K=3):
+    """Allocate and fill N [n, K*K] (and M); with `check`, synchronise and
+    raise on a coordinate error reported by the device flag."""
     n = coords.shape[0]
-    N = torch.empty((n, 9), dtype=torch.int32, device=coords.device)
+    N = torch.empty((n, K * K), dtype=torch.int32, device=coords.device)
     M = torch.empty((T, H, W), dtype=torch.int32, device=coords.device) if with_map else None
     flag = torch.zeros(1, dtype=torch.int32, device=coords.device)
-    sv_build_index(coords, frame_offsets, T, H, W, N, M, flag, stream)
+    if K == 3:
+        sv_build_index(coords, frame_offsets, T, H, W, N, M, flag, stream)
+    else:
+        sv_build_index_k(coords, frame_offsets, T, H, W, K, N, M, flag, stream)
     if check:
         f = int(flag.item())
         if f & SV_FLAG_BAD_OFFSETS:
@@ -384,23 +476,26 @@ def build_index(coords, frame_offsets, T, H, W, with_map=False, check=True, stre
     return (N, M) if with_map else N
 
 
+# The conveniences below take the neighbourhood from the shapes (Wt or N
+# with K*K taps); 3 x 3 goes through the original entry points.
 def sparseconv2d_fwd(X, N, Wt, bias=None, kernel="auto"):
     Y = torch.empty((X.shape[0], Wt.shape[2]), dtype=X.dtype, device=X.device)
-    sv_sparseconv2d_fwd(X, N, Wt, bias, Y, kernel)
+    (sv_sparseconv2d_fwd if Wt.shape[0] == 9 else sv_sparseconv2d_fwd_k)(X, N, Wt, bias, Y, kernel)
     return Y
 
 
 def sparseconv2d_bwd_dx(dY, N, Wt, kernel="auto"):
     dX = torch.empty((dY.shape[0], Wt.shape[1]), dtype=dY.dtype, device=dY.device)
-    sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, kernel)
+    (sv_sparseconv2d_bwd_dx if Wt.shape[0] == 9 else sv_sparseconv2d_bwd_dx_k)(dY, N, Wt, dX, kernel)
     return dX
 
 
 def sparseconv2d_bwd_dw(X, N, dY, with_db=True, workspace=None):
     Ci, Co = X.shape[1], dY.shape[1]
-    dW = torch.empty((9, Ci, Co), dtype=torch.float32, device=X.device)
+    taps = N.shape[1]
+    dW = torch.empty((taps, Ci, Co), dtype=torch.float32, device=X.device)
     db = torch.empty((Co,), dtype=torch.float32, device=X.device) if with_db else None
-    sv_sparseconv2d_bwd_dw(X, N, dY, dW, db, False, workspace)
+    (sv_sparseconv2d_bwd_dw if taps == 9 else sv_sparseconv2d_bwd_dw_k)(X, N, dY, dW, db, False, workspace)
     return dW, db
 
 

@@ -96,7 +96,7 @@ class Layer:
     coords: np.ndarray          # int32 [n], flat p = y*W + x
     frame_offsets: np.ndarray   # int32 [T+1]
     X: np.ndarray               # float32 [n, Ci] (bf16-exact when dtype == bf16)
-    Wt: np.ndarray              # float32 [9, Ci, Co]
+    Wt: np.ndarray              # float32 [taps, Ci, Co] (taps = 9 at 3 x 3)
     b: np.ndarray               # float32 [Co]
     dY: np.ndarray              # float32 [n, Co]
     dtype: str
@@ -216,10 +216,11 @@ def make_staged(key: str = "c5", scale_T: Optional[int] = None) -> Staged:
 
 def make_random_case(seed: int, T: int, H: int, W: int, keep, Ci: int, Co: int,
                      dtype: str = "f32", shuffle: bool = False,
-                     bias: bool = True) -> Layer:
+                     bias: bool = True, ksize: int = 3) -> Layer:
     """Small property-test case.  `keep` is a ratio in [0, 1], or a list of
     per-frame counts; frames may be empty.  `shuffle` permutes the tokens
-    inside each frame (any order is a valid packing)."""
+    inside each frame (any order is a valid packing).  `ksize`: K of the
+    K x K weights (K*K taps, std 1/sqrt(K*K*C_in))."""
     rs = _streams([7919, seed])
     frames = []
     for t in range(T):
@@ -231,7 +232,8 @@ def make_random_case(seed: int, T: int, H: int, W: int, keep, Ci: int, Co: int,
     coords, offs = pack(frames)
     n = coords.shape[0]
     X = _normal(rs["X"], (n, Ci), 1.0, dtype)
-    Wt = _normal(rs["W"], (9, Ci, Co), 1.0 / np.sqrt(9.0 * max(Ci, 1)), dtype)
+    taps = ksize * ksize
+    Wt = _normal(rs["W"], (taps, Ci, Co), 1.0 / np.sqrt(float(taps) * max(Ci, 1)), dtype)
     b = _normal(rs["b"], (Co,), 1.0, dtype) if bias else np.zeros((Co,), np.float32)
     dY = _normal(rs["dY"], (n, Co), 1.0, dtype)
     return Layer(T, H, W, coords, offs, X, Wt, b, dY, dtype, f"random seed={seed}")

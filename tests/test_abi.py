@@ -198,3 +198,48 @@ def test_xattn_validation_and_workspace(lib):
     for m, n, d in [(1, 1, 64), (1, 58822, 256), (4, 181248, 128), (16, 10 ** 7, 256)]:
         assert ws(0, m, n, d) <= 520 * m * (d + 2) * 4 + 1024
         assert ws(1, m, n, d) <= 520 * m * (d + 1) * 4 + 512
+
+
+def test_kxk_validation_and_workspace(lib):
+    """K x K entry points: K even or < 1 is an argument error, odd K > 7
+    unsupported; workspace sizes scale with K*K and the K = 3 forms size
+    exactly as the 3 x 3 calls."""
+    F32, BF16 = ops.SV_F32, ops.SV_BF16
+    for K, want in [(0, ops.SV_ERR_INVALID_ARG), (4, ops.SV_ERR_INVALID_ARG), (-3, ops.SV_ERR_INVALID_ARG),
+                    (9, ops.SV_ERR_UNSUPPORTED)]:
+        assert lib.sv_build_index_k(FAKE, FAKE, 1, 4, 4, K, 1, FAKE, None, None, None) == want
+        assert lib.sv_sparseconv2d_fwd_k(FAKE, FAKE, FAKE, None, FAKE, 8, K, 4, 4, F32, 0, None, 0, None) == want
+        assert lib.sv_sparseconv2d_bwd_dx_k(FAKE, FAKE, FAKE, FAKE, 8, K, 4, 4, F32, 0, None) == want
+        assert lib.sv_sparseconv2d_bwd_dw_k(FAKE, FAKE, FAKE, FAKE, None, 8, K, 4, 4, F32, 0, None, 0,
+                                            None) == want
+        assert lib.sv_workspace_bytes_k(ops.SV_OP_FWD, 8, K, 64, 64, BF16) == 0
+    # rows beyond 2^31 / (K*K)
+    assert lib.sv_sparseconv2d_fwd_k(FAKE, FAKE, FAKE, None, FAKE, (2 ** 31) // 49 + 1, 7, 4, 4, F32, 0, None, 0,
+                                     None) == ops.SV_ERR_INVALID_ARG
+    # the MFMA forward needs K*K repacked weight taps
+    for K in (1, 3, 5, 7):
+        b = lib.sv_workspace_bytes_k(ops.SV_OP_FWD, 8, K, 64, 64, BF16)
+        assert K * K * 64 * 64 * 2 <= b < K * K * 64 * 64 * 2 + 256
+        assert lib.sv_sparseconv2d_fwd_k(FAKE, FAKE, FAKE, None, FAKE, 8, K, 64, 64, BF16, 0, None, 0,
+                                         None) == ops.SV_ERR_WORKSPACE
+    for op in (ops.SV_OP_FWD, ops.SV_OP_DX, ops.SV_OP_DW):
+        for n, C in [(0, 64), (22656, 256), (181248, 128)]:
+            assert lib.sv_workspace_bytes_k(op, n, 3, C, C, BF16) == lib.sv_workspace_bytes(op, n, C, C, BF16)
+    # dW partials stay bounded by 64 slices of K*K taps
+    for K in (1, 5, 7):
+        b = lib.sv_workspace_bytes_k(ops.SV_OP_DW, 22656, K, 256, 256, BF16)
+        assert 0 < b <= 64 * K * K * 256 * 256 * 4 + 64 * 256 * 4 + 512
+    # chunk descriptors: ksize 0 reads as 3, 5 needs more N table, 9 / 2 rejected
+    passes = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
+    offs = (np.arange(257, dtype=np.int32) * 59).astype(np.int32)
+    d = _desc(256, offs)
+    base = lib.sv_chunked_workspace_bytes(ctypes.byref(d), passes)
+    d.ksize = 3
+    assert lib.sv_chunked_workspace_bytes(ctypes.byref(d), passes) == base
+    d.ksize = 5
+    assert lib.sv_chunked_workspace_bytes(ctypes.byref(d), passes) > base
+    d.ksize = 2
+    assert lib.sv_chunked_workspace_bytes(ctypes.byref(d), passes) == 0
+    assert lib.sv_sparseconv2d_chunked(ctypes.byref(d), passes, None, 0, None) == ops.SV_ERR_INVALID_ARG
+    d.ksize = 9
+    assert lib.sv_sparseconv2d_chunked(ctypes.byref(d), passes, None, 0, None) == ops.SV_ERR_UNSUPPORTED
