@@ -31,6 +31,16 @@
  *                     scaled by 1/sqrt(d) unless another scale is given.
  *                     The backward is the chain rule through scores, row
  *                     softmax and the weighted sum.
+ *   orc_adapter_fwd   The bottleneck adapter (Overall Architecture: adapters
+ *   orc_adapter_bwd   with sparse spatial convolutions run on the pruned
+ *                     tokens; Key Design 3: the visual features inside are
+ *                     down-projected).  No further internals are printed;
+ *                     the reading is the plain residual bottleneck
+ *                     H1 = X Wd + bd, H2 = conv_K(H1) + bc,
+ *                     Y = X + H2 Wu + bu, no activation.  A projection is
+ *                     the K x K layer above with one tap and N[k][0] = k.
+ *                     The backward is the chain rule through the three
+ *                     layers and the residual.
  *
  * Readings of points the page leaves open:
  *   - K odd; tap order j = K*(dy+r) + (dx+r) with r = K/2 and dy, dx in
@@ -368,4 +378,60 @@ void orc_xattn_bwd(const double *Q, const double *X, const double *dO,
         }
     free(P);
     free(dS);
+}
+
+/* ------------------------------------------------------------------------
+ * Bottleneck adapter: down-projection C -> r, K x K SparseConv2D r -> r,
+ * up-projection r -> C, residual.  Wd [C][r], Wc [taps][r][r], Wu [r][C],
+ * biases nullable; H1, H2 [n][r] and Y [n][C] written. */
+static int32_t *identity_table(int64_t n)
+{
+    int32_t *I = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    for (int64_t k = 0; k < n; ++k) I[k] = (int32_t)k;
+    return I;
+}
+
+void orc_adapter_fwd(const double *X, const int32_t *N, int64_t n, int32_t taps, int32_t C, int32_t r,
+                     const double *Wd, const double *bd, const double *Wc, const double *bc,
+                     const double *Wu, const double *bu, double *H1, double *H2, double *Y)
+{
+    int32_t *I = identity_table(n);
+    orc_fwd(X, I, Wd, bd, H1, n, C, r, 1);
+    orc_fwd(H1, N, Wc, bc, H2, n, r, r, taps);
+    orc_fwd(H2, I, Wu, bu, Y, n, r, C, 1);
+    for (int64_t e = 0; e < n * C; ++e) Y[e] += X[e];
+    free(I);
+}
+
+/* Gradients of <Y, dY>:
+ *   dWu = H2^T dY, dbu = sum_k dY[k], dH2 = dY Wu^T;
+ *   dWc, dbc, dH1: the K x K layer's backward at (H1, dH2);
+ *   dWd = X^T dH1, dbd = sum_k dH1[k], dX = dY + dH1 Wd^T.
+ * H1 and H2 are recomputed from X. */
+void orc_adapter_bwd(const double *X, const int32_t *N, int64_t n, int32_t taps, int32_t C, int32_t r,
+                     const double *Wd, const double *bd, const double *Wc, const double *bc,
+                     const double *Wu, const double *dY, double *dX, double *dWd, double *dbd,
+                     double *dWc, double *dbc, double *dWu, double *dbu)
+{
+    const size_t hr = sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)r;
+    double *H1 = (double *)malloc(hr), *H2 = (double *)malloc(hr);
+    double *dH1 = (double *)malloc(hr), *dH2 = (double *)malloc(hr);
+    int32_t *I = identity_table(n);
+    orc_fwd(X, I, Wd, bd, H1, n, C, r, 1);
+    orc_fwd(H1, N, Wc, bc, H2, n, r, r, taps);
+    orc_bwd_dw(H2, I, dY, dWu, n, r, C, 1);
+    orc_bwd_db(dY, dbu, n, C);
+    orc_bwd_dx(dY, I, Wu, dH2, n, r, C, 1);
+    orc_bwd_dw(H1, N, dH2, dWc, n, r, r, taps);
+    orc_bwd_db(dH2, dbc, n, r);
+    orc_bwd_dx(dH2, N, Wc, dH1, n, r, r, taps);
+    orc_bwd_dw(X, I, dH1, dWd, n, C, r, 1);
+    orc_bwd_db(dH1, dbd, n, r);
+    orc_bwd_dx(dH1, I, Wd, dX, n, C, r, 1);
+    for (int64_t e = 0; e < n * C; ++e) dX[e] += dY[e];
+    free(I);
+    free(H1);
+    free(H2);
+    free(dH1);
+    free(dH2);
 }

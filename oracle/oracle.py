@@ -9,7 +9,8 @@ Every function takes numpy arrays, converts floating inputs to float64
 (exactly: bf16 and fp32 values are representable in float64) and returns
 float64 results.  See ``oracle.c`` for the definitions and the passages of
 "SV-TAD: Native Sparse Convolutions for Efficient Temporal Action Detection"
-(paper notes page, Key Designs 1 and 2) that each one follows.
+(paper notes page: Overall Architecture, Key Designs 1 to 3) that each one
+follows.
 """
 from __future__ import annotations
 
@@ -67,9 +68,11 @@ class Oracle:
         lib.orc_bwd_db.argtypes = [P, P, i64, i32]
         lib.orc_xattn_fwd.argtypes = [P, P, P, P, i64, i64, i32, ctypes.c_double]
         lib.orc_xattn_bwd.argtypes = [P, P, P, P, P, i64, i64, i32, ctypes.c_double]
+        lib.orc_adapter_fwd.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+        lib.orc_adapter_bwd.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P]
         for f in ("orc_fwd", "orc_fwd_rows", "orc_bwd_dx", "orc_bwd_dx_rows",
                   "orc_bwd_dx_scatter", "orc_bwd_dw", "orc_bwd_dw_rows", "orc_bwd_db",
-                  "orc_xattn_fwd", "orc_xattn_bwd"):
+                  "orc_xattn_fwd", "orc_xattn_bwd", "orc_adapter_fwd", "orc_adapter_bwd"):
             getattr(lib, f).restype = None
         self.lib = lib
         self.path = path
@@ -182,6 +185,37 @@ class Oracle:
         self.lib.orc_xattn_bwd(_p(Q), _p(Xp), _p(dO), _p(dQ), _p(dX), m, n, d, sc)
         return dQ, dX[:n]
 
+    def adapter_fwd(self, X, N, Wd, bd, Wc, bc, Wu, bu):
+        """Bottleneck adapter: returns (Y [n,C], H1 [n,r], H2 [n,r]) for
+        H1 = X Wd + bd, H2 = conv_K(H1; N, Wc) + bc, Y = X + H2 Wu + bu.
+        Wd [C,r], Wc [K*K,r,r], Wu [r,C]; biases may be None."""
+        X, N, Wd, Wc, Wu = _f64(X), _i32(N), _f64(Wd), _f64(Wc), _f64(Wu)
+        n, C = X.shape
+        r = Wd.shape[1]
+        assert Wd.shape == (C, r) and Wc.shape == (N.shape[1], r, r) and Wu.shape == (r, C)
+        bd, bc, bu = (None if v is None else _f64(v) for v in (bd, bc, bu))
+        H1 = np.empty((n, r), dtype=np.float64)
+        H2 = np.empty((n, r), dtype=np.float64)
+        Y = np.empty((n, C), dtype=np.float64)
+        self.lib.orc_adapter_fwd(_p(X), _p(N), n, N.shape[1], C, r, _p(Wd), _p(bd), _p(Wc), _p(bc), _p(Wu),
+                                 _p(bu), _p(H1), _p(H2), _p(Y))
+        return Y, H1, H2
+
+    def adapter_bwd(self, X, N, Wd, bd, Wc, bc, Wu, dY):
+        """Gradients of <Y, dY> for Y = adapter_fwd(...): a dict with dX,
+        dWd, dbd, dWc, dbc, dWu, dbu."""
+        X, N, Wd, Wc, Wu, dY = _f64(X), _i32(N), _f64(Wd), _f64(Wc), _f64(Wu), _f64(dY)
+        n, C = X.shape
+        r = Wd.shape[1]
+        taps = N.shape[1]
+        assert Wd.shape == (C, r) and Wc.shape == (taps, r, r) and Wu.shape == (r, C) and dY.shape == (n, C)
+        bd, bc = (None if v is None else _f64(v) for v in (bd, bc))
+        g = {"dX": np.empty((n, C)), "dWd": np.empty((C, r)), "dbd": np.empty(r), "dWc": np.empty((taps, r, r)),
+             "dbc": np.empty(r), "dWu": np.empty((r, C)), "dbu": np.empty(C)}
+        self.lib.orc_adapter_bwd(_p(X), _p(N), n, taps, C, r, _p(Wd), _p(bd), _p(Wc), _p(bc), _p(Wu), _p(dY),
+                                 *(_p(g[k]) for k in ("dX", "dWd", "dbd", "dWc", "dbc", "dWu", "dbu")))
+        return g
+
 
 def _taps(N, Wt):
     """Number of taps of a call: the columns of N, which must match the
@@ -257,6 +291,14 @@ def bwd_dw_rows(X, N, dY, rows):
 
 def bwd_db(dY):
     return default().bwd_db(dY)
+
+
+def adapter_fwd(X, N, Wd, bd, Wc, bc, Wu, bu):
+    return default().adapter_fwd(X, N, Wd, bd, Wc, bc, Wu, bu)
+
+
+def adapter_bwd(X, N, Wd, bd, Wc, bc, Wu, dY):
+    return default().adapter_bwd(X, N, Wd, bd, Wc, bc, Wu, dY)
 
 
 def xattn_fwd(Q, X, scale=None):

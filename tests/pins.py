@@ -470,6 +470,88 @@ def pin_kxk_index_and_dense(orc):
     assert st != 0, "even K must be rejected"
 
 
+# ------------------------------------------------------- bottleneck adapter
+def _adapter_case(c, K, r, seed):
+    L = case_layer(c)
+    C = L.X.shape[1]
+    rng = np.random.default_rng(seed)
+    P = {"Wd": rng.standard_normal((C, r)), "bd": rng.standard_normal(r),
+         "Wc": rng.standard_normal((K * K, r, r)), "bc": rng.standard_normal(r),
+         "Wu": rng.standard_normal((r, C)), "bu": rng.standard_normal(C)}
+    dY = rng.standard_normal((L.n, C))
+    return L, P, dY
+
+
+def adapter_dense_torch(L, P, dY):
+    """The adapter on the dense grid in torch float64: kept tokens scattered
+    into a zero T x H x W grid, the down-projection applied per cell and the
+    pruned cells zeroed again (a pruned neighbour is zero padding), an
+    ordinary zero-padded K x K conv2d, the kept cells gathered, the
+    up-projection and the residual; autograd of <Y, dY> for the gradients."""
+    T, H, W = L.T, L.H, L.W
+    t = {k: torch.tensor(np.asarray(v, dtype=np.float64), requires_grad=True) for k, v in P.items()}
+    X = torch.tensor(np.asarray(L.X, dtype=np.float64), requires_grad=True)
+    C, r = X.shape[1], t["Wd"].shape[1]
+    f = torch.as_tensor(frame_of(L.frame_offsets))
+    p = torch.as_tensor(np.asarray(L.coords, dtype=np.int64))
+    grid = torch.zeros(T, H * W, C, dtype=torch.float64).index_put((f, p), X)
+    mask = torch.zeros(T, H * W, 1, dtype=torch.float64).index_put((f, p), torch.ones(L.n, 1, dtype=torch.float64))
+    h1 = (grid @ t["Wd"] + t["bd"]) * mask
+    wc = t["Wc"].reshape(int(round(t["Wc"].shape[0] ** 0.5)), -1, r, r).permute(3, 2, 0, 1)
+    h2 = F.conv2d(h1.reshape(T, H, W, r).permute(0, 3, 1, 2), wc, padding=wc.shape[2] // 2)
+    h2 = h2.permute(0, 2, 3, 1).reshape(T, H * W, r)[f, p] + t["bc"]
+    Y = X + h2 @ t["Wu"] + t["bu"]
+    (Y * torch.as_tensor(np.asarray(dY, dtype=np.float64))).sum().backward()
+    g = {"d" + k: v.grad.numpy() for k, v in t.items()}
+    g["dX"] = X.grad.numpy()
+    return Y.detach().numpy(), h1[f, p].detach().numpy(), h2.detach().numpy(), g
+
+
+def pin_adapter_dense_torch(orc):
+    """Adapter forward (Y, H1, H2) and backward (dX and all six parameter
+    gradients) against the dense-grid torch reference, K = 1, 3, 5."""
+    for K in (1, 3, 5):
+        for i, c in enumerate((CASES[1], CASES[3], CASES[5])):
+            L, P, dY = _adapter_case(c, K, r=2 + i, seed=300 + 10 * K + i)
+            st, N, _ = orc.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K=K)
+            Yr, H1r, H2r, gr = adapter_dense_torch(L, P, dY)
+            Y, H1, H2 = orc.adapter_fwd(L.X, N, P["Wd"], P["bd"], P["Wc"], P["bc"], P["Wu"], P["bu"])
+            close(Y, Yr, 1e-12, f"adapter K={K} Y {c}")
+            close(H1, H1r, 1e-12, f"adapter K={K} H1 {c}")
+            close(H2, H2r, 1e-12, f"adapter K={K} H2 {c}")
+            g = orc.adapter_bwd(L.X, N, P["Wd"], P["bd"], P["Wc"], P["bc"], P["Wu"], dY)
+            for k in ("dX", "dWd", "dbd", "dWc", "dbc", "dWu", "dbu"):
+                close(g[k], gr[k], 1e-12, f"adapter K={K} {k} {c}")
+
+
+def pin_adapter_special_cases(orc):
+    """Zero up-projection: Y = X exactly, dX = dY exactly, the down and conv
+    gradients vanish and dWu = H2^T dY.  Centre-tap identity conv: the adapter
+    is X + (X Wd + bd) Wu + bu, a closed form of two matrix products."""
+    L, P, dY = _adapter_case(CASES[3], 3, r=3, seed=401)
+    st, N, _ = orc.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    Z = np.zeros_like(P["Wu"])
+    Y, H1, H2 = orc.adapter_fwd(L.X, N, P["Wd"], P["bd"], P["Wc"], P["bc"], Z, None)
+    assert np.array_equal(Y, np.asarray(L.X, dtype=np.float64)), "zero up-projection: Y must be X"
+    g = orc.adapter_bwd(L.X, N, P["Wd"], P["bd"], P["Wc"], P["bc"], Z, dY)
+    assert np.array_equal(g["dX"], dY), "zero up-projection: dX must be dY"
+    for k in ("dWd", "dbd", "dWc", "dbc"):
+        assert not np.any(g[k]), f"zero up-projection: {k} must vanish"
+    close(g["dWu"], H2.T @ dY, 1e-12, "zero up-projection dWu")
+    close(g["dbu"], dY.sum(0), 1e-12, "zero up-projection dbu")
+    r = P["Wd"].shape[1]
+    Wc = np.zeros((9, r, r))
+    Wc[4] = np.eye(r)
+    X = np.asarray(L.X, dtype=np.float64)
+    Y, H1, H2 = orc.adapter_fwd(X, N, P["Wd"], P["bd"], Wc, None, P["Wu"], P["bu"])
+    close(Y, X + (X @ P["Wd"] + P["bd"]) @ P["Wu"] + P["bu"], 1e-12, "centre-tap identity conv")
+    close(H2, H1, 0.0, "centre-tap identity conv: H2 = H1")
+    g = orc.adapter_bwd(X, N, P["Wd"], P["bd"], Wc, None, P["Wu"], dY)
+    dH = dY @ P["Wu"].T
+    close(g["dX"], dY + dH @ P["Wd"].T, 1e-12, "centre-tap identity conv dX")
+    close(g["dWd"], X.T @ dH, 1e-12, "centre-tap identity conv dWd")
+
+
 ALL_PINS = [
     pin_golden_hand_3x4,
     pin_golden_frames_2x2,
@@ -489,4 +571,6 @@ ALL_PINS = [
     pin_xattn_torch,
     pin_xattn_finite_differences,
     pin_xattn_permutation_and_extremes,
+    pin_adapter_dense_torch,
+    pin_adapter_special_cases,
 ]

@@ -52,6 +52,17 @@ MUTANTS = [
     ("cross-attention softmax without the max shift",
      "for (int64_t j = 0; j < n; ++j) sum += exp(srow[j] - mx);\n        for (int64_t j = 0; j < n; ++j) {\n            double pj = exp(srow[j] - mx) / sum;",
      "for (int64_t j = 0; j < n; ++j) sum += exp(srow[j]);\n        for (int64_t j = 0; j < n; ++j) {\n            double pj = exp(srow[j]) / sum;", 0),
+    ("adapter forward without the residual",
+     "for (int64_t e = 0; e < n * C; ++e) Y[e] += X[e];", "", 0),
+    ("adapter backward without the residual's gradient",
+     "for (int64_t e = 0; e < n * C; ++e) dX[e] += dY[e];", "", 0),
+    ("adapter dWu from the down-projected features",
+     "orc_bwd_dw(H2, I, dY, dWu, n, r, C, 1);", "orc_bwd_dw(H1, I, dY, dWu, n, r, C, 1);", 0),
+    ("adapter dbd from the upstream gradient",
+     "orc_bwd_db(dH1, dbd, n, r);", "orc_bwd_db(dH2, dbd, n, r);", 0),
+    ("adapter conv on the input instead of the down-projection",
+     "orc_fwd(H1, N, Wc, bc, H2, n, r, r, taps);\n    orc_fwd(H2, I, Wu, bu, Y, n, r, C, 1);",
+     "orc_fwd(X, N, Wc, bc, H2, n, r, r, taps);\n    orc_fwd(H2, I, Wu, bu, Y, n, r, C, 1);", 0),
     ("cross-attention lse without the shift added back",
      "lse[q] = mx + log(sum);", "lse[q] = log(sum);", 0),
     ("cross-attention dX drops the value term",
