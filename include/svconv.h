@@ -277,6 +277,53 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc *desc, uint32_
  * descriptors. */
 size_t sv_chunked_host_workspace_bytes(const sv_chunked_host_desc *desc, uint32_t passes);
 
+/* Bottleneck adapter ("SV-TAD: Native Sparse Convolutions for Efficient
+ * Temporal Action Detection", Overall Architecture and Key Design 3: lightweight
+ * bottleneck adapters run on the pruned tokens; the visual features inside
+ * them are down-projected).  The page prints no further internals; read as
+ * the plain residual bottleneck
+ *   H1 = X Wd + bd                    down-projection C -> r (a 1 x 1 SparseConv2D)
+ *   H2 = SparseConv2D_KxK(H1) + bc    r -> r over the neighbour table N
+ *   Y  = X + H2 Wu + bu               up-projection r -> C; the residual is
+ *                                     added in the projection's kernel,
+ *                                     before its one rounding
+ * with no activation (the page names none).  Layouts, row-major, all in
+ * `dtype` except N: X, Y [n][C]; N [n][K*K] (sv_build_index_k);
+ * Wd [C][r] (a [1][C][r] weight), Wc [K*K][r][r], Wu [r][C]; biases bd [r],
+ * bc [r], bu [C], each nullable; H1, H2 [n][r] written, kept for the
+ * backward (H1 is also what the cross-attention below attends over).
+ * The three layers run the kernels of the calls above (MFMA when `kernel`
+ * and the shapes allow, per layer; SV_ERR_UNSUPPORTED if MFMA is forced and
+ * a layer does not fit), in order on `stream`.  Workspace:
+ * sv_adapter_workspace_bytes(0, ...) bytes, 256-byte aligned (an identity
+ * table for the projections and the repacked weights).  K as in the _k
+ * calls. */
+sv_status sv_adapter_fwd(const void *X, const int32_t *N, int64_t n, int32_t K, int32_t C, int32_t r,
+                         const void *Wd, const void *bd, const void *Wc, const void *bc,
+                         const void *Wu, const void *bu, void *H1, void *H2, void *Y,
+                         sv_dtype dtype, sv_kernel kernel, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Adapter backward for an upstream gradient dY [n][C], given the forward's
+ * H1 and H2:
+ *   dWu = H2^T dY,  dbu = sum_k dY[k];      dH2 = dY Wu^T
+ *   dWc, dbc = the K x K weight gradient of (H1, dH2);  dH1 = its input gradient
+ *   dWd = X^T dH1,  dbd = sum_k dH1[k];     dX  = dY + dH1 Wd^T
+ * (the last sum in one kernel, before its one rounding).  dW* and db* are
+ * fp32, overwritten; db* nullable.  dH2 and dH1 are held in the workspace in
+ * `dtype` (sv_adapter_workspace_bytes(1, ...) bytes, 256-byte aligned).
+ * Deterministic. */
+sv_status sv_adapter_bwd(const void *X, const int32_t *N, int64_t n, int32_t K, int32_t C, int32_t r,
+                         const void *Wd, const void *Wc, const void *Wu,
+                         const void *H1, const void *H2, const void *dY,
+                         void *dX, float *dWd, float *dbd, float *dWc, float *dbc,
+                         float *dWu, float *dbu, sv_dtype dtype, sv_kernel kernel,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* Workspace bytes of sv_adapter_fwd (backward == 0) or sv_adapter_bwd;
+ * 0 for invalid sizes.  Depends only on the arguments. */
+size_t sv_adapter_workspace_bytes(int32_t backward, int64_t n, int32_t K, int32_t C, int32_t r,
+                                  sv_dtype dtype);
+
 /* Asymmetric cross-attention (Key Design 3): auxiliary tokens Q [m][d]
  * (such as the CLS token) query the down-projected sparse visual tokens
  * X [n][d], which serve as keys and as values; only the auxiliary tokens are

@@ -48,21 +48,23 @@ sv_status conv_args_ok(int64_t n, int taps, int32_t Ci, int32_t Co, sv_dtype dt,
 }
 
 // Forward with the repacked weights already in `V` (MFMA path) or straight
-// from Wt (VALU path).
+// from Wt (VALU path); R: nullable residual added to Y.
 sv_status run_fwd_prepared(bool mfma, const void* X, const int32_t* N, const void* Wt, const void* V,
                            const void* bias, void* Y, int64_t n, int32_t Ci, int32_t Co, int taps,
-                           sv_dtype dt, hipStream_t s) {
+                           sv_dtype dt, hipStream_t s, const void* R = nullptr) {
     if (n == 0) return SV_OK;
     if (mfma)
         return hip_status(launch_conv_mfma_packed(static_cast<const uint16_t*>(X), N,
                                                   static_cast<const uint16_t*>(V),
                                                   static_cast<const uint16_t*>(bias),
+                                                  static_cast<const uint16_t*>(R),
                                                   static_cast<uint16_t*>(Y), n, Ci, Co, taps, s));
-    return hip_status(launch_conv_valu(dt == SV_BF16, false, X, N, Wt, bias, Y, n, Ci, Co, taps, s));
+    return hip_status(launch_conv_valu(dt == SV_BF16, false, X, N, Wt, bias, R, Y, n, Ci, Co, taps, s));
 }
 
+// Input gradient; R: nullable residual added to dX.
 sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int64_t n, int32_t Ci,
-                 int32_t Co, int taps, sv_dtype dt, sv_kernel kernel, hipStream_t s) {
+                 int32_t Co, int taps, sv_dtype dt, sv_kernel kernel, hipStream_t s, const void* R = nullptr) {
     bool mfma = false;
     sv_status st = choose(kernel, dt, true, Ci, Co, n, taps, &mfma);
     if (st != SV_OK) return st;
@@ -70,8 +72,9 @@ sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int
     if (mfma)
         return hip_status(launch_conv_mfma_packed(static_cast<const uint16_t*>(dY), N,
                                                   static_cast<const uint16_t*>(Wt), nullptr,
+                                                  static_cast<const uint16_t*>(R),
                                                   static_cast<uint16_t*>(dX), n, Co, Ci, taps, s));
-    return hip_status(launch_conv_valu(dt == SV_BF16, true, dY, N, Wt, nullptr, dX, n, Ci, Co, taps, s));
+    return hip_status(launch_conv_valu(dt == SV_BF16, true, dY, N, Wt, nullptr, R, dX, n, Ci, Co, taps, s));
 }
 
 // Bytes of repacked weights the forward needs when the MFMA kernel may run.
@@ -559,6 +562,132 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
     const sv_status result = run();
     for (int i = 0; i < 3 * kSets + 1; ++i) (void)hipEventDestroy(ev[i]);
     return result;
+}
+
+// ------------------------------------------------------ bottleneck adapter
+namespace {
+
+// Workspace of the adapter: the identity table of the two projections, then
+// either the shared repack region of the three forwards or dH2 | dH1 | the
+// shared dW region of the three weight gradients (the passes run in order
+// on one stream, so one region serves them all).
+struct AdapterLayout {
+    int taps = 0;
+    size_t id_bytes = 0, h_bytes = 0, rest_bytes = 0, total = 0;
+};
+
+sv_status adapter_layout(bool backward, int64_t n, int32_t K, int32_t C, int32_t r, sv_dtype dt, AdapterLayout* L) {
+    sv_status st = taps_of(K, &L->taps);
+    if (st != SV_OK) return st;
+    if (n < 0 || n > max_rows(L->taps) || C <= 0 || r <= 0 || !valid_dtype(dt)) return SV_ERR_INVALID_ARG;
+    const size_t es = dt == SV_BF16 ? 2 : 4;
+    L->id_bytes = align_up(static_cast<size_t>(n) * sizeof(int32_t));
+    if (!backward) {
+        L->h_bytes = 0;
+        L->rest_bytes = std::max({fwd_ws_bytes(C, r, dt, n, 1), fwd_ws_bytes(r, r, dt, n, L->taps),
+                                  fwd_ws_bytes(r, C, dt, n, 1)});
+    } else {
+        L->h_bytes = align_up(static_cast<size_t>(n) * r * es);
+        const bool bf = dt == SV_BF16;
+        L->rest_bytes = std::max({dw_workspace_bytes(plan_dw(n, r, C, bf, 1)),
+                                  dw_workspace_bytes(plan_dw(n, r, r, bf, L->taps)),
+                                  dw_workspace_bytes(plan_dw(n, C, r, bf, 1))});
+    }
+    L->total = L->id_bytes + 2 * L->h_bytes + align_up(L->rest_bytes);
+    return SV_OK;
+}
+
+// One forward pass of a layer (repack into `V` when the MFMA kernel runs).
+sv_status adapter_layer_fwd(const void* X, const int32_t* N, const void* Wt, const void* bias, const void* R,
+                            void* Y, int64_t n, int32_t Ci, int32_t Co, int taps, sv_dtype dt, sv_kernel kernel,
+                            void* V, hipStream_t s) {
+    bool mfma = false;
+    sv_status st = choose(kernel, dt, false, Ci, Co, n, taps, &mfma);
+    if (st != SV_OK) return st;
+    if (mfma) {
+        st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(V), Ci, Co,
+                                          taps, s));
+        if (st != SV_OK) return st;
+    }
+    return run_fwd_prepared(mfma, X, N, Wt, V, bias, Y, n, Ci, Co, taps, dt, s, R);
+}
+
+}  // namespace
+
+size_t sv_adapter_workspace_bytes(int32_t backward, int64_t n, int32_t K, int32_t C, int32_t r, sv_dtype dtype) {
+    AdapterLayout L;
+    if (adapter_layout(backward != 0, n, K, C, r, dtype, &L) != SV_OK) return 0;
+    return L.total;
+}
+
+sv_status sv_adapter_fwd(const void* X, const int32_t* N, int64_t n, int32_t K, int32_t C, int32_t r,
+                         const void* Wd, const void* bd, const void* Wc, const void* bc, const void* Wu,
+                         const void* bu, void* H1, void* H2, void* Y, sv_dtype dtype, sv_kernel kernel,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    AdapterLayout L;
+    sv_status st = adapter_layout(false, n, K, C, r, dtype, &L);
+    if (st != SV_OK) return st;
+    if (!valid_kernel(kernel)) return SV_ERR_INVALID_ARG;
+    if (!Wd || !Wc || !Wu || (n > 0 && (!X || !N || !H1 || !H2 || !Y))) return SV_ERR_INVALID_ARG;
+    bool m;
+    // every pass must fit the requested kernel before anything is enqueued
+    if (choose(kernel, dtype, false, C, r, n, 1, &m) != SV_OK ||
+        choose(kernel, dtype, false, r, r, n, L.taps, &m) != SV_OK ||
+        choose(kernel, dtype, false, r, C, n, 1, &m) != SV_OK)
+        return SV_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return SV_ERR_INVALID_ARG;
+    if (n == 0) return SV_OK;
+    int32_t* I = static_cast<int32_t*>(workspace);
+    void* V = static_cast<char*>(workspace) + L.id_bytes;
+    if ((st = hip_status(launch_iota(I, n, stream))) != SV_OK) return st;
+    if ((st = adapter_layer_fwd(X, I, Wd, bd, nullptr, H1, n, C, r, 1, dtype, kernel, V, stream)) != SV_OK)
+        return st;
+    if ((st = adapter_layer_fwd(H1, N, Wc, bc, nullptr, H2, n, r, r, L.taps, dtype, kernel, V, stream)) != SV_OK)
+        return st;
+    return adapter_layer_fwd(H2, I, Wu, bu, X, Y, n, r, C, 1, dtype, kernel, V, stream);
+}
+
+sv_status sv_adapter_bwd(const void* X, const int32_t* N, int64_t n, int32_t K, int32_t C, int32_t r,
+                         const void* Wd, const void* Wc, const void* Wu, const void* H1, const void* H2,
+                         const void* dY, void* dX, float* dWd, float* dbd, float* dWc, float* dbc, float* dWu,
+                         float* dbu, sv_dtype dtype, sv_kernel kernel, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    AdapterLayout L;
+    sv_status st = adapter_layout(true, n, K, C, r, dtype, &L);
+    if (st != SV_OK) return st;
+    if (!valid_kernel(kernel)) return SV_ERR_INVALID_ARG;
+    if (!Wd || !Wc || !Wu || !dWd || !dWc || !dWu) return SV_ERR_INVALID_ARG;
+    if (n > 0 && (!X || !N || !H1 || !H2 || !dY || !dX)) return SV_ERR_INVALID_ARG;
+    bool m;
+    if (choose(kernel, dtype, true, r, C, n, 1, &m) != SV_OK ||
+        choose(kernel, dtype, true, r, r, n, L.taps, &m) != SV_OK ||
+        choose(kernel, dtype, true, C, r, n, 1, &m) != SV_OK)
+        return SV_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return SV_ERR_INVALID_ARG;
+    const bool bf = dtype == SV_BF16;
+    char* base = static_cast<char*>(workspace);
+    int32_t* I = reinterpret_cast<int32_t*>(base);
+    void* dH2 = base + L.id_bytes;
+    void* dH1 = base + L.id_bytes + L.h_bytes;
+    void* dws = base + L.id_bytes + 2 * L.h_bytes;
+    if ((st = hip_status(launch_iota(I, n, stream))) != SV_OK) return st;
+    // up-projection: dWu, dbu, then dH2 = dY Wu^T
+    if ((st = hip_status(launch_dw(plan_dw(n, r, C, bf, 1), bf, H2, I, dY, dWu, dbu, n, r, C, 0, dws, stream))) !=
+        SV_OK)
+        return st;
+    if ((st = run_dx(dY, I, Wu, dH2, n, r, C, 1, dtype, kernel, stream)) != SV_OK) return st;
+    // K x K convolution: dWc, dbc, then dH1
+    if ((st = hip_status(launch_dw(plan_dw(n, r, r, bf, L.taps), bf, H1, N, dH2, dWc, dbc, n, r, r, 0, dws,
+                                   stream))) != SV_OK)
+        return st;
+    if ((st = run_dx(dH2, N, Wc, dH1, n, r, r, L.taps, dtype, kernel, stream)) != SV_OK) return st;
+    // down-projection: dWd, dbd, then dX = dY + dH1 Wd^T
+    if ((st = hip_status(launch_dw(plan_dw(n, C, r, bf, 1), bf, X, I, dH1, dWd, dbd, n, C, r, 0, dws, stream))) !=
+        SV_OK)
+        return st;
+    return run_dx(dH1, I, Wd, dX, n, C, r, 1, dtype, kernel, stream, dY);
 }
 
 // ------------------------------------------------------ cross-attention

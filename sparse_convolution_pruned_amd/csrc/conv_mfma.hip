@@ -7,7 +7,7 @@
 //
 // One kernel serves both passes and every K x K neighbourhood it is built
 // for (TAPS = K * K = 1, 9, 25 or 49; P = TAPS - 1).  It computes
-//     out[k][c] = sum_j sum_i A[N[k, j]][i] * B[P - j][c][i]  (+ bias[c])
+//     out[k][c] = sum_j sum_i A[N[k, j]][i] * B[P - j][c][i]  (+ bias[c]) (+ R[k][c])
 // with B stored [tap][output channel][contracted channel]:
 //   input gradient: A = dY, B = Wt itself ([TAPS][C_in][C_out]: tap P-j of
 //     the weights meets the row gathered through tap j, the mirror of the
@@ -83,13 +83,15 @@ __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const
             for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[ks][mb], b[ks][nb], acc[mb][nb]);
 }
 
-// A [n][K], B [TAPS][NO][K], bias [NO] (nullable), out [n][NO]; K % 32 == 0,
+// A [n][K], B [TAPS][NO][K], bias [NO] (nullable), res [n][NO] (nullable: a
+// residual added before the one rounding to bf16), out [n][NO]; K % 32 == 0,
 // NO % 16 == 0.
-template <int TAPS>
+template <int TAPS, bool RES>
 __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uint16_t* __restrict__ A,
                                                       const int32_t* __restrict__ Nt,
                                                       const uint16_t* __restrict__ B,
                                                       const uint16_t* __restrict__ bias,
+                                                      const uint16_t* __restrict__ res,
                                                       uint16_t* __restrict__ out, int n, int K, int NO) {
     __shared__ __align__(16) uint16_t sA[(CM_WIN + 1) * CM_LDA];
     __shared__ __align__(16) uint16_t sB[2][CM_SB];   // weight tiles, written by direct loads
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
         }
     }
 
-    // ---- epilogue: bias, round to bf16, stage the 128 x 128 tile in LDS
+    // ---- epilogue: bias (and residual), round to bf16, stage the 128 x 128 tile in LDS
     // (rows 0-63 over the window, rows 64-127 over the weight buffers), then
     // write whole 16-byte row pieces.
     constexpr int OLD = CM_BN + 8;      // 272-byte pitch: rows 4 apart in opposite bank halves
@@ -283,18 +285,40 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     uint16_t* const sOutLo = sA;
     uint16_t* const sOutHi = &sB[0][0];
     __syncthreads();
+    if (!RES) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int cl = wn * 64 + nb * 32 + l32;
-        const float bv = (bias && n0 + cl < NO) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
+        for (int nb = 0; nb < 2; ++nb) {
+            const int cl = wn * 64 + nb * 32 + l32;
+            const float bv = (bias && n0 + cl < NO) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+                for (int g = 0; g < 4; ++g)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    (wm ? sOutHi : sOutLo)[(mb * 32 + g * 8 + lhi * 4 + q) * OLD + cl] =
-                        f32_to_bf16(acc[mb][nb][g * 4 + q] + bv);
+                    for (int q = 0; q < 4; ++q)
+                        (wm ? sOutHi : sOutLo)[(mb * 32 + g * 8 + lhi * 4 + q) * OLD + cl] =
+                            f32_to_bf16(acc[mb][nb][g * 4 + q] + bv);
+        }
+    } else {
+        // Residual: lanes 0-31 and 32-63 each read 64 contiguous bytes of
+        // one row.
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int cl = wn * 64 + nb * 32 + l32;
+            const bool cok = n0 + cl < NO;
+            const float bv = (bias && cok) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int rl = mb * 32 + g * 8 + lhi * 4 + q;
+                        const int64_t row = k0 + wm * 64 + rl;
+                        const float rv = (cok && row < n) ? bf16_to_f32(res[row * NO + n0 + cl]) : 0.f;
+                        (wm ? sOutHi : sOutLo)[rl * OLD + cl] = f32_to_bf16(acc[mb][nb][g * 4 + q] + bv + rv);
+                    }
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -349,17 +373,28 @@ hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, in
     return hipGetLastError();
 }
 
+template <int TAPS>
+static void launch_taps(dim3 grid, hipStream_t stream, const uint16_t* A, const int32_t* N, const uint16_t* B,
+                        const uint16_t* bias, const uint16_t* R, uint16_t* out, int n, int K, int NO) {
+    // the residual variant is its own instantiation: a runtime test of R
+    // changes the code the compiler emits for the main loop
+    if (R)
+        hipLaunchKernelGGL((k_conv_mfma<TAPS, true>), grid, dim3(256), 0, stream, A, N, B, bias, R, out, n, K, NO);
+    else
+        hipLaunchKernelGGL((k_conv_mfma<TAPS, false>), grid, dim3(256), 0, stream, A, N, B, bias, R, out, n, K, NO);
+}
+
 hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const uint16_t* B,
-                                   const uint16_t* bias, uint16_t* out, int64_t n, int K, int NO, int taps,
-                                   hipStream_t stream) {
+                                   const uint16_t* bias, const uint16_t* R, uint16_t* out, int64_t n, int K,
+                                   int NO, int taps, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>(((n + CM_BM - 1) / CM_BM) * ((NO + CM_BN - 1) / CM_BN)));
     const int nn = static_cast<int>(n);
     switch (taps) {
-        case 1: hipLaunchKernelGGL(k_conv_mfma<1>, grid, dim3(256), 0, stream, A, N, B, bias, out, nn, K, NO); break;
-        case 9: hipLaunchKernelGGL(k_conv_mfma<9>, grid, dim3(256), 0, stream, A, N, B, bias, out, nn, K, NO); break;
-        case 25: hipLaunchKernelGGL(k_conv_mfma<25>, grid, dim3(256), 0, stream, A, N, B, bias, out, nn, K, NO); break;
-        case 49: hipLaunchKernelGGL(k_conv_mfma<49>, grid, dim3(256), 0, stream, A, N, B, bias, out, nn, K, NO); break;
+        case 1: launch_taps<1>(grid, stream, A, N, B, bias, R, out, nn, K, NO); break;
+        case 9: launch_taps<9>(grid, stream, A, N, B, bias, R, out, nn, K, NO); break;
+        case 25: launch_taps<25>(grid, stream, A, N, B, bias, R, out, nn, K, NO); break;
+        case 49: launch_taps<49>(grid, stream, A, N, B, bias, R, out, nn, K, NO); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -11,6 +11,7 @@
 // channels at a time, the gathered neighbour rows and the matching weight
 // slice are staged in LDS (as fp32) and every thread accumulates a 4 x 4 block
 // of outputs with FMAs.  A tap whose entry is -1 stages zeros (zero padding).
+// An optional residual R [n][channels produced] is added before the store.
 //
 // Weight gradient: one workgroup per (tap, 64 input channels, 64 output
 // channels, token slice); 16 tokens at a time the gathered X rows and the dY
@@ -26,6 +27,7 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ A,
                                                    const int32_t* __restrict__ Nt,
                                                    const T* __restrict__ Wt,
                                                    const T* __restrict__ bias,
+                                                   const T* __restrict__ R,
                                                    T* __restrict__ out, int n, int Ci, int Co, int taps) {
     // K: channels contracted per tap; NO: channels produced.
     const int K = DX ? Co : Ci;
@@ -104,13 +106,14 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ A,
             if (col >= NO) continue;
             float v = acc[p][q];
             if (!DX && bias) v += Elem<T>::load(bias + col);
+            if (R) v += Elem<T>::load(R + row * NO + col);
             Elem<T>::store(out + row * NO + col, v);
         }
     }
 }
 
 hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N, const void* Wt,
-                            const void* bias, void* out, int64_t n, int Ci, int Co, int taps,
+                            const void* bias, const void* R, void* out, int64_t n, int Ci, int Co, int taps,
                             hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const size_t lds = static_cast<size_t>(VT_M) * taps * sizeof(int);
@@ -121,16 +124,18 @@ hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
         auto a = static_cast<const uint16_t*>(A);
         auto w = static_cast<const uint16_t*>(Wt);
         auto b = static_cast<const uint16_t*>(bias);
+        auto r = static_cast<const uint16_t*>(R);
         auto o = static_cast<uint16_t*>(out);
-        if (dx) hipLaunchKernelGGL((k_conv_valu<uint16_t, true>), grid, dim3(256), lds, stream, a, N, w, b, o, nn, Ci, Co, taps);
-        else hipLaunchKernelGGL((k_conv_valu<uint16_t, false>), grid, dim3(256), lds, stream, a, N, w, b, o, nn, Ci, Co, taps);
+        if (dx) hipLaunchKernelGGL((k_conv_valu<uint16_t, true>), grid, dim3(256), lds, stream, a, N, w, b, r, o, nn, Ci, Co, taps);
+        else hipLaunchKernelGGL((k_conv_valu<uint16_t, false>), grid, dim3(256), lds, stream, a, N, w, b, r, o, nn, Ci, Co, taps);
     } else {
         auto a = static_cast<const float*>(A);
         auto w = static_cast<const float*>(Wt);
         auto b = static_cast<const float*>(bias);
+        auto r = static_cast<const float*>(R);
         auto o = static_cast<float*>(out);
-        if (dx) hipLaunchKernelGGL((k_conv_valu<float, true>), grid, dim3(256), lds, stream, a, N, w, b, o, nn, Ci, Co, taps);
-        else hipLaunchKernelGGL((k_conv_valu<float, false>), grid, dim3(256), lds, stream, a, N, w, b, o, nn, Ci, Co, taps);
+        if (dx) hipLaunchKernelGGL((k_conv_valu<float, true>), grid, dim3(256), lds, stream, a, N, w, b, r, o, nn, Ci, Co, taps);
+        else hipLaunchKernelGGL((k_conv_valu<float, false>), grid, dim3(256), lds, stream, a, N, w, b, r, o, nn, Ci, Co, taps);
     }
     return hipGetLastError();
 }

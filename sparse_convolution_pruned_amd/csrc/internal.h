@@ -106,11 +106,14 @@ hipError_t launch_build_index(const int32_t* coords, const int32_t* offs, int fr
 // In the conv launchers `taps` = K * K: the columns of N and the leading
 // dimension of the weights; tap taps-1-j is the mirror of tap j.
 //
+// Both paths add an optional residual R (nullable, shaped like the output)
+// before the single rounding of the output.
+//
 // VALU path (fp32 or bf16, any channel count).  `dx` selects the input
 // gradient: A = dY [n][Co], output [n][Ci], weights read transposed with the
 // tap mirrored; otherwise A = X [n][Ci], output [n][Co].
 hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
-                            const void* Wt, const void* bias, void* out, int64_t n,
+                            const void* Wt, const void* bias, const void* R, void* out, int64_t n,
                             int Ci, int Co, int taps, hipStream_t stream);
 
 // MFMA path (bf16, taps in {1, 9, 25, 49}).  One gather-GEMM serves both
@@ -121,8 +124,8 @@ hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
 // weights repacked by launch_repack_fwd (V[taps-1-j][o][i] = Wt[j][i][o])
 // into conv_mfma_fwd_workspace(Ci, Co, taps) bytes.
 hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const uint16_t* B,
-                                   const uint16_t* bias, uint16_t* out, int64_t n, int K, int NO,
-                                   int taps, hipStream_t stream);
+                                   const uint16_t* bias, const uint16_t* R, uint16_t* out, int64_t n, int K,
+                                   int NO, int taps, hipStream_t stream);
 hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream);
 size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps);
 // bf16, a tap count the kernel is built for, contracted channels a multiple
@@ -168,5 +171,7 @@ hipError_t launch_stage_gather(const void* src, int64_t n_src, const int32_t* ro
                                void* dst, int C, int elem_bytes, hipStream_t stream);
 hipError_t launch_stage_scatter(const void* src, const int32_t* rows, int64_t n_rows, void* dst,
                                 int64_t n_dst, int C, int elem_bytes, hipStream_t stream);
+// dst[k] = k for k < n: the neighbour table of a 1 x 1 neighbourhood.
+hipError_t launch_iota(int32_t* dst, int64_t n, hipStream_t stream);
 
 }  // namespace svc

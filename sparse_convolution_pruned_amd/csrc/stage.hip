@@ -149,4 +149,18 @@ hipError_t launch_copy_bytes(const void* src, void* dst, int64_t bytes, hipStrea
     return hipSuccess;
 }
 
+// The identity neighbour table of a 1 x 1 neighbourhood: dst[k] = k.
+__global__ __launch_bounds__(256) void k_iota(int32_t* __restrict__ dst, int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; k < n; k += stride)
+        dst[k] = static_cast<int32_t>(k);
+}
+
+hipError_t launch_iota(int32_t* dst, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int blocks = static_cast<int>(std::min<int64_t>((n + 255) / 256, 1024));
+    hipLaunchKernelGGL(k_iota, dim3(blocks), dim3(256), 0, stream, dst, n);
+    return hipGetLastError();
+}
+
 }  // namespace svc

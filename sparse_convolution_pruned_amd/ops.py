@@ -43,6 +43,7 @@ SYMBOLS = (
     "sv_build_index_k", "sv_sparseconv2d_fwd_k", "sv_sparseconv2d_bwd_dx_k",
     "sv_sparseconv2d_bwd_dw_k", "sv_workspace_bytes_k", "sv_sparseconv2d_chunked",
     "sv_chunked_workspace_bytes", "sv_sparseconv2d_chunked_host", "sv_chunked_host_workspace_bytes",
+    "sv_adapter_fwd", "sv_adapter_bwd", "sv_adapter_workspace_bytes",
     "sv_stage_gather", "sv_stage_scatter", "sv_status_string", "sv_version",
     "sv_xattn_fwd", "sv_xattn_bwd", "sv_xattn_workspace_bytes",
 )
@@ -119,6 +120,9 @@ def load(path: str = LIB_PATH):
         "sv_xattn_fwd": ([P, P, i64, i64, i32, ctypes.c_float, E, P, P, P, sz, P], E),
         "sv_xattn_bwd": ([P, P, P, P, P, i64, i64, i32, ctypes.c_float, E, P, P, P, sz, P], E),
         "sv_xattn_workspace_bytes": ([i32, i64, i64, i32], sz),
+        "sv_adapter_fwd": ([P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, E, E, P, sz, P], E),
+        "sv_adapter_bwd": ([P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, E, E, P, sz, P], E),
+        "sv_adapter_workspace_bytes": ([i32, i64, i32, i32, i32, E], sz),
         "sv_status_string": ([E], ctypes.c_char_p),
         "sv_version": ([], ctypes.c_char_p),
     }
@@ -403,7 +407,77 @@ def sv_stage_scatter(src, rows, dst, stream=None):
     _check(st, "sv_stage_scatter")
 
 
+def sv_adapter_workspace_bytes(backward, n, K, C, r, dtype) -> int:
+    dt = SV_BF16 if dtype in (torch.bfloat16, SV_BF16, "bf16") else SV_F32
+    return int(load().sv_adapter_workspace_bytes(1 if backward else 0, int(n), int(K), int(C), int(r), dt))
+
+
+def _adapter_shapes(X, N, Wd, Wc, Wu):
+    n, C = X.shape
+    r = Wd.shape[1]
+    taps = Wc.shape[0]
+    assert Wd.shape == (C, r) and Wc.shape == (taps, r, r) and Wu.shape == (r, C) and N.shape == (n, taps)
+    assert X.dtype == Wd.dtype == Wc.dtype == Wu.dtype and N.dtype == torch.int32
+    return n, C, r, ksize_of_taps(taps)
+
+
+def sv_adapter_fwd(X, N, Wd, bd, Wc, bc, Wu, bu, H1, H2, Y, workspace, kernel="auto", stream=None):
+    n, C, r, K = _adapter_shapes(X, N, Wd, Wc, Wu)
+    assert H1.shape == H2.shape == (n, r) and Y.shape == (n, C)
+    assert H1.dtype == H2.dtype == Y.dtype == X.dtype
+    for b, w in ((bd, r), (bc, r), (bu, C)):
+        assert b is None or (b.shape == (w,) and b.dtype == X.dtype)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_adapter_fwd(_ptr(X), _ptr(N), n, K, C, r, _ptr(Wd), _ptr(bd), _ptr(Wc), _ptr(bc), _ptr(Wu),
+                               _ptr(bu), _ptr(H1), _ptr(H2), _ptr(Y), _dt(X), _kernel(kernel), _ptr(workspace), wsb,
+                               _stream(stream))
+    _check(st, "sv_adapter_fwd")
+
+
+def sv_adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, dX, dWd, dbd, dWc, dbc, dWu, dbu, workspace, kernel="auto",
+                   stream=None):
+    n, C, r, K = _adapter_shapes(X, N, Wd, Wc, Wu)
+    assert H1.shape == H2.shape == (n, r) and dY.shape == dX.shape == (n, C)
+    assert dWd.shape == (C, r) and dWc.shape == Wc.shape and dWu.shape == (r, C)
+    for g in (dWd, dbd, dWc, dbc, dWu, dbu):
+        assert g is None or g.dtype == torch.float32
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_adapter_bwd(_ptr(X), _ptr(N), n, K, C, r, _ptr(Wd), _ptr(Wc), _ptr(Wu), _ptr(H1), _ptr(H2),
+                               _ptr(dY), _ptr(dX), _ptr(dWd), _ptr(dbd), _ptr(dWc), _ptr(dbc), _ptr(dWu),
+                               _ptr(dbu), _dt(X), _kernel(kernel), _ptr(workspace), wsb, _stream(stream))
+    _check(st, "sv_adapter_bwd")
+
+
 # ---------------------------------------------------------- conveniences
+def adapter_fwd(X, N, Wd, bd, Wc, bc, Wu, bu, kernel="auto"):
+    """Bottleneck adapter Y = X + (conv_K(X Wd + bd) + bc) Wu + bu.
+    Returns (Y, H1, H2); H1 and H2 feed adapter_bwd."""
+    n, C = X.shape
+    r = Wd.shape[1]
+    H1 = torch.empty((n, r), dtype=X.dtype, device=X.device)
+    H2 = torch.empty_like(H1)
+    Y = torch.empty_like(X)
+    ws = torch.empty(max(256, sv_adapter_workspace_bytes(False, n, ksize_of_taps(Wc.shape[0]), C, r, X.dtype)),
+                     dtype=torch.uint8, device=X.device)
+    sv_adapter_fwd(X, N, Wd, bd, Wc, bc, Wu, bu, H1, H2, Y, ws, kernel)
+    return Y, H1, H2
+
+
+def adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, kernel="auto"):
+    """Returns a dict: dX (X's dtype) and fp32 dWd, dbd, dWc, dbc, dWu, dbu."""
+    n, C = X.shape
+    r = Wd.shape[1]
+    f32 = dict(dtype=torch.float32, device=X.device)
+    g = {"dX": torch.empty_like(X), "dWd": torch.empty((C, r), **f32), "dbd": torch.empty((r,), **f32),
+         "dWc": torch.empty(tuple(Wc.shape), **f32), "dbc": torch.empty((r,), **f32),
+         "dWu": torch.empty((r, C), **f32), "dbu": torch.empty((C,), **f32)}
+    ws = torch.empty(max(256, sv_adapter_workspace_bytes(True, n, ksize_of_taps(Wc.shape[0]), C, r, X.dtype)),
+                     dtype=torch.uint8, device=X.device)
+    sv_adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, g["dX"], g["dWd"], g["dbd"], g["dWc"], g["dbc"], g["dWu"],
+                   g["dbu"], ws, kernel)
+    return g
+
+
 def sv_xattn_workspace_bytes(backward, m, n, d) -> int:
     return int(load().sv_xattn_workspace_bytes(1 if backward else 0, int(m), int(n), int(d)))
 

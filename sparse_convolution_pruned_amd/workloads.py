@@ -237,3 +237,65 @@ def make_random_case(seed: int, T: int, H: int, W: int, keep, Ci: int, Co: int,
     b = _normal(rs["b"], (Co,), 1.0, dtype) if bias else np.zeros((Co,), np.float32)
     dY = _normal(rs["dY"], (n, Co), 1.0, dtype)
     return Layer(T, H, W, coords, offs, X, Wt, b, dY, dtype, f"random seed={seed}")
+
+
+@dataclass
+class AdapterCase:
+    """Inputs of one bottleneck adapter (down-projection C -> r, K x K
+    SparseConv2D r -> r, up-projection r -> C, residual) on a token set."""
+    T: int
+    H: int
+    W: int
+    coords: np.ndarray          # int32 [n]
+    frame_offsets: np.ndarray   # int32 [T+1]
+    X: np.ndarray               # [n, C]
+    Wd: np.ndarray              # [C, r]
+    bd: np.ndarray              # [r]
+    Wc: np.ndarray              # [K*K, r, r]
+    bc: np.ndarray              # [r]
+    Wu: np.ndarray              # [r, C]
+    bu: np.ndarray              # [C]
+    dY: np.ndarray              # [n, C]
+    K: int
+    dtype: str
+    name: str = ""
+
+    @property
+    def n(self) -> int:
+        return int(self.coords.shape[0])
+
+
+def _adapter_params(rs, n, C, r, K, dtype):
+    """Weights ~ N(0, 1/fan_in) (so every layer keeps unit scale), biases
+    ~ N(0, 0.1^2), X and dY ~ N(0, 1); bf16-representable for bf16."""
+    taps = K * K
+    return dict(X=_normal(rs["X"], (n, C), 1.0, dtype),
+                Wd=_normal(rs["W"], (C, r), 1.0 / np.sqrt(C), dtype),
+                bd=_normal(rs["b"], (r,), 0.1, dtype),
+                Wc=_normal(rs["W"], (taps, r, r), 1.0 / np.sqrt(taps * r), dtype),
+                bc=_normal(rs["b"], (r,), 0.1, dtype),
+                Wu=_normal(rs["W"], (r, C), 1.0 / np.sqrt(r), dtype),
+                bu=_normal(rs["b"], (C,), 0.1, dtype),
+                dY=_normal(rs["dY"], (n, C), 1.0, dtype))
+
+
+def make_adapter_case(seed: int, T: int, H: int, W: int, keep, C: int, r: int, K: int = 3,
+                      dtype: str = "f32", shuffle: bool = False) -> AdapterCase:
+    """Small adapter case on a random token set (as make_random_case)."""
+    L = make_random_case(seed, T, H, W, keep, 1, 1, dtype, shuffle=shuffle)
+    rs = _streams([7927, seed])
+    p = _adapter_params(rs, L.n, C, r, K, dtype)
+    return AdapterCase(T, H, W, L.coords, L.frame_offsets, K=K, dtype=dtype, name=f"adapter seed={seed}", **p)
+
+
+def make_adapter_stage0(C: int = 1024, r: int = 256, K: int = 3, scale_T: Optional[int] = None) -> AdapterCase:
+    """The adapter on the first-stage token set of the c5 workload (384
+    frames of a 16 x 16 grid, keep U[.5, .7]): a ViT width C = 1024 (the
+    large video ViT the page evaluates) around a bottleneck of r = 256, the
+    channel width of the c5 SparseConv2D layers."""
+    S = make_staged("c5", scale_T)
+    st = S.stages[0]
+    rs = _streams([7933, C, r, K])
+    p = _adapter_params(rs, int(st["coords"].shape[0]), C, r, K, "bf16")
+    return AdapterCase(S.T, S.H, S.W, st["coords"], st["frame_offsets"], K=K, dtype="bf16",
+                       name=f"adapter C={C} r={r} K={K} on c5 stage 0", **p)

@@ -243,3 +243,28 @@ def test_kxk_validation_and_workspace(lib):
     assert lib.sv_sparseconv2d_chunked(ctypes.byref(d), passes, None, 0, None) == ops.SV_ERR_INVALID_ARG
     d.ksize = 9
     assert lib.sv_sparseconv2d_chunked(ctypes.byref(d), passes, None, 0, None) == ops.SV_ERR_UNSUPPORTED
+
+
+def test_adapter_validation_and_workspace(lib):
+    F32, BF16 = ops.SV_F32, ops.SV_BF16
+    ws = lib.sv_adapter_workspace_bytes
+    assert ws(0, 100, 3, 64, 0, BF16) == 0 and ws(0, 100, 4, 64, 32, BF16) == 0 and ws(1, -1, 3, 64, 32, BF16) == 0
+    # forward: identity table + the largest repacked weight; backward: + dH2, dH1 and dW partials
+    f = ws(0, 1000, 3, 1024, 256, BF16)
+    assert 1000 * 4 + 1024 * 256 * 2 <= f <= 1000 * 4 + 9 * 256 * 256 * 2 + 1024
+    b = ws(1, 58822, 3, 1024, 256, BF16)
+    assert b >= 58822 * 4 + 2 * 58822 * 256 * 2
+    args = (FAKE, FAKE, 8, 3, 64, 32, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE)
+    assert lib.sv_adapter_fwd(*args, BF16, 0, None, 0, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_adapter_fwd(*args, BF16, 7, FAKE, 1 << 20, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_adapter_fwd(*args, F32, 2, FAKE, 1 << 20, None) == ops.SV_ERR_UNSUPPORTED
+    bad = (FAKE, FAKE, 8, 2, 64, 32) + args[6:]
+    assert lib.sv_adapter_fwd(*bad, BF16, 0, FAKE, 1 << 20, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_adapter_fwd(FAKE, FAKE, 8, 3, 64, 32, None, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                              BF16, 0, FAKE, 1 << 20, None) == ops.SV_ERR_INVALID_ARG
+    bargs = (FAKE, FAKE, 8, 3, 64, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+             None)
+    assert lib.sv_adapter_bwd(*bargs, BF16, 0, None, 0, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_adapter_bwd(*bargs, BF16, 0, ctypes.c_void_p(4097), 1 << 30, None) == ops.SV_ERR_INVALID_ARG
+    nodw = bargs[:13] + (None,) + bargs[14:]
+    assert lib.sv_adapter_bwd(*nodw, BF16, 0, FAKE, 1 << 30, None) == ops.SV_ERR_INVALID_ARG
