@@ -42,7 +42,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4", "c4-host", "xattn"])
+    p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4", "c4-host", "xattn",
+                                                                "adapter"])
     p.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     p.add_argument("--ksize", type=int, default=3, choices=[1, 3, 5, 7],
                    help="single-layer workloads: K of a K x K neighbourhood (weights of the same "
@@ -56,8 +57,8 @@ def parse():
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one plain device copy of this size (HBM counter calibration)")
     a = p.parse_args()
-    if a.ksize != 3 and a.workload not in ("c2", "c3a", "c3b", "c4"):
-        p.error("--ksize applies to the single-layer workloads c2, c3a, c3b and c4")
+    if a.ksize != 3 and a.workload not in ("c2", "c3a", "c3b", "c4", "adapter"):
+        p.error("--ksize applies to the single-layer workloads c2, c3a, c3b, c4 and to the adapter")
     return a
 
 
@@ -482,6 +483,69 @@ def xattn_workload(args):
           flush=True)
 
 
+def adapter_workload(args):
+    """The bottleneck adapter (down-projection C -> r, K x K SparseConv2D
+    r -> r, up-projection r -> C, residual) over the c5 first-stage tokens
+    (n = 58,822 of a 16 x 16 grid, 384 frames) at C = 1024, r = 256, bf16:
+    forward and backward timed separately with HIP events on the stream
+    they run on."""
+    import torch
+    from sparse_convolution_pruned_amd import ops, workloads as wl
+
+    K = args.ksize
+    A = wl.make_adapter_stage0(K=K)
+    bf = torch.bfloat16
+    dev = lambda a, d=None: (torch.from_numpy(a).to(d) if d is not None else torch.from_numpy(a)).cuda()
+    X = dev(A.X, bf)
+    N = ops.build_index(dev(A.coords), dev(A.frame_offsets), A.T, A.H, A.W, K=K)
+    P = {k: dev(getattr(A, k), bf) for k in ("Wd", "bd", "Wc", "bc", "Wu", "bu")}
+    dY = dev(A.dY, bf)
+    n, C = A.X.shape
+    r, taps = A.Wd.shape[1], K * K
+    H1 = torch.empty((n, r), dtype=bf, device="cuda")
+    H2 = torch.empty_like(H1)
+    Y = torch.empty_like(X)
+    dX = torch.empty_like(X)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dWd, dbd = torch.empty((C, r), **f32), torch.empty((r,), **f32)
+    dWc, dbc = torch.empty((taps, r, r), **f32), torch.empty((r,), **f32)
+    dWu, dbu = torch.empty((r, C), **f32), torch.empty((C,), **f32)
+    wf = torch.empty(max(256, ops.sv_adapter_workspace_bytes(False, n, K, C, r, bf)), dtype=torch.uint8, device="cuda")
+    wb = torch.empty(max(256, ops.sv_adapter_workspace_bytes(True, n, K, C, r, bf)), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        ops.sv_adapter_fwd(X, N, P["Wd"], P["bd"], P["Wc"], P["bc"], P["Wu"], P["bu"], H1, H2, Y, wf, args.kernel)
+
+    def bwd():
+        ops.sv_adapter_bwd(X, N, P["Wd"], P["Wc"], P["Wu"], H1, H2, dY, dX, dWd, dbd, dWc, dbc, dWu, dbu, wb,
+                           args.kernel)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(args.steps):
+        fwd()
+    ev[1].record()
+    for _ in range(args.steps):
+        bwd()
+    ev[2].record()
+    torch.cuda.synchronize()
+    tf = ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
+    tb = ev[1].elapsed_time(ev[2]) * 1e-3 / args.steps
+    fl_f = 2.0 * n * (C * r + taps * r * r + r * C)
+    fl_b = 2 * fl_f
+    print(json.dumps({"workload": "adapter", "name": A.name, "n": n, "C": C, "r": r, "ksize": K,
+                      "kernel": args.kernel, "fwd_ms": round(tf * 1e3, 4), "bwd_ms": round(tb * 1e3, 4),
+                      "fwd_tflops": round(fl_f / tf / 1e12, 2), "bwd_tflops": round(fl_b / tb / 1e12, 2),
+                      "step_tflops": round((fl_f + fl_b) / (tf + tb) / 1e12, 2),
+                      "frac_bf16_peak": round((fl_f + fl_b) / (tf + tb) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "workspace_mb": {"fwd": round(wf.numel() / 2 ** 20, 2), "bwd": round(wb.numel() / 2 ** 20, 2)}}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -495,6 +559,8 @@ def main():
         return host_stream_workload(args)
     if args.workload == "xattn":
         return xattn_workload(args)
+    if args.workload == "adapter":
+        return adapter_workload(args)
     if args.workload != "c5":
         return layer_workload(args)
 
