@@ -300,24 +300,38 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
                             f32_to_bf16(acc[mb][nb][g * 4 + q] + bv);
         }
     } else {
-        // Residual: lanes 0-31 and 32-63 each read 64 contiguous bytes of
-        // one row.
+        // Residual: all 64 values of the thread requested at once (raw
+        // buffer loads; entries past n or NO get an out-of-range offset and
+        // read as zero), so one wait covers them.  Lanes 0-31 and 32-63 each
+        // read 64 contiguous bytes of one row.
+        const rsrc_t rR = make_rsrc(res, static_cast<uint32_t>(n) * NO * 2);
+        uint16_t rv[2][2][16];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int cl = wn * 64 + nb * 32 + l32;
-            const bool cok = n0 + cl < NO;
-            const float bv = (bias && cok) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
+                for (int e = 0; e < 16; ++e) {
+                    const int rl = mb * 32 + (e >> 2) * 8 + lhi * 4 + (e & 3);
+                    const int64_t row = k0 + wm * 64 + rl;
+                    const uint32_t off = (n0 + cl < NO && row < n)
+                                             ? static_cast<uint32_t>(row * NO + n0 + cl) * 2u : kOob;
+                    rv[nb][mb][e] = __builtin_amdgcn_raw_buffer_load_b16(rR, off, 0, 0);
+                }
+        }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int rl = mb * 32 + g * 8 + lhi * 4 + q;
-                        const int64_t row = k0 + wm * 64 + rl;
-                        const float rv = (cok && row < n) ? bf16_to_f32(res[row * NO + n0 + cl]) : 0.f;
-                        (wm ? sOutHi : sOutLo)[rl * OLD + cl] = f32_to_bf16(acc[mb][nb][g * 4 + q] + bv + rv);
-                    }
+        for (int nb = 0; nb < 2; ++nb) {
+            const int cl = wn * 64 + nb * 32 + l32;
+            const float bv = (bias && n0 + cl < NO) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int rl = mb * 32 + (e >> 2) * 8 + lhi * 4 + (e & 3);
+                    (wm ? sOutHi : sOutLo)[rl * OLD + cl] =
+                        f32_to_bf16(acc[mb][nb][e] + bv + bf16_to_f32(rv[nb][mb][e]));
+                }
         }
     }
     __syncthreads();
@@ -359,8 +373,9 @@ __global__ __launch_bounds__(256) void k_repack_fwd(const uint16_t* __restrict__
 bool conv_mfma_supported(bool dx, int Ci, int Co, int64_t n, int taps) {
     const int K = dx ? Co : Ci, NO = dx ? Ci : Co;
     const bool built = taps == 1 || taps == 9 || taps == 25 || taps == 49;
+    // A, the output (and a residual shaped like it) and B within one buffer range
     return built && K > 0 && NO > 0 && K % 32 == 0 && NO % 16 == 0 && n * K * 2 <= kMaxRange &&
-           static_cast<int64_t>(taps) * NO * K * 2 <= kMaxRange;
+           n * NO * 2 <= kMaxRange && static_cast<int64_t>(taps) * NO * K * 2 <= kMaxRange;
 }
 
 size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps) {

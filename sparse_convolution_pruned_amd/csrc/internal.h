@@ -129,8 +129,8 @@ hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const ui
 hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream);
 size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps);
 // bf16, a tap count the kernel is built for, contracted channels a multiple
-// of 32, output channels of 16, and the n rows of A within the 2 GiB range
-// of a buffer load.
+// of 32, output channels of 16, and the n rows of A and of the output within
+// the 2 GiB range of a buffer load.
 bool conv_mfma_supported(bool dx, int Ci, int Co, int64_t n, int taps);
 
 // dW: split-K plan, partial kernels, reduction.
