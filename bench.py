@@ -113,9 +113,16 @@ class StagedRun:
                                dtype=torch.uint8, device="cuda")
         # dW and dX of a layer both read dY and nothing else either writes, so
         # dW can run on a second stream (default priority) while dX runs on
-        # the caller's; the streams join at the end of the step.
+        # the caller's; the streams join at the end of the step.  The side
+        # stream also builds the later stages' index tables and repacks the
+        # later layers' forward weights at the start of the step, off the
+        # forward chain.
         self.side = torch.cuda.Stream() if dw_stream == "side" else None
         self.ready = [torch.cuda.Event() for _ in range(self.L)]
+        self.ev_start, self.ev_prep, self.ev_join = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
+        self.plan = None
+        vb = max(256, ops.sv_workspace_bytes(ops.SV_OP_FWD, max(self.ns), C, C, bf))
+        self.V = [torch.empty(vb, dtype=torch.uint8, device="cuda") for _ in range(self.L)]
 
     def flops(self):
         """Effective FLOPs per step: 2 * n * 9 * C_in * C_out per pass, all
@@ -124,12 +131,14 @@ class StagedRun:
         return sum(3 * 2 * self.ns[self.stage_of[l]] * 9 * C * C for l in range(self.L))
 
     def step(self, ev=None, overlap=True):
-        """One pass of the whole hot path.  With `overlap` each layer's dW
-        runs on the side stream concurrently with its dX; without it (the
-        instrumented repeat) every call runs alone, in order, on the current
-        stream, so that its HIP events bracket that call's kernels only."""
+        """One pass of the whole hot path.  With `overlap` and the side stream
+        the step is scheduled over three streams (see __init__); without it
+        (the instrumented repeat) every call runs alone, in order, on the
+        current stream, so that its HIP events bracket that call's kernels
+        only."""
+        if overlap and self.side is not None:
+            return self._step_streams()
         ops, kern = self.ops, self.kernel
-        side = self.side if overlap else None
         rec = ev.record if ev is not None else (lambda *a, **k: None)
         S = self.S
         for s in range(len(self.ns)):
@@ -147,21 +156,11 @@ class StagedRun:
                                     workspace=self.fws)
             rec("fwd", t, units=self.ns[s])
         g = self.dy_last
-        main = self.torch.cuda.current_stream()
         for l in reversed(range(self.L)):
             s = self.stage_of[l]
-            if side is not None:
-                # dY of this layer is ready on the main stream at this point
-                self.ready[l].record(main)
-                with self.torch.cuda.stream(side):
-                    side.wait_event(self.ready[l])
-                    t = rec("dw", None)
-                    ops.sv_sparseconv2d_bwd_dw(self.xs[l], self.N[s], g, self.dW[l], self.db[l], False, self.ws)
-                    rec("dw", t, units=self.ns[s])
-            else:
-                t = rec("dw", None)
-                ops.sv_sparseconv2d_bwd_dw(self.xs[l], self.N[s], g, self.dW[l], self.db[l], False, self.ws)
-                rec("dw", t, units=self.ns[s])
+            t = rec("dw", None)
+            ops.sv_sparseconv2d_bwd_dw(self.xs[l], self.N[s], g, self.dW[l], self.db[l], False, self.ws)
+            rec("dw", t, units=self.ns[s])
             t = rec("dx", None)
             ops.sv_sparseconv2d_bwd_dx(g, self.N[s], self.W[l], self.gx[l], kern)
             rec("dx", t, units=self.ns[s])
@@ -171,8 +170,96 @@ class StagedRun:
                 ops.sv_stage_scatter(g, self.sels[s], self.gscat[l])
                 rec("scatter", t, units=self.ns[s])
                 g = self.gscat[l]
-        if side is not None:
-            main.wait_stream(side)          # the next step overwrites the activations dW reads
+
+    def _step_streams(self):
+        """The timed step over two streams; every kernel of the in-order
+        step runs, with the same inputs and outputs.  Its library calls are
+        prepared once (arguments converted, entry points looked up), so that
+        issuing a step costs the host a few microseconds per call: through
+        the checking wrappers the ~60 calls of a step took longer on the host
+        than the step takes on the GPU."""
+        if self.plan is None:
+            self.plan = self._prepare_streams()
+        for f in self.plan:
+            f()
+
+    def _prepare_streams(self):
+        import ctypes
+
+        ops, torch, S = self.ops, self.torch, self.S
+        if self.kernel == "valu":
+            raise SystemExit("the three-stream step uses the MFMA forward; use --dw-stream same with --kernel valu")
+        lib = ops.load()
+        main, side = torch.cuda.current_stream(), self.side
+        hs = {id(x): ctypes.c_void_p(x.cuda_stream) for x in (main, side)}
+        P = lambda t: None if t is None else t.data_ptr()
+        bf, C, K = ops.SV_BF16, self.C, 3
+        plan = []
+
+        def call(name, *args):
+            fn = getattr(lib, name)
+
+            def f():
+                st = fn(*args)
+                if st != ops.SV_OK:
+                    raise ops.SvError(st, name)
+            plan.append(f)
+
+        def record(ev, stream):
+            plan.append(lambda: ev.record(stream))
+
+        def wait(stream, ev):
+            plan.append(lambda: stream.wait_event(ev))
+
+        def index(s, stream):
+            call("sv_build_index", P(self.coords[s]), P(self.offs[s]), S.T, S.H, S.W, self.ns[s], P(self.N[s]),
+                 None, P(self.flag), hs[id(stream)])
+
+        def repack(l, stream):
+            call("sv_repack_fwd_k", P(self.W[l]), K, C, C, bf, P(self.V[l]), self.V[l].numel(), hs[id(stream)])
+
+        vb = self.ws.numel()
+        # side stream: the later stages' index tables and layers' weights
+        record(self.ev_start, main)
+        wait(side, self.ev_start)
+        for s in range(1, len(self.ns)):
+            index(s, side)
+        for l in range(1, self.L):
+            repack(l, side)
+        record(self.ev_prep, side)
+        # main stream: forward
+        index(0, main)
+        repack(0, main)
+        for l in range(self.L):
+            s = self.stage_of[l]
+            if l == 1:
+                wait(main, self.ev_prep)
+            if l > 0 and self.stage_of[l - 1] != s:
+                call("sv_stage_gather", P(self.ys[l - 1]), self.ns[s - 1], P(self.sels[s]), self.ns[s], P(self.xs[l]),
+                     C, bf, hs[id(main)])
+            call("sv_sparseconv2d_fwd_packed_k", P(self.xs[l]), P(self.N[s]), P(self.V[l]), P(self.b[l]),
+                 P(self.ys[l]), self.ns[s], K, C, C, bf, hs[id(main)])
+        # backward: each layer's dW (partials and their reduction) on the
+        # side stream, dX and the stage scatters on main
+        g = self.dy_last
+        for l in reversed(range(self.L)):
+            s = self.stage_of[l]
+            record(self.ready[l], main)         # dY of this layer is ready on the main stream
+            wait(side, self.ready[l])
+            call("sv_sparseconv2d_bwd_dw", P(self.xs[l]), P(self.N[s]), P(g), P(self.dW[l]), P(self.db[l]),
+                 self.ns[s], C, C, bf, 0, P(self.ws), vb, hs[id(side)])
+            call("sv_sparseconv2d_bwd_dx", P(g), P(self.N[s]), P(self.W[l]), P(self.gx[l]), self.ns[s], C, C, bf,
+                 ops.KERNELS[self.kernel], hs[id(main)])
+            g = self.gx[l]
+            if l > 0 and self.stage_of[l - 1] != s:
+                call("sv_stage_scatter", P(g), P(self.sels[s]), self.ns[s], P(self.gscat[l]), self.ns[s - 1], C, bf,
+                     hs[id(main)])
+                g = self.gscat[l]
+        # the next step overwrites the activations and the workspace the
+        # side stream reads
+        record(self.ev_join, side)
+        wait(main, self.ev_join)
+        return plan
 
     def cpu_sample(self, frames, min_seconds=10.0):
         """The oracle on the first `frames` frames of the same workload:

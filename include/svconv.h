@@ -180,6 +180,39 @@ sv_status sv_sparseconv2d_bwd_dw_k(const void *X, const int32_t *N, const void *
 size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_t C_out,
                             sv_dtype dtype);
 
+/* Split forms, for callers that schedule the pieces of a training step
+ * themselves (same definitions as above; Key Design 2's forward and
+ * dedicated backward kernels):
+ *   sv_repack_fwd_k writes the forward's repacked weights
+ *     V[taps-1-j][o][i] = Wt[j][i][o] (bf16 only; V device, 16-byte aligned,
+ *     at least sv_workspace_bytes_k(SV_OP_FWD, ...) bytes for a shape the
+ *     MFMA kernel takes), and sv_sparseconv2d_fwd_packed_k runs the forward
+ *     on the MFMA kernel from that V (SV_ERR_UNSUPPORTED where the kernel does
+ *     not fit).  Weights repacked once serve any number of forward calls and
+ *     can be prepared on another stream ahead of them.
+ *   sv_sparseconv2d_bwd_dw_partials_k then sv_sparseconv2d_bwd_dw_reduce_k,
+ *     with the same arguments and workspace and in this order (the second
+ *     may run on another stream once the first has finished), equal one
+ *     sv_sparseconv2d_bwd_dw_k call bit for bit: the first writes the token
+ *     slices' partials into the workspace (or dW itself with one slice), the
+ *     second adds them in fixed order.  db must be given to both or to
+ *     neither.  The workspace stays in use until the second completes. */
+sv_status sv_repack_fwd_k(const void *Wt, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                          void *V, size_t V_bytes, hipStream_t stream);
+sv_status sv_sparseconv2d_fwd_packed_k(const void *X, const int32_t *N, const void *V,
+                                       const void *bias, void *Y, int64_t n, int32_t K,
+                                       int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                       hipStream_t stream);
+sv_status sv_sparseconv2d_bwd_dw_partials_k(const void *X, const int32_t *N, const void *dY,
+                                            float *dW, float *db, int64_t n, int32_t K,
+                                            int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                            int32_t accumulate, void *workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
+sv_status sv_sparseconv2d_bwd_dw_reduce_k(float *dW, float *db, int64_t n, int32_t K, int32_t C_in,
+                                          int32_t C_out, sv_dtype dtype, int32_t accumulate,
+                                          const void *workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
 /* Chunked execution over whole frames (Key Design 2's chunking): the frames
  * are processed chunk_frames at a time; for each chunk the index table is
  * built with chunk-local indices into the workspace, then the requested

@@ -192,6 +192,74 @@ sv_status sv_sparseconv2d_bwd_dw(const void* X, const int32_t* N, const void* dY
                                     workspace_bytes, stream);
 }
 
+// ------------------------------------------- split forms for scheduling
+sv_status sv_repack_fwd_k(const void* Wt, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype, void* V,
+                          size_t V_bytes, hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
+    if (st != SV_OK) return st;
+    if (C_in <= 0 || C_out <= 0 || !valid_dtype(dtype) || !Wt || !V) return SV_ERR_INVALID_ARG;
+    if (dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
+    if (V_bytes < conv_mfma_fwd_workspace(C_in, C_out, taps)) return SV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(V) % 16) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_repack_fwd(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(V), C_in, C_out,
+                                        taps, stream));
+}
+
+sv_status sv_sparseconv2d_fwd_packed_k(const void* X, const int32_t* N, const void* V, const void* bias, void* Y,
+                                       int64_t n, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                       hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
+    if (st != SV_OK) return st;
+    if ((st = conv_args_ok(n, taps, C_in, C_out, dtype, SV_KERNEL_MFMA)) != SV_OK) return st;
+    if (!V || (n > 0 && (!X || !N || !Y))) return SV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(V) % 16) return SV_ERR_INVALID_ARG;
+    bool mfma = false;
+    if ((st = choose(SV_KERNEL_MFMA, dtype, false, C_in, C_out, n, taps, &mfma)) != SV_OK) return st;
+    return run_fwd_prepared(true, X, N, nullptr, V, bias, Y, n, C_in, C_out, taps, dtype, stream);
+}
+
+namespace {
+
+// Shared checks of the two phases of the weight gradient.
+sv_status dw_phase_args(int64_t n, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype, const void* workspace,
+                        size_t workspace_bytes, DwPlan* plan) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
+    if (st != SV_OK) return st;
+    if ((st = conv_args_ok(n, taps, C_in, C_out, dtype, SV_KERNEL_AUTO)) != SV_OK) return st;
+    *plan = plan_dw(n, C_in, C_out, dtype == SV_BF16, taps);
+    const size_t need = dw_workspace_bytes(*plan);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SV_ERR_WORKSPACE;
+    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16) return SV_ERR_INVALID_ARG;
+    return SV_OK;
+}
+
+}  // namespace
+
+sv_status sv_sparseconv2d_bwd_dw_partials_k(const void* X, const int32_t* N, const void* dY, float* dW, float* db,
+                                            int64_t n, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                            int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+    DwPlan plan;
+    sv_status st = dw_phase_args(n, K, C_in, C_out, dtype, workspace, workspace_bytes, &plan);
+    if (st != SV_OK) return st;
+    if (!dW || (n > 0 && (!X || !N || !dY))) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_dw_partials(plan, dtype == SV_BF16, X, N, dY, dW, db, n, C_in, C_out,
+                                         accumulate ? 1 : 0, workspace, stream));
+}
+
+sv_status sv_sparseconv2d_bwd_dw_reduce_k(float* dW, float* db, int64_t n, int32_t K, int32_t C_in, int32_t C_out,
+                                          sv_dtype dtype, int32_t accumulate, const void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+    DwPlan plan;
+    sv_status st = dw_phase_args(n, K, C_in, C_out, dtype, workspace, workspace_bytes, &plan);
+    if (st != SV_OK) return st;
+    if (!dW) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_dw_reduce(plan, dW, db, C_in, C_out, accumulate ? 1 : 0, workspace, stream));
+}
+
 // ------------------------------------------------------------ chunk driver
 namespace {
 

@@ -394,9 +394,11 @@ size_t dw_workspace_bytes(const DwPlan& p) {
     return up(p.partial_floats * sizeof(float)) + up(p.db_floats * sizeof(float));
 }
 
-hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t* N, const void* dY,
-                     float* dW, float* db, int64_t n, int Ci, int Co, int accumulate, void* ws,
-                     hipStream_t stream) {
+// Phase 1: the partial kernels (dW straight into dW with one slice, else
+// the slices' partials into the workspace; db partials likewise).
+hipError_t launch_dw_partials(const DwPlan& plan, bool bf16, const void* X, const int32_t* N, const void* dY,
+                              float* dW, float* db, int64_t n, int Ci, int Co, int accumulate, void* ws,
+                              hipStream_t stream) {
     auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
     float* part = static_cast<float*>(ws);
     float* dbpart = reinterpret_cast<float*>(static_cast<char*>(ws) + up(plan.partial_floats * sizeof(float)));
@@ -414,24 +416,31 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
                            static_cast<const uint16_t*>(dY), direct ? dW : part,
                            db ? (direct ? db : dbpart) : nullptr, static_cast<int>(n), Ci, Co, plan.taps,
                            static_cast<int>(plan.slice_tokens), direct ? 1 : 0, accumulate);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    } else {
-        err = launch_dw_valu(bf16, X, N, dY, direct ? dW : part, n, Ci, Co, plan.taps, plan.slices,
-                             plan.slice_tokens, direct ? 1 : 0, accumulate, stream);
-        if (err != hipSuccess) return err;
-        if (db) {
-            dim3 grid(static_cast<unsigned>(ceil_div(Co, 64)), plan.slices);
-            if (bf16)
-                hipLaunchKernelGGL(k_db_partial<uint16_t>, grid, dim3(256), 0, stream,
-                                   static_cast<const uint16_t*>(dY), dbpart, static_cast<int>(n), Co,
-                                   plan.slice_tokens);
-            else
-                hipLaunchKernelGGL(k_db_partial<float>, grid, dim3(256), 0, stream,
-                                   static_cast<const float*>(dY), dbpart, static_cast<int>(n), Co,
-                                   plan.slice_tokens);
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-        }
+        return hipGetLastError();
     }
+    err = launch_dw_valu(bf16, X, N, dY, direct ? dW : part, n, Ci, Co, plan.taps, plan.slices,
+                         plan.slice_tokens, direct ? 1 : 0, accumulate, stream);
+    if (err != hipSuccess || !db) return err;
+    dim3 grid(static_cast<unsigned>(ceil_div(Co, 64)), plan.slices);
+    if (bf16)
+        hipLaunchKernelGGL(k_db_partial<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(dY),
+                           dbpart, static_cast<int>(n), Co, plan.slice_tokens);
+    else
+        hipLaunchKernelGGL(k_db_partial<float>, grid, dim3(256), 0, stream, static_cast<const float*>(dY), dbpart,
+                           static_cast<int>(n), Co, plan.slice_tokens);
+    return hipGetLastError();
+}
+
+// Phase 2: the fixed-order reduction of whatever phase 1 left in the
+// workspace (nothing with one slice on the MFMA path).
+hipError_t launch_dw_reduce(const DwPlan& plan, float* dW, float* db, int Ci, int Co, int accumulate,
+                            const void* ws, hipStream_t stream) {
+    auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+    const float* part = static_cast<const float*>(ws);
+    const float* dbpart =
+        reinterpret_cast<const float*>(static_cast<const char*>(ws) + up(plan.partial_floats * sizeof(float)));
+    const bool direct = plan.slices == 1;
+    hipError_t err = hipSuccess;
     // db partials of the MFMA kernel go through the dW reduction launch.
     bool db_done = db && plan.mfma && direct;
     if (!direct) {
@@ -456,6 +465,14 @@ hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t
         err = hipGetLastError();
     }
     return err;
+}
+
+hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t* N, const void* dY,
+                     float* dW, float* db, int64_t n, int Ci, int Co, int accumulate, void* ws,
+                     hipStream_t stream) {
+    hipError_t err = launch_dw_partials(plan, bf16, X, N, dY, dW, db, n, Ci, Co, accumulate, ws, stream);
+    if (err != hipSuccess) return err;
+    return launch_dw_reduce(plan, dW, db, Ci, Co, accumulate, ws, stream);
 }
 
 }  // namespace svc

@@ -147,6 +147,14 @@ size_t dw_workspace_bytes(const DwPlan& p);
 hipError_t launch_dw(const DwPlan& plan, bool bf16, const void* X, const int32_t* N,
                      const void* dY, float* dW, float* db, int64_t n, int Ci, int Co,
                      int accumulate, void* ws, hipStream_t stream);
+// The two phases of launch_dw, for callers that put them on different
+// streams: the partial kernels, then the fixed-order reduction of the
+// workspace they wrote (same plan, dW, db and workspace).
+hipError_t launch_dw_partials(const DwPlan& plan, bool bf16, const void* X, const int32_t* N,
+                              const void* dY, float* dW, float* db, int64_t n, int Ci, int Co,
+                              int accumulate, void* ws, hipStream_t stream);
+hipError_t launch_dw_reduce(const DwPlan& plan, float* dW, float* db, int Ci, int Co, int accumulate,
+                            const void* ws, hipStream_t stream);
 
 // Asymmetric cross-attention: key blocks of kpb keys, partials in the
 // workspace (fwd_bytes / bwd_bytes), head width d in {64, 128, 256}.

@@ -41,7 +41,9 @@ SYMBOLS = (
     "sv_build_index", "sv_sparseconv2d_fwd", "sv_sparseconv2d_bwd_dx",
     "sv_sparseconv2d_bwd_dw", "sv_workspace_bytes",
     "sv_build_index_k", "sv_sparseconv2d_fwd_k", "sv_sparseconv2d_bwd_dx_k",
-    "sv_sparseconv2d_bwd_dw_k", "sv_workspace_bytes_k", "sv_sparseconv2d_chunked",
+    "sv_sparseconv2d_bwd_dw_k", "sv_workspace_bytes_k",
+    "sv_repack_fwd_k", "sv_sparseconv2d_fwd_packed_k", "sv_sparseconv2d_bwd_dw_partials_k",
+    "sv_sparseconv2d_bwd_dw_reduce_k", "sv_sparseconv2d_chunked",
     "sv_chunked_workspace_bytes", "sv_sparseconv2d_chunked_host", "sv_chunked_host_workspace_bytes",
     "sv_adapter_fwd", "sv_adapter_bwd", "sv_adapter_workspace_bytes",
     "sv_stage_gather", "sv_stage_scatter", "sv_status_string", "sv_version",
@@ -111,6 +113,10 @@ def load(path: str = LIB_PATH):
         "sv_sparseconv2d_bwd_dx_k": ([P, P, P, P, i64, i32, i32, i32, E, E, P], E),
         "sv_sparseconv2d_bwd_dw_k": ([P, P, P, P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
         "sv_workspace_bytes_k": ([E, i64, i32, i32, i32, E], sz),
+        "sv_repack_fwd_k": ([P, i32, i32, i32, E, P, sz, P], E),
+        "sv_sparseconv2d_fwd_packed_k": ([P, P, P, P, P, i64, i32, i32, i32, E, P], E),
+        "sv_sparseconv2d_bwd_dw_partials_k": ([P, P, P, P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
+        "sv_sparseconv2d_bwd_dw_reduce_k": ([P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
         "sv_sparseconv2d_chunked": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32, P, sz, P], E),
         "sv_chunked_workspace_bytes": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32], sz),
         "sv_sparseconv2d_chunked_host": ([ctypes.POINTER(ChunkedHostDesc), ctypes.c_uint32, P, sz, P, P, P], E),
@@ -310,6 +316,44 @@ def sv_sparseconv2d_bwd_dw_k(X, N, dY, dW, db=None, accumulate=False, workspace=
                                          _dt(X), 1 if accumulate else 0, _ptr(workspace), wsb,
                                          _stream(stream))
     _check(st, "sv_sparseconv2d_bwd_dw_k")
+
+
+def sv_repack_fwd_k(Wt, V, stream=None):
+    taps, Ci, Co = Wt.shape
+    wsb = V.numel() * V.element_size()
+    st = load().sv_repack_fwd_k(_ptr(Wt), ksize_of_taps(taps), Ci, Co, _dt(Wt), _ptr(V), wsb, _stream(stream))
+    _check(st, "sv_repack_fwd_k")
+
+
+def sv_sparseconv2d_fwd_packed_k(X, N, V, bias, Y, K, stream=None):
+    n, Ci = X.shape
+    Co = Y.shape[1]
+    assert N.shape == (n, K * K) and Y.shape[0] == n and X.dtype == Y.dtype and N.dtype == torch.int32
+    if bias is not None:
+        assert bias.dtype == X.dtype and bias.shape == (Co,)
+    st = load().sv_sparseconv2d_fwd_packed_k(_ptr(X), _ptr(N), _ptr(V), _ptr(bias), _ptr(Y), n, K, Ci, Co, _dt(X),
+                                             _stream(stream))
+    _check(st, "sv_sparseconv2d_fwd_packed_k")
+
+
+def sv_sparseconv2d_bwd_dw_partials_k(X, N, dY, dW, db, workspace, accumulate=False, stream=None):
+    n, Ci = X.shape
+    taps, Co = dW.shape[0], dY.shape[1]
+    assert dY.shape[0] == n and N.shape == (n, taps) and dW.shape == (taps, Ci, Co) and dW.dtype == torch.float32
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sv_sparseconv2d_bwd_dw_partials_k(_ptr(X), _ptr(N), _ptr(dY), _ptr(dW), _ptr(db), n,
+                                                  ksize_of_taps(taps), Ci, Co, _dt(X), 1 if accumulate else 0,
+                                                  _ptr(workspace), wsb, _stream(stream))
+    _check(st, "sv_sparseconv2d_bwd_dw_partials_k")
+
+
+def sv_sparseconv2d_bwd_dw_reduce_k(dW, db, n, dtype, workspace, accumulate=False, stream=None):
+    taps, Ci, Co = dW.shape
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dt = SV_BF16 if dtype in (torch.bfloat16, SV_BF16, "bf16") else SV_F32
+    st = load().sv_sparseconv2d_bwd_dw_reduce_k(_ptr(dW), _ptr(db), int(n), ksize_of_taps(taps), Ci, Co, dt,
+                                                1 if accumulate else 0, _ptr(workspace), wsb, _stream(stream))
+    _check(st, "sv_sparseconv2d_bwd_dw_reduce_k")
 
 
 def make_chunked_desc(T, H, W, coords, frame_offsets, frame_offsets_host, C_in, C_out, dtype,

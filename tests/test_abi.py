@@ -268,3 +268,28 @@ def test_adapter_validation_and_workspace(lib):
     assert lib.sv_adapter_bwd(*bargs, BF16, 0, ctypes.c_void_p(4097), 1 << 30, None) == ops.SV_ERR_INVALID_ARG
     nodw = bargs[:13] + (None,) + bargs[14:]
     assert lib.sv_adapter_bwd(*nodw, BF16, 0, FAKE, 1 << 30, None) == ops.SV_ERR_INVALID_ARG
+
+
+def test_split_forms_validation(lib):
+    F32, BF16 = ops.SV_F32, ops.SV_BF16
+    need = lib.sv_workspace_bytes_k(ops.SV_OP_FWD, 8, 3, 64, 64, BF16)
+    assert lib.sv_repack_fwd_k(FAKE, 3, 64, 64, F32, FAKE, need, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_repack_fwd_k(FAKE, 3, 64, 64, BF16, FAKE, need - 1, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_repack_fwd_k(FAKE, 4, 64, 64, BF16, FAKE, need, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_repack_fwd_k(None, 3, 64, 64, BF16, FAKE, need, None) == ops.SV_ERR_INVALID_ARG
+    # the packed forward runs only on the matrix cores
+    assert lib.sv_sparseconv2d_fwd_packed_k(FAKE, FAKE, FAKE, None, FAKE, 8, 3, 48, 64, BF16, None) == \
+        ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_fwd_packed_k(FAKE, FAKE, FAKE, None, FAKE, 8, 3, 64, 64, F32, None) == \
+        ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_fwd_packed_k(FAKE, FAKE, None, None, FAKE, 8, 3, 64, 64, BF16, None) == \
+        ops.SV_ERR_INVALID_ARG
+    dneed = lib.sv_workspace_bytes_k(ops.SV_OP_DW, 22656, 3, 256, 256, BF16)
+    assert lib.sv_sparseconv2d_bwd_dw_partials_k(FAKE, FAKE, FAKE, FAKE, None, 22656, 3, 256, 256, BF16, 0, FAKE,
+                                                 dneed - 1, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_sparseconv2d_bwd_dw_reduce_k(FAKE, None, 22656, 3, 256, 256, BF16, 0, FAKE, dneed - 1,
+                                               None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_sparseconv2d_bwd_dw_reduce_k(None, None, 22656, 3, 256, 256, BF16, 0, FAKE, dneed,
+                                               None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_bwd_dw_partials_k(FAKE, FAKE, FAKE, FAKE, None, 22656, 6, 256, 256, BF16, 0, FAKE,
+                                                 dneed, None) == ops.SV_ERR_INVALID_ARG

@@ -144,7 +144,8 @@ def test_chunked_kxk(K):
     N = ops.build_index(coords, offs, L.T, L.H, L.W, K=K)
     assert torch.equal(Y, ops.sparseconv2d_fwd(X, N, Wt, b))
     assert torch.equal(dX, ops.sparseconv2d_bwd_dx(dY, N, Wt))
-    Nr = host(N)
+    st, Nr, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K=K)
+    assert np.array_equal(host(N), Nr)
     assert_close(host(dW), O.bwd_dw(L.X, Nr, L.dY), "bf16", f"chunked K={K} dW")
     assert_close(host(db), O.bwd_db(L.dY), "bf16", f"chunked K={K} db")
 
@@ -176,3 +177,45 @@ def test_full_size_layer_kxk(K):
                                    rng.choice(taps * C, size=24, replace=False)])).astype(np.int64)
     assert_close(host(dW).reshape(taps * C, -1)[ji], O.bwd_dw_rows(L.X, Nr, L.dY, ji), "bf16", f"K={K} dW")
     assert_close(host(db), O.bwd_db(L.dY), "bf16", f"K={K} db")
+
+
+@pytest.mark.parametrize("K", [3, 5])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_split_forms_equal_single_calls(dt, K):
+    """Repacked weights then the packed forward equal the forward call; the
+    dW partials then their reduction (on a second stream) equal the dW call:
+    bit for bit."""
+    L = wl.make_random_case(70 + K, 3, 14, 14, 0.5, 128, 128, dt, ksize=K)
+    t = tdtype(dt)
+    st, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K=K)
+    X, Wt, b, dY, Nd = dev(L.X, t), dev(L.Wt, t), dev(L.b, t), dev(L.dY, t), dev(N)
+    n, taps = L.n, K * K
+    dW1 = torch.empty((taps, 128, 128), dtype=torch.float32, device="cuda")
+    db1 = torch.empty((128,), dtype=torch.float32, device="cuda")
+    ops.sv_sparseconv2d_bwd_dw_k(X, Nd, dY, dW1, db1)
+    dW2, db2 = torch.full_like(dW1, 5.0), torch.full_like(db1, 5.0)
+    ws = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_DW, n, K, 128, 128, t)), dtype=torch.uint8,
+                     device="cuda")
+    ops.sv_sparseconv2d_bwd_dw_partials_k(X, Nd, dY, dW2, db2, ws)
+    done = torch.cuda.Event()
+    done.record()
+    other = torch.cuda.Stream()
+    other.wait_event(done)
+    ops.sv_sparseconv2d_bwd_dw_reduce_k(dW2, db2, n, t, ws, stream=other)
+    torch.cuda.current_stream().wait_stream(other)
+    torch.cuda.synchronize()
+    assert torch.equal(dW1, dW2) and torch.equal(db1, db2)
+    if dt == "bf16":
+        Y1 = ops.sparseconv2d_fwd(X, Nd, Wt, b)
+        V = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_FWD, n, K, 128, 128, t)), dtype=torch.uint8,
+                        device="cuda")
+        ops.sv_repack_fwd_k(Wt, V)
+        Y2 = torch.empty_like(Y1)
+        ops.sv_sparseconv2d_fwd_packed_k(X, Nd, V, b, Y2, K)
+        torch.cuda.synchronize()
+        assert torch.equal(Y1, Y2)
+    else:
+        V = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+        with pytest.raises(ops.SvError) as e:
+            ops.sv_repack_fwd_k(Wt, V)
+        assert e.value.status == ops.SV_ERR_UNSUPPORTED
