@@ -276,16 +276,16 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
         }
     }
 
-    // ---- epilogue: bias (and residual), round to bf16, stage the 128 x 128 tile in LDS
-    // (rows 0-63 over the window, rows 64-127 over the weight buffers), then
-    // write whole 16-byte row pieces.
+    // ---- epilogue.  Without a residual: bias, round to bf16, stage the
+    // 128 x 128 tile in LDS (rows 0-63 over the window, rows 64-127 over the
+    // weight buffers), then write whole 16-byte row pieces.
     constexpr int OLD = CM_BN + 8;      // 272-byte pitch: rows 4 apart in opposite bank halves
     static_assert(64 * OLD <= (CM_WIN + 1) * CM_LDA && 64 * OLD <= 2 * CM_SB,
                   "output tile halves must fit the window and the weight buffers");
     uint16_t* const sOutLo = sA;
     uint16_t* const sOutHi = &sB[0][0];
-    __syncthreads();
     if (!RES) {
+        __syncthreads();
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int cl = wn * 64 + nb * 32 + l32;
@@ -299,51 +299,77 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
                         (wm ? sOutHi : sOutLo)[(mb * 32 + g * 8 + lhi * 4 + q) * OLD + cl] =
                             f32_to_bf16(acc[mb][nb][g * 4 + q] + bv);
         }
-    } else {
-        // Residual: all 64 values of the thread requested at once (raw
-        // buffer loads; entries past n or NO get an out-of-range offset and
-        // read as zero), so one wait covers them.  Lanes 0-31 and 32-63 each
-        // read 64 contiguous bytes of one row.
-        const rsrc_t rR = make_rsrc(res, static_cast<uint32_t>(n) * NO * 2);
-        uint16_t rv[2][2][16];
+        __syncthreads();
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int cl = wn * 64 + nb * 32 + l32;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int rl = mb * 32 + (e >> 2) * 8 + lhi * 4 + (e & 3);
-                    const int64_t row = k0 + wm * 64 + rl;
-                    const uint32_t off = (n0 + cl < NO && row < n)
-                                             ? static_cast<uint32_t>(row * NO + n0 + cl) * 2u : kOob;
-                    rv[nb][mb][e] = __builtin_amdgcn_raw_buffer_load_b16(rR, off, 0, 0);
-                }
+        for (int u = 0; u < (CM_BM * CM_BN / 8) / 256; ++u) {
+            const int q = tid + 256 * u;
+            const int rl = q >> 4, ch = q & 15;
+            const int64_t row = k0 + rl;
+            const int col = n0 + ch * 8;
+            if (row < n && col < NO)
+                *reinterpret_cast<uint4*>(out + row * NO + col) =
+                    *reinterpret_cast<const uint4*>(&(rl < 64 ? sOutLo : sOutHi)[(rl & 63) * OLD + ch * 8]);
         }
+        return;
+    }
+    // With a residual: the fp32 sums (bias included) are staged in LDS a
+    // quarter tile per region (pass mb holds rows wm*64 + mb*32 .. +31 of
+    // both halves: wm = 0 over the window, wm = 1 over the weight buffers),
+    // and every thread then adds 16-byte pieces of the residual row and
+    // writes 16-byte pieces of the output, rounding once.  The residual
+    // pieces are requested before the first barrier (rows past n read as
+    // zero through an out-of-range offset; NO % 16 == 0 keeps every piece
+    // wholly inside or outside the row).
+    constexpr int OLF = CM_BN + 8;      // 544-byte pitch: rows 4 apart 32 banks apart
+    static_assert(32 * OLF * 4 <= (CM_WIN + 1) * CM_LDA * 2 && 32 * OLF * 4 <= 2 * CM_SB * 2,
+                  "an fp32 quarter tile must fit the window and the weight buffers");
+    float* const fLo = reinterpret_cast<float*>(sA);
+    float* const fHi = reinterpret_cast<float*>(&sB[0][0]);
+    const rsrc_t rR = make_rsrc(res, static_cast<uint32_t>(n) * NO * 2);
+    uint4 rres[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = tid + 256 * u;
+            const int h = q >> 9, r = (q >> 4) & 31, ch = q & 15;
+            const int64_t row = k0 + h * 64 + mb * 32 + r;
+            const int col = n0 + ch * 8;
+            rres[mb][u] = load16(rR, (row < n && col < NO) ? static_cast<uint32_t>((row * NO + col) * 2) : kOob);
+        }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        __syncthreads();                // the rounds (mb = 0) or the previous pass's reads are done
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int cl = wn * 64 + nb * 32 + l32;
             const float bv = (bias && n0 + cl < NO) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int rl = mb * 32 + (e >> 2) * 8 + lhi * 4 + (e & 3);
-                    (wm ? sOutHi : sOutLo)[rl * OLD + cl] =
-                        f32_to_bf16(acc[mb][nb][e] + bv + bf16_to_f32(rv[nb][mb][e]));
-                }
+            for (int e = 0; e < 16; ++e)
+                (wm ? fHi : fLo)[((e >> 2) * 8 + lhi * 4 + (e & 3)) * OLF + cl] = acc[mb][nb][e] + bv;
         }
-    }
-    __syncthreads();
+        __syncthreads();
 #pragma unroll
-    for (int u = 0; u < (CM_BM * CM_BN / 8) / 256; ++u) {
-        const int q = tid + 256 * u;
-        const int rl = q >> 4, ch = q & 15;
-        const int64_t row = k0 + rl;
-        const int col = n0 + ch * 8;
-        if (row < n && col < NO)
-            *reinterpret_cast<uint4*>(out + row * NO + col) =
-                *reinterpret_cast<const uint4*>(&(rl < 64 ? sOutLo : sOutHi)[(rl & 63) * OLD + ch * 8]);
+        for (int u = 0; u < 4; ++u) {
+            const int q = tid + 256 * u;
+            const int h = q >> 9, r = (q >> 4) & 31, ch = q & 15;
+            const int64_t row = k0 + h * 64 + mb * 32 + r;
+            const int col = n0 + ch * 8;
+            const float* src = (h ? fHi : fLo) + r * OLF + ch * 8;
+            const float4 a = *reinterpret_cast<const float4*>(src);
+            const float4 b = *reinterpret_cast<const float4*>(src + 4);
+            const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            const uint32_t w[4] = {rres[mb][u].x, rres[mb][u].y, rres[mb][u].z, rres[mb][u].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t lo = f32_to_bf16(v[2 * p] + bf16_to_f32(static_cast<uint16_t>(w[p] & 0xffffu)));
+                const uint32_t hi = f32_to_bf16(v[2 * p + 1] + bf16_to_f32(static_cast<uint16_t>(w[p] >> 16)));
+                o[p] = lo | (hi << 16);
+            }
+            if (row < n && col < NO)
+                *reinterpret_cast<uint4*>(out + row * NO + col) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
     }
 }
 
