@@ -22,7 +22,7 @@ def pinned(a, dtype=None):
     return t.pin_memory()
 
 
-def run_both(L, chunk_frames, passes, dt=torch.bfloat16, kernel="auto"):
+def run_both(L, chunk_frames, passes, dt=torch.bfloat16, kernel="auto", ksize=3):
     n, Ci, Co = L.n, L.X.shape[1], L.Wt.shape[2]
     Wt, b = dev(L.Wt, dt), dev(L.b, dt)
     # device driver
@@ -30,11 +30,11 @@ def run_both(L, chunk_frames, passes, dt=torch.bfloat16, kernel="auto"):
     X, dY = dev(L.X, dt), dev(L.dY, dt)
     Y = torch.zeros((n, Co), dtype=dt, device="cuda")
     dX = torch.zeros((n, Ci), dtype=dt, device="cuda")
-    dW = torch.zeros((9, Ci, Co), dtype=torch.float32, device="cuda")
+    dW = torch.zeros((ksize * ksize, Ci, Co), dtype=torch.float32, device="cuda")
     db = torch.zeros((Co,), dtype=torch.float32, device="cuda")
     offs_h = torch.from_numpy(L.frame_offsets.copy())
     d = ops.make_chunked_desc(L.T, L.H, L.W, coords, offs, offs_h, Ci, Co, dt, chunk_frames, X=X, Wt=Wt,
-                              bias=b, Y=Y, dY=dY, dX=dX, dW=dW, db=db, kernel=kernel)
+                              bias=b, Y=Y, dY=dY, dX=dX, dW=dW, db=db, kernel=kernel, ksize=ksize)
     ws = torch.empty(max(256, ops.sv_chunked_workspace_bytes(d, passes)), dtype=torch.uint8, device="cuda")
     ops.sv_sparseconv2d_chunked(d, passes, ws)
     # host-streamed driver
@@ -46,7 +46,7 @@ def run_both(L, chunk_frames, passes, dt=torch.bfloat16, kernel="auto"):
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     hd = ops.make_chunked_host_desc(L.T, L.H, L.W, pinned(L.coords), pinned(L.frame_offsets), Ci, Co, dt,
                                     chunk_frames, X_host=Xh, Wt=Wt, bias=b, Y_host=Yh, dY_host=dYh,
-                                    dX_host=dXh, dW=dW2, db=db2, err_flag=flag, kernel=kernel)
+                                    dX_host=dXh, dW=dW2, db=db2, err_flag=flag, kernel=kernel, ksize=ksize)
     hwsb = ops.sv_chunked_host_workspace_bytes(hd, passes)
     assert hwsb >= ops.sv_chunked_workspace_bytes(d, passes)
     hws = torch.empty(max(256, hwsb), dtype=torch.uint8, device="cuda")
@@ -93,6 +93,15 @@ def test_ragged_chunks_and_empty_frames(passes):
         assert same(dX, dXh)
     if passes & ops.SV_PASS_DW:
         assert same(dW, dW2) and same(db, db2)
+
+
+@pytest.mark.parametrize("ksize", [1, 5])
+def test_kxk_descriptor(ksize):
+    """A K x K descriptor through both drivers (ragged chunks, an empty frame)."""
+    L = wl.make_random_case(33 + ksize, 5, 14, 14, [60, 0, 120, 7, 196], 128, 128, "bf16", ksize=ksize)
+    print("host-streamed K =", ksize, "n =", L.n, flush=True)
+    (Y, dX, dW, db), (Yh, dXh, dW2, db2) = run_both(L, 2, ALL, ksize=ksize)
+    assert same(Y, Yh) and same(dX, dXh) and same(dW, dW2) and same(db, db2)
 
 
 def test_fp32_valu_kernels():
