@@ -52,12 +52,10 @@ namespace svc {
 constexpr int CM_BM = 128;              // tokens per tile
 constexpr int CM_BN = 128;              // output channels per tile
 constexpr int CM_KC = 64;               // channels per round
-constexpr int CM_WIN = 192;             // window rows held in LDS
-constexpr int CM_ZROW = CM_WIN;         // an all-zero row: target of -1 entries
+constexpr int CM_WIN = 192;             // window rows held in LDS (more than one tap)
 constexpr int CM_LDA = CM_KC + 8;       // 144 B pitch: conflict-free 16-byte row reads
 constexpr int CM_LDB = CM_KC;           // weight tile rows: 128 B, XOR-swizzled 16-byte chunks
 constexpr int CM_SB = CM_BN * CM_LDB;
-constexpr int CM_WREGS = (CM_WIN * (CM_KC / 8) + 255) / 256;   // window pieces per thread (6)
 
 // One round: 4 k-steps of 16, all fragments read first, then 16 MFMAs.
 __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const uint16_t* __restrict__ sb,
@@ -93,7 +91,17 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
                                                       const uint16_t* __restrict__ bias,
                                                       const uint16_t* __restrict__ res,
                                                       uint16_t* __restrict__ out, int n, int K, int NO) {
-    __shared__ __align__(16) uint16_t sA[(CM_WIN + 1) * CM_LDA];
+    // Window rows held in LDS: 192 (a tile's rows and the neighbours around
+    // them).  With one tap the window is the tile's own 128 rows, and two
+    // windows are held, double-buffered like the weight tiles: one barrier
+    // per round instead of two, and the next window's store no longer waits
+    // for every wave to leave the current one.
+    constexpr bool DBW = TAPS == 1;
+    constexpr int WIN = DBW ? CM_BM : CM_WIN;
+    constexpr int ZROW = WIN;                      // an all-zero row: target of -1 entries
+    constexpr int WBUF = (WIN + 1) * CM_LDA;       // one window buffer
+    constexpr int WREGS = (WIN * (CM_KC / 8) + 255) / 256;
+    __shared__ __align__(16) uint16_t sA[(DBW ? 2 : 1) * WBUF];
     __shared__ __align__(16) uint16_t sB[2][CM_SB];   // weight tiles, written by direct loads
     __shared__ int sN[CM_BM * TAPS];
     __shared__ short sRow[CM_BM * TAPS];
@@ -115,8 +123,8 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     const int R = nchunks * TAPS;
 
     if (tid == 0) { sLo = 0x7fffffff; sHi = -1; }
-    if (tid < CM_KC / 8)
-        *reinterpret_cast<uint4*>(&sA[CM_ZROW * CM_LDA + tid * 8]) = make_uint4(0, 0, 0, 0);
+    if (tid < (DBW ? 2 : 1) * (CM_KC / 8))
+        *reinterpret_cast<uint4*>(&sA[(tid >> 3) * WBUF + ZROW * CM_LDA + (tid & 7) * 8]) = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
     // ---- the tile's slice of N, its row range, and the LDS row of every entry
@@ -154,10 +162,10 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     __syncthreads();
     const int wlo = sLo;
     const int span = (sHi >= 0) ? sHi - wlo + 1 : 0;
-    const bool window = span <= CM_WIN;
+    const bool window = span <= WIN;
     for (int e = tid; e < CM_BM * TAPS; e += 256) {
         const int m = sN[e];
-        sRow[e] = static_cast<short>(m < 0 ? CM_ZROW : (window ? m - wlo : e / TAPS));
+        sRow[e] = static_cast<short>(m < 0 ? ZROW : (window ? m - wlo : e / TAPS));
     }
 
     // ---- staging helpers: raw buffer loads, 16-byte pieces.  Pieces outside
@@ -171,19 +179,19 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     auto load_window = [&](int c, uint4* regs) {
         const int c0 = c * CM_KC, kc = kc_of(c);
 #pragma unroll
-        for (int u = 0; u < CM_WREGS; ++u) {
+        for (int u = 0; u < WREGS; ++u) {
             const int q = tid + 256 * u;
             const int r = q >> 3, ch = q & 7;
             const bool ok = r < span && ch * 8 < kc;
             regs[u] = load16(rA, ok ? (static_cast<uint32_t>(wlo + r) * K + c0 + ch * 8) * 2 : kOob);
         }
     };
-    auto store_window = [&](const uint4* regs) {
+    auto store_window = [&](const uint4* regs, int buf) {
 #pragma unroll
-        for (int u = 0; u < CM_WREGS; ++u) {
+        for (int u = 0; u < WREGS; ++u) {
             const int q = tid + 256 * u;
-            const int r = q >> 3, ch = q & 7;     // r < CM_WIN: rows past span hold zeros
-            *reinterpret_cast<uint4*>(&sA[r * CM_LDA + ch * 8]) = regs[u];
+            const int r = q >> 3, ch = q & 7;     // r < WIN: rows past span hold zeros
+            *reinterpret_cast<uint4*>(&sA[buf * WBUF + r * CM_LDA + ch * 8]) = regs[u];
         }
     };
     // Weight tile of round rr (chunk rr / TAPS, tap rr % TAPS): B[P-j][n0 + nn][c0 + ...],
@@ -240,10 +248,10 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
-    uint4 wreg[CM_WREGS];
+    uint4 wreg[WREGS];
     if (window && span > 0) {
         load_window(0, wreg);
-        store_window(wreg);
+        store_window(wreg, 0);
     }
     issue_B(0, 0);
     __syncthreads();                      // also waits for the direct loads
@@ -266,11 +274,15 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
         // Always the full 4 k-steps: a 32-channel tail chunk is zero-filled
         // past its end in both operands, and one code path keeps the
         // accumulators in fixed registers.
-        mma_round(sA, sB[r & 1], arow, acc);
+        mma_round(sA + (DBW && window ? (c & 1) * WBUF : 0), sB[r & 1], arow, acc);
         if (r + 1 < R) {
-            if (window && span > 0 && (r + 1) % TAPS == 0) {
+            if (DBW) {
+                // the other window buffer was last read in round r - 1,
+                // before the previous barrier
+                if (window && span > 0) store_window(wreg, (c + 1) & 1);
+            } else if (window && span > 0 && (r + 1) % TAPS == 0) {
                 __syncthreads();           // every wave is done with this chunk's window
-                store_window(wreg);
+                store_window(wreg, 0);
             }
             __syncthreads();
         }
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     // 128 x 128 tile in LDS (rows 0-63 over the window, rows 64-127 over the
     // weight buffers), then write whole 16-byte row pieces.
     constexpr int OLD = CM_BN + 8;      // 272-byte pitch: rows 4 apart in opposite bank halves
-    static_assert(64 * OLD <= (CM_WIN + 1) * CM_LDA && 64 * OLD <= 2 * CM_SB,
+    static_assert(64 * OLD <= (DBW ? 2 : 1) * WBUF && 64 * OLD <= 2 * CM_SB,
                   "output tile halves must fit the window and the weight buffers");
     uint16_t* const sOutLo = sA;
     uint16_t* const sOutHi = &sB[0][0];
@@ -321,7 +333,7 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     // zero through an out-of-range offset; NO % 16 == 0 keeps every piece
     // wholly inside or outside the row).
     constexpr int OLF = CM_BN + 8;      // 544-byte pitch: rows 4 apart 32 banks apart
-    static_assert(32 * OLF * 4 <= (CM_WIN + 1) * CM_LDA * 2 && 32 * OLF * 4 <= 2 * CM_SB * 2,
+    static_assert(32 * OLF * 4 <= (DBW ? 2 : 1) * WBUF * 2 && 32 * OLF * 4 <= 2 * CM_SB * 2,
                   "an fp32 quarter tile must fit the window and the weight buffers");
     float* const fLo = reinterpret_cast<float*>(sA);
     float* const fHi = reinterpret_cast<float*>(&sB[0][0]);
