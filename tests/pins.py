@@ -427,6 +427,32 @@ def pin_xattn_permutation_and_extremes(orc):
     assert np.array_equal(dQ, np.zeros((3, 8))) and dX.shape == (0, 8)
 
 
+def pin_index_invariants(orc):
+    """Properties every table must have, checked directly on the oracle's
+    N for K = 1, 3, 5: the centre column is the token itself; the mirror
+    property (token m is tap j of k exactly when k is tap K*K-1-j of m);
+    every entry lies in the token's own frame at the right cell; and, for
+    ascending packing inside a frame, |N[k, j] - k| <= (K/2)(W + 1)."""
+    for K in (1, 3, 5):
+        taps, r = K * K, K // 2
+        for c in CASES:
+            L = case_layer(c)
+            st, N, _ = orc.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K=K)
+            assert st == 0
+            n = L.n
+            f = frame_of(L.frame_offsets)
+            assert np.array_equal(N[:, taps // 2], np.arange(n)), (K, c)
+            k, j = np.nonzero(N >= 0)
+            m = N[k, j]
+            assert np.array_equal(N[m, taps - 1 - j], k), (K, c)
+            assert np.array_equal(f[m], f[k]), (K, c)
+            ym, xm = np.divmod(L.coords[m], L.W)
+            yk, xk = np.divmod(L.coords[k], L.W)
+            assert np.array_equal(ym - yk, j // K - r) and np.array_equal(xm - xk, j % K - r), (K, c)
+            if not c[-1]:               # ascending packing
+                assert np.all(np.abs(m - k) <= r * (L.W + 1)), (K, c)
+
+
 # ------------------------------------------------------------ K x K kernels
 # The Background states the idea for K x K neighbourhoods; the page's tables
 # and kernels are 3 x 3.  The same definitions with K = 1, 5, 7.
@@ -557,6 +583,7 @@ ALL_PINS = [
     pin_golden_frames_2x2,
     pin_index_bruteforce,
     pin_index_errors,
+    pin_index_invariants,
     pin_keep_all_is_dense_conv,
     pin_fwd_dense_recon,
     pin_bwd_autograd,
