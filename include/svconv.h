@@ -3,8 +3,9 @@
  *
  * C ABI.  Plain pointers and sizes only; every pointer argument named "device"
  * is device memory owned by the caller; the library never allocates, never
- * frees, never synchronises the stream and keeps no state other than a cached
- * device property.  All work is enqueued asynchronously on the caller's
+ * frees, never synchronises the stream (unless the SV_SYNC_CHECK debugging
+ * aid below is switched on) and keeps no state other than a cached device
+ * property.  All work is enqueued asynchronously on the caller's
  * hipStream_t (NULL = the default stream).  No C++ exception crosses this
  * boundary.  Status codes report argument errors synchronously, before any
  * work is enqueued; data errors found on the device (coordinates) are OR-ed
@@ -94,7 +95,14 @@ typedef enum sv_op { SV_OP_FWD = 0, SV_OP_DX = 1, SV_OP_DW = 2 } sv_op;
  *                 cleared by the library).  Tokens with a bad coordinate get
  *                 an all -1 row; with duplicates N is unspecified.
  * Returns SV_ERR_INVALID_ARG for null required pointers or bad sizes,
- * SV_ERR_UNSUPPORTED for H*W > 16384. */
+ * SV_ERR_UNSUPPORTED for H*W > 16384.
+ *
+ * Debugging aid: with SV_SYNC_CHECK=1 in the environment (read at every
+ * call), this call and the chunk drivers wait for their stream after
+ * enqueuing and return the device flag's verdict instead (SV_ERR_COORD_RANGE,
+ * SV_ERR_DUPLICATE_COORD, or SV_ERR_INVALID_ARG for SV_FLAG_BAD_OFFSETS).
+ * The flag is never cleared by the library, so earlier bits count too.
+ * Without the variable nothing ever synchronises. */
 sv_status sv_build_index(const int32_t *coords, const int32_t *frame_offsets,
                          int32_t T, int32_t H, int32_t W, int64_t n,
                          int32_t *N_out, int32_t *M_out, int32_t *err_flag,

@@ -6,6 +6,7 @@
 #include "internal.h"
 
 #include <cmath>
+#include <cstdlib>
 
 using namespace svc;
 
@@ -28,6 +29,23 @@ sv_status taps_of(int32_t K, int* taps) {
 }
 
 bool valid_dtype(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
+
+// Opt-in check for debugging (SV_SYNC_CHECK=1 in the environment, read at
+// every call): after enqueuing an index build the call waits for its stream
+// and turns the bits of the device error flag into a status.  The flag
+// accumulates, so a bit set by an earlier call is reported again.
+sv_status sync_check(const int32_t* err_flag, hipStream_t stream) {
+    const char* e = getenv("SV_SYNC_CHECK");
+    if (!err_flag || !e || e[0] != '1') return SV_OK;
+    int32_t f = 0;
+    if (hipMemcpyAsync(&f, err_flag, sizeof(f), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return SV_ERR_HIP;
+    if (f & SV_FLAG_BAD_OFFSETS) return SV_ERR_INVALID_ARG;
+    if (f & SV_FLAG_COORD_RANGE) return SV_ERR_COORD_RANGE;
+    if (f & SV_FLAG_DUPLICATE) return SV_ERR_DUPLICATE_COORD;
+    return SV_OK;
+}
 bool valid_kernel(sv_kernel k) { return k == SV_KERNEL_AUTO || k == SV_KERNEL_VALU || k == SV_KERNEL_MFMA; }
 sv_status hip_status(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
 size_t align_up(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -97,8 +115,10 @@ sv_status sv_build_index_k(const int32_t* coords, const int32_t* frame_offsets, 
     if (!frame_offsets || (n > 0 && (!coords || !N_out))) return SV_ERR_INVALID_ARG;
     if (static_cast<int64_t>(H) * W > kMaxCells) return SV_ERR_UNSUPPORTED;
     if (T == 0) return SV_OK;
-    return hip_status(launch_build_index(coords, frame_offsets, 0, T, H, W, K, n, 0, N_out, M_out,
-                                         err_flag, stream));
+    if ((st = hip_status(launch_build_index(coords, frame_offsets, 0, T, H, W, K, n, 0, N_out, M_out, err_flag,
+                                            stream))) != SV_OK)
+        return st;
+    return sync_check(err_flag, stream);
 }
 
 sv_status sv_build_index(const int32_t* coords, const int32_t* frame_offsets, int32_t T, int32_t H,
@@ -388,7 +408,7 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
         return hip_status(launch_dw(plan, d->dtype == SV_BF16, d->X, Nc, d->dY, d->dW, d->db, 0, d->C_in,
                                     d->C_out, 0, dws, stream));
     }
-    return SV_OK;
+    return sync_check(d->err_flag, stream);
 }
 
 // ------------------------------------------------- host-streamed chunk driver
@@ -629,7 +649,7 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
     };
     const sv_status result = run();
     for (int i = 0; i < 3 * kSets + 1; ++i) (void)hipEventDestroy(ev[i]);
-    return result;
+    return result != SV_OK ? result : sync_check(d->err_flag, compute);
 }
 
 // ------------------------------------------------------ bottleneck adapter

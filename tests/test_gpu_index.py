@@ -98,3 +98,38 @@ def test_index_grid_too_large_rejected():
     with pytest.raises(ops.SvError) as ei:
         ops.sv_build_index(c, o, 1, 129, 128, N)
     assert ei.value.status == ops.SV_ERR_UNSUPPORTED
+
+
+def test_sync_check_turns_the_flag_into_a_status(monkeypatch):
+    """SV_SYNC_CHECK=1: the index build and the chunk driver wait for their
+    stream and return the device flag's verdict."""
+    c, o = dev(np.array([0, 5, 5], np.int32)), dev(np.array([0, 3], np.int32))
+    N = torch.empty((3, 9), dtype=torch.int32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ops.sv_build_index(c, o, 1, 3, 4, N, None, flag)          # off: no status
+    torch.cuda.synchronize()
+    assert int(flag.item()) & ops.SV_FLAG_DUPLICATE
+    monkeypatch.setenv("SV_SYNC_CHECK", "1")
+    flag.zero_()
+    with pytest.raises(ops.SvError) as e:
+        ops.sv_build_index(c, o, 1, 3, 4, N, None, flag)
+    assert e.value.status == ops.SV_ERR_DUPLICATE_COORD
+    flag.zero_()
+    c2 = dev(np.array([0, 5, 12], np.int32))
+    with pytest.raises(ops.SvError) as e:
+        ops.sv_build_index(c2, o, 1, 3, 4, N, None, flag)
+    assert e.value.status == ops.SV_ERR_COORD_RANGE
+    # a clean call passes, and the chunk driver reports through the same path
+    flag.zero_()
+    ops.sv_build_index(dev(np.array([0, 5, 11], np.int32)), o, 1, 3, 4, N, None, flag)
+    offs_h = torch.tensor([0, 3], dtype=torch.int32)
+    X = torch.zeros((3, 8), dtype=torch.float32, device="cuda")
+    Wt = torch.zeros((9, 8, 8), dtype=torch.float32, device="cuda")
+    Y = torch.empty((3, 8), dtype=torch.float32, device="cuda")
+    d = ops.make_chunked_desc(1, 3, 4, c, o, offs_h, 8, 8, torch.float32, 1, X=X, Wt=Wt, Y=Y, err_flag=flag)
+    ws = torch.empty(max(256, ops.sv_chunked_workspace_bytes(d, ops.SV_PASS_FWD)), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ops.SvError) as e:
+        ops.sv_sparseconv2d_chunked(d, ops.SV_PASS_FWD, ws)
+    assert e.value.status == ops.SV_ERR_DUPLICATE_COORD
+    monkeypatch.delenv("SV_SYNC_CHECK")
+    torch.cuda.synchronize()
