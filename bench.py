@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "SparseConv2D fwd+bwd effective TFLOP/s & HBM GB/s vs roofline, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
+HBM_TBPS = 8.0               # MI355X HBM3E
 PCIE_GBPS_PER_DIRECTION = 64.0   # PCIe 5.0 x16 host link, one direction
 PEAK_F32_TFLOPS = 157.3      # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
@@ -49,6 +50,9 @@ def parse():
                    help="single-layer workloads: K of a K x K neighbourhood (weights of the same "
                         "distribution, std 1/sqrt(K*K*C))")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cold", action="store_true",
+                   help="c5 and single-layer workloads: write a 1 GiB scratch buffer between steps (outside "
+                        "the timed events) so that no input stays in the caches; warm (default) is primary")
     p.add_argument("--dw-stream", choices=["side", "same"], default="side",
                    help="run each layer's weight gradient on a second stream, concurrent with its "
                         "input gradient (side), or in order on one stream (same)")
@@ -338,6 +342,36 @@ class Events:
         return out
 
 
+def timed_cold(torch, step, steps):
+    """Seconds of `steps` steps, each timed by HIP events on the current
+    stream, with 1 GiB of scratch written between steps (outside the
+    events): the 256 MB MALL and the L2s then hold none of the inputs."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    total = 0.0
+    for i in range(steps):
+        scratch.fill_(i & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        e1.synchronize()
+        total += e0.elapsed_time(e1) * 1e-3
+    del scratch
+    return total
+
+
+def host_cpu():
+    """The host CPU's model name, for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def source_sha(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -426,11 +460,14 @@ def layer_workload(args):
         step()
     torch.cuda.reset_peak_memory_stats()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / args.steps
+    if args.cold:
+        sec = timed_cold(torch, step, args.steps) / args.steps
+    else:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / args.steps
     # each pass alone (device time of `steps` back-to-back calls)
     pass_ms = {}
     if not chunked:
@@ -443,8 +480,14 @@ def layer_workload(args):
             torch.cuda.synchronize()
             pass_ms[name] = round(e0.elapsed_time(e1) / args.steps, 4)
     fl = len(passes) * 2 * n * taps * C * C
+    # gather model per conv pass: every neighbour row read from memory, no reuse
+    gather_bytes = n * (taps * 2 * C + 2 * C + 4 * taps)
+    gather_gbps = {k: round(gather_bytes / (v * 1e-3) / 1e9, 1) for k, v in pass_ms.items() if k != "index"}
+    valid = None if chunked else round(float((N >= 0).sum().item()) / max(N.numel(), 1), 4)
     print(json.dumps({"workload": args.workload, "name": cfg["name"], "kernel": args.kernel, "ksize": K, "n": n,
-                      "ms_per_step": round(sec * 1e3, 4), "pass_ms": pass_ms, "tflops": round(fl / sec / 1e12, 3),
+                      "cache": "cold" if args.cold else "warm", "valid_tap_fraction": valid,
+                      "ms_per_step": round(sec * 1e3, 4), "pass_ms": pass_ms, "gbps_gather_model": gather_gbps,
+                      "tflops": round(fl / sec / 1e12, 3),
                       "frac_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "peak_mem_mb": round(torch.cuda.max_memory_allocated() / 2 ** 20, 1),
                       "workspace_mb": round(ws.numel() / 2 ** 20, 2)}), flush=True)
@@ -661,11 +704,14 @@ def main():
 
     # timed region: K steps, no instrumentation
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run.step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if args.cold:
+        wall = timed_cold(torch, run.step, args.steps)
+    else:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run.step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
     fl = run.flops()
     tflops = fl / (wall / args.steps) / 1e12
@@ -690,6 +736,8 @@ def main():
         "gather": (0, 4 * C + 4),
         "scatter": (0, 4 * C + 4),
     }
+    # gather model: each of the 9 neighbour rows read from memory, no reuse
+    gather_unit = 9 * 2 * C + 2 * C + 36
     breakdown = {}
     for k, d in kinds.items():
         f_unit, b_unit = per_unit[k]
@@ -701,6 +749,10 @@ def main():
             "tflops": round(f_unit * d["units"] / sec / 1e12, 2) if f_unit else None,
             "gbps_compulsory": round(b_unit * d["units"] / sec / 1e9, 1),
         }
+        if k in ("fwd", "dx", "dw"):
+            g = gather_unit * d["units"] / sec / 1e9
+            breakdown[k]["gbps_gather_model"] = round(g, 1)
+            breakdown[k]["frac_hbm_gather_model"] = round(g / (HBM_TBPS * 1e3), 4)
     # Dominant kernel: k_conv_mfma runs in every forward (after the weight
     # repack) and every input gradient; the input-gradient entry point
     # launches it alone, so its HIP events time exactly that kernel.
@@ -744,6 +796,8 @@ def main():
             "workload": "T=384 frames, 16x16 grid, 3 nested pruning stages (keep U[.5,.7]/U[.3,.5]/"
                         "U[.15,.3]), 2 layers per stage, C_in=C_out=256, fwd+bwd through 6 layers",
             "tokens_per_stage": run.ns,
+            "valid_tap_fraction": [round(float((Nt >= 0).sum().item()) / Nt.numel(), 4) for Nt in run.N],
+            "cache": "cold" if args.cold else "warm",
             "kernel": args.kernel,
             "dw_stream": args.dw_stream,
             "flops_per_step": fl,
@@ -768,6 +822,7 @@ def main():
             "unit": "TFLOP/s",
             "cores": threads,
             "kind": "oracle",
+            "cpu": host_cpu(),
             "sample": f"{passes} pass(es) over the first {args.cpu_frames} of 384 frames of the same "
                       f"workload: index build per stage, fwd through 6 layers, dW+db+dX back "
                       f"through them, float64 loops ({cdt:.1f} s)",

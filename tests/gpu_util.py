@@ -45,9 +45,21 @@ def normwise(gpu, ref) -> float:
     return err / scale
 
 
+def p999(gpu, ref) -> float:
+    """99.9th percentile of the elementwise error, relative to max |ref|
+    (reported beside the normwise error; the bound is on the normwise one)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    scale = float(np.max(np.abs(ref))) or 1.0
+    return float(np.percentile(np.abs(gpu - ref), 99.9)) / scale
+
+
 def assert_close(gpu, ref, dt: str, what: str):
     e = normwise(gpu, ref)
     assert np.all(np.isfinite(np.asarray(gpu, dtype=np.float64))), f"{what}: non-finite output"
+    print(f"  {what}: normwise {e:.2e}, elementwise p99.9 {p999(gpu, ref):.2e}")
     assert e <= TOL[dt], f"{what}: normwise error {e:.3e} > {TOL[dt]:.0e}"
     return e
 
