@@ -74,6 +74,28 @@ def test_bf16(case, kernel):
     check_against_oracle(L, N, kernel, what=f"bf16 {kernel} {case}")
 
 
+# Channel counts where the automatic choice splits the passes: the forward
+# contracts 32 or 64 channels and produces 16 or 48 (MFMA, a partial output
+# tile), the input gradient contracts 16 or 48 (VALU); dW on VALU.
+AUTO_SPLIT_CASES = [
+    (17, 2, 14, 14, 0.5, 32, 16, False),
+    (18, 3, 9, 13, [40, 0, 117], 64, 48, True),
+]
+
+
+@pytest.mark.parametrize("case", AUTO_SPLIT_CASES, ids=lambda c: f"seed{c[0]}")
+def test_bf16_auto_partial_tiles(case):
+    seed, T, H, W, keep, Ci, Co, sh = case
+    L = wl.make_random_case(seed, T, H, W, keep, Ci, Co, "bf16", shuffle=sh)
+    print(f"case {case} n={L.n}", flush=True)
+    st, N, _ = O.build_index(L.coords, L.frame_offsets, T, H, W)
+    check_against_oracle(L, N, "auto", what=f"bf16 auto {case}")
+    # forcing the matrix cores where the input gradient's contraction does not fit is refused
+    with pytest.raises(ops.SvError) as e:
+        run_all(L, N, "mfma")
+    assert e.value.status == ops.SV_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_arbitrary_table_gather_mode(kernel):
     """Any N with entries in [-1, n) is a valid table for the kernels; random
