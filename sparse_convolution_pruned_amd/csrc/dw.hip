@@ -306,8 +306,20 @@ __global__ __launch_bounds__(256) void k_reduce_slices4(const float4* __restrict
                                                         int Co) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < count4; e += stride) {
+        // loads issued 8 slices at a time (one wait per batch instead of one
+        // per slice), added in slice order
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < slices; ++s) {
+        int s = 0;
+        for (; s + 8 <= slices; s += 8) {
+            float4 p[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) p[u] = part[static_cast<int64_t>(s + u) * count4 + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                v.x += p[u].x; v.y += p[u].y; v.z += p[u].z; v.w += p[u].w;
+            }
+        }
+        for (; s < slices; ++s) {
             const float4 p = part[static_cast<int64_t>(s) * count4 + e];
             v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
         }
@@ -340,7 +352,15 @@ __global__ __launch_bounds__(256) void k_reduce_slices(const float* __restrict__
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < count; e += stride) {
         float v = 0.f;
-        for (int s = 0; s < slices; ++s) v += part[static_cast<int64_t>(s) * count + e];
+        int s = 0;
+        for (; s + 8 <= slices; s += 8) {
+            float p[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) p[u] = part[static_cast<int64_t>(s + u) * count + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v += p[u];
+        }
+        for (; s < slices; ++s) v += part[static_cast<int64_t>(s) * count + e];
         out[e] = accumulate ? out[e] + v : v;
     }
 }
