@@ -382,7 +382,7 @@ DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16, int taps) {
         // a fixed cost for the extra reduction launch.  Depends on the
         // arguments only, so workspace sizing and the call agree.
         const int64_t tiles = ceil_div(static_cast<int64_t>(taps) * (Ci / DW_BI), 3) * (Co / DW_BO);
-        const double flops = 2.0 * static_cast<double>(n) * (3 * tiles / (Co / DW_BO)) * DW_BI * Co;
+        const double flops = 2.0 * static_cast<double>(n) * static_cast<double>(3 * tiles / (Co / DW_BO)) * DW_BI * Co;
         const double dwb = static_cast<double>(taps) * Ci * Co * 4;
         double best = 1e30;
         slices = 1;
@@ -390,7 +390,7 @@ DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16, int taps) {
             if (s > 1 && ceil_div(n, s) < 4 * DW_TK) break;
             const double rounds = static_cast<double>(ceil_div(tiles * s, 256));
             const double t = rounds * flops / static_cast<double>(tiles * s) / 4e12 +
-                             (s > 1 ? (2.0 * s * dwb / 5e12 + 4e-6) : 0.0);
+                             (s > 1 ? (2.0 * static_cast<double>(s) * dwb / 5e12 + 4e-6) : 0.0);
             if (t < best) { best = t; slices = s; }
         }
     } else {

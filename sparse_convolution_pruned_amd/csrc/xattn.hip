@@ -33,6 +33,11 @@
 
 namespace svc {
 
+// 64-bit minimum (the unqualified device min() may resolve to its int
+// overload and truncate).
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+
 constexpr int XA_THREADS = 256;
 constexpr int XA_GROUPS = XA_THREADS / 16;
 constexpr int XA_MQ = 4;                 // queries per pass
@@ -120,8 +125,8 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_fwd_part(const T* __restri
     // Each group walks its keys two at a time with the next two rows already
     // requested (request indices are clamped into the block, so no load sits
     // behind a branch).
-    const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
-    auto row = [&](int64_t j) { return X + min(j, kend - 1) * D + lane * EPL; };
+    const int64_t kbeg = b * kpb, kend = min64(n, kbeg + kpb);
+    auto row = [&](int64_t j) { return X + min64(j, kend - 1) * D + lane * EPL; };
     auto fold = [&](const float* x) {
 #pragma unroll
         for (int qi = 0; qi < MQ; ++qi) {
@@ -303,8 +308,8 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_dsum(const T* __restri
         }
         ss[qi] = 0.f;
     }
-    const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
-    auto row = [&](int64_t j) { return X + min(j, kend - 1) * D + lane * EPL; };
+    const int64_t kbeg = b * kpb, kend = min64(n, kbeg + kpb);
+    auto row = [&](int64_t j) { return X + min64(j, kend - 1) * D + lane * EPL; };
     auto fold = [&](const float* x) {
 #pragma unroll
         for (int qi = 0; qi < MQ; ++qi) {
@@ -394,8 +399,8 @@ __global__ __launch_bounds__(XA_THREADS) void k_xattn_bwd_part(const T* __restri
         for (int e = 0; e < EPL; ++e) dq[qi][e] = 0.f;
     }
 
-    const int64_t kbeg = b * kpb, kend = min(n, kbeg + kpb);
-    auto row = [&](int64_t j) { return X + min(j, kend - 1) * D + lane * EPL; };
+    const int64_t kbeg = b * kpb, kend = min64(n, kbeg + kpb);
+    auto row = [&](int64_t j) { return X + min64(j, kend - 1) * D + lane * EPL; };
     auto key = [&](int64_t j, const float* x) {
         float dx[EPL];
         if (accumulate) load_part<T, EPL>(dX + j * D + lane * EPL, dx);
