@@ -99,7 +99,7 @@ typedef enum sv_op { SV_OP_FWD = 0, SV_OP_DX = 1, SV_OP_DW = 2 } sv_op;
  *
  * Debugging aid: with SV_SYNC_CHECK=1 in the environment (read at every
  * call), this call and the chunk drivers wait for their stream after
- * enqueuing and return the device flag's verdict instead (SV_ERR_COORD_RANGE,
+ * enqueuing and return the status the device flag implies (SV_ERR_COORD_RANGE,
  * SV_ERR_DUPLICATE_COORD, or SV_ERR_INVALID_ARG for SV_FLAG_BAD_OFFSETS).
  * The flag is never cleared by the library, so earlier bits count too.
  * Without the variable nothing ever synchronises. */

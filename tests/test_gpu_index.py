@@ -102,7 +102,7 @@ def test_index_grid_too_large_rejected():
 
 def test_sync_check_turns_the_flag_into_a_status(monkeypatch):
     """SV_SYNC_CHECK=1: the index build and the chunk driver wait for their
-    stream and return the device flag's verdict."""
+    stream and return the status the device flag implies."""
     c, o = dev(np.array([0, 5, 5], np.int32)), dev(np.array([0, 3], np.int32))
     N = torch.empty((3, 9), dtype=torch.int32, device="cuda")
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
