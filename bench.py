@@ -136,11 +136,12 @@ class StagedRun:
 
     def step(self, ev=None, overlap=True):
         """One pass of the whole hot path.  With `overlap` and the side stream
-        the step is scheduled over three streams (see __init__); without it
+        the step is scheduled over two streams (see __init__; the MFMA
+        kernels only: with --kernel valu the step runs in order); without it
         (the instrumented repeat) every call runs alone, in order, on the
         current stream, so that its HIP events bracket that call's kernels
         only."""
-        if overlap and self.side is not None:
+        if overlap and self.side is not None and self.kernel != "valu":
             return self._step_streams()
         ops, kern = self.ops, self.kernel
         rec = ev.record if ev is not None else (lambda *a, **k: None)
@@ -191,8 +192,6 @@ class StagedRun:
         import ctypes
 
         ops, torch, S = self.ops, self.torch, self.S
-        if self.kernel == "valu":
-            raise SystemExit("the three-stream step uses the MFMA forward; use --dw-stream same with --kernel valu")
         lib = ops.load()
         main, side = torch.cuda.current_stream(), self.side
         hs = {id(x): ctypes.c_void_p(x.cuda_stream) for x in (main, side)}
