@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 METRIC = "SparseConv2D fwd+bwd effective TFLOP/s & HBM GB/s vs roofline, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
 HBM_TBPS = 8.0               # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector
 PCIE_GBPS_PER_DIRECTION = 64.0   # PCIe 5.0 x16 host link, one direction
 PEAK_F32_TFLOPS = 157.3      # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
@@ -756,22 +757,26 @@ def main():
     # repack) and every input gradient; the input-gradient entry point
     # launches it alone, so its HIP events time exactly that kernel.
     conv_ms = kinds["fwd"]["ms"] + kinds["dx"]["ms"]
+    valu = args.kernel == "valu"
     if conv_ms >= kinds["dw"]["ms"]:
-        dom, kname, kfiles = "dx", "k_conv_mfma", ["sparse_convolution_pruned_amd/csrc/conv_mfma.hip"]
+        dom, kname, kfiles = "dx", ("k_conv_valu" if valu else "k_conv_mfma"), \
+            ["sparse_convolution_pruned_amd/csrc/" + ("conv_valu.hip" if valu else "conv_mfma.hip")]
     else:
         dom, kname, kfiles = "dw", "k_dw_mfma", ["sparse_convolution_pruned_amd/csrc/dw.hip"]
+    # the VALU conv kernels are bound by fp32 vector arithmetic
+    bound, peak = ("alu", PEAK_FP32_VALU_TFLOPS) if (valu and dom == "dx") else ("mfma", PEAK_BF16_TFLOPS)
     d = kinds[dom]
     # per launch: FLOPs of the tokens it processed / its duration, averaged
     # over launches weighted by duration (sum of FLOPs / sum of durations)
     achieved = per_unit[dom][0] * d["units"] / (d["ms"] / 1e3) / 1e12
     tr = traffic_record(kname, kfiles)
     roofline = {
-        "bound": "mfma",
+        "bound": bound,
         "kernel": kname,
         "achieved": round(achieved, 2),
-        "peak": PEAK_BF16_TFLOPS,
+        "peak": peak,
         "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "frac": round(achieved / peak, 4),
         "traffic": None if tr is None else tr["bytes_per_launch"],
         "avg_launch_us": round(d["ms"] * 1e3 / d["launches"], 2),
         "flops_per_launch": round(per_unit[dom][0] * d["units"] / d["launches"]),
