@@ -95,6 +95,19 @@ sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int
     return hip_status(launch_conv_valu(dt == SV_BF16, true, dY, N, Wt, nullptr, R, dX, n, Ci, Co, taps, s));
 }
 
+// Forward and input gradient of one chunk, both on the MFMA kernel, in one
+// paired launch (the forward from the repacked weights V, the input
+// gradient from Wt); the two problems' tiles fill the chip together.
+sv_status run_fwd_dx_pair(const void* X, const void* dY, const int32_t* N, const void* Wt, const void* V,
+                          const void* bias, void* Y, void* dX, int64_t n, int32_t Ci, int32_t Co, int taps,
+                          hipStream_t s) {
+    if (n == 0) return SV_OK;
+    return hip_status(launch_conv_mfma_pair(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(V),
+                                            static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(Y), Ci, Co,
+                                            static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(Wt),
+                                            static_cast<uint16_t*>(dX), Co, Ci, N, n, taps, s));
+}
+
 // Bytes of repacked weights the forward needs when the MFMA kernel may run.
 size_t fwd_ws_bytes(int32_t Ci, int32_t Co, sv_dtype dt, int64_t n, int taps) {
     return (dt == SV_BF16 && conv_mfma_supported(false, Ci, Co, n, taps)) ? conv_mfma_fwd_workspace(Ci, Co, taps)
@@ -362,7 +375,8 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     int32_t* Nc = static_cast<int32_t*>(workspace);
     void* Vw = static_cast<char*>(workspace) + L.n_bytes;
     void* dws = static_cast<char*>(workspace) + L.n_bytes + L.w_bytes;
-    bool fwd_mfma = false;
+    bool fwd_mfma = false, dx_mfma = false;
+    if (passes & SV_PASS_DX) choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.max_tokens, L.taps, &dx_mfma);
     if (passes & SV_PASS_FWD) {
         choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.max_tokens, L.taps, &fwd_mfma);
         if (fwd_mfma && d->T > 0) {
@@ -383,16 +397,21 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
         if (st != SV_OK) return st;
         const char* X = d->X ? static_cast<const char*>(d->X) + t0 * d->C_in * es : nullptr;
         const char* dY = d->dY ? static_cast<const char*>(d->dY) + t0 * d->C_out * es : nullptr;
-        if (passes & SV_PASS_FWD) {
-            st = run_fwd_prepared(fwd_mfma, X, Nc, d->Wt, Vw, d->bias,
-                                  static_cast<char*>(d->Y) + t0 * d->C_out * es, nc, d->C_in, d->C_out,
-                                  L.taps, d->dtype, stream);
+        char* Yc = (passes & SV_PASS_FWD) ? static_cast<char*>(d->Y) + t0 * d->C_out * es : nullptr;
+        char* dXc = (passes & SV_PASS_DX) ? static_cast<char*>(d->dX) + t0 * d->C_in * es : nullptr;
+        if (fwd_mfma && dx_mfma) {
+            st = run_fwd_dx_pair(X, dY, Nc, d->Wt, Vw, d->bias, Yc, dXc, nc, d->C_in, d->C_out, L.taps, stream);
             if (st != SV_OK) return st;
-        }
-        if (passes & SV_PASS_DX) {
-            st = run_dx(dY, Nc, d->Wt, static_cast<char*>(d->dX) + t0 * d->C_in * es, nc, d->C_in,
-                        d->C_out, L.taps, d->dtype, d->kernel, stream);
-            if (st != SV_OK) return st;
+        } else {
+            if (passes & SV_PASS_FWD) {
+                st = run_fwd_prepared(fwd_mfma, X, Nc, d->Wt, Vw, d->bias, Yc, nc, d->C_in, d->C_out, L.taps,
+                                      d->dtype, stream);
+                if (st != SV_OK) return st;
+            }
+            if (passes & SV_PASS_DX) {
+                st = run_dx(dY, Nc, d->Wt, dXc, nc, d->C_in, d->C_out, L.taps, d->dtype, d->kernel, stream);
+                if (st != SV_OK) return st;
+            }
         }
         if (passes & SV_PASS_DW) {
             const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16, L.taps);
@@ -534,7 +553,8 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
         st[b].dX = p;
     }
 
-    bool fwd_mfma = false;
+    bool fwd_mfma = false, dx_mfma = false;
+    if (passes & SV_PASS_DX) choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.dev.max_tokens, taps, &dx_mfma);
     if (passes & SV_PASS_FWD) {
         choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.dev.max_tokens, taps, &fwd_mfma);
         if (fwd_mfma && d->T > 0) {
@@ -616,15 +636,21 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
             sv_status s2 = hip_status(launch_build_index(coords_g, offs_g, f0, f1 - f0, d->H, d->W, L.dev.K, nc,
                                                          t0, Nc, nullptr, d->err_flag, compute));
             if (s2 != SV_OK) return s2;
-            if (passes & SV_PASS_FWD) {
-                s2 = run_fwd_prepared(fwd_mfma, st[b].X, Nc, d->Wt, Vw, d->bias, st[b].Y, nc, d->C_in, d->C_out,
-                                      taps, d->dtype, compute);
+            if (fwd_mfma && dx_mfma) {
+                s2 = run_fwd_dx_pair(st[b].X, st[b].dY, Nc, d->Wt, Vw, d->bias, st[b].Y, st[b].dX, nc, d->C_in,
+                                     d->C_out, taps, compute);
                 if (s2 != SV_OK) return s2;
-            }
-            if (passes & SV_PASS_DX) {
-                s2 = run_dx(st[b].dY, Nc, d->Wt, st[b].dX, nc, d->C_in, d->C_out, taps, d->dtype, d->kernel,
-                            compute);
-                if (s2 != SV_OK) return s2;
+            } else {
+                if (passes & SV_PASS_FWD) {
+                    s2 = run_fwd_prepared(fwd_mfma, st[b].X, Nc, d->Wt, Vw, d->bias, st[b].Y, nc, d->C_in,
+                                          d->C_out, taps, d->dtype, compute);
+                    if (s2 != SV_OK) return s2;
+                }
+                if (passes & SV_PASS_DX) {
+                    s2 = run_dx(st[b].dY, Nc, d->Wt, st[b].dX, nc, d->C_in, d->C_out, taps, d->dtype, d->kernel,
+                                compute);
+                    if (s2 != SV_OK) return s2;
+                }
             }
             if (passes & SV_PASS_DW) {
                 const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16, taps);

@@ -83,14 +83,26 @@ __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const
 
 // A [n][K], B [TAPS][NO][K], bias [NO] (nullable), res [n][NO] (nullable: a
 // residual added before the one rounding to bf16), out [n][NO]; K % 32 == 0,
-// NO % 16 == 0.
-template <int TAPS, bool RES>
-__global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uint16_t* __restrict__ A,
+// NO % 16 == 0.  With PAIR the grid also covers a second problem on the
+// same N (`second`: its own A, B, output and channel counts, no bias or
+// residual): logical tiles from second.tiles_first on belong to it.  The
+// chunk driver pairs a chunk's forward and input gradient this way, so that
+// the two small launches fill the chip together.
+struct ConvSecond {
+    const uint16_t* A;
+    const uint16_t* B;
+    uint16_t* out;
+    int K, NO, tiles_first;
+};
+
+template <int TAPS, bool RES, bool PAIR>
+__global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uint16_t* __restrict__ A0,
                                                       const int32_t* __restrict__ Nt,
-                                                      const uint16_t* __restrict__ B,
-                                                      const uint16_t* __restrict__ bias,
+                                                      const uint16_t* __restrict__ B0,
+                                                      const uint16_t* __restrict__ bias0,
                                                       const uint16_t* __restrict__ res,
-                                                      uint16_t* __restrict__ out, int n, int K, int NO) {
+                                                      uint16_t* __restrict__ out0, int n, int K0, int NO0,
+                                                      ConvSecond second) {
     // Window rows held in LDS: 192 (a tile's rows and the neighbours around
     // them).  With one tap the window is the tile's own 128 rows, and two
     // windows are held, double-buffered like the weight tiles: one barrier
@@ -115,8 +127,16 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     const int l32 = lane & 31, lhi = lane >> 5;
     // 1-D grid: logical tile = (token tile, output-channel tile), the
     // output-channel tiles of one token range adjacent and on one XCD.
+    int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const bool two = PAIR && logical >= second.tiles_first;
+    const uint16_t* __restrict__ A = two ? second.A : A0;
+    const uint16_t* __restrict__ B = two ? second.B : B0;
+    const uint16_t* __restrict__ bias = two ? nullptr : bias0;
+    uint16_t* __restrict__ out = two ? second.out : out0;
+    const int K = two ? second.K : K0;
+    const int NO = two ? second.NO : NO0;
+    if (two) logical -= second.tiles_first;
     const int tilesN = (NO + CM_BN - 1) / CM_BN;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t k0 = static_cast<int64_t>(logical / tilesN) * CM_BM;
     const int n0 = (logical % tilesN) * CM_BN;
     const int nchunks = (K + CM_KC - 1) / CM_KC;
@@ -428,29 +448,53 @@ hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, in
 
 template <int TAPS>
 static void launch_taps(dim3 grid, hipStream_t stream, const uint16_t* A, const int32_t* N, const uint16_t* B,
-                        const uint16_t* bias, const uint16_t* R, uint16_t* out, int n, int K, int NO) {
-    // the residual variant is its own instantiation: a runtime test of R
-    // changes the code the compiler emits for the main loop
-    if (R)
-        hipLaunchKernelGGL((k_conv_mfma<TAPS, true>), grid, dim3(256), 0, stream, A, N, B, bias, R, out, n, K, NO);
+                        const uint16_t* bias, const uint16_t* R, uint16_t* out, int n, int K, int NO,
+                        const ConvSecond* second) {
+    // the residual and paired variants are instantiations of their own: a
+    // runtime test changes the code the compiler emits for the main loop
+    const ConvSecond none{nullptr, nullptr, nullptr, 0, 0, 0};
+    if (second)
+        hipLaunchKernelGGL((k_conv_mfma<TAPS, false, true>), grid, dim3(256), 0, stream, A, N, B, bias, nullptr,
+                           out, n, K, NO, *second);
+    else if (R)
+        hipLaunchKernelGGL((k_conv_mfma<TAPS, true, false>), grid, dim3(256), 0, stream, A, N, B, bias, R, out, n,
+                           K, NO, none);
     else
-        hipLaunchKernelGGL((k_conv_mfma<TAPS, false>), grid, dim3(256), 0, stream, A, N, B, bias, R, out, n, K, NO);
+        hipLaunchKernelGGL((k_conv_mfma<TAPS, false, false>), grid, dim3(256), 0, stream, A, N, B, bias, R, out, n,
+                           K, NO, none);
+}
+
+static hipError_t launch_any(dim3 grid, int taps, hipStream_t stream, const uint16_t* A, const int32_t* N,
+                             const uint16_t* B, const uint16_t* bias, const uint16_t* R, uint16_t* out, int n,
+                             int K, int NO, const ConvSecond* second) {
+    switch (taps) {
+        case 1: launch_taps<1>(grid, stream, A, N, B, bias, R, out, n, K, NO, second); break;
+        case 9: launch_taps<9>(grid, stream, A, N, B, bias, R, out, n, K, NO, second); break;
+        case 25: launch_taps<25>(grid, stream, A, N, B, bias, R, out, n, K, NO, second); break;
+        case 49: launch_taps<49>(grid, stream, A, N, B, bias, R, out, n, K, NO, second); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+static int64_t conv_tiles(int64_t n, int NO) { return ((n + CM_BM - 1) / CM_BM) * ((NO + CM_BN - 1) / CM_BN); }
+
+hipError_t launch_conv_mfma_pair(const uint16_t* A1, const uint16_t* B1, const uint16_t* bias1, uint16_t* out1,
+                                 int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
+                                 int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t t1 = conv_tiles(n, NO1), t2 = conv_tiles(n, NO2);
+    const ConvSecond second{A2, B2, out2, K2, NO2, static_cast<int>(t1)};
+    return launch_any(dim3(static_cast<unsigned>(t1 + t2)), taps, stream, A1, N, B1, bias1, nullptr, out1,
+                      static_cast<int>(n), K1, NO1, &second);
 }
 
 hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const uint16_t* B,
                                    const uint16_t* bias, const uint16_t* R, uint16_t* out, int64_t n, int K,
                                    int NO, int taps, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    dim3 grid(static_cast<unsigned>(((n + CM_BM - 1) / CM_BM) * ((NO + CM_BN - 1) / CM_BN)));
-    const int nn = static_cast<int>(n);
-    switch (taps) {
-        case 1: launch_taps<1>(grid, stream, A, N, B, bias, R, out, nn, K, NO); break;
-        case 9: launch_taps<9>(grid, stream, A, N, B, bias, R, out, nn, K, NO); break;
-        case 25: launch_taps<25>(grid, stream, A, N, B, bias, R, out, nn, K, NO); break;
-        case 49: launch_taps<49>(grid, stream, A, N, B, bias, R, out, nn, K, NO); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return launch_any(dim3(static_cast<unsigned>(conv_tiles(n, NO))), taps, stream, A, N, B, bias, R, out,
+                      static_cast<int>(n), K, NO, nullptr);
 }
 
 }  // namespace svc

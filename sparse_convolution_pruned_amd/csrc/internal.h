@@ -126,6 +126,12 @@ hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
 hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const uint16_t* B,
                                    const uint16_t* bias, const uint16_t* R, uint16_t* out, int64_t n, int K,
                                    int NO, int taps, hipStream_t stream);
+// Two problems on the same N in one launch: (A1, B1, bias1) -> out1 and
+// (A2, B2) -> out2, each as launch_conv_mfma_packed (no residual).  The
+// chunk driver runs a chunk's forward and input gradient together this way.
+hipError_t launch_conv_mfma_pair(const uint16_t* A1, const uint16_t* B1, const uint16_t* bias1, uint16_t* out1,
+                                 int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
+                                 int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream);
 hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream);
 size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps);
 // bf16, a tap count the kernel is built for, contracted channels a multiple
