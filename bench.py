@@ -14,8 +14,9 @@ is K steps between two device synchronisations.
 
 Output: one JSON line (metric, value in effective TFLOP/s over kept tokens,
 ms_per_step, a per-kernel breakdown, the roofline of the dominant kernel
-measured with HIP events on its launch stream, and the CPU oracle timed on
-a bounded sample of the same workload).
+measured with HIP events on its launch stream, the CPU oracle timed on
+a bounded sample of the same workload, and, as context, the vendor dense
+GEMM timed on matrices of the same shapes as each stage's passes).
 """
 from __future__ import annotations
 
@@ -51,6 +52,8 @@ def parse():
                    help="single-layer workloads: K of a K x K neighbourhood (weights of the same "
                         "distribution, std 1/sqrt(K*K*C))")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense-gemm", action="store_true",
+                   help="c5: skip timing the vendor dense GEMMs of the same shapes (context only)")
     p.add_argument("--cold", action="store_true",
                    help="c5 and single-layer workloads: write a 1 GiB scratch buffer between steps (outside "
                         "the timed events) so that no input stays in the caches; warm (default) is primary")
@@ -332,6 +335,15 @@ class Events:
         self.items.append((kind, start, e, units))
         return None
 
+    def per_units(self, kind):
+        """Average duration in microseconds of one kind's calls, grouped by
+        the number of tokens they processed."""
+        g = {}
+        for k, s, e, units in self.items:
+            if k == kind:
+                g.setdefault(units, []).append(s.elapsed_time(e) * 1e3)
+        return {u: sum(v) / len(v) for u, v in g.items()}
+
     def summary(self):
         out = {}
         for kind, s, e, units in self.items:
@@ -340,6 +352,53 @@ class Events:
             d["launches"] += 1
             d["units"] += units
         return out
+
+
+def dense_gemm_context(torch, ns, C, ev, reps=20):
+    """The vendor library on dense bf16 GEMMs of the same shapes as the c5
+    passes, with no gather: [n, 9C] x [9C, C] for a forward or input
+    gradient and [9C, n] x [n, C] for a weight gradient, timed with HIP
+    events beside this library's own per-stage input-gradient and
+    weight-gradient calls (from the instrumented region).  Context for the
+    roofline fraction: what a tuned dense GEMM reaches at these sizes."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    K = 9 * C
+
+    def timeit(f):
+        for _ in range(3):
+            f()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            f()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / reps
+
+    conv_us, dw_us = [], []
+    for n in ns:
+        A = torch.randn(n, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        B = torch.randn(K, C, device="cuda", dtype=torch.bfloat16, generator=g)
+        D = torch.randn(n, C, device="cuda", dtype=torch.bfloat16, generator=g)
+        conv_us.append(timeit(lambda: A @ B))
+        At = A.t()
+        dw_us.append(timeit(lambda: At @ D))
+        del A, B, D, At
+    dx, dw = ev.per_units("dx"), ev.per_units("dw")
+    fl = [2.0 * n * K * C for n in ns]
+    r = lambda v: [round(x, 1) for x in v]
+    return {
+        "library": f"torch.matmul (hipBLASLt) bf16, dense operands, torch {torch.__version__}",
+        "tokens_per_stage": ns,
+        "dense_conv_shape_us": r(conv_us),
+        "dense_conv_shape_tflops": r([f / t / 1e6 for f, t in zip(fl, conv_us)]),
+        "ours_dx_us": r([dx[n] for n in ns]),
+        "ours_dx_tflops": r([f / dx[n] / 1e6 for f, n in zip(fl, ns)]),
+        "dense_dw_shape_us": r(dw_us),
+        "dense_dw_shape_tflops": r([f / t / 1e6 for f, t in zip(fl, dw_us)]),
+        "ours_dw_us": r([dw[n] for n in ns]),
+        "ours_dw_tflops": r([f / dw[n] / 1e6 for f, n in zip(fl, ns)]),
+    }
 
 
 def timed_cold(torch, step, steps):
@@ -812,6 +871,8 @@ def main():
         "kernels": breakdown,
         "roofline": roofline,
     }
+    if not args.no_dense_gemm and args.kernel != "valu":
+        out["dense_gemm_same_shape"] = dense_gemm_context(torch, run.ns, C, ev)
     if args.calibrate_copy_mib:
         nb = args.calibrate_copy_mib * 2 ** 20
         a = torch.empty(nb, dtype=torch.uint8, device="cuda")
