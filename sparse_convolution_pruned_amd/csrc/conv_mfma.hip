@@ -20,7 +20,10 @@
 // Workgroup: 256 threads = 4 waves (2 x 2); output tile 128 tokens x 128
 // channels; each wave 64 x 64 = 2 x 2 blocks of 32 x 32.  Two workgroups fit
 // on a compute unit at 3 x 3 (67 KiB of LDS each) and 5 x 5 (78 KiB); one at
-// 7 x 7 (96 KiB).  The 1-D grid is remapped so that
+// 7 x 7 (96 KiB).  Plain 3 x 3 calls whose 128-token tiles would need one
+// more dispatch round than 192-token tiles use the latter: each wave 96 x 64
+// = 3 x 2 blocks, a 256-row window, 80 KiB of LDS, still two per compute
+// unit.  The 1-D grid is remapped so that
 // each XCD runs a contiguous range of tiles (neighbouring token ranges and
 // the channel tiles of one range share rows in that XCD's L2).
 //
@@ -49,7 +52,8 @@
 
 namespace svc {
 
-constexpr int CM_BM = 128;              // tokens per tile
+constexpr int CM_BM = 128;              // tokens per tile (two 32-row blocks per wave)
+constexpr int CM_BM3 = 192;             // tokens per tile with three 32-row blocks per wave
 constexpr int CM_BN = 128;              // output channels per tile
 constexpr int CM_KC = 64;               // channels per round
 constexpr int CM_WIN = 192;             // window rows held in LDS (more than one tap)
@@ -57,18 +61,20 @@ constexpr int CM_LDA = CM_KC + 8;       // 144 B pitch: conflict-free 16-byte ro
 constexpr int CM_LDB = CM_KC;           // weight tile rows: 128 B, XOR-swizzled 16-byte chunks
 constexpr int CM_SB = CM_BN * CM_LDB;
 
-// One round: 4 k-steps of 16, all fragments read first, then 16 MFMAs.
+// One round: 4 k-steps of 16, all fragments read first, then 8 * MB MFMAs
+// (MB 32-row blocks of tokens per wave).
+template <int MB>
 __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const uint16_t* __restrict__ sb,
-                                          const int arow[2], floatx16_t acc[2][2]) {
+                                          const int arow[MB], floatx16_t acc[MB][2]) {
     constexpr int KS = CM_KC / 16;
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
     const int l32 = lane & 31, lhi = lane >> 5;
-    bf16x8_t a[KS][2], b[KS][2];
+    bf16x8_t a[KS][MB], b[KS][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int kof = ks * 16 + lhi * 8;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) a[ks][mb] = frag_row(&sA[arow[mb] * CM_LDA + kof]);
+        for (int mb = 0; mb < MB; ++mb) a[ks][mb] = frag_row(&sA[arow[mb] * CM_LDA + kof]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
             b[ks][nb] = frag_row(&sb[(wn * 64 + nb * 32 + l32) * CM_LDB + (((2 * ks + lhi) ^ ((l32 >> 1) & 7)) << 3)]);
@@ -76,7 +82,7 @@ __device__ __forceinline__ void mma_round(const uint16_t* __restrict__ sA, const
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[ks][mb], b[ks][nb], acc[mb][nb]);
 }
@@ -95,7 +101,11 @@ struct ConvSecond {
     int K, NO, tiles_first;
 };
 
-template <int TAPS, bool RES, bool PAIR>
+// MB = 2: 128-token tiles (every variant).  MB = 3: 192-token tiles, 3 x 3
+// neighbourhoods without residual or pair only (80 KiB of LDS, two per
+// compute unit); chosen when it needs fewer dispatch rounds (see
+// conv_tile_blocks).
+template <int TAPS, bool RES, bool PAIR, int MB>
 __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uint16_t* __restrict__ A0,
                                                       const int32_t* __restrict__ Nt,
                                                       const uint16_t* __restrict__ B0,
@@ -108,15 +118,18 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     // windows are held, double-buffered like the weight tiles: one barrier
     // per round instead of two, and the next window's store no longer waits
     // for every wave to leave the current one.
+    static_assert(MB == 2 || (MB == 3 && TAPS == 9 && !RES && !PAIR), "192-token tiles: 3 x 3 plain calls only");
+    constexpr int BM = 64 * MB;                    // tokens per tile
     constexpr bool DBW = TAPS == 1;
-    constexpr int WIN = DBW ? CM_BM : CM_WIN;
+    // the 192-token tile's neighbours span at most 192 + 2 (W + 1) rows
+    constexpr int WIN = DBW ? BM : (MB == 2 ? CM_WIN : 256);
     constexpr int ZROW = WIN;                      // an all-zero row: target of -1 entries
     constexpr int WBUF = (WIN + 1) * CM_LDA;       // one window buffer
     constexpr int WREGS = (WIN * (CM_KC / 8) + 255) / 256;
     __shared__ __align__(16) uint16_t sA[(DBW ? 2 : 1) * WBUF];
     __shared__ __align__(16) uint16_t sB[2][CM_SB];   // weight tiles, written by direct loads
-    __shared__ int sN[CM_BM * TAPS];
-    __shared__ short sRow[CM_BM * TAPS];
+    __shared__ int sN[BM * TAPS];
+    __shared__ short sRow[BM * TAPS];
     __shared__ int sLo, sHi;
 
     // The wave index is uniform; through the scalar unit it keeps every
@@ -137,7 +150,7 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     const int NO = two ? second.NO : NO0;
     if (two) logical -= second.tiles_first;
     const int tilesN = (NO + CM_BN - 1) / CM_BN;
-    const int64_t k0 = static_cast<int64_t>(logical / tilesN) * CM_BM;
+    const int64_t k0 = static_cast<int64_t>(logical / tilesN) * BM;
     const int n0 = (logical % tilesN) * CM_BN;
     const int nchunks = (K + CM_KC - 1) / CM_KC;
     const int R = nchunks * TAPS;
@@ -149,17 +162,17 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
 
     // ---- the tile's slice of N, its row range, and the LDS row of every entry
     {
-        // The tile's N rows are contiguous: 128 * TAPS consecutive ints, all
+        // The tile's N rows are contiguous: BM * TAPS consecutive ints, all
         // loads issued before any is used.
-        constexpr int NE = (CM_BM * TAPS + 255) / 256;
+        constexpr int NE = (BM * TAPS + 255) / 256;
         const int64_t base = k0 * TAPS;
         const int64_t lim = static_cast<int64_t>(n) * TAPS;
         int m[NE];
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
             const int e = tid + 256 * u;
-            const bool ok = e < CM_BM * TAPS && base + e < lim;
-            const int v = Nt[min(base + min(e, CM_BM * TAPS - 1), lim - 1)];   // clamped: branch-free
+            const bool ok = e < BM * TAPS && base + e < lim;
+            const int v = Nt[min(base + min(e, BM * TAPS - 1), lim - 1)];   // clamped: branch-free
             m[u] = ok ? v : -1;
         }
         int lo = 0x7fffffff, hi = -1;
@@ -167,7 +180,7 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
         for (int u = 0; u < NE; ++u) {
             const int e = tid + 256 * u;
             const int v = clamp_index(m[u], n);
-            if (e < CM_BM * TAPS) sN[e] = v;
+            if (e < BM * TAPS) sN[e] = v;
             if (v >= 0) { lo = min(lo, v); hi = max(hi, v); }
         }
         // Reduce within the wave first (same-address LDS atomics from every
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     const int wlo = sLo;
     const int span = (sHi >= 0) ? sHi - wlo + 1 : 0;
     const bool window = span <= WIN;
-    for (int e = tid; e < CM_BM * TAPS; e += 256) {
+    for (int e = tid; e < BM * TAPS; e += 256) {
         const int m = sN[e];
         sRow[e] = static_cast<short>(m < 0 ? ZROW : (window ? m - wlo : e / TAPS));
     }
@@ -247,12 +260,12 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t*)(sb + (wave * 4 + u) * 512), 16,
                                                      bChunk[u] * 8 < kc ? bOff[u] + roff : kOob, 0, 0, 0);
     };
-    // Gather mode: the 128 rows of tap j, chunk c, straight into sA.
+    // Gather mode: the BM rows of tap j, chunk c, straight into sA.
     auto stage_gather = [&](int rr) {
         const int c = rr / TAPS, j = rr - c * TAPS;
         const int c0 = c * CM_KC, kc = kc_of(c);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < BM / 32; ++u) {
             const int q = tid + 256 * u;
             const int r = q >> 3, ch = q & 7;
             const int m = sN[r * TAPS + j];
@@ -262,9 +275,9 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
         }
     };
 
-    floatx16_t acc[2][2];
+    floatx16_t acc[MB][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < MB; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
@@ -288,13 +301,13 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
         // Mid-chunk, the next chunk's window rows go out first.
         if (window && span > 0 && j == TAPS / 2 && c + 1 < nchunks) load_window(c + 1, wreg);
         if (r + 1 < R) issue_B(r + 1, (r + 1) & 1);
-        int arow[2];
+        int arow[MB];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) arow[mb] = sRow[(wm * 64 + mb * 32 + l32) * TAPS + j];
+        for (int mb = 0; mb < MB; ++mb) arow[mb] = sRow[(wm * 32 * MB + mb * 32 + l32) * TAPS + j];
         // Always the full 4 k-steps: a 32-channel tail chunk is zero-filled
         // past its end in both operands, and one code path keeps the
         // accumulators in fixed registers.
-        mma_round(sA + (DBW && window ? (c & 1) * WBUF : 0), sB[r & 1], arow, acc);
+        mma_round<MB>(sA + (DBW && window ? (c & 1) * WBUF : 0), sB[r & 1], arow, acc);
         if (r + 1 < R) {
             if (DBW) {
                 // the other window buffer was last read in round r - 1,
@@ -309,10 +322,12 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
     }
 
     // ---- epilogue.  Without a residual: bias, round to bf16, stage the
-    // 128 x 128 tile in LDS (rows 0-63 over the window, rows 64-127 over the
-    // weight buffers), then write whole 16-byte row pieces.
+    // BM x 128 tile in LDS (the first wave row's BM / 2 rows over the window,
+    // the second's over the weight buffers), then write whole 16-byte row
+    // pieces.
     constexpr int OLD = CM_BN + 8;      // 272-byte pitch: rows 4 apart in opposite bank halves
-    static_assert(64 * OLD <= (DBW ? 2 : 1) * WBUF && 64 * OLD <= 2 * CM_SB,
+    constexpr int HALF = BM / 2;
+    static_assert(HALF * OLD <= (DBW ? 2 : 1) * WBUF && HALF * OLD <= 2 * CM_SB,
                   "output tile halves must fit the window and the weight buffers");
     uint16_t* const sOutLo = sA;
     uint16_t* const sOutHi = &sB[0][0];
@@ -323,7 +338,7 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
             const int cl = wn * 64 + nb * 32 + l32;
             const float bv = (bias && n0 + cl < NO) ? bf16_to_f32(bias[n0 + cl]) : 0.f;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -333,14 +348,15 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
         }
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < (CM_BM * CM_BN / 8) / 256; ++u) {
+        for (int u = 0; u < (BM * CM_BN / 8) / 256; ++u) {
             const int q = tid + 256 * u;
             const int rl = q >> 4, ch = q & 15;
             const int64_t row = k0 + rl;
             const int col = n0 + ch * 8;
+            const bool hi = rl >= HALF;
             if (row < n && col < NO)
                 *reinterpret_cast<uint4*>(out + row * NO + col) =
-                    *reinterpret_cast<const uint4*>(&(rl < 64 ? sOutLo : sOutHi)[(rl & 63) * OLD + ch * 8]);
+                    *reinterpret_cast<const uint4*>(&(hi ? sOutHi : sOutLo)[(rl - (hi ? HALF : 0)) * OLD + ch * 8]);
         }
         return;
     }
@@ -454,14 +470,14 @@ static void launch_taps(dim3 grid, hipStream_t stream, const uint16_t* A, const 
     // runtime test changes the code the compiler emits for the main loop
     const ConvSecond none{nullptr, nullptr, nullptr, 0, 0, 0};
     if (second)
-        hipLaunchKernelGGL((k_conv_mfma<TAPS, false, true>), grid, dim3(256), 0, stream, A, N, B, bias, nullptr,
+        hipLaunchKernelGGL((k_conv_mfma<TAPS, false, true, 2>), grid, dim3(256), 0, stream, A, N, B, bias, nullptr,
                            out, n, K, NO, *second);
     else if (R)
-        hipLaunchKernelGGL((k_conv_mfma<TAPS, true, false>), grid, dim3(256), 0, stream, A, N, B, bias, R, out, n,
-                           K, NO, none);
+        hipLaunchKernelGGL((k_conv_mfma<TAPS, true, false, 2>), grid, dim3(256), 0, stream, A, N, B, bias, R, out,
+                           n, K, NO, none);
     else
-        hipLaunchKernelGGL((k_conv_mfma<TAPS, false, false>), grid, dim3(256), 0, stream, A, N, B, bias, R, out, n,
-                           K, NO, none);
+        hipLaunchKernelGGL((k_conv_mfma<TAPS, false, false, 2>), grid, dim3(256), 0, stream, A, N, B, bias, R, out,
+                           n, K, NO, none);
 }
 
 static hipError_t launch_any(dim3 grid, int taps, hipStream_t stream, const uint16_t* A, const int32_t* N,
@@ -477,7 +493,25 @@ static hipError_t launch_any(dim3 grid, int taps, hipStream_t stream, const uint
     return hipGetLastError();
 }
 
-static int64_t conv_tiles(int64_t n, int NO) { return ((n + CM_BM - 1) / CM_BM) * ((NO + CM_BN - 1) / CM_BN); }
+static int64_t conv_tiles(int64_t n, int NO, int bm = CM_BM) {
+    return ((n + bm - 1) / bm) * ((NO + CM_BN - 1) / CM_BN);
+}
+
+// Row blocks per wave for a plain 3 x 3 call: 3 (192-token tiles) when that
+// takes fewer dispatch rounds of the 512 workgroup slots of a 256-CU part
+// (two per compute unit) than 128-token tiles, else 2.  A 192-token tile
+// costs about 1.25 times a 128-token one (0.83 instead of 1 KB of LDS reads
+// per MFMA), so it only pays when it saves a round: at 39,389 tokens and 256
+// output channels, 616 tiles (2 rounds) become 412 (1 round).  Depends on
+// the arguments only.  Every output element sums the same products in the
+// same order either way, so the choice does not change the result.
+static int conv_tile_blocks(int64_t n, int NO, int taps) {
+    if (taps != 9) return 2;
+    constexpr int64_t kSlots = 512;
+    const int64_t r2 = (conv_tiles(n, NO, CM_BM) + kSlots - 1) / kSlots;
+    const int64_t r3 = (conv_tiles(n, NO, CM_BM3) + kSlots - 1) / kSlots;
+    return r3 < r2 ? 3 : 2;
+}
 
 hipError_t launch_conv_mfma_pair(const uint16_t* A1, const uint16_t* B1, const uint16_t* bias1, uint16_t* out1,
                                  int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
@@ -493,6 +527,12 @@ hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const ui
                                    const uint16_t* bias, const uint16_t* R, uint16_t* out, int64_t n, int K,
                                    int NO, int taps, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
+    if (!R && conv_tile_blocks(n, NO, taps) == 3) {
+        const ConvSecond none{nullptr, nullptr, nullptr, 0, 0, 0};
+        hipLaunchKernelGGL((k_conv_mfma<9, false, false, 3>), dim3(static_cast<unsigned>(conv_tiles(n, NO, CM_BM3))),
+                           dim3(256), 0, stream, A, N, B, bias, nullptr, out, static_cast<int>(n), K, NO, none);
+        return hipGetLastError();
+    }
     return launch_any(dim3(static_cast<unsigned>(conv_tiles(n, NO))), taps, stream, A, N, B, bias, R, out,
                       static_cast<int>(n), K, NO, nullptr);
 }

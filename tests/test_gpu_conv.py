@@ -96,6 +96,28 @@ def test_bf16_auto_partial_tiles(case):
     assert e.value.status == ops.SV_ERR_UNSUPPORTED
 
 
+# Token counts for which plain 3 x 3 calls of the MFMA kernel take 192-token
+# tiles: with 32 output channels (one channel tile) 128-token tiles need two
+# dispatch rounds of the 512 slots (more than 65,536 tokens) where 192-token
+# tiles need one (at most 98,304 tokens).  189 of 256 cells kept per frame
+# leave a ragged last tile (75,600 tokens); the shuffled packing spreads a
+# tile's neighbours too far for the window, so it stages rows tap by tap.
+TILE192_CASES = [
+    (21, 400, 16, 16, 189, 32, 32, False),
+    (22, 300, 16, 16, 230, 32, 32, True),
+]
+
+
+@pytest.mark.parametrize("case", TILE192_CASES, ids=lambda c: f"seed{c[0]}")
+def test_bf16_192_token_tiles(case):
+    seed, T, H, W, keep, Ci, Co, sh = case
+    L = wl.make_random_case(seed, T, H, W, [keep] * T, Ci, Co, "bf16", shuffle=sh)
+    assert 65536 < L.n <= 98304
+    print(f"case {case} n={L.n}", flush=True)
+    st, N, _ = O.build_index(L.coords, L.frame_offsets, T, H, W)
+    check_against_oracle(L, N, "mfma", what=f"bf16 192-token tiles {case}")
+
+
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_arbitrary_table_gather_mode(kernel):
     """Any N with entries in [-1, n) is a valid table for the kernels; random
