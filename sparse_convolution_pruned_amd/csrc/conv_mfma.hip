@@ -32,11 +32,12 @@
 // (K/2)(W+1) packed positions of k and a tile's gathered rows sit in one
 // short range [lo, hi].
 // The kernel reads the tile's N slice, finds lo/hi, and when the range holds
-// at most 192 rows it stages exactly those rows (64 channels at a time, 16-byte
-// coalesced loads) in LDS once for all taps; A fragments are then read
-// from LDS by row index (N - lo; -1 maps to an all-zero row).  Tiles whose rows
-// are spread wider (another packing order, grids wider than 31 at 3 x 3)
-// fall back to staging the 128 gathered rows tap by tap.  Both modes feed the same MFMA
+// at most 192 rows (256 for a 192-token tile) it stages exactly those rows
+// (64 channels at a time, 16-byte coalesced loads) in LDS once for all taps;
+// A fragments are then read from LDS by row index (N - lo; -1 maps to an
+// all-zero row).  Tiles whose rows are spread wider (another packing order,
+// grids wider than 31 at 3 x 3) fall back to staging the tile's gathered rows
+// tap by tap.  Both modes feed the same MFMA
 // sequence, so the result does not depend on the mode.
 //
 // Pipeline.  The K loop runs over rounds (64-channel chunk, tap).  At the
@@ -44,7 +45,7 @@
 // the free LDS buffer and the loads of round r + 2 are issued, all ahead of
 // round r's MFMAs; the next chunk's window rows load into registers half-way
 // through the current chunk.  One barrier per round; each round's 4 k-steps
-// are unrolled with all fragment reads issued before the 16 MFMAs.  The
+// are unrolled with all fragment reads issued before the 16 (or 24) MFMAs.  The
 // output tile leaves through LDS so that global stores are whole 16-byte row
 // pieces.
 #include "internal.h"
@@ -113,15 +114,14 @@ __global__ __launch_bounds__(256, TAPS <= 25 ? 2 : 1) void k_conv_mfma(const uin
                                                       const uint16_t* __restrict__ res,
                                                       uint16_t* __restrict__ out0, int n, int K0, int NO0,
                                                       ConvSecond second) {
-    // Window rows held in LDS: 192 (a tile's rows and the neighbours around
-    // them).  With one tap the window is the tile's own 128 rows, and two
+    // Window rows held in LDS: 192 for a 128-token tile, 256 for a 192-token
+    // one (a tile's rows and the neighbours around them).  With one tap the window is the tile's own 128 rows, and two
     // windows are held, double-buffered like the weight tiles: one barrier
     // per round instead of two, and the next window's store no longer waits
     // for every wave to leave the current one.
     static_assert(MB == 2 || (MB == 3 && TAPS == 9 && !RES && !PAIR), "192-token tiles: 3 x 3 plain calls only");
     constexpr int BM = 64 * MB;                    // tokens per tile
     constexpr bool DBW = TAPS == 1;
-    // the 192-token tile's neighbours span at most 192 + 2 (W + 1) rows
     constexpr int WIN = DBW ? BM : (MB == 2 ? CM_WIN : 256);
     constexpr int ZROW = WIN;                      // an all-zero row: target of -1 entries
     constexpr int WBUF = (WIN + 1) * CM_LDA;       // one window buffer
