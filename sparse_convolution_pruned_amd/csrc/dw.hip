@@ -33,14 +33,17 @@ hipError_t launch_dw_valu(bool bf16, const void* X, const int32_t* N, const void
 // nothing.
 //
 // The contraction runs over tokens while both operands are stored with
-// channels contiguous.  Each step of 64 tokens is staged transposed: the
-// workgroup's 512 8 x 8 blocks (3 units x 8 token groups x 16 channel groups
-// of gathered X rows, 8 x 16 of dY rows; one per thread) are loaded as
-// 16-byte rows (the X rows through N[k][unit's tap]), transposed in registers
-// and written to LDS channel-major, [tile][channel][token], where every MFMA
-// fragment is one 16-byte read.  At the start of step s the tiles of step
-// s + 1 go into the free LDS buffer and the row loads of step s + 2 are
-// issued, ahead of step s's MFMAs; each step ends with a single barrier.
+// channels contiguous.  Each step of 64 tokens is staged as it is stored:
+// the gathered X rows of the three units (through N[k][unit's tap]) and the
+// dY rows, 128 channels each, go straight from memory into LDS through
+// buffer_load ... lds (gfx950: 16 bytes per lane, 1 KB per wave instruction,
+// no registers and no LDS store instructions).  The MFMA fragments, which
+// need 8 tokens per lane along k, come from those rows through the
+// transposing LDS read ds_read_b64_tr_b16.  The step of s + 1 is requested
+// into the free buffer at the start of step s, ahead of step s's MFMAs;
+// each step ends with a single barrier, which also waits for it.  Staging
+// 8 x 8 blocks through registers with v_perm transposes and LDS stores took
+// 8-13% longer per call.
 //
 // The N entries a step needs (64 tokens x 3 units) are fetched once per
 // workgroup by one wave, lane = token, two steps ahead, and passed through a
@@ -52,11 +55,26 @@ hipError_t launch_dw_valu(bool bf16, const void* X, const int32_t* N, const void
 // as zeros without a memory request or a branch.  The host sends inputs
 // larger than the buffer range (2 GiB) to the VALU kernel.
 constexpr int DW_BI = 128, DW_BO = 128, DW_TK = 64, DW_THREADS = 512;
-constexpr int DW_LD = DW_TK + 8;                 // 144-byte rows
-constexpr int DW_TILE = 128 * DW_LD;             // one [128 channels][64 tokens] tile
-constexpr int DW_BUF = 4 * DW_TILE;              // 3 X tiles + 1 dY tile
-constexpr int DW_NTAB = 2 * 3 * DW_TK;           // N table: [2 buffers][3 units][64 tokens]
-constexpr size_t DW_LDS = 2 * DW_BUF * sizeof(uint16_t) + DW_NTAB * sizeof(int);
+// A staged tile: the step's 64 rows of 128 channels (256 bytes), row-major.
+// A direct load writes 4 rows (1 KB) per wave instruction; token T = 16 q + b
+// (b = 0..15, q = 0..3) is row q of block b, blocks 1088 bytes apart, so
+// that the four consecutive tokens of a transposing read start in four
+// different 64-byte bank quarters.
+constexpr int DW_BLK = 1088;                      // bytes per block of 4 rows
+constexpr int DW_TILEB = 16 * DW_BLK;             // bytes per tile
+constexpr int DW_BUFB = 4 * DW_TILEB;             // 3 X tiles + 1 dY tile
+constexpr int DW_NTAB = 2 * 3 * DW_TK;            // N table: [2 buffers][3 units][64 tokens]
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+__device__ __forceinline__ v4s_t tr_read(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(p));
+}
+__device__ __forceinline__ bf16x8_t cat8(v4s_t lo, v4s_t hi) {
+    const short8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ int tok_addr(int T) { return (T & 15) * DW_BLK + (T >> 4) * 256; }
 
 __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restrict__ X,
                                                         const int32_t* __restrict__ Nt,
@@ -64,8 +82,12 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
                                                         float* __restrict__ out, float* __restrict__ dbout,
                                                         int n, int Ci, int Co, int taps, int slice_tokens,
                                                         int direct, int accumulate) {
-    extern __shared__ __align__(16) uint16_t dwsm[];   // 2 buffers of DW_BUF, then the N table
-    int* const ntab = reinterpret_cast<int*>(dwsm + 2 * DW_BUF);
+    // Two buffers as two arrays: the compiler then sees that a step's direct
+    // loads (into one) never alias its fragment reads (from the other) and
+    // waits for them only at the barrier.
+    __shared__ __align__(16) char sbuf0[DW_BUFB];
+    __shared__ __align__(16) char sbuf1[DW_BUFB];
+    __shared__ int ntab[DW_NTAB];
 
     // 1-D grid of tiles x slices: logical id = slice * tiles + tile, so the
     // tiles of one token slice (which gather the same X and dY rows) sit
@@ -79,59 +101,35 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     const int grp = bid % groups;
     const int o0 = (bid / groups) * DW_BO;
     const int kbeg = slice * slice_tokens;
-    const int cnt = max(0, min(n - kbeg, slice_tokens));     // tokens of this slice
+    const int cnt = max(0, min(n - kbeg, slice_tokens));
     const int steps = (cnt + DW_TK - 1) / DW_TK;
-    // one group per output tile also sums db (group 1 at 3 x 3: kernel row 1
-    // of the first input tile)
     const bool do_db = dbout != nullptr && grp == min(1, groups - 1);
 
-    // The wave index is uniform across a wave; reading it through the scalar
-    // unit lets every per-wave condition below compile to a scalar branch.
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, lhi = lane >> 5;
     const int wi = wave & 3, wo = wave >> 2;
-
-    // This thread's 8 x 8 block: tile = wave >> 1 (units 0..2 of the group,
-    // then dY), token group tid & 7, channel group (tid >> 3) & 15.  The block
-    // lands at LDS rows cg*8 + e, column tg*8: bank group (tg + e) mod 8 with
-    // the 144-byte pitch, so the 8 lanes that share a write cycle (8 token
-    // groups) never collide.
-    const int tile = wave >> 1, tg = tid & 7, cg = (tid >> 3) & 15;
+    // staging role: tile (wave >> 1: units 0..2, then dY), blocks 8 (wave & 1) .. +7
+    const int tile = wave >> 1;
     const bool is_x = tile < 3;
-    // this wave's unit (X tiles only): its tap and input-channel tile
     const int unit = 3 * grp + (is_x ? tile : 0);
     const bool xlive = is_x && unit < units;
-    const int utap = unit % taps, ui0 = (unit / taps) * DW_BI;
-    const uint32_t nrow = static_cast<uint32_t>(taps) * 4;   // bytes per N row
+    const int ui0 = (unit / taps) * DW_BI;
+    const uint32_t nrow = static_cast<uint32_t>(taps) * 4;
     const rsrc_t rX = make_rsrc(X, static_cast<uint32_t>(n) * Ci * 2);
     const rsrc_t rN = make_rsrc(Nt + static_cast<int64_t>(kbeg) * taps, static_cast<uint32_t>(cnt) * nrow);
     const rsrc_t rY = make_rsrc(dY + static_cast<int64_t>(kbeg) * Co, static_cast<uint32_t>(cnt) * Co * 2);
-    const uint32_t nOff = static_cast<uint32_t>(tg * 8) * nrow + utap * 4;
-    const uint32_t yOff = static_cast<uint32_t>(tg * 8) * Co * 2 + (o0 + cg * 8) * 2;
-    const uint32_t xCol = (ui0 + cg * 8) * 2, rowX = Ci * 2, rowY = Co * 2;
-    uint4 rr[8];
-    int ni[8];
-    // N entries are used as they are loaded and tested only when the rows
-    // they point to are requested: a test right after a load would make the
-    // wave wait for it (and for the row loads queued before it) on the spot.
-    //   load_n: this thread's 8 entries straight from N (first two steps);
-    //   fetch_n / put_n: the loader wave's 3 entries (lane = token) into the
-    //     table buffer of the step's parity;
-    //   get_n: this thread's 8 entries from the table.
+    // lane of a direct load: row q = lane >> 4 of the block, 16-byte chunk lane & 15
+    const int dq = lane >> 4, dch = lane & 15;
+    const uint32_t xCol = (ui0 + dch * 8) * 2, rowX = Ci * 2, rowY = Co * 2;
+    const uint32_t yCol = (o0 + dch * 8) * 2;
+    const int blk0 = (wave & 1) * 8;
+
+    // N entries: the loader wave (lane = token) fetches the three units'
+    // columns two steps ahead into a double-buffered table.
     const bool loader = wave == 6;
-    int nreg[3];
-    // the loader's column of N for each unit of the group (-1: empty unit)
-    int ltap[3];
+    int nreg[3], ltap[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) ltap[t] = 3 * grp + t < units ? (3 * grp + t) % taps : -1;
-    auto load_n = [&](int s) {
-        if (is_x) {
-            const uint32_t base = nOff + static_cast<uint32_t>(s * DW_TK) * nrow;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) ni[t] = load4(rN, base + t * nrow);
-        }
-    };
     auto fetch_n = [&](int s) {
         const uint32_t base = static_cast<uint32_t>(s * DW_TK + lane) * nrow;
 #pragma unroll
@@ -141,111 +139,118 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
 #pragma unroll
         for (int t = 0; t < 3; ++t) ntab[((s & 1) * 3 + t) * DW_TK + lane] = nreg[t];
     };
-    auto get_n = [&](int s) {
-        const int* p = &ntab[((s & 1) * 3 + tile) * DW_TK + tg * 8];
-        const int4 a = *reinterpret_cast<const int4*>(p), b = *reinterpret_cast<const int4*>(p + 4);
-        ni[0] = a.x; ni[1] = a.y; ni[2] = a.z; ni[3] = a.w;
-        ni[4] = b.x; ni[5] = b.y; ni[6] = b.z; ni[7] = b.w;
-    };
-    auto load_rows = [&](int s) {
-        if (is_x) {
-            const int lim = cnt - s * DW_TK - tg * 8;     // tokens t < lim lie in the slice
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    // Stage step s into `buf`: 8 direct loads per wave, block blk0 + j
+    // holding tokens 16 q + blk0 + j.  Rows of pruned neighbours, of empty
+    // units and of tokens past the slice read as zeros.
+    auto stage = [&](int s, char* buf) {
+        char* tb = buf + tile * DW_TILEB;
+        const int lim = cnt - s * DW_TK;
+        // this lane's 8 table entries (tokens 16 dq + blk0 .. +7), two 16-byte reads
+        const int* nt = &ntab[((s & 1) * 3 + (is_x ? tile : 0)) * DW_TK + 16 * dq + blk0];
+        const int4 e0 = *reinterpret_cast<const int4*>(nt), e1 = *reinterpret_cast<const int4*>(nt + 4);
+        const int m8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+        const rsrc_t rs = is_x ? rX : rY;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const bool ok = xlive && static_cast<unsigned>(ni[t]) < static_cast<unsigned>(n) && t < lim;
-                rr[t] = load16(rX, ok ? __umul24(static_cast<unsigned>(ni[t]), rowX) + xCol : kOob);
-            }
-        } else {
-            const uint32_t base = yOff + static_cast<uint32_t>(s * DW_TK) * rowY;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) rr[t] = load16(rY, base + t * rowY);   // past the slice: zeros
+        for (int j = 0; j < 8; ++j) {
+            const int T = 16 * dq + blk0 + j;
+            const int m = m8[j];
+            const uint32_t xo = (xlive && T < lim && static_cast<unsigned>(m) < static_cast<unsigned>(n))
+                                    ? __umul24(static_cast<unsigned>(m), rowX) + xCol : kOob;
+            const uint32_t yo = T < lim ? static_cast<uint32_t>(s * DW_TK + T) * rowY + yCol : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tb + (blk0 + j) * DW_BLK), 16,
+                                                     is_x ? xo : yo, 0, 0, 0);
         }
     };
-    auto store_rows = [&](int buf) {
-        uint16_t* sb = dwsm + buf * DW_BUF + tile * DW_TILE;
-        uint4 c[8];
-        transpose8x8_b16(rr, c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(&sb[(cg * 8 + e) * DW_LD + tg * 8]) = c[e];
-    };
+
+    // Fragment reads through ds_read_b64_tr_b16.  Source lane: G = lane >> 4,
+    // a = lane & 3, v = (lane >> 2) & 3, k half kh = G >> 1; it names the
+    // 8-byte piece of token 32 kh + 8 ks + 4 h + v at channel 16 (G & 1) + 4 a
+    // of the wave's 32 (A) or 32-of-64 (B) channels.  The read returns to
+    // lane l channel l mod 32 of four consecutive tokens, so two reads (h =
+    // 0, 1) give the 8 tokens of the lane's k slots; A and B use the same
+    // token order, so every product meets its partner.
+    const int G = lane >> 4, fa = lane & 3, fv = (lane >> 2) & 3, kh = G >> 1;
+    const int colA = (wi * 32 + 16 * (G & 1) + 4 * fa) * 2;
+    const int colB = (wo * 64 + 16 * (G & 1) + 4 * fa) * 2;
 
     floatx16_t acc[3][2];
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[t][b] = zero16();
-    // db: thread = (output channel o0 + (tid & 127), 16-token quarter tid >> 7)
-    // of each step's dY tile, summed with bf16 dot products against ones.
-    float dbacc = 0.f;
-    typedef __attribute__((__vector_size__(2 * sizeof(short)))) short short2_t;
-    const short2_t ones = __builtin_bit_cast(short2_t, 0x3f803f80u);
+    // db: thread = (16-byte chunk tid & 15 of the 128 output channels,
+    // tokens tid >> 4 and 32 + (tid >> 4))
+    float dbacc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dbacc[e] = 0.f;
 
-    if (steps > 0) {
-        load_n(0);
-        load_rows(0);
-        store_rows(0);
-        if (steps > 1) { load_n(1); load_rows(1); }
-        if (loader && steps > 2) {
-            fetch_n(2);
-            put_n(2);
-            if (steps > 3) fetch_n(3);
-        }
-    }
-    __syncthreads();
-
-    // One step.  With `all` every look-ahead exists (s + 4 < steps): the
-    // main loop runs that form without any branch around loads and stores,
-    // so the compiler's wait counts stay exact; the last steps take the
-    // guarded form.
-    auto step = [&](int s, bool all) {
-        const bool n1 = all || s + 1 < steps, n2 = all || s + 2 < steps;
-        const bool n3 = all || s + 3 < steps, n4 = all || s + 4 < steps;
-        // Step s + 2's N entries from the table (written in step s - 1), the
-        // next step's tiles into the free buffer (last read in step s - 1),
-        // the loader wave's table entries for step s + 3 (into the buffer
-        // step s + 1 read in step s - 1) and the row loads of step s + 2:
-        // all ahead of this step's MFMAs.  The loader's entries go out
-        // before the row loads, so that neither waits behind the other.
-        if (is_x && n2) get_n(s + 2);
-        if (n1) store_rows((s + 1) & 1);
-        if (loader && n3) {
-            put_n(s + 3);
-            if (n4) fetch_n(s + 4);
-        }
-        if (n2) load_rows(s + 2);
-        const uint16_t* __restrict__ sb = dwsm + (s & 1) * DW_BUF;
-        const uint16_t* __restrict__ sd = sb + 3 * DW_TILE;
+    auto mma_step = [&](const char* xb) {
+        const char* yb = xb + 3 * DW_TILEB;
 #pragma unroll
         for (int ks = 0; ks < DW_TK / 16; ++ks) {
-            const int kof = ks * 16 + lhi * 8;
+            const int t0 = 32 * kh + 8 * ks + fv;
+            const int r0 = tok_addr(t0), r1 = tok_addr(t0 + 4);
             bf16x8_t a[3], b[2];
 #pragma unroll
-            for (int t = 0; t < 3; ++t) a[t] = frag_row(&sb[t * DW_TILE + (wi * 32 + l32) * DW_LD + kof]);
+            for (int t = 0; t < 3; ++t)
+                a[t] = cat8(tr_read(xb + t * DW_TILEB + r0 + colA), tr_read(xb + t * DW_TILEB + r1 + colA));
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) b[nb] = frag_row(&sd[(wo * 64 + nb * 32 + l32) * DW_LD + kof]);
+            for (int nb = 0; nb < 2; ++nb)
+                b[nb] = cat8(tr_read(yb + r0 + colB + nb * 64), tr_read(yb + r1 + colB + nb * 64));
 #pragma unroll
             for (int t = 0; t < 3; ++t)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) acc[t][nb] = mfma32(a[t], b[nb], acc[t][nb]);
         }
         if (do_db) {
-            const uint16_t* p = &sd[(tid & 127) * DW_LD + (tid >> 7) * 16];
-            const uint4 v0 = *reinterpret_cast<const uint4*>(p);
-            const uint4 v1 = *reinterpret_cast<const uint4*>(p + 8);
-            const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            const int c = tid & 15, q = tid >> 4;
 #pragma unroll
-            for (int h = 0; h < 8; ++h)
-                dbacc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short2_t, w[h]), ones, dbacc, false);
+            for (int u = 0; u < 2; ++u) {
+                const uint4 v = *reinterpret_cast<const uint4*>(yb + tok_addr(q + 32 * u) + c * 16);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    dbacc[2 * h] += bf16_to_f32(static_cast<uint16_t>(w[h] & 0xffffu));
+                    dbacc[2 * h + 1] += bf16_to_f32(static_cast<uint16_t>(w[h] >> 16));
+                }
+            }
         }
-        if (n1) __syncthreads();
+    };
+
+    // prologue: table entries of steps 0 and 1, step 0 staged
+    if (loader) {
+        if (steps > 0) { fetch_n(0); put_n(0); }
+        if (steps > 1) { fetch_n(1); put_n(1); }
+        if (steps > 2) fetch_n(2);
+    }
+    __syncthreads();
+    if (steps > 0) stage(0, sbuf0);
+    __syncthreads();                       // also waits for the direct loads
+
+    // Step s: step s + 1 is staged into the other buffer (last read in step
+    // s - 1; its table entries were written in step s - 1), the loader puts
+    // step s + 2's entries into the table slot of step s's (read in step
+    // s - 1) and fetches step s + 3's; one barrier per step waits for all of
+    // it, the direct loads included.
+    auto step = [&](int s, const char* cur, char* nxt) {
+        if (s + 1 < steps) stage(s + 1, nxt);
+        if (loader && s + 2 < steps) {
+            put_n(s + 2);
+            if (s + 3 < steps) fetch_n(s + 3);
+        }
+        mma_step(cur);
+        __syncthreads();
     };
     int s = 0;
-    for (; s + 4 < steps; ++s) step(s, true);
-    for (; s < steps; ++s) step(s, false);
+    for (; s + 1 < steps; s += 2) {
+        step(s, sbuf0, sbuf1);
+        step(s + 1, sbuf1, sbuf0);
+    }
+    if (s < steps) step(s, sbuf0, sbuf1);
 
-    // D block (32 input channels x 32 output channels): lane holds output
-    // channel l32 and input channels 8g + 4*lhi + q.
     float* dst = out + (direct ? 0 : static_cast<int64_t>(slice) * taps * Ci * Co);
+    const int l32 = lane & 31, lhi = lane >> 5;
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
         const int u = 3 * grp + t;
@@ -266,13 +271,16 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
                 }
     }
     if (do_db) {
-        // the four quarters of each channel, added in a fixed order
-        float* red = reinterpret_cast<float*>(dwsm);
+        // 32 threads share each 8-channel chunk; added in thread order
+        float* red = reinterpret_cast<float*>(sbuf0);
         __syncthreads();
-        red[tid] = dbacc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[e * DW_THREADS + tid] = dbacc[e];
         __syncthreads();
         if (tid < DW_BO) {
-            const float v = ((red[tid] + red[tid + 128]) + red[tid + 256]) + red[tid + 384];
+            const int c = tid >> 3, e = tid & 7;
+            float v = 0.f;
+            for (int r = 0; r < DW_THREADS / 16; ++r) v += red[e * DW_THREADS + r * 16 + c];
             float* d = dbout + (direct ? 0 : static_cast<int64_t>(slice) * Co) + o0 + tid;
             *d = (direct && accumulate) ? *d + v : v;
         }
@@ -425,14 +433,9 @@ hipError_t launch_dw_partials(const DwPlan& plan, bool bf16, const void* X, cons
     const bool direct = plan.slices == 1;
     hipError_t err;
     if (plan.mfma) {
-        // 145.5 KiB of dynamic LDS: above the default limit, so raise it once.
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(k_dw_mfma), hipFuncAttributeMaxDynamicSharedMemorySize,
-            static_cast<int>(DW_LDS));
-        if (attr != hipSuccess) return attr;
         const int groups = (plan.taps * (Ci / DW_BI) + 2) / 3;
         dim3 grid(groups * (Co / DW_BO) * plan.slices);
-        hipLaunchKernelGGL(k_dw_mfma, grid, dim3(DW_THREADS), DW_LDS, stream, static_cast<const uint16_t*>(X), N,
+        hipLaunchKernelGGL(k_dw_mfma, grid, dim3(DW_THREADS), 0, stream, static_cast<const uint16_t*>(X), N,
                            static_cast<const uint16_t*>(dY), direct ? dW : part,
                            db ? (direct ? db : dbpart) : nullptr, static_cast<int>(n), Ci, Co, plan.taps,
                            static_cast<int>(plan.slice_tokens), direct ? 1 : 0, accumulate);
