@@ -38,29 +38,6 @@ __device__ __forceinline__ int clamp_index(int m, int n) {
     return (static_cast<unsigned>(m) < static_cast<unsigned>(n)) ? m : -1;
 }
 
-// 8x8 transpose of 16-bit elements held as 8 rows of 4 dwords (element 2d in
-// the low half of dword d, element 2d+1 in the high half).  out[c] is column c
-// of the input, in the same packing.  Each output dword takes one half of a
-// dword from each of two neighbouring rows: one byte permute (v_perm_b32,
-// bytes 0-3 from the second operand, 4-7 from the first).
-__device__ __forceinline__ void transpose8x8_b16(const uint4 in[8], uint4 out[8]) {
-    uint32_t r[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        r[i][0] = in[i].x; r[i][1] = in[i].y; r[i][2] = in[i].z; r[i][3] = in[i].w;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        // even c: low halves  (a & 0xffff) | (b << 16)
-        // odd c:  high halves (a >> 16) | (b & 0xffff0000)
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t o[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(r[2 * p + 1][c >> 1], r[2 * p][c >> 1], sel);
-        out[c] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
-
 // Raw buffer loads: a 128-bit resource (base, byte range) in scalar
 // registers, 32-bit per-lane byte offsets, and the hardware range check: a
 // load at an offset at or past the range returns zeros and makes no memory
