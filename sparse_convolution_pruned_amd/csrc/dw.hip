@@ -39,9 +39,9 @@ hipError_t launch_dw_valu(bool bf16, const void* X, const int32_t* N, const void
 // buffer_load ... lds (gfx950: 16 bytes per lane, 1 KB per wave instruction,
 // no registers and no LDS store instructions).  The MFMA fragments, which
 // need 8 tokens per lane along k, come from those rows through the
-// transposing LDS read ds_read_b64_tr_b16.  The step of s + 1 is requested
-// into the free buffer at the start of step s, ahead of step s's MFMAs;
-// each step ends with a single barrier, which also waits for it.  Staging
+// transposing LDS read ds_read_b64_tr_b16.  Step s + 1 is requested into
+// the free buffer during step s, after its first k-step of MFMAs; each step
+// ends with a single barrier, which also waits for those loads.  Staging
 // 8 x 8 blocks through registers with v_perm transposes and LDS stores took
 // 8-13% longer per call.
 //
@@ -143,12 +143,15 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     // Stage step s into `buf`: 8 direct loads per wave, block blk0 + j
     // holding tokens 16 q + blk0 + j.  Rows of pruned neighbours, of empty
     // units and of tokens past the slice read as zeros.
-    auto stage = [&](int s, char* buf) {
+    // this lane's 8 table entries of step s (tokens 16 dq + blk0 .. +7), two 16-byte reads
+    auto entries = [&](int s, int4& e0, int4& e1) {
+        const int* nt = &ntab[((s & 1) * 3 + (is_x ? tile : 0)) * DW_TK + 16 * dq + blk0];
+        e0 = *reinterpret_cast<const int4*>(nt);
+        e1 = *reinterpret_cast<const int4*>(nt + 4);
+    };
+    auto issue = [&](int s, char* buf, const int4& e0, const int4& e1) {
         char* tb = buf + tile * DW_TILEB;
         const int lim = cnt - s * DW_TK;
-        // this lane's 8 table entries (tokens 16 dq + blk0 .. +7), two 16-byte reads
-        const int* nt = &ntab[((s & 1) * 3 + (is_x ? tile : 0)) * DW_TK + 16 * dq + blk0];
-        const int4 e0 = *reinterpret_cast<const int4*>(nt), e1 = *reinterpret_cast<const int4*>(nt + 4);
         const int m8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
         const rsrc_t rs = is_x ? rX : rY;
 #pragma unroll
@@ -185,10 +188,23 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
 #pragma unroll
     for (int e = 0; e < 8; ++e) dbacc[e] = 0.f;
 
-    auto mma_step = [&](const char* xb) {
+    auto stage = [&](int s, char* buf) {
+        int4 e0, e1;
+        entries(s, e0, e1);
+        issue(s, buf, e0, e1);
+    };
+    // Step s's MFMAs from buffer xb.  With `more`, step s + 1 is staged into
+    // nxt: its table entries are read first and its direct loads issued
+    // after the first k-step, so that neither the table read's latency nor
+    // the issue of the loads comes before the first MFMAs (issued at the
+    // start of the step, they cost 7-10% of the call).
+    auto mma_step = [&](const char* xb, int s, char* nxt, bool more) {
         const char* yb = xb + 3 * DW_TILEB;
+        int4 e0, e1;
+        if (more) entries(s + 1, e0, e1);
 #pragma unroll
         for (int ks = 0; ks < DW_TK / 16; ++ks) {
+            if (ks == 1 && more) issue(s + 1, nxt, e0, e1);
             const int t0 = 32 * kh + 8 * ks + fv;
             const int r0 = tok_addr(t0), r1 = tok_addr(t0 + 4);
             bf16x8_t a[3], b[2];
@@ -234,12 +250,11 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     // s - 1) and fetches step s + 3's; one barrier per step waits for all of
     // it, the direct loads included.
     auto step = [&](int s, const char* cur, char* nxt) {
-        if (s + 1 < steps) stage(s + 1, nxt);
         if (loader && s + 2 < steps) {
             put_n(s + 2);
             if (s + 3 < steps) fetch_n(s + 3);
         }
-        mma_step(cur);
+        mma_step(cur, s, nxt, s + 1 < steps);
         __syncthreads();
     };
     int s = 0;
