@@ -40,7 +40,7 @@ hipError_t launch_dw_valu(bool bf16, const void* X, const int32_t* N, const void
 // no registers and no LDS store instructions).  The MFMA fragments, which
 // need 8 tokens per lane along k, come from those rows through the
 // transposing LDS read ds_read_b64_tr_b16.  Step s + 1 is requested into
-// the free buffer during step s, after its first k-step of MFMAs; each step
+// the free buffer during step s, after its second k-step of MFMAs; each step
 // ends with a single barrier, which also waits for those loads.  Staging
 // 8 x 8 blocks through registers with v_perm transposes and LDS stores took
 // 8-13% longer per call.
@@ -195,16 +195,17 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     };
     // Step s's MFMAs from buffer xb.  With `more`, step s + 1 is staged into
     // nxt: its table entries are read first and its direct loads issued
-    // after the first k-step, so that neither the table read's latency nor
+    // after the second k-step, so that neither the table read's latency nor
     // the issue of the loads comes before the first MFMAs (issued at the
-    // start of the step, they cost 7-10% of the call).
+    // start of the step, they cost 9-12% of the call), while the loads still
+    // have two k-steps to land before the barrier.
     auto mma_step = [&](const char* xb, int s, char* nxt, bool more) {
         const char* yb = xb + 3 * DW_TILEB;
         int4 e0, e1;
         if (more) entries(s + 1, e0, e1);
 #pragma unroll
         for (int ks = 0; ks < DW_TK / 16; ++ks) {
-            if (ks == 1 && more) issue(s + 1, nxt, e0, e1);
+            if (ks == 2 && more) issue(s + 1, nxt, e0, e1);
             const int t0 = 32 * kh + 8 * ks + fv;
             const int r0 = tok_addr(t0), r1 = tok_addr(t0 + 4);
             bf16x8_t a[3], b[2];
