@@ -59,7 +59,8 @@ def parse():
                         "the timed events) so that no input stays in the caches; warm (default) is primary")
     p.add_argument("--dw-stream", choices=["side", "same"], default="side",
                    help="run each layer's weight gradient on a second stream, concurrent with its "
-                        "input gradient (side), or in order on one stream (same)")
+                        "input gradient (side), or in order on one stream (same); for c4 the chunk "
+                        "driver's dW stream")
     p.add_argument("--cpu-frames", type=int, default=384,
                    help="frames of the workload the CPU oracle is timed on")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -484,9 +485,12 @@ def layer_workload(args):
     passes = cfg["passes"]
     chunked = "chunk_frames" in cfg
     if chunked:
+        # the chunks' weight gradients on a second stream (default priority),
+        # beside the next chunks' index builds and convolutions
+        dws = torch.cuda.Stream() if args.dw_stream == "side" else None
         desc = ops.make_chunked_desc(L.T, L.H, L.W, coords, offs, torch.from_numpy(L.frame_offsets.copy()),
                                      C, C, bf, cfg["chunk_frames"], X=X, Wt=Wt, bias=b, Y=Y, dY=dY,
-                                     dX=dX, dW=dW, db=db, kernel=args.kernel, ksize=K)
+                                     dX=dX, dW=dW, db=db, kernel=args.kernel, ksize=K, dw_stream=dws)
         pm = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
         ws = torch.empty(max(256, ops.sv_chunked_workspace_bytes(desc, pm)), dtype=torch.uint8, device="cuda")
 
@@ -549,7 +553,8 @@ def layer_workload(args):
                       "tflops": round(fl / sec / 1e12, 3),
                       "frac_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "peak_mem_mb": round(torch.cuda.max_memory_allocated() / 2 ** 20, 1),
-                      "workspace_mb": round(ws.numel() / 2 ** 20, 2)}), flush=True)
+                      "workspace_mb": round(ws.numel() / 2 ** 20, 2),
+                      "dw_stream": args.dw_stream if chunked else None}), flush=True)
 
 
 def host_stream_workload(args):

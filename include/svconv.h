@@ -248,6 +248,20 @@ typedef struct sv_chunked_desc {
     int32_t *err_flag;                  /* device int32, nullable                */
     int32_t ksize;                      /* K of a K x K neighbourhood (the _k calls);
                                            0 selects 3.  N, Wt, dW then hold K*K taps */
+    hipStream_t dw_stream;              /* nullable.  With the DW pass and FWD or DX,
+                                           each chunk's dW + db runs on this stream,
+                                           concurrently with the next chunks' index
+                                           builds and convolutions on the call's
+                                           stream.  It first waits for the work
+                                           enqueued on the call's stream before the
+                                           call, and the call's stream waits for it
+                                           at the end, so on the call's stream the
+                                           results are complete in stream order and
+                                           bit-identical to the one-stream run.  The
+                                           workspace then holds a second N table
+                                           (sv_chunked_workspace_bytes counts it).
+                                           The call's own stream here means the
+                                           one-stream run. */
 } sv_chunked_desc;
 
 sv_status sv_sparseconv2d_chunked(const sv_chunked_desc *desc, uint32_t passes,

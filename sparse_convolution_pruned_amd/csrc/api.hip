@@ -302,6 +302,7 @@ struct ChunkLayout {
     size_t n_bytes = 0;       // chunk-local N table
     size_t w_bytes = 0;       // forward weights repacked for the MFMA kernel
     size_t dw_bytes = 0;      // dW/db partials of the largest plan
+    size_t n2_bytes = 0;      // second N table when dW runs on its own stream
     size_t total = 0;
 };
 
@@ -332,9 +333,26 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
     }
     L->n_bytes = align_up(static_cast<size_t>(L->max_tokens) * L->taps * sizeof(int32_t));
     L->w_bytes = (passes & SV_PASS_FWD) ? fwd_ws_bytes(d->C_in, d->C_out, d->dtype, L->max_tokens, L->taps) : 0;
-    L->total = L->n_bytes + L->w_bytes + L->dw_bytes;
+    const bool split = d->dw_stream && (passes & SV_PASS_DW) && (passes & (SV_PASS_FWD | SV_PASS_DX));
+    L->n2_bytes = split ? L->n_bytes : 0;
+    L->total = L->n_bytes + L->w_bytes + L->dw_bytes + L->n2_bytes;
     return true;
 }
+
+// Events of a call, destroyed when the call returns (a recorded event is
+// released by the runtime once the device has passed it).
+struct CallEvents {
+    hipEvent_t ev[6] = {};
+    int made = 0;
+    bool make(int k) {
+        for (; made < k; ++made)
+            if (hipEventCreateWithFlags(&ev[made], hipEventDisableTiming) != hipSuccess) return false;
+        return true;
+    }
+    ~CallEvents() {
+        for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
+    }
+};
 
 }  // namespace
 
@@ -388,13 +406,34 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
         }
     }
     const int32_t* ho = d->frame_offsets_host;
+    // With a dW stream (the workspace then has a second N table): chunk c's
+    // table is built into table c & 1 on `stream`; the dW stream waits for
+    // that build (ev_idx), and the build of chunk c + 2 into the same table
+    // waits for chunk c's dW (ev_dw).
+    const bool split = L.n2_bytes > 0 && d->dw_stream != stream;
+    hipStream_t ds = split ? d->dw_stream : stream;
+    int32_t* Ntab[2] = {Nc, split ? reinterpret_cast<int32_t*>(static_cast<char*>(dws) + L.dw_bytes) : Nc};
+    CallEvents E;
+    hipEvent_t ev_start = nullptr, ev_join = nullptr, *ev_idx = nullptr, *ev_dw = nullptr;
+    if (split && d->T > 0) {
+        if (!E.make(6)) return SV_ERR_HIP;
+        ev_start = E.ev[0];
+        ev_idx = E.ev + 1;
+        ev_dw = E.ev + 3;
+        ev_join = E.ev[5];
+        if (hipEventRecord(ev_start, stream) != hipSuccess || hipStreamWaitEvent(ds, ev_start, 0) != hipSuccess)
+            return SV_ERR_HIP;
+    }
     bool first = true;
-    for (int f0 = 0; f0 < d->T; f0 += d->chunk_frames) {
+    for (int f0 = 0, ci = 0; f0 < d->T; f0 += d->chunk_frames, ++ci) {
         const int f1 = std::min(d->T, f0 + d->chunk_frames);
         const int64_t t0 = ho[f0], nc = static_cast<int64_t>(ho[f1]) - t0;
+        int32_t* Nc = Ntab[ci & 1];
+        if (split && ci >= 2 && hipStreamWaitEvent(stream, ev_dw[ci & 1], 0) != hipSuccess) return SV_ERR_HIP;
         sv_status st = hip_status(launch_build_index(d->coords, d->frame_offsets, f0, f1 - f0, d->H, d->W, L.K,
                                                      nc, t0, Nc, nullptr, d->err_flag, stream));
         if (st != SV_OK) return st;
+        if (split && hipEventRecord(ev_idx[ci & 1], stream) != hipSuccess) return SV_ERR_HIP;
         const char* X = d->X ? static_cast<const char*>(d->X) + t0 * d->C_in * es : nullptr;
         const char* dY = d->dY ? static_cast<const char*>(d->dY) + t0 * d->C_out * es : nullptr;
         char* Yc = (passes & SV_PASS_FWD) ? static_cast<char*>(d->Y) + t0 * d->C_out * es : nullptr;
@@ -414,13 +453,18 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
             }
         }
         if (passes & SV_PASS_DW) {
+            if (split && hipStreamWaitEvent(ds, ev_idx[ci & 1], 0) != hipSuccess) return SV_ERR_HIP;
             const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16, L.taps);
             st = hip_status(launch_dw(plan, d->dtype == SV_BF16, X, Nc, dY, d->dW, d->db, nc, d->C_in,
-                                      d->C_out, first ? 0 : 1, dws, stream));
+                                      d->C_out, first ? 0 : 1, dws, ds));
             if (st != SV_OK) return st;
+            if (split && hipEventRecord(ev_dw[ci & 1], ds) != hipSuccess) return SV_ERR_HIP;
         }
         first = false;
     }
+    if (split && d->T > 0 &&
+        (hipEventRecord(ev_join, ds) != hipSuccess || hipStreamWaitEvent(stream, ev_join, 0) != hipSuccess))
+        return SV_ERR_HIP;
     if (first && (passes & SV_PASS_DW)) {
         // No frames at all: the gradients of an empty sum are zero.
         const DwPlan plan = plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16, L.taps);

@@ -69,6 +69,7 @@ class ChunkedDesc(ctypes.Structure):
         ("Y", ctypes.c_void_p), ("dY", ctypes.c_void_p), ("dX", ctypes.c_void_p),
         ("dW", ctypes.c_void_p), ("db", ctypes.c_void_p), ("err_flag", ctypes.c_void_p),
         ("ksize", ctypes.c_int32),
+        ("dw_stream", ctypes.c_void_p),
     ]
 
 
@@ -358,10 +359,11 @@ def sv_sparseconv2d_bwd_dw_reduce_k(dW, db, n, dtype, workspace, accumulate=Fals
 
 def make_chunked_desc(T, H, W, coords, frame_offsets, frame_offsets_host, C_in, C_out, dtype,
                       chunk_frames, X=None, Wt=None, bias=None, Y=None, dY=None, dX=None,
-                      dW=None, db=None, err_flag=None, kernel="auto", ksize=3):
+                      dW=None, db=None, err_flag=None, kernel="auto", ksize=3, dw_stream=None):
     """Build the descriptor; `frame_offsets_host` must be a CPU int32 tensor
     (kept referenced by the returned object).  `ksize`: K of the K x K
-    neighbourhood."""
+    neighbourhood.  `dw_stream`: a torch stream for the chunks' weight
+    gradients (None: everything on the call's stream)."""
     assert frame_offsets_host.device.type == "cpu" and frame_offsets_host.dtype == torch.int32
     fh = frame_offsets_host.contiguous()
     d = ChunkedDesc()
@@ -374,7 +376,8 @@ def make_chunked_desc(T, H, W, coords, frame_offsets, frame_offsets_host, C_in, 
     d.X, d.Wt, d.bias, d.Y = _ptr(X), _ptr(Wt), _ptr(bias), _ptr(Y)
     d.dY, d.dX, d.dW, d.db, d.err_flag = _ptr(dY), _ptr(dX), _ptr(dW), _ptr(db), _ptr(err_flag)
     d.ksize = int(ksize)
-    d._keep = (fh, coords, frame_offsets, X, Wt, bias, Y, dY, dX, dW, db, err_flag)
+    d.dw_stream = None if dw_stream is None else dw_stream.cuda_stream
+    d._keep = (fh, coords, frame_offsets, X, Wt, bias, Y, dY, dX, dW, db, err_flag, dw_stream)
     return d
 
 

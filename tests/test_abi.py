@@ -117,6 +117,22 @@ def test_chunked_workspace_flat_in_T(lib):
         == ops.SV_ERR_INVALID_ARG
 
 
+def test_chunked_dw_stream_workspace(lib):
+    """With a dW stream the workspace holds a second N table (4 * 9 bytes
+    per token of the largest chunk, rounded up), and only when the dW pass
+    runs beside a forward or input-gradient pass."""
+    T = 512
+    offs = (np.arange(T + 1, dtype=np.int32) * 59).astype(np.int32)
+    d = _desc(T, offs)
+    full = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
+    one = {p: lib.sv_chunked_workspace_bytes(ctypes.byref(d), p) for p in (full, ops.SV_PASS_DW)}
+    d.dw_stream = 1     # any non-null handle: only the layout is computed here
+    two = {p: lib.sv_chunked_workspace_bytes(ctypes.byref(d), p) for p in (full, ops.SV_PASS_DW)}
+    ntab = (256 * 59 * 9 * 4 + 255) // 256 * 256
+    assert two[full] == one[full] + ntab
+    assert two[ops.SV_PASS_DW] == one[ops.SV_PASS_DW]
+
+
 def test_workloads_shapes():
     """The synthetic workloads have the sizes the configurations state."""
     assert wl.make_layer("c1").n == 98
