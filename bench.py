@@ -710,9 +710,13 @@ def adapter_workload(args):
     def fwd():
         ops.sv_adapter_fwd(X, N, P["Wd"], P["bd"], P["Wc"], P["bc"], P["Wu"], P["bu"], H1, H2, Y, wf, args.kernel)
 
+    # the three weight gradients on a second stream (default priority),
+    # beside the input gradients
+    dws = torch.cuda.Stream() if args.dw_stream == "side" else None
+
     def bwd():
         ops.sv_adapter_bwd(X, N, P["Wd"], P["Wc"], P["Wu"], H1, H2, dY, dX, dWd, dbd, dWc, dbc, dWu, dbu, wb,
-                           args.kernel)
+                           args.kernel, dw_stream=dws)
 
     for _ in range(args.warmup):
         fwd()
@@ -736,7 +740,8 @@ def adapter_workload(args):
                       "fwd_tflops": round(fl_f / tf / 1e12, 2), "bwd_tflops": round(fl_b / tb / 1e12, 2),
                       "step_tflops": round((fl_f + fl_b) / (tf + tb) / 1e12, 2),
                       "frac_bf16_peak": round((fl_f + fl_b) / (tf + tb) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                      "workspace_mb": {"fwd": round(wf.numel() / 2 ** 20, 2), "bwd": round(wb.numel() / 2 ** 20, 2)}}),
+                      "workspace_mb": {"fwd": round(wf.numel() / 2 ** 20, 2), "bwd": round(wb.numel() / 2 ** 20, 2)},
+                      "dw_stream": args.dw_stream}),
           flush=True)
 
 

@@ -367,13 +367,19 @@ sv_status sv_adapter_fwd(const void *X, const int32_t *N, int64_t n, int32_t K, 
  * (the last sum in one kernel, before its one rounding).  dW* and db* are
  * fp32, overwritten; db* nullable.  dH2 and dH1 are held in the workspace in
  * `dtype` (sv_adapter_workspace_bytes(1, ...) bytes, 256-byte aligned).
- * Deterministic. */
+ * Deterministic.
+ * dw_stream (nullable; the call's own stream means the same): the three
+ * weight gradients run on it, each after the tensor it reads is ready on
+ * `stream`, beside the input gradients on `stream`; `stream` waits for it at
+ * the end, so on `stream` every output is complete in stream order and
+ * bit-identical to the one-stream run. */
 sv_status sv_adapter_bwd(const void *X, const int32_t *N, int64_t n, int32_t K, int32_t C, int32_t r,
                          const void *Wd, const void *Wc, const void *Wu,
                          const void *H1, const void *H2, const void *dY,
                          void *dX, float *dWd, float *dbd, float *dWc, float *dbc,
                          float *dWu, float *dbu, sv_dtype dtype, sv_kernel kernel,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+                         void *workspace, size_t workspace_bytes, hipStream_t stream,
+                         hipStream_t dw_stream);
 /* Workspace bytes of sv_adapter_fwd (backward == 0) or sv_adapter_bwd;
  * 0 for invalid sizes.  Depends only on the arguments. */
 size_t sv_adapter_workspace_bytes(int32_t backward, int64_t n, int32_t K, int32_t C, int32_t r,

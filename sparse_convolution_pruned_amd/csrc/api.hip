@@ -810,7 +810,7 @@ sv_status sv_adapter_bwd(const void* X, const int32_t* N, int64_t n, int32_t K, 
                          const void* Wd, const void* Wc, const void* Wu, const void* H1, const void* H2,
                          const void* dY, void* dX, float* dWd, float* dbd, float* dWc, float* dbc, float* dWu,
                          float* dbu, sv_dtype dtype, sv_kernel kernel, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, hipStream_t dw_stream) {
     AdapterLayout L;
     sv_status st = adapter_layout(true, n, K, C, r, dtype, &L);
     if (st != SV_OK) return st;
@@ -830,22 +830,41 @@ sv_status sv_adapter_bwd(const void* X, const int32_t* N, int64_t n, int32_t K, 
     void* dH2 = base + L.id_bytes;
     void* dH1 = base + L.id_bytes + L.h_bytes;
     void* dws = base + L.id_bytes + 2 * L.h_bytes;
+    // With a dW stream each weight gradient waits (event) for the tensor it
+    // reads, produced on `stream`; they run in order on that stream and share
+    // one partials region.  Nothing either stream reads is overwritten.
+    const bool split = dw_stream && dw_stream != stream && n > 0;
+    hipStream_t ds = split ? dw_stream : stream;
+    CallEvents E;
+    if (split && !E.make(4)) return SV_ERR_HIP;
+    auto handoff = [&](int e) -> sv_status {
+        if (!split) return SV_OK;
+        if (hipEventRecord(E.ev[e], stream) != hipSuccess || hipStreamWaitEvent(ds, E.ev[e], 0) != hipSuccess)
+            return SV_ERR_HIP;
+        return SV_OK;
+    };
     if ((st = hip_status(launch_iota(I, n, stream))) != SV_OK) return st;
+    if ((st = handoff(0)) != SV_OK) return st;
     // up-projection: dWu, dbu, then dH2 = dY Wu^T
-    if ((st = hip_status(launch_dw(plan_dw(n, r, C, bf, 1), bf, H2, I, dY, dWu, dbu, n, r, C, 0, dws, stream))) !=
+    if ((st = hip_status(launch_dw(plan_dw(n, r, C, bf, 1), bf, H2, I, dY, dWu, dbu, n, r, C, 0, dws, ds))) !=
         SV_OK)
         return st;
     if ((st = run_dx(dY, I, Wu, dH2, n, r, C, 1, dtype, kernel, stream)) != SV_OK) return st;
+    if ((st = handoff(1)) != SV_OK) return st;
     // K x K convolution: dWc, dbc, then dH1
     if ((st = hip_status(launch_dw(plan_dw(n, r, r, bf, L.taps), bf, H1, N, dH2, dWc, dbc, n, r, r, 0, dws,
-                                   stream))) != SV_OK)
+                                   ds))) != SV_OK)
         return st;
     if ((st = run_dx(dH2, N, Wc, dH1, n, r, r, L.taps, dtype, kernel, stream)) != SV_OK) return st;
+    if ((st = handoff(2)) != SV_OK) return st;
     // down-projection: dWd, dbd, then dX = dY + dH1 Wd^T
-    if ((st = hip_status(launch_dw(plan_dw(n, C, r, bf, 1), bf, X, I, dH1, dWd, dbd, n, C, r, 0, dws, stream))) !=
+    if ((st = hip_status(launch_dw(plan_dw(n, C, r, bf, 1), bf, X, I, dH1, dWd, dbd, n, C, r, 0, dws, ds))) !=
         SV_OK)
         return st;
-    return run_dx(dH1, I, Wd, dX, n, C, r, 1, dtype, kernel, stream, dY);
+    if ((st = run_dx(dH1, I, Wd, dX, n, C, r, 1, dtype, kernel, stream, dY)) != SV_OK) return st;
+    if (split && (hipEventRecord(E.ev[3], ds) != hipSuccess || hipStreamWaitEvent(stream, E.ev[3], 0) != hipSuccess))
+        return SV_ERR_HIP;
+    return SV_OK;
 }
 
 // ------------------------------------------------------ cross-attention

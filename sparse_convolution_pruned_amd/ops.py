@@ -128,7 +128,7 @@ def load(path: str = LIB_PATH):
         "sv_xattn_bwd": ([P, P, P, P, P, i64, i64, i32, ctypes.c_float, E, P, P, P, sz, P], E),
         "sv_xattn_workspace_bytes": ([i32, i64, i64, i32], sz),
         "sv_adapter_fwd": ([P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, E, E, P, sz, P], E),
-        "sv_adapter_bwd": ([P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, E, E, P, sz, P], E),
+        "sv_adapter_bwd": ([P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, E, E, P, sz, P, P], E),
         "sv_adapter_workspace_bytes": ([i32, i64, i32, i32, i32, E], sz),
         "sv_status_string": ([E], ctypes.c_char_p),
         "sv_version": ([], ctypes.c_char_p),
@@ -482,7 +482,7 @@ def sv_adapter_fwd(X, N, Wd, bd, Wc, bc, Wu, bu, H1, H2, Y, workspace, kernel="a
 
 
 def sv_adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, dX, dWd, dbd, dWc, dbc, dWu, dbu, workspace, kernel="auto",
-                   stream=None):
+                   stream=None, dw_stream=None):
     n, C, r, K = _adapter_shapes(X, N, Wd, Wc, Wu)
     assert H1.shape == H2.shape == (n, r) and dY.shape == dX.shape == (n, C)
     assert dWd.shape == (C, r) and dWc.shape == Wc.shape and dWu.shape == (r, C)
@@ -491,7 +491,8 @@ def sv_adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, dX, dWd, dbd, dWc, dbc, dWu, db
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().sv_adapter_bwd(_ptr(X), _ptr(N), n, K, C, r, _ptr(Wd), _ptr(Wc), _ptr(Wu), _ptr(H1), _ptr(H2),
                                _ptr(dY), _ptr(dX), _ptr(dWd), _ptr(dbd), _ptr(dWc), _ptr(dbc), _ptr(dWu),
-                               _ptr(dbu), _dt(X), _kernel(kernel), _ptr(workspace), wsb, _stream(stream))
+                               _ptr(dbu), _dt(X), _kernel(kernel), _ptr(workspace), wsb, _stream(stream),
+                               None if dw_stream is None else ctypes.c_void_p(dw_stream.cuda_stream))
     _check(st, "sv_adapter_bwd")
 
 
@@ -510,8 +511,10 @@ def adapter_fwd(X, N, Wd, bd, Wc, bc, Wu, bu, kernel="auto"):
     return Y, H1, H2
 
 
-def adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, kernel="auto"):
-    """Returns a dict: dX (X's dtype) and fp32 dWd, dbd, dWc, dbc, dWu, dbu."""
+def adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, kernel="auto", dw_stream=None):
+    """Returns a dict: dX (X's dtype) and fp32 dWd, dbd, dWc, dbc, dWu, dbu.
+    `dw_stream`: a torch stream for the three weight gradients (None: all on
+    the current stream)."""
     n, C = X.shape
     r = Wd.shape[1]
     f32 = dict(dtype=torch.float32, device=X.device)
@@ -521,7 +524,7 @@ def adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, kernel="auto"):
     ws = torch.empty(max(256, sv_adapter_workspace_bytes(True, n, ksize_of_taps(Wc.shape[0]), C, r, X.dtype)),
                      dtype=torch.uint8, device=X.device)
     sv_adapter_bwd(X, N, Wd, Wc, Wu, H1, H2, dY, g["dX"], g["dWd"], g["dbd"], g["dWc"], g["dbc"], g["dWu"],
-                   g["dbu"], ws, kernel)
+                   g["dbu"], ws, kernel, dw_stream=dw_stream)
     return g
 
 

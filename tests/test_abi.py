@@ -280,10 +280,10 @@ def test_adapter_validation_and_workspace(lib):
                               BF16, 0, FAKE, 1 << 20, None) == ops.SV_ERR_INVALID_ARG
     bargs = (FAKE, FAKE, 8, 3, 64, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
              None)
-    assert lib.sv_adapter_bwd(*bargs, BF16, 0, None, 0, None) == ops.SV_ERR_WORKSPACE
-    assert lib.sv_adapter_bwd(*bargs, BF16, 0, ctypes.c_void_p(4097), 1 << 30, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_adapter_bwd(*bargs, BF16, 0, None, 0, None, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_adapter_bwd(*bargs, BF16, 0, ctypes.c_void_p(4097), 1 << 30, None, None) == ops.SV_ERR_INVALID_ARG
     nodw = bargs[:13] + (None,) + bargs[14:]
-    assert lib.sv_adapter_bwd(*nodw, BF16, 0, FAKE, 1 << 30, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_adapter_bwd(*nodw, BF16, 0, FAKE, 1 << 30, None, None) == ops.SV_ERR_INVALID_ARG
 
 
 def test_split_forms_validation(lib):

@@ -97,3 +97,39 @@ def test_adapter_full_size_stage0():
     workload (the benchmark's adapter shape), every output element checked."""
     A = wl.make_adapter_stage0()
     check(A, "auto", "c5 stage 0")
+
+
+@pytest.mark.parametrize("K", [1, 3])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_adapter_bwd_dw_stream_bitwise(K, dt):
+    """The three weight gradients on a second stream give the same bits as
+    the one-stream backward: every kernel and its inputs are the same, and
+    the caller's stream alone orders the results."""
+    A = wl.make_adapter_case(68, 4, 16, 16, 0.6, 256, 128, K, dt)
+    t = tdtype(A.dtype)
+    X = dev(A.X, t)
+    N = ops.build_index(dev(A.coords), dev(A.frame_offsets), A.T, A.H, A.W, K=A.K)
+    P = {k: dev(getattr(A, k), t) for k in ("Wd", "bd", "Wc", "bc", "Wu", "bu")}
+    Y, H1, H2 = ops.adapter_fwd(X, N, P["Wd"], P["bd"], P["Wc"], P["bc"], P["Wu"], P["bu"])
+    dY = dev(A.dY, t)
+    a = ops.adapter_bwd(X, N, P["Wd"], P["Wc"], P["Wu"], H1, H2, dY)
+    b = ops.adapter_bwd(X, N, P["Wd"], P["Wc"], P["Wu"], H1, H2, dY, dw_stream=torch.cuda.Stream())
+    a = {k: v.cpu() for k, v in a.items()}
+    b = {k: v.cpu() for k, v in b.items()}      # ordered by the current stream alone
+    for k in GRADS:
+        assert torch.equal(a[k], b[k]), f"{k} differs with the dW stream"
+
+
+def test_adapter_bwd_dw_stream_full_size():
+    A = wl.make_adapter_stage0()
+    t = tdtype(A.dtype)
+    X = dev(A.X, t)
+    N = ops.build_index(dev(A.coords), dev(A.frame_offsets), A.T, A.H, A.W, K=A.K)
+    P = {k: dev(getattr(A, k), t) for k in ("Wd", "bd", "Wc", "bc", "Wu", "bu")}
+    Y, H1, H2 = ops.adapter_fwd(X, N, P["Wd"], P["bd"], P["Wc"], P["bc"], P["Wu"], P["bu"])
+    dY = dev(A.dY, t)
+    a = {k: v.cpu() for k, v in ops.adapter_bwd(X, N, P["Wd"], P["Wc"], P["Wu"], H1, H2, dY).items()}
+    b = {k: v.cpu() for k, v in ops.adapter_bwd(X, N, P["Wd"], P["Wc"], P["Wu"], H1, H2, dY,
+                                                 dw_stream=torch.cuda.Stream()).items()}
+    for k in GRADS:
+        assert torch.equal(a[k], b[k]), f"{k} differs with the dW stream"
