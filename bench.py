@@ -34,9 +34,12 @@ if ROOT not in sys.path:
 METRIC = "SparseConv2D fwd+bwd effective TFLOP/s & HBM GB/s vs roofline, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
 HBM_TBPS = 8.0               # MI355X HBM3E
-PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector
+# fp32 vector peak of this build: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP (FMA)
+# x 2.4 GHz = 78.6 TFLOP/s.  The 157.3 TFLOP/s of the data sheet counts packed
+# fp32 (two FMAs per lane per instruction), which this library's kernels are
+# built without.
+PEAK_FP32_VALU_TFLOPS = 78.6
 PCIE_GBPS_PER_DIRECTION = 64.0   # PCIe 5.0 x16 host link, one direction
-PEAK_F32_TFLOPS = 157.3      # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 
 
@@ -132,6 +135,9 @@ class StagedRun:
         self.plan = None
         vb = max(256, ops.sv_workspace_bytes(ops.SV_OP_FWD, max(self.ns), C, C, bf))
         self.V = [torch.empty(vb, dtype=torch.uint8, device="cuda") for _ in range(self.L)]
+        # the input gradient's weights in fragment order, per layer
+        pb = max(256, ops.sv_workspace_bytes(ops.SV_OP_DX, max(self.ns), C, C, bf))
+        self.P = [torch.empty(pb, dtype=torch.uint8, device="cuda") for _ in range(self.L)]
 
     def flops(self):
         """Effective FLOPs per step: 2 * n * 9 * C_in * C_out per pass, all
@@ -151,10 +157,18 @@ class StagedRun:
         ops, kern = self.ops, self.kernel
         rec = ev.record if ev is not None else (lambda *a, **k: None)
         S = self.S
+        packed = kern != "valu"
         for s in range(len(self.ns)):
             t = rec("index", None)
             ops.sv_build_index(self.coords[s], self.offs[s], S.T, S.H, S.W, self.N[s], None, self.flag)
             rec("index", t, units=self.ns[s])
+        if packed:
+            # every layer's weights, repacked for the forward and the input gradient
+            t = rec("repack", None)
+            for l in range(self.L):
+                ops.sv_repack_fwd_k(self.W[l], self.V[l])
+                ops.sv_repack_dx_k(self.W[l], self.P[l])
+            rec("repack", t, units=self.L)
         for l in range(self.L):
             s = self.stage_of[l]
             if l > 0 and self.stage_of[l - 1] != s:
@@ -162,8 +176,11 @@ class StagedRun:
                 ops.sv_stage_gather(self.ys[l - 1], self.sels[s], self.xs[l])
                 rec("gather", t, units=self.ns[s])
             t = rec("fwd", None)
-            ops.sv_sparseconv2d_fwd(self.xs[l], self.N[s], self.W[l], self.b[l], self.ys[l], kern,
-                                    workspace=self.fws)
+            if packed:
+                ops.sv_sparseconv2d_fwd_packed_k(self.xs[l], self.N[s], self.V[l], self.b[l], self.ys[l], 3)
+            else:
+                ops.sv_sparseconv2d_fwd(self.xs[l], self.N[s], self.W[l], self.b[l], self.ys[l], kern,
+                                        workspace=self.fws)
             rec("fwd", t, units=self.ns[s])
         g = self.dy_last
         for l in reversed(range(self.L)):
@@ -172,7 +189,10 @@ class StagedRun:
             ops.sv_sparseconv2d_bwd_dw(self.xs[l], self.N[s], g, self.dW[l], self.db[l], False, self.ws)
             rec("dw", t, units=self.ns[s])
             t = rec("dx", None)
-            ops.sv_sparseconv2d_bwd_dx(g, self.N[s], self.W[l], self.gx[l], kern)
+            if packed:
+                ops.sv_sparseconv2d_bwd_dx_packed_k(g, self.N[s], self.P[l], self.gx[l], 3)
+            else:
+                ops.sv_sparseconv2d_bwd_dx(g, self.N[s], self.W[l], self.gx[l], kern)
             rec("dx", t, units=self.ns[s])
             g = self.gx[l]
             if l > 0 and self.stage_of[l - 1] != s:
@@ -225,6 +245,7 @@ class StagedRun:
 
         def repack(l, stream):
             call("sv_repack_fwd_k", P(self.W[l]), K, C, C, bf, P(self.V[l]), self.V[l].numel(), hs[id(stream)])
+            call("sv_repack_dx_k", P(self.W[l]), K, C, C, bf, P(self.P[l]), self.P[l].numel(), hs[id(stream)])
 
         vb = self.ws.numel()
         # side stream: the later stages' index tables and layers' weights
@@ -234,10 +255,11 @@ class StagedRun:
             index(s, side)
         for l in range(1, self.L):
             repack(l, side)
+        call("sv_repack_dx_k", P(self.W[0]), K, C, C, bf, P(self.P[0]), self.P[0].numel(), hs[id(side)])
         record(self.ev_prep, side)
         # main stream: forward
         index(0, main)
-        repack(0, main)
+        call("sv_repack_fwd_k", P(self.W[0]), K, C, C, bf, P(self.V[0]), self.V[0].numel(), hs[id(main)])
         for l in range(self.L):
             s = self.stage_of[l]
             if l == 1:
@@ -256,8 +278,8 @@ class StagedRun:
             wait(side, self.ready[l])
             call("sv_sparseconv2d_bwd_dw", P(self.xs[l]), P(self.N[s]), P(g), P(self.dW[l]), P(self.db[l]),
                  self.ns[s], C, C, bf, 0, P(self.ws), vb, hs[id(side)])
-            call("sv_sparseconv2d_bwd_dx", P(g), P(self.N[s]), P(self.W[l]), P(self.gx[l]), self.ns[s], C, C, bf,
-                 ops.KERNELS[self.kernel], hs[id(main)])
+            call("sv_sparseconv2d_bwd_dx_packed_k", P(g), P(self.N[s]), P(self.P[l]), P(self.gx[l]), self.ns[s], K,
+                 C, C, bf, hs[id(main)])
             g = self.gx[l]
             if l > 0 and self.stage_of[l - 1] != s:
                 call("sv_stage_scatter", P(g), P(self.sels[s]), self.ns[s], P(self.gscat[l]), self.ns[s - 1], C, bf,
@@ -786,15 +808,18 @@ def main():
     tflops = fl / (wall / args.steps) / 1e12
 
     # instrumented timed region: the same K steps with HIP events per call,
-    # every call alone on the current stream (no dW/dX overlap), so that the
-    # per-kernel durations are the kernels' own
+    # every call alone on the current stream (no dW/dX overlap), so that
+    # the per-kernel durations are the kernels' own.  The host issues these
+    # calls slower than the GPU runs them, and an event pair around a call
+    # would then also time the host's gap before the kernel; so the region
+    # starts behind a spin kernel long enough for the host to queue all of
+    # it, and the GPU runs the calls back to back.
     ev = Events(torch)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    torch.cuda._sleep(int(6.0e6 * args.steps))          # ~3 ms per step at ~2 GHz: the host's pace here
     for _ in range(args.steps):
         run.step(ev, overlap=False)
     torch.cuda.synchronize()
-    ms_instr = (time.perf_counter() - t1) * 1e3 / args.steps
     kinds = ev.summary()
     C = run.C
     per_unit = {  # algorithmic FLOPs and compulsory HBM bytes per token (bf16)
@@ -804,6 +829,8 @@ def main():
         "index": (0, 40),
         "gather": (0, 4 * C + 4),
         "scatter": (0, 4 * C + 4),
+        # per layer: Wt read and written twice (forward and input-gradient layouts)
+        "repack": (0, 4 * 9 * C * C * 2),
     }
     # gather model: each of the 9 neighbour rows read from memory, no reuse
     gather_unit = 9 * 2 * C + 2 * C + 36
@@ -822,22 +849,24 @@ def main():
             g = gather_unit * d["units"] / sec / 1e9
             breakdown[k]["gbps_gather_model"] = round(g, 1)
             breakdown[k]["frac_hbm_gather_model"] = round(g / (HBM_TBPS * 1e3), 4)
-    # Dominant kernel: k_conv_mfma runs in every forward (after the weight
-    # repack) and every input gradient; the input-gradient entry point
-    # launches it alone, so its HIP events time exactly that kernel.
+    # Dominant kernel: the conv kernel runs in every forward and every input
+    # gradient (k_conv_bfrag at C = 256: the packed entry points launch it
+    # alone, so their HIP events time exactly that kernel).
     conv_ms = kinds["fwd"]["ms"] + kinds["dx"]["ms"]
     valu = args.kernel == "valu"
     if conv_ms >= kinds["dw"]["ms"]:
-        dom, kname, kfiles = "dx", ("k_conv_valu" if valu else "k_conv_mfma"), \
-            ["sparse_convolution_pruned_amd/csrc/" + ("conv_valu.hip" if valu else "conv_mfma.hip")]
+        dom = ("fwd", "dx")
+        kname = "k_conv_valu" if valu else "k_conv_bfrag"
+        kfiles = ["sparse_convolution_pruned_amd/csrc/" + ("conv_valu.hip" if valu else "conv_bfrag.hip")]
     else:
-        dom, kname, kfiles = "dw", "k_dw_mfma", ["sparse_convolution_pruned_amd/csrc/dw.hip"]
+        dom, kname, kfiles = ("dw",), "k_dw_mfma", ["sparse_convolution_pruned_amd/csrc/dw.hip"]
     # the VALU conv kernels are bound by fp32 vector arithmetic
-    bound, peak = ("alu", PEAK_FP32_VALU_TFLOPS) if (valu and dom == "dx") else ("mfma", PEAK_BF16_TFLOPS)
-    d = kinds[dom]
+    bound, peak = ("alu", PEAK_FP32_VALU_TFLOPS) if (valu and dom != ("dw",)) else ("mfma", PEAK_BF16_TFLOPS)
+    d = {"ms": sum(kinds[k]["ms"] for k in dom), "units": sum(kinds[k]["units"] for k in dom),
+         "launches": sum(kinds[k]["launches"] for k in dom)}
     # per launch: FLOPs of the tokens it processed / its duration, averaged
     # over launches weighted by duration (sum of FLOPs / sum of durations)
-    achieved = per_unit[dom][0] * d["units"] / (d["ms"] / 1e3) / 1e12
+    achieved = per_unit[dom[0]][0] * d["units"] / (d["ms"] / 1e3) / 1e12
     tr = traffic_record(kname, kfiles)
     roofline = {
         "bound": bound,
@@ -848,7 +877,7 @@ def main():
         "frac": round(achieved / peak, 4),
         "traffic": None if tr is None else tr["bytes_per_launch"],
         "avg_launch_us": round(d["ms"] * 1e3 / d["launches"], 2),
-        "flops_per_launch": round(per_unit[dom][0] * d["units"] / d["launches"]),
+        "flops_per_launch": round(per_unit[dom[0]][0] * d["units"] / d["launches"]),
         "launches_timed": d["launches"],
     }
     step_bytes = sum(per_unit[k][1] * kinds[k]["units"] for k in kinds) / args.steps
@@ -877,7 +906,6 @@ def main():
         },
         "hbm_gbps_compulsory": round(step_bytes / (wall / args.steps) / 1e9, 1),
         "peak_mem_mb": round(torch.cuda.max_memory_allocated() / 2 ** 20, 1),
-        "ms_per_step_instrumented": round(ms_instr, 4),
         "kernels": breakdown,
         "roofline": roofline,
     }

@@ -114,8 +114,9 @@ sv_status sv_build_index(const int32_t *coords, const int32_t *frame_offsets,
  *   Y [n][C_out] written; all device, all in `dtype` except N.
  *   workspace: device, 16-byte aligned, at least
  *   sv_workspace_bytes(SV_OP_FWD, ...) bytes (0 unless the bf16 matrix-core
- *   kernel can run; it receives the weights repacked per tap as
- *   [tap][C_out][C_in]); contents are scratch.
+ *   kernels can run; it receives the weights repacked for them: as
+ *   [tap][C_out][C_in], or in MFMA fragment order when C_in is a multiple of
+ *   64 and C_out of 256); contents are scratch.
  * SV_ERR_UNSUPPORTED if `kernel` is MFMA and the shape/dtype does not fit it;
  * SV_ERR_WORKSPACE if the MFMA kernel runs and the workspace is short. */
 sv_status sv_sparseconv2d_fwd(const void *X, const int32_t *N, const void *Wt,
@@ -124,13 +125,24 @@ sv_status sv_sparseconv2d_fwd(const void *X, const int32_t *N, const void *Wt,
                               sv_kernel kernel, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
-/* Input gradient (the adjoint of the forward sum, written as gathers thanks
- * to the mirrored offsets: token m is tap j of k exactly when k is tap 8-j
- * of m):  dX[k][i] = sum_j sum_o dY[N[k,8-j]][o] Wt[j][i][o].
- *   dY [n][C_out], N [n][9], Wt [9][C_in][C_out], dX [n][C_in] written. */
+/* Key Design 2's dedicated backward kernels, input gradient.  The page
+ * prints no backward formula; this is the adjoint of the forward sum,
+ * written as gathers thanks to the mirrored offsets (token m is tap j of k
+ * exactly when k is tap 8-j of m):
+ *   dX[k][i] = sum_j sum_o dY[N[k,8-j]][o] Wt[j][i][o].
+ *   dY [n][C_out], N [n][9], Wt [9][C_in][C_out], dX [n][C_in] written.
+ *   workspace: device, nullable.  When the bf16 matrix-core path runs on a
+ *   shape whose weights it takes in fragment order (C_out a multiple of 64,
+ *   C_in of 256) and Wt is 16-byte aligned, a workspace of at least
+ *   sv_workspace_bytes(SV_OP_DX, ...) bytes (16-byte aligned) receives the
+ *   repacked weights and the faster kernel runs; without one the kernel that
+ *   reads Wt directly runs.  Both give the same bits.
+ * SV_ERR_UNSUPPORTED if `kernel` is MFMA and the shape/dtype does not fit it;
+ * SV_ERR_WORKSPACE if a workspace is given but is short. */
 sv_status sv_sparseconv2d_bwd_dx(const void *dY, const int32_t *N, const void *Wt,
                                  void *dX, int64_t n, int32_t C_in, int32_t C_out,
-                                 sv_dtype dtype, sv_kernel kernel, hipStream_t stream);
+                                 sv_dtype dtype, sv_kernel kernel, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* Weight (and bias) gradient, a split-K reduction over tokens:
  *   dW[j][i][o] (+)= sum_k X[N[k,j]][i] dY[k][o],   db[o] (+)= sum_k dY[k][o].
@@ -148,7 +160,8 @@ sv_status sv_sparseconv2d_bwd_dw(const void *X, const int32_t *N, const void *dY
                                  hipStream_t stream);
 
 /* Workspace bytes an operation needs for these sizes (FWD: the repacked
- * weights of the bf16 matrix-core kernel, else 0; DX: 0; DW: token-slice
+ * weights of the bf16 matrix-core kernels, else 0; DX: the fragment-order
+ * weights where the input gradient takes them, else 0; DW: token-slice
  * partials).  Depends only on its arguments, never on the device. */
 size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype);
 
@@ -179,7 +192,8 @@ sv_status sv_sparseconv2d_fwd_k(const void *X, const int32_t *N, const void *Wt,
                                 hipStream_t stream);
 sv_status sv_sparseconv2d_bwd_dx_k(const void *dY, const int32_t *N, const void *Wt,
                                    void *dX, int64_t n, int32_t K, int32_t C_in, int32_t C_out,
-                                   sv_dtype dtype, sv_kernel kernel, hipStream_t stream);
+                                   sv_dtype dtype, sv_kernel kernel, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 sv_status sv_sparseconv2d_bwd_dw_k(const void *X, const int32_t *N, const void *dY,
                                    float *dW, float *db, int64_t n, int32_t K, int32_t C_in,
                                    int32_t C_out, sv_dtype dtype, int32_t accumulate,
@@ -198,6 +212,12 @@ size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_
  *     on the MFMA kernel from that V (SV_ERR_UNSUPPORTED where the kernel does
  *     not fit).  Weights repacked once serve any number of forward calls and
  *     can be prepared on another stream ahead of them.
+ *   sv_repack_dx_k writes the input gradient's weights in MFMA fragment
+ *     order (bf16, 3 x 3, C_out a multiple of 64 and C_in of 256, else
+ *     SV_ERR_UNSUPPORTED; Wt and P 16-byte aligned, P at least
+ *     sv_workspace_bytes_k(SV_OP_DX, ...) bytes), and
+ *     sv_sparseconv2d_bwd_dx_packed_k runs the input gradient from that P;
+ *     the pair equals sv_sparseconv2d_bwd_dx_k bit for bit.
  *   sv_sparseconv2d_bwd_dw_partials_k then sv_sparseconv2d_bwd_dw_reduce_k,
  *     with the same arguments and workspace and in this order (the second
  *     may run on another stream once the first has finished), equal one
@@ -211,6 +231,11 @@ sv_status sv_sparseconv2d_fwd_packed_k(const void *X, const int32_t *N, const vo
                                        const void *bias, void *Y, int64_t n, int32_t K,
                                        int32_t C_in, int32_t C_out, sv_dtype dtype,
                                        hipStream_t stream);
+sv_status sv_repack_dx_k(const void *Wt, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                         void *P, size_t P_bytes, hipStream_t stream);
+sv_status sv_sparseconv2d_bwd_dx_packed_k(const void *dY, const int32_t *N, const void *P, void *dX,
+                                          int64_t n, int32_t K, int32_t C_in, int32_t C_out,
+                                          sv_dtype dtype, hipStream_t stream);
 sv_status sv_sparseconv2d_bwd_dw_partials_k(const void *X, const int32_t *N, const void *dY,
                                             float *dW, float *db, int64_t n, int32_t K,
                                             int32_t C_in, int32_t C_out, sv_dtype dtype,

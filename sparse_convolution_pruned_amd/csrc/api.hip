@@ -71,6 +71,13 @@ sv_status run_fwd_prepared(bool mfma, const void* X, const int32_t* N, const voi
                            const void* bias, void* Y, int64_t n, int32_t Ci, int32_t Co, int taps,
                            sv_dtype dt, hipStream_t s, const void* R = nullptr) {
     if (n == 0) return SV_OK;
+    if (mfma && conv_bfrag_ok(Ci, Co, taps)) {
+        // V holds the weights in fragment order (launch_repack_fwd)
+        if (R) return SV_ERR_UNSUPPORTED;
+        return hip_status(launch_conv_bfrag(static_cast<const uint16_t*>(X), N, static_cast<const uint16_t*>(V),
+                                            static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(Y), n, Ci, Co,
+                                            taps, s));
+    }
     if (mfma)
         return hip_status(launch_conv_mfma_packed(static_cast<const uint16_t*>(X), N,
                                                   static_cast<const uint16_t*>(V),
@@ -80,13 +87,20 @@ sv_status run_fwd_prepared(bool mfma, const void* X, const int32_t* N, const voi
     return hip_status(launch_conv_valu(dt == SV_BF16, false, X, N, Wt, bias, R, Y, n, Ci, Co, taps, s));
 }
 
-// Input gradient; R: nullable residual added to dX.
+// Input gradient; R: nullable residual added to dX.  P: nullable, the
+// weights in fragment order for the input gradient (launch_repack_frag with
+// dx = true), used when the fragment kernel takes the shape; without it the
+// MFMA path reads Wt directly.
 sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int64_t n, int32_t Ci,
-                 int32_t Co, int taps, sv_dtype dt, sv_kernel kernel, hipStream_t s, const void* R = nullptr) {
+                 int32_t Co, int taps, sv_dtype dt, sv_kernel kernel, hipStream_t s, const void* R = nullptr,
+                 const void* P = nullptr) {
     bool mfma = false;
     sv_status st = choose(kernel, dt, true, Ci, Co, n, taps, &mfma);
     if (st != SV_OK) return st;
     if (n == 0) return SV_OK;
+    if (mfma && P && !R && conv_bfrag_ok(Co, Ci, taps))
+        return hip_status(launch_conv_bfrag(static_cast<const uint16_t*>(dY), N, static_cast<const uint16_t*>(P),
+                                            nullptr, static_cast<uint16_t*>(dX), n, Co, Ci, taps, s));
     if (mfma)
         return hip_status(launch_conv_mfma_packed(static_cast<const uint16_t*>(dY), N,
                                                   static_cast<const uint16_t*>(Wt), nullptr,
@@ -99,9 +113,15 @@ sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int
 // paired launch (the forward from the repacked weights V, the input
 // gradient from Wt); the two problems' tiles fill the chip together.
 sv_status run_fwd_dx_pair(const void* X, const void* dY, const int32_t* N, const void* Wt, const void* V,
-                          const void* bias, void* Y, void* dX, int64_t n, int32_t Ci, int32_t Co, int taps,
-                          hipStream_t s) {
+                          const void* P, const void* bias, void* Y, void* dX, int64_t n, int32_t Ci, int32_t Co,
+                          int taps, hipStream_t s) {
     if (n == 0) return SV_OK;
+    if (conv_bfrag_ok(Ci, Co, taps) || conv_bfrag_ok(Co, Ci, taps)) {
+        // fragment-order weights: each pass runs on its own launch
+        sv_status st = run_fwd_prepared(true, X, N, Wt, V, bias, Y, n, Ci, Co, taps, SV_BF16, s);
+        if (st != SV_OK) return st;
+        return run_dx(dY, N, Wt, dX, n, Ci, Co, taps, SV_BF16, SV_KERNEL_MFMA, s, nullptr, P);
+    }
     return hip_status(launch_conv_mfma_pair(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(V),
                                             static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(Y), Ci, Co,
                                             static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(Wt),
@@ -112,6 +132,14 @@ sv_status run_fwd_dx_pair(const void* X, const void* dY, const int32_t* N, const
 size_t fwd_ws_bytes(int32_t Ci, int32_t Co, sv_dtype dt, int64_t n, int taps) {
     return (dt == SV_BF16 && conv_mfma_supported(false, Ci, Co, n, taps)) ? conv_mfma_fwd_workspace(Ci, Co, taps)
                                                                            : 0;
+}
+
+// Bytes of fragment-order weights the input gradient takes when the
+// fragment kernel can run it (same size as the forward's repack), else 0.
+size_t dx_ws_bytes(int32_t Ci, int32_t Co, sv_dtype dt, int64_t n, int taps) {
+    return (dt == SV_BF16 && conv_mfma_supported(true, Ci, Co, n, taps) && conv_bfrag_ok(Co, Ci, taps))
+               ? conv_mfma_fwd_workspace(Ci, Co, taps)
+               : 0;
 }
 
 }  // namespace
@@ -172,19 +200,34 @@ sv_status sv_sparseconv2d_fwd(const void* X, const int32_t* N, const void* Wt, c
 
 sv_status sv_sparseconv2d_bwd_dx_k(const void* dY, const int32_t* N, const void* Wt, void* dX, int64_t n,
                                    int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype, sv_kernel kernel,
-                                   hipStream_t stream) {
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int taps = 0;
     sv_status st = taps_of(K, &taps);
     if (st != SV_OK) return st;
     if ((st = conv_args_ok(n, taps, C_in, C_out, dtype, kernel)) != SV_OK) return st;
     if (!Wt || (n > 0 && (!dY || !N || !dX))) return SV_ERR_INVALID_ARG;
+    bool mfma = false;
+    if ((st = choose(kernel, dtype, true, C_in, C_out, n, taps, &mfma)) != SV_OK) return st;
+    const size_t need = dx_ws_bytes(C_in, C_out, dtype, n, taps);
+    // The repack reads Wt in 16-byte pieces; a Wt that is not 16-byte
+    // aligned takes the kernel that reads it directly.
+    if (mfma && need > 0 && workspace && reinterpret_cast<uintptr_t>(Wt) % 16 == 0) {
+        if (workspace_bytes < need) return SV_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return SV_ERR_INVALID_ARG;
+        if (n == 0) return SV_OK;
+        st = hip_status(launch_repack_frag(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(workspace),
+                                           C_in, C_out, taps, true, stream));
+        if (st != SV_OK) return st;
+        return run_dx(dY, N, Wt, dX, n, C_in, C_out, taps, dtype, kernel, stream, nullptr, workspace);
+    }
     return run_dx(dY, N, Wt, dX, n, C_in, C_out, taps, dtype, kernel, stream);
 }
 
 sv_status sv_sparseconv2d_bwd_dx(const void* dY, const int32_t* N, const void* Wt, void* dX,
                                  int64_t n, int32_t C_in, int32_t C_out, sv_dtype dtype,
-                                 sv_kernel kernel, hipStream_t stream) {
-    return sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, n, 3, C_in, C_out, dtype, kernel, stream);
+                                 sv_kernel kernel, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, n, 3, C_in, C_out, dtype, kernel, workspace, workspace_bytes,
+                                    stream);
 }
 
 size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype) {
@@ -192,6 +235,7 @@ size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_
     if (taps_of(K, &taps) != SV_OK) return 0;
     if (n < 0 || C_in <= 0 || C_out <= 0 || !valid_dtype(dtype)) return 0;
     if (op == SV_OP_FWD) return fwd_ws_bytes(C_in, C_out, dtype, n, taps);
+    if (op == SV_OP_DX) return dx_ws_bytes(C_in, C_out, dtype, n, taps);
     if (op != SV_OP_DW) return 0;
     return dw_workspace_bytes(plan_dw(n, C_in, C_out, dtype == SV_BF16, taps));
 }
@@ -253,6 +297,34 @@ sv_status sv_sparseconv2d_fwd_packed_k(const void* X, const int32_t* N, const vo
     return run_fwd_prepared(true, X, N, nullptr, V, bias, Y, n, C_in, C_out, taps, dtype, stream);
 }
 
+sv_status sv_repack_dx_k(const void* Wt, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype, void* P,
+                         size_t P_bytes, hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
+    if (st != SV_OK) return st;
+    if (C_in <= 0 || C_out <= 0 || !valid_dtype(dtype) || !Wt || !P) return SV_ERR_INVALID_ARG;
+    if (dtype != SV_BF16 || !conv_bfrag_ok(C_out, C_in, taps)) return SV_ERR_UNSUPPORTED;
+    if (P_bytes < conv_mfma_fwd_workspace(C_in, C_out, taps)) return SV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(P) % 16 || reinterpret_cast<uintptr_t>(Wt) % 16) return SV_ERR_INVALID_ARG;
+    return hip_status(launch_repack_frag(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(P), C_in, C_out,
+                                         taps, true, stream));
+}
+
+sv_status sv_sparseconv2d_bwd_dx_packed_k(const void* dY, const int32_t* N, const void* P, void* dX, int64_t n,
+                                          int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                          hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
+    if (st != SV_OK) return st;
+    if ((st = conv_args_ok(n, taps, C_in, C_out, dtype, SV_KERNEL_MFMA)) != SV_OK) return st;
+    if (!P || (n > 0 && (!dY || !N || !dX))) return SV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(P) % 16) return SV_ERR_INVALID_ARG;
+    if (dx_ws_bytes(C_in, C_out, dtype, n, taps) == 0) return SV_ERR_UNSUPPORTED;
+    if (n == 0) return SV_OK;
+    return hip_status(launch_conv_bfrag(static_cast<const uint16_t*>(dY), N, static_cast<const uint16_t*>(P),
+                                        nullptr, static_cast<uint16_t*>(dX), n, C_out, C_in, taps, stream));
+}
+
 namespace {
 
 // Shared checks of the two phases of the weight gradient.
@@ -303,7 +375,10 @@ struct ChunkLayout {
     size_t w_bytes = 0;       // forward weights repacked for the MFMA kernel
     size_t dw_bytes = 0;      // dW/db partials of the largest plan
     size_t n2_bytes = 0;      // second N table when dW runs on its own stream
+    size_t p_bytes = 0;       // input-gradient weights in fragment order
     size_t total = 0;
+    // the input-gradient weights sit after everything else
+    size_t p_off() const { return n_bytes + w_bytes + dw_bytes + n2_bytes; }
 };
 
 int ksize_of(int32_t ksize) { return ksize == 0 ? 3 : ksize; }
@@ -335,7 +410,10 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
     L->w_bytes = (passes & SV_PASS_FWD) ? fwd_ws_bytes(d->C_in, d->C_out, d->dtype, L->max_tokens, L->taps) : 0;
     const bool split = d->dw_stream && (passes & SV_PASS_DW) && (passes & (SV_PASS_FWD | SV_PASS_DX));
     L->n2_bytes = split ? L->n_bytes : 0;
-    L->total = L->n_bytes + L->w_bytes + L->dw_bytes + L->n2_bytes;
+    L->p_bytes = ((passes & SV_PASS_DX) && d->kernel != SV_KERNEL_VALU)
+                     ? dx_ws_bytes(d->C_in, d->C_out, d->dtype, L->max_tokens, L->taps)
+                     : 0;
+    L->total = L->n_bytes + L->w_bytes + L->dw_bytes + L->n2_bytes + L->p_bytes;
     return true;
 }
 
@@ -395,6 +473,15 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     void* dws = static_cast<char*>(workspace) + L.n_bytes + L.w_bytes;
     bool fwd_mfma = false, dx_mfma = false;
     if (passes & SV_PASS_DX) choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.max_tokens, L.taps, &dx_mfma);
+    void* Pw = (dx_mfma && L.p_bytes > 0 && reinterpret_cast<uintptr_t>(d->Wt) % 16 == 0)
+                   ? static_cast<char*>(workspace) + L.p_off()
+                   : nullptr;
+    if (Pw && d->T > 0) {
+        // the input gradient's weights, in fragment order, once for every chunk
+        sv_status st = hip_status(launch_repack_frag(static_cast<const uint16_t*>(d->Wt), static_cast<uint16_t*>(Pw),
+                                                     d->C_in, d->C_out, L.taps, true, stream));
+        if (st != SV_OK) return st;
+    }
     if (passes & SV_PASS_FWD) {
         choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.max_tokens, L.taps, &fwd_mfma);
         if (fwd_mfma && d->T > 0) {
@@ -439,7 +526,7 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
         char* Yc = (passes & SV_PASS_FWD) ? static_cast<char*>(d->Y) + t0 * d->C_out * es : nullptr;
         char* dXc = (passes & SV_PASS_DX) ? static_cast<char*>(d->dX) + t0 * d->C_in * es : nullptr;
         if (fwd_mfma && dx_mfma) {
-            st = run_fwd_dx_pair(X, dY, Nc, d->Wt, Vw, d->bias, Yc, dXc, nc, d->C_in, d->C_out, L.taps, stream);
+            st = run_fwd_dx_pair(X, dY, Nc, d->Wt, Vw, Pw, d->bias, Yc, dXc, nc, d->C_in, d->C_out, L.taps, stream);
             if (st != SV_OK) return st;
         } else {
             if (passes & SV_PASS_FWD) {
@@ -448,7 +535,8 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
                 if (st != SV_OK) return st;
             }
             if (passes & SV_PASS_DX) {
-                st = run_dx(dY, Nc, d->Wt, dXc, nc, d->C_in, d->C_out, L.taps, d->dtype, d->kernel, stream);
+                st = run_dx(dY, Nc, d->Wt, dXc, nc, d->C_in, d->C_out, L.taps, d->dtype, d->kernel, stream, nullptr,
+                            Pw);
                 if (st != SV_OK) return st;
             }
         }
@@ -599,6 +687,14 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
 
     bool fwd_mfma = false, dx_mfma = false;
     if (passes & SV_PASS_DX) choose(d->kernel, d->dtype, true, d->C_in, d->C_out, L.dev.max_tokens, taps, &dx_mfma);
+    void* Pw = (dx_mfma && L.dev.p_bytes > 0 && reinterpret_cast<uintptr_t>(d->Wt) % 16 == 0)
+                   ? base + L.dev.p_off()
+                   : nullptr;
+    if (Pw && d->T > 0) {
+        sv_status st0 = hip_status(launch_repack_frag(static_cast<const uint16_t*>(d->Wt), static_cast<uint16_t*>(Pw),
+                                                      d->C_in, d->C_out, taps, true, compute));
+        if (st0 != SV_OK) return st0;
+    }
     if (passes & SV_PASS_FWD) {
         choose(d->kernel, d->dtype, false, d->C_in, d->C_out, L.dev.max_tokens, taps, &fwd_mfma);
         if (fwd_mfma && d->T > 0) {
@@ -681,8 +777,8 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
                                                          t0, Nc, nullptr, d->err_flag, compute));
             if (s2 != SV_OK) return s2;
             if (fwd_mfma && dx_mfma) {
-                s2 = run_fwd_dx_pair(st[b].X, st[b].dY, Nc, d->Wt, Vw, d->bias, st[b].Y, st[b].dX, nc, d->C_in,
-                                     d->C_out, taps, compute);
+                s2 = run_fwd_dx_pair(st[b].X, st[b].dY, Nc, d->Wt, Vw, Pw, d->bias, st[b].Y, st[b].dX, nc,
+                                     d->C_in, d->C_out, taps, compute);
                 if (s2 != SV_OK) return s2;
             } else {
                 if (passes & SV_PASS_FWD) {
@@ -692,7 +788,7 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
                 }
                 if (passes & SV_PASS_DX) {
                     s2 = run_dx(st[b].dY, Nc, d->Wt, st[b].dX, nc, d->C_in, d->C_out, taps, d->dtype, d->kernel,
-                                compute);
+                                compute, nullptr, Pw);
                     if (s2 != SV_OK) return s2;
                 }
             }

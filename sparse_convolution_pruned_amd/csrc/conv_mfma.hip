@@ -457,6 +457,8 @@ size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps) {
 }
 
 hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream) {
+    // shapes the fragment-order kernel takes get its layout (same size)
+    if (conv_bfrag_ok(Ci, Co, taps)) return launch_repack_frag(Wt, V, Ci, Co, taps, false, stream);
     dim3 grid((Co + 31) / 32, (Ci + 31) / 32, taps);
     hipLaunchKernelGGL(k_repack_fwd, grid, dim3(256), 0, stream, Wt, V, Ci, Co);
     return hipGetLastError();

@@ -15,13 +15,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest, ties to even; NaN stays NaN (quiet bit set).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
+// Round to nearest, ties to even; NaN stays NaN (quiet bit set).  This is
+// gfx950's conversion instruction (v_cvt_pk_bf16_f32), which produces exactly
+// those bits -- (u + 0x7fff + ((u >> 16) & 1)) >> 16 for a non-NaN pattern u,
+// (u >> 16) | 0x40 for a NaN -- for every one of the 2^32 fp32 inputs
+// (compared on the GPU).  One instruction, where the bit arithmetic took ten
+// and a per-value branch for the NaN test took more: an epilogue rounds 128
+// values per lane.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -110,6 +111,17 @@ hipError_t launch_conv_mfma_pair(const uint16_t* A1, const uint16_t* B1, const u
                                  int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
                                  int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream);
 hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream);
+// Weight operand in fragment order (conv_bfrag.hip): the MFMA kernel that
+// streams B from memory into registers.  conv_bfrag_ok: the shapes it is
+// built for (3 x 3, contracted channels a multiple of 64, produced channels
+// a multiple of 256).  The repack writes taps * Ci * Co bf16 in fragment
+// order for the forward (dx = false: K = Ci, NO = Co) or the input gradient
+// (dx = true: K = Co, NO = Ci, taps mirrored).
+bool conv_bfrag_ok(int K, int NO, int taps);
+hipError_t launch_repack_frag(const uint16_t* Wt, uint16_t* Bf, int Ci, int Co, int taps, bool dx,
+                              hipStream_t stream);
+hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t* Bf, const uint16_t* bias,
+                             uint16_t* out, int64_t n, int K, int NO, int taps, hipStream_t stream);
 size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps);
 // bf16, a tap count the kernel is built for, contracted channels a multiple
 // of 32, output channels of 16, and the n rows of A and of the output within

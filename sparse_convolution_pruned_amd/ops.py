@@ -42,7 +42,8 @@ SYMBOLS = (
     "sv_sparseconv2d_bwd_dw", "sv_workspace_bytes",
     "sv_build_index_k", "sv_sparseconv2d_fwd_k", "sv_sparseconv2d_bwd_dx_k",
     "sv_sparseconv2d_bwd_dw_k", "sv_workspace_bytes_k",
-    "sv_repack_fwd_k", "sv_sparseconv2d_fwd_packed_k", "sv_sparseconv2d_bwd_dw_partials_k",
+    "sv_repack_fwd_k", "sv_sparseconv2d_fwd_packed_k", "sv_repack_dx_k", "sv_sparseconv2d_bwd_dx_packed_k",
+    "sv_sparseconv2d_bwd_dw_partials_k",
     "sv_sparseconv2d_bwd_dw_reduce_k", "sv_sparseconv2d_chunked",
     "sv_chunked_workspace_bytes", "sv_sparseconv2d_chunked_host", "sv_chunked_host_workspace_bytes",
     "sv_adapter_fwd", "sv_adapter_bwd", "sv_adapter_workspace_bytes",
@@ -106,16 +107,18 @@ def load(path: str = LIB_PATH):
     sig = {
         "sv_build_index": ([P, P, i32, i32, i32, i64, P, P, P, P], E),
         "sv_sparseconv2d_fwd": ([P, P, P, P, P, i64, i32, i32, E, E, P, sz, P], E),
-        "sv_sparseconv2d_bwd_dx": ([P, P, P, P, i64, i32, i32, E, E, P], E),
+        "sv_sparseconv2d_bwd_dx": ([P, P, P, P, i64, i32, i32, E, E, P, sz, P], E),
         "sv_sparseconv2d_bwd_dw": ([P, P, P, P, P, i64, i32, i32, E, i32, P, sz, P], E),
         "sv_workspace_bytes": ([E, i64, i32, i32, E], sz),
         "sv_build_index_k": ([P, P, i32, i32, i32, i32, i64, P, P, P, P], E),
         "sv_sparseconv2d_fwd_k": ([P, P, P, P, P, i64, i32, i32, i32, E, E, P, sz, P], E),
-        "sv_sparseconv2d_bwd_dx_k": ([P, P, P, P, i64, i32, i32, i32, E, E, P], E),
+        "sv_sparseconv2d_bwd_dx_k": ([P, P, P, P, i64, i32, i32, i32, E, E, P, sz, P], E),
         "sv_sparseconv2d_bwd_dw_k": ([P, P, P, P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
         "sv_workspace_bytes_k": ([E, i64, i32, i32, i32, E], sz),
         "sv_repack_fwd_k": ([P, i32, i32, i32, E, P, sz, P], E),
         "sv_sparseconv2d_fwd_packed_k": ([P, P, P, P, P, i64, i32, i32, i32, E, P], E),
+        "sv_repack_dx_k": ([P, i32, i32, i32, E, P, sz, P], E),
+        "sv_sparseconv2d_bwd_dx_packed_k": ([P, P, P, P, i64, i32, i32, i32, E, P], E),
         "sv_sparseconv2d_bwd_dw_partials_k": ([P, P, P, P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
         "sv_sparseconv2d_bwd_dw_reduce_k": ([P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
         "sv_sparseconv2d_chunked": ([ctypes.POINTER(ChunkedDesc), ctypes.c_uint32, P, sz, P], E),
@@ -213,13 +216,25 @@ def sv_sparseconv2d_fwd(X, N, Wt, bias, Y, kernel="auto", workspace=None, stream
     _check(st, "sv_sparseconv2d_fwd")
 
 
-def sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, kernel="auto", stream=None):
+def _dx_workspace(workspace, need, device):
+    """The input gradient's workspace: allocated when omitted (None), none
+    at all for workspace=0 (the kernel that reads Wt directly runs)."""
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+    if isinstance(workspace, int) and workspace == 0:
+        return None
+    return workspace
+
+
+def sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, kernel="auto", workspace=None, stream=None):
     n, Co = dY.shape
     Ci = Wt.shape[1]
     assert Wt.shape == (9, Ci, Co) and dX.shape == (n, Ci) and N.shape == (n, 9)
     assert dY.dtype == Wt.dtype == dX.dtype and N.dtype == torch.int32
+    workspace = _dx_workspace(workspace, sv_workspace_bytes(SV_OP_DX, n, Ci, Co, dY.dtype), dY.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().sv_sparseconv2d_bwd_dx(_ptr(dY), _ptr(N), _ptr(Wt), _ptr(dX), n, Ci, Co,
-                                       _dt(dY), _kernel(kernel), _stream(stream))
+                                       _dt(dY), _kernel(kernel), _ptr(workspace), wsb, _stream(stream))
     _check(st, "sv_sparseconv2d_bwd_dx")
 
 
@@ -289,14 +304,16 @@ def sv_sparseconv2d_fwd_k(X, N, Wt, bias, Y, kernel="auto", workspace=None, stre
     _check(st, "sv_sparseconv2d_fwd_k")
 
 
-def sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, kernel="auto", stream=None):
+def sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, kernel="auto", workspace=None, stream=None):
     n, Co = dY.shape
     taps, Ci = Wt.shape[0], Wt.shape[1]
     K = ksize_of_taps(taps)
     assert Wt.shape == (taps, Ci, Co) and dX.shape == (n, Ci) and N.shape == (n, taps)
     assert dY.dtype == Wt.dtype == dX.dtype and N.dtype == torch.int32
+    workspace = _dx_workspace(workspace, sv_workspace_bytes_k(SV_OP_DX, n, K, Ci, Co, dY.dtype), dY.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().sv_sparseconv2d_bwd_dx_k(_ptr(dY), _ptr(N), _ptr(Wt), _ptr(dX), n, K, Ci, Co,
-                                         _dt(dY), _kernel(kernel), _stream(stream))
+                                         _dt(dY), _kernel(kernel), _ptr(workspace), wsb, _stream(stream))
     _check(st, "sv_sparseconv2d_bwd_dx_k")
 
 
@@ -335,6 +352,22 @@ def sv_sparseconv2d_fwd_packed_k(X, N, V, bias, Y, K, stream=None):
     st = load().sv_sparseconv2d_fwd_packed_k(_ptr(X), _ptr(N), _ptr(V), _ptr(bias), _ptr(Y), n, K, Ci, Co, _dt(X),
                                              _stream(stream))
     _check(st, "sv_sparseconv2d_fwd_packed_k")
+
+
+def sv_repack_dx_k(Wt, P, stream=None):
+    taps, Ci, Co = Wt.shape
+    wsb = P.numel() * P.element_size()
+    st = load().sv_repack_dx_k(_ptr(Wt), ksize_of_taps(taps), Ci, Co, _dt(Wt), _ptr(P), wsb, _stream(stream))
+    _check(st, "sv_repack_dx_k")
+
+
+def sv_sparseconv2d_bwd_dx_packed_k(dY, N, P, dX, K, stream=None):
+    n, Co = dY.shape
+    Ci = dX.shape[1]
+    assert N.shape == (n, K * K) and dX.shape[0] == n and dY.dtype == dX.dtype and N.dtype == torch.int32
+    st = load().sv_sparseconv2d_bwd_dx_packed_k(_ptr(dY), _ptr(N), _ptr(P), _ptr(dX), n, K, Ci, Co, _dt(dY),
+                                                _stream(stream))
+    _check(st, "sv_sparseconv2d_bwd_dx_packed_k")
 
 
 def sv_sparseconv2d_bwd_dw_partials_k(X, N, dY, dW, db, workspace, accumulate=False, stream=None):

@@ -56,11 +56,11 @@ def test_validation_without_device(lib):
     assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 4, 4, F32, 9, None, 0, None) == ops.SV_ERR_INVALID_ARG
     # null required pointers
     assert lib.sv_sparseconv2d_fwd(None, FAKE, FAKE, None, FAKE, 8, 4, 4, F32, 0, None, 0, None) == ops.SV_ERR_INVALID_ARG
-    assert lib.sv_sparseconv2d_bwd_dx(FAKE, None, FAKE, FAKE, 8, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_bwd_dx(FAKE, None, FAKE, FAKE, 8, 4, 4, F32, 0, None, 0, None) == ops.SV_ERR_INVALID_ARG
     # MFMA forced where it does not fit: fp32, or channels not multiples of 32/16
     assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 64, F32, 2, None, 0, None) == ops.SV_ERR_UNSUPPORTED
     assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 48, 64, BF16, 2, None, 0, None) == ops.SV_ERR_UNSUPPORTED
-    assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, 8, 64, 40, BF16, 2, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, 8, 64, 40, BF16, 2, None, 0, None) == ops.SV_ERR_UNSUPPORTED
     # forward on the matrix cores without its weight workspace
     assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 64, BF16, 0, None, 0, None) == ops.SV_ERR_WORKSPACE
     assert lib.sv_workspace_bytes(ops.SV_OP_FWD, 8, 64, 64, BF16) >= 9 * 64 * 64 * 2
@@ -225,7 +225,7 @@ def test_kxk_validation_and_workspace(lib):
                     (9, ops.SV_ERR_UNSUPPORTED)]:
         assert lib.sv_build_index_k(FAKE, FAKE, 1, 4, 4, K, 1, FAKE, None, None, None) == want
         assert lib.sv_sparseconv2d_fwd_k(FAKE, FAKE, FAKE, None, FAKE, 8, K, 4, 4, F32, 0, None, 0, None) == want
-        assert lib.sv_sparseconv2d_bwd_dx_k(FAKE, FAKE, FAKE, FAKE, 8, K, 4, 4, F32, 0, None) == want
+        assert lib.sv_sparseconv2d_bwd_dx_k(FAKE, FAKE, FAKE, FAKE, 8, K, 4, 4, F32, 0, None, 0, None) == want
         assert lib.sv_sparseconv2d_bwd_dw_k(FAKE, FAKE, FAKE, FAKE, None, 8, K, 4, 4, F32, 0, None, 0,
                                             None) == want
         assert lib.sv_workspace_bytes_k(ops.SV_OP_FWD, 8, K, 64, 64, BF16) == 0
@@ -299,6 +299,25 @@ def test_split_forms_validation(lib):
     assert lib.sv_sparseconv2d_fwd_packed_k(FAKE, FAKE, FAKE, None, FAKE, 8, 3, 64, 64, F32, None) == \
         ops.SV_ERR_UNSUPPORTED
     assert lib.sv_sparseconv2d_fwd_packed_k(FAKE, FAKE, None, None, FAKE, 8, 3, 64, 64, BF16, None) == \
+        ops.SV_ERR_INVALID_ARG
+    # input gradient in fragment order: bf16 3 x 3 with C_out % 64 == 0 and C_in % 256 == 0
+    xneed = lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 256, 256, BF16)
+    assert xneed == 9 * 256 * 256 * 2
+    assert lib.sv_workspace_bytes(ops.SV_OP_DX, 22656, 256, 256, BF16) == xneed
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 128, 128, BF16) == 0
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 256, 256, F32) == 0
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 5, 256, 256, BF16) == 0
+    assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, 22656, 256, 256, BF16, 0, FAKE, xneed - 1,
+                                      None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_repack_dx_k(FAKE, 3, 256, 256, BF16, FAKE, xneed - 1, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_repack_dx_k(FAKE, 3, 128, 128, BF16, FAKE, xneed, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_repack_dx_k(FAKE, 3, 256, 256, F32, FAKE, xneed, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_repack_dx_k(None, 3, 256, 256, BF16, FAKE, xneed, None) == ops.SV_ERR_INVALID_ARG
+    assert lib.sv_repack_dx_k(FAKE, 3, 256, 256, BF16, ctypes.c_void_p(4104), xneed, None) == \
+        ops.SV_ERR_INVALID_ARG
+    assert lib.sv_sparseconv2d_bwd_dx_packed_k(FAKE, FAKE, FAKE, FAKE, 8, 3, 128, 128, BF16, None) == \
+        ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_bwd_dx_packed_k(FAKE, FAKE, None, FAKE, 8, 3, 256, 256, BF16, None) == \
         ops.SV_ERR_INVALID_ARG
     dneed = lib.sv_workspace_bytes_k(ops.SV_OP_DW, 22656, 3, 256, 256, BF16)
     assert lib.sv_sparseconv2d_bwd_dw_partials_k(FAKE, FAKE, FAKE, FAKE, None, 22656, 3, 256, 256, BF16, 0, FAKE,

@@ -1,0 +1,142 @@
+"""The matrix-core kernel that streams the weights in fragment order
+(bf16, 3 x 3, contracted channels a multiple of 64, produced channels a
+multiple of 256): forward and input gradient against the oracle in every
+staging mode and tile height, and bit for bit against the kernel that reads
+Wt directly (the input gradient without a workspace).  The split forms
+(repack, then the packed call) must equal the single calls bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_convolution_pruned_amd import ops, workloads as wl
+from tests.gpu_util import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+bf = torch.bfloat16
+
+
+def dx_both(dY, Nd, Wt):
+    """Input gradient with a workspace (fragment-order kernel) and without
+    (the kernel that reads Wt directly)."""
+    n, Ci = dY.shape[0], Wt.shape[1]
+    a = torch.empty((n, Ci), dtype=bf, device="cuda")
+    b = torch.empty((n, Ci), dtype=bf, device="cuda")
+    ops.sv_sparseconv2d_bwd_dx(dY, Nd, Wt, a, "mfma")
+    ops.sv_sparseconv2d_bwd_dx(dY, Nd, Wt, b, "mfma", workspace=0)
+    torch.cuda.synchronize()
+    return a, b
+
+
+def check_case(L, N, what):
+    X, Wt, b, dY = dev(L.X, bf), dev(L.Wt, bf), dev(L.b, bf), dev(L.dY, bf)
+    Nd = dev(N)
+    Y = ops.sparseconv2d_fwd(X, Nd, Wt, b, "mfma")
+    dXf, dXd = dx_both(dY, Nd, Wt)
+    assert torch.equal(dXf.view(torch.int16), dXd.view(torch.int16)), f"{what}: fragment and direct dX differ"
+    assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), "bf16", f"{what} Y")
+    assert_close(host(dXf), O.bwd_dx(L.dY, N, L.Wt), "bf16", f"{what} dX")
+
+
+# (seed, T, H, W, keep, Ci, Co, shuffle); Co % 256 == 0 puts the forward on
+# the fragment kernel, Ci % 256 == 0 the input gradient.
+CASES = [
+    (31, 3, 16, 16, 0.6, 256, 256, False),              # window mode, ragged last tile, MB = 2
+    (32, 4, 16, 16, 0.5, 256, 256, True),               # shuffled packing: gather mode tap by tap
+    (33, 2, 40, 40, 0.5, 256, 256, False),              # grid 40 wide: tiles outside the window
+    (34, 5, 14, 14, [0, 1, 196, 0, 60], 512, 256, False),  # empty frames; C_in 512 (8 chunks)
+    (35, 3, 16, 16, 0.4, 256, 512, False),              # two output-channel tiles
+    (36, 2, 14, 14, 0.7, 64, 256, False),               # one 64-channel chunk in the forward
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c[0]}")
+def test_fragment_kernel(case):
+    seed, T, H, W, keep, Ci, Co, sh = case
+    L = wl.make_random_case(seed, T, H, W, keep, Ci, Co, "bf16", shuffle=sh)
+    print(f"case {case} n={L.n}", flush=True)
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, T, H, W)
+    check_case(L, N, f"{case}")
+
+
+@pytest.mark.parametrize("n_frames,keep,mb", [(200, 200, 3), (230, 230, 4), (120, 170, 2)])
+def test_tile_heights(n_frames, keep, mb):
+    """Token counts that select 128-, 192- and 256-token tiles (the
+    smallest tile whose grid fits one round of 256 workgroups)."""
+    L = wl.make_random_case(40 + mb, n_frames, 16, 16, [keep] * n_frames, 256, 256, "bf16")
+    n = L.n
+    lim = {2: (0, 256 * 128), 3: (256 * 128, 256 * 192), 4: (256 * 192, 10 ** 9)}[mb]
+    assert lim[0] < n <= lim[1], n
+    print(f"n={n} frames={n_frames} MB={mb}", flush=True)
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    check_case(L, N, f"MB={mb}")
+
+
+def test_random_table_and_out_of_range():
+    """Any N works: a random table with -1 entries and entries outside
+    [0, n) (read as padding) puts every tile in gather mode."""
+    L = wl.make_random_case(51, 2, 16, 16, 0.8, 256, 256, "bf16")
+    rng = np.random.default_rng(5)
+    n = L.n
+    N = rng.integers(-1, n, size=(n, 9)).astype(np.int32)
+    N[rng.random((n, 9)) < 0.05] = n + 3
+    N[rng.random((n, 9)) < 0.05] = -7
+    Nclean = np.where((N >= 0) & (N < n), N, -1).astype(np.int32)
+    X, Wt, b, dY = dev(L.X, bf), dev(L.Wt, bf), dev(L.b, bf), dev(L.dY, bf)
+    Nd = dev(N)
+    Y = ops.sparseconv2d_fwd(X, Nd, Wt, b, "mfma")
+    dXf, dXd = dx_both(dY, Nd, Wt)
+    assert torch.equal(dXf.view(torch.int16), dXd.view(torch.int16))
+    assert_close(host(Y), O.fwd(L.X, Nclean, L.Wt, L.b), "bf16", "random N Y")
+    assert_close(host(dXf), O.bwd_dx(L.dY, Nclean, L.Wt), "bf16", "random N dX")
+
+
+def test_split_forms_bitwise():
+    """Repack once, then the packed calls: equal to the single calls."""
+    L = wl.make_random_case(52, 6, 16, 16, 0.55, 256, 256, "bf16")
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    X, Wt, b, dY = dev(L.X, bf), dev(L.Wt, bf), dev(L.b, bf), dev(L.dY, bf)
+    Nd = dev(N)
+    n = L.n
+    V = torch.empty(ops.sv_workspace_bytes(ops.SV_OP_FWD, n, 256, 256, bf), dtype=torch.uint8, device="cuda")
+    P = torch.empty(ops.sv_workspace_bytes(ops.SV_OP_DX, n, 256, 256, bf), dtype=torch.uint8, device="cuda")
+    ops.sv_repack_fwd_k(Wt, V)
+    ops.sv_repack_dx_k(Wt, P)
+    Y1 = torch.empty((n, 256), dtype=bf, device="cuda")
+    dX1 = torch.empty((n, 256), dtype=bf, device="cuda")
+    ops.sv_sparseconv2d_fwd_packed_k(X, Nd, V, b, Y1, 3)
+    ops.sv_sparseconv2d_bwd_dx_packed_k(dY, Nd, P, dX1, 3)
+    Y2 = ops.sparseconv2d_fwd(X, Nd, Wt, b, "mfma")
+    dX2 = ops.sparseconv2d_bwd_dx(dY, Nd, Wt, "mfma")
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    assert torch.equal(dX1.view(torch.int16), dX2.view(torch.int16))
+    assert_close(host(dX1), O.bwd_dx(L.dY, N, L.Wt), "bf16", "packed dX")
+
+
+def test_chunk_driver_c256_bitwise():
+    """The chunk driver at C = 256 (forward and input gradient on the
+    fragment kernel from weights repacked once per call) gives the
+    unchunked calls' Y and dX bit for bit."""
+    L = wl.make_random_case(53, 12, 16, 16, 0.5, 256, 256, "bf16")
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    X, Wt, b, dY = dev(L.X, bf), dev(L.Wt, bf), dev(L.b, bf), dev(L.dY, bf)
+    n = L.n
+    Y = torch.empty((n, 256), dtype=bf, device="cuda")
+    dX = torch.empty((n, 256), dtype=bf, device="cuda")
+    dW = torch.empty((9, 256, 256), dtype=torch.float32, device="cuda")
+    db = torch.empty((256,), dtype=torch.float32, device="cuda")
+    desc = ops.make_chunked_desc(L.T, L.H, L.W, dev(L.coords), dev(L.frame_offsets),
+                                 torch.from_numpy(L.frame_offsets.copy()), 256, 256, bf, 5, X=X, Wt=Wt, bias=b,
+                                 Y=Y, dY=dY, dX=dX, dW=dW, db=db)
+    pm = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
+    ws = torch.empty(max(256, ops.sv_chunked_workspace_bytes(desc, pm)), dtype=torch.uint8, device="cuda")
+    ops.sv_sparseconv2d_chunked(desc, pm, ws)
+    Nd = dev(N)
+    Yr = ops.sparseconv2d_fwd(X, Nd, Wt, b, "mfma")
+    dXr = ops.sparseconv2d_bwd_dx(dY, Nd, Wt, "mfma")
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yr.view(torch.int16))
+    assert torch.equal(dX.view(torch.int16), dXr.view(torch.int16))
+    assert_close(host(dW), O.bwd_dw(L.X, N, L.dY), "bf16", "chunked dW")
