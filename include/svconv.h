@@ -231,6 +231,30 @@ sv_status sv_sparseconv2d_fwd_packed_k(const void *X, const int32_t *N, const vo
                                        const void *bias, void *Y, int64_t n, int32_t K,
                                        int32_t C_in, int32_t C_out, sv_dtype dtype,
                                        hipStream_t stream);
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the weight
+ * gradient of sv_sparseconv2d_bwd_dw_k with its token-slice partials kept in
+ * a device array of the library instead of a caller workspace.  Same
+ * arguments as sv_sparseconv2d_bwd_dw_k minus the workspace, same plan,
+ * kernels and summation order, so the same bits.
+ *   The array holds SV_NOALLOC_SCRATCH_BYTES bytes on every GPU the library
+ *   runs on, from module load until the process ends; it is found (with
+ *   hipGetSymbolAddress) on the first call on each device, which must be the
+ *   current device of the calling thread and the device of `stream`.
+ *   Shapes whose partials exceed it (sv_workspace_bytes_k(SV_OP_DW, ...) >
+ *   SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_WORKSPACE.
+ *   All calls on one GPU share that GPU's array and it keeps the last call's
+ *   contents (nothing in it needs to start at zero): calls that may overlap
+ *   on one GPU -- on different streams, or from different threads without
+ *   ordering -- race, and must be ordered by the caller.
+ * Allocates nothing and never synchronises; SV_ERR_HIP if the device or the
+ * array cannot be found. */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sv_status sv_sparseconv2d_bwd_dw_noalloc_k(const void *X, const int32_t *N, const void *dY,
+                                           float *dW, float *db, int64_t n, int32_t K,
+                                           int32_t C_in, int32_t C_out, sv_dtype dtype,
+                                           int32_t accumulate, hipStream_t stream);
+
 sv_status sv_repack_dx_k(const void *Wt, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
                          void *P, size_t P_bytes, hipStream_t stream);
 sv_status sv_sparseconv2d_bwd_dx_packed_k(const void *dY, const int32_t *N, const void *P, void *dX,

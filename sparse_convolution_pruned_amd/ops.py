@@ -49,7 +49,9 @@ SYMBOLS = (
     "sv_adapter_fwd", "sv_adapter_bwd", "sv_adapter_workspace_bytes",
     "sv_stage_gather", "sv_stage_scatter", "sv_status_string", "sv_version",
     "sv_xattn_fwd", "sv_xattn_bwd", "sv_xattn_workspace_bytes",
+    "sv_sparseconv2d_bwd_dw_noalloc_k",
 )
+SV_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SvError(RuntimeError):
@@ -133,6 +135,7 @@ def load(path: str = LIB_PATH):
         "sv_adapter_fwd": ([P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, E, E, P, sz, P], E),
         "sv_adapter_bwd": ([P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, E, E, P, sz, P, P], E),
         "sv_adapter_workspace_bytes": ([i32, i64, i32, i32, i32, E], sz),
+        "sv_sparseconv2d_bwd_dw_noalloc_k": ([P, P, P, P, P, i64, i32, i32, i32, E, i32, P], E),
         "sv_status_string": ([E], ctypes.c_char_p),
         "sv_version": ([], ctypes.c_char_p),
     }
@@ -352,6 +355,22 @@ def sv_sparseconv2d_fwd_packed_k(X, N, V, bias, Y, K, stream=None):
     st = load().sv_sparseconv2d_fwd_packed_k(_ptr(X), _ptr(N), _ptr(V), _ptr(bias), _ptr(Y), n, K, Ci, Co, _dt(X),
                                              _stream(stream))
     _check(st, "sv_sparseconv2d_fwd_packed_k")
+
+
+def sv_sparseconv2d_bwd_dw_noalloc_k(X, N, dY, dW, db=None, accumulate=False, stream=None):
+    """The weight gradient with its partials in the library's device array
+    (no workspace argument, nothing allocated)."""
+    n, Ci = X.shape
+    Co = dY.shape[1]
+    taps = dW.shape[0]
+    K = ksize_of_taps(taps)
+    assert dY.shape[0] == n and N.shape == (n, taps) and dW.shape == (taps, Ci, Co)
+    assert dW.dtype == torch.float32 and X.dtype == dY.dtype
+    if db is not None:
+        assert db.dtype == torch.float32 and db.shape == (Co,)
+    st = load().sv_sparseconv2d_bwd_dw_noalloc_k(_ptr(X), _ptr(N), _ptr(dY), _ptr(dW), _ptr(db), n, K, Ci, Co,
+                                                 _dt(X), 1 if accumulate else 0, _stream(stream))
+    _check(st, "sv_sparseconv2d_bwd_dw_noalloc_k")
 
 
 def sv_repack_dx_k(Wt, P, stream=None):

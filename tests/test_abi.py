@@ -286,6 +286,22 @@ def test_adapter_validation_and_workspace(lib):
     assert lib.sv_adapter_bwd(*nodw, BF16, 0, FAKE, 1 << 30, None, None) == ops.SV_ERR_INVALID_ARG
 
 
+def test_noalloc_validation(lib):
+    """The allocation-free weight gradient checks its arguments and the
+    size of its partials before it touches a device."""
+    F32, BF16 = ops.SV_F32, ops.SV_BF16
+    f = lib.sv_sparseconv2d_bwd_dw_noalloc_k
+    assert f(FAKE, FAKE, FAKE, FAKE, None, -1, 3, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 8, 4, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 8, 9, 4, 4, F32, 0, None) == ops.SV_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, None, None, 8, 3, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert f(FAKE, None, FAKE, FAKE, None, 8, 3, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 8, 3, 4, 4, 7, 0, None) == ops.SV_ERR_INVALID_ARG
+    big = 2_000_000
+    assert lib.sv_workspace_bytes(ops.SV_OP_DW, big, 512, 512, BF16) > ops.SV_NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, FAKE, FAKE, FAKE, None, big, 3, 512, 512, BF16, 0, None) == ops.SV_ERR_WORKSPACE
+
+
 def test_split_forms_validation(lib):
     F32, BF16 = ops.SV_F32, ops.SV_BF16
     need = lib.sv_workspace_bytes_k(ops.SV_OP_FWD, 8, 3, 64, 64, BF16)
