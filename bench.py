@@ -163,11 +163,9 @@ class StagedRun:
             ops.sv_build_index(self.coords[s], self.offs[s], S.T, S.H, S.W, self.N[s], None, self.flag)
             rec("index", t, units=self.ns[s])
         if packed:
-            # every layer's weights, repacked for the forward and the input gradient
+            # every layer's weights, repacked for the forward and the input gradient in one launch
             t = rec("repack", None)
-            for l in range(self.L):
-                ops.sv_repack_fwd_k(self.W[l], self.V[l])
-                ops.sv_repack_dx_k(self.W[l], self.P[l])
+            ops.sv_repack_layers_k(self.W, self.V, self.P)
             rec("repack", t, units=self.L)
         for l in range(self.L):
             s = self.stage_of[l]
@@ -243,27 +241,25 @@ class StagedRun:
             call("sv_build_index", P(self.coords[s]), P(self.offs[s]), S.T, S.H, S.W, self.ns[s], P(self.N[s]),
                  None, P(self.flag), hs[id(stream)])
 
-        def repack(l, stream):
-            call("sv_repack_fwd_k", P(self.W[l]), K, C, C, bf, P(self.V[l]), self.V[l].numel(), hs[id(stream)])
-            call("sv_repack_dx_k", P(self.W[l]), K, C, C, bf, P(self.P[l]), self.P[l].numel(), hs[id(stream)])
+        # every layer's weights, repacked for the forward and the input
+        # gradient in one launch (host arrays of device pointers, kept alive)
+        self._rp = [(ctypes.c_void_p * self.L)(*[t.data_ptr() for t in ts]) for ts in (self.W, self.V, self.P)]
 
         vb = self.ws.numel()
-        # side stream: the later stages' index tables and layers' weights
+        # side stream: the later stages' index tables
         record(self.ev_start, main)
         wait(side, self.ev_start)
         for s in range(1, len(self.ns)):
             index(s, side)
-        for l in range(1, self.L):
-            repack(l, side)
-        call("sv_repack_dx_k", P(self.W[0]), K, C, C, bf, P(self.P[0]), self.P[0].numel(), hs[id(side)])
         record(self.ev_prep, side)
-        # main stream: forward
+        # main stream: index, all weights, forward
         index(0, main)
-        call("sv_repack_fwd_k", P(self.W[0]), K, C, C, bf, P(self.V[0]), self.V[0].numel(), hs[id(main)])
+        call("sv_repack_layers_k", self.L, self._rp[0], self._rp[1], self.V[0].numel(), self._rp[2], self.P[0].numel(),
+             K, C, C, bf, hs[id(main)])
         for l in range(self.L):
             s = self.stage_of[l]
-            if l == 1:
-                wait(main, self.ev_prep)
+            if l == self.lps:
+                wait(main, self.ev_prep)        # the stage-1 and stage-2 tables
             if l > 0 and self.stage_of[l - 1] != s:
                 call("sv_stage_gather", P(self.ys[l - 1]), self.ns[s - 1], P(self.sels[s]), self.ns[s], P(self.xs[l]),
                      C, bf, hs[id(main)])

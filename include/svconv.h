@@ -257,6 +257,18 @@ sv_status sv_sparseconv2d_bwd_dw_noalloc_k(const void *X, const int32_t *N, cons
 
 sv_status sv_repack_dx_k(const void *Wt, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
                          void *P, size_t P_bytes, hipStream_t stream);
+/* The repacks of several layers of one shape in a single launch, for a
+ * step that repacks every layer's weights up front (Key Design 2's forward
+ * and backward kernels consume them): for i < count (1..16), V[i] receives
+ * what sv_repack_fwd_k(Wt[i], ...) writes and P[i] what sv_repack_dx_k(Wt[i],
+ * ...) writes.  Wt, V, P: host arrays of device pointers; V or P may be
+ * NULL (that layout is not written), but not their entries; every V[i]
+ * holds V_bytes and every P[i] P_bytes (16-byte aligned; each at least
+ * sv_workspace_bytes_k(SV_OP_FWD / SV_OP_DX, ...)).  bf16 only; P needs a
+ * shape sv_repack_dx_k takes (else SV_ERR_UNSUPPORTED). */
+sv_status sv_repack_layers_k(int32_t count, const void *const *Wt, void *const *V, size_t V_bytes,
+                             void *const *P, size_t P_bytes, int32_t K, int32_t C_in, int32_t C_out,
+                             sv_dtype dtype, hipStream_t stream);
 sv_status sv_sparseconv2d_bwd_dx_packed_k(const void *dY, const int32_t *N, const void *P, void *dX,
                                           int64_t n, int32_t K, int32_t C_in, int32_t C_out,
                                           sv_dtype dtype, hipStream_t stream);

@@ -310,6 +310,39 @@ sv_status sv_repack_dx_k(const void* Wt, int32_t K, int32_t C_in, int32_t C_out,
                                          taps, true, stream));
 }
 
+sv_status sv_repack_layers_k(int32_t count, const void* const* Wt, void* const* V, size_t V_bytes, void* const* P,
+                             size_t P_bytes, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
+                             hipStream_t stream) {
+    int taps = 0;
+    sv_status st = taps_of(K, &taps);
+    if (st != SV_OK) return st;
+    if (count < 1 || count > kRepackMax || !Wt || C_in <= 0 || C_out <= 0 || !valid_dtype(dtype))
+        return SV_ERR_INVALID_ARG;
+    if (dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
+    const size_t need = conv_mfma_fwd_workspace(C_in, C_out, taps);
+    for (int i = 0; i < count; ++i) {
+        if (!Wt[i] || (V && !V[i]) || (P && !P[i])) return SV_ERR_INVALID_ARG;
+        if ((V && reinterpret_cast<uintptr_t>(V[i]) % 16) || (P && reinterpret_cast<uintptr_t>(P[i]) % 16))
+            return SV_ERR_INVALID_ARG;
+    }
+    if (V && (!conv_mfma_supported(false, C_in, C_out, 1, taps))) return SV_ERR_UNSUPPORTED;
+    if (P && !conv_bfrag_ok(C_out, C_in, taps)) return SV_ERR_UNSUPPORTED;
+    if ((V && V_bytes < need) || (P && P_bytes < need)) return SV_ERR_WORKSPACE;
+    const bool vfrag = V && conv_bfrag_ok(C_in, C_out, taps);
+    auto W16 = reinterpret_cast<const uint16_t* const*>(Wt);
+    if (vfrag || P) {
+        st = hip_status(launch_repack_batch(count, W16, vfrag ? reinterpret_cast<uint16_t* const*>(V) : nullptr,
+                                            reinterpret_cast<uint16_t* const*>(P), C_in, C_out, taps, stream));
+        if (st != SV_OK) return st;
+    }
+    if (V && !vfrag)
+        for (int i = 0; i < count; ++i)
+            if ((st = hip_status(launch_repack_fwd(W16[i], static_cast<uint16_t*>(V[i]), C_in, C_out, taps, stream))) !=
+                SV_OK)
+                return st;
+    return SV_OK;
+}
+
 sv_status sv_sparseconv2d_bwd_dx_packed_k(const void* dY, const int32_t* N, const void* P, void* dX, int64_t n,
                                           int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
                                           hipStream_t stream) {

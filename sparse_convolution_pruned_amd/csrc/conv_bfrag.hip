@@ -344,6 +344,65 @@ __global__ __launch_bounds__(256) void k_repack_frag(const uint16_t* __restrict_
     }
 }
 
+// Several layers' weights in one launch: blockIdx.y = (layer, layout), the
+// layout's fragment order as k_repack_frag writes it.
+struct RepackBatch {
+    const uint16_t* W[kRepackMax];
+    uint16_t* out[2][kRepackMax];     // [0]: forward (nullable), [1]: input gradient (nullable)
+};
+
+__global__ __launch_bounds__(256) void k_repack_batch(RepackBatch b, int taps, int Ci, int Co) {
+    const int layer = blockIdx.y >> 1, dx = blockIdx.y & 1;
+    uint16_t* Bf = b.out[dx][layer];
+    if (!Bf) return;
+    const uint16_t* Wt = b.W[layer];
+    const int K = dx ? Co : Ci, NO = dx ? Ci : Co;
+    const int NG = NO / 64;
+    const int64_t total = static_cast<int64_t>(taps) * K * NO / 8;
+    for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
+         idx += static_cast<int64_t>(gridDim.x) * 256) {
+        const int lane = static_cast<int>(idx & 63);
+        int64_t t = idx >> 6;
+        const int nb = static_cast<int>(t & 1);
+        t >>= 1;
+        const int ks = static_cast<int>(t & 3);
+        t >>= 2;
+        const int g = static_cast<int>(t % NG);
+        const int64_t rr = t / NG;
+        const int c = static_cast<int>(rr / taps), j = static_cast<int>(rr % taps);
+        const int k = 64 * c + 16 * ks + 8 * (lane >> 5);
+        const int col = 64 * g + 32 * nb + (lane & 31);
+        uint32_t w[4];
+        if (dx) {
+            const uint16_t* s = Wt + (static_cast<int64_t>(taps - 1 - j) * Ci + col) * Co + k;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) w[p] = static_cast<uint32_t>(s[2 * p]) | (static_cast<uint32_t>(s[2 * p + 1]) << 16);
+        } else {
+            const uint16_t* s = Wt + (static_cast<int64_t>(j) * Ci + k) * Co + col;
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                w[p] = static_cast<uint32_t>(s[(2 * p) * Co]) | (static_cast<uint32_t>(s[(2 * p + 1) * Co]) << 16);
+        }
+        *reinterpret_cast<uint4*>(Bf + idx * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+hipError_t launch_repack_batch(int count, const uint16_t* const* W, uint16_t* const* V, uint16_t* const* P, int Ci,
+                               int Co, int taps, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    if (count > kRepackMax) return hipErrorInvalidValue;
+    RepackBatch b{};
+    for (int i = 0; i < count; ++i) {
+        b.W[i] = W[i];
+        b.out[0][i] = V ? V[i] : nullptr;
+        b.out[1][i] = P ? P[i] : nullptr;
+    }
+    const int64_t total = static_cast<int64_t>(taps) * Ci * Co / 8;
+    const int bx = static_cast<int>(std::min<int64_t>((total + 255) / 256, 1024));
+    hipLaunchKernelGGL(k_repack_batch, dim3(bx, 2 * count), dim3(256), 0, stream, b, taps, Ci, Co);
+    return hipGetLastError();
+}
+
 bool conv_bfrag_ok(int K, int NO, int taps) {
     return taps == 9 && K > 0 && NO > 0 && K % BF_KC == 0 && NO % BF_BN == 0 &&
            static_cast<int64_t>(taps) * NO * K * 2 <= kMaxRange;

@@ -120,6 +120,13 @@ hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, in
 bool conv_bfrag_ok(int K, int NO, int taps);
 hipError_t launch_repack_frag(const uint16_t* Wt, uint16_t* Bf, int Ci, int Co, int taps, bool dx,
                               hipStream_t stream);
+// Up to kRepackMax layers' weights (Wt[i], all of one shape) into both
+// fragment orders in one launch: V[i] for the forward, P[i] for the input
+// gradient (V, P or their entries nullable); the shapes must suit
+// conv_bfrag_ok for each layout written.
+constexpr int kRepackMax = 16;
+hipError_t launch_repack_batch(int count, const uint16_t* const* W, uint16_t* const* V, uint16_t* const* P, int Ci,
+                               int Co, int taps, hipStream_t stream);
 hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t* Bf, const uint16_t* bias,
                              uint16_t* out, int64_t n, int K, int NO, int taps, hipStream_t stream);
 size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps);

@@ -42,7 +42,7 @@ SYMBOLS = (
     "sv_sparseconv2d_bwd_dw", "sv_workspace_bytes",
     "sv_build_index_k", "sv_sparseconv2d_fwd_k", "sv_sparseconv2d_bwd_dx_k",
     "sv_sparseconv2d_bwd_dw_k", "sv_workspace_bytes_k",
-    "sv_repack_fwd_k", "sv_sparseconv2d_fwd_packed_k", "sv_repack_dx_k", "sv_sparseconv2d_bwd_dx_packed_k",
+    "sv_repack_fwd_k", "sv_sparseconv2d_fwd_packed_k", "sv_repack_dx_k", "sv_repack_layers_k", "sv_sparseconv2d_bwd_dx_packed_k",
     "sv_sparseconv2d_bwd_dw_partials_k",
     "sv_sparseconv2d_bwd_dw_reduce_k", "sv_sparseconv2d_chunked",
     "sv_chunked_workspace_bytes", "sv_sparseconv2d_chunked_host", "sv_chunked_host_workspace_bytes",
@@ -120,6 +120,7 @@ def load(path: str = LIB_PATH):
         "sv_repack_fwd_k": ([P, i32, i32, i32, E, P, sz, P], E),
         "sv_sparseconv2d_fwd_packed_k": ([P, P, P, P, P, i64, i32, i32, i32, E, P], E),
         "sv_repack_dx_k": ([P, i32, i32, i32, E, P, sz, P], E),
+        "sv_repack_layers_k": ([i32, P, P, sz, P, sz, i32, i32, i32, E, P], E),
         "sv_sparseconv2d_bwd_dx_packed_k": ([P, P, P, P, i64, i32, i32, i32, E, P], E),
         "sv_sparseconv2d_bwd_dw_partials_k": ([P, P, P, P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
         "sv_sparseconv2d_bwd_dw_reduce_k": ([P, P, i64, i32, i32, i32, E, i32, P, sz, P], E),
@@ -378,6 +379,19 @@ def sv_repack_dx_k(Wt, P, stream=None):
     wsb = P.numel() * P.element_size()
     st = load().sv_repack_dx_k(_ptr(Wt), ksize_of_taps(taps), Ci, Co, _dt(Wt), _ptr(P), wsb, _stream(stream))
     _check(st, "sv_repack_dx_k")
+
+
+def sv_repack_layers_k(Wts, Vs=None, Ps=None, stream=None):
+    """One launch repacking every layer's weights (all of one shape) for the
+    forward (Vs) and the input gradient (Ps); either list may be None."""
+    count = len(Wts)
+    taps, Ci, Co = Wts[0].shape
+    arr = lambda ts: None if ts is None else (ctypes.c_void_p * count)(*[t.data_ptr() for t in ts])
+    vb = 0 if Vs is None else min(v.numel() * v.element_size() for v in Vs)
+    pb = 0 if Ps is None else min(p.numel() * p.element_size() for p in Ps)
+    st = load().sv_repack_layers_k(count, arr(Wts), arr(Vs), vb, arr(Ps), pb, ksize_of_taps(taps), Ci, Co,
+                                   _dt(Wts[0]), _stream(stream))
+    _check(st, "sv_repack_layers_k")
 
 
 def sv_sparseconv2d_bwd_dx_packed_k(dY, N, P, dX, K, stream=None):

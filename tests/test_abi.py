@@ -286,6 +286,22 @@ def test_adapter_validation_and_workspace(lib):
     assert lib.sv_adapter_bwd(*nodw, BF16, 0, FAKE, 1 << 30, None, None) == ops.SV_ERR_INVALID_ARG
 
 
+def test_repack_layers_validation(lib):
+    F32, BF16 = ops.SV_F32, ops.SV_BF16
+    f = lib.sv_repack_layers_k
+    arr = lambda k, v=4096: (ctypes.c_void_p * k)(*([v] * k))
+    need = lib.sv_workspace_bytes_k(ops.SV_OP_FWD, 8, 3, 256, 256, BF16)
+    assert f(0, arr(1), arr(1), need, arr(1), need, 3, 256, 256, BF16, None) == ops.SV_ERR_INVALID_ARG
+    assert f(17, arr(17), arr(17), need, arr(17), need, 3, 256, 256, BF16, None) == ops.SV_ERR_INVALID_ARG
+    assert f(2, None, arr(2), need, arr(2), need, 3, 256, 256, BF16, None) == ops.SV_ERR_INVALID_ARG
+    assert f(2, arr(2), arr(2), need, arr(2), need, 3, 256, 256, F32, None) == ops.SV_ERR_UNSUPPORTED
+    assert f(2, arr(2), arr(2), need - 1, arr(2), need, 3, 256, 256, BF16, None) == ops.SV_ERR_WORKSPACE
+    assert f(2, arr(2), arr(2), need, arr(2), need - 1, 3, 256, 256, BF16, None) == ops.SV_ERR_WORKSPACE
+    assert f(2, arr(2), arr(2, 4100), need, None, 0, 3, 256, 256, BF16, None) == ops.SV_ERR_INVALID_ARG
+    assert f(2, arr(2), None, 0, arr(2), need, 3, 128, 128, BF16, None) == ops.SV_ERR_UNSUPPORTED
+    assert f(2, arr(2), arr(2), need, arr(2), need, 4, 256, 256, BF16, None) == ops.SV_ERR_INVALID_ARG
+
+
 def test_noalloc_validation(lib):
     """The allocation-free weight gradient checks its arguments and the
     size of its partials before it touches a device."""

@@ -140,3 +140,28 @@ def test_chunk_driver_c256_bitwise():
     assert torch.equal(Y.view(torch.int16), Yr.view(torch.int16))
     assert torch.equal(dX.view(torch.int16), dXr.view(torch.int16))
     assert_close(host(dW), O.bwd_dw(L.X, N, L.dY), "bf16", "chunked dW")
+
+
+@pytest.mark.parametrize("C", [256, 128])
+def test_repack_layers_equals_single_repacks(C):
+    """One launch for several layers writes exactly what the per-layer
+    repacks write (fragment order at C = 256; at C = 128 the forward's
+    per-tap layout and no input-gradient layout)."""
+    g = torch.Generator(device="cuda").manual_seed(3)
+    Ws = [torch.randn(9, C, C, device="cuda", generator=g).to(bf) for _ in range(5)]
+    nbytes = ops.sv_workspace_bytes(ops.SV_OP_FWD, 1000, C, C, bf)
+    new = lambda: torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    V1, V2 = [new() for _ in Ws], [new() for _ in Ws]
+    dx = C == 256
+    P1 = [new() for _ in Ws] if dx else None
+    P2 = [new() for _ in Ws] if dx else None
+    ops.sv_repack_layers_k(Ws, V1, P1)
+    for i, W in enumerate(Ws):
+        ops.sv_repack_fwd_k(W, V2[i])
+        if dx:
+            ops.sv_repack_dx_k(W, P2[i])
+    torch.cuda.synchronize()
+    for i in range(len(Ws)):
+        assert torch.equal(V1[i], V2[i]), f"forward layout of layer {i}"
+        if dx:
+            assert torch.equal(P1[i], P2[i]), f"input-gradient layout of layer {i}"
