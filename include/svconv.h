@@ -68,7 +68,7 @@ typedef enum sv_kernel { SV_KERNEL_AUTO = 0, SV_KERNEL_VALU = 1, SV_KERNEL_MFMA 
 /* Bits of the device error flag written by sv_build_index. */
 #define SV_FLAG_COORD_RANGE   1  /* a coordinate p < 0 or p >= H*W                        */
 #define SV_FLAG_DUPLICATE     2  /* two tokens of one frame on one cell                   */
-#define SV_FLAG_BAD_OFFSETS   4  /* frame_offsets not non-decreasing within [0, n]        */
+#define SV_FLAG_BAD_OFFSETS   4  /* frame_offsets not non-decreasing from 0 to exactly n   */
 
 /* Passes of sv_sparseconv2d_chunked. */
 #define SV_PASS_FWD 1u

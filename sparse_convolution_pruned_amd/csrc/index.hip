@@ -28,6 +28,11 @@ __global__ __launch_bounds__(kIndexThreads) void k_build_index(
     const bool ok = beg >= tok_base && end >= beg && end - tok_base <= n_rows &&
                     end - beg <= cells;
     if (!ok) flag |= SV_FLAG_BAD_OFFSETS;
+    // ... and the frames together must cover all n_rows of it: the first
+    // frame starts at row 0 and the last ends at row n_rows (rows outside
+    // every frame would be left unwritten).
+    if (blockIdx.x == 0 && beg != tok_base) flag |= SV_FLAG_BAD_OFFSETS;
+    if (blockIdx.x == gridDim.x - 1 && end != tok_base + n_rows) flag |= SV_FLAG_BAD_OFFSETS;
 
     for (int c = threadIdx.x; c < cells; c += kIndexThreads) smap[c] = -1;
     __syncthreads();

@@ -1,14 +1,15 @@
 """The host-streamed chunk driver (per-token tensors in pinned host memory,
 double-buffered through the device on two copy streams) against the device
 chunk driver: the same kernels run on the same chunks in the same order, so
-Y, dX, dW and db must match bit for bit.  The device driver itself is checked
-against the oracle in test_gpu_configs."""
+Y, dX, dW and db must match bit for bit.  Config 4 is also compared with the
+oracle directly, every element."""
 import numpy as np
 import pytest
 import torch
 
+from oracle import oracle as O
 from sparse_convolution_pruned_amd import ops, workloads as wl
-from tests.gpu_util import dev
+from tests.gpu_util import assert_close, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +70,11 @@ def test_c4_host_streamed():
     (Y, dX, dW, db), (Yh, dXh, dW2, db2) = run_both(L, 256, ALL)
     assert same(Y, Yh) and same(dX, dXh)
     assert same(dW, dW2) and same(db, db2)
+    _, Nr, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    assert_close(host(Yh), O.fwd(L.X, Nr, L.Wt, L.b), "bf16", "c4 host-streamed Y")
+    assert_close(host(dXh), O.bwd_dx(L.dY, Nr, L.Wt), "bf16", "c4 host-streamed dX")
+    assert_close(host(dW2), O.bwd_dw(L.X, Nr, L.dY), "bf16", "c4 host-streamed dW")
+    assert_close(host(db2), O.bwd_db(L.dY), "bf16", "c4 host-streamed db")
     Ls = wl.make_layer("c4", scale_T=256)
     C = L.X.shape[1]
     d_full = ops.make_chunked_host_desc(L.T, L.H, L.W, pinned(L.coords), pinned(L.frame_offsets), C, C,

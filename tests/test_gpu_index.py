@@ -91,6 +91,14 @@ def test_index_bad_offsets_flag():
     assert flag & ops.SV_FLAG_BAD_OFFSETS
 
 
+@pytest.mark.parametrize("offs", [[0, 2], [1, 3], [0, 1, 2]])
+def test_index_offsets_must_cover_all_rows(offs):
+    # three rows, but the frames cover only rows 0..1, 1..2 or 0..1: some
+    # row of N would be left unwritten, which the flag reports
+    _, _, flag = gpu_index(np.array([0, 5, 7], np.int32), np.array(offs, np.int32), len(offs) - 1, 3, 4)
+    assert flag & ops.SV_FLAG_BAD_OFFSETS
+
+
 def test_index_grid_too_large_rejected():
     c = dev(np.zeros(1, np.int32))
     o = dev(np.array([0, 1], np.int32))
