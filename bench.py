@@ -48,13 +48,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c5", choices=["c5", "c2", "c3a", "c3b", "c4", "c4-host", "xattn",
+    p.add_argument("--workload", default="c5", choices=["c5", "c1", "c2", "c3a", "c3b", "c4", "c4-host", "xattn",
                                                                 "adapter"])
     p.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     p.add_argument("--ksize", type=int, default=3, choices=[1, 3, 5, 7],
                    help="single-layer workloads: K of a K x K neighbourhood (weights of the same "
                         "distribution, std 1/sqrt(K*K*C))")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="c5: skip measuring the other configurations (c1, c2, c3a, c3b, c4) for the record")
     p.add_argument("--no-dense-gemm", action="store_true",
                    help="c5: skip timing the vendor dense GEMMs of the same shapes (context only)")
     p.add_argument("--cold", action="store_true",
@@ -69,8 +71,8 @@ def parse():
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one plain device copy of this size (HBM counter calibration)")
     a = p.parse_args()
-    if a.ksize != 3 and a.workload not in ("c2", "c3a", "c3b", "c4", "adapter"):
-        p.error("--ksize applies to the single-layer workloads c2, c3a, c3b, c4 and to the adapter")
+    if a.ksize != 3 and a.workload not in ("c1", "c2", "c3a", "c3b", "c4", "adapter"):
+        p.error("--ksize applies to the single-layer workloads c1, c2, c3a, c3b, c4 and to the adapter")
     return a
 
 
@@ -475,59 +477,71 @@ def traffic_record(kernel_name, kernel_files):
     return rec
 
 
-def layer_workload(args):
-    """Single-layer workloads (c2, c3a, c3b, c4), for the design notes'
-    per-configuration table; prints one JSON line of its own."""
+def measure_layer(key, kernel="auto", ksize=3, steps=20, warmup=3, dw_stream="side", cold=False, scale_T=None):
+    """One single-layer configuration (c1, c2, c3a, c3b, c4) timed on the
+    GPU: the whole configuration per step (index build and its passes; c4
+    through the chunk driver), then each pass alone over `steps`
+    back-to-back calls between HIP events on the calling stream.  Returns a
+    dict: ms per step and per pass, effective TFLOP/s, the fraction of the
+    bf16 MFMA peak (fp32 vector peak for fp32), the gather-model HBM rate and
+    its fraction, peak device memory and the workspace."""
     import numpy as np
     import torch
     from sparse_convolution_pruned_amd import ops, workloads as wl
 
-    L = wl.make_layer(args.workload)
-    cfg = wl.CONFIGS[args.workload]
-    bf = torch.bfloat16
+    L = wl.make_layer(key, scale_T=scale_T) if scale_T else wl.make_layer(key)
+    cfg = wl.CONFIGS[key]
+    dt = torch.bfloat16 if L.dtype == "bf16" else torch.float32
+    es = 2 if L.dtype == "bf16" else 4
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    mem0 = torch.cuda.memory_allocated()
     dev = lambda a, d=None: (torch.from_numpy(a).to(d) if d is not None else torch.from_numpy(a)).cuda()
     coords, offs = dev(L.coords), dev(L.frame_offsets)
-    K = args.ksize
+    K = ksize
     taps = K * K
-    n, C = L.n, L.X.shape[1]
+    n, Ci, Co = L.n, L.X.shape[1], L.Wt.shape[2]
     Wk = L.Wt
     if K != 3:
         rng = np.random.default_rng(900 + K)
-        Wk = wl.round_bf16(rng.standard_normal((taps, C, C)).astype(np.float32) / np.sqrt(taps * C))
-    X, Wt, b, dY = dev(L.X, bf), dev(Wk, bf), dev(L.b, bf), dev(L.dY, bf)
+        Wk = wl.round_bf16(rng.standard_normal((taps, Ci, Co)).astype(np.float32) / np.sqrt(taps * Ci))
+    X, Wt, b, dY = dev(L.X, dt), dev(Wk, dt), dev(L.b, dt), dev(L.dY, dt)
     N = torch.empty((n, taps), dtype=torch.int32, device="cuda")
-    Y = torch.empty((n, C), dtype=bf, device="cuda")
-    dX = torch.empty((n, C), dtype=bf, device="cuda")
-    dW = torch.empty((taps, C, C), dtype=torch.float32, device="cuda")
-    db = torch.empty((C,), dtype=torch.float32, device="cuda")
+    Y = torch.empty((n, Co), dtype=dt, device="cuda")
+    dX = torch.empty((n, Ci), dtype=dt, device="cuda")
+    dW = torch.empty((taps, Ci, Co), dtype=torch.float32, device="cuda")
+    db = torch.empty((Co,), dtype=torch.float32, device="cuda")
     passes = cfg["passes"]
     chunked = "chunk_frames" in cfg
     if chunked:
         # the chunks' weight gradients on a second stream (default priority),
         # beside the next chunks' index builds and convolutions
-        dws = torch.cuda.Stream() if args.dw_stream == "side" else None
+        dws = torch.cuda.Stream() if dw_stream == "side" else None
         desc = ops.make_chunked_desc(L.T, L.H, L.W, coords, offs, torch.from_numpy(L.frame_offsets.copy()),
-                                     C, C, bf, cfg["chunk_frames"], X=X, Wt=Wt, bias=b, Y=Y, dY=dY,
-                                     dX=dX, dW=dW, db=db, kernel=args.kernel, ksize=K, dw_stream=dws)
+                                     Ci, Co, dt, cfg["chunk_frames"], X=X, Wt=Wt, bias=b, Y=Y, dY=dY,
+                                     dX=dX, dW=dW, db=db, kernel=kernel, ksize=K, dw_stream=dws)
         pm = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
         ws = torch.empty(max(256, ops.sv_chunked_workspace_bytes(desc, pm)), dtype=torch.uint8, device="cuda")
 
         def step():
             ops.sv_sparseconv2d_chunked(desc, pm, ws)
     else:
-        ws = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_DW, n, K, C, C, bf)), dtype=torch.uint8,
+        ws = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_DW, n, K, Ci, Co, dt)), dtype=torch.uint8,
                          device="cuda")
-        fws = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_FWD, n, K, C, C, bf)), dtype=torch.uint8,
+        fws = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_FWD, n, K, Ci, Co, dt)), dtype=torch.uint8,
+                          device="cuda")
+        xws = torch.empty(max(256, ops.sv_workspace_bytes_k(ops.SV_OP_DX, n, K, Ci, Co, dt)), dtype=torch.uint8,
                           device="cuda")
         if K == 3:
             run = {"index": lambda: ops.sv_build_index(coords, offs, L.T, L.H, L.W, N),
-                   "fwd": lambda: ops.sv_sparseconv2d_fwd(X, N, Wt, b, Y, args.kernel, workspace=fws),
-                   "dx": lambda: ops.sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, args.kernel),
+                   "fwd": lambda: ops.sv_sparseconv2d_fwd(X, N, Wt, b, Y, kernel, workspace=fws),
+                   "dx": lambda: ops.sv_sparseconv2d_bwd_dx(dY, N, Wt, dX, kernel, workspace=xws),
                    "dw": lambda: ops.sv_sparseconv2d_bwd_dw(X, N, dY, dW, db, False, ws)}
         else:
             run = {"index": lambda: ops.sv_build_index_k(coords, offs, L.T, L.H, L.W, K, N),
-                   "fwd": lambda: ops.sv_sparseconv2d_fwd_k(X, N, Wt, b, Y, args.kernel, workspace=fws),
-                   "dx": lambda: ops.sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, args.kernel),
+                   "fwd": lambda: ops.sv_sparseconv2d_fwd_k(X, N, Wt, b, Y, kernel, workspace=fws),
+                   "dx": lambda: ops.sv_sparseconv2d_bwd_dx_k(dY, N, Wt, dX, kernel, workspace=xws),
                    "dw": lambda: ops.sv_sparseconv2d_bwd_dw_k(X, N, dY, dW, db, False, ws)}
 
         def step():
@@ -537,42 +551,96 @@ def layer_workload(args):
                 run["dx"]()
             if "dw" in passes:
                 run["dw"]()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
-    torch.cuda.reset_peak_memory_stats()
     torch.cuda.synchronize()
-    if args.cold:
-        sec = timed_cold(torch, step, args.steps) / args.steps
+    if cold:
+        sec = timed_cold(torch, step, steps) / steps
     else:
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             step()
         torch.cuda.synchronize()
-        sec = (time.perf_counter() - t0) / args.steps
+        sec = (time.perf_counter() - t0) / steps
     # each pass alone (device time of `steps` back-to-back calls)
     pass_ms = {}
     if not chunked:
         for name in ["index", "fwd"] + [p for p in ("dx", "dw") if p in passes]:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(args.steps):
+            for _ in range(steps):
                 run[name]()
             e1.record()
             torch.cuda.synchronize()
-            pass_ms[name] = round(e0.elapsed_time(e1) / args.steps, 4)
-    fl = len(passes) * 2 * n * taps * C * C
+            pass_ms[name] = round(e0.elapsed_time(e1) / steps, 4)
+    fl_pass = 2 * n * taps * Ci * Co
+    fl = len(passes) * fl_pass
     # gather model per conv pass: every neighbour row read from memory, no reuse
-    gather_bytes = n * (taps * 2 * C + 2 * C + 4 * taps)
-    gather_gbps = {k: round(gather_bytes / (v * 1e-3) / 1e9, 1) for k, v in pass_ms.items() if k != "index"}
-    valid = None if chunked else round(float((N >= 0).sum().item()) / max(N.numel(), 1), 4)
-    print(json.dumps({"workload": args.workload, "name": cfg["name"], "kernel": args.kernel, "ksize": K, "n": n,
-                      "cache": "cold" if args.cold else "warm", "valid_tap_fraction": valid,
-                      "ms_per_step": round(sec * 1e3, 4), "pass_ms": pass_ms, "gbps_gather_model": gather_gbps,
-                      "tflops": round(fl / sec / 1e12, 3),
-                      "frac_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
-                      "peak_mem_mb": round(torch.cuda.max_memory_allocated() / 2 ** 20, 1),
-                      "workspace_mb": round(ws.numel() / 2 ** 20, 2),
-                      "dw_stream": args.dw_stream if chunked else None}), flush=True)
+    gather_bytes = n * (taps * es * Ci + es * Co + 4 * taps)
+    peak = PEAK_BF16_TFLOPS if L.dtype == "bf16" else PEAK_FP32_VALU_TFLOPS
+    out = {"name": cfg["name"], "kernel": kernel, "ksize": K, "n": n, "dtype": L.dtype,
+           "valid_tap_fraction": None if chunked else round(float((N >= 0).sum().item()) / max(N.numel(), 1), 4),
+           "ms_per_step": round(sec * 1e3, 4), "passes": list(passes),
+           "tflops": round(fl / sec / 1e12, 3),
+           "roofline_mfma" if L.dtype == "bf16" else "roofline_fp32_vector":
+               {"peak_tflops": peak, "frac": round(fl / sec / 1e12 / peak, 4)},
+           "roofline_hbm_gather_model": {"gbps": round(len(passes) * gather_bytes / sec / 1e9, 1),
+                                         "frac": round(len(passes) * gather_bytes / sec / 1e9 / PEAK_HBM_GBPS, 4)},
+           "peak_mem_mb": round((torch.cuda.max_memory_allocated() - mem0) / 2 ** 20, 1),
+           "workspace_mb": round(ws.numel() / 2 ** 20, 2)}
+    if pass_ms:
+        out["pass_ms"] = pass_ms
+        out["pass_tflops"] = {k: round(fl_pass / (v * 1e-3) / 1e12, 2) for k, v in pass_ms.items() if k != "index"}
+    if chunked:
+        out["dw_stream"] = dw_stream
+    return out
+
+
+def configs_record(steps=20, warmup=3):
+    """The other configurations, for the driver-run record beside the c5
+    headline: c1 (fp32), c2 on both kernels, c3a, c3b, c4 (chunked) and c4's
+    device memory at 384 frames (the workspace does not grow with T); each
+    with ms per step and per pass, TFLOP/s and its roofline fractions."""
+    rec = {}
+    rec["c1"] = measure_layer("c1", steps=steps, warmup=warmup)
+    rec["c2_mfma"] = measure_layer("c2", "mfma", steps=steps, warmup=warmup)
+    rec["c2_valu"] = measure_layer("c2", "valu", steps=max(3, steps // 4), warmup=1)
+    rec["c3a"] = measure_layer("c3a", steps=steps, warmup=warmup)
+    rec["c3b"] = measure_layer("c3b", steps=steps, warmup=warmup)
+    rec["c4"] = measure_layer("c4", steps=steps, warmup=warmup)
+    short = measure_layer("c4", steps=3, warmup=1, scale_T=384)
+    rec["c4"]["memory_by_T"] = {"384": {"peak_mem_mb": short["peak_mem_mb"], "workspace_mb": short["workspace_mb"]},
+                                "3072": {"peak_mem_mb": rec["c4"]["peak_mem_mb"],
+                                         "workspace_mb": rec["c4"]["workspace_mb"]}}
+    return rec
+
+
+def index_build_cpu_ms(reps=5):
+    """The oracle's index build alone on the host for the c5 first stage
+    (58,822 tokens over 384 frames of a 16 x 16 grid): context for the
+    page's index build on the CPU."""
+    from oracle import oracle as O
+    from sparse_convolution_pruned_amd import workloads as wl
+
+    S = wl.make_staged("c5")
+    st = S.stages[0]
+    O.build_index(st["coords"], st["frame_offsets"], S.T, S.H, S.W)
+    best = 1e30
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        O.build_index(st["coords"], st["frame_offsets"], S.T, S.H, S.W)
+        best = min(best, time.perf_counter() - t0)
+    return {"ms": round(best * 1e3, 3), "tokens": int(st["coords"].shape[0]), "frames": S.T,
+            "note": "best of %d, single call of the float64/int32 oracle on the host (index arithmetic only)" % reps}
+
+
+def layer_workload(args):
+    """Single-layer workloads (c1, c2, c3a, c3b, c4), for the design notes'
+    per-configuration table; prints one JSON line of its own."""
+    r = measure_layer(args.workload, args.kernel, args.ksize, args.steps, args.warmup, args.dw_stream, args.cold)
+    r["workload"] = args.workload
+    r["cache"] = "cold" if args.cold else "warm"
+    print(json.dumps(r), flush=True)
 
 
 def host_stream_workload(args):
@@ -907,6 +975,8 @@ def main():
     }
     if not args.no_dense_gemm and args.kernel != "valu":
         out["dense_gemm_same_shape"] = dense_gemm_context(torch, run.ns, C, ev)
+    if not args.no_configs and args.kernel == "auto":
+        out["configs"] = configs_record()
     if args.calibrate_copy_mib:
         nb = args.calibrate_copy_mib * 2 ** 20
         a = torch.empty(nb, dtype=torch.uint8, device="cuda")
@@ -925,6 +995,7 @@ def main():
             "sample": f"{passes} pass(es) over the first {args.cpu_frames} of 384 frames of the same "
                       f"workload: index build per stage, fwd through 6 layers, dW+db+dX back "
                       f"through them, float64 loops ({cdt:.1f} s)",
+            "index_build": index_build_cpu_ms(),
         }
     print(json.dumps(out), flush=True)
 
