@@ -13,6 +13,8 @@
 //
 // The MFMA kernel (bf16, C_in and C_out multiples of 128) is described
 // below; other shapes and fp32 use the VALU kernel in conv_valu.hip.
+#include <type_traits>
+
 #include "internal.h"
 #include "mfma.h"
 
@@ -199,26 +201,59 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     // the issue of the loads comes before the first MFMAs (issued at the
     // start of the step, they cost 9-12% of the call), while the loads still
     // have two k-steps to land before the barrier.
-    auto mma_step = [&](const char* xb, int s, char* nxt, bool more) {
+    auto mma_step = [&](const char* xb, int s, char* nxt, auto more_c) {
+        constexpr bool more = decltype(more_c)::value;
         const char* yb = xb + 3 * DW_TILEB;
         int4 e0, e1;
-        if (more) entries(s + 1, e0, e1);
-#pragma unroll
-        for (int ks = 0; ks < DW_TK / 16; ++ks) {
-            if (ks == 2 && more) issue(s + 1, nxt, e0, e1);
+        if constexpr (more) entries(s + 1, e0, e1);
+        // k-step ks's fragments are read during k-step ks - 1: after the
+        // barrier every wave of the workgroup starts a step at once, and
+        // reading a k-step's fragments just before its own MFMAs had all of
+        // them reading (MFMAs idle) and then all multiplying (LDS idle).
+        // Scheduling barriers keep each k-step's reads ahead of the MFMAs of
+        // the previous one.
+        auto frags = [&](int ks, bf16x8_t* a, bf16x8_t* b) __attribute__((always_inline)) {
             const int t0 = 32 * kh + 8 * ks + fv;
             const int r0 = tok_addr(t0), r1 = tok_addr(t0 + 4);
-            bf16x8_t a[3], b[2];
 #pragma unroll
             for (int t = 0; t < 3; ++t)
                 a[t] = cat8(tr_read(xb + t * DW_TILEB + r0 + colA), tr_read(xb + t * DW_TILEB + r1 + colA));
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
                 b[nb] = cat8(tr_read(yb + r0 + colB + nb * 64), tr_read(yb + r1 + colB + nb * 64));
+        };
+        bf16x8_t a[3], b[2], an[3], bn[2];
+        frags(0, a, b);
+#pragma unroll
+        for (int ks = 0; ks < DW_TK / 16; ++ks) {
+            if (ks < DW_TK / 16 - 1) frags(ks + 1, an, bn);
+            if constexpr (more) {
+                if (ks == 2) issue(s + 1, nxt, e0, e1);
+            }
 #pragma unroll
             for (int t = 0; t < 3; ++t)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) acc[t][nb] = mfma32(a[t], b[nb], acc[t][nb]);
+            // Two of the next k-step's reads after each MFMA: in-order issue
+            // would otherwise hold all ten reads behind the six MFMAs' issue.
+            if (ks < DW_TK / 16 - 1) {
+                const bool dma = more && ks == 2;
+                if (dma) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 5; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                if (!dma) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 3; ++t) a[t] = an[t];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) b[nb] = bn[nb];
         }
         if (do_db) {
             const int c = tid & 15, q = tid >> 4;
@@ -250,20 +285,30 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     // step s + 2's entries into the table slot of step s's (read in step
     // s - 1) and fetches step s + 3's; one barrier per step waits for all of
     // it, the direct loads included.
-    auto step = [&](int s, const char* cur, char* nxt) {
+    // Whether a step stages the next one is a compile-time flag (only the
+    // last step does not), so that each step is one straight-line block the
+    // scheduler can interleave.
+    auto step = [&](int s, const char* cur, char* nxt, auto more_c) {
         if (loader && s + 2 < steps) {
             put_n(s + 2);
             if (s + 3 < steps) fetch_n(s + 3);
         }
-        mma_step(cur, s, nxt, s + 1 < steps);
+        mma_step(cur, s, nxt, more_c);
         __syncthreads();
     };
+    using stage_next = std::integral_constant<bool, true>;
+    using last_step = std::integral_constant<bool, false>;
     int s = 0;
-    for (; s + 1 < steps; s += 2) {
-        step(s, sbuf0, sbuf1);
-        step(s + 1, sbuf1, sbuf0);
+    for (; s + 2 < steps; s += 2) {
+        step(s, sbuf0, sbuf1, stage_next{});
+        step(s + 1, sbuf1, sbuf0, stage_next{});
     }
-    if (s < steps) step(s, sbuf0, sbuf1);
+    if (s + 1 < steps) {
+        step(s, sbuf0, sbuf1, stage_next{});
+        step(s + 1, sbuf1, sbuf0, last_step{});
+    } else if (s < steps) {
+        step(s, sbuf0, sbuf1, last_step{});
+    }
 
     float* dst = out + (direct ? 0 : static_cast<int64_t>(slice) * taps * Ci * Co);
     const int l32 = lane & 31, lhi = lane >> 5;
@@ -391,6 +436,8 @@ __global__ __launch_bounds__(256) void k_reduce_slices(const float* __restrict__
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+constexpr int64_t kDwSlots = 192;   // workgroups per dispatch round in the cost model
+
 DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16, int taps) {
     DwPlan p{};
     p.taps = taps;
@@ -401,10 +448,15 @@ DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16, int taps) {
     const int64_t step = p.mfma ? DW_TK : 16;
     if (p.mfma) {
         // Split-K factor from a small cost model: one workgroup per compute
-        // unit of a 256-CU part at ~4 TFLOP/s, counted in whole dispatch
-        // rounds, plus the fp32 partials written and read back (~5 TB/s) and
-        // a fixed cost for the extra reduction launch.  Depends on the
-        // arguments only, so workspace sizing and the call agree.
+        // unit at ~4 TFLOP/s, counted in whole dispatch rounds of
+        // kDwSlots workgroups, plus the fp32 partials written and read back
+        // (~5 TB/s) and a fixed cost for the extra reduction launch.  The
+        // rounds are counted against three quarters of a 256-CU part: in a
+        // training step the weight gradient runs beside the input gradient,
+        // and on the c5 backward the smaller split (16 slices instead of 21
+        // at 58,822 tokens) made the whole step 2.5-3% faster although the
+        // call alone is ~7% slower.  Depends on the arguments only, so
+        // workspace sizing and the call agree.
         const int64_t tiles = ceil_div(static_cast<int64_t>(taps) * (Ci / DW_BI), 3) * (Co / DW_BO);
         const double flops = 2.0 * static_cast<double>(n) * static_cast<double>(3 * tiles / (Co / DW_BO)) * DW_BI * Co;
         const double dwb = static_cast<double>(taps) * Ci * Co * 4;
@@ -412,7 +464,7 @@ DwPlan plan_dw(int64_t n, int Ci, int Co, bool bf16, int taps) {
         slices = 1;
         for (int64_t s = 1; s <= 64; ++s) {
             if (s > 1 && ceil_div(n, s) < 4 * DW_TK) break;
-            const double rounds = static_cast<double>(ceil_div(tiles * s, 256));
+            const double rounds = static_cast<double>(ceil_div(tiles * s, kDwSlots));
             const double t = rounds * flops / static_cast<double>(tiles * s) / 4e12 +
                              (s > 1 ? (2.0 * static_cast<double>(s) * dwb / 5e12 + 4e-6) : 0.0);
             if (t < best) { best = t; slices = s; }

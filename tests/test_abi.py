@@ -313,9 +313,11 @@ def test_noalloc_validation(lib):
     assert f(FAKE, FAKE, FAKE, None, None, 8, 3, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
     assert f(FAKE, None, FAKE, FAKE, None, 8, 3, 4, 4, F32, 0, None) == ops.SV_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, FAKE, None, 8, 3, 4, 4, 7, 0, None) == ops.SV_ERR_INVALID_ARG
+    # a 5 x 5 layer with 2M tokens: the planner splits the tokens into
+    # several dispatch rounds of slices, whose partials exceed the array
     big = 2_000_000
-    assert lib.sv_workspace_bytes(ops.SV_OP_DW, big, 512, 512, BF16) > ops.SV_NOALLOC_SCRATCH_BYTES
-    assert f(FAKE, FAKE, FAKE, FAKE, None, big, 3, 512, 512, BF16, 0, None) == ops.SV_ERR_WORKSPACE
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DW, big, 5, 512, 512, BF16) > ops.SV_NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, FAKE, FAKE, FAKE, None, big, 5, 512, 512, BF16, 0, None) == ops.SV_ERR_WORKSPACE
 
 
 def test_split_forms_validation(lib):

@@ -37,7 +37,7 @@ def both(L, N, K=3, accumulate=False, seed_dw=None):
 
 
 def test_two_calls_second_smaller():
-    # first: a c5-sized layer (split-K partials ~24 MB), then a small one
+    # first: a c5-sized layer (split-K partials ~38 MB), then a small one
     L1 = wl.make_random_case(61, 160, 16, 16, 0.6, 256, 256, "bf16")
     L2 = wl.make_random_case(62, 7, 16, 16, 0.4, 256, 256, "bf16")
     assert L2.n < L1.n
@@ -61,10 +61,11 @@ def test_fp32_kxk_and_accumulate():
 
 
 def test_rejects_beyond_the_array():
+    # a 5 x 5 layer with 2M tokens: partials of several rounds of slices
     n = 2_000_000
-    need = ops.sv_workspace_bytes(ops.SV_OP_DW, n, 512, 512, torch.bfloat16)
-    assert need > ops.SV_NOALLOC_SCRATCH_BYTES
     lib = ops.load()
-    st = lib.sv_sparseconv2d_bwd_dw_noalloc_k(1 << 12, 1 << 12, 1 << 12, 1 << 12, None, n, 3, 512, 512,
+    need = lib.sv_workspace_bytes_k(ops.SV_OP_DW, n, 5, 512, 512, ops.SV_BF16)
+    assert need > ops.SV_NOALLOC_SCRATCH_BYTES
+    st = lib.sv_sparseconv2d_bwd_dw_noalloc_k(1 << 12, 1 << 12, 1 << 12, 1 << 12, None, n, 5, 512, 512,
                                               ops.SV_BF16, 0, None)
     assert st == ops.SV_ERR_WORKSPACE
