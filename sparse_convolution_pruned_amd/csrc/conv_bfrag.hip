@@ -233,13 +233,33 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
                 if (ks == 1 && more) rows_from(mn, win, rown);
                 if (ks < 3) read_a(buf, rowb, ks + 1, an);
                 else if (more) read_a(buf, rown, 0, an);
-                __builtin_amdgcn_sched_barrier(0);
+                // MFMAs column block by column block, so that B register
+                // nb is free for the next round's fragment after MB MFMAs.
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma32(a[mb], bq[ks][nb], acc[mb][nb]);
+                    for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma32(a[mb], bq[ks][nb], acc[mb][nb]);
+                    bq[ks][nb] = loadB(rr + 1, ks, nb);
+                }
+                // Issue order: one A read after each of the first MFMAs,
+                // each B load right after the last MFMA that reads its
+                // register.  A wave issues in order, so loads and reads
+                // queued behind the k-step's MFMAs would wait for their
+                // issue; between them they go out in the MFMAs' shadow.
+                if (ks < 3 || more) {
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) bq[ks][nb] = loadB(rr + 1, ks, nb);
+                    for (int mb = 0; mb < MB; ++mb) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                } else {
+                    __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
+                }
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    if (nb > 0) __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) a[mb] = an[mb];
