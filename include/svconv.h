@@ -4,7 +4,8 @@
  * C ABI.  Plain pointers and sizes only; every pointer argument named "device"
  * is device memory owned by the caller; the library never allocates, never
  * frees, never synchronises the stream (unless the SV_SYNC_CHECK debugging
- * aid below is switched on) and keeps no state other than a cached device
+ * aid below is switched on, or sv_sparseconv2d_chunked is given no host copy
+ * of the frame offsets) and keeps no state other than a cached device
  * property.  All work is enqueued asynchronously on the caller's
  * hipStream_t (NULL = the default stream).  No C++ exception crosses this
  * boundary.  Status codes report argument errors synchronously, before any
@@ -102,7 +103,7 @@ typedef enum sv_op { SV_OP_FWD = 0, SV_OP_DX = 1, SV_OP_DW = 2 } sv_op;
  * enqueuing and return the status the device flag implies (SV_ERR_COORD_RANGE,
  * SV_ERR_DUPLICATE_COORD, or SV_ERR_INVALID_ARG for SV_FLAG_BAD_OFFSETS).
  * The flag is never cleared by the library, so earlier bits count too.
- * Without the variable nothing ever synchronises. */
+ * Without the variable nothing here synchronises. */
 sv_status sv_build_index(const int32_t *coords, const int32_t *frame_offsets,
                          int32_t T, int32_t H, int32_t W, int64_t n,
                          int32_t *N_out, int32_t *M_out, int32_t *err_flag,
@@ -144,7 +145,10 @@ sv_status sv_sparseconv2d_bwd_dx(const void *dY, const int32_t *N, const void *W
                                  sv_dtype dtype, sv_kernel kernel, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
-/* Weight (and bias) gradient, a split-K reduction over tokens:
+/* Weight (and bias) gradient, a split-K reduction over tokens ("SV-TAD:
+ * Native Sparse Convolutions for Efficient Temporal Action Detection",
+ * Key Design 2: the method has dedicated backward kernels; the page prints
+ * no backward formula, and this one is the adjoint of the forward sum):
  *   dW[j][i][o] (+)= sum_k X[N[k,j]][i] dY[k][o],   db[o] (+)= sum_k dY[k][o].
  * Token slices write fp32 partials to the workspace, then a fixed-order
  * reduction adds them (deterministic: the same inputs give the same bits).
@@ -297,7 +301,14 @@ typedef struct sv_chunked_desc {
     int32_t chunk_frames;               /* >= 1                                  */
     const int32_t *coords;              /* device [n]                            */
     const int32_t *frame_offsets;       /* device [T+1]                          */
-    const int32_t *frame_offsets_host;  /* host [T+1], the same values           */
+    const int32_t *frame_offsets_host;  /* host [T+1], the same values, or NULL:
+                                           the call then copies frame_offsets to
+                                           the host and waits for that copy on
+                                           `stream` (it needs the chunk
+                                           boundaries to size its launches), and
+                                           the workspace is sized for chunks of
+                                           chunk_frames full frames (H*W tokens
+                                           each) */
     const void *X;                      /* device [n][C_in]   (FWD, DW)          */
     const void *Wt;                     /* device [9][C_in][C_out] (FWD, DX)     */
     const void *bias;                   /* device [C_out], nullable              */
@@ -331,8 +342,9 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc *desc, uint32_t passes,
 
 /* Workspace bytes sv_sparseconv2d_chunked needs for this descriptor (reads
  * only the host fields: T, H, W, C_in, C_out, dtype, chunk_frames,
- * frame_offsets_host, ksize).  Returns 0 and nothing else on bad
- * descriptors.  sv_sparseconv2d_chunked returns SV_ERR_UNSUPPORTED for an
+ * frame_offsets_host, ksize; with frame_offsets_host NULL, the bound for
+ * chunks of full frames, which covers any offsets).  Returns 0 and nothing
+ * else on bad descriptors.  sv_sparseconv2d_chunked returns SV_ERR_UNSUPPORTED for an
  * odd ksize above 7 and SV_ERR_INVALID_ARG for other bad ones. */
 size_t sv_chunked_workspace_bytes(const sv_chunked_desc *desc, uint32_t passes);
 

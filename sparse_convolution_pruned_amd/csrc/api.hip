@@ -3,6 +3,8 @@
 // stream.  Declarations and contracts: include/svconv.h.
 #include <limits>
 
+#include <vector>
+
 #include "internal.h"
 
 #include <cmath>
@@ -416,13 +418,29 @@ struct ChunkLayout {
 
 int ksize_of(int32_t ksize) { return ksize == 0 ? 3 : ksize; }
 
+// Upper bound of dw_workspace_bytes(plan_dw(toks, ...)) over toks <= max_tokens:
+// a plan has at most 64 slices and, with more than one, at least 256 tokens
+// per slice (both planners), so slices <= min(64, max_tokens / 256 + 1).
+size_t dw_bytes_bound(int64_t max_tokens, int Ci, int Co, int taps) {
+    const int64_t s = std::min<int64_t>(64, max_tokens / 256 + 1);
+    const size_t part = s > 1 ? static_cast<size_t>(s) * taps * Ci * Co * sizeof(float) : 0;
+    return align_up(part) + align_up(static_cast<size_t>(s) * Co * sizeof(float));
+}
+
 bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
-    if (!d || !d->frame_offsets_host || d->T < 0 || d->H <= 0 || d->W <= 0 ||
+    if (!d || d->T < 0 || d->H <= 0 || d->W <= 0 ||
         d->chunk_frames <= 0 || d->C_in <= 0 || d->C_out <= 0 || !valid_dtype(d->dtype))
         return false;
     L->K = ksize_of(d->ksize);
     if (taps_of(L->K, &L->taps) != SV_OK) return false;
     const int32_t* ho = d->frame_offsets_host;
+    if (!ho) {
+        // No host copy of the offsets: the bound for chunks of chunk_frames
+        // full frames (every chunk holds at most chunk_frames * H * W tokens).
+        L->max_tokens = static_cast<int64_t>(std::min(d->T, d->chunk_frames)) * d->H * d->W;
+        if (L->max_tokens > max_rows(L->taps)) return false;
+        L->dw_bytes = (passes & SV_PASS_DW) ? dw_bytes_bound(L->max_tokens, d->C_in, d->C_out, L->taps) : 0;
+    } else {
     if (ho[0] != 0) return false;
     for (int t = 0; t < d->T; ++t)
         if (ho[t + 1] < ho[t]) return false;
@@ -438,6 +456,7 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
         if (passes & SV_PASS_DW)
             L->dw_bytes = std::max(L->dw_bytes, dw_workspace_bytes(plan_dw(toks, d->C_in, d->C_out,
                                                                           d->dtype == SV_BF16, L->taps)));
+    }
     }
     L->n_bytes = align_up(static_cast<size_t>(L->max_tokens) * L->taps * sizeof(int32_t));
     L->w_bytes = (passes & SV_PASS_FWD) ? fwd_ws_bytes(d->C_in, d->C_out, d->dtype, L->max_tokens, L->taps) : 0;
@@ -479,6 +498,24 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
     if (d && taps_of(ksize_of(d->ksize), &taps0) == SV_ERR_UNSUPPORTED) return SV_ERR_UNSUPPORTED;
     ChunkLayout L;
     if (!chunk_layout(d, passes, &L)) return SV_ERR_INVALID_ARG;
+    if (!d->frame_offsets_host) {
+        // The chunk boundaries are needed on the host: copy the offsets and
+        // wait for the copy (the one place the library waits on a stream).
+        // The workspace was sized for the bound, which covers the exact
+        // layout of the call below.
+        if (!d->frame_offsets) return SV_ERR_INVALID_ARG;
+        std::vector<int32_t> ho(static_cast<size_t>(d->T) + 1);
+        if (hipMemcpyAsync(ho.data(), d->frame_offsets, ho.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                           stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return SV_ERR_HIP;
+        sv_chunked_desc dd = *d;
+        dd.frame_offsets_host = ho.data();
+        ChunkLayout E;
+        if (!chunk_layout(&dd, passes, &E)) return SV_ERR_INVALID_ARG;
+        if (E.total > L.total) return SV_ERR_INVALID_ARG;    // offsets beyond full frames
+        return sv_sparseconv2d_chunked(&dd, passes, workspace, workspace_bytes, stream);
+    }
     if (passes & ~(SV_PASS_FWD | SV_PASS_DX | SV_PASS_DW)) return SV_ERR_INVALID_ARG;
     if (!valid_kernel(d->kernel)) return SV_ERR_INVALID_ARG;
     if (static_cast<int64_t>(d->H) * d->W > kMaxCells) return SV_ERR_UNSUPPORTED;
@@ -611,7 +648,7 @@ struct HostLayout {
 };
 
 bool host_layout(const sv_chunked_host_desc* d, uint32_t passes, HostLayout* L) {
-    if (!d) return false;
+    if (!d || !d->frame_offsets_host) return false;
     // The device driver's layout reads only host fields; build it from a
     // descriptor carrying the same ones.
     sv_chunked_desc dd{};

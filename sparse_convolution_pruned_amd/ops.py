@@ -426,19 +426,23 @@ def sv_sparseconv2d_bwd_dw_reduce_k(dW, db, n, dtype, workspace, accumulate=Fals
 def make_chunked_desc(T, H, W, coords, frame_offsets, frame_offsets_host, C_in, C_out, dtype,
                       chunk_frames, X=None, Wt=None, bias=None, Y=None, dY=None, dX=None,
                       dW=None, db=None, err_flag=None, kernel="auto", ksize=3, dw_stream=None):
-    """Build the descriptor; `frame_offsets_host` must be a CPU int32 tensor
-    (kept referenced by the returned object).  `ksize`: K of the K x K
-    neighbourhood.  `dw_stream`: a torch stream for the chunks' weight
-    gradients (None: everything on the call's stream)."""
-    assert frame_offsets_host.device.type == "cpu" and frame_offsets_host.dtype == torch.int32
-    fh = frame_offsets_host.contiguous()
+    """Build the descriptor; `frame_offsets_host` is a CPU int32 tensor
+    (kept referenced by the returned object) or None: then the workspace is
+    sized for chunks of full frames and the call copies the offsets to the
+    host, waiting for that copy.  `ksize`: K of the K x K neighbourhood.
+    `dw_stream`: a torch stream for the chunks' weight gradients (None:
+    everything on the call's stream)."""
+    fh = None
+    if frame_offsets_host is not None:
+        assert frame_offsets_host.device.type == "cpu" and frame_offsets_host.dtype == torch.int32
+        fh = frame_offsets_host.contiguous()
     d = ChunkedDesc()
     d.T, d.H, d.W, d.C_in, d.C_out = int(T), int(H), int(W), int(C_in), int(C_out)
     d.dtype = SV_BF16 if dtype == torch.bfloat16 else SV_F32
     d.kernel = _kernel(kernel)
     d.chunk_frames = int(chunk_frames)
     d.coords, d.frame_offsets = _ptr(coords), _ptr(frame_offsets)
-    d.frame_offsets_host = fh.data_ptr()
+    d.frame_offsets_host = None if fh is None else fh.data_ptr()
     d.X, d.Wt, d.bias, d.Y = _ptr(X), _ptr(Wt), _ptr(bias), _ptr(Y)
     d.dY, d.dX, d.dW, d.db, d.err_flag = _ptr(dY), _ptr(dX), _ptr(dW), _ptr(db), _ptr(err_flag)
     d.ksize = int(ksize)

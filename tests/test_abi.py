@@ -117,6 +117,34 @@ def test_chunked_workspace_flat_in_T(lib):
         == ops.SV_ERR_INVALID_ARG
 
 
+def test_chunked_workspace_without_host_offsets(lib):
+    """Without a host copy of the offsets the workspace is sized for chunks
+    of full frames: at least what any actual offsets need."""
+    rng = np.random.default_rng(4)
+    for C, K, dt, chunk in [(128, 3, ops.SV_BF16, 256), (256, 3, ops.SV_BF16, 8), (64, 5, ops.SV_F32, 3),
+                            (512, 3, ops.SV_BF16, 1), (128, 1, ops.SV_BF16, 40)]:
+        for passes in (ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW, ops.SV_PASS_DW, ops.SV_PASS_FWD):
+            T = 300
+            none = _desc(T, np.zeros(1, np.int32), C=C, chunk=chunk)
+            none.frame_offsets_host = None
+            none.dtype, none.ksize = dt, K
+            bound = lib.sv_chunked_workspace_bytes(ctypes.byref(none), passes)
+            assert bound > 0
+            for keep in (1.0, 0.5, 0.05):
+                counts = rng.binomial(196, keep, size=T).astype(np.int32)
+                offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+                d = _desc(T, offs, C=C, chunk=chunk)
+                d.dtype, d.ksize = dt, K
+                exact = lib.sv_chunked_workspace_bytes(ctypes.byref(d), passes)
+                assert 0 < exact <= bound, (C, K, chunk, passes, keep, exact, bound)
+            # every frame full: the bound's token count is reached
+            full_offs = (np.arange(T + 1) * 196).astype(np.int32)     # referenced: the descriptor holds a raw pointer
+            full = _desc(T, full_offs, C=C, chunk=chunk)
+            full.dtype, full.ksize = dt, K
+            if not passes & ops.SV_PASS_DW:
+                assert lib.sv_chunked_workspace_bytes(ctypes.byref(full), passes) == bound
+
+
 def test_chunked_dw_stream_workspace(lib):
     """With a dW stream the workspace holds a second N table (4 * 9 bytes
     per token of the largest chunk, rounded up), and only when the dW pass

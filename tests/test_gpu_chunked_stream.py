@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 ALL = ops.SV_PASS_FWD | ops.SV_PASS_DX | ops.SV_PASS_DW
 
 
-def run(L, chunk_frames, passes, dw_stream, dt=torch.bfloat16, kernel="auto", ksize=3):
+def run(L, chunk_frames, passes, dw_stream, dt=torch.bfloat16, kernel="auto", ksize=3, host_offsets=True):
     n, Ci, Co = L.n, L.X.shape[1], L.Wt.shape[2]
     Wt, b = dev(L.Wt, dt), dev(L.b, dt)
     coords, offs = dev(L.coords), dev(L.frame_offsets)
@@ -28,7 +28,7 @@ def run(L, chunk_frames, passes, dw_stream, dt=torch.bfloat16, kernel="auto", ks
     dW = torch.full((ksize * ksize, Ci, Co), 7.0, dtype=torch.float32, device="cuda")
     db = torch.full((Co,), 7.0, dtype=torch.float32, device="cuda")
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
-    offs_h = torch.from_numpy(L.frame_offsets.copy())
+    offs_h = torch.from_numpy(L.frame_offsets.copy()) if host_offsets else None
     d = ops.make_chunked_desc(L.T, L.H, L.W, coords, offs, offs_h, Ci, Co, dt, chunk_frames, X=X, Wt=Wt,
                               bias=b, Y=Y, dY=dY, dX=dX, dW=dW, db=db, err_flag=flag, kernel=kernel,
                               ksize=ksize, dw_stream=dw_stream)
@@ -71,3 +71,17 @@ def test_kxk_and_valu():
     check(L, 2, ksize=5)
     L = wl.make_random_case(84, 6, 14, 14, 0.5, 48, 40, "f32")
     check(L, 2, dt=torch.float32)
+
+
+@pytest.mark.parametrize("dw_side", [False, True])
+def test_without_host_offsets(dw_side):
+    """No host copy of the frame offsets: the workspace is sized for full
+    frames and the call reads the offsets from the device itself; the
+    results equal the call with the host copy bit for bit."""
+    L = wl.make_random_case(83, 9, 14, 14, [30, 0, 196, 80, 5, 0, 150, 99, 61], 256, 256, "bf16")
+    print(f"n={L.n} dw_side={dw_side}", flush=True)
+    side = torch.cuda.Stream() if dw_side else None
+    a = run(L, 2, ALL, side)
+    b = run(L, 2, ALL, side, host_offsets=False)
+    for name, u, v in zip(("Y", "dX", "dW", "db"), a, b):
+        assert torch.equal(u, v), f"{name} differs without the host offsets"
