@@ -21,15 +21,16 @@
 //   - Only the gathered rows (the tile's neighbour window) sit in LDS,
 //     brought in by direct-to-LDS buffer loads (no staging registers) and
 //     double-buffered per 64-channel chunk: one barrier per chunk.
-//   - Each wave owns MB * 32 tokens x 128 output channels (MB x 4 blocks of
-//     32 x 32, accumulators in the AGPRs).  An MFMA then costs 256 bytes of
-//     LDS reads and 256 bytes of weight loads when MB = 4; k_conv_mfma's
+//   - Each wave owns MB * 32 tokens x NB * 32 output channels (MB x NB
+//     blocks of 32 x 32, accumulators in the AGPRs; NB = 4, or 2 where the
+//     smaller tile fills more of the chip).  An MFMA then costs 256 bytes of
+//     LDS reads and 256 bytes of weight loads when MB = NB = 4; k_conv_mfma's
 //     64 x 64 blocks read 512 bytes of LDS per MFMA, the whole LDS bandwidth
 //     of a compute unit when all four SIMDs issue.
-//   - Workgroup: 4 waves, 2 x 2, tile 64 MB tokens x 256 channels, one
-//     workgroup (one wave per SIMD) per compute unit.  The host picks MB in
-//     {2, 3, 4} so that the grid is one round of at most 256 tiles where it
-//     can.  Measured on the c5 stages: with two workgroups per compute unit
+//   - Workgroup: 4 waves, 2 x 2, tile 64 MB tokens x 64 NB channels, one
+//     workgroup (one wave per SIMD) per compute unit.  The host picks the
+//     smallest tile (MB in {2, 3, 4}, NB in {2, 4}) whose grid is one round
+//     of at most 256 tiles where it can.  Measured on the c5 stages: with two workgroups per compute unit
 //     the shader clock fell to ~1.7 GHz against ~2.1 GHz with one, and a
 //     lone wave per SIMD issues MFMAs back to back (32 cycles each) when its
 //     operands are in flight early enough, which the software pipelining
@@ -54,7 +55,7 @@
 namespace svc {
 
 constexpr int BF_WAVES = 4;              // waves per workgroup (2 x 2)
-constexpr int BF_BN = 256;               // output channels per tile (128 per wave)
+constexpr int BF_BN = 256;               // output channels per tile at NB = 4 (128 per wave)
 constexpr int BF_KC = 64;                // contracted channels per chunk
 constexpr int BF_HALO = 32;              // window rows on either side of the tile
 constexpr int BF_ROWB = 128;             // bytes per window row
@@ -62,14 +63,16 @@ constexpr int BF_MAXTILES = 256;         // one workgroup per compute unit of a 
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// MB: 32-row blocks of tokens per wave; tile 64 * MB tokens.
-template <int TAPS, int MB>
+// MB: 32-row blocks of tokens per wave, NB: 32-column blocks of output
+// channels per wave; tile 64 * MB tokens x 64 * NB channels.
+template <int TAPS, int MB, int NB>
 __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t* __restrict__ A,
                                                                const int32_t* __restrict__ Nt,
                                                                const uint16_t* __restrict__ Bf,
                                                                const uint16_t* __restrict__ bias,
                                                                uint16_t* __restrict__ out, int n, int K, int NO) {
-    constexpr int BM = 64 * MB, BN = BF_BN, NT = 64 * BF_WAVES;
+    constexpr int BM = 64 * MB, BN = 64 * NB, NT = 64 * BF_WAVES;
+    static_assert(NB == 2 || NB == 4, "a wave's channels are whole 64-channel groups");
     // Window rows are requested before the tile's N slice has arrived, from
     // the fixed start k0 - HALO: with tokens packed frame-major and in
     // ascending flat order inside a frame, every neighbour of token k lies
@@ -133,26 +136,26 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void_t*)(buf + b * 1024), 16, off, 0, 0, 0);
         }
     };
-    // B fragments of round rr for this wave's 128 output channels (two
+    // B fragments of round rr for this wave's NB * 32 output channels (NB / 2
     // 64-channel groups): a per-lane offset in one register and a uniform one
     // in a scalar register.  The loads issued during the last round re-read
     // that round (unused).
     const uint32_t bLane = static_cast<uint32_t>(lane * 16);
-    const uint32_t bWave = static_cast<uint32_t>((n0 / 64 + 2 * wn) * 8192);
+    const uint32_t bWave = static_cast<uint32_t>((n0 / 64 + (NB / 2) * wn) * 8192);
     const uint32_t bRound = static_cast<uint32_t>(NO / 64) * 8192;
-    auto loadB = [&](int rr, int ks, int nb) __attribute__((always_inline)) {     // nb 0..3: 32-column block of the wave
+    auto loadB = [&](int rr, int ks, int nb) __attribute__((always_inline)) {     // nb < NB: 32-column block of the wave
         const uint32_t so = bWave + static_cast<uint32_t>(min(rr, R - 1)) * bRound + (nb >> 1) * 8192 +
                             (ks * 2 + (nb & 1)) * 1024;
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(rB, bLane, __builtin_amdgcn_readfirstlane(so), 0);
         return __builtin_bit_cast(bf16x8_t, v);
     };
 
-    floatx16_t acc[MB][4];
+    floatx16_t acc[MB][NB];
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = zero16();
-    bf16x8_t bq[4][4];
+        for (int b = 0; b < NB; ++b) acc[a][b] = zero16();
+    bf16x8_t bq[4][NB];
 
     // ---- prologue: the N slice, the speculative window of chunk 0 and the
     // first round's B fragments are all requested before anything waits.
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) bq[ks][nb] = loadB(0, ks, nb);
+        for (int nb = 0; nb < NB; ++nb) bq[ks][nb] = loadB(0, ks, nb);
     __syncthreads();                     // sOut cleared
     {
         bool outside = false;
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
                 // MFMAs column block by column block, so that B register
                 // nb is free for the next round's fragment after MB MFMAs.
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
+                for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma32(a[mb], bq[ks][nb], acc[mb][nb]);
                     bq[ks][nb] = loadB(rr + 1, ks, nb);
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
                     __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
                 }
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
+                for (int nb = 0; nb < NB; ++nb) {
                     if (nb > 0) __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 }
@@ -312,8 +315,8 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
     // and the barriers between passes took about a tenth of the kernel.
     const rsrc_t rO = make_rsrc(out, static_cast<uint32_t>(n) * NO * 2);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int col = n0 + wn * 128 + nb * 32 + l32;
+    for (int nb = 0; nb < NB; ++nb) {
+        const int col = n0 + wn * (NB * 32) + nb * 32 + l32;
         const float bv = bias ? bf16_to_f32(bias[col]) : 0.f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -439,28 +442,42 @@ hipError_t launch_repack_frag(const uint16_t* Wt, uint16_t* Bf, int Ci, int Co, 
     return hipGetLastError();
 }
 
-// Row blocks per wave: the smallest MB in {2, 3, 4} whose grid is one round
-// of at most 256 tiles (one per compute unit of a 256-CU part), else 4.
-// Depends on the arguments only; every MB gives the same bits.
-static int bfrag_blocks(int64_t n, int NO) {
-    const int64_t tilesN = NO / BF_BN;
-    for (int mb = 2; mb <= 4; ++mb)
-        if (((n + 64 * mb - 1) / (64 * mb)) * tilesN <= BF_MAXTILES) return mb;
-    return 4;
+// Tile shape: the smallest tile (fewest tokens x channels per workgroup)
+// whose grid is one round of at most 256 tiles (one per compute unit of a
+// 256-CU part); at equal size, 256 channels (NB = 4: half the A reads per
+// MFMA).  Without such a tile, the largest one.  Depends on the arguments
+// only; every shape gives the same bits.
+struct BfragShape {
+    int mb, nb;
+};
+static BfragShape bfrag_shape(int64_t n, int NO) {
+    static const BfragShape order[] = {{2, 2}, {3, 2}, {2, 4}, {3, 4}, {4, 4}};    // by tile size
+    for (const BfragShape& t : order) {
+        if (NO % (64 * t.nb) != 0) continue;
+        const int64_t tiles = ((n + 64 * t.mb - 1) / (64 * t.mb)) * (NO / (64 * t.nb));
+        if (tiles <= BF_MAXTILES) return t;
+    }
+    return {4, 4};
 }
 
 hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t* Bf, const uint16_t* bias,
                              uint16_t* out, int64_t n, int K, int NO, int taps, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     if (!conv_bfrag_ok(K, NO, taps)) return hipErrorInvalidValue;
-    const int mb = bfrag_blocks(n, NO);
-    const dim3 grid(static_cast<unsigned>(((n + 64 * mb - 1) / (64 * mb)) * (NO / BF_BN)));
+    const BfragShape t = bfrag_shape(n, NO);
+    const dim3 grid(static_cast<unsigned>(((n + 64 * t.mb - 1) / (64 * t.mb)) * (NO / (64 * t.nb))));
+    const dim3 block(64 * BF_WAVES);
     const int ni = static_cast<int>(n);
-    switch (mb) {
-        case 2: hipLaunchKernelGGL((k_conv_bfrag<9, 2>), grid, dim3(64 * BF_WAVES), 0, stream, A, N, Bf, bias, out, ni, K, NO); break;
-        case 3: hipLaunchKernelGGL((k_conv_bfrag<9, 3>), grid, dim3(64 * BF_WAVES), 0, stream, A, N, Bf, bias, out, ni, K, NO); break;
-        default: hipLaunchKernelGGL((k_conv_bfrag<9, 4>), grid, dim3(64 * BF_WAVES), 0, stream, A, N, Bf, bias, out, ni, K, NO); break;
-    }
+    if (t.nb == 2 && t.mb == 2)
+        hipLaunchKernelGGL((k_conv_bfrag<9, 2, 2>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
+    else if (t.nb == 2)
+        hipLaunchKernelGGL((k_conv_bfrag<9, 3, 2>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
+    else if (t.mb == 2)
+        hipLaunchKernelGGL((k_conv_bfrag<9, 2, 4>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
+    else if (t.mb == 3)
+        hipLaunchKernelGGL((k_conv_bfrag<9, 3, 4>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
+    else
+        hipLaunchKernelGGL((k_conv_bfrag<9, 4, 4>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
     return hipGetLastError();
 }
 

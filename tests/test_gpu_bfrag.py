@@ -1,7 +1,7 @@
 """The matrix-core kernel that streams the weights in fragment order
 (bf16, 3 x 3, contracted channels a multiple of 64, produced channels a
 multiple of 256): forward and input gradient against the oracle in every
-staging mode and tile height, and bit for bit against the kernel that reads
+staging mode and tile shape, and bit for bit against the kernel that reads
 Wt directly (the input gradient without a workspace).  The split forms
 (repack, then the packed call) must equal the single calls bit for bit."""
 import numpy as np
@@ -46,7 +46,8 @@ CASES = [
     (32, 4, 16, 16, 0.5, 256, 256, True),               # shuffled packing: gather mode tap by tap
     (33, 2, 40, 40, 0.5, 256, 256, False),              # grid 40 wide: tiles outside the window
     (34, 5, 14, 14, [0, 1, 196, 0, 60], 512, 256, False),  # empty frames; C_in 512 (8 chunks)
-    (35, 3, 16, 16, 0.4, 256, 512, False),              # two output-channel tiles
+    (35, 3, 16, 16, 0.4, 256, 512, False),              # several output-channel tiles
+    (37, 90, 16, 16, 0.8, 256, 512, False),             # 18,450 tokens: 192 x 256 tiles forward, 192 x 128 dX
     (36, 2, 14, 14, 0.7, 64, 256, False),               # one 64-channel chunk in the forward
 ]
 
@@ -60,17 +61,25 @@ def test_fragment_kernel(case):
     check_case(L, N, f"{case}")
 
 
-@pytest.mark.parametrize("n_frames,keep,mb", [(200, 200, 3), (230, 230, 4), (120, 170, 2)])
-def test_tile_heights(n_frames, keep, mb):
-    """Token counts that select 128-, 192- and 256-token tiles (the
-    smallest tile whose grid fits one round of 256 workgroups)."""
-    L = wl.make_random_case(40 + mb, n_frames, 16, 16, [keep] * n_frames, 256, 256, "bf16")
+# (frames, kept per frame, tokens x channels of the tile the host picks at
+# 256 channels: the smallest tile whose grid fits one round of 256
+# workgroups, 256-channel tiles first at equal size)
+TILES = [(60, 200, "128x128"), (100, 200, "192x128"), (140, 200, "128x256"), (200, 200, "192x256"),
+         (230, 230, "256x256")]
+TILE_RANGE = {"128x128": (0, 128 * 128), "192x128": (128 * 128, 128 * 192), "128x256": (128 * 192, 256 * 128),
+              "192x256": (256 * 128, 256 * 192), "256x256": (256 * 192, 10 ** 9)}
+
+
+@pytest.mark.parametrize("n_frames,keep,tile", TILES, ids=[t[2] for t in TILES])
+def test_tile_shapes(n_frames, keep, tile):
+    """Token counts that select each tile shape."""
+    L = wl.make_random_case(40 + n_frames, n_frames, 16, 16, [keep] * n_frames, 256, 256, "bf16")
     n = L.n
-    lim = {2: (0, 256 * 128), 3: (256 * 128, 256 * 192), 4: (256 * 192, 10 ** 9)}[mb]
-    assert lim[0] < n <= lim[1], n
-    print(f"n={n} frames={n_frames} MB={mb}", flush=True)
+    lo, hi = TILE_RANGE[tile]
+    assert lo < n <= hi, n
+    print(f"n={n} frames={n_frames} tile={tile}", flush=True)
     _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
-    check_case(L, N, f"MB={mb}")
+    check_case(L, N, f"tile {tile}")
 
 
 def test_random_table_and_out_of_range():
