@@ -134,7 +134,7 @@ sv_status sv_sparseconv2d_fwd(const void *X, const int32_t *N, const void *Wt,
  *   dY [n][C_out], N [n][9], Wt [9][C_in][C_out], dX [n][C_in] written.
  *   workspace: device, nullable.  When the bf16 matrix-core path runs on a
  *   shape whose weights it takes in fragment order (C_out a multiple of 64,
- *   C_in of 256) and Wt is 16-byte aligned, a workspace of at least
+ *   C_in of 128) and Wt is 16-byte aligned, a workspace of at least
  *   sv_workspace_bytes(SV_OP_DX, ...) bytes (16-byte aligned) receives the
  *   repacked weights and the faster kernel runs; without one the kernel that
  *   reads Wt directly runs.  Both give the same bits.
@@ -217,7 +217,7 @@ size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_
  *     not fit).  Weights repacked once serve any number of forward calls and
  *     can be prepared on another stream ahead of them.
  *   sv_repack_dx_k writes the input gradient's weights in MFMA fragment
- *     order (bf16, 3 x 3, C_out a multiple of 64 and C_in of 256, else
+ *     order (bf16, 3 x 3, C_out a multiple of 64 and C_in of 128, else
  *     SV_ERR_UNSUPPORTED; Wt and P 16-byte aligned, P at least
  *     sv_workspace_bytes_k(SV_OP_DX, ...) bytes), and
  *     sv_sparseconv2d_bwd_dx_packed_k runs the input gradient from that P;

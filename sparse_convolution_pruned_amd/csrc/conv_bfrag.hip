@@ -36,7 +36,7 @@
 //     operands are in flight early enough, which the software pipelining
 //     below arranges.
 //
-// Fragment order of B (K % 64 == 0, NO % 256 == 0), 16-byte pieces:
+// Fragment order of B (K % 64 == 0, NO % 128 == 0), 16-byte pieces:
 //   Bf[r][g][ks][nb][lane] = B(j, k, col) for e = 0..7 along k, with
 //   round r = c * TAPS + j (chunk c of 64 contracted channels, tap j),
 //   g = 64-channel group of the output, ks = k-step of 16, nb = 32-column
@@ -427,7 +427,7 @@ hipError_t launch_repack_batch(int count, const uint16_t* const* W, uint16_t* co
 }
 
 bool conv_bfrag_ok(int K, int NO, int taps) {
-    return taps == 9 && K > 0 && NO > 0 && K % BF_KC == 0 && NO % BF_BN == 0 &&
+    return taps == 9 && K > 0 && NO > 0 && K % BF_KC == 0 && NO % 128 == 0 &&
            static_cast<int64_t>(taps) * NO * K * 2 <= kMaxRange;
 }
 
@@ -445,19 +445,19 @@ hipError_t launch_repack_frag(const uint16_t* Wt, uint16_t* Bf, int Ci, int Co, 
 // Tile shape: the smallest tile (fewest tokens x channels per workgroup)
 // whose grid is one round of at most 256 tiles (one per compute unit of a
 // 256-CU part); at equal size, 256 channels (NB = 4: half the A reads per
-// MFMA).  Without such a tile, the largest one.  Depends on the arguments
-// only; every shape gives the same bits.
+// MFMA).  Without such a tile, the largest one the channel count allows.
+// Depends on the arguments only; every shape gives the same bits.
 struct BfragShape {
     int mb, nb;
 };
 static BfragShape bfrag_shape(int64_t n, int NO) {
-    static const BfragShape order[] = {{2, 2}, {3, 2}, {2, 4}, {3, 4}, {4, 4}};    // by tile size
+    static const BfragShape order[] = {{2, 2}, {3, 2}, {2, 4}, {4, 2}, {3, 4}, {4, 4}};    // by tile size
     for (const BfragShape& t : order) {
         if (NO % (64 * t.nb) != 0) continue;
         const int64_t tiles = ((n + 64 * t.mb - 1) / (64 * t.mb)) * (NO / (64 * t.nb));
         if (tiles <= BF_MAXTILES) return t;
     }
-    return {4, 4};
+    return NO % 256 == 0 ? BfragShape{4, 4} : BfragShape{4, 2};
 }
 
 hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t* Bf, const uint16_t* bias,
@@ -470,8 +470,10 @@ hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t
     const int ni = static_cast<int>(n);
     if (t.nb == 2 && t.mb == 2)
         hipLaunchKernelGGL((k_conv_bfrag<9, 2, 2>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
-    else if (t.nb == 2)
+    else if (t.nb == 2 && t.mb == 3)
         hipLaunchKernelGGL((k_conv_bfrag<9, 3, 2>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
+    else if (t.nb == 2)
+        hipLaunchKernelGGL((k_conv_bfrag<9, 4, 2>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
     else if (t.mb == 2)
         hipLaunchKernelGGL((k_conv_bfrag<9, 2, 4>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
     else if (t.mb == 3)

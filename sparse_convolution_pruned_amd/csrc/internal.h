@@ -114,7 +114,7 @@ hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, in
 // Weight operand in fragment order (conv_bfrag.hip): the MFMA kernel that
 // streams B from memory into registers.  conv_bfrag_ok: the shapes it is
 // built for (3 x 3, contracted channels a multiple of 64, produced channels
-// a multiple of 256).  The repack writes taps * Ci * Co bf16 in fragment
+// a multiple of 128).  The repack writes taps * Ci * Co bf16 in fragment
 // order for the forward (dx = false: K = Ci, NO = Co) or the input gradient
 // (dx = true: K = Co, NO = Ci, taps mirrored).
 bool conv_bfrag_ok(int K, int NO, int taps);

@@ -326,7 +326,8 @@ def test_repack_layers_validation(lib):
     assert f(2, arr(2), arr(2), need - 1, arr(2), need, 3, 256, 256, BF16, None) == ops.SV_ERR_WORKSPACE
     assert f(2, arr(2), arr(2), need, arr(2), need - 1, 3, 256, 256, BF16, None) == ops.SV_ERR_WORKSPACE
     assert f(2, arr(2), arr(2, 4100), need, None, 0, 3, 256, 256, BF16, None) == ops.SV_ERR_INVALID_ARG
-    assert f(2, arr(2), None, 0, arr(2), need, 3, 128, 128, BF16, None) == ops.SV_ERR_UNSUPPORTED
+    # input-gradient layout needs C_in a multiple of 128
+    assert f(2, arr(2), None, 0, arr(2), need, 3, 192, 192, BF16, None) == ops.SV_ERR_UNSUPPORTED
     assert f(2, arr(2), arr(2), need, arr(2), need, 4, 256, 256, BF16, None) == ops.SV_ERR_INVALID_ARG
 
 
@@ -362,22 +363,23 @@ def test_split_forms_validation(lib):
         ops.SV_ERR_UNSUPPORTED
     assert lib.sv_sparseconv2d_fwd_packed_k(FAKE, FAKE, None, None, FAKE, 8, 3, 64, 64, BF16, None) == \
         ops.SV_ERR_INVALID_ARG
-    # input gradient in fragment order: bf16 3 x 3 with C_out % 64 == 0 and C_in % 256 == 0
+    # input gradient in fragment order: bf16 3 x 3 with C_out % 64 == 0 and C_in % 128 == 0
     xneed = lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 256, 256, BF16)
     assert xneed == 9 * 256 * 256 * 2
     assert lib.sv_workspace_bytes(ops.SV_OP_DX, 22656, 256, 256, BF16) == xneed
-    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 128, 128, BF16) == 0
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 128, 128, BF16) == 9 * 128 * 128 * 2
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 192, 192, BF16) == 0
     assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 256, 256, F32) == 0
     assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 5, 256, 256, BF16) == 0
     assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, 22656, 256, 256, BF16, 0, FAKE, xneed - 1,
                                       None) == ops.SV_ERR_WORKSPACE
     assert lib.sv_repack_dx_k(FAKE, 3, 256, 256, BF16, FAKE, xneed - 1, None) == ops.SV_ERR_WORKSPACE
-    assert lib.sv_repack_dx_k(FAKE, 3, 128, 128, BF16, FAKE, xneed, None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_repack_dx_k(FAKE, 3, 192, 192, BF16, FAKE, xneed, None) == ops.SV_ERR_UNSUPPORTED
     assert lib.sv_repack_dx_k(FAKE, 3, 256, 256, F32, FAKE, xneed, None) == ops.SV_ERR_UNSUPPORTED
     assert lib.sv_repack_dx_k(None, 3, 256, 256, BF16, FAKE, xneed, None) == ops.SV_ERR_INVALID_ARG
     assert lib.sv_repack_dx_k(FAKE, 3, 256, 256, BF16, ctypes.c_void_p(4104), xneed, None) == \
         ops.SV_ERR_INVALID_ARG
-    assert lib.sv_sparseconv2d_bwd_dx_packed_k(FAKE, FAKE, FAKE, FAKE, 8, 3, 128, 128, BF16, None) == \
+    assert lib.sv_sparseconv2d_bwd_dx_packed_k(FAKE, FAKE, FAKE, FAKE, 8, 3, 192, 192, BF16, None) == \
         ops.SV_ERR_UNSUPPORTED
     assert lib.sv_sparseconv2d_bwd_dx_packed_k(FAKE, FAKE, None, FAKE, 8, 3, 256, 256, BF16, None) == \
         ops.SV_ERR_INVALID_ARG

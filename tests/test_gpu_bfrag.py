@@ -1,6 +1,6 @@
 """The matrix-core kernel that streams the weights in fragment order
 (bf16, 3 x 3, contracted channels a multiple of 64, produced channels a
-multiple of 256): forward and input gradient against the oracle in every
+multiple of 128): forward and input gradient against the oracle in every
 staging mode and tile shape, and bit for bit against the kernel that reads
 Wt directly (the input gradient without a workspace).  The split forms
 (repack, then the packed call) must equal the single calls bit for bit."""
@@ -39,8 +39,8 @@ def check_case(L, N, what):
     assert_close(host(dXf), O.bwd_dx(L.dY, N, L.Wt), "bf16", f"{what} dX")
 
 
-# (seed, T, H, W, keep, Ci, Co, shuffle); Co % 256 == 0 puts the forward on
-# the fragment kernel, Ci % 256 == 0 the input gradient.
+# (seed, T, H, W, keep, Ci, Co, shuffle); Co % 128 == 0 puts the forward on
+# the fragment kernel, Ci % 128 == 0 the input gradient.
 CASES = [
     (31, 3, 16, 16, 0.6, 256, 256, False),              # window mode, ragged last tile, MB = 2
     (32, 4, 16, 16, 0.5, 256, 256, True),               # shuffled packing: gather mode tap by tap
@@ -48,6 +48,8 @@ CASES = [
     (34, 5, 14, 14, [0, 1, 196, 0, 60], 512, 256, False),  # empty frames; C_in 512 (8 chunks)
     (35, 3, 16, 16, 0.4, 256, 512, False),              # several output-channel tiles
     (37, 90, 16, 16, 0.8, 256, 512, False),             # 18,450 tokens: 192 x 256 tiles forward, 192 x 128 dX
+    (38, 6, 14, 14, 0.5, 128, 128, False),              # 128 channels: 128 x 128 tiles
+    (39, 40, 14, 14, 0.7, 128, 256, True),              # 128 -> 256, gather mode
     (36, 2, 14, 14, 0.7, 64, 256, False),               # one 64-channel chunk in the forward
 ]
 
@@ -61,23 +63,26 @@ def test_fragment_kernel(case):
     check_case(L, N, f"{case}")
 
 
-# (frames, kept per frame, tokens x channels of the tile the host picks at
-# 256 channels: the smallest tile whose grid fits one round of 256
-# workgroups, 256-channel tiles first at equal size)
-TILES = [(60, 200, "128x128"), (100, 200, "192x128"), (140, 200, "128x256"), (200, 200, "192x256"),
-         (230, 230, "256x256")]
-TILE_RANGE = {"128x128": (0, 128 * 128), "192x128": (128 * 128, 128 * 192), "128x256": (128 * 192, 256 * 128),
-              "192x256": (256 * 128, 256 * 192), "256x256": (256 * 192, 10 ** 9)}
+# (frames, kept per frame, channels, tokens x channels of the tile the host
+# picks: the smallest tile whose grid fits one round of 256 workgroups,
+# 256-channel tiles first at equal size; without one, the largest tile)
+TILES = [(60, 200, 256, "128x128"), (100, 200, 256, "192x128"), (140, 200, 256, "128x256"),
+         (200, 200, 256, "192x256"), (230, 230, 256, "256x256"), (230, 240, 128, "256x128"),
+         (300, 240, 128, "256x128 x2 rounds")]
+TILE_RANGE = {(256, "128x128"): (0, 128 * 128), (256, "192x128"): (128 * 128, 128 * 192),
+              (256, "128x256"): (128 * 192, 256 * 128), (256, "192x256"): (256 * 128, 256 * 192),
+              (256, "256x256"): (256 * 192, 10 ** 9), (128, "256x128"): (256 * 192, 256 * 256),
+              (128, "256x128 x2 rounds"): (256 * 256, 10 ** 9)}
 
 
-@pytest.mark.parametrize("n_frames,keep,tile", TILES, ids=[t[2] for t in TILES])
-def test_tile_shapes(n_frames, keep, tile):
+@pytest.mark.parametrize("n_frames,keep,C,tile", TILES, ids=[t[3] for t in TILES])
+def test_tile_shapes(n_frames, keep, C, tile):
     """Token counts that select each tile shape."""
-    L = wl.make_random_case(40 + n_frames, n_frames, 16, 16, [keep] * n_frames, 256, 256, "bf16")
+    L = wl.make_random_case(40 + n_frames, n_frames, 16, 16, [keep] * n_frames, C, C, "bf16")
     n = L.n
-    lo, hi = TILE_RANGE[tile]
+    lo, hi = TILE_RANGE[(C, tile)]
     assert lo < n <= hi, n
-    print(f"n={n} frames={n_frames} tile={tile}", flush=True)
+    print(f"n={n} frames={n_frames} C={C} tile={tile}", flush=True)
     _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
     check_case(L, N, f"tile {tile}")
 
@@ -151,17 +156,17 @@ def test_chunk_driver_c256_bitwise():
     assert_close(host(dW), O.bwd_dw(L.X, N, L.dY), "bf16", "chunked dW")
 
 
-@pytest.mark.parametrize("C", [256, 128])
+@pytest.mark.parametrize("C", [256, 128, 192])
 def test_repack_layers_equals_single_repacks(C):
     """One launch for several layers writes exactly what the per-layer
-    repacks write (fragment order at C = 256; at C = 128 the forward's
-    per-tap layout and no input-gradient layout)."""
+    repacks write (fragment order at C = 256 and 128; at C = 192 the
+    forward's per-tap layout and no input-gradient layout)."""
     g = torch.Generator(device="cuda").manual_seed(3)
     Ws = [torch.randn(9, C, C, device="cuda", generator=g).to(bf) for _ in range(5)]
     nbytes = ops.sv_workspace_bytes(ops.SV_OP_FWD, 1000, C, C, bf)
     new = lambda: torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
     V1, V2 = [new() for _ in Ws], [new() for _ in Ws]
-    dx = C == 256
+    dx = C % 128 == 0
     P1 = [new() for _ in Ws] if dx else None
     P2 = [new() for _ in Ws] if dx else None
     ops.sv_repack_layers_k(Ws, V1, P1)
