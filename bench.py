@@ -233,11 +233,43 @@ class StagedRun:
                     raise ops.SvError(st, name)
             plan.append(f)
 
+        # Cross-stream ordering uses HIP events created without the system
+        # scope fence (and without timing): every producer and consumer here
+        # is a kernel on this device, so a device-scope release suffices.
+        # With torch's events each record cost the queue ~6 us (a
+        # system-scope cache write-back) before the next kernel could start.
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        flags = 0x2 | 0x20000000          # hipEventDisableTiming | hipEventDisableSystemFence
+        events = {}
+
+        def hev(ev):
+            if id(ev) not in events:
+                h = ctypes.c_void_p()
+                if hip.hipEventCreateWithFlags(ctypes.byref(h), flags) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                events[id(ev)] = h
+            return events[id(ev)]
+        self._hip_events = events
+
         def record(ev, stream):
-            plan.append(lambda: ev.record(stream))
+            e, s_ = hev(ev), hs[id(stream)]
+
+            def f():
+                if hip.hipEventRecord(e, s_) != 0:
+                    raise RuntimeError("hipEventRecord failed")
+            plan.append(f)
 
         def wait(stream, ev):
-            plan.append(lambda: stream.wait_event(ev))
+            e, s_ = hev(ev), hs[id(stream)]
+
+            def f():
+                if hip.hipStreamWaitEvent(s_, e, 0) != 0:
+                    raise RuntimeError("hipStreamWaitEvent failed")
+            plan.append(f)
 
         def index(s, stream):
             call("sv_build_index", P(self.coords[s]), P(self.offs[s]), S.T, S.H, S.W, self.ns[s], P(self.N[s]),

@@ -470,13 +470,18 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
 }
 
 // Events of a call, destroyed when the call returns (a recorded event is
-// released by the runtime once the device has passed it).
+// released by the runtime once the device has passed it).  They only order
+// kernels of this device on two streams, so they are made without the
+// system-scope fence: a device-scope release suffices, and the fence's
+// cache write-back held the next kernel on the recording stream for ~6 us.
 struct CallEvents {
     hipEvent_t ev[6] = {};
     int made = 0;
     bool make(int k) {
         for (; made < k; ++made)
-            if (hipEventCreateWithFlags(&ev[made], hipEventDisableTiming) != hipSuccess) return false;
+            if (hipEventCreateWithFlags(&ev[made], hipEventDisableTiming | hipEventDisableSystemFence) !=
+                hipSuccess)
+                return false;
         return true;
     }
     ~CallEvents() {
