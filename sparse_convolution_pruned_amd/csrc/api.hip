@@ -73,9 +73,9 @@ sv_status run_fwd_prepared(bool mfma, const void* X, const int32_t* N, const voi
                            const void* bias, void* Y, int64_t n, int32_t Ci, int32_t Co, int taps,
                            sv_dtype dt, hipStream_t s, const void* R = nullptr) {
     if (n == 0) return SV_OK;
-    if (mfma && conv_bfrag_ok(Ci, Co, taps)) {
-        // V holds the weights in fragment order (launch_repack_fwd)
-        if (R) return SV_ERR_UNSUPPORTED;
+    if (mfma && !R && conv_bfrag_ok(Ci, Co, taps)) {
+        // V holds the weights in fragment order (launch_repack_fwd); a call
+        // with a residual has them in the per-tap layout for k_conv_mfma
         return hip_status(launch_conv_bfrag(static_cast<const uint16_t*>(X), N, static_cast<const uint16_t*>(V),
                                             static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(Y), n, Ci, Co,
                                             taps, s));
@@ -934,8 +934,9 @@ sv_status adapter_layer_fwd(const void* X, const int32_t* N, const void* Wt, con
     sv_status st = choose(kernel, dt, false, Ci, Co, n, taps, &mfma);
     if (st != SV_OK) return st;
     if (mfma) {
+        // with a residual the layer runs on k_conv_mfma: its per-tap layout
         st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(V), Ci, Co,
-                                          taps, s));
+                                          taps, s, R == nullptr));
         if (st != SV_OK) return st;
     }
     return run_fwd_prepared(mfma, X, N, Wt, V, bias, Y, n, Ci, Co, taps, dt, s, R);

@@ -78,8 +78,10 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
     // ascending flat order inside a frame, every neighbour of token k lies
     // within (W + 1) packed positions of k, so for grids up to 31 wide the
     // tile's rows fall inside [k0 - 32, k0 + BM + 32).  Tiles whose rows do
-    // not (other packings, wider grids) switch to gather mode.
-    constexpr int WIN = BM + 2 * BF_HALO;
+    // not (other packings, wider grids) switch to gather mode.  With one tap
+    // (1 x 1) the rows are the tile's own: no halo.
+    constexpr int HALO = TAPS == 1 ? 0 : BF_HALO;
+    constexpr int WIN = BM + 2 * HALO;
     constexpr int ZROW = WIN;                       // all-zero row: target of -1 entries
     constexpr int WB = (WIN + 1) * BF_ROWB;         // bytes per window buffer
     // Two buffers as two arrays, used through compile-time choices only: the
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
     const int n0 = (logical % tilesN) * BN;
     const int nchunks = K / BF_KC;
     const int R = nchunks * TAPS;
-    const int wlo = max(0, k0 - BF_HALO);
+    const int wlo = max(0, k0 - HALO);
 
     const rsrc_t rA = make_rsrc(A, static_cast<uint32_t>(n) * K * 2);
     const rsrc_t rB = make_rsrc(Bf, static_cast<uint32_t>(TAPS) * NO * K * 2);
@@ -426,8 +428,11 @@ hipError_t launch_repack_batch(int count, const uint16_t* const* W, uint16_t* co
     return hipGetLastError();
 }
 
+// 1 x 1 only with at least 8 rounds (512 contracted channels): with fewer,
+// prologue and epilogue dominate and k_conv_mfma's two workgroups per CU
+// overlap them better (c3a at 1 x 1: forward 14.4 against 18.9 us).
 bool conv_bfrag_ok(int K, int NO, int taps) {
-    return taps == 9 && K > 0 && NO > 0 && K % BF_KC == 0 && NO % 128 == 0 &&
+    return (taps == 9 || (taps == 1 && K >= 512)) && K > 0 && NO > 0 && K % BF_KC == 0 && NO % 128 == 0 &&
            static_cast<int64_t>(taps) * NO * K * 2 <= kMaxRange;
 }
 
@@ -460,26 +465,35 @@ static BfragShape bfrag_shape(int64_t n, int NO) {
     return NO % 256 == 0 ? BfragShape{4, 4} : BfragShape{4, 2};
 }
 
+template <int TAPS>
+static void launch_bfrag_taps(BfragShape t, dim3 grid, hipStream_t stream, const uint16_t* A, const int32_t* N,
+                              const uint16_t* Bf, const uint16_t* bias, uint16_t* out, int n, int K, int NO) {
+    const dim3 block(64 * BF_WAVES);
+    if (t.nb == 2 && t.mb == 2)
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 2, 2>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+    else if (t.nb == 2 && t.mb == 3)
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 3, 2>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+    else if (t.nb == 2)
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 4, 2>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+    else if (t.mb == 2)
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 2, 4>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+    else if (t.mb == 3)
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 3, 4>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+    else
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 4, 4>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+}
+
 hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t* Bf, const uint16_t* bias,
                              uint16_t* out, int64_t n, int K, int NO, int taps, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     if (!conv_bfrag_ok(K, NO, taps)) return hipErrorInvalidValue;
     const BfragShape t = bfrag_shape(n, NO);
     const dim3 grid(static_cast<unsigned>(((n + 64 * t.mb - 1) / (64 * t.mb)) * (NO / (64 * t.nb))));
-    const dim3 block(64 * BF_WAVES);
     const int ni = static_cast<int>(n);
-    if (t.nb == 2 && t.mb == 2)
-        hipLaunchKernelGGL((k_conv_bfrag<9, 2, 2>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
-    else if (t.nb == 2 && t.mb == 3)
-        hipLaunchKernelGGL((k_conv_bfrag<9, 3, 2>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
-    else if (t.nb == 2)
-        hipLaunchKernelGGL((k_conv_bfrag<9, 4, 2>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
-    else if (t.mb == 2)
-        hipLaunchKernelGGL((k_conv_bfrag<9, 2, 4>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
-    else if (t.mb == 3)
-        hipLaunchKernelGGL((k_conv_bfrag<9, 3, 4>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
+    if (taps == 1)
+        launch_bfrag_taps<1>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO);
     else
-        hipLaunchKernelGGL((k_conv_bfrag<9, 4, 4>), grid, block, 0, stream, A, N, Bf, bias, out, ni, K, NO);
+        launch_bfrag_taps<9>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO);
     return hipGetLastError();
 }
 

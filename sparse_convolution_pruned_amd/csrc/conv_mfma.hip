@@ -456,9 +456,10 @@ size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps) {
     return (static_cast<size_t>(taps) * Ci * Co * sizeof(uint16_t) + 255) & ~static_cast<size_t>(255);
 }
 
-hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream) {
+hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream,
+                             bool allow_frag) {
     // shapes the fragment-order kernel takes get its layout (same size)
-    if (conv_bfrag_ok(Ci, Co, taps)) return launch_repack_frag(Wt, V, Ci, Co, taps, false, stream);
+    if (allow_frag && conv_bfrag_ok(Ci, Co, taps)) return launch_repack_frag(Wt, V, Ci, Co, taps, false, stream);
     dim3 grid((Co + 31) / 32, (Ci + 31) / 32, taps);
     hipLaunchKernelGGL(k_repack_fwd, grid, dim3(256), 0, stream, Wt, V, Ci, Co);
     return hipGetLastError();

@@ -110,11 +110,14 @@ hipError_t launch_conv_mfma_packed(const uint16_t* A, const int32_t* N, const ui
 hipError_t launch_conv_mfma_pair(const uint16_t* A1, const uint16_t* B1, const uint16_t* bias1, uint16_t* out1,
                                  int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
                                  int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream);
-hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream);
+// allow_frag = false keeps the per-tap layout even where the fragment-order
+// kernel could run (a call with a residual, which only k_conv_mfma takes).
+hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, int taps, hipStream_t stream,
+                             bool allow_frag = true);
 // Weight operand in fragment order (conv_bfrag.hip): the MFMA kernel that
 // streams B from memory into registers.  conv_bfrag_ok: the shapes it is
-// built for (3 x 3, contracted channels a multiple of 64, produced channels
-// a multiple of 128).  The repack writes taps * Ci * Co bf16 in fragment
+// built for (3 x 3 or 1 x 1, contracted channels a multiple of 64, produced
+// channels a multiple of 128).  The repack writes taps * Ci * Co bf16 in fragment
 // order for the forward (dx = false: K = Ci, NO = Co) or the input gradient
 // (dx = true: K = Co, NO = Ci, taps mirrored).
 bool conv_bfrag_ok(int K, int NO, int taps);

@@ -179,3 +179,20 @@ def test_repack_layers_equals_single_repacks(C):
         assert torch.equal(V1[i], V2[i]), f"forward layout of layer {i}"
         if dx:
             assert torch.equal(P1[i], P2[i]), f"input-gradient layout of layer {i}"
+
+
+@pytest.mark.parametrize("Ci,Co", [(512, 256), (1024, 128), (256, 512)])
+def test_one_by_one(Ci, Co):
+    """1 x 1 layers with at least 512 contracted channels run on the
+    fragment kernel (no halo: the window is the tile's own rows); forward
+    and input gradient against the oracle."""
+    L = wl.make_random_case(61, 5, 14, 14, 0.6, Ci, Co, "bf16", ksize=1)
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K=1)
+    print(f"n={L.n} Ci={Ci} Co={Co}", flush=True)
+    X, Wt, b, dY = dev(L.X, bf), dev(L.Wt, bf), dev(L.b, bf), dev(L.dY, bf)
+    Nd = dev(N)
+    Y = ops.sparseconv2d_fwd(X, Nd, Wt, b, "mfma")
+    dX = ops.sparseconv2d_bwd_dx(dY, Nd, Wt, "mfma")
+    torch.cuda.synchronize()
+    assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), "bf16", f"1x1 {Ci}->{Co} Y")
+    assert_close(host(dX), O.bwd_dx(L.dY, N, L.Wt), "bf16", f"1x1 {Ci}->{Co} dX")
