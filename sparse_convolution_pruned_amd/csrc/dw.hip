@@ -105,7 +105,12 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
     const int kbeg = slice * slice_tokens;
     const int cnt = max(0, min(n - kbeg, slice_tokens));
     const int steps = (cnt + DW_TK - 1) / DW_TK;
-    const bool do_db = dbout != nullptr && grp == min(1, groups - 1);
+    // db: the 16 eight-channel chunks of the tile's 128 output channels are
+    // dealt out over the groups (chunk c to group c mod groups), and within
+    // a workgroup chunk number w of its own to wave w, lane = token (with one
+    // group, a second chunk w + 8).  Summing all of db in one group made its
+    // two workgroups per slice the last to finish.
+    const int nch_db = dbout != nullptr ? (16 - grp + groups - 1) / groups : 0;   // chunks of this group
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,9 +191,14 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
         for (int b = 0; b < 2; ++b) acc[t][b] = zero16();
     // db: thread = (16-byte chunk tid & 15 of the 128 output channels,
     // tokens tid >> 4 and 32 + (tid >> 4))
-    float dbacc[8];
+    const int wv = tid >> 6;                  // the wave, as a lane value (for the db chunk tests)
+    const bool db0 = wv < nch_db, db1 = wv + 8 < nch_db;
+    const int dbc0 = grp + wv * groups, dbc1 = grp + (wv + 8) * groups;     // chunk indices (when live)
+    float dbacc[2][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dbacc[e] = 0.f;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dbacc[u][e] = 0.f;
 
     auto stage = [&](int s, char* buf) {
         int4 e0, e1;
@@ -255,18 +265,20 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) b[nb] = bn[nb];
         }
-        if (do_db) {
-            const int c = tid & 15, q = tid >> 4;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint4 v = *reinterpret_cast<const uint4*>(yb + tok_addr(q + 32 * u) + c * 16);
+        if (db0) {
+            // this lane's token of the step; tokens past the slice were
+            // staged as zeros
+            auto add8 = [&](int c, float* acc8) __attribute__((always_inline)) {
+                const uint4 v = *reinterpret_cast<const uint4*>(yb + tok_addr(lane) + c * 16);
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    dbacc[2 * h] += bf16_to_f32(static_cast<uint16_t>(w[h] & 0xffffu));
-                    dbacc[2 * h + 1] += bf16_to_f32(static_cast<uint16_t>(w[h] >> 16));
+                    acc8[2 * h] += bf16_to_f32(static_cast<uint16_t>(w[h] & 0xffffu));
+                    acc8[2 * h + 1] += bf16_to_f32(static_cast<uint16_t>(w[h] >> 16));
                 }
-            }
+            };
+            add8(dbc0, dbacc[0]);
+            if (db1) add8(dbc1, dbacc[1]);
         }
     };
 
@@ -331,19 +343,26 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
                     *d = (direct && accumulate) ? *d + v : v;
                 }
     }
-    if (do_db) {
-        // 32 threads share each 8-channel chunk; added in thread order
+    if (nch_db > 0) {
+        // each chunk's 64 lanes added in lane order, per channel
         float* red = reinterpret_cast<float*>(sbuf0);
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[e * DW_THREADS + tid] = dbacc[e];
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[(u * 8 + e) * DW_THREADS + tid] = dbacc[u][e];
         __syncthreads();
-        if (tid < DW_BO) {
-            const int c = tid >> 3, e = tid & 7;
-            float v = 0.f;
-            for (int r = 0; r < DW_THREADS / 16; ++r) v += red[e * DW_THREADS + r * 16 + c];
-            float* d = dbout + (direct ? 0 : static_cast<int64_t>(slice) * Co) + o0 + tid;
-            *d = (direct && accumulate) ? *d + v : v;
+        // thread (u, chunk slot w, channel e) = tid: u = tid >> 6, w = (tid >> 3) & 7, e = tid & 7
+        if (tid < 128) {
+            const int u = tid >> 6, w = (tid >> 3) & 7, e = tid & 7;
+            const int k = w + 8 * u;                         // the group's chunk number
+            if (k < nch_db) {
+                const int c = grp + k * groups;
+                float v = 0.f;
+                for (int l = 0; l < 64; ++l) v += red[(u * 8 + e) * DW_THREADS + w * 64 + l];
+                float* d = dbout + (direct ? 0 : static_cast<int64_t>(slice) * Co) + o0 + c * 8 + e;
+                *d = (direct && accumulate) ? *d + v : v;
+            }
         }
     }
 }
