@@ -609,12 +609,14 @@ def measure_layer(key, kernel="auto", ksize=3, steps=20, warmup=3, dw_stream="si
     fl = len(passes) * fl_pass
     # gather model per conv pass: every neighbour row read from memory, no reuse
     gather_bytes = n * (taps * es * Ci + es * Co + 4 * taps)
-    peak = PEAK_BF16_TFLOPS if L.dtype == "bf16" else PEAK_FP32_VALU_TFLOPS
+    # fp32 data, or the VALU kernel on bf16 data: fp32 FMAs on the vector ALUs
+    on_valu = kernel == "valu" or L.dtype != "bf16"
+    peak = PEAK_FP32_VALU_TFLOPS if on_valu else PEAK_BF16_TFLOPS
     out = {"name": cfg["name"], "kernel": kernel, "ksize": K, "n": n, "dtype": L.dtype,
            "valid_tap_fraction": None if chunked else round(float((N >= 0).sum().item()) / max(N.numel(), 1), 4),
            "ms_per_step": round(sec * 1e3, 4), "passes": list(passes),
            "tflops": round(fl / sec / 1e12, 3),
-           "roofline_mfma" if L.dtype == "bf16" else "roofline_fp32_vector":
+           "roofline_fp32_vector" if on_valu else "roofline_mfma":
                {"peak_tflops": peak, "frac": round(fl / sec / 1e12 / peak, 4)},
            "roofline_hbm_gather_model": {"gbps": round(len(passes) * gather_bytes / sec / 1e9, 1),
                                          "frac": round(len(passes) * gather_bytes / sec / 1e9 / PEAK_HBM_GBPS, 4)},

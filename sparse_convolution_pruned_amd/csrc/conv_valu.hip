@@ -6,23 +6,62 @@
 // Any odd K x K neighbourhood: `taps` = K * K columns of N, weights
 // [taps][C_in][C_out], and tap taps-1-j mirrors tap j.
 //
-// Forward / input gradient: one workgroup per 64 tokens x 64 output channels.
-// The tile's 64 x taps slice of N is read once into LDS; then, tap by tap, 16
-// channels at a time, the gathered neighbour rows and the matching weight
-// slice are staged in LDS (as fp32) and every thread accumulates a 4 x 4 block
-// of outputs with FMAs.  A tap whose entry is -1 stages zeros (zero padding).
-// An optional residual R [n][channels produced] is added before the store.
+// Forward / input gradient: one workgroup per 128 tokens x 64 output
+// channels.  The tile's 128 x taps slice of N is read once into LDS; then, tap
+// by tap, 16 channels at a time, the gathered neighbour rows and the matching
+// weight slice are staged in LDS (as fp32) and every thread accumulates an
+// 8 x 4 block of outputs with FMAs.  A tap whose entry is -1 stages zeros
+// (zero padding).  An optional residual R [n][channels produced] is added
+// before the store.
 //
 // Weight gradient: one workgroup per (tap, 64 input channels, 64 output
 // channels, token slice); 16 tokens at a time the gathered X rows and the dY
 // rows are staged in LDS and each thread accumulates a 4 x 4 block of dW.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace svc {
 
+// Weight-gradient tile.
 constexpr int VT_M = 64, VT_N = 64, VT_K = 16;
 
-template <typename T, bool DX>
+// Four consecutive elements from global memory as fp32 (VEC: one 16- or
+// 8-byte load; the caller checks alignment and range).
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    static __device__ __forceinline__ void load(const float* p, float* v) {
+        const float4 x = *reinterpret_cast<const float4*>(p);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
+};
+template <> struct Vec4<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        v[0] = bf16_to_f32(static_cast<uint16_t>(x.x & 0xffffu));
+        v[1] = bf16_to_f32(static_cast<uint16_t>(x.x >> 16));
+        v[2] = bf16_to_f32(static_cast<uint16_t>(x.y & 0xffffu));
+        v[3] = bf16_to_f32(static_cast<uint16_t>(x.y >> 16));
+    }
+};
+
+// Forward / input-gradient tile: FT_M tokens x FT_N produced channels per
+// workgroup of 256 threads, FT_K contracted channels per round (one tap j, one
+// chunk of channels c0).  Thread (ty, tx) owns the 8 x 4 outputs rows
+// 8 ty .. 8 ty + 7, columns 4 tx .. 4 tx + 3, read from LDS as 128-bit
+// vectors: 12 floats per 32 FMAs (a 4 x 4 block reads 8 per 16, and then the
+// LDS rather than the FMA pipes sets the pace).
+//
+// Rounds are software-pipelined over two LDS buffers: round r + 1's elements
+// are loaded into registers while round r's FMAs run, then written to the
+// other buffer; one barrier per round.  VEC (channel counts multiples of 4,
+// A and the weights aligned to 4 elements): each thread stages four
+// consecutive channels with one 16- or 8-byte load.  Every output sums its
+// terms in the same order either way: taps, then chunks, then channels.
+constexpr int FT_M = 128, FT_N = 64, FT_K = 16;
+constexpr int FT_PA = FT_M + 4, FT_PB = FT_N + 4;   // padded LDS rows, multiples of 4 floats
+
+template <typename T, bool DX, bool VEC>
 __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ A,
                                                    const int32_t* __restrict__ Nt,
                                                    const T* __restrict__ Wt,
@@ -32,111 +71,173 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ A,
     // K: channels contracted per tap; NO: channels produced.
     const int K = DX ? Co : Ci;
     const int NO = DX ? Ci : Co;
-    __shared__ float sA[VT_K][VT_M + 4];
-    __shared__ float sB[VT_K][VT_N + 4];
-    extern __shared__ int sN[];              // [VT_M][taps], dynamic
+    __shared__ __align__(16) float sA[2][FT_K][FT_PA];
+    __shared__ __align__(16) float sB[2][FT_K][FT_PB];
+    extern __shared__ int sN[];              // [FT_M][taps], dynamic
 
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * VT_M;
-    const int n0 = blockIdx.y * VT_N;
+    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * FT_M;
+    const int n0 = blockIdx.y * FT_N;
 
-    for (int e = tid; e < VT_M * taps; e += 256) {
+    for (int e = tid; e < FT_M * taps; e += 256) {
         const int64_t k = k0 + e / taps;
         sN[e] = (k < n) ? clamp_index(Nt[k * taps + e % taps], n) : -1;
     }
-    float acc[4][4];
+    float acc[8][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
     __syncthreads();
 
-    for (int j = 0; j < taps; ++j) {
+    const int nck = (K + FT_K - 1) / FT_K;
+    const int rounds = taps * nck;
+    // Staged elements of one round, as fp32: A (FT_M x FT_K) 8 per thread,
+    // B (FT_K x FT_N) 4 per thread.
+    float va[8], vb[4];
+    auto fetch = [&](int r) {
+        const int j = r / nck, c0 = (r - j * nck) * FT_K;
         // Input gradient: the row gathered through tap j meets weight tap
         // taps-1-j.
         const int jt = DX ? taps - 1 - j : j;
         const T* __restrict__ Wj = Wt + static_cast<int64_t>(jt) * Ci * Co;
-        for (int c0 = 0; c0 < K; c0 += VT_K) {
-            for (int e = tid; e < VT_M * VT_K; e += 256) {
-                const int r = e / VT_K, kk = e % VT_K;
-                const int m = sN[r * taps + j];
-                float v = 0.f;
-                if (m >= 0 && c0 + kk < K) v = Elem<T>::load(A + static_cast<int64_t>(m) * K + c0 + kk);
-                sA[kk][r] = v;
+        if (VEC) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {   // A: row tid / 4 + 64 i, channels c0 + 4 (tid % 4) ..
+                const int row = (tid >> 2) + 64 * i, kq = (tid & 3) * 4;
+                const int m = sN[row * taps + j];
+                if (m >= 0 && c0 + kq < K) Vec4<T>::load(A + static_cast<int64_t>(m) * K + c0 + kq, va + 4 * i);
+                else va[4 * i] = va[4 * i + 1] = va[4 * i + 2] = va[4 * i + 3] = 0.f;
             }
-            for (int e = tid; e < VT_K * VT_N; e += 256) {
-                float v = 0.f;
-                if (!DX) {
-                    const int kk = e / VT_N, nn = e % VT_N;
-                    if (c0 + kk < K && n0 + nn < NO)
-                        v = Elem<T>::load(Wj + static_cast<int64_t>(c0 + kk) * Co + n0 + nn);
-                    sB[kk][nn] = v;
-                } else {
-                    // B(o, i) = Wt[taps-1-j][i][o]: read along o (contiguous).
-                    const int nn = e / VT_K, kk = e % VT_K;
-                    if (c0 + kk < K && n0 + nn < NO)
-                        v = Elem<T>::load(Wj + static_cast<int64_t>(n0 + nn) * Co + c0 + kk);
-                    sB[kk][nn] = v;
+            if (!DX) {   // B(kk, c) = Wj[c0 + kk][n0 + c]: kk = tid / 16, c = 4 (tid % 16) ..
+                const int kk = tid >> 4, cq = (tid & 15) * 4;
+                if (c0 + kk < K && n0 + cq < NO) Vec4<T>::load(Wj + static_cast<int64_t>(c0 + kk) * Co + n0 + cq, vb);
+                else vb[0] = vb[1] = vb[2] = vb[3] = 0.f;
+            } else {     // B(kk, c) = Wt[taps-1-j][n0 + c][c0 + kk]: c = tid / 4, kk = 4 (tid % 4) ..
+                const int c = tid >> 2, kq = (tid & 3) * 4;
+                if (n0 + c < NO && c0 + kq < K) Vec4<T>::load(Wj + static_cast<int64_t>(n0 + c) * Co + c0 + kq, vb);
+                else vb[0] = vb[1] = vb[2] = vb[3] = 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {   // A: row tid / 16 + 16 i, channel c0 + tid % 16
+                const int row = (tid >> 4) + 16 * i, kk = tid & 15;
+                const int m = sN[row * taps + j];
+                va[i] = (m >= 0 && c0 + kk < K) ? Elem<T>::load(A + static_cast<int64_t>(m) * K + c0 + kk) : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (!DX) {   // kk = tid / 64 + 4 i, c = tid % 64
+                    const int kk = (tid >> 6) + 4 * i, c = tid & 63;
+                    vb[i] = (c0 + kk < K && n0 + c < NO)
+                                ? Elem<T>::load(Wj + static_cast<int64_t>(c0 + kk) * Co + n0 + c) : 0.f;
+                } else {     // c = tid / 16 + 16 i, kk = tid % 16 (read along Co, contiguous)
+                    const int c = (tid >> 4) + 16 * i, kk = tid & 15;
+                    vb[i] = (c0 + kk < K && n0 + c < NO)
+                                ? Elem<T>::load(Wj + static_cast<int64_t>(n0 + c) * Co + c0 + kk) : 0.f;
                 }
             }
-            __syncthreads();
-#pragma unroll
-            for (int kk = 0; kk < VT_K; ++kk) {
-                float a[4], b[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    a[q] = sA[kk][ty + 16 * q];
-                    b[q] = sB[kk][tx + 16 * q];
-                }
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[p][q] = fmaf(a[p], b[q], acc[p][q]);
-            }
-            __syncthreads();
         }
-    }
+    };
+    auto commit = [&](int buf) {
+        if (VEC) {
+            const int kq = (tid & 3) * 4;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int64_t row = k0 + ty + 16 * p;
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sA[buf][kq + q][(tid >> 2) + 64 * i] = va[4 * i + q];
+            if (!DX) {
+                *reinterpret_cast<float4*>(&sB[buf][tid >> 4][(tid & 15) * 4]) = make_float4(vb[0], vb[1], vb[2], vb[3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sB[buf][kq + q][tid >> 2] = vb[q];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sA[buf][tid & 15][(tid >> 4) + 16 * i] = va[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (!DX) sB[buf][(tid >> 6) + 4 * i][tid & 63] = vb[i];
+                else sB[buf][tid & 15][(tid >> 4) + 16 * i] = vb[i];
+            }
+        }
+    };
+
+    fetch(0);
+    commit(0);
+    __syncthreads();
+    for (int r = 0; r < rounds; ++r) {
+        const int cur = r & 1;
+        const bool more = r + 1 < rounds;
+        if (more) fetch(r + 1);
+        const float* __restrict__ pa = &sA[cur][0][8 * ty];
+        const float* __restrict__ pb = &sB[cur][0][4 * tx];
+        // Unrolled by 2 only: fully unrolled, the compiler issued all 48
+        // LDS reads of the round ahead of the FMAs (~250 VGPRs, one wave per
+        // SIMD).
+#pragma unroll 2
+        for (int kk = 0; kk < FT_K; ++kk) {
+            const float4 a0 = *reinterpret_cast<const float4*>(pa + kk * FT_PA);
+            const float4 a1 = *reinterpret_cast<const float4*>(pa + kk * FT_PA + 4);
+            const float4 b = *reinterpret_cast<const float4*>(pb + kk * FT_PB);
+            const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[p][q] = fmaf(av[p], bv[q], acc[p][q]);
+        }
+        if (more) commit(cur ^ 1);
+        __syncthreads();
+    }
+
+    const int col = n0 + 4 * tx;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t row = k0 + 8 * ty + p;
         if (row >= n) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int col = n0 + tx + 16 * q;
-            if (col >= NO) continue;
+            if (col + q >= NO) continue;
             float v = acc[p][q];
-            if (!DX && bias) v += Elem<T>::load(bias + col);
-            if (R) v += Elem<T>::load(R + row * NO + col);
-            Elem<T>::store(out + row * NO + col, v);
+            if (!DX && bias) v += Elem<T>::load(bias + col + q);
+            if (R) v += Elem<T>::load(R + row * NO + col + q);
+            Elem<T>::store(out + row * NO + col + q, v);
         }
     }
+}
+
+template <typename T>
+static void launch_valu_typed(bool dx, bool vec, dim3 grid, size_t lds, hipStream_t stream, const T* A,
+                              const int32_t* N, const T* Wt, const T* bias, const T* R, T* out, int n, int Ci,
+                              int Co, int taps) {
+    const dim3 block(256);
+    if (dx && vec) hipLaunchKernelGGL((k_conv_valu<T, true, true>), grid, block, lds, stream, A, N, Wt, bias, R, out, n, Ci, Co, taps);
+    else if (dx) hipLaunchKernelGGL((k_conv_valu<T, true, false>), grid, block, lds, stream, A, N, Wt, bias, R, out, n, Ci, Co, taps);
+    else if (vec) hipLaunchKernelGGL((k_conv_valu<T, false, true>), grid, block, lds, stream, A, N, Wt, bias, R, out, n, Ci, Co, taps);
+    else hipLaunchKernelGGL((k_conv_valu<T, false, false>), grid, block, lds, stream, A, N, Wt, bias, R, out, n, Ci, Co, taps);
 }
 
 hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N, const void* Wt,
                             const void* bias, const void* R, void* out, int64_t n, int Ci, int Co, int taps,
                             hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    const size_t lds = static_cast<size_t>(VT_M) * taps * sizeof(int);
+    const size_t lds = static_cast<size_t>(FT_M) * taps * sizeof(int);
     const int NO = dx ? Ci : Co;
-    dim3 grid(static_cast<unsigned>((n + VT_M - 1) / VT_M), static_cast<unsigned>((NO + VT_N - 1) / VT_N));
+    dim3 grid(static_cast<unsigned>((n + FT_M - 1) / FT_M), static_cast<unsigned>((NO + FT_N - 1) / FT_N));
     const int nn = static_cast<int>(n);
-    if (bf16) {
-        auto a = static_cast<const uint16_t*>(A);
-        auto w = static_cast<const uint16_t*>(Wt);
-        auto b = static_cast<const uint16_t*>(bias);
-        auto r = static_cast<const uint16_t*>(R);
-        auto o = static_cast<uint16_t*>(out);
-        if (dx) hipLaunchKernelGGL((k_conv_valu<uint16_t, true>), grid, dim3(256), lds, stream, a, N, w, b, r, o, nn, Ci, Co, taps);
-        else hipLaunchKernelGGL((k_conv_valu<uint16_t, false>), grid, dim3(256), lds, stream, a, N, w, b, r, o, nn, Ci, Co, taps);
-    } else {
-        auto a = static_cast<const float*>(A);
-        auto w = static_cast<const float*>(Wt);
-        auto b = static_cast<const float*>(bias);
-        auto r = static_cast<const float*>(R);
-        auto o = static_cast<float*>(out);
-        if (dx) hipLaunchKernelGGL((k_conv_valu<float, true>), grid, dim3(256), lds, stream, a, N, w, b, r, o, nn, Ci, Co, taps);
-        else hipLaunchKernelGGL((k_conv_valu<float, false>), grid, dim3(256), lds, stream, a, N, w, b, r, o, nn, Ci, Co, taps);
-    }
+    // four-channel loads: channel counts multiples of 4 and A, Wt aligned to 4 elements
+    const size_t es = bf16 ? 2 : 4;
+    const bool vec = Ci % 4 == 0 && Co % 4 == 0 && reinterpret_cast<uintptr_t>(A) % (4 * es) == 0 &&
+                     reinterpret_cast<uintptr_t>(Wt) % (4 * es) == 0;
+    if (bf16)
+        launch_valu_typed(dx, vec, grid, lds, stream, static_cast<const uint16_t*>(A), N,
+                          static_cast<const uint16_t*>(Wt), static_cast<const uint16_t*>(bias),
+                          static_cast<const uint16_t*>(R), static_cast<uint16_t*>(out), nn, Ci, Co, taps);
+    else
+        launch_valu_typed(dx, vec, grid, lds, stream, static_cast<const float*>(A), N, static_cast<const float*>(Wt),
+                          static_cast<const float*>(bias), static_cast<const float*>(R), static_cast<float*>(out),
+                          nn, Ci, Co, taps);
     return hipGetLastError();
 }
 

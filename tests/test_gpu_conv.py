@@ -53,6 +53,35 @@ def test_f32_valu(case):
     check_against_oracle(L, N, "valu", what=f"f32 {case}")
 
 
+def dev_at(a, dtype, offset):
+    """`a` on the GPU, `offset` elements into its storage (contiguous)."""
+    src = dev(a, dtype).reshape(-1)
+    buf = torch.zeros(src.numel() + offset, dtype=dtype, device="cuda")
+    buf[offset:].copy_(src)
+    return buf[offset:].view(a.shape)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_valu_vector_loads(dt, offset):
+    # Channel counts multiples of 4 over three 128-token tiles with a ragged
+    # tail and a ragged channel tile: four-channel loads when X, dY and the
+    # weights are aligned (offset 0), element-wise staging when they are not
+    # (offset 1); both against the oracle.
+    L = wl.make_random_case(7, 3, 14, 14, 0.45, 48, 80, dt, shuffle=True)
+    assert 256 < L.n < 384
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
+    t = tdtype(dt)
+    X, Wt, dY, b = (dev_at(a, t, offset) for a in (L.X, L.Wt, L.dY, L.b))
+    assert (X.data_ptr() % 8 == 0) == (offset == 0)
+    Nd = dev(N)
+    Y = ops.sparseconv2d_fwd(X, Nd, Wt, b, "valu")
+    dX = ops.sparseconv2d_bwd_dx(dY, Nd, Wt, "valu")
+    torch.cuda.synchronize()
+    assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), dt, f"Y offset {offset}")
+    assert_close(host(dX), O.bwd_dx(L.dY, N, L.Wt), dt, f"dX offset {offset}")
+
+
 BF16_CASES = [
     # MFMA-compatible channel counts (C_in % 32, C_out % 16 and the reverse for dX)
     (11, 3, 14, 14, 0.4, 128, 128, False),
