@@ -111,15 +111,24 @@ sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int
     return hip_status(launch_conv_valu(dt == SV_BF16, true, dY, N, Wt, nullptr, R, dX, n, Ci, Co, taps, s));
 }
 
-// Forward and input gradient of one chunk, both on the MFMA kernel, in one
-// paired launch (the forward from the repacked weights V, the input
-// gradient from Wt); the two problems' tiles fill the chip together.
+// Forward and input gradient of one chunk, both on the MFMA kernels, in one
+// paired launch where one kernel takes both shapes: k_conv_bfrag with V and
+// P in fragment order, else k_conv_mfma (the forward from the repacked
+// weights V, the input gradient from Wt).  The two problems' tiles fill the
+// chip together.
 sv_status run_fwd_dx_pair(const void* X, const void* dY, const int32_t* N, const void* Wt, const void* V,
                           const void* P, const void* bias, void* Y, void* dX, int64_t n, int32_t Ci, int32_t Co,
                           int taps, hipStream_t s) {
     if (n == 0) return SV_OK;
+    if (P && conv_bfrag_ok(Ci, Co, taps) && conv_bfrag_ok(Co, Ci, taps))
+        // both passes on the fragment kernel (V and P in fragment order)
+        return hip_status(launch_conv_bfrag_pair(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(V),
+                                                 static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(Y), Ci,
+                                                 Co, static_cast<const uint16_t*>(dY),
+                                                 static_cast<const uint16_t*>(P), static_cast<uint16_t*>(dX), Co,
+                                                 Ci, N, n, taps, s));
     if (conv_bfrag_ok(Ci, Co, taps) || conv_bfrag_ok(Co, Ci, taps)) {
-        // fragment-order weights: each pass runs on its own launch
+        // fragment-order weights for one of the passes: each runs on its own launch
         sv_status st = run_fwd_prepared(true, X, N, Wt, V, bias, Y, n, Ci, Co, taps, SV_BF16, s);
         if (st != SV_OK) return st;
         return run_dx(dY, N, Wt, dX, n, Ci, Co, taps, SV_BF16, SV_KERNEL_MFMA, s, nullptr, P);
@@ -446,16 +455,16 @@ bool chunk_layout(const sv_chunked_desc* d, uint32_t passes, ChunkLayout* L) {
         if (ho[t + 1] < ho[t]) return false;
     L->max_tokens = 0;
     // With the dW pass even an empty video needs the (zero-token) plan's db partials.
+    const bool bf = d->dtype == SV_BF16;
     L->dw_bytes = (passes & SV_PASS_DW)
-                      ? dw_workspace_bytes(plan_dw(0, d->C_in, d->C_out, d->dtype == SV_BF16, L->taps))
+                      ? dw_workspace_bytes(plan_dw(0, d->C_in, d->C_out, bf, L->taps))
                       : 0;
     for (int f0 = 0; f0 < d->T; f0 += d->chunk_frames) {
         const int f1 = std::min(d->T, f0 + d->chunk_frames);
         const int64_t toks = static_cast<int64_t>(ho[f1]) - ho[f0];
         L->max_tokens = std::max(L->max_tokens, toks);
         if (passes & SV_PASS_DW)
-            L->dw_bytes = std::max(L->dw_bytes, dw_workspace_bytes(plan_dw(toks, d->C_in, d->C_out,
-                                                                          d->dtype == SV_BF16, L->taps)));
+            L->dw_bytes = std::max(L->dw_bytes, dw_workspace_bytes(plan_dw(toks, d->C_in, d->C_out, bf, L->taps)));
     }
     }
     L->n_bytes = align_up(static_cast<size_t>(L->max_tokens) * L->taps * sizeof(int32_t));

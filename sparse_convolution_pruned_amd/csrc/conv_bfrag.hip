@@ -63,15 +63,37 @@ constexpr int BF_MAXTILES = 256;         // one workgroup per compute unit of a 
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// The second problem of a paired launch: same N, taps and tile shape, no
+// bias; its tiles follow the first problem's `tiles1`.
+struct BfragSecond {
+    const uint16_t* A;
+    const uint16_t* Bf;
+    uint16_t* out;
+    int K, NO, tiles1;
+};
+
 // MB: 32-row blocks of tokens per wave, NB: 32-column blocks of output
-// channels per wave; tile 64 * MB tokens x 64 * NB channels.
-template <int TAPS, int MB, int NB>
-__global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t* __restrict__ A,
+// channels per wave; tile 64 * MB tokens x 64 * NB channels.  PAIR: the
+// grid also holds the tiles of a second problem on the same N (the chunk
+// driver's forward and input gradient), so that two problems too small to
+// fill the chip run side by side in one launch.
+template <int TAPS, int MB, int NB, bool PAIR>
+__global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t* __restrict__ A1,
                                                                const int32_t* __restrict__ Nt,
-                                                               const uint16_t* __restrict__ Bf,
-                                                               const uint16_t* __restrict__ bias,
-                                                               uint16_t* __restrict__ out, int n, int K, int NO) {
+                                                               const uint16_t* __restrict__ B1,
+                                                               const uint16_t* __restrict__ bias1,
+                                                               uint16_t* __restrict__ out1, int n, int K1, int NO1,
+                                                               BfragSecond p2) {
     constexpr int BM = 64 * MB, BN = 64 * NB, NT = 64 * BF_WAVES;
+    int logical = xcd_remap(blockIdx.x, gridDim.x);
+    bool second = false;
+    if constexpr (PAIR) second = logical >= p2.tiles1;
+    if (second) logical -= p2.tiles1;
+    const uint16_t* __restrict__ A = second ? p2.A : A1;
+    const uint16_t* __restrict__ Bf = second ? p2.Bf : B1;
+    const uint16_t* __restrict__ bias = second ? nullptr : bias1;
+    uint16_t* __restrict__ out = second ? p2.out : out1;
+    const int K = second ? p2.K : K1, NO = second ? p2.NO : NO1;
     static_assert(NB == 2 || NB == 4, "a wave's channels are whole 64-channel groups");
     // Window rows are requested before the tile's N slice has arrived, from
     // the fixed start k0 - HALO: with tokens packed frame-major and in
@@ -96,7 +118,6 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;        // token half, channel half of the tile
     const int l32 = lane & 31, lhi = lane >> 5;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int tilesN = NO / BN;
     const int k0 = (logical / tilesN) * BM;
     const int n0 = (logical % tilesN) * BN;
@@ -451,36 +472,41 @@ hipError_t launch_repack_frag(const uint16_t* Wt, uint16_t* Bf, int Ci, int Co, 
 // whose grid is one round of at most 256 tiles (one per compute unit of a
 // 256-CU part); at equal size, 256 channels (NB = 4: half the A reads per
 // MFMA).  Without such a tile, the largest one the channel count allows.
-// Depends on the arguments only; every shape gives the same bits.
+// A paired launch (NO2 > 0) counts both problems' tiles and needs a shape
+// that divides both channel counts.  Depends on the arguments only; every
+// shape gives the same bits.
 struct BfragShape {
     int mb, nb;
 };
-static BfragShape bfrag_shape(int64_t n, int NO) {
+static int64_t bfrag_tiles(BfragShape t, int64_t n, int NO) {
+    return NO > 0 ? ((n + 64 * t.mb - 1) / (64 * t.mb)) * (NO / (64 * t.nb)) : 0;
+}
+static BfragShape bfrag_shape(int64_t n, int NO, int NO2 = 0) {
     static const BfragShape order[] = {{2, 2}, {3, 2}, {2, 4}, {4, 2}, {3, 4}, {4, 4}};    // by tile size
     for (const BfragShape& t : order) {
-        if (NO % (64 * t.nb) != 0) continue;
-        const int64_t tiles = ((n + 64 * t.mb - 1) / (64 * t.mb)) * (NO / (64 * t.nb));
-        if (tiles <= BF_MAXTILES) return t;
+        if (NO % (64 * t.nb) != 0 || NO2 % (64 * t.nb) != 0) continue;
+        if (bfrag_tiles(t, n, NO) + bfrag_tiles(t, n, NO2) <= BF_MAXTILES) return t;
     }
-    return NO % 256 == 0 ? BfragShape{4, 4} : BfragShape{4, 2};
+    return NO % 256 == 0 && NO2 % 256 == 0 ? BfragShape{4, 4} : BfragShape{4, 2};
 }
 
-template <int TAPS>
+template <int TAPS, bool PAIR>
 static void launch_bfrag_taps(BfragShape t, dim3 grid, hipStream_t stream, const uint16_t* A, const int32_t* N,
-                              const uint16_t* Bf, const uint16_t* bias, uint16_t* out, int n, int K, int NO) {
+                              const uint16_t* Bf, const uint16_t* bias, uint16_t* out, int n, int K, int NO,
+                              const BfragSecond& p2) {
     const dim3 block(64 * BF_WAVES);
     if (t.nb == 2 && t.mb == 2)
-        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 2, 2>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 2, 2, PAIR>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO, p2);
     else if (t.nb == 2 && t.mb == 3)
-        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 3, 2>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 3, 2, PAIR>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO, p2);
     else if (t.nb == 2)
-        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 4, 2>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 4, 2, PAIR>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO, p2);
     else if (t.mb == 2)
-        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 2, 4>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 2, 4, PAIR>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO, p2);
     else if (t.mb == 3)
-        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 3, 4>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 3, 4, PAIR>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO, p2);
     else
-        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 4, 4>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO);
+        hipLaunchKernelGGL((k_conv_bfrag<TAPS, 4, 4, PAIR>), grid, block, 0, stream, A, N, Bf, bias, out, n, K, NO, p2);
 }
 
 hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t* Bf, const uint16_t* bias,
@@ -488,12 +514,30 @@ hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t
     if (n <= 0) return hipSuccess;
     if (!conv_bfrag_ok(K, NO, taps)) return hipErrorInvalidValue;
     const BfragShape t = bfrag_shape(n, NO);
-    const dim3 grid(static_cast<unsigned>(((n + 64 * t.mb - 1) / (64 * t.mb)) * (NO / (64 * t.nb))));
+    const dim3 grid(static_cast<unsigned>(bfrag_tiles(t, n, NO)));
     const int ni = static_cast<int>(n);
+    const BfragSecond none{};
     if (taps == 1)
-        launch_bfrag_taps<1>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO);
+        launch_bfrag_taps<1, false>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO, none);
     else
-        launch_bfrag_taps<9>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO);
+        launch_bfrag_taps<9, false>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO, none);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_bfrag_pair(const uint16_t* A1, const uint16_t* B1, const uint16_t* bias1, uint16_t* out1,
+                                  int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
+                                  int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    if (!conv_bfrag_ok(K1, NO1, taps) || !conv_bfrag_ok(K2, NO2, taps)) return hipErrorInvalidValue;
+    const BfragShape t = bfrag_shape(n, NO1, NO2);
+    const int64_t tiles1 = bfrag_tiles(t, n, NO1);
+    const dim3 grid(static_cast<unsigned>(tiles1 + bfrag_tiles(t, n, NO2)));
+    const int ni = static_cast<int>(n);
+    const BfragSecond p2{A2, B2, out2, K2, NO2, static_cast<int>(tiles1)};
+    if (taps == 1)
+        launch_bfrag_taps<1, true>(t, grid, stream, A1, N, B1, bias1, out1, ni, K1, NO1, p2);
+    else
+        launch_bfrag_taps<9, true>(t, grid, stream, A1, N, B1, bias1, out1, ni, K1, NO1, p2);
     return hipGetLastError();
 }
 

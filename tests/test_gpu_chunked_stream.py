@@ -10,8 +10,9 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import oracle as O
 from sparse_convolution_pruned_amd import ops, workloads as wl
-from tests.gpu_util import dev
+from tests.gpu_util import assert_close, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +86,25 @@ def test_without_host_offsets(dw_side):
     b = run(L, 2, ALL, side, host_offsets=False)
     for name, u, v in zip(("Y", "dX", "dW", "db"), a, b):
         assert torch.equal(u, v), f"{name} differs without the host offsets"
+
+
+@pytest.mark.parametrize("Ci,Co,ksize", [(128, 256, 3), (256, 128, 3), (512, 512, 1)])
+def test_paired_fragment_launch(Ci, Co, ksize):
+    """Chunks whose forward and input gradient both fit the fragment kernel
+    run them as one paired launch: Y and dX equal the unchunked calls bit for
+    bit (same summation order whatever the tile shape) and the oracle."""
+    L = wl.make_random_case(85, 6, 14, 14, [150, 0, 196, 33, 120, 90], Ci, Co, "bf16", ksize=ksize)
+    print(f"n={L.n} Ci={Ci} Co={Co} K={ksize}", flush=True)
+    Y, dX, _, _ = run(L, 2, ALL, torch.cuda.Stream(), ksize=ksize)
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K=ksize)
+    dt = torch.bfloat16
+    X, Wt, b, dY, Nd = dev(L.X, dt), dev(L.Wt, dt), dev(L.b, dt), dev(L.dY, dt), dev(N)
+    Y1 = torch.empty((L.n, Co), dtype=dt, device="cuda")
+    dX1 = torch.empty((L.n, Ci), dtype=dt, device="cuda")
+    ops.sv_sparseconv2d_fwd_k(X, Nd, Wt, b, Y1, "mfma")
+    ops.sv_sparseconv2d_bwd_dx_k(dY, Nd, Wt, dX1, "mfma")
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y1.cpu()), "Y differs from the unchunked call"
+    assert torch.equal(dX, dX1.cpu()), "dX differs from the unchunked call"
+    assert_close(host(Y1), O.fwd(L.X, N, L.Wt, L.b), "bf16", "paired Y")
+    assert_close(host(dX1), O.bwd_dx(L.dY, N, L.Wt), "bf16", "paired dX")
