@@ -4,8 +4,9 @@
  * C ABI.  Plain pointers and sizes only; every pointer argument named "device"
  * is device memory owned by the caller; the library never allocates, never
  * frees, never synchronises the stream (unless the SV_SYNC_CHECK debugging
- * aid below is switched on, or sv_sparseconv2d_chunked is given no host copy
- * of the frame offsets) and keeps no state other than a cached device
+ * aid below is switched on, sv_sparseconv2d_chunked is given no host copy
+ * of the frame offsets, or in sv_sparseconv2d_chunked_host, which orders its
+ * copy engines from the host) and keeps no state other than a cached device
  * property.  All work is enqueued asynchronously on the caller's
  * hipStream_t (NULL = the default stream).  No C++ exception crosses this
  * boundary.  Status codes report argument errors synchronously, before any
@@ -355,26 +356,29 @@ size_t sv_chunked_workspace_bytes(const sv_chunked_desc *desc, uint32_t passes);
  * holds only the weights, the gradients and a workspace sized by one chunk,
  * so total device memory does not grow with T).
  *
- * Each chunk's coordinates, frame offsets, X and dY are copied (by a copy
- * kernel that reads the page-locked host memory over the bus, so that every
- * cross-stream wait stays on the GPU) into one of three device staging sets
- * on `h2d`, computed on `compute` (index build,
- * then the requested passes, exactly as sv_sparseconv2d_chunked), and its Y
- * and dX copied back on `d2h`.  Events order the three streams: uploads run
- * up to two chunks ahead of the compute, and a chunk's results go back while
- * the next chunks compute.  Results are identical to sv_sparseconv2d_chunked
- * (same kernels, same chunk order; dW/db accumulate on the device in chunk
- * order).
+ * Each chunk's coordinates, frame offsets, X and dY are copied by the copy
+ * engines (hipMemcpyAsync) into one of four device staging sets on `h2d`,
+ * computed on `compute` (index build, then the requested passes, exactly as
+ * sv_sparseconv2d_chunked), and its Y and dX copied back on `d2h`.  Uploads
+ * run two chunks ahead of the compute, and a chunk's results go back while
+ * the next chunks compute.  The copy streams never wait on another stream's
+ * event (a copy queued behind such a wait can hold the host thread in the
+ * runtime until it fires); the call orders them from the host instead: it
+ * waits (on the host) for a chunk's compute before queuing its download,
+ * and for a staging set's download before queuing the next upload into it.
+ * So, unlike the other calls, this one blocks the host: it returns once the
+ * last chunk's compute has finished and its download is queued.  Results
+ * are identical to sv_sparseconv2d_chunked (same kernels, same chunk order;
+ * dW/db accumulate on the device in chunk order).
  *
  * All host arrays must be page-locked (hipHostMalloc, or a pinned torch
- * tensor; anything else is SV_ERR_INVALID_ARG) and must stay valid, and Y / dX unread, until `compute`
- * completes: the call returns as soon as the work is enqueued, and it makes
- * `compute` wait for the last copies, so synchronising `compute` suffices.
- * The three streams must be distinct.  Uploads start only after the work
- * already enqueued on `compute`, so back-to-back calls on one workspace are
- * ordered.  The call creates (and releases) ten HIP events; it allocates no
- * memory.  On a HIP error part of the work may
- * already be enqueued. */
+ * tensor; anything else is SV_ERR_INVALID_ARG) and must stay valid, and
+ * Y / dX unread, until `compute` completes: the call makes `compute` wait
+ * for the last copies, so synchronising `compute` suffices.  The three
+ * streams must be distinct.  The call first waits (on the host) for the
+ * work already enqueued on `compute`, so back-to-back calls on one workspace
+ * are ordered.  It creates (and releases) thirteen HIP events; it allocates
+ * no memory.  On a HIP error part of the work may already be enqueued. */
 typedef struct sv_chunked_host_desc {
     int32_t T, H, W;
     int32_t C_in, C_out;
@@ -400,7 +404,7 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc *desc, uint32_
                                        hipStream_t compute, hipStream_t h2d, hipStream_t d2h);
 
 /* Workspace bytes sv_sparseconv2d_chunked_host needs: the device driver's
- * workspace plus three staging sets of the largest chunk's coordinates,
+ * workspace plus four staging sets of the largest chunk's coordinates,
  * offsets and per-token tensors.  Independent of T.  Returns 0 on bad
  * descriptors. */
 size_t sv_chunked_host_workspace_bytes(const sv_chunked_host_desc *desc, uint32_t passes);

@@ -651,7 +651,8 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
 
 namespace {
 
-constexpr int kSets = 3;              // staging sets of the host-streamed driver
+constexpr int kSets = 4;              // staging sets of the host-streamed driver
+constexpr int kAhead = 2;             // chunks uploaded ahead of the compute
 
 struct HostLayout {
     ChunkLayout dev;                  // N table, repacked weights, dW partials
@@ -730,22 +731,17 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return SV_ERR_WORKSPACE;
     if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256) return SV_ERR_INVALID_ARG;
 
-    // Device-visible addresses of the page-locked host arrays; an array
-    // that is not page-locked is an argument error.
-    auto dev_view = [](const void* h, const void** out) {
-        *out = nullptr;
-        if (!h) return true;
+    // The host arrays must be page-locked (the copy engines then move them
+    // without staging and the copies are asynchronous); anything else is an
+    // argument error.
+    auto pinned = [](const void* h) {
         void* p = nullptr;
-        if (hipHostGetDevicePointer(&p, const_cast<void*>(h), 0) != hipSuccess) return false;
-        *out = p;
-        return true;
+        return !h || hipHostGetDevicePointer(&p, const_cast<void*>(h), 0) == hipSuccess;
     };
-    const void *coords_dv, *offs_dv, *X_dv, *dY_dv, *Y_dv, *dX_dv;
-    if (!dev_view(d->coords_host, &coords_dv) || !dev_view(d->frame_offsets_host, &offs_dv) ||
-        !dev_view((passes & (SV_PASS_FWD | SV_PASS_DW)) ? d->X_host : nullptr, &X_dv) ||
-        !dev_view((passes & (SV_PASS_DX | SV_PASS_DW)) ? d->dY_host : nullptr, &dY_dv) ||
-        !dev_view((passes & SV_PASS_FWD) ? d->Y_host : nullptr, &Y_dv) ||
-        !dev_view((passes & SV_PASS_DX) ? d->dX_host : nullptr, &dX_dv)) {
+    if (!pinned(d->coords_host) || !pinned(d->frame_offsets_host) ||
+        !pinned((passes & (SV_PASS_FWD | SV_PASS_DW)) ? d->X_host : nullptr) ||
+        !pinned((passes & (SV_PASS_DX | SV_PASS_DW)) ? d->dY_host : nullptr) ||
+        !pinned((passes & SV_PASS_FWD) ? d->Y_host : nullptr) || !pinned((passes & SV_PASS_DX) ? d->dX_host : nullptr)) {
         (void)hipGetLastError();          // clear the query's error state
         return SV_ERR_INVALID_ARG;
     }
@@ -799,9 +795,17 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
 
     // Chunk c uses staging set c % kSets.  ev_in[b]: the chunk's inputs are
     // in set b; ev_done[b]: its compute finished; ev_out[b]: its results left
-    // set b (set b is free again).  ev_start: everything enqueued on
-    // `compute` before this call (a previous call on the same workspace ends
-    // there, after its last copies), which the first uploads wait for.
+    // set b (set b is free again).  The transfers are copy-engine copies
+    // (hipMemcpyAsync), and neither copy stream ever waits on another
+    // stream's event: a copy queued behind such a wait that has not fired
+    // holds the host thread in the runtime until it fires, which put the
+    // whole pipeline in lockstep.  The host orders them instead: it queues
+    // chunk c's download once its compute has finished, and the upload into
+    // a set once that set's previous chunk has been downloaded.  With uploads
+    // kAhead = 2 chunks ahead of the compute and four sets, each of those
+    // waits is for work queued about a chunk earlier, so that the host keeps
+    // the copy engines and the compute stream fed.  The compute stream waits
+    // on the upload stream's events on the GPU (kernels only).
     hipEvent_t ev[3 * kSets + 1] = {};
     for (int i = 0; i < 3 * kSets + 1; ++i)
         if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
@@ -818,82 +822,100 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
         *t0 = ho[*f0];
         *nc = static_cast<int64_t>(ho[*f1]) - *t0;
     };
+    auto h2d_copy = [&](void* dst, const void* src, int64_t bytes) {
+        return bytes > 0 ? hipMemcpyAsync(dst, src, static_cast<size_t>(bytes), hipMemcpyHostToDevice, h2d)
+                         : hipSuccess;
+    };
+    auto d2h_copy = [&](void* dst, const void* src, int64_t bytes) {
+        return bytes > 0 ? hipMemcpyAsync(dst, src, static_cast<size_t>(bytes), hipMemcpyDeviceToHost, d2h)
+                         : hipSuccess;
+    };
     auto upload = [&](int ci) -> hipError_t {
         const int b = ci % kSets;
         int f0, f1;
         int64_t t0, nc;
         chunk_bounds(ci, &f0, &f1, &t0, &nc);
         hipError_t e = hipSuccess;
-        if (ci >= kSets && (e = hipStreamWaitEvent(h2d, ev_out[b], 0)) != hipSuccess) return e;
-        if ((e = launch_copy_bytes(static_cast<const int32_t*>(coords_dv) + t0, st[b].coords,
-                                   nc * static_cast<int64_t>(sizeof(int32_t)), h2d)))
+        if (ci >= kSets && (e = hipEventSynchronize(ev_out[b])) != hipSuccess) return e;
+        if ((e = h2d_copy(st[b].coords, d->coords_host + t0, nc * static_cast<int64_t>(sizeof(int32_t)))))
             return e;
-        if ((e = launch_copy_bytes(static_cast<const int32_t*>(offs_dv) + f0, st[b].offs,
-                                   (f1 - f0 + 1) * static_cast<int64_t>(sizeof(int32_t)), h2d)))
+        if ((e = h2d_copy(st[b].offs, ho + f0, (f1 - f0 + 1) * static_cast<int64_t>(sizeof(int32_t))))) return e;
+        if (L.x_b && (e = h2d_copy(st[b].X, static_cast<const char*>(d->X_host) + t0 * d->C_in * es,
+                                   nc * d->C_in * static_cast<int64_t>(es))))
             return e;
-        if (L.x_b && (e = launch_copy_bytes(static_cast<const char*>(X_dv) + t0 * d->C_in * es, st[b].X,
-                                            nc * d->C_in * static_cast<int64_t>(es), h2d)))
-            return e;
-        if (L.dy_b && (e = launch_copy_bytes(static_cast<const char*>(dY_dv) + t0 * d->C_out * es, st[b].dY,
-                                             nc * d->C_out * static_cast<int64_t>(es), h2d)))
+        if (L.dy_b && (e = h2d_copy(st[b].dY, static_cast<const char*>(d->dY_host) + t0 * d->C_out * es,
+                                    nc * d->C_out * static_cast<int64_t>(es))))
             return e;
         return hipEventRecord(ev_in[b], h2d);
     };
+    auto download = [&](int ci) -> hipError_t {
+        const int b = ci % kSets;
+        int f0, f1;
+        int64_t t0, nc;
+        chunk_bounds(ci, &f0, &f1, &t0, &nc);
+        hipError_t e = hipEventSynchronize(ev_done[b]);
+        if (e != hipSuccess) return e;
+        if ((passes & SV_PASS_FWD) && (e = d2h_copy(static_cast<char*>(d->Y_host) + t0 * d->C_out * es, st[b].Y,
+                                                    nc * d->C_out * static_cast<int64_t>(es))))
+            return e;
+        if ((passes & SV_PASS_DX) && (e = d2h_copy(static_cast<char*>(d->dX_host) + t0 * d->C_in * es, st[b].dX,
+                                                   nc * d->C_in * static_cast<int64_t>(es))))
+            return e;
+        return hipEventRecord(ev_out[b], d2h);
+    };
+    auto compute_chunk = [&](int ci) -> sv_status {
+        const int b = ci % kSets;
+        int f0, f1;
+        int64_t t0, nc;
+        chunk_bounds(ci, &f0, &f1, &t0, &nc);
+        if (hipStreamWaitEvent(compute, ev_in[b], 0) != hipSuccess) return SV_ERR_HIP;
+        // The staged slices hold global frame offsets and the chunk's own
+        // coordinates; the index kernel reads offs[f0 + f] and coords[k]
+        // for global k, so it gets both bases shifted back.
+        const int32_t* coords_g = st[b].coords - t0;
+        const int32_t* offs_g = st[b].offs - f0;
+        sv_status s2 = hip_status(launch_build_index(coords_g, offs_g, f0, f1 - f0, d->H, d->W, L.dev.K, nc, t0,
+                                                     Nc, nullptr, d->err_flag, compute));
+        if (s2 != SV_OK) return s2;
+        if (fwd_mfma && dx_mfma) {
+            s2 = run_fwd_dx_pair(st[b].X, st[b].dY, Nc, d->Wt, Vw, Pw, d->bias, st[b].Y, st[b].dX, nc, d->C_in,
+                                 d->C_out, taps, compute);
+            if (s2 != SV_OK) return s2;
+        } else {
+            if (passes & SV_PASS_FWD) {
+                s2 = run_fwd_prepared(fwd_mfma, st[b].X, Nc, d->Wt, Vw, d->bias, st[b].Y, nc, d->C_in, d->C_out,
+                                      taps, d->dtype, compute);
+                if (s2 != SV_OK) return s2;
+            }
+            if (passes & SV_PASS_DX) {
+                s2 = run_dx(st[b].dY, Nc, d->Wt, st[b].dX, nc, d->C_in, d->C_out, taps, d->dtype, d->kernel,
+                            compute, nullptr, Pw);
+                if (s2 != SV_OK) return s2;
+            }
+        }
+        if (passes & SV_PASS_DW) {
+            const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16, taps);
+            s2 = hip_status(launch_dw(plan, d->dtype == SV_BF16, st[b].X, Nc, st[b].dY, d->dW, d->db, nc, d->C_in,
+                                      d->C_out, ci == 0 ? 0 : 1, dws, compute));
+            if (s2 != SV_OK) return s2;
+        }
+        return hip_status(hipEventRecord(ev_done[b], compute));
+    };
     auto run = [&]() -> sv_status {
-        if (hipEventRecord(ev_start, compute) != hipSuccess || hipStreamWaitEvent(h2d, ev_start, 0) != hipSuccess)
+        // The staging sets are free once everything enqueued on `compute`
+        // before this call is done (a previous call on this workspace ends
+        // there, after its last copies).
+        if (hipEventRecord(ev_start, compute) != hipSuccess || hipEventSynchronize(ev_start) != hipSuccess)
             return SV_ERR_HIP;
-        // Uploads run up to kSets - 1 chunks ahead of the compute.
-        for (int ci = 0; ci < std::min(nchunks, kSets - 1); ++ci)
+        for (int ci = 0; ci < std::min(nchunks, kAhead); ++ci)
             if (upload(ci) != hipSuccess) return SV_ERR_HIP;
         for (int ci = 0; ci < nchunks; ++ci) {
-            const int b = ci % kSets;
-            int f0, f1;
-            int64_t t0, nc;
-            chunk_bounds(ci, &f0, &f1, &t0, &nc);
-            if (ci + kSets - 1 < nchunks && upload(ci + kSets - 1) != hipSuccess) return SV_ERR_HIP;
-            if (hipStreamWaitEvent(compute, ev_in[b], 0) != hipSuccess) return SV_ERR_HIP;
-            // The staged slices hold global frame offsets and the chunk's own
-            // coordinates; the index kernel reads offs[f0 + f] and coords[k]
-            // for global k, so it gets both bases shifted back.
-            const int32_t* coords_g = st[b].coords - t0;
-            const int32_t* offs_g = st[b].offs - f0;
-            sv_status s2 = hip_status(launch_build_index(coords_g, offs_g, f0, f1 - f0, d->H, d->W, L.dev.K, nc,
-                                                         t0, Nc, nullptr, d->err_flag, compute));
+            const sv_status s2 = compute_chunk(ci);
             if (s2 != SV_OK) return s2;
-            if (fwd_mfma && dx_mfma) {
-                s2 = run_fwd_dx_pair(st[b].X, st[b].dY, Nc, d->Wt, Vw, Pw, d->bias, st[b].Y, st[b].dX, nc,
-                                     d->C_in, d->C_out, taps, compute);
-                if (s2 != SV_OK) return s2;
-            } else {
-                if (passes & SV_PASS_FWD) {
-                    s2 = run_fwd_prepared(fwd_mfma, st[b].X, Nc, d->Wt, Vw, d->bias, st[b].Y, nc, d->C_in,
-                                          d->C_out, taps, d->dtype, compute);
-                    if (s2 != SV_OK) return s2;
-                }
-                if (passes & SV_PASS_DX) {
-                    s2 = run_dx(st[b].dY, Nc, d->Wt, st[b].dX, nc, d->C_in, d->C_out, taps, d->dtype, d->kernel,
-                                compute, nullptr, Pw);
-                    if (s2 != SV_OK) return s2;
-                }
-            }
-            if (passes & SV_PASS_DW) {
-                const DwPlan plan = plan_dw(nc, d->C_in, d->C_out, d->dtype == SV_BF16, taps);
-                s2 = hip_status(launch_dw(plan, d->dtype == SV_BF16, st[b].X, Nc, st[b].dY, d->dW, d->db, nc,
-                                          d->C_in, d->C_out, ci == 0 ? 0 : 1, dws, compute));
-                if (s2 != SV_OK) return s2;
-            }
-            if (hipEventRecord(ev_done[b], compute) != hipSuccess) return SV_ERR_HIP;
-            if (hipStreamWaitEvent(d2h, ev_done[b], 0) != hipSuccess) return SV_ERR_HIP;
-            if ((passes & SV_PASS_FWD) &&
-                launch_copy_bytes(st[b].Y, const_cast<char*>(static_cast<const char*>(Y_dv)) + t0 * d->C_out * es,
-                                  nc * d->C_out * static_cast<int64_t>(es), d2h) != hipSuccess)
-                return SV_ERR_HIP;
-            if ((passes & SV_PASS_DX) &&
-                launch_copy_bytes(st[b].dX, const_cast<char*>(static_cast<const char*>(dX_dv)) + t0 * d->C_in * es,
-                                  nc * d->C_in * static_cast<int64_t>(es), d2h) != hipSuccess)
-                return SV_ERR_HIP;
-            if (hipEventRecord(ev_out[b], d2h) != hipSuccess) return SV_ERR_HIP;
+            if (ci >= 1 && download(ci - 1) != hipSuccess) return SV_ERR_HIP;
+            if (ci + kAhead < nchunks && upload(ci + kAhead) != hipSuccess) return SV_ERR_HIP;
         }
+        if (download(nchunks - 1) != hipSuccess) return SV_ERR_HIP;
         // Synchronising `compute` then covers every copy of the call.
         return hip_status(hipStreamWaitEvent(compute, ev_out[(nchunks - 1) % kSets], 0));
     };

@@ -182,9 +182,6 @@ hipError_t launch_xattn_bwd(const XattnPlan& p, bool bf16, const void* Q, const 
                             const void* dO, const float* lse, int m, int64_t n, int d, float scale, float* dQ,
                             void* dX, void* ws, hipStream_t stream);
 
-// Copies `bytes` bytes with a kernel (either side may be page-locked host
-// memory the device can address).
-hipError_t launch_copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_stage_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n_rows,
                                void* dst, int C, int elem_bytes, hipStream_t stream);
 hipError_t launch_stage_scatter(const void* src, const int32_t* rows, int64_t n_rows, void* dst,

@@ -92,63 +92,6 @@ hipError_t launch_stage_scatter(const void* src, const int32_t* rows, int64_t n_
     return scatter_as<uint16_t>(src, rows, n_rows, dst, n_dst, static_cast<int>(rb / 2), stream);
 }
 
-// Byte copy through a kernel, for the host-streamed chunk driver: one side
-// is page-locked host memory, which the GPU reads and writes directly over
-// the bus.  Ordering across streams then rests on GPU-side waits before a
-// kernel launch (a copy engine transfer queued behind a cross-stream wait
-// can hold the host thread until that wait is satisfied).  16-byte words
-// when both ends allow it, 4-byte words otherwise; a byte tail.
-// A small grid with four independent words per thread per iteration: eight
-// workgroups keep enough bytes in flight for the bus, and the copies then
-// disturb the kernels they overlap least (measured: 8 workgroups 3.9 ms per
-// host-streamed config-4 pass, 64 workgroups 4.3 ms, 2 workgroups 5.8 ms).
-template <typename V>
-__global__ __launch_bounds__(256) void k_copy_words(const V* __restrict__ src, V* __restrict__ dst, int64_t words) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    for (; e + 3 * stride < words; e += 4 * stride) {
-        V v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = src[e + u * stride];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) dst[e + u * stride] = v[u];
-    }
-    for (; e < words; e += stride) dst[e] = src[e];
-}
-
-__global__ void k_copy_tail(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int bytes) {
-    if (static_cast<int>(threadIdx.x) < bytes) dst[threadIdx.x] = src[threadIdx.x];
-}
-
-hipError_t launch_copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
-    if (bytes <= 0) return hipSuccess;
-    const uintptr_t a = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
-    const int wb = (a % 16 == 0) ? 16 : (a % 4 == 0 ? 4 : 1);
-    const int64_t words = bytes / wb;
-    if (words > 0) {
-        const int blocks = static_cast<int>(std::min<int64_t>((words + 255) / 256, 8));
-        if (wb == 16)
-            hipLaunchKernelGGL(k_copy_words<uint4>, dim3(blocks), dim3(256), 0, stream,
-                               static_cast<const uint4*>(src), static_cast<uint4*>(dst), words);
-        else if (wb == 4)
-            hipLaunchKernelGGL(k_copy_words<uint32_t>, dim3(blocks), dim3(256), 0, stream,
-                               static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), words);
-        else
-            hipLaunchKernelGGL(k_copy_words<uint8_t>, dim3(blocks), dim3(256), 0, stream,
-                               static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), words);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const int tail = static_cast<int>(bytes - words * wb);
-    if (tail > 0) {
-        hipLaunchKernelGGL(k_copy_tail, dim3(1), dim3(64), 0, stream,
-                           static_cast<const uint8_t*>(src) + words * wb, static_cast<uint8_t*>(dst) + words * wb,
-                           tail);
-        return hipGetLastError();
-    }
-    return hipSuccess;
-}
-
 // The identity neighbour table of a 1 x 1 neighbourhood: dst[k] = k.
 __global__ __launch_bounds__(256) void k_iota(int32_t* __restrict__ dst, int64_t n) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
