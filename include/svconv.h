@@ -118,7 +118,7 @@ sv_status sv_build_index(const int32_t *coords, const int32_t *frame_offsets,
  *   sv_workspace_bytes(SV_OP_FWD, ...) bytes (0 unless the bf16 matrix-core
  *   kernels can run; it receives the weights repacked for them: as
  *   [tap][C_out][C_in], or in MFMA fragment order when C_in is a multiple of
- *   64 and C_out of 256); contents are scratch.
+ *   64 and C_out of 128); contents are scratch.
  * SV_ERR_UNSUPPORTED if `kernel` is MFMA and the shape/dtype does not fit it;
  * SV_ERR_WORKSPACE if the MFMA kernel runs and the workspace is short. */
 sv_status sv_sparseconv2d_fwd(const void *X, const int32_t *N, const void *Wt,
@@ -182,7 +182,9 @@ size_t sv_workspace_bytes(sv_op op, int64_t n, int32_t C_in, int32_t C_out, sv_d
  * adapter; K = 1 is the pointwise projection around it (N[k][0] = k) and
  * 5 and 7 widen the receptive field with the same index table and
  * kernels.  Both kernel families serve every K listed; the MFMA conditions
- * of sv_kernel are unchanged.  n * taps must stay below 2^31.
+ * of sv_kernel are unchanged, and the fragment-order weights (workspaces
+ * of FWD and DX) apply at K = 3, 5 and 7 (at K = 1 from 512 contracted
+ * channels).  n * taps must stay below 2^31.
  * Returns SV_ERR_INVALID_ARG for an even or non-positive K and
  * SV_ERR_UNSUPPORTED for an odd K above 7 (sv_workspace_bytes_k: 0), then
  * behaves exactly as the 3 x 3 call of the same name. */
@@ -218,7 +220,8 @@ size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_
  *     not fit).  Weights repacked once serve any number of forward calls and
  *     can be prepared on another stream ahead of them.
  *   sv_repack_dx_k writes the input gradient's weights in MFMA fragment
- *     order (bf16, 3 x 3, C_out a multiple of 64 and C_in of 128, else
+ *     order (bf16, K of 3, 5 or 7, or K = 1 with C_out of at least 512;
+ *     C_out a multiple of 64 and C_in of 128; else
  *     SV_ERR_UNSUPPORTED; Wt and P 16-byte aligned, P at least
  *     sv_workspace_bytes_k(SV_OP_DX, ...) bytes), and
  *     sv_sparseconv2d_bwd_dx_packed_k runs the input gradient from that P;

@@ -120,7 +120,7 @@ sv_status run_fwd_dx_pair(const void* X, const void* dY, const int32_t* N, const
                           const void* P, const void* bias, void* Y, void* dX, int64_t n, int32_t Ci, int32_t Co,
                           int taps, hipStream_t s) {
     if (n == 0) return SV_OK;
-    if (P && conv_bfrag_ok(Ci, Co, taps) && conv_bfrag_ok(Co, Ci, taps))
+    if (P && conv_bfrag_pair_ok(Ci, Co, Co, Ci, taps))
         // both passes on the fragment kernel (V and P in fragment order)
         return hip_status(launch_conv_bfrag_pair(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(V),
                                                  static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(Y), Ci,

@@ -2,7 +2,8 @@
 // streamed from memory straight into registers ("SV-TAD: Native Sparse
 // Convolutions for Efficient Temporal Action Detection", Key Design 2: the
 // wide-channel path, y_k = sum_j W_j x[N[k, j]] as an implicit GEMM with
-// M = tokens, K = 9 * C, N = output channels; -1 entries are zero padding).
+// M = tokens, K = taps * C, N = output channels; -1 entries are zero
+// padding).  Taps: 9 (3 x 3), 25 and 49 (5 x 5, 7 x 7) and 1 (1 x 1).
 //
 // Same product as k_conv_mfma (conv_mfma.hip),
 //     out[k][c] = sum_j sum_i A[N[k, j]][i] * B[P - j][c][i]  (+ bias[c]),
@@ -97,12 +98,14 @@ __global__ __launch_bounds__(64 * BF_WAVES, 1) void k_conv_bfrag(const uint16_t*
     static_assert(NB == 2 || NB == 4, "a wave's channels are whole 64-channel groups");
     // Window rows are requested before the tile's N slice has arrived, from
     // the fixed start k0 - HALO: with tokens packed frame-major and in
-    // ascending flat order inside a frame, every neighbour of token k lies
-    // within (W + 1) packed positions of k, so for grids up to 31 wide the
-    // tile's rows fall inside [k0 - 32, k0 + BM + 32).  Tiles whose rows do
-    // not (other packings, wider grids) switch to gather mode.  With one tap
-    // (1 x 1) the rows are the tile's own: no halo.
-    constexpr int HALO = TAPS == 1 ? 0 : BF_HALO;
+    // ascending flat order inside a frame, every neighbour of token k at
+    // most R rows and columns away (K = 2R + 1) lies within R (W + 1) packed
+    // positions of k.  So the tile's rows fall inside [k0 - HALO,
+    // k0 + BM + HALO) with HALO = 32 for 3 x 3 on grids up to 31 wide, and
+    // HALO = 64 for 5 x 5 (up to 31 wide) and 7 x 7 (up to 20 wide).  Tiles
+    // whose rows do not (other packings, wider grids) switch to gather mode.
+    // With one tap (1 x 1) the rows are the tile's own: no halo.
+    constexpr int HALO = TAPS == 1 ? 0 : (TAPS == 9 ? BF_HALO : 2 * BF_HALO);
     constexpr int WIN = BM + 2 * HALO;
     constexpr int ZROW = WIN;                       // all-zero row: target of -1 entries
     constexpr int WB = (WIN + 1) * BF_ROWB;         // bytes per window buffer
@@ -453,8 +456,13 @@ hipError_t launch_repack_batch(int count, const uint16_t* const* W, uint16_t* co
 // prologue and epilogue dominate and k_conv_mfma's two workgroups per CU
 // overlap them better (c3a at 1 x 1: forward 14.4 against 18.9 us).
 bool conv_bfrag_ok(int K, int NO, int taps) {
-    return (taps == 9 || (taps == 1 && K >= 512)) && K > 0 && NO > 0 && K % BF_KC == 0 && NO % 128 == 0 &&
-           static_cast<int64_t>(taps) * NO * K * 2 <= kMaxRange;
+    return (taps == 9 || taps == 25 || taps == 49 || (taps == 1 && K >= 512)) && K > 0 && NO > 0 &&
+           K % BF_KC == 0 && NO % 128 == 0 && static_cast<int64_t>(taps) * NO * K * 2 <= kMaxRange;
+}
+
+// The paired launch is built for 3 x 3 and 1 x 1 only.
+bool conv_bfrag_pair_ok(int K1, int NO1, int K2, int NO2, int taps) {
+    return (taps == 1 || taps == 9) && conv_bfrag_ok(K1, NO1, taps) && conv_bfrag_ok(K2, NO2, taps);
 }
 
 hipError_t launch_repack_frag(const uint16_t* Wt, uint16_t* Bf, int Ci, int Co, int taps, bool dx,
@@ -517,10 +525,12 @@ hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t
     const dim3 grid(static_cast<unsigned>(bfrag_tiles(t, n, NO)));
     const int ni = static_cast<int>(n);
     const BfragSecond none{};
-    if (taps == 1)
-        launch_bfrag_taps<1, false>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO, none);
-    else
-        launch_bfrag_taps<9, false>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO, none);
+    switch (taps) {
+        case 1: launch_bfrag_taps<1, false>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO, none); break;
+        case 9: launch_bfrag_taps<9, false>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO, none); break;
+        case 25: launch_bfrag_taps<25, false>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO, none); break;
+        default: launch_bfrag_taps<49, false>(t, grid, stream, A, N, Bf, bias, out, ni, K, NO, none); break;
+    }
     return hipGetLastError();
 }
 
@@ -528,7 +538,7 @@ hipError_t launch_conv_bfrag_pair(const uint16_t* A1, const uint16_t* B1, const 
                                   int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
                                   int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    if (!conv_bfrag_ok(K1, NO1, taps) || !conv_bfrag_ok(K2, NO2, taps)) return hipErrorInvalidValue;
+    if (!conv_bfrag_pair_ok(K1, NO1, K2, NO2, taps)) return hipErrorInvalidValue;
     const BfragShape t = bfrag_shape(n, NO1, NO2);
     const int64_t tiles1 = bfrag_tiles(t, n, NO1);
     const dim3 grid(static_cast<unsigned>(tiles1 + bfrag_tiles(t, n, NO2)));

@@ -116,11 +116,13 @@ hipError_t launch_repack_fwd(const uint16_t* Wt, uint16_t* V, int Ci, int Co, in
                              bool allow_frag = true);
 // Weight operand in fragment order (conv_bfrag.hip): the MFMA kernel that
 // streams B from memory into registers.  conv_bfrag_ok: the shapes it is
-// built for (3 x 3 or 1 x 1, contracted channels a multiple of 64, produced
-// channels a multiple of 128).  The repack writes taps * Ci * Co bf16 in fragment
+// built for (3 x 3, 5 x 5, 7 x 7 or 1 x 1, contracted channels a multiple of
+// 64, produced channels a multiple of 128); conv_bfrag_pair_ok: those its
+// paired launch takes (3 x 3 and 1 x 1).  The repack writes taps * Ci * Co bf16 in fragment
 // order for the forward (dx = false: K = Ci, NO = Co) or the input gradient
 // (dx = true: K = Co, NO = Ci, taps mirrored).
 bool conv_bfrag_ok(int K, int NO, int taps);
+bool conv_bfrag_pair_ok(int K1, int NO1, int K2, int NO2, int taps);
 hipError_t launch_repack_frag(const uint16_t* Wt, uint16_t* Bf, int Ci, int Co, int taps, bool dx,
                               hipStream_t stream);
 // Up to kRepackMax layers' weights (Wt[i], all of one shape) into both
@@ -133,7 +135,7 @@ hipError_t launch_repack_batch(int count, const uint16_t* const* W, uint16_t* co
 hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t* Bf, const uint16_t* bias,
                              uint16_t* out, int64_t n, int K, int NO, int taps, hipStream_t stream);
 // Two problems on the same N in one launch, each as launch_conv_bfrag (the
-// second without bias): both shapes must suit conv_bfrag_ok.
+// second without bias): the shapes must suit conv_bfrag_pair_ok.
 hipError_t launch_conv_bfrag_pair(const uint16_t* A1, const uint16_t* B1, const uint16_t* bias1, uint16_t* out1,
                                   int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
                                   int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream);

@@ -363,14 +363,17 @@ def test_split_forms_validation(lib):
         ops.SV_ERR_UNSUPPORTED
     assert lib.sv_sparseconv2d_fwd_packed_k(FAKE, FAKE, None, None, FAKE, 8, 3, 64, 64, BF16, None) == \
         ops.SV_ERR_INVALID_ARG
-    # input gradient in fragment order: bf16 3 x 3 with C_out % 64 == 0 and C_in % 128 == 0
+    # input gradient in fragment order: bf16 3 x 3, 5 x 5, 7 x 7 with C_out % 64 == 0 and C_in % 128 == 0
     xneed = lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 256, 256, BF16)
     assert xneed == 9 * 256 * 256 * 2
     assert lib.sv_workspace_bytes(ops.SV_OP_DX, 22656, 256, 256, BF16) == xneed
     assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 128, 128, BF16) == 9 * 128 * 128 * 2
     assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 192, 192, BF16) == 0
     assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 3, 256, 256, F32) == 0
-    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 5, 256, 256, BF16) == 0
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 5, 256, 256, BF16) == 25 * 256 * 256 * 2
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 7, 128, 256, BF16) == 49 * 128 * 256 * 2
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 1, 256, 256, BF16) == 0     # 1 x 1: from 512
+    assert lib.sv_workspace_bytes_k(ops.SV_OP_DX, 22656, 1, 256, 512, BF16) == 512 * 256 * 2
     assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, 22656, 256, 256, BF16, 0, FAKE, xneed - 1,
                                       None) == ops.SV_ERR_WORKSPACE
     assert lib.sv_repack_dx_k(FAKE, 3, 256, 256, BF16, FAKE, xneed - 1, None) == ops.SV_ERR_WORKSPACE

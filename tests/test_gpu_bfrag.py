@@ -1,6 +1,6 @@
 """The matrix-core kernel that streams the weights in fragment order
-(bf16, 3 x 3, contracted channels a multiple of 64, produced channels a
-multiple of 128): forward and input gradient against the oracle in every
+(bf16, 3 x 3, 5 x 5, 7 x 7 or 1 x 1, contracted channels a multiple of 64,
+produced channels a multiple of 128): forward and input gradient against the oracle in every
 staging mode and tile shape, and bit for bit against the kernel that reads
 Wt directly (the input gradient without a workspace).  The split forms
 (repack, then the packed call) must equal the single calls bit for bit."""
@@ -196,3 +196,35 @@ def test_one_by_one(Ci, Co):
     torch.cuda.synchronize()
     assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), "bf16", f"1x1 {Ci}->{Co} Y")
     assert_close(host(dX), O.bwd_dx(L.dY, N, L.Wt), "bf16", f"1x1 {Ci}->{Co} dX")
+
+
+# (seed, T, H, W, keep, Ci, Co, shuffle, K)
+KXK_CASES = [
+    (71, 4, 14, 14, 0.6, 128, 128, False, 5),    # window mode: reach 2W + 2 = 30 rows
+    (72, 4, 16, 16, 0.6, 256, 128, False, 7),    # window mode: reach 3W + 3 = 51 of the 64-row halo
+    (73, 3, 16, 16, 0.5, 128, 256, True, 5),     # shuffled packing: gather mode
+    (74, 3, 24, 24, 0.5, 128, 128, False, 7),    # 24 wide: reach 75 rows, gather mode
+    (75, 9, 14, 14, [0, 1, 196, 0, 60, 3, 150, 0, 77], 256, 256, False, 7),   # empty frames, ragged tail
+]
+
+
+@pytest.mark.parametrize("case", KXK_CASES, ids=lambda c: f"seed{c[0]}-K{c[-1]}")
+def test_fragment_kernel_kxk(case):
+    """5 x 5 and 7 x 7 layers on the fragment kernel (a 64-row halo):
+    forward and input gradient against the oracle, and the input gradient
+    bit for bit against the kernel that reads Wt directly."""
+    seed, T, H, W, keep, Ci, Co, sh, K = case
+    L = wl.make_random_case(seed, T, H, W, keep, Ci, Co, "bf16", shuffle=sh, ksize=K)
+    _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W, K=K)
+    print(f"n={L.n} K={K} Ci={Ci} Co={Co} shuffle={sh}", flush=True)
+    X, Wt, b, dY = dev(L.X, bf), dev(L.Wt, bf), dev(L.b, bf), dev(L.dY, bf)
+    Nd = dev(N)
+    Y = ops.sparseconv2d_fwd(X, Nd, Wt, b, "mfma")
+    dXf = torch.empty((L.n, Ci), dtype=bf, device="cuda")
+    dXd = torch.empty((L.n, Ci), dtype=bf, device="cuda")
+    ops.sv_sparseconv2d_bwd_dx_k(dY, Nd, Wt, dXf, "mfma")
+    ops.sv_sparseconv2d_bwd_dx_k(dY, Nd, Wt, dXd, "mfma", workspace=0)
+    torch.cuda.synchronize()
+    assert torch.equal(dXf.view(torch.int16), dXd.view(torch.int16)), f"K={K}: fragment and direct dX differ"
+    assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), "bf16", f"K={K} {case} Y")
+    assert_close(host(dXf), O.bwd_dx(L.dY, N, L.Wt), "bf16", f"K={K} {case} dX")
