@@ -625,6 +625,11 @@ def measure_layer(key, kernel="auto", ksize=3, steps=20, warmup=3, dw_stream="si
     if pass_ms:
         out["pass_ms"] = pass_ms
         out["pass_tflops"] = {k: round(fl_pass / (v * 1e-3) / 1e12, 2) for k, v in pass_ms.items() if k != "index"}
+        # each conv pass alone against the gather-model HBM roofline (the
+        # index build and the weight repack excluded: a table and repacked
+        # weights serve every pass and layer that share them)
+        out["pass_frac_hbm_gather_model"] = {k: round(gather_bytes / (v * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
+                                             for k, v in pass_ms.items() if k in ("fwd", "dx")}
     if chunked:
         out["dw_stream"] = dw_stream
     return out
