@@ -61,6 +61,14 @@ def test_validation_without_device(lib):
     assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 64, F32, 2, None, 0, None) == ops.SV_ERR_UNSUPPORTED
     assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 48, 64, BF16, 2, None, 0, None) == ops.SV_ERR_UNSUPPORTED
     assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, 8, 64, 40, BF16, 2, None, 0, None) == ops.SV_ERR_UNSUPPORTED
+    # the matrix-core kernels read their operands through 32-bit buffer offsets: 2 GiB at most
+    # (2^22 tokens of 256 bf16 channels is exactly that; one token more is refused when MFMA is forced)
+    lim = 1 << 22
+    assert lib.sv_workspace_bytes(ops.SV_OP_FWD, lim, 256, 256, BF16) > 0
+    assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, lim + 1, 256, 256, BF16, 2, None, 0,
+                                   None) == ops.SV_ERR_UNSUPPORTED
+    assert lib.sv_sparseconv2d_bwd_dx(FAKE, FAKE, FAKE, FAKE, lim + 1, 256, 256, BF16, 2, None, 0,
+                                      None) == ops.SV_ERR_UNSUPPORTED
     # forward on the matrix cores without its weight workspace
     assert lib.sv_sparseconv2d_fwd(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 64, BF16, 0, None, 0, None) == ops.SV_ERR_WORKSPACE
     assert lib.sv_workspace_bytes(ops.SV_OP_FWD, 8, 64, 64, BF16) >= 9 * 64 * 64 * 2
