@@ -4,7 +4,9 @@ Here they are exactly 2 GiB (16,384 frames of a fully kept 16 x 16 grid:
 2^22 tokens x 256 channels bf16).  The neighbour table, the forward and the
 input gradient are checked on sampled rows (the first, the last, tile
 boundaries and random ones) against the oracle, which computes them one by
-one from those rows' neighbours.  (One token more is refused: test_abi.)"""
+one from those rows' neighbours; the weight and bias gradients over all the
+tokens with dY nonzero only on the sampled rows.  (One token more is
+refused: test_abi.)"""
 import numpy as np
 import pytest
 import torch
@@ -59,7 +61,7 @@ def test_two_gib_operands():
     Xs = X[need_d].float().cpu().numpy()
     Wh, bh = Wt.float().cpu().numpy(), b.float().cpu().numpy()
     Ys = Y[rows_d].float().cpu().numpy()
-    del X, Y
+    del Y
     assert_close(Ys, O.fwd_rows(Xs, Nsub, Wh, bh, sub), "bf16", "2 GiB forward, sampled rows")
 
     dY = rand_dev(g, (n, C))
@@ -69,3 +71,21 @@ def test_two_gib_operands():
     dYs = dY[need_d].float().cpu().numpy()
     dXs = dX[rows_d].float().cpu().numpy()
     assert_close(dXs, O.bwd_dx_rows(dYs, Nsub, Wh, sub), "bf16", "2 GiB input gradient, sampled rows")
+
+    # weight and bias gradients over all 2^22 tokens, with dY zero except on
+    # the sampled rows: the kernels still address every token (and split
+    # them into slices as usual), while the exact sums reduce to those rows,
+    # which the oracle computes on a compact problem (the neighbour rows
+    # first with no taps and no gradient, then the sampled tokens)
+    del dX
+    dY.zero_()
+    dY[rows_d] = rand_dev(g, (rows.size, C))
+    dW, db = ops.sparseconv2d_bwd_dw(X, N, dY)
+    torch.cuda.synchronize()
+    print(f"n={n}: weight gradient done", flush=True)
+    m = need.size
+    Xc = np.concatenate([Xs, np.zeros((rows.size, C), np.float32)])
+    Nc = np.concatenate([np.full((m, 9), -1, np.int32), Nsub])
+    dYc = np.concatenate([np.zeros((m, C), np.float32), dY[rows_d].float().cpu().numpy()])
+    assert_close(dW.cpu().numpy(), O.bwd_dw(Xc, Nc, dYc), "bf16", "2 GiB weight gradient")
+    assert_close(db.cpu().numpy(), O.bwd_db(dYc), "bf16", "2 GiB bias gradient")
