@@ -56,7 +56,6 @@
 namespace svc {
 
 constexpr int BF_WAVES = 4;              // waves per workgroup (2 x 2)
-constexpr int BF_BN = 256;               // output channels per tile at NB = 4 (128 per wave)
 constexpr int BF_KC = 64;                // contracted channels per chunk
 constexpr int BF_HALO = 32;              // window rows on either side of the tile
 constexpr int BF_ROWB = 128;             // bytes per window row
