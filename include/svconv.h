@@ -446,7 +446,9 @@ sv_status sv_adapter_fwd(const void *X, const int32_t *N, int64_t n, int32_t K, 
  *   dWd = X^T dH1,  dbd = sum_k dH1[k];     dX  = dY + dH1 Wd^T
  * (the last sum in one kernel, before its one rounding).  dW* and db* are
  * fp32, overwritten; db* nullable.  dH2 and dH1 are held in the workspace in
- * `dtype` (sv_adapter_workspace_bytes(1, ...) bytes, 256-byte aligned).
+ * `dtype` (sv_adapter_workspace_bytes(1, ...) bytes, 256-byte aligned), with
+ * the weight-gradient partials and the input gradients' weights repacked in
+ * fragment order where the bf16 matrix-core kernel takes them.
  * Deterministic.
  * dw_stream (nullable; the call's own stream means the same): the three
  * weight gradients run on it, each after the tensor it reads is ready on

@@ -933,7 +933,7 @@ namespace {
 // on one stream, so one region serves them all).
 struct AdapterLayout {
     int taps = 0;
-    size_t id_bytes = 0, h_bytes = 0, rest_bytes = 0, total = 0;
+    size_t id_bytes = 0, h_bytes = 0, rest_bytes = 0, p_bytes = 0, total = 0;
 };
 
 sv_status adapter_layout(bool backward, int64_t n, int32_t K, int32_t C, int32_t r, sv_dtype dt, AdapterLayout* L) {
@@ -952,8 +952,11 @@ sv_status adapter_layout(bool backward, int64_t n, int32_t K, int32_t C, int32_t
         L->rest_bytes = std::max({dw_workspace_bytes(plan_dw(n, r, C, bf, 1)),
                                   dw_workspace_bytes(plan_dw(n, r, r, bf, L->taps)),
                                   dw_workspace_bytes(plan_dw(n, C, r, bf, 1))});
+        // the input gradients' weights in fragment order, where the fragment
+        // kernel takes them (the last one, with its residual, never does)
+        L->p_bytes = std::max(dx_ws_bytes(r, C, dt, n, 1), dx_ws_bytes(r, r, dt, n, L->taps));
     }
-    L->total = L->id_bytes + 2 * L->h_bytes + align_up(L->rest_bytes);
+    L->total = L->id_bytes + 2 * L->h_bytes + align_up(L->rest_bytes) + align_up(L->p_bytes);
     return SV_OK;
 }
 
@@ -1033,6 +1036,23 @@ sv_status sv_adapter_bwd(const void* X, const int32_t* N, int64_t n, int32_t K, 
     void* dH2 = base + L.id_bytes;
     void* dH1 = base + L.id_bytes + L.h_bytes;
     void* dws = base + L.id_bytes + 2 * L.h_bytes;
+    void* Pw = L.p_bytes ? base + L.id_bytes + 2 * L.h_bytes + align_up(L.rest_bytes) : nullptr;
+    // An input gradient on the fragment kernel where it takes the shape: its
+    // weights repacked into Pw first (the calls run in order on `stream`, so
+    // one region serves all three).
+    auto dx_layer = [&](const void* g, const int32_t* Nt, const void* Wt, void* out, int32_t Ci, int32_t Co,
+                        int taps, const void* R) -> sv_status {
+        const void* P = nullptr;
+        if (Pw && !R && kernel != SV_KERNEL_VALU && dx_ws_bytes(Ci, Co, dtype, n, taps) > 0 &&
+            reinterpret_cast<uintptr_t>(Wt) % 16 == 0) {
+            const sv_status s1 = hip_status(launch_repack_frag(static_cast<const uint16_t*>(Wt),
+                                                               static_cast<uint16_t*>(Pw), Ci, Co, taps, true,
+                                                               stream));
+            if (s1 != SV_OK) return s1;
+            P = Pw;
+        }
+        return run_dx(g, Nt, Wt, out, n, Ci, Co, taps, dtype, kernel, stream, R, P);
+    };
     // With a dW stream each weight gradient waits (event) for the tensor it
     // reads, produced on `stream`; they run in order on that stream and share
     // one partials region.  Nothing either stream reads is overwritten.
@@ -1052,19 +1072,19 @@ sv_status sv_adapter_bwd(const void* X, const int32_t* N, int64_t n, int32_t K, 
     if ((st = hip_status(launch_dw(plan_dw(n, r, C, bf, 1), bf, H2, I, dY, dWu, dbu, n, r, C, 0, dws, ds))) !=
         SV_OK)
         return st;
-    if ((st = run_dx(dY, I, Wu, dH2, n, r, C, 1, dtype, kernel, stream)) != SV_OK) return st;
+    if ((st = dx_layer(dY, I, Wu, dH2, r, C, 1, nullptr)) != SV_OK) return st;
     if ((st = handoff(1)) != SV_OK) return st;
     // K x K convolution: dWc, dbc, then dH1
     if ((st = hip_status(launch_dw(plan_dw(n, r, r, bf, L.taps), bf, H1, N, dH2, dWc, dbc, n, r, r, 0, dws,
                                    ds))) != SV_OK)
         return st;
-    if ((st = run_dx(dH2, N, Wc, dH1, n, r, r, L.taps, dtype, kernel, stream)) != SV_OK) return st;
+    if ((st = dx_layer(dH2, N, Wc, dH1, r, r, L.taps, nullptr)) != SV_OK) return st;
     if ((st = handoff(2)) != SV_OK) return st;
     // down-projection: dWd, dbd, then dX = dY + dH1 Wd^T
     if ((st = hip_status(launch_dw(plan_dw(n, C, r, bf, 1), bf, X, I, dH1, dWd, dbd, n, C, r, 0, dws, ds))) !=
         SV_OK)
         return st;
-    if ((st = run_dx(dH1, I, Wd, dX, n, C, r, 1, dtype, kernel, stream, dY)) != SV_OK) return st;
+    if ((st = dx_layer(dH1, I, Wd, dX, C, r, 1, dY)) != SV_OK) return st;
     if (split && (hipEventRecord(E.ev[3], ds) != hipSuccess || hipStreamWaitEvent(stream, E.ev[3], 0) != hipSuccess))
         return SV_ERR_HIP;
     return SV_OK;
