@@ -118,7 +118,7 @@ sv_status run_dx(const void* dY, const int32_t* N, const void* Wt, void* dX, int
 // chip together.
 sv_status run_fwd_dx_pair(const void* X, const void* dY, const int32_t* N, const void* Wt, const void* V,
                           const void* P, const void* bias, void* Y, void* dX, int64_t n, int32_t Ci, int32_t Co,
-                          int taps, hipStream_t s) {
+                          int taps, int slots, hipStream_t s) {
     if (n == 0) return SV_OK;
     if (P && conv_bfrag_pair_ok(Ci, Co, Co, Ci, taps))
         // both passes on the fragment kernel (V and P in fragment order)
@@ -126,7 +126,7 @@ sv_status run_fwd_dx_pair(const void* X, const void* dY, const int32_t* N, const
                                                  static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(Y), Ci,
                                                  Co, static_cast<const uint16_t*>(dY),
                                                  static_cast<const uint16_t*>(P), static_cast<uint16_t*>(dX), Co,
-                                                 Ci, N, n, taps, s));
+                                                 Ci, N, n, taps, slots, s));
     if (conv_bfrag_ok(Ci, Co, taps) || conv_bfrag_ok(Co, Ci, taps)) {
         // fragment-order weights for one of the passes: each runs on its own launch
         sv_status st = run_fwd_prepared(true, X, N, Wt, V, bias, Y, n, Ci, Co, taps, SV_BF16, s);
@@ -610,7 +610,14 @@ sv_status sv_sparseconv2d_chunked(const sv_chunked_desc* d, uint32_t passes, voi
         char* Yc = (passes & SV_PASS_FWD) ? static_cast<char*>(d->Y) + t0 * d->C_out * es : nullptr;
         char* dXc = (passes & SV_PASS_DX) ? static_cast<char*>(d->dX) + t0 * d->C_in * es : nullptr;
         if (fwd_mfma && dx_mfma) {
-            st = run_fwd_dx_pair(X, dY, Nc, d->Wt, Vw, Pw, d->bias, Yc, dXc, nc, d->C_in, d->C_out, L.taps, stream);
+            // With the weight gradients on their own stream the paired
+            // launch takes about half the chip (larger tiles): a dW
+            // workgroup needs more LDS than a conv workgroup leaves free on
+            // its compute unit, so with the conv grid on every unit the
+            // chunk's dW waited for it (config 4: 0.506-0.517 -> 0.490-0.492
+            // ms per pass).
+            st = run_fwd_dx_pair(X, dY, Nc, d->Wt, Vw, Pw, d->bias, Yc, dXc, nc, d->C_in, d->C_out, L.taps,
+                                 split ? kBfragSlots / 2 : kBfragSlots, stream);
             if (st != SV_OK) return st;
         } else {
             if (passes & SV_PASS_FWD) {
@@ -879,7 +886,7 @@ sv_status sv_sparseconv2d_chunked_host(const sv_chunked_host_desc* d, uint32_t p
         if (s2 != SV_OK) return s2;
         if (fwd_mfma && dx_mfma) {
             s2 = run_fwd_dx_pair(st[b].X, st[b].dY, Nc, d->Wt, Vw, Pw, d->bias, st[b].Y, st[b].dX, nc, d->C_in,
-                                 d->C_out, taps, compute);
+                                 d->C_out, taps, kBfragSlots, compute);
             if (s2 != SV_OK) return s2;
         } else {
             if (passes & SV_PASS_FWD) {

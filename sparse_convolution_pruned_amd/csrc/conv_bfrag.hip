@@ -479,20 +479,20 @@ hipError_t launch_repack_frag(const uint16_t* Wt, uint16_t* Bf, int Ci, int Co, 
 // whose grid is one round of at most 256 tiles (one per compute unit of a
 // 256-CU part); at equal size, 256 channels (NB = 4: half the A reads per
 // MFMA).  Without such a tile, the largest one the channel count allows.
-// A paired launch (NO2 > 0) counts both problems' tiles and needs a shape
-// that divides both channel counts.  Depends on the arguments only; every
-// shape gives the same bits.
+// A paired launch (NO2 > 0) counts both problems' tiles against `slots` and
+// needs a shape that divides both channel counts.  Depends on the arguments
+// only; every shape gives the same bits.
 struct BfragShape {
     int mb, nb;
 };
 static int64_t bfrag_tiles(BfragShape t, int64_t n, int NO) {
     return NO > 0 ? ((n + 64 * t.mb - 1) / (64 * t.mb)) * (NO / (64 * t.nb)) : 0;
 }
-static BfragShape bfrag_shape(int64_t n, int NO, int NO2 = 0) {
+static BfragShape bfrag_shape(int64_t n, int NO, int NO2 = 0, int slots = BF_MAXTILES) {
     static const BfragShape order[] = {{2, 2}, {3, 2}, {2, 4}, {4, 2}, {3, 4}, {4, 4}};    // by tile size
     for (const BfragShape& t : order) {
         if (NO % (64 * t.nb) != 0 || NO2 % (64 * t.nb) != 0) continue;
-        if (bfrag_tiles(t, n, NO) + bfrag_tiles(t, n, NO2) <= BF_MAXTILES) return t;
+        if (bfrag_tiles(t, n, NO) + bfrag_tiles(t, n, NO2) <= slots) return t;
     }
     return NO % 256 == 0 && NO2 % 256 == 0 ? BfragShape{4, 4} : BfragShape{4, 2};
 }
@@ -535,10 +535,10 @@ hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t
 
 hipError_t launch_conv_bfrag_pair(const uint16_t* A1, const uint16_t* B1, const uint16_t* bias1, uint16_t* out1,
                                   int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
-                                  int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream) {
+                                  int NO2, const int32_t* N, int64_t n, int taps, int slots, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    if (!conv_bfrag_pair_ok(K1, NO1, K2, NO2, taps)) return hipErrorInvalidValue;
-    const BfragShape t = bfrag_shape(n, NO1, NO2);
+    if (!conv_bfrag_pair_ok(K1, NO1, K2, NO2, taps) || slots < 1) return hipErrorInvalidValue;
+    const BfragShape t = bfrag_shape(n, NO1, NO2, slots);
     const int64_t tiles1 = bfrag_tiles(t, n, NO1);
     const dim3 grid(static_cast<unsigned>(tiles1 + bfrag_tiles(t, n, NO2)));
     const int ni = static_cast<int>(n);

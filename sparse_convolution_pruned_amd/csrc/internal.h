@@ -135,10 +135,13 @@ hipError_t launch_repack_batch(int count, const uint16_t* const* W, uint16_t* co
 hipError_t launch_conv_bfrag(const uint16_t* A, const int32_t* N, const uint16_t* Bf, const uint16_t* bias,
                              uint16_t* out, int64_t n, int K, int NO, int taps, hipStream_t stream);
 // Two problems on the same N in one launch, each as launch_conv_bfrag (the
-// second without bias): the shapes must suit conv_bfrag_pair_ok.
+// second without bias): the shapes must suit conv_bfrag_pair_ok.  slots:
+// the workgroups the tile shape may count on (kBfragSlots, one per compute
+// unit, or fewer to leave room for a kernel on another stream).
+constexpr int kBfragSlots = 256;
 hipError_t launch_conv_bfrag_pair(const uint16_t* A1, const uint16_t* B1, const uint16_t* bias1, uint16_t* out1,
                                   int K1, int NO1, const uint16_t* A2, const uint16_t* B2, uint16_t* out2, int K2,
-                                  int NO2, const int32_t* N, int64_t n, int taps, hipStream_t stream);
+                                  int NO2, const int32_t* N, int64_t n, int taps, int slots, hipStream_t stream);
 size_t conv_mfma_fwd_workspace(int Ci, int Co, int taps);
 // bf16, a tap count the kernel is built for, contracted channels a multiple
 // of 32, output channels of 16, and the n rows of A and of the output within
