@@ -207,6 +207,95 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ A,
     }
 }
 
+// Small problems: one workgroup per 16 tokens x 16 produced channels, one
+// output per thread, 64 contracted channels per round, the next round
+// prefetched into registers.  A 128 x 64 tile holds one workgroup on its
+// compute unit and walks its rounds with each wave waiting on its loads, so
+// while the wide tiles number fewer than the compute units a pass takes the
+// same time whatever the token count (about 80 us at 64 channels, 300 us at
+// 256, for 98 tokens as for 16,000).  The small tiles spread the same work
+// over 32 times as many workgroups; measured, they win up to about 96 wide
+// tiles.  The terms of every output are summed in the same order (taps, then
+// channels), so both kernels give the same bits.
+constexpr int ST_M = 16, ST_N = 16, ST_K = 64;
+constexpr int64_t kValuSmallBelow = 96;     // 128 x 64 tiles under which the small kernel runs
+
+template <typename T, bool DX>
+__global__ __launch_bounds__(256) void k_conv_valu_small(const T* __restrict__ A, const int32_t* __restrict__ Nt,
+                                                         const T* __restrict__ Wt, const T* __restrict__ bias,
+                                                         const T* __restrict__ R, T* __restrict__ out, int n, int Ci,
+                                                         int Co, int taps) {
+    const int K = DX ? Co : Ci;
+    const int NO = DX ? Ci : Co;
+    __shared__ float sA[2][ST_K][ST_M + 1];     // [channel][row]
+    __shared__ float sB[2][ST_K][ST_N + 1];     // [channel][column]
+    extern __shared__ int sN[];                 // [ST_M][taps], dynamic
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * ST_M;
+    const int n0 = blockIdx.y * ST_N;
+    for (int e = tid; e < ST_M * taps; e += 256) {
+        const int64_t k = k0 + e / taps;
+        sN[e] = (k < n) ? clamp_index(Nt[k * taps + e % taps], n) : -1;
+    }
+    __syncthreads();
+
+    const int nck = (K + ST_K - 1) / ST_K;
+    const int rounds = taps * nck;
+    // Round r's elements: A (16 rows x 64 channels) and B (64 x 16), four of each per thread.
+    float va[4], vb[4];
+    auto fetch = [&](int r) {
+        const int j = r / nck, c0 = (r - j * nck) * ST_K;
+        const int jt = DX ? taps - 1 - j : j;        // input gradient: the mirrored weight tap
+        const T* __restrict__ Wj = Wt + static_cast<int64_t>(jt) * Ci * Co;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i;
+            const int row = e >> 6, kk = e & 63;
+            const int m = sN[row * taps + j];
+            va[i] = (m >= 0 && c0 + kk < K) ? Elem<T>::load(A + static_cast<int64_t>(m) * K + c0 + kk) : 0.f;
+            if (!DX) {   // B(kk, c) = Wj[c0 + kk][n0 + c]
+                const int kb = e >> 4, c = e & 15;
+                vb[i] = (c0 + kb < K && n0 + c < NO) ? Elem<T>::load(Wj + static_cast<int64_t>(c0 + kb) * Co + n0 + c)
+                                                     : 0.f;
+            } else {     // B(kk, c) = Wt[taps-1-j][n0 + c][c0 + kk], read along Co
+                const int c = e >> 6, kb = e & 63;
+                vb[i] = (c0 + kb < K && n0 + c < NO) ? Elem<T>::load(Wj + static_cast<int64_t>(n0 + c) * Co + c0 + kb)
+                                                     : 0.f;
+            }
+        }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i;
+            sA[buf][e & 63][e >> 6] = va[i];
+            if (!DX) sB[buf][e >> 4][e & 15] = vb[i];
+            else sB[buf][e & 63][e >> 6] = vb[i];
+        }
+    };
+    float acc = 0.f;
+    fetch(0);
+    commit(0);
+    __syncthreads();
+    for (int r = 0; r < rounds; ++r) {
+        const int cur = r & 1;
+        const bool more = r + 1 < rounds;
+        if (more) fetch(r + 1);
+#pragma unroll 8
+        for (int kk = 0; kk < ST_K; ++kk) acc = fmaf(sA[cur][kk][ty], sB[cur][kk][tx], acc);
+        if (more) commit(cur ^ 1);
+        __syncthreads();
+    }
+    const int64_t row = k0 + ty;
+    const int col = n0 + tx;
+    if (row < n && col < NO) {
+        float v = acc;
+        if (!DX && bias) v += Elem<T>::load(bias + col);
+        if (R) v += Elem<T>::load(R + row * NO + col);
+        Elem<T>::store(out + row * NO + col, v);
+    }
+}
+
 template <typename T>
 static void launch_valu_typed(bool dx, bool vec, dim3 grid, size_t lds, hipStream_t stream, const T* A,
                               const int32_t* N, const T* Wt, const T* bias, const T* R, T* out, int n, int Ci,
@@ -226,6 +315,26 @@ hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
     const int NO = dx ? Ci : Co;
     dim3 grid(static_cast<unsigned>((n + FT_M - 1) / FT_M), static_cast<unsigned>((NO + FT_N - 1) / FT_N));
     const int nn = static_cast<int>(n);
+    if (static_cast<int64_t>(grid.x) * grid.y < kValuSmallBelow) {
+        const dim3 sgrid(static_cast<unsigned>((n + ST_M - 1) / ST_M), static_cast<unsigned>((NO + ST_N - 1) / ST_N));
+        const size_t slds = static_cast<size_t>(ST_M) * taps * sizeof(int);
+#define SV_VALU_SMALL(T)                                                                                              \
+    do {                                                                                                              \
+        auto a = static_cast<const T*>(A);                                                                            \
+        auto w = static_cast<const T*>(Wt);                                                                           \
+        auto b = static_cast<const T*>(bias);                                                                         \
+        auto r = static_cast<const T*>(R);                                                                            \
+        auto o = static_cast<T*>(out);                                                                                \
+        if (dx) hipLaunchKernelGGL((k_conv_valu_small<T, true>), sgrid, dim3(256), slds, stream, a, N, w, b, r, o, nn, \
+                                   Ci, Co, taps);                                                                     \
+        else hipLaunchKernelGGL((k_conv_valu_small<T, false>), sgrid, dim3(256), slds, stream, a, N, w, b, r, o, nn,  \
+                                Ci, Co, taps);                                                                        \
+    } while (0)
+        if (bf16) SV_VALU_SMALL(uint16_t);
+        else SV_VALU_SMALL(float);
+#undef SV_VALU_SMALL
+        return hipGetLastError();
+    }
     // four-channel loads: channel counts multiples of 4 and A, Wt aligned to 4 elements
     const size_t es = bf16 ? 2 : 4;
     const bool vec = Ci % 4 == 0 && Co % 4 == 0 && reinterpret_cast<uintptr_t>(A) % (4 * es) == 0 &&

@@ -64,12 +64,13 @@ def dev_at(a, dtype, offset):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("offset", [0, 1])
 def test_valu_vector_loads(dt, offset):
-    # Channel counts multiples of 4 over three 128-token tiles with a ragged
-    # tail and a ragged channel tile: four-channel loads when X, dY and the
-    # weights are aligned (offset 0), element-wise staging when they are not
-    # (offset 1); both against the oracle.
-    L = wl.make_random_case(7, 3, 14, 14, 0.45, 48, 80, dt, shuffle=True)
-    assert 256 < L.n < 384
+    # Channel counts multiples of 4 over 128 x 64 tiles with a ragged token
+    # tail and a ragged channel tile (at least 96 tiles per pass, so the wide
+    # tile kernel runs): four-channel loads when X, dY and the weights are
+    # aligned (offset 0), element-wise staging when they are not (offset 1);
+    # both against the oracle.
+    L = wl.make_random_case(7, 140, 14, 14, 0.45, 48, 80, dt, shuffle=True)
+    assert 96 * 128 < L.n < 97 * 128
     _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
     t = tdtype(dt)
     X, Wt, dY, b = (dev_at(a, t, offset) for a in (L.X, L.Wt, L.dY, L.b))
@@ -80,6 +81,36 @@ def test_valu_vector_loads(dt, offset):
     torch.cuda.synchronize()
     assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), dt, f"Y offset {offset}")
     assert_close(host(dX), O.bwd_dx(L.dY, N, L.Wt), dt, f"dX offset {offset}")
+
+
+def pad_rows(a, extra):
+    return np.concatenate([a, np.zeros((extra,) + a.shape[1:], a.dtype)])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("taps", [9, 25])
+def test_valu_small_and_wide_tiles_agree(dt, taps):
+    # Below 96 tiles of 128 tokens x 64 channels the VALU passes run on
+    # 16 x 16 tiles.  Both kernels sum each output's terms in the same order,
+    # so a problem on the small tiles and the same rows inside a problem on
+    # the wide ones (the extra rows referenced by no one, with no neighbours)
+    # give the same bits.  The small problem is also checked against the oracle.
+    rng = np.random.default_rng(40 + taps)
+    n, big, Ci, Co = 300, 12300, 64, 96
+    L = wl.make_random_case(41, 1, 40, 40, [n], Ci, Co, dt, ksize=3 if taps == 9 else 5)
+    N = rng.integers(-1, n, size=(n, taps)).astype(np.int32)
+    assert -(-n // 128) * -(-Co // 64) < 96 <= -(-big // 128) * -(-Ci // 64)
+    t = tdtype(dt)
+    Nb = np.concatenate([N, np.full((big - n, taps), -1, np.int32)])
+    Wd, bd = dev(L.Wt, t), dev(L.b, t)
+    Y = ops.sparseconv2d_fwd(dev(L.X, t), dev(N), Wd, bd, "valu")
+    dX = ops.sparseconv2d_bwd_dx(dev(L.dY, t), dev(N), Wd, "valu")
+    Yb = ops.sparseconv2d_fwd(dev(pad_rows(L.X, big - n), t), dev(Nb), Wd, bd, "valu")
+    dXb = ops.sparseconv2d_bwd_dx(dev(pad_rows(L.dY, big - n), t), dev(Nb), Wd, "valu")
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Yb[:n]) and torch.equal(dX, dXb[:n])
+    assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), dt, f"small tiles Y taps {taps}")
+    assert_close(host(dX), O.bwd_dx(L.dY, N, L.Wt), dt, f"small tiles dX taps {taps}")
 
 
 BF16_CASES = [
