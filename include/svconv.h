@@ -230,9 +230,9 @@ size_t sv_workspace_bytes_k(sv_op op, int64_t n, int32_t K, int32_t C_in, int32_
  *     with the same arguments and workspace and in this order (the second
  *     may run on another stream once the first has finished), equal one
  *     sv_sparseconv2d_bwd_dw_k call bit for bit: the first writes the token
- *     slices' partials into the workspace (or dW itself with one slice), the
- *     second adds them in fixed order.  db must be given to both or to
- *     neither.  The workspace stays in use until the second completes. */
+ *     slices' partials into the workspace (or dW and db themselves with one
+ *     slice), the second adds them in fixed order.  db must be given to both
+ *     or to neither.  The workspace stays in use until the second completes. */
 sv_status sv_repack_fwd_k(const void *Wt, int32_t K, int32_t C_in, int32_t C_out, sv_dtype dtype,
                           void *V, size_t V_bytes, hipStream_t stream);
 sv_status sv_sparseconv2d_fwd_packed_k(const void *X, const int32_t *N, const void *V,

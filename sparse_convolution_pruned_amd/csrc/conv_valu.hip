@@ -208,28 +208,57 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ A,
 }
 
 // Small problems: one workgroup per 16 tokens x 16 produced channels, one
-// output per thread, 64 contracted channels per round, the next round
-// prefetched into registers.  A 128 x 64 tile holds one workgroup on its
-// compute unit and walks its rounds with each wave waiting on its loads, so
-// while the wide tiles number fewer than the compute units a pass takes the
-// same time whatever the token count (about 80 us at 64 channels, 300 us at
-// 256, for 98 tokens as for 16,000).  The small tiles spread the same work
-// over 32 times as many workgroups; measured, they win up to about 96 wide
-// tiles.  The terms of every output are summed in the same order (taps, then
-// channels), so both kernels give the same bits.
-constexpr int ST_M = 16, ST_N = 16, ST_K = 64;
-constexpr int64_t kValuSmallBelow = 96;     // 128 x 64 tiles under which the small kernel runs
+// output per thread, 64 contracted channels per round, the next round loaded
+// into registers while the current one is summed.  A 128 x 64 tile holds one
+// workgroup on its compute unit and walks its rounds with each wave waiting
+// on its loads, so while the wide tiles number fewer than the compute units
+// a pass takes the same time whatever the token count (about 80 us at 64
+// channels, 300 us at 256, for 98 tokens as for 16,000).  The small tiles
+// spread the same work over 32 times as many workgroups; measured, they win
+// up to about 190 wide tiles.  The terms of every output are summed in the
+// same order (taps, then channels), so both kernels give the same bits.
+//
+// Both operands sit in LDS with the contracted index contiguous, so a
+// thread reads four channels of its row and of its column with two 128-bit
+// reads per four FMAs.  The loads are raw buffer loads: an element out of
+// range (a pruned neighbour, a channel or token past the end) gets an offset
+// past the buffer's range and reads as zero, with no branch.  Operands above
+// 2 GiB go to the wide kernels (host check).  Loading further rounds ahead
+// was measured slower.
+constexpr int ST_M = 16, ST_N = 16, ST_K = 64, ST_P = ST_K + 4;
+constexpr int64_t kValuSmallBelow = 192;    // 128 x 64 tiles under which the small kernel runs
+
+template <typename T> __device__ __forceinline__ uint32_t raw_load(rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ uint32_t raw_load<float>(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ uint32_t raw_load<uint16_t>(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+template <typename T> __device__ __forceinline__ float raw_f32(uint32_t v) {
+    return __uint_as_float(sizeof(T) == 2 ? v << 16 : v);
+}
+// acc += a[0] b[0] + ... + a[3] b[3], one term at a time in that order.
+__device__ __forceinline__ float fma4(const float4 a, const float4 b, float acc) {
+    acc = fmaf(a.x, b.x, acc);
+    acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc);
+    return fmaf(a.w, b.w, acc);
+}
 
 template <typename T, bool DX>
 __global__ __launch_bounds__(256) void k_conv_valu_small(const T* __restrict__ A, const int32_t* __restrict__ Nt,
                                                          const T* __restrict__ Wt, const T* __restrict__ bias,
                                                          const T* __restrict__ R, T* __restrict__ out, int n, int Ci,
                                                          int Co, int taps) {
+    constexpr uint32_t es = sizeof(T);
     const int K = DX ? Co : Ci;
     const int NO = DX ? Ci : Co;
-    __shared__ float sA[2][ST_K][ST_M + 1];     // [channel][row]
-    __shared__ float sB[2][ST_K][ST_N + 1];     // [channel][column]
-    extern __shared__ int sN[];                 // [ST_M][taps], dynamic
+    const rsrc_t rA = make_rsrc(A, static_cast<uint32_t>(static_cast<int64_t>(n) * K * es));
+    const rsrc_t rW = make_rsrc(Wt, static_cast<uint32_t>(static_cast<int64_t>(taps) * Ci * Co * es));
+    __shared__ __align__(16) float sA[2][ST_M][ST_P];     // [row][channel]
+    __shared__ __align__(16) float sB[2][ST_N][ST_P];     // [column][channel]
+    extern __shared__ int sN[];                           // [ST_M][taps], dynamic
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int64_t k0 = static_cast<int64_t>(blockIdx.x) * ST_M;
     const int n0 = blockIdx.y * ST_N;
@@ -241,48 +270,55 @@ __global__ __launch_bounds__(256) void k_conv_valu_small(const T* __restrict__ A
 
     const int nck = (K + ST_K - 1) / ST_K;
     const int rounds = taps * nck;
-    // Round r's elements: A (16 rows x 64 channels) and B (64 x 16), four of each per thread.
-    float va[4], vb[4];
+    // Round r: A (16 rows x 64 channels) and B (64 channels x 16 columns),
+    // four elements of each per thread, held raw until written to LDS.
+    uint32_t va[4], vb[4];
     auto fetch = [&](int r) {
         const int j = r / nck, c0 = (r - j * nck) * ST_K;
         const int jt = DX ? taps - 1 - j : j;        // input gradient: the mirrored weight tap
-        const T* __restrict__ Wj = Wt + static_cast<int64_t>(jt) * Ci * Co;
+        const uint32_t wj = static_cast<uint32_t>(jt) * Ci * Co;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = tid + 256 * i;
             const int row = e >> 6, kk = e & 63;
             const int m = sN[row * taps + j];
-            va[i] = (m >= 0 && c0 + kk < K) ? Elem<T>::load(A + static_cast<int64_t>(m) * K + c0 + kk) : 0.f;
-            if (!DX) {   // B(kk, c) = Wj[c0 + kk][n0 + c]
-                const int kb = e >> 4, c = e & 15;
-                vb[i] = (c0 + kb < K && n0 + c < NO) ? Elem<T>::load(Wj + static_cast<int64_t>(c0 + kb) * Co + n0 + c)
-                                                     : 0.f;
-            } else {     // B(kk, c) = Wt[taps-1-j][n0 + c][c0 + kk], read along Co
-                const int c = e >> 6, kb = e & 63;
-                vb[i] = (c0 + kb < K && n0 + c < NO) ? Elem<T>::load(Wj + static_cast<int64_t>(n0 + c) * Co + c0 + kb)
-                                                     : 0.f;
+            va[i] = raw_load<T>(rA, (m >= 0 && c0 + kk < K) ? (static_cast<uint32_t>(m) * K + c0 + kk) * es : kOob);
+            int kb, c;
+            uint32_t w;
+            if (!DX) {   // B(kb, c) = Wt[j][c0 + kb][n0 + c]
+                kb = e >> 4;
+                c = e & 15;
+                w = wj + static_cast<uint32_t>(c0 + kb) * Co + n0 + c;
+            } else {     // B(kb, c) = Wt[taps-1-j][n0 + c][c0 + kb], read along Co
+                c = e >> 6;
+                kb = e & 63;
+                w = wj + static_cast<uint32_t>(n0 + c) * Co + c0 + kb;
             }
+            vb[i] = raw_load<T>(rW, (c0 + kb < K && n0 + c < NO) ? w * es : kOob);
         }
     };
     auto commit = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = tid + 256 * i;
-            sA[buf][e & 63][e >> 6] = va[i];
-            if (!DX) sB[buf][e >> 4][e & 15] = vb[i];
-            else sB[buf][e & 63][e >> 6] = vb[i];
+            sA[buf][e >> 6][e & 63] = raw_f32<T>(va[i]);
+            if (!DX) sB[buf][e & 15][e >> 4] = raw_f32<T>(vb[i]);
+            else sB[buf][e >> 6][e & 63] = raw_f32<T>(vb[i]);
         }
     };
-    float acc = 0.f;
     fetch(0);
     commit(0);
     __syncthreads();
+    float acc = 0.f;
     for (int r = 0; r < rounds; ++r) {
         const int cur = r & 1;
         const bool more = r + 1 < rounds;
         if (more) fetch(r + 1);
-#pragma unroll 8
-        for (int kk = 0; kk < ST_K; ++kk) acc = fmaf(sA[cur][kk][ty], sB[cur][kk][tx], acc);
+        const float* __restrict__ a = &sA[cur][ty][0];
+        const float* __restrict__ bb = &sB[cur][tx][0];
+#pragma unroll 4
+        for (int kk = 0; kk < ST_K; kk += 4)
+            acc = fma4(*reinterpret_cast<const float4*>(a + kk), *reinterpret_cast<const float4*>(bb + kk), acc);
         if (more) commit(cur ^ 1);
         __syncthreads();
     }
@@ -315,7 +351,9 @@ hipError_t launch_conv_valu(bool bf16, bool dx, const void* A, const int32_t* N,
     const int NO = dx ? Ci : Co;
     dim3 grid(static_cast<unsigned>((n + FT_M - 1) / FT_M), static_cast<unsigned>((NO + FT_N - 1) / FT_N));
     const int nn = static_cast<int>(n);
-    if (static_cast<int64_t>(grid.x) * grid.y < kValuSmallBelow) {
+    const int64_t esz = bf16 ? 2 : 4;
+    if (static_cast<int64_t>(grid.x) * grid.y < kValuSmallBelow && n * (dx ? Co : Ci) * esz <= kMaxRange &&
+        static_cast<int64_t>(taps) * Ci * Co * esz <= kMaxRange) {
         const dim3 sgrid(static_cast<unsigned>((n + ST_M - 1) / ST_M), static_cast<unsigned>((NO + ST_N - 1) / ST_N));
         const size_t slds = static_cast<size_t>(ST_M) * taps * sizeof(int);
 #define SV_VALU_SMALL(T)                                                                                              \
@@ -417,11 +455,110 @@ __global__ __launch_bounds__(256) void k_dw_valu(const T* __restrict__ X,
     }
 }
 
+// Small problems: 16 input x 16 output channels per workgroup, one output per
+// thread, 64 tokens per round, the next round loaded into registers while
+// the current one is summed, both operands in LDS with the tokens contiguous
+// (as in k_conv_valu_small).  Each output adds its tokens in ascending
+// order, as k_dw_valu does, so the two give the same bits.  Measured, it is
+// the faster of the two at up to 64 x 64 channels whatever the token count
+// (at 32,000 tokens and 64 channels: 149 against 171 us), and otherwise while
+// k_dw_valu's grid is under 256 workgroups.
+constexpr int DS_M = 16, DS_N = 16, DS_K = 64, DS_P = DS_K + 4;
+constexpr int DS_NMAX = 2048;                // most tokens per slice (the slice's N column sits in LDS)
+constexpr int64_t kDwValuSmallBelow = 256;   // k_dw_valu workgroups under which this kernel runs
+constexpr int64_t kDwValuSmallChannels = 64 * 64;   // C_in x C_out up to which it always runs
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_dw_valu_small(const T* __restrict__ X, const int32_t* __restrict__ Nt,
+                                                       const T* __restrict__ dY, float* __restrict__ out, int n,
+                                                       int Ci, int Co, int taps, int64_t slice_tokens, int direct,
+                                                       int accumulate) {
+    constexpr uint32_t es = sizeof(T);
+    const rsrc_t rX = make_rsrc(X, static_cast<uint32_t>(static_cast<int64_t>(n) * Ci * es));
+    const rsrc_t rD = make_rsrc(dY, static_cast<uint32_t>(static_cast<int64_t>(n) * Co * es));
+    __shared__ __align__(16) float sG[2][DS_M][DS_P];     // [input channel][token]
+    __shared__ __align__(16) float sD[2][DS_N][DS_P];     // [output channel][token]
+    __shared__ int sNc[DS_NMAX];                          // N[k][j] over the slice
+    const int tilesI = (Ci + DS_M - 1) / DS_M;
+    const int i0 = (blockIdx.x % tilesI) * DS_M;
+    const int o0 = (blockIdx.x / tilesI) * DS_N;
+    const int j = blockIdx.y;
+    const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * slice_tokens;
+    const int64_t kend = min(static_cast<int64_t>(n), kbeg + slice_tokens);
+    const int rounds = kend > kbeg ? static_cast<int>((kend - kbeg + DS_K - 1) / DS_K) : 0;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    for (int t = tid; t < kend - kbeg; t += 256) sNc[t] = clamp_index(Nt[(kbeg + t) * taps + j], n);
+    __syncthreads();
+    uint32_t vg[4], vd[4];
+    auto fetch = [&](int r) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            const int kk = e >> 4, c = e & 15;
+            const int t = r * DS_K + kk;                 // token kbeg + t
+            const bool in = kbeg + t < kend;
+            const int m = in ? sNc[t] : -1;
+            vg[q] = raw_load<T>(rX, (m >= 0 && i0 + c < Ci) ? (static_cast<uint32_t>(m) * Ci + i0 + c) * es : kOob);
+            vd[q] = raw_load<T>(rD, (in && o0 + c < Co) ? (static_cast<uint32_t>(kbeg + t) * Co + o0 + c) * es
+                                                        : kOob);
+        }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            sG[buf][e & 15][e >> 4] = raw_f32<T>(vg[q]);
+            sD[buf][e & 15][e >> 4] = raw_f32<T>(vd[q]);
+        }
+    };
+    if (rounds > 0) {
+        fetch(0);
+        commit(0);
+    }
+    __syncthreads();
+    float acc = 0.f;
+    for (int r = 0; r < rounds; ++r) {
+        const int cur = r & 1;
+        const bool more = r + 1 < rounds;
+        if (more) fetch(r + 1);
+        const float* __restrict__ g = &sG[cur][ty][0];
+        const float* __restrict__ d = &sD[cur][tx][0];
+#pragma unroll 4
+        for (int kk = 0; kk < DS_K; kk += 4)
+            acc = fma4(*reinterpret_cast<const float4*>(g + kk), *reinterpret_cast<const float4*>(d + kk), acc);
+        if (more) commit(cur ^ 1);
+        __syncthreads();
+    }
+    const int i = i0 + ty, o = o0 + tx;
+    if (i < Ci && o < Co) {
+        float* dst = out + (direct ? static_cast<int64_t>(j) * Ci * Co
+                                   : (static_cast<int64_t>(blockIdx.z) * taps + j) * Ci * Co) +
+                     static_cast<int64_t>(i) * Co + o;
+        *dst = (direct && accumulate) ? *dst + acc : acc;
+    }
+}
+
 hipError_t launch_dw_valu(bool bf16, const void* X, const int32_t* N, const void* dY, float* out,
                           int64_t n, int Ci, int Co, int taps, int slices, int64_t slice_tokens,
                           int direct, int accumulate, hipStream_t stream) {
     const int tiles = ((Ci + VT_M - 1) / VT_M) * ((Co + VT_N - 1) / VT_N);
     dim3 grid(tiles, taps, slices);
+    const int64_t es = bf16 ? 2 : 4;
+    const bool small = static_cast<int64_t>(tiles) * taps * slices < kDwValuSmallBelow ||
+                       static_cast<int64_t>(Ci) * Co <= kDwValuSmallChannels;
+    if (small && slice_tokens <= DS_NMAX && n * Ci * es <= kMaxRange && n * Co * es <= kMaxRange) {
+        const int stiles = ((Ci + DS_M - 1) / DS_M) * ((Co + DS_N - 1) / DS_N);
+        const dim3 sgrid(stiles, taps, slices);
+        if (bf16)
+            hipLaunchKernelGGL(k_dw_valu_small<uint16_t>, sgrid, dim3(256), 0, stream,
+                               static_cast<const uint16_t*>(X), N, static_cast<const uint16_t*>(dY), out,
+                               static_cast<int>(n), Ci, Co, taps, slice_tokens, direct, accumulate);
+        else
+            hipLaunchKernelGGL(k_dw_valu_small<float>, sgrid, dim3(256), 0, stream, static_cast<const float*>(X),
+                               N, static_cast<const float*>(dY), out, static_cast<int>(n), Ci, Co, taps,
+                               slice_tokens, direct, accumulate);
+        return hipGetLastError();
+    }
     if (bf16)
         hipLaunchKernelGGL(k_dw_valu<uint16_t>, grid, dim3(256), 0, stream,
                            static_cast<const uint16_t*>(X), N, static_cast<const uint16_t*>(dY), out,

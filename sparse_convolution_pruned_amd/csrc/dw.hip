@@ -368,9 +368,12 @@ __global__ __launch_bounds__(DW_THREADS) void k_dw_mfma(const uint16_t* __restri
 }
 
 // db partials: block = 64 columns x 4 row phases; fixed-order combine in LDS.
+// With one slice (`direct`) the sums go straight to db, added to it under
+// `accumulate`.
 template <typename T>
 __global__ __launch_bounds__(256) void k_db_partial(const T* __restrict__ dY, float* __restrict__ part,
-                                                    int n, int Co, int64_t slice_tokens) {
+                                                    int n, int Co, int64_t slice_tokens, int direct,
+                                                    int accumulate) {
     __shared__ float red[4][64];
     const int c = threadIdx.x & 63, ph = threadIdx.x >> 6;
     const int o = blockIdx.x * 64 + c;
@@ -381,8 +384,11 @@ __global__ __launch_bounds__(256) void k_db_partial(const T* __restrict__ dY, fl
         for (int64_t k = kbeg + ph; k < kend; k += 4) sum += Elem<T>::load(dY + k * Co + o);
     red[ph][c] = sum;
     __syncthreads();
-    if (ph == 0 && o < Co)
-        part[static_cast<int64_t>(blockIdx.y) * Co + o] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    if (ph == 0 && o < Co) {
+        const float v = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+        float* d = part + static_cast<int64_t>(blockIdx.y) * Co + o;
+        *d = (direct && accumulate) ? *d + v : v;
+    }
 }
 
 // out[e] (+)= sum_{s < slices} part[s][e], s ascending (4 floats per thread).
@@ -532,12 +538,13 @@ hipError_t launch_dw_partials(const DwPlan& plan, bool bf16, const void* X, cons
                          plan.slice_tokens, direct ? 1 : 0, accumulate, stream);
     if (err != hipSuccess || !db) return err;
     dim3 grid(static_cast<unsigned>(ceil_div(Co, 64)), plan.slices);
+    float* dbdst = direct ? db : dbpart;
     if (bf16)
         hipLaunchKernelGGL(k_db_partial<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(dY),
-                           dbpart, static_cast<int>(n), Co, plan.slice_tokens);
+                           dbdst, static_cast<int>(n), Co, plan.slice_tokens, direct ? 1 : 0, accumulate);
     else
-        hipLaunchKernelGGL(k_db_partial<float>, grid, dim3(256), 0, stream, static_cast<const float*>(dY), dbpart,
-                           static_cast<int>(n), Co, plan.slice_tokens);
+        hipLaunchKernelGGL(k_db_partial<float>, grid, dim3(256), 0, stream, static_cast<const float*>(dY), dbdst,
+                           static_cast<int>(n), Co, plan.slice_tokens, direct ? 1 : 0, accumulate);
     return hipGetLastError();
 }
 
@@ -551,8 +558,9 @@ hipError_t launch_dw_reduce(const DwPlan& plan, float* dW, float* db, int Ci, in
         reinterpret_cast<const float*>(static_cast<const char*>(ws) + up(plan.partial_floats * sizeof(float)));
     const bool direct = plan.slices == 1;
     hipError_t err = hipSuccess;
-    // db partials of the MFMA kernel go through the dW reduction launch.
-    bool db_done = db && plan.mfma && direct;
+    // With one slice both kernels wrote db directly; otherwise the db
+    // partials go through the dW reduction launch.
+    bool db_done = db && direct;
     if (!direct) {
         const int64_t count = static_cast<int64_t>(plan.taps) * Ci * Co;
         if (count % 4 == 0) {

@@ -65,12 +65,12 @@ def dev_at(a, dtype, offset):
 @pytest.mark.parametrize("offset", [0, 1])
 def test_valu_vector_loads(dt, offset):
     # Channel counts multiples of 4 over 128 x 64 tiles with a ragged token
-    # tail and a ragged channel tile (at least 96 tiles per pass, so the wide
-    # tile kernel runs): four-channel loads when X, dY and the weights are
-    # aligned (offset 0), element-wise staging when they are not (offset 1);
-    # both against the oracle.
-    L = wl.make_random_case(7, 140, 14, 14, 0.45, 48, 80, dt, shuffle=True)
-    assert 96 * 128 < L.n < 97 * 128
+    # tail and a ragged channel tile (at least 192 tiles per pass, so the
+    # wide tile kernel runs): four-channel loads when X, dY and the weights
+    # are aligned (offset 0), element-wise staging when they are not (offset
+    # 1); both against the oracle.
+    L = wl.make_random_case(7, 280, 14, 14, 0.45, 48, 80, dt, shuffle=True)
+    assert 192 * 128 < L.n < 193 * 128
     _, N, _ = O.build_index(L.coords, L.frame_offsets, L.T, L.H, L.W)
     t = tdtype(dt)
     X, Wt, dY, b = (dev_at(a, t, offset) for a in (L.X, L.Wt, L.dY, L.b))
@@ -90,16 +90,16 @@ def pad_rows(a, extra):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("taps", [9, 25])
 def test_valu_small_and_wide_tiles_agree(dt, taps):
-    # Below 96 tiles of 128 tokens x 64 channels the VALU passes run on
+    # Below 192 tiles of 128 tokens x 64 channels the VALU passes run on
     # 16 x 16 tiles.  Both kernels sum each output's terms in the same order,
     # so a problem on the small tiles and the same rows inside a problem on
     # the wide ones (the extra rows referenced by no one, with no neighbours)
     # give the same bits.  The small problem is also checked against the oracle.
     rng = np.random.default_rng(40 + taps)
-    n, big, Ci, Co = 300, 12300, 64, 96
+    n, big, Ci, Co = 300, 24600, 64, 96
     L = wl.make_random_case(41, 1, 40, 40, [n], Ci, Co, dt, ksize=3 if taps == 9 else 5)
     N = rng.integers(-1, n, size=(n, taps)).astype(np.int32)
-    assert -(-n // 128) * -(-Co // 64) < 96 <= -(-big // 128) * -(-Ci // 64)
+    assert -(-n // 128) * -(-Co // 64) < 192 <= -(-big // 128) * -(-Ci // 64)
     t = tdtype(dt)
     Nb = np.concatenate([N, np.full((big - n, taps), -1, np.int32)])
     Wd, bd = dev(L.Wt, t), dev(L.b, t)
@@ -111,6 +111,49 @@ def test_valu_small_and_wide_tiles_agree(dt, taps):
     assert torch.equal(Y, Yb[:n]) and torch.equal(dX, dXb[:n])
     assert_close(host(Y), O.fwd(L.X, N, L.Wt, L.b), dt, f"small tiles Y taps {taps}")
     assert_close(host(dX), O.bwd_dx(L.dY, N, L.Wt), dt, f"small tiles dX taps {taps}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_valu_dw_small_and_wide_tiles_agree(dt):
+    # The VALU weight gradient runs on 16 x 16 tiles up to 64 x 64 channels,
+    # and when its 64 x 64 grid would be under 256 workgroups.
+    # dW[:, :64, :64] and db[:64] of a 352-channel problem (wide tiles, 324
+    # workgroups; not a multiple of 128, so not the matrix-core kernel in
+    # bf16) whose first 64 channels are those of a 64-channel problem
+    # (small tiles) are the same sums in the same order: the same bits, also
+    # when added to existing values.  Under 512 tokens both take one token
+    # slice.  The small problem is also checked against the oracle, and a
+    # 2,000-token one with three slices.
+    rng = np.random.default_rng(43)
+    n, C, Cb = 300, 64, 352
+    t = tdtype(dt)
+    L = wl.make_random_case(44, 1, 40, 40, [n], Cb, Cb, dt)
+    N = dev(rng.integers(-1, n, size=(n, 9)).astype(np.int32))
+    Xb, dYb = dev(L.X, t), dev(L.dY, t)
+    Xs, dYs = Xb[:, :C].contiguous(), dYb[:, :C].contiguous()
+    start = torch.from_numpy(rng.standard_normal((9, Cb, Cb)).astype(np.float32)).cuda()
+    dbs0 = torch.from_numpy(rng.standard_normal(Cb).astype(np.float32)).cuda()
+    outs = []
+    for X, dY, Cc in ((Xs, dYs, C), (Xb, dYb, Cb)):
+        dW, db = ops.sparseconv2d_bwd_dw(X, N, dY)
+        dWa = start[:, :Cc, :Cc].clone(memory_format=torch.contiguous_format)    # never `start` itself
+        dba = dbs0[:Cc].clone()
+        ops.sv_sparseconv2d_bwd_dw(X, N, dY, dWa, dba, accumulate=True)
+        outs.append((dW, db, dWa, dba))
+    torch.cuda.synchronize()
+    (dW, db, dWa, dba), (dWb, dbb, dWab, dbab) = outs
+    assert torch.equal(dW, dWb[:, :C, :C]) and torch.equal(db, dbb[:C])
+    assert torch.equal(dWa, dWab[:, :C, :C]) and torch.equal(dba, dbab[:C])
+    Xh, dYh, Nh = host(Xs), host(dYs), host(N)
+    assert_close(host(dW), O.bwd_dw(Xh, Nh, dYh), dt, "small-tile dW")
+    assert_close(host(db), O.bwd_db(dYh), dt, "small-tile db")
+    assert_close(host(dWa), host(start[:, :C, :C]) + O.bwd_dw(Xh, Nh, dYh), dt, "small-tile dW accumulated")
+    L2 = wl.make_random_case(45, 1, 50, 50, [2000], C, C, dt)
+    _, N2, _ = O.build_index(L2.coords, L2.frame_offsets, 1, 50, 50)
+    dW2, db2 = ops.sparseconv2d_bwd_dw(dev(L2.X, t), dev(N2), dev(L2.dY, t))
+    torch.cuda.synchronize()
+    assert_close(host(dW2), O.bwd_dw(L2.X, N2, L2.dY), dt, "small-tile dW, three slices")
+    assert_close(host(db2), O.bwd_db(L2.dY), dt, "small-tile db, three slices")
 
 
 BF16_CASES = [
