@@ -395,8 +395,14 @@ __global__ __launch_bounds__(256) void k_dw_valu(const T* __restrict__ X,
                                                  const T* __restrict__ dY, float* __restrict__ out,
                                                  int n, int Ci, int Co, int taps, int64_t slice_tokens,
                                                  int direct, int accumulate) {
-    __shared__ float sG[VT_K][VT_M + 4];
-    __shared__ float sD[VT_K][VT_N + 4];
+    // Each thread owns 4 consecutive input x 4 consecutive output channels
+    // and reads them as one 128-bit LDS read per operand per token.  Rounds
+    // of VT_K tokens are double-buffered: round r + 1 is loaded into
+    // registers while round r is summed, then written to the other buffer,
+    // one barrier per round.  (Plain 64-bit addressing: inputs above 2 GiB
+    // come here.)
+    __shared__ __align__(16) float sG[2][VT_K][VT_M + 4];
+    __shared__ __align__(16) float sD[2][VT_K][VT_N + 4];
     const int tilesI = (Ci + VT_M - 1) / VT_M;
     const int i0 = (blockIdx.x % tilesI) * VT_M;
     const int o0 = (blockIdx.x / tilesI) * VT_N;
@@ -404,14 +410,12 @@ __global__ __launch_bounds__(256) void k_dw_valu(const T* __restrict__ X,
     const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * slice_tokens;
     const int64_t kend = min(static_cast<int64_t>(n), kbeg + slice_tokens);
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    float acc[4][4];
+    constexpr int PER = VT_K * VT_M / 256;          // elements of each operand per thread and round
+    float vg[PER], vd[PER];
+    auto fetch = [&](int64_t kb) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-
-    for (int64_t kb = kbeg; kb < kend; kb += VT_K) {
-        for (int e = tid; e < VT_K * VT_M; e += 256) {
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + 256 * u;
             const int kk = e / VT_M, c = e % VT_M;
             const int64_t k = kb + kk;
             float g = 0.f, d = 0.f;
@@ -420,34 +424,56 @@ __global__ __launch_bounds__(256) void k_dw_valu(const T* __restrict__ X,
                 if (m >= 0 && i0 + c < Ci) g = Elem<T>::load(X + static_cast<int64_t>(m) * Ci + i0 + c);
                 if (o0 + c < Co) d = Elem<T>::load(dY + k * Co + o0 + c);
             }
-            sG[kk][c] = g;
-            sD[kk][c] = d;
+            vg[u] = g;
+            vd[u] = d;
         }
-        __syncthreads();
+    };
+    auto commit = [&](int buf) {
 #pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + 256 * u;
+            sG[buf][e / VT_M][e % VT_M] = vg[u];
+            sD[buf][e / VT_M][e % VT_M] = vd[u];
+        }
+    };
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+
+    if (kbeg < kend) {
+        fetch(kbeg);
+        commit(0);
+    }
+    __syncthreads();
+    int cur = 0;
+    for (int64_t kb = kbeg; kb < kend; kb += VT_K) {
+        const bool more = kb + VT_K < kend;
+        if (more) fetch(kb + VT_K);
+#pragma unroll 4
         for (int kk = 0; kk < VT_K; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a[q] = sG[kk][ty + 16 * q];
-                b[q] = sD[kk][tx + 16 * q];
-            }
+            const float4 a4 = *reinterpret_cast<const float4*>(&sG[cur][kk][4 * ty]);
+            const float4 b4 = *reinterpret_cast<const float4*>(&sD[cur][kk][4 * tx]);
+            const float a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
             for (int p = 0; p < 4; ++p)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) acc[p][q] = fmaf(a[p], b[q], acc[p][q]);
         }
+        if (more) commit(cur ^ 1);
         __syncthreads();
+        cur ^= 1;
     }
     float* dst = out + (direct ? static_cast<int64_t>(j) * Ci * Co
                                : (static_cast<int64_t>(blockIdx.z) * taps + j) * Ci * Co);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int i = i0 + ty + 16 * p;
+        const int i = i0 + 4 * ty + p;
         if (i >= Ci) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int o = o0 + tx + 16 * q;
+            const int o = o0 + 4 * tx + q;
             if (o >= Co) continue;
             float* d = dst + static_cast<int64_t>(i) * Co + o;
             *d = (direct && accumulate) ? *d + acc[p][q] : acc[p][q];
