@@ -952,7 +952,7 @@ sv_status adapter_layout(bool backward, int64_t n, int32_t K, int32_t C, int32_t
     if (!backward) {
         L->h_bytes = 0;
         L->rest_bytes = std::max({fwd_ws_bytes(C, r, dt, n, 1), fwd_ws_bytes(r, r, dt, n, L->taps),
-                                  fwd_ws_bytes(r, C, dt, n, 1)});
+                                  fwd_ws_bytes(r, C, dt, n, 1), dense_res_ws_bytes(r, C)});
     } else {
         L->h_bytes = align_up(static_cast<size_t>(n) * r * es);
         const bool bf = dt == SV_BF16;
@@ -961,7 +961,8 @@ sv_status adapter_layout(bool backward, int64_t n, int32_t K, int32_t C, int32_t
                                   dw_workspace_bytes(plan_dw(n, C, r, bf, 1))});
         // the input gradients' weights in fragment order, where the fragment
         // kernel takes them (the last one, with its residual, never does)
-        L->p_bytes = std::max(dx_ws_bytes(r, C, dt, n, 1), dx_ws_bytes(r, r, dt, n, L->taps));
+        L->p_bytes = std::max({dx_ws_bytes(r, C, dt, n, 1), dx_ws_bytes(r, r, dt, n, L->taps),
+                               dense_res_ws_bytes(r, C)});
     }
     L->total = L->id_bytes + 2 * L->h_bytes + align_up(L->rest_bytes) + align_up(L->p_bytes);
     return SV_OK;
@@ -974,6 +975,15 @@ sv_status adapter_layer_fwd(const void* X, const int32_t* N, const void* Wt, con
     bool mfma = false;
     sv_status st = choose(kernel, dt, false, Ci, Co, n, taps, &mfma);
     if (st != SV_OK) return st;
+    if (mfma && R && taps == 1 && dense_res_supported(dt == SV_BF16, Ci, Co, n)) {
+        // the up-projection with its residual: the dense streaming kernel
+        st = hip_status(launch_repack_dense(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(V), Ci, Co,
+                                            false, s));
+        if (st != SV_OK || n == 0) return st;
+        return hip_status(launch_dense_res(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(V),
+                                           static_cast<const uint16_t*>(bias), static_cast<const uint16_t*>(R),
+                                           static_cast<uint16_t*>(Y), n, Ci, Co, s));
+    }
     if (mfma) {
         // with a residual the layer runs on k_conv_mfma: its per-tap layout
         st = hip_status(launch_repack_fwd(static_cast<const uint16_t*>(Wt), static_cast<uint16_t*>(V), Ci, Co,
@@ -1049,6 +1059,21 @@ sv_status sv_adapter_bwd(const void* X, const int32_t* N, int64_t n, int32_t K, 
     // one region serves all three).
     auto dx_layer = [&](const void* g, const int32_t* Nt, const void* Wt, void* out, int32_t Ci, int32_t Co,
                         int taps, const void* R) -> sv_status {
+        if (R && Pw && taps == 1 && kernel != SV_KERNEL_VALU && dense_res_supported(bf, Co, Ci, n)) {
+            // dX = R + g W^T on the dense streaming kernel (K = Co contracted,
+            // Ci produced), when the MFMA path takes the layer
+            bool m = false;
+            const sv_status s0 = choose(kernel, dtype, true, Ci, Co, n, taps, &m);
+            if (s0 != SV_OK) return s0;
+            if (m) {
+                const sv_status s1 = hip_status(launch_repack_dense(static_cast<const uint16_t*>(Wt),
+                                                                    static_cast<uint16_t*>(Pw), Co, Ci, true, stream));
+                if (s1 != SV_OK || n == 0) return s1;
+                return hip_status(launch_dense_res(static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(Pw),
+                                                   nullptr, static_cast<const uint16_t*>(R),
+                                                   static_cast<uint16_t*>(out), n, Co, Ci, stream));
+            }
+        }
         const void* P = nullptr;
         if (Pw && !R && kernel != SV_KERNEL_VALU && dx_ws_bytes(Ci, Co, dtype, n, taps) > 0 &&
             reinterpret_cast<uintptr_t>(Wt) % 16 == 0) {

@@ -187,6 +187,16 @@ hipError_t launch_xattn_bwd(const XattnPlan& p, bool bf16, const void* Q, const 
                             const void* dO, const float* lse, int m, int64_t n, int d, float scale, float* dQ,
                             void* dX, void* ws, hipStream_t stream);
 
+// Dense 1 x 1 layer with a residual, Y = A B + bias + R (bf16; K in {64,
+// 128, 256} contracted channels, Co a multiple of 256): B repacked into
+// fragment order (dense_res_ws_bytes) from W = B (trans = false, [K][Co]) or
+// W = B^T (trans = true, [Co][K]); bias and R nullable.
+bool dense_res_supported(bool bf16, int K, int Co, int64_t n);
+size_t dense_res_ws_bytes(int K, int Co);
+hipError_t launch_repack_dense(const uint16_t* W, uint16_t* Bf, int K, int Co, bool trans, hipStream_t stream);
+hipError_t launch_dense_res(const uint16_t* A, const uint16_t* Bf, const uint16_t* bias, const uint16_t* R,
+                            uint16_t* Y, int64_t n, int K, int Co, hipStream_t stream);
+
 hipError_t launch_stage_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n_rows,
                                void* dst, int C, int elem_bytes, hipStream_t stream);
 hipError_t launch_stage_scatter(const void* src, const int32_t* rows, int64_t n_rows, void* dst,
