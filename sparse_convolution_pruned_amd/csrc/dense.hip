@@ -32,7 +32,10 @@
 // (94 us); the next tile's R requested a tile earlier into registers (the
 // compiler then waited for every load at the loop head); 32-token tiles with
 // two LDS tile buffers (77 us); 128-wide blocks with two workgroups per
-// compute unit (80 us: every A row is then fetched by twice as many waves).
+// compute unit (80 us: every A row is then fetched by twice as many waves);
+// half of the B block in registers to make room for two 64-token tile
+// buffers (512 registers, and the compiler's waits at the head of the
+// two-tile loop took every load in flight).
 #include "internal.h"
 #include "mfma.h"
 
@@ -41,7 +44,6 @@ namespace svc {
 constexpr int DR_TOK = 64;        // tokens per tile
 constexpr int DR_CB = 256;        // output channels per workgroup
 constexpr int DR_THREADS = 256;   // 4 waves, one per SIMD
-constexpr int DR_KMAX = 256;      // contracted channels held in LDS
 
 // B in fragment order: [Co / 256][K / 16][8 channel blocks][64 lanes][8 bf16].
 // Piece (ks, j) of channel block cb is the MFMA A-operand fragment of output
