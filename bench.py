@@ -134,7 +134,6 @@ class StagedRun:
         self.side = torch.cuda.Stream() if dw_stream == "side" else None
         self.ready = [torch.cuda.Event() for _ in range(self.L)]
         self.ev_start, self.ev_prep, self.ev_join = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
-        self.ev_wfwd, self.ev_wdx = torch.cuda.Event(), torch.cuda.Event()
         self.plan = None
         vb = max(256, ops.sv_workspace_bytes(ops.SV_OP_FWD, max(self.ns), C, C, bf))
         self.V = [torch.empty(vb, dtype=torch.uint8, device="cuda") for _ in range(self.L)]
@@ -281,25 +280,16 @@ class StagedRun:
         self._rp = [(ctypes.c_void_p * self.L)(*[t.data_ptr() for t in ts]) for ts in (self.W, self.V, self.P)]
 
         vb = self.ws.numel()
-        # side stream: every layer's forward weights (one launch), the later
-        # stages' index tables, then every layer's input-gradient weights;
-        # the main stream meanwhile builds the first stage's table.  (With
-        # both repacks in one launch on the main stream after that table the
-        # first forward started ~18 us into the step.)
+        # side stream: the later stages' index tables
         record(self.ev_start, main)
         wait(side, self.ev_start)
-        call("sv_repack_layers_k", self.L, self._rp[0], self._rp[1], self.V[0].numel(), None, 0, K, C, C, bf,
-             hs[id(side)])
-        record(self.ev_wfwd, side)
         for s in range(1, len(self.ns)):
             index(s, side)
         record(self.ev_prep, side)
-        call("sv_repack_layers_k", self.L, self._rp[0], None, 0, self._rp[2], self.P[0].numel(), K, C, C, bf,
-             hs[id(side)])
-        record(self.ev_wdx, side)
-        # main stream: index, forward
+        # main stream: index, all weights, forward
         index(0, main)
-        wait(main, self.ev_wfwd)
+        call("sv_repack_layers_k", self.L, self._rp[0], self._rp[1], self.V[0].numel(), self._rp[2], self.P[0].numel(),
+             K, C, C, bf, hs[id(main)])
         for l in range(self.L):
             s = self.stage_of[l]
             if l == self.lps:
@@ -312,7 +302,6 @@ class StagedRun:
         # backward: each layer's dW (partials and their reduction) on the
         # side stream, dX and the stage scatters on main
         g = self.dy_last
-        wait(main, self.ev_wdx)                 # the input-gradient weights
         for l in reversed(range(self.L)):
             s = self.stage_of[l]
             record(self.ready[l], main)         # dY of this layer is ready on the main stream
