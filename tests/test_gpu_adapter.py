@@ -79,6 +79,17 @@ def test_adapter_mfma_forced_and_unsupported():
     assert e.value.status == ops.SV_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("C, r, T, keep", [(256, 128, 1, 0.15), (512, 256, 3, 1.0), (256, 64, 5, 0.4)])
+def test_adapter_dense_residual_tiles(C, r, T, keep):
+    """The residual layers on the dense streaming kernel (output width a
+    multiple of 256): fewer tokens than one 64-token tile (38), whole tiles
+    only with two 256-wide output blocks (C = 512, 3 full 16 x 16 frames: 768
+    tokens), and a ragged last tile (510 tokens, K = 64 contracted channels)."""
+    A = wl.make_adapter_case(70 + T, T, 16, 16, keep, C, r, 3, "bf16")
+    print(f"n = {A.n}", flush=True)
+    check(A, "auto", f"dense residual C={C} r={r} n={A.n}")
+
+
 def test_adapter_empty_and_deterministic():
     A = wl.make_adapter_case(66, 2, 14, 14, [0, 0], 128, 64, 3, "bf16")
     assert A.n == 0
